@@ -1,0 +1,165 @@
+/*
+ * ssc.h -- spatial-spectral coupling on AMD Instinct MI355X (gfx950).
+ *
+ * The coupling of deep functional-map pipelines is the product
+ *     Pi_NM Phi_M = softmax(F_N F_M^T * scale) Phi_M,
+ * i.e. scaled dot-product attention with Q = F_N (target descriptors,
+ * n_N x d), K = F_M (source descriptors, n_M x d) and V = Phi_M (source
+ * Laplace-Beltrami basis, n_M x k); the softmax runs over source vertices
+ * for every target vertex and scale is 1/sqrt(d) for the pages' coupling
+ * ("Spatial-Spectral Coupling as Attention", project page, section
+ * "How it works"; the map Pi_NM itself is never formed, section
+ * "The bottleneck").
+ *
+ * Two variants, each with forward and backward:
+ *   dense  -- the exact coupling;
+ *   geo    -- Geo-FlashAttention (section "Geo-FlashAttention" and its
+ *             pipeline figure): both shapes are split into patches, source
+ *             keys are pooled per patch, source patches are scored against
+ *             each target patch, the top s are kept, and every target row
+ *             takes the exact softmax over the union of its patch's selected
+ *             source patches only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to dense row-major arrays
+ *   (row stride = width), 16-byte aligned.  The caller owns every buffer;
+ *   the library never allocates device memory.  Scratch space comes from
+ *   the caller through (ws, ws_bytes); ssc_workspace_bytes() gives the size.
+ * - dtype selects the storage of Q, K, V and dO: SSC_BF16 (bf16 bits,
+ *   MFMA bf16 x bf16 -> fp32) or SSC_F32 (fp32 MFMA).  O, lse, dQ, dK, dV
+ *   are always fp32.  lse is in natural log.
+ * - Supported shapes: d in {64, 128}; 1 <= k <= 256 (padded internally to
+ *   the next of 32, 64, 128, 224, 256); n_M >= 1; n_N >= 0 (n_N = 0 is a
+ *   no-op).  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= min(P_M, 64).
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *   stream) and re-entrant: no global mutable state, no host sync.
+ *   Argument validation happens before any HIP call; on failure nothing is
+ *   launched and an error status is returned.  SSC_ERR_HIP means a launch
+ *   failed; ssc_last_hip_error() returns that hipError_t (thread-local).
+ * - Workspaces must not be shared by calls that may run concurrently.
+ * - Outputs must not overlap inputs.  Non-finite inputs are undefined.
+ */
+#ifndef SSC_H
+#define SSC_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSC_OK = 0,
+  SSC_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, overlap */
+  SSC_ERR_UNSUPPORTED = 2,  /* d, k, P or s outside the compiled set */
+  SSC_ERR_WORKSPACE = 3,    /* ws too small (or NULL with ws_bytes > 0) */
+  SSC_ERR_HIP = 4           /* a HIP launch failed */
+} ssc_status;
+
+typedef enum { SSC_F32 = 0, SSC_BF16 = 1 } ssc_dtype;
+
+typedef enum {
+  SSC_OP_DENSE_FWD = 0,
+  SSC_OP_DENSE_BWD = 1,
+  SSC_OP_PATCH_TOPK = 2,
+  SSC_OP_GEO_FWD = 3,
+  SSC_OP_GEO_BWD = 4
+} ssc_op;
+
+typedef void* ssc_stream; /* hipStream_t */
+
+/* Bytes of scratch an entry point needs for these sizes (0 if the sizes are
+ * invalid).  Arguments not used by an op are ignored. */
+size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                           int P_N, int P_M, int s);
+
+/*
+ * Dense forward (project page, "How it works"):
+ *   O[i, :] = sum_j softmax_j(scale * Q[i].K[j]) V[j, :],
+ *   lse[i]  = log sum_j exp(scale * Q[i].K[j]).
+ * Q [n_N x d], K [n_M x d], V [n_M x k] in `dtype`; O [n_N x k] fp32,
+ * lse [n_N] fp32.
+ */
+ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                              const void* Q, const void* K, const void* V, float scale,
+                              float* O, float* lse, void* ws, size_t ws_bytes,
+                              ssc_stream stream);
+
+/*
+ * Dense backward: gradients of <dO, O> for the coupling above, recomputing
+ * the softmax from lse (no map stored):
+ *   D_i = sum_c dO_ic O_ic,  dS = P * (dO V^T - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
+ * O and lse are the forward's outputs for the same inputs.  dO [n_N x k] in
+ * `dtype`; dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ */
+ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                              const void* Q, const void* K, const void* V, float scale,
+                              const float* O, const void* dO, const float* lse,
+                              float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                              ssc_stream stream);
+
+/*
+ * Patch scoring and top-s selection (project page, "Geo-FlashAttention":
+ * pool source keys, score source patches, keep the top R per target patch).
+ * Rows of Q are patch-sorted: target patch p owns rows [offN[p], offN[p+1]);
+ * likewise offM for K.  offN [P_N+1] and offM [P_M+1] are int32 device
+ * arrays with off[0] = 0, off[P] = n and non-decreasing entries.
+ *   Qbar_p = mean of Q rows of patch p,  Kbar_q = mean of K rows of patch q
+ *   (fp64 accumulation; an empty patch has mean 0),
+ *   C[p, q] = <Qbar_p, Kbar_q>  (fp64, unscaled),
+ *   idx[p, 0..s-1] = the s source patches with the largest C[p, :],
+ *   ordered by (score descending, index ascending): ties go to the lower
+ *   index, so the result is unique.
+ * idx [P_N x s] int32.  scores [P_N x P_M] fp64 is optional (may be NULL).
+ * Offsets that break the rules above make every patch empty (no fault).
+ */
+ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN,
+                            const void* Q, int n_M, int P_M, const int* offM, const void* K,
+                            int s, int* idx, double* scores, void* ws, size_t ws_bytes,
+                            ssc_stream stream);
+
+/*
+ * Geo forward: for every target row i of patch p, the softmax of
+ * scale * Q[i].K[j] over j in J_p = union of source patches idx[p, :]
+ * (patch-sorted rows, offsets as above), and
+ *   O[i] = sum_{j in J_p} softmax_j V[j],  lse[i] = log sum_{j in J_p} exp(.).
+ * A row whose support is empty gets O = 0 and lse = -inf.  idx entries must
+ * lie in [0, P_M) and be distinct within a row; if any idx entry or offset
+ * breaks the rules, nothing is computed and O, lse are left untouched.
+ */
+ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN,
+                            int n_M, int P_M, const int* offM, int s, const int* idx,
+                            const void* Q, const void* K, const void* V, float scale,
+                            float* O, float* lse, void* ws, size_t ws_bytes, ssc_stream stream);
+
+/*
+ * Geo backward: gradients of <dO, O_geo> for the FIXED selection idx (the
+ * selection is piecewise constant in the inputs).  Same formulas as the
+ * dense backward restricted to the selected support; source rows outside
+ * every support get dK = dV = 0.  Outputs are fully overwritten.
+ */
+ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN,
+                            int n_M, int P_M, const int* offM, int s, const int* idx,
+                            const void* Q, const void* K, const void* V, float scale,
+                            const float* O, const void* dO, const float* lse,
+                            float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                            ssc_stream stream);
+
+/* Static text for a status code. */
+const char* ssc_status_string(ssc_status status);
+
+/* hipError_t of the last SSC_ERR_HIP on this thread (0 if none). */
+int ssc_last_hip_error(void);
+
+/* Internal tile constants, exposed for tests and FLOP accounting:
+ * which = 0: padded k for a given k (returns 0 if unsupported),
+ * which = 1: row-group granularity of the padded patch layout. */
+int ssc_query(int which, int arg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSC_H */

@@ -1,0 +1,298 @@
+"""Spatial-spectral coupling on AMD Instinct MI355X (gfx950).
+
+The coupling of deep functional-map pipelines, Pi_NM Phi_M =
+softmax(F_N F_M^T / sqrt(d)) Phi_M, is scaled dot-product attention with the
+target descriptors as queries, the source descriptors as keys and the source
+Laplace-Beltrami basis as values ("Spatial-Spectral Coupling as Attention",
+project page, section "How it works").  This package is a thin ctypes
+binding over `libssc.so`, whose hand-written HIP kernels compute both the
+exact dense coupling and the Geo-FlashAttention coupling (section
+"Geo-FlashAttention"), forward and backward.  Every step runs in the library;
+Python only checks arguments, allocates outputs and workspaces with torch and
+passes device pointers plus the current HIP stream.
+
+The five entry points carry the C ABI's names (declared in include/ssc.h):
+coupling_dense_fwd, coupling_dense_bwd, patch_score_topk, coupling_geo_fwd,
+coupling_geo_bwd.  `dense_coupling` and `geo_coupling` wrap them as
+autograd functions.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "CouplingError", "lib", "library_path", "workspace_bytes", "kpad",
+    "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
+    "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
+    "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libssc.so")
+
+OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD = range(5)
+_F32, _BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
+           4: "HIP launch failed"}
+
+
+class CouplingError(RuntimeError):
+    """A non-zero status from libssc.so."""
+
+    def __init__(self, fn: str, status: int, hip: int = 0):
+        msg = f"{fn}: {_STATUS.get(status, 'status %d' % status)}"
+        if status == 4:
+            msg += f" (hipError_t {hip})"
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "ssc_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "ssc_status_string": (ctypes.c_char_p, [_i]),
+    "ssc_last_hip_error": (_i, []),
+    "ssc_query": (_i, [_i, _i]),
+    "coupling_dense_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_dense_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "patch_score_topk": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_geo_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp,
+                              _vp, _vp, _sz, _vp]),
+    "coupling_geo_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssc.so (raises if it has not been built: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with "
+                "`python -m spatial_spectral_coupling_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def kpad(k: int) -> int:
+    """Internal padded width of the basis (0 if k is unsupported)."""
+    return int(lib().ssc_query(0, int(k)))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def workspace_bytes(op: int, dtype: torch.dtype, n_N: int, n_M: int, d: int, k: int,
+                    P_N: int = 0, P_M: int = 0, s: int = 0) -> int:
+    code = _BF16 if dtype == torch.bfloat16 else _F32
+    return int(lib().ssc_workspace_bytes(op, code, n_N, n_M, d, k, P_N, P_M, s))
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous (row-major)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ws(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=dev)
+
+
+def _call(name: str, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CouplingError(name, st, lib().ssc_last_hip_error())
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d) if scale is None else scale)
+
+
+def _same_dtype(*ts):
+    t0 = ts[0]
+    for t in ts[1:]:
+        if t.dtype != t0.dtype:
+            raise TypeError("Q, K, V (and dO) must share one dtype")
+    return _dt(t0)
+
+
+def _i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
+# ---------------------------------------------------------------------------
+# the five entry points
+# ---------------------------------------------------------------------------
+def coupling_dense_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: Optional[float] = None,
+                       O: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = softmax(Q K^T * scale) V (fp32) and lse (natural log), no map stored."""
+    dev = _check_dev(Q, K, V)
+    code = _same_dtype(Q, K, V)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    if K.shape != (n_M, d):
+        raise ValueError("K must be n_M x d")
+    O = torch.empty(n_N, k, dtype=torch.float32, device=dev) if O is None else O
+    lse = torch.empty(n_N, dtype=torch.float32, device=dev) if lse is None else lse
+    _check_dev(O, lse)
+    ws = _ws(lib().ssc_workspace_bytes(OP_DENSE_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_dense_fwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _scale(scale, d),
+          _p(O), _p(lse), _p(ws), ws.numel(), _stream(dev))
+    return O, lse
+
+
+def coupling_dense_bwd(Q, K, V, O, dO, lse, scale: Optional[float] = None):
+    """dQ, dK, dV (fp32) of <dO, O> for the dense coupling."""
+    dev = _check_dev(Q, K, V, O, dO, lse)
+    code = _same_dtype(Q, K, V, dO)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
+    dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_DENSE_BWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_dense_bwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _scale(scale, d),
+          _p(O), _p(dO), _p(lse), _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
+    return dQ, dK, dV
+
+
+def patch_score_topk(Q, offN, K, offM, s: int, return_scores: bool = False):
+    """Top-s source patches per target patch from patch-mean descriptors.
+
+    Q, K are patch-sorted; offN, offM int32 offsets (length P + 1) on the
+    device.  Returns idx [P_N x s] int32 (and scores [P_N x P_M] fp64).
+    """
+    dev = _check_dev(Q, K, offN, offM)
+    code = _same_dtype(Q, K)
+    _i32(offN, "offN")
+    _i32(offM, "offM")
+    n_N, d = Q.shape
+    n_M = K.shape[0]
+    P_N, P_M = offN.numel() - 1, offM.numel() - 1
+    idx = torch.empty(P_N, s, dtype=torch.int32, device=dev)
+    scores = torch.empty(P_N, P_M, dtype=torch.float64, device=dev) if return_scores else None
+    ws = _ws(lib().ssc_workspace_bytes(OP_PATCH_TOPK, code, n_N, n_M, d, 1, P_N, P_M, s), dev)
+    _call("patch_score_topk", code, d, n_N, P_N, _p(offN), _p(Q), n_M, P_M, _p(offM), _p(K), int(s),
+          _p(idx), _p(scores), _p(ws), ws.numel(), _stream(dev))
+    return (idx, scores) if return_scores else idx
+
+
+def coupling_geo_fwd(Q, K, V, offN, offM, idx, scale: Optional[float] = None):
+    """Geo-FlashAttention forward on patch-sorted rows: O (fp32), lse."""
+    dev = _check_dev(Q, K, V, offN, offM, idx)
+    code = _same_dtype(Q, K, V)
+    _i32(offN, "offN")
+    _i32(offM, "offM")
+    _i32(idx, "idx")
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    P_N, P_M = offN.numel() - 1, offM.numel() - 1
+    s = idx.shape[1]
+    O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
+    lse = torch.empty(n_N, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_GEO_FWD, code, n_N, n_M, d, k, P_N, P_M, s), dev)
+    _call("coupling_geo_fwd", code, d, k, n_N, P_N, _p(offN), n_M, P_M, _p(offM), s, _p(idx),
+          _p(Q), _p(K), _p(V), _scale(scale, d), _p(O), _p(lse), _p(ws), ws.numel(), _stream(dev))
+    return O, lse
+
+
+def coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO, lse, scale: Optional[float] = None):
+    """Geo-FlashAttention backward for the fixed selection idx: dQ, dK, dV (fp32)."""
+    dev = _check_dev(Q, K, V, offN, offM, idx, O, dO, lse)
+    code = _same_dtype(Q, K, V, dO)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    P_N, P_M = offN.numel() - 1, offM.numel() - 1
+    s = idx.shape[1]
+    dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
+    dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_GEO_BWD, code, n_N, n_M, d, k, P_N, P_M, s), dev)
+    _call("coupling_geo_bwd", code, d, k, n_N, P_N, _p(offN), n_M, P_M, _p(offM), s, _p(idx),
+          _p(Q), _p(K), _p(V), _scale(scale, d), _p(O), _p(dO), _p(lse), _p(dQ), _p(dK), _p(dV),
+          _p(ws), ws.numel(), _stream(dev))
+    return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
+# autograd wrappers
+# ---------------------------------------------------------------------------
+class _Dense(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, scale):
+        O, lse = coupling_dense_fwd(Q, K, V, scale)
+        ctx.save_for_backward(Q, K, V, O, lse)
+        ctx.scale = scale
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, O, lse = ctx.saved_tensors
+        dQ, dK, dV = coupling_dense_bwd(Q, K, V, O, dO.to(Q.dtype).contiguous(), lse, ctx.scale)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype), None
+
+
+class _Geo(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, offN, offM, idx, scale):
+        O, lse = coupling_geo_fwd(Q, K, V, offN, offM, idx, scale)
+        ctx.save_for_backward(Q, K, V, offN, offM, idx, O, lse)
+        ctx.scale = scale
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, offN, offM, idx, O, lse = ctx.saved_tensors
+        dQ, dK, dV = coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO.to(Q.dtype).contiguous(), lse,
+                                      ctx.scale)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype), None, None, None, None
+
+
+def dense_coupling(Q, K, V, scale: Optional[float] = None):
+    """Differentiable Pi_NM Phi_M (dense, exact)."""
+    return _Dense.apply(Q, K, V, _scale(scale, Q.shape[1]))
+
+
+def geo_coupling(Q, K, V, offN, offM, s: int, scale: Optional[float] = None):
+    """Differentiable Geo-FlashAttention coupling; selection recomputed per call."""
+    idx = patch_score_topk(Q.detach(), offN, K.detach(), offM, s)
+    return _Geo.apply(Q, K, V, offN, offM, idx, _scale(scale, Q.shape[1]))

@@ -1,0 +1,459 @@
+// C ABI of the coupling library: validation, workspace layout and launches.
+// Entry points and their contracts are declared in include/ssc.h.
+#include "ssc.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace ssc;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+const int kKPads[] = {32, 64, 128, 224, 256};
+
+int kpad_for(int k) {
+  for (int kp : kKPads)
+    if (k >= 1 && k <= kp) return kp;
+  return 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Buf& a, const Buf& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output must be disjoint from every input and from the other outputs.
+bool disjoint(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Buf& i : ins)
+      if (overlaps(*o, i)) return false;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlaps(*o, *o2)) return false;
+  }
+  return true;
+}
+
+bool all_ok(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr size_t kNone = ~size_t(0);
+
+struct Layout {
+  size_t Kp = kNone, Kg = kNone, Vp = kNone, Vg = kNone;
+  size_t Qp = kNone, Qg = kNone, dOp = kNone, dOg = kNone, lse2p = kNone, Dp = kNone;
+  size_t poffN = kNone, poffM = kNone, itemsQ = kNone, itemsK = kNone, counters = kNone;
+  size_t inv_off = kNone, inv_idx = kNone, scratch = kNone;
+  size_t Qbar = kNone, KbarT = kNone;
+  size_t total = 0;
+  int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
+};
+
+Layout make_layout(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k, int P_N, int P_M, int s) {
+  Layout L;
+  const size_t es = t == SSC_BF16 ? 2 : 4;
+  const size_t KP = (size_t)kpad_for(k);
+  const bool geo = op == SSC_OP_GEO_FWD || op == SSC_OP_GEO_BWD;
+  L.npadN = (int)round_up((size_t)n_N + (geo ? (size_t)kGroup * P_N : 0), kGroup);
+  L.npadM = (int)round_up((size_t)n_M + (geo ? (size_t)kGroup * P_M : 0), kGroup);
+  const size_t nN = (size_t)L.npadN, nM = (size_t)L.npadM;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  switch (op) {
+    case SSC_OP_DENSE_FWD:
+    case SSC_OP_GEO_FWD:
+      L.Kp = take(nM * d * es);
+      L.Vg = take(nM * KP * es);
+      break;
+    case SSC_OP_DENSE_BWD:
+    case SSC_OP_GEO_BWD:
+      L.Kp = take(nM * d * es);
+      L.Kg = take(nM * d * es);
+      L.Vp = take(nM * KP * es);
+      L.Qp = take(nN * d * es);
+      L.Qg = take(nN * d * es);
+      L.dOp = take(nN * KP * es);
+      L.dOg = take(nN * KP * es);
+      L.lse2p = take(nN * 4);
+      L.Dp = take(nN * 4);
+      break;
+    case SSC_OP_PATCH_TOPK:
+      L.Qbar = take((size_t)P_N * d * 8);
+      L.KbarT = take((size_t)d * P_M * 8);
+      break;
+  }
+  if (geo) {
+    L.poffN = take(((size_t)P_N + 1) * 4);
+    L.poffM = take(((size_t)P_M + 1) * 4);
+    L.itemsQ = take(((size_t)(n_N + kRowsPerWG - 1) / kRowsPerWG + P_N) * sizeof(Item));
+    L.itemsK = take(((size_t)(n_M + kRowsPerWG - 1) / kRowsPerWG + P_M) * sizeof(Item));
+    L.counters = take(8 * 4);
+    L.scratch = take(((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    if (op == SSC_OP_GEO_BWD) {
+      L.inv_off = take(((size_t)P_M + 1) * 4);
+      L.inv_idx = take((size_t)P_N * s * 4);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+ssc_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SSC_OK;
+  g_last_hip = (int)e;
+  return SSC_ERR_HIP;
+}
+
+#define SSC_TRY(expr)                        \
+  do {                                       \
+    const hipError_t e_ = (expr);            \
+    if (e_ != hipSuccess) return hip_status(e_); \
+  } while (0)
+
+DType dt(ssc_dtype t) { return t == SSC_BF16 ? DType::BF16 : DType::F32; }
+
+// Shape checks shared by the coupling entry points.
+ssc_status check_shape(ssc_dtype t, int n_N, int n_M, int d, int k) {
+  if (t != SSC_F32 && t != SSC_BF16) return SSC_ERR_INVALID_ARG;
+  if (n_N < 0 || n_M < 1 || d < 1 || k < 1) return SSC_ERR_INVALID_ARG;
+  const int KP = kpad_for(k);
+  if (KP == 0 || !supported(dt(t), d, KP)) return SSC_ERR_UNSUPPORTED;
+  return SSC_OK;
+}
+
+ssc_status check_patches(int n_N, int P_N, int n_M, int P_M, int s) {
+  if (P_N < 1 || P_M < 1 || s < 1 || s > P_M) return SSC_ERR_INVALID_ARG;
+  if (P_N > 8192 || P_M > 8192) return SSC_ERR_UNSUPPORTED;
+  (void)n_N;
+  (void)n_M;
+  return SSC_OK;
+}
+
+ssc_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (L.total == 0) return SSC_OK;
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  return SSC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, int k, int P_N, int P_M,
+                           int s) {
+  switch (op) {
+    case SSC_OP_DENSE_FWD:
+    case SSC_OP_DENSE_BWD:
+      if (check_shape(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
+      break;
+    case SSC_OP_GEO_FWD:
+    case SSC_OP_GEO_BWD:
+      if (check_shape(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
+      if (check_patches(n_N, P_N, n_M, P_M, s) != SSC_OK) return 0;
+      break;
+    case SSC_OP_PATCH_TOPK:
+      if (d != 64 && d != 128) return 0;
+      if (check_patches(n_N, P_N, n_M, P_M, s) != SSC_OK) return 0;
+      break;
+    default:
+      return 0;
+  }
+  return make_layout(op, dtype, n_N, n_M, d, k, P_N, P_M, s).total;
+}
+
+const char* ssc_status_string(ssc_status status) {
+  switch (status) {
+    case SSC_OK: return "ok";
+    case SSC_ERR_INVALID_ARG: return "invalid argument";
+    case SSC_ERR_UNSUPPORTED: return "unsupported shape";
+    case SSC_ERR_WORKSPACE: return "workspace too small";
+    case SSC_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int ssc_last_hip_error(void) { return g_last_hip; }
+
+int ssc_query(int which, int arg) {
+  if (which == 0) return kpad_for(arg);
+  if (which == 1) return kGroup;
+  return -1;
+}
+
+ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                              const void* V, float scale, float* O, float* lse, void* ws, size_t ws_bytes,
+                              ssc_stream stream) {
+  ssc_status st = check_shape(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, O, lse})) return SSC_ERR_INVALID_ARG;
+  const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const Layout L = make_layout(SSC_OP_DENSE_FWD, dtype, n_N, n_M, d, k, 0, 0, 0);
+  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
+  const Buf bO{O, (size_t)n_N * k * 4}, bl{lse, (size_t)n_N * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bO, bl, bw}, {bQ, bK, bV})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  const int ngroups = L.npadM / kGroup;
+  const void* Kp = K;
+  if (n_M % kGroup != 0) {
+    PackArgs pk{};
+    pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.n = n_M; pk.w = d; pk.W = d;
+    SSC_TRY(launch_pack(dt(dtype), pk, ngroups, s));
+    Kp = pk.Xp;
+  }
+  PackArgs pv{};
+  pv.X = V; pv.Xg = at<char>(ws, L.Vg); pv.n = n_M; pv.w = k; pv.W = KP;
+  SSC_TRY(launch_pack(dt(dtype), pv, ngroups, s));
+
+  FwdArgs a{};
+  a.Q = Q; a.Kp = Kp; a.Vg = pv.Xg; a.O = O; a.lse = lse;
+  a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
+  a.npadM = L.npadM; a.n_M = n_M;
+  SSC_TRY(launch_fwd(dt(dtype), d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG, s));
+  return SSC_OK;
+}
+
+ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                              const void* V, float scale, const float* O, const void* dO, const float* lse,
+                              float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_shape(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (!all_ok({Q, K, V, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
+  const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const Layout L = make_layout(SSC_OP_DENSE_BWD, dtype, n_N, n_M, d, k, 0, 0, 0);
+  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
+  const Buf bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * es}, bl{lse, (size_t)n_N * 4};
+  const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
+  const Buf bw{ws, ws_bytes};
+  if (!disjoint({bdQ, bdK, bdV, bw}, {bQ, bK, bV, bO, bdO, bl})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  const DType T = dt(dtype);
+
+  PackArgs pk{};
+  pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.Xg = at<char>(ws, L.Kg); pk.n = n_M; pk.w = d; pk.W = d;
+  SSC_TRY(launch_pack(T, pk, L.npadM / kGroup, s));
+  PackArgs pv{};
+  pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+  SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, s));
+  PackArgs pq{};
+  pq.X = Q; pq.Xp = at<char>(ws, L.Qp); pq.Xg = at<char>(ws, L.Qg); pq.n = n_N; pq.w = d; pq.W = d;
+  SSC_TRY(launch_pack(T, pq, L.npadN / kGroup, s));
+  PackArgs po{};
+  po.X = dO; po.Xp = at<char>(ws, L.dOp); po.Xg = at<char>(ws, L.dOg); po.n = n_N; po.w = k; po.W = KP;
+  po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
+  SSC_TRY(launch_pack(T, po, L.npadN / kGroup, s));
+
+  const float c2 = scale * kLog2e;
+  if (n_N > 0) {
+    DqArgs q{};
+    q.Qp = pq.Xp; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp;
+    q.Kp = pk.Xp; q.Vp = pv.Xp; q.Kg = pk.Xg; q.dQ = dQ;
+    q.n_N = n_N; q.c2 = c2; q.scale = scale; q.npadM = L.npadM; q.n_M = n_M;
+    SSC_TRY(launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG, s));
+  }
+  DkvArgs b{};
+  b.Kp = pk.Xp; b.Vp = pv.Xp; b.Qp = pq.Xp; b.dOp = po.Xp; b.Qg = pq.Xg; b.dOg = po.Xg;
+  b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
+  b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.npadN = L.npadN; b.n_N = n_N;
+  SSC_TRY(launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG, s));
+  return SSC_OK;
+}
+
+ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN, const void* Q, int n_M,
+                            int P_M, const int* offM, const void* K, int s, int* idx, double* scores, void* ws,
+                            size_t ws_bytes, ssc_stream stream) {
+  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_INVALID_ARG;
+  if (n_N < 0 || n_M < 0) return SSC_ERR_INVALID_ARG;
+  ssc_status st = check_patches(n_N, P_N, n_M, P_M, s);
+  if (st != SSC_OK) return st;
+  if (d != 64 && d != 128) return SSC_ERR_UNSUPPORTED;
+  if (!all_ok({offN, offM, idx})) return SSC_ERR_INVALID_ARG;
+  if ((n_N > 0 && !all_ok({Q})) || (n_M > 0 && !all_ok({K}))) return SSC_ERR_INVALID_ARG;
+  if (scores != nullptr && !aligned16(scores)) return SSC_ERR_INVALID_ARG;
+  const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const Layout L = make_layout(SSC_OP_PATCH_TOPK, dtype, n_N, n_M, d, 1, P_N, P_M, s);
+  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es};
+  const Buf boN{offN, ((size_t)P_N + 1) * 4}, boM{offM, ((size_t)P_M + 1) * 4};
+  const Buf bi{idx, (size_t)P_N * s * 4}, bs{scores, (size_t)P_N * P_M * 8}, bw{ws, ws_bytes};
+  if (!disjoint({bi, bs, bw}, {bQ, bK, boN, boM})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PoolArgs pa{};
+  pa.Q = Q; pa.K = K; pa.offN = offN; pa.offM = offM;
+  pa.n_N = n_N; pa.n_M = n_M; pa.P_N = P_N; pa.P_M = P_M; pa.d = d;
+  pa.Qbar = at<double>(ws, L.Qbar); pa.KbarT = at<double>(ws, L.KbarT);
+  SSC_TRY(launch_pool(dt(dtype), pa, hs));
+  TopkArgs ta{};
+  ta.Qbar = pa.Qbar; ta.KbarT = pa.KbarT; ta.P_N = P_N; ta.P_M = P_M; ta.d = d; ta.s = s;
+  ta.idx = idx; ta.scores = scores;
+  SSC_TRY(launch_topk(ta, hs));
+  return SSC_OK;
+}
+
+namespace {
+
+ssc_status geo_common_checks(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN, int n_M, int P_M,
+                             const int* offM, int s, const int* idx) {
+  ssc_status st = check_shape(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if ((st = check_patches(n_N, P_N, n_M, P_M, s)) != SSC_OK) return st;
+  if (!all_ok({offN, offM, idx})) return SSC_ERR_INVALID_ARG;
+  return SSC_OK;
+}
+
+ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int* offM, const int* idx, int n_N,
+                           int n_M, int P_N, int P_M, int s, bool inverse, hipStream_t hs) {
+  PlanArgs pl{};
+  pl.offN = offN; pl.offM = offM; pl.idx = idx;
+  pl.n_N = n_N; pl.n_M = n_M; pl.P_N = P_N; pl.P_M = P_M; pl.s = s;
+  pl.poffN = at<int>(ws, L.poffN); pl.poffM = at<int>(ws, L.poffM);
+  pl.itemsQ = at<Item>(ws, L.itemsQ); pl.itemsK = at<Item>(ws, L.itemsK);
+  pl.counters = at<int>(ws, L.counters); pl.scratch = at<int>(ws, L.scratch);
+  if (inverse) {
+    pl.inv_off = at<int>(ws, L.inv_off);
+    pl.inv_idx = at<int>(ws, L.inv_idx);
+  }
+  SSC_TRY(launch_plan(pl, hs));
+  return SSC_OK;
+}
+
+}  // namespace
+
+ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN, int n_M, int P_M,
+                            const int* offM, int s, const int* idx, const void* Q, const void* K, const void* V,
+                            float scale, float* O, float* lse, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = geo_common_checks(dtype, d, k, n_N, P_N, offN, n_M, P_M, offM, s, idx);
+  if (st != SSC_OK) return st;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, O, lse})) return SSC_ERR_INVALID_ARG;
+  const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const Layout L = make_layout(SSC_OP_GEO_FWD, dtype, n_N, n_M, d, k, P_N, P_M, s);
+  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
+  const Buf boN{offN, ((size_t)P_N + 1) * 4}, boM{offM, ((size_t)P_M + 1) * 4}, bi{idx, (size_t)P_N * s * 4};
+  const Buf bO{O, (size_t)n_N * k * 4}, bl{lse, (size_t)n_N * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bO, bl, bw}, {bQ, bK, bV, boN, boM, bi})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  const DType T = dt(dtype);
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs)) != SSC_OK) return st;
+  int* counters = at<int>(ws, L.counters);
+
+  PackArgs pk{};
+  pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.n = n_M; pk.w = d; pk.W = d;
+  pk.poff = at<int>(ws, L.poffM); pk.off = offM; pk.P = P_M; pk.n_groups = counters + 3;
+  SSC_TRY(launch_pack(T, pk, L.npadM / kGroup, hs));
+  PackArgs pv = pk;
+  pv.X = V; pv.Xp = nullptr; pv.Xg = at<char>(ws, L.Vg); pv.w = k; pv.W = KP;
+  SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+
+  FwdArgs a{};
+  a.Q = Q; a.Kp = pk.Xp; a.Vg = pv.Xg; a.O = O; a.lse = lse;
+  a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
+  a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN;
+  a.idx = idx; a.s = s; a.poffM = pk.poff; a.offM = offM;
+  SSC_TRY(launch_fwd(T, d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs));
+  return SSC_OK;
+}
+
+ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN, int n_M, int P_M,
+                            const int* offM, int s, const int* idx, const void* Q, const void* K, const void* V,
+                            float scale, const float* O, const void* dO, const float* lse, float* dQ, float* dK,
+                            float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = geo_common_checks(dtype, d, k, n_N, P_N, offN, n_M, P_M, offM, s, idx);
+  if (st != SSC_OK) return st;
+  if (!all_ok({Q, K, V, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
+  const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const Layout L = make_layout(SSC_OP_GEO_BWD, dtype, n_N, n_M, d, k, P_N, P_M, s);
+  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
+  const Buf bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * es}, bl{lse, (size_t)n_N * 4};
+  const Buf boN{offN, ((size_t)P_N + 1) * 4}, boM{offM, ((size_t)P_M + 1) * 4}, bi{idx, (size_t)P_N * s * 4};
+  const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
+  const Buf bw{ws, ws_bytes};
+  if (!disjoint({bdQ, bdK, bdV, bw}, {bQ, bK, bV, bO, bdO, bl, boN, boM, bi})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  const DType T = dt(dtype);
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs)) != SSC_OK) return st;
+  int* counters = at<int>(ws, L.counters);
+  int* poffN = at<int>(ws, L.poffN);
+  int* poffM = at<int>(ws, L.poffM);
+
+  PackArgs pk{};
+  pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.Xg = at<char>(ws, L.Kg); pk.n = n_M; pk.w = d; pk.W = d;
+  pk.poff = poffM; pk.off = offM; pk.P = P_M; pk.n_groups = counters + 3;
+  SSC_TRY(launch_pack(T, pk, L.npadM / kGroup, hs));
+  PackArgs pv = pk;
+  pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.Xg = nullptr; pv.w = k; pv.W = KP;
+  SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+  PackArgs pq{};
+  pq.X = Q; pq.Xp = at<char>(ws, L.Qp); pq.Xg = at<char>(ws, L.Qg); pq.n = n_N; pq.w = d; pq.W = d;
+  pq.poff = poffN; pq.off = offN; pq.P = P_N; pq.n_groups = counters + 2;
+  SSC_TRY(launch_pack(T, pq, L.npadN / kGroup, hs));
+  PackArgs po = pq;
+  po.X = dO; po.Xp = at<char>(ws, L.dOp); po.Xg = at<char>(ws, L.dOg); po.w = k; po.W = KP;
+  po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
+  SSC_TRY(launch_pack(T, po, L.npadN / kGroup, hs));
+
+  const float c2 = scale * kLog2e;
+  if (n_N > 0) {
+    DqArgs q{};
+    q.Qp = pq.Xp; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp;
+    q.Kp = pk.Xp; q.Vp = pv.Xp; q.Kg = pk.Xg; q.dQ = dQ;
+    q.n_N = n_N; q.c2 = c2; q.scale = scale;
+    q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.poffN = poffN;
+    q.idx = idx; q.s = s; q.poffM = poffM; q.offM = offM;
+    SSC_TRY(launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs));
+  }
+  DkvArgs b{};
+  b.Kp = pk.Xp; b.Vp = pv.Xp; b.Qp = pq.Xp; b.dOp = po.Xp; b.Qg = pq.Xg; b.dOg = po.Xg;
+  b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
+  b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale;
+  b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.poffM = poffM;
+  b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.poffN = poffN; b.offN = offN;
+  SSC_TRY(launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG + P_M, hs));
+  return SSC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Host-visible argument blocks and launchers of the coupling kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ssc {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// Work item of the row-block kernels: (patch, first row within the patch).
+struct Item {
+  int patch, row0;
+};
+
+// Forward: O = softmax(Q K^T scale) V over each row's key stream.
+struct FwdArgs {
+  const void* Q;        // caller's Q [n_N x D], patch-sorted rows
+  const void* Kp;       // source rows, padded layout [npadM x D]
+  const void* Vg;       // source V, grouped-transposed [npadM/16][KP][16]
+  float* O;             // [n_N x k]
+  float* lse;           // [n_N]
+  int n_N, k;
+  float c2;             // scale * log2(e)
+  const Item* items;    // nullptr: dense (item = blockIdx.x)
+  const int* n_items;
+  const int* offN;      // geo: target offsets [P_N + 1]
+  const int* idx;       // geo: [P_N x s]
+  int s;
+  const int* poffM;     // geo: padded source offsets
+  const int* offM;      // geo: source offsets
+  int npadM, n_M;       // dense key stream
+};
+
+// dQ pass.
+struct DqArgs {
+  const void* Qp;       // target rows, padded layout [npadN x D]
+  const void* dOp;      // [npadN x KP]
+  const float* lse2p;   // [npadN] lse * log2(e); +inf on padding
+  const float* Dp;      // [npadN] rowdot(dO, O); 0 on padding
+  const void* Kp;       // [npadM x D]
+  const void* Vp;       // [npadM x KP]
+  const void* Kg;       // [npadM/16][D][16]
+  float* dQ;            // [n_N x D]
+  int n_N;
+  float c2, scale;
+  const Item* items;
+  const int* n_items;
+  const int* offN;
+  const int* poffN;
+  const int* idx;
+  int s;
+  const int* poffM;
+  const int* offM;
+  int npadM, n_M;
+};
+
+// dK / dV pass.
+struct DkvArgs {
+  const void* Kp;       // [npadM x D]
+  const void* Vp;       // [npadM x KP]
+  const void* Qp;       // [npadN x D]
+  const void* dOp;      // [npadN x KP]
+  const void* Qg;       // [npadN/16][D][16]
+  const void* dOg;      // [npadN/16][KP][16]
+  const float* lse2p;
+  const float* Dp;
+  float* dK;            // [n_M x D]
+  float* dV;            // [n_M x k]
+  int n_M, k;
+  float c2, scale;
+  const Item* items;    // (source patch, first key row); nullptr: dense
+  const int* n_items;
+  const int* offM;
+  const int* poffM;
+  const int* inv_off;   // geo: [P_M + 1] CSR of target patches selecting q
+  const int* inv_idx;
+  const int* poffN;
+  const int* offN;
+  int npadN, n_N;       // dense query stream
+};
+
+// Packing of one tensor into the padded patch layout.
+struct PackArgs {
+  const void* X;        // [n x w] rows in patch-sorted order
+  void* Xp;             // [npad x W] or nullptr
+  void* Xg;             // [npad/16][W][16] or nullptr
+  int n, w, W;
+  const int* poff;      // nullptr: dense (position = row)
+  const int* off;
+  int P;
+  const int* n_groups;  // geo: total groups (written by the planner)
+  // rowdot / lse extras (target side only; may be nullptr)
+  const float* O;       // [n x w]
+  const float* lse;     // [n]
+  float* Dp;            // [npad]
+  float* lse2p;         // [npad]
+};
+
+// Planner of the geo layout: padded offsets, work items, inverse lists.
+struct PlanArgs {
+  const int* offN;
+  const int* offM;
+  const int* idx;
+  int n_N, n_M, P_N, P_M, s;
+  int* poffN;           // [P_N + 1]
+  int* poffM;           // [P_M + 1]
+  Item* itemsQ;         // row blocks of target patches
+  Item* itemsK;         // row blocks of source patches
+  int* counters;        // [0] n itemsQ, [1] n itemsK, [2] groups N, [3] groups M, [4] status
+  int* inv_off;         // [P_M + 1] or nullptr
+  int* inv_idx;         // [P_N * s]
+  int* scratch;         // [P_M] counters for the inverse fill
+};
+
+struct PoolArgs {
+  const void* Q;
+  const void* K;
+  const int* offN;
+  const int* offM;
+  int n_N, n_M, P_N, P_M, d;
+  double* Qbar;         // [P_N x d]
+  double* KbarT;        // [d x P_M]
+};
+
+struct TopkArgs {
+  const double* Qbar;
+  const double* KbarT;
+  int P_N, P_M, d, s;
+  int* idx;
+  double* scores;       // optional
+};
+
+// Launchers (return hipGetLastError() after the launch).
+hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);
+hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
+bool supported(DType t, int D, int KP);
+hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st);
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+}  // namespace ssc

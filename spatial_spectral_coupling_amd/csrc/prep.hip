@@ -1,0 +1,306 @@
+// Preparation kernels of the coupling:
+//   pack_kernel  -- rows of one tensor into the padded patch layout (row-major
+//                   copy and grouped-transposed copy), plus D = rowdot(dO, O)
+//                   and lse * log2(e) on the target side of the backward;
+//   plan_kernel  -- validates patch offsets and the selection, builds padded
+//                   offsets, work items and the inverse selection lists;
+//   pool_kernel  -- patch-mean descriptors in fp64 ("pool source keys");
+//   topk_kernel  -- patch scores <Qbar_p, Kbar_q> in fp64 and the top-s source
+//                   patches per target patch, ties to the lower index
+//                   ("score source patches", "keep the top R per target
+//                   patch": project page, section "Geo-FlashAttention").
+//
+// Padded patch layout: patch p occupies padded positions
+// [poff[p], poff[p+1]) with poff[p+1] - poff[p] = roundup(|p|, 16); its rows
+// sit at the front in their patch-sorted order and the tail is zero.  The
+// grouped-transposed copy stores every group of 16 positions as a [W][16]
+// block, so a tile of 64 gathered positions is four contiguous blocks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+
+namespace ssc {
+
+// ---------------------------------------------------------------------------
+// pack
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int WMAX = 256;
+  __shared__ __attribute__((aligned(16))) T tile[kGroup * (WMAX + E)];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int pos0 = g * kGroup;
+  int row0, nrows;
+  if (a.poff == nullptr) {
+    row0 = pos0;
+    nrows = min(max(a.n - pos0, 0), kGroup);
+  } else {
+    if (g >= *a.n_groups) return;
+    // patch p: the last one with poff[p] <= pos0 (binary search, uniform)
+    int lo = 0, hi = a.P - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.poff[mid] <= pos0) lo = mid;
+      else hi = mid - 1;
+    }
+    const int local = pos0 - a.poff[lo];
+    row0 = a.off[lo] + local;
+    nrows = min(max(a.off[lo + 1] - a.off[lo] - local, 0), kGroup);
+  }
+  const int W = a.W, w = a.w, pitch = W + E;
+  const T* X = reinterpret_cast<const T*>(a.X);
+  for (int e = tid; e < kGroup * W; e += 256) {
+    const int r = e / W, c = e - r * W;
+    T v = T(0.f);
+    if (r < nrows && c < w) v = X[(size_t)(row0 + r) * w + c];
+    tile[r * pitch + c] = v;
+  }
+  __syncthreads();
+  if (a.Xp != nullptr) {
+    T* Xp = reinterpret_cast<T*>(a.Xp);
+    const int cpr = W / E;
+    for (int e = tid; e < kGroup * cpr; e += 256) {
+      const int r = e / cpr, cc = e - r * cpr;
+      st_chunk(Xp + (size_t)(pos0 + r) * W + cc * E, *reinterpret_cast<const Chunk*>(tile + r * pitch + cc * E));
+    }
+  }
+  if (a.Xg != nullptr) {
+    T* blk = reinterpret_cast<T*>(a.Xg) + (size_t)g * W * kGroup;
+    constexpr int CPG = kGroup / E;
+    for (int e = tid; e < W * CPG; e += 256) {
+      const int c = e / CPG, part = e - c * CPG;
+      T v[E];
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] = tile[(part * E + j) * pitch + c];
+      st_chunk(blk + c * kGroup + part * E, *reinterpret_cast<const Chunk*>(v));
+    }
+  }
+  if (a.Dp != nullptr) {
+    // 16 lanes per row: partial dot products, then a butterfly over the 16.
+    const int r = tid >> 4, j = tid & 15;
+    float part = 0.f;
+    if (r < nrows) {
+      const float* O = a.O + (size_t)(row0 + r) * w;
+      for (int c = j; c < w; c += 16) part += to_f32(tile[r * pitch + c]) * O[c];
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 16);
+    if (j == 0) {
+      a.Dp[pos0 + r] = r < nrows ? part : 0.f;
+      float l2 = INFINITY;
+      if (r < nrows) {
+        const float l = a.lse[row0 + r];
+        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      }
+      a.lse2p[pos0 + r] = l2;
+    }
+  }
+}
+
+hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (t == DType::BF16) hipLaunchKernelGGL(pack_kernel<bf16>, dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(pack_kernel<float>, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// plan (one workgroup of 1024 threads)
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+// Exclusive scan of f(i), i < n, written to out[0..n] (out[n] = total).
+// Chunked over the block with a running carry; returns the total.
+template <typename F>
+__device__ int block_scan_excl(int n, F f, int* out, int* lds /* kPlanThreads + 1 */) {
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < n; base += kPlanThreads) {
+    const int i = base + tid;
+    const int v = i < n ? f(i) : 0;
+    lds[tid] = v;
+    __syncthreads();
+    for (int s = 1; s < kPlanThreads; s <<= 1) {
+      const int add = tid >= s ? lds[tid - s] : 0;
+      __syncthreads();
+      lds[tid] += add;
+      __syncthreads();
+    }
+    if (i < n) out[i] = carry + lds[tid] - v;
+    const int chunk_total = lds[kPlanThreads - 1];
+    __syncthreads();
+    carry += chunk_total;
+  }
+  if (tid == 0) out[n] = carry;
+  __syncthreads();
+  return carry;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int lds[kPlanThreads + 1];
+  const int tid = threadIdx.x;
+  // ---- validation
+  int bad = 0;
+  if (tid == 0) {
+    bad |= a.offN[0] != 0 || a.offN[a.P_N] != a.n_N;
+    bad |= a.offM[0] != 0 || a.offM[a.P_M] != a.n_M;
+  }
+  for (int p = tid; p < a.P_N; p += kPlanThreads) bad |= a.offN[p] > a.offN[p + 1];
+  for (int q = tid; q < a.P_M; q += kPlanThreads) bad |= a.offM[q] > a.offM[q + 1];
+  if (a.idx != nullptr) {
+    const int n = a.P_N * a.s;
+    for (int e = tid; e < n; e += kPlanThreads) {
+      const int q = a.idx[e];
+      bad |= q < 0 || q >= a.P_M;
+      const int p = e / a.s, r = e - p * a.s;
+      for (int r2 = 0; r2 < r; ++r2) bad |= a.idx[p * a.s + r2] == q;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (bad) {
+    if (tid == 0) {
+      a.counters[0] = a.counters[1] = a.counters[2] = a.counters[3] = 0;
+      a.counters[4] = 1;
+    }
+    return;
+  }
+  // ---- padded offsets
+  const int* offN = a.offN;
+  const int* offM = a.offM;
+  const int gN = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + kGroup - 1) & ~(kGroup - 1); },
+                                 a.poffN, lds);
+  const int gM = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + kGroup - 1) & ~(kGroup - 1); },
+                                 a.poffM, lds);
+  // ---- work items (row blocks of kRowsPerWG within a patch)
+  int* tmp = a.scratch;  // [max(P_N, P_M) + 1]
+  const int nQ = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + kRowsPerWG - 1) / kRowsPerWG; },
+                                 tmp, lds);
+  for (int p = tid; p < a.P_N; p += kPlanThreads) {
+    const int b = tmp[p], nt = tmp[p + 1] - b;
+    for (int t = 0; t < nt; ++t) a.itemsQ[b + t] = Item{p, t * kRowsPerWG};
+  }
+  __syncthreads();
+  const int nK = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + kRowsPerWG - 1) / kRowsPerWG; },
+                                 tmp, lds);
+  for (int q = tid; q < a.P_M; q += kPlanThreads) {
+    const int b = tmp[q], nt = tmp[q + 1] - b;
+    for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * kRowsPerWG};
+  }
+  __syncthreads();
+  // ---- inverse selection lists: inv[q] = target patches p with q in idx[p]
+  if (a.inv_off != nullptr && a.idx != nullptr) {
+    for (int q = tid; q < a.P_M; q += kPlanThreads) tmp[q] = 0;
+    __syncthreads();
+    const int n = a.P_N * a.s;
+    for (int e = tid; e < n; e += kPlanThreads) atomicAdd(&tmp[a.idx[e]], 1);
+    __syncthreads();
+    block_scan_excl(a.P_M, [=](int q) { return tmp[q]; }, a.inv_off, lds);
+    for (int q = tid; q < a.P_M; q += kPlanThreads) tmp[q] = 0;
+    __syncthreads();
+    for (int e = tid; e < n; e += kPlanThreads) {
+      const int q = a.idx[e];
+      const int slot = atomicAdd(&tmp[q], 1);
+      a.inv_idx[a.inv_off[q] + slot] = e / a.s;
+    }
+    __syncthreads();
+    // each list ascending (insertion sort; lists hold distinct patches)
+    for (int q = tid; q < a.P_M; q += kPlanThreads) {
+      const int b = a.inv_off[q], e = a.inv_off[q + 1];
+      for (int i = b + 1; i < e; ++i) {
+        const int v = a.inv_idx[i];
+        int j = i - 1;
+        while (j >= b && a.inv_idx[j] > v) {
+          a.inv_idx[j + 1] = a.inv_idx[j];
+          --j;
+        }
+        a.inv_idx[j + 1] = v;
+      }
+    }
+  }
+  if (tid == 0) {
+    a.counters[0] = nQ;
+    a.counters[1] = nK;
+    a.counters[2] = gN / kGroup;
+    a.counters[3] = gM / kGroup;
+    a.counters[4] = 0;
+  }
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// patch pooling (fp64 sums in row order, then the mean)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  const int b = blockIdx.x;
+  const bool tgt = b < a.P_N;
+  const int p = tgt ? b : b - a.P_N;
+  const int* off = tgt ? a.offN : a.offM;
+  const int n = tgt ? a.n_N : a.n_M;
+  const T* X = reinterpret_cast<const T*>(tgt ? a.Q : a.K);
+  const int begin = min(max(off[p], 0), n);
+  const int end = min(max(off[p + 1], begin), n);
+  const int cnt = end - begin;
+  for (int c = threadIdx.x; c < a.d; c += 256) {
+    double s = 0.0;
+    for (int r = begin; r < end; ++r) s += (double)to_f32(X[(size_t)r * a.d + c]);
+    const double mean = cnt > 0 ? s / (double)cnt : 0.0;
+    if (tgt) a.Qbar[(size_t)p * a.d + c] = mean;
+    else a.KbarT[(size_t)c * a.P_M + p] = mean;
+  }
+}
+
+hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st) {
+  const int grid = a.P_N + a.P_M;
+  if (t == DType::BF16) hipLaunchKernelGGL(pool_kernel<bf16>, dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(pool_kernel<float>, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scores and top-s (one workgroup per target patch, the score row in LDS)
+// ---------------------------------------------------------------------------
+constexpr int kMaxPatches = 8192;
+constexpr int kMaxD = 128;
+
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ double qb[kMaxD];
+  __shared__ double C[kMaxPatches];
+  const int p = blockIdx.x, tid = threadIdx.x;
+  for (int c = tid; c < a.d; c += 256) qb[c] = a.Qbar[(size_t)p * a.d + c];
+  __syncthreads();
+  for (int q = tid; q < a.P_M; q += 256) {
+    double acc = 0.0;
+    for (int c = 0; c < a.d; ++c) acc = fma(qb[c], a.KbarT[(size_t)c * a.P_M + q], acc);
+    C[q] = acc;
+    if (a.scores != nullptr) a.scores[(size_t)p * a.P_M + q] = acc;
+  }
+  __syncthreads();
+  // rank of q in the strict order (score desc, index asc)
+  for (int q = tid; q < a.P_M; q += 256) {
+    const double v = C[q];
+    int rank = 0;
+    for (int q2 = 0; q2 < a.P_M; ++q2) {
+      const double v2 = C[q2];
+      rank += (v2 > v) || (v2 == v && q2 < q);
+    }
+    if (rank < a.s) a.idx[(size_t)p * a.s + rank] = q;
+  }
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3(a.P_N), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ssc

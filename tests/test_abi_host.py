@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/ssc.h declares, and
+reject bad arguments with the documented status before any HIP call.  Every
+call below fails validation, so nothing reaches the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import spatial_spectral_coupling_amd as ssc
+from spatial_spectral_coupling_amd import build as ssc_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssc.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ssc.library_path):
+        ssc_build.build()
+    return ssc.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk", "coupling_geo_fwd",
+              "coupling_geo_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_queries(L):
+    for code, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (UNSUPPORTED, b"unsupported shape"),
+                       (WORKSPACE, b"workspace too small"), (HIPERR, b"HIP launch failed")):
+        assert L.ssc_status_string(code) == text
+    assert [L.ssc_query(0, k) for k in (1, 30, 32, 33, 100, 200, 224, 225, 256, 257, 0)] == \
+        [32, 32, 32, 64, 128, 224, 224, 256, 256, 0, 0]
+    assert L.ssc_query(1, 0) == 16
+    assert L.ssc_last_hip_error() == 0
+
+
+def test_workspace_sizes(L):
+    w = L.ssc_workspace_bytes
+    assert w(ssc.OP_DENSE_FWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) >= 60000 * 224 * 2
+    assert w(ssc.OP_DENSE_BWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) > w(ssc.OP_DENSE_FWD, BF16, 60000, 60000,
+                                                                          128, 200, 0, 0, 0)
+    assert w(ssc.OP_GEO_BWD, BF16, 60000, 60000, 128, 200, 256, 256, 16) > 0
+    assert w(ssc.OP_PATCH_TOPK, BF16, 60000, 60000, 128, 0, 256, 256, 16) >= 2 * 256 * 128 * 8
+    assert w(ssc.OP_DENSE_FWD, BF16, 10, 10, 96, 200, 0, 0, 0) == 0      # d unsupported
+    assert w(ssc.OP_DENSE_FWD, BF16, 10, 10, 128, 300, 0, 0, 0) == 0     # k unsupported
+    assert w(ssc.OP_GEO_FWD, BF16, 10, 10, 128, 200, 4, 4, 5) == 0       # s > P_M
+    assert w(ssc.OP_DENSE_FWD, F32, 10, 10, 128, 256, 0, 0, 0) == 0      # fp32 compiled up to k = 128
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+# distinct, 16-byte aligned fake device addresses far apart (never dereferenced)
+A = [P(0x100000 * (i + 1)) for i in range(12)]
+
+
+def dense_fwd(L, dtype=BF16, nN=64, nM=64, d=128, k=200, Q=None, K=None, V=None, O=None, lse=None,
+              ws=None, wsb=1 << 30):
+    pick = lambda x, default: default if x is None else x
+    return L.coupling_dense_fwd(dtype, nN, nM, d, k, pick(Q, A[0]), pick(K, A[1]), pick(V, A[2]), 0.1,
+                                pick(O, A[3]), pick(lse, A[4]), ws, wsb, None)
+
+
+def test_dense_fwd_validation(L):
+    assert dense_fwd(L, d=96) == UNSUPPORTED
+    assert dense_fwd(L, k=257) == UNSUPPORTED
+    assert dense_fwd(L, nM=0) == INVALID
+    assert dense_fwd(L, nN=-1) == INVALID
+    assert dense_fwd(L, dtype=7) == INVALID
+    assert dense_fwd(L, nN=0) == OK                         # nothing to do, nothing launched
+    assert dense_fwd(L, Q=P(0)) == INVALID                  # null pointer
+    assert dense_fwd(L, K=P(0x100008)) == INVALID           # misaligned
+    assert dense_fwd(L, ws=None) == WORKSPACE               # no workspace
+    assert dense_fwd(L, ws=A[5], wsb=16) == WORKSPACE       # too small
+    assert dense_fwd(L, O=A[0], ws=A[5]) == INVALID         # output aliases an input
+    assert dense_fwd(L, lse=A[3], ws=A[5]) == INVALID       # two outputs overlap
+
+
+def test_dense_bwd_validation(L):
+    f = L.coupling_dense_bwd
+    args = lambda **kw: [kw.get("dt", BF16), kw.get("nN", 64), kw.get("nM", 64), kw.get("d", 128), kw.get("k", 200),
+                         A[0], A[1], A[2], 0.1, A[3], A[4], A[5], kw.get("dQ", A[6]), A[7], A[8],
+                         kw.get("ws", None), kw.get("wsb", 0), None]
+    assert f(*args(d=100)) == UNSUPPORTED
+    assert f(*args(nM=0)) == INVALID
+    assert f(*args()) == WORKSPACE
+    assert f(*args(dQ=A[0], ws=A[9], wsb=1 << 40)) == INVALID   # dQ aliases Q
+
+
+def test_patch_topk_validation(L):
+    f = L.patch_score_topk
+    base = dict(dt=BF16, d=128, nN=100, PN=4, nM=100, PM=4, s=2, ws=A[9], wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["dt"], a["d"], a["nN"], a["PN"], A[0], A[1], a["nM"], a["PM"], A[2], A[3], a["s"], A[4],
+                 None, a["ws"], a["wsb"], None)
+
+    assert call(s=5) == INVALID
+    assert call(s=0) == INVALID
+    assert call(PN=0) == INVALID
+    assert call(PM=9000, s=2) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+
+
+def test_geo_validation(L):
+    f = L.coupling_geo_fwd
+
+    def call(s=2, PM=4, d=128, ws=None, wsb=0):
+        return f(BF16, d, 200, 100, 4, A[0], 100, PM, A[1], s, A[2], A[3], A[4], A[5], 0.1, A[6], A[7], ws, wsb,
+                 None)
+
+    assert call(s=0) == INVALID
+    assert call(s=5) == INVALID
+    assert call(d=32) == UNSUPPORTED
+    assert call() == WORKSPACE
+    g = L.coupling_geo_bwd
+    assert g(BF16, 128, 200, 100, 4, A[0], 100, 4, A[1], 2, A[2], A[3], A[4], A[5], 0.1, A[6], A[7], A[8],
+             A[9], A[10], A[11], None, 0, None) == WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ssc, "_lib", None)
+    monkeypatch.setattr(ssc, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ssc.lib()
