@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the spatial-spectral coupling on one MI355X.
+
+One step = the whole hot path on the 60k-vertex workload (n_N = n_M = 60000,
+d = 128, k = 200, bf16 inputs, fp32 accumulation): the exact dense coupling
+forward + backward, then the Geo-FlashAttention pipeline on the same tensors
+(P = 256 geodesic-FPS patches per shape, top-s = 16): patch scoring / top-s,
+forward, backward.  Inputs are synthetic stand-ins (random-Fourier-feature
+descriptors on perturbed sphere meshes, QR-orthonormal basis) and are
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is ms per step (lower is better); per-coupling
+ms, effective TFLOP/s against the bf16 MFMA peak and peak GiB are included,
+plus the 160k geo coupling (P = 640) as an informational sub-record, the
+roofline record of the dominant kernel (measured with HIP events on its own
+stream inside the library) and the fp64 oracle timed on the host cores on a
+bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms per coupling fwd+bwd + TFLOP/s (% MFMA peak) + peak GiB at 60k/160k verts"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(pairs: float, d: int, k: int) -> float:
+    """fwd + bwd work of the coupling per (target, source) pair visited:
+    fwd 2(d + k), bwd 2(3d + 2k) (one recompute of the scores)."""
+    return 2.0 * pairs * (4 * d + 3 * k)
+
+
+def dkv_flops(pairs: float, d: int, k: int) -> float:
+    """Algorithmic work of the dK/dV kernel: scores, dP, dV and dK."""
+    return 2.0 * pairs * (2 * d + 2 * k)
+
+
+def executed_pairs(offN, offM, idx) -> int:
+    import numpy as np
+    nT = np.diff(offN).astype(np.int64)
+    nS = np.diff(offM).astype(np.int64)
+    return int(np.sum(nT * nS[idx].sum(axis=1)))
+
+
+def to_dev(a, dtype, torch, np):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def prepare(c, torch, np, gen):
+    dt = c["dtype"]
+    dense = {x: to_dev(c[x], dt, torch, np) for x in ("Q", "K", "V", "dO")}
+    permN, offN = gen.patch_sort(c["labN"], c["P"])
+    permM, offM = gen.patch_sort(c["labM"], c["P"])
+    geo = dict(Q=to_dev(c["Q"][permN], dt, torch, np), K=to_dev(c["K"][permM], dt, torch, np),
+               V=to_dev(c["V"][permM], dt, torch, np), dO=to_dev(c["dO"][permN], dt, torch, np),
+               offN=torch.from_numpy(offN).cuda(), offM=torch.from_numpy(offM).cuda())
+    return dense, geo, offN, offM
+
+
+def time_steps(fns, steps, warmup, torch):
+    """Run the phases `fns` (list of callables) per step; returns per-phase ms
+    (averaged) and total wall ms per step (events on the current stream)."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for j, f in enumerate(fns):
+            f()
+            ev[s][j + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    phase = [sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) / steps for j in range(len(fns))]
+    total = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
+    return phase, total, wall
+
+
+def cpu_baseline(c, offN, offM, idx_np, np):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to ms
+    per step: dense fwd+bwd for 2048 target rows (x n_N / 2048), patch scoring
+    and top-s in full, geo fwd+bwd for 48 target patches (x P / 48)."""
+    from oracle import dense_bwd, dense_fwd, geo_bwd, geo_fwd, patch_means, patch_scores, topk, upcast
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    dt, sc, n, P, s = c["dtype"], c["scale"], c["n"], c["P"], c["s"]
+    Q, K, V, dO = (upcast(c[x], dt) for x in ("Q", "K", "V", "dO"))
+    rows = np.arange(2048)
+    t0 = time.perf_counter()
+    dense_fwd(Q[rows], K, V, sc)
+    dense_bwd(Q, K, V, dO, sc, rows=rows)
+    t_dense = (time.perf_counter() - t0) * n / len(rows)
+    t0 = time.perf_counter()
+    C = patch_scores(patch_means(Q, c["labN"], P), patch_means(K, c["labM"], P))
+    topk(C, s)
+    t_topk = time.perf_counter() - t0
+    pats = np.arange(48)
+    labN_s = np.where(np.isin(c["labN"], pats), c["labN"], -1)
+    t0 = time.perf_counter()
+    geo_fwd(Q, K, V, labN_s, c["labM"], idx_np, sc)
+    geo_bwd(Q, K, V, dO, labN_s, c["labM"], idx_np, sc)
+    t_geo = (time.perf_counter() - t0) * P / len(pats)
+    total_ms = (t_dense + t_topk + t_geo) * 1e3
+    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: dense fwd+bwd on 2048 of {n} target rows (x{n / 2048:.1f}), "
+                       f"patch scores + top-s in full, geo fwd+bwd on 48 of {P} target patches "
+                       f"(x{P / 48:.1f}); ms per step extrapolated"),
+            "dense_ms": round(t_dense * 1e3, 1), "geo_ms": round((t_topk + t_geo) * 1e3, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-160k", action="store_true", help="skip the informational 160k geo record")
+    ap.add_argument("--dense-only", action="store_true", help="time only the dense coupling (profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the coupling runs on a single "
+                                   "MI355X (multi-GPU sharding is a design note, not implemented)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import spatial_spectral_coupling_amd as ssc
+
+    if not os.path.exists(ssc.library_path):
+        from spatial_spectral_coupling_amd import build as b
+        b.build()
+    torch.cuda.set_device(0)
+    log("generating the 60k workload")
+    c = gen.make_config(3)
+    n, d, k, sc, s = c["n"], c["d"], c["k"], c["scale"], c["s"]
+    dense, geo, offN, offM = prepare(c, torch, np, gen)
+    torch.cuda.synchronize()
+    out = {}
+
+    def dense_fb():
+        O, lse = ssc.coupling_dense_fwd(dense["Q"], dense["K"], dense["V"], sc)
+        ssc.coupling_dense_bwd(dense["Q"], dense["K"], dense["V"], O, dense["dO"], lse, sc)
+
+    st = {}
+
+    def geo_topk():
+        st["idx"] = ssc.patch_score_topk(geo["Q"], geo["offN"], geo["K"], geo["offM"], s)
+
+    def geo_fb():
+        O, lse = ssc.coupling_geo_fwd(geo["Q"], geo["K"], geo["V"], geo["offN"], geo["offM"], st["idx"], sc)
+        ssc.coupling_geo_bwd(geo["Q"], geo["K"], geo["V"], geo["offN"], geo["offM"], st["idx"], O, geo["dO"],
+                             lse, sc)
+
+    fns = [dense_fb] if args.dense_only else [dense_fb, geo_topk, geo_fb]
+    log("timing", args.steps, "steps after", args.warmup, "warmup")
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_mem = torch.cuda.memory_allocated()
+    with ssc.KernelTimer("dkv", capacity=args.steps + 4) as kt:
+        phase, total_ms, wall_ms = time_steps(fns, args.steps, 0, torch)
+        dkv_ms, dkv_n = kt.read()
+    peak_gib = torch.cuda.max_memory_allocated() / 2 ** 30
+    dkv_avg = dkv_ms / max(dkv_n, 1)
+    pairs_dense = float(n) * n
+    f_dense = algorithmic_flops(pairs_dense, d, k)
+    dense_ms = phase[0]
+    rec = {"dense": {"ms": round(dense_ms, 4), "tflops": round(f_dense / dense_ms / 1e9, 1),
+                     "pct_peak": round(100 * f_dense / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                     "algorithmic_flop": f_dense}}
+    if not args.dense_only:
+        idx_np = st["idx"].cpu().numpy()
+        pairs_geo = executed_pairs(offN, offM, idx_np)
+        f_geo = algorithmic_flops(pairs_geo, d, k)
+        geo_ms = phase[1] + phase[2]
+        rec["geo"] = {"ms": round(geo_ms, 4), "topk_ms": round(phase[1], 4), "fwd_bwd_ms": round(phase[2], 4),
+                      "tflops": round(f_geo / geo_ms / 1e9, 1),
+                      "pct_peak": round(100 * f_geo / geo_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                      "executed_pairs": pairs_geo, "algorithmic_flop": f_geo,
+                      "P": c["P"], "s": s}
+    achieved = dkv_flops(pairs_dense, d, k) / dkv_avg / 1e9
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": f"ssc::dkv_kernel<bf16,{d},{ssc.kpad(k)}> (dense dK/dV pass)",
+            "launch_ms": round(dkv_avg, 4), "launches": dkv_n,
+            "flop_per_launch": dkv_flops(pairs_dense, d, k)}
+
+    if not args.no_160k and not args.dense_only:
+        log("generating the 160k workload")
+        c4 = gen.make_config(4)
+        _, geo4, offN4, offM4 = prepare(c4, torch, np, gen)
+        del _
+        st4 = {}
+
+        def g4_topk():
+            st4["idx"] = ssc.patch_score_topk(geo4["Q"], geo4["offN"], geo4["K"], geo4["offM"], c4["s"])
+
+        def g4_fb():
+            O, lse = ssc.coupling_geo_fwd(geo4["Q"], geo4["K"], geo4["V"], geo4["offN"], geo4["offM"], st4["idx"],
+                                          c4["scale"])
+            ssc.coupling_geo_bwd(geo4["Q"], geo4["K"], geo4["V"], geo4["offN"], geo4["offM"], st4["idx"], O,
+                                 geo4["dO"], lse, c4["scale"])
+
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        ph4, _, _ = time_steps([g4_topk, g4_fb], args.steps, args.warmup, torch)
+        pk4 = torch.cuda.max_memory_allocated() / 2 ** 30
+        p4 = executed_pairs(offN4, offM4, st4["idx"].cpu().numpy())
+        f4 = algorithmic_flops(p4, c4["d"], c4["k"])
+        g4 = ph4[0] + ph4[1]
+        rec["geo_160k"] = {"ms": round(g4, 4), "topk_ms": round(ph4[0], 4), "fwd_bwd_ms": round(ph4[1], 4),
+                           "tflops": round(f4 / g4 / 1e9, 1),
+                           "pct_peak": round(100 * f4 / g4 / 1e9 / PEAK_BF16_TFLOPS, 2),
+                           "executed_pairs": p4, "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
+        del geo4
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.dense_only:
+        log("timing the oracle on a sample")
+        cpu = cpu_baseline(c, offN, offM, st["idx"].cpu().numpy(), np)
+
+    line = {
+        "metric": METRIC, "value": round(total_ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms, 4), "wall_ms_per_step": round(wall_ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (RFF descriptors on perturbed sphere meshes, QR basis, geodesic FPS patches)",
+        "config": {"workload": ("spatial-spectral coupling fwd+bwd, dense then geo (P=256, s=16), "
+                                f"n_N=n_M={n}, d={d}, k={k}, bf16 in / fp32 accumulate"),
+                   "n": n, "d": d, "k": k, "P": c["P"], "s": s},
+        "peak_gib": round(peak_gib, 3), "peak_gib_above_inputs": round(peak_gib - base_mem / 2 ** 30, 3),
+        **rec,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,9 +31,10 @@
  *   are always fp32.  lse is in natural log.
  * - Supported shapes: d in {64, 128}; 1 <= k <= 256 (padded internally to
  *   the next of 32, 64, 128, 224, 256); n_M >= 1; n_N >= 0 (n_N = 0 is a
- *   no-op).  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= min(P_M, 64).
+ *   no-op).  fp32 inputs: k <= 128.  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= P_M.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
- *   stream) and re-entrant: no global mutable state, no host sync.
+ *   stream) and re-entrant: no global mutable state (the optional kernel
+ *   timer below is per thread), no host sync.
  *   Argument validation happens before any HIP call; on failure nothing is
  *   launched and an error status is returned.  SSC_ERR_HIP means a launch
  *   failed; ssc_last_hip_error() returns that hipError_t (thread-local).
@@ -113,7 +114,8 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
  *   ordered by (score descending, index ascending): ties go to the lower
  *   index, so the result is unique.
  * idx [P_N x s] int32.  scores [P_N x P_M] fp64 is optional (may be NULL).
- * Offsets that break the rules above make every patch empty (no fault).
+ * Offsets that break the rules above give unspecified scores, but every read
+ * stays inside rows [0, n) (they are clamped), so they cannot fault.
  */
 ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN,
                             const void* Q, int n_M, int P_M, const int* offM, const void* K,
@@ -152,6 +154,20 @@ const char* ssc_status_string(ssc_status status);
 
 /* hipError_t of the last SSC_ERR_HIP on this thread (0 if none). */
 int ssc_last_hip_error(void);
+
+/*
+ * Kernel timer (measurement aid).  ssc_timer_arm(family, capacity) makes the
+ * calling thread bracket each subsequent launch of one kernel family with a
+ * pair of HIP events recorded on that launch's stream; `capacity` event pairs
+ * are created up front (family NULL or capacity <= 0 disarms and frees them).
+ * Families: "fwd", "dq", "dkv" (dense) and "geo_fwd", "geo_dq", "geo_dkv".
+ * ssc_timer_read() waits for the recorded events and returns the summed
+ * milliseconds and the number of timed launches (negated if more launches
+ * happened than pairs were available), then starts a new count.
+ * Both return an ssc_status.
+ */
+int ssc_timer_arm(const char* family, int capacity);
+int ssc_timer_read(float* total_ms, int* count);
 
 /* Internal tile constants, exposed for tests and FLOP accounting:
  * which = 0: padded k for a given k (returns 0 if unsupported),

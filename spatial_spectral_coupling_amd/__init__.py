@@ -27,7 +27,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "CouplingError", "lib", "library_path", "workspace_bytes", "kpad",
+    "CouplingError", "KernelTimer", "lib", "library_path", "workspace_bytes", "kpad",
     "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
     "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
@@ -60,6 +60,8 @@ _SIGS = {
     "ssc_status_string": (ctypes.c_char_p, [_i]),
     "ssc_last_hip_error": (_i, []),
     "ssc_query": (_i, [_i, _i]),
+    "ssc_timer_arm": (_i, [ctypes.c_char_p, _i]),
+    "ssc_timer_read": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
     "coupling_dense_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
     "coupling_dense_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _sz, _vp]),
@@ -91,6 +93,36 @@ def lib() -> ctypes.CDLL:
 def kpad(k: int) -> int:
     """Internal padded width of the basis (0 if k is unsupported)."""
     return int(lib().ssc_query(0, int(k)))
+
+
+class KernelTimer:
+    """HIP-event timing of one kernel family inside the library, recorded on
+    the stream each launch uses: `with KernelTimer("dkv", 64) as t: ...;
+    t.read()` returns (summed ms, number of launches)."""
+
+    def __init__(self, family: str, capacity: int = 256):
+        self.family, self.capacity = family, capacity
+        self.total_ms, self.count = 0.0, 0
+
+    def __enter__(self):
+        st = lib().ssc_timer_arm(self.family.encode(), int(self.capacity))
+        if st != 0:
+            raise CouplingError("ssc_timer_arm", st, lib().ssc_last_hip_error())
+        return self
+
+    def read(self):
+        ms, n = ctypes.c_float(0), ctypes.c_int(0)
+        st = lib().ssc_timer_read(ctypes.byref(ms), ctypes.byref(n))
+        if st != 0:
+            raise CouplingError("ssc_timer_read", st, lib().ssc_last_hip_error())
+        if n.value < 0:
+            raise RuntimeError("kernel timer overflow: raise the capacity")
+        self.total_ms, self.count = float(ms.value), int(n.value)
+        return self.total_ms, self.count
+
+    def __exit__(self, *exc):
+        lib().ssc_timer_arm(None, 0)
+        return False
 
 
 def _dt(t: torch.Tensor) -> int:

@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <string>
+#include <vector>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -140,6 +142,35 @@ ssc_status hip_status(hipError_t e) {
 
 DType dt(ssc_dtype t) { return t == SSC_BF16 ? DType::BF16 : DType::F32; }
 
+// Kernel timer: when armed for a kernel family, every launch of that family
+// on this thread is bracketed by a pair of HIP events recorded on the
+// launch's own stream.  Pairs are created when the timer is armed, so timed
+// loops create nothing.
+struct KernelTimer {
+  std::string family;
+  std::vector<hipEvent_t> ev;  // start/stop interleaved
+  size_t used = 0;             // pairs consumed
+  bool overflow = false;
+};
+thread_local KernelTimer g_timer;
+
+template <typename F>
+hipError_t timed(const char* family, hipStream_t s, F&& launch) {
+  KernelTimer& t = g_timer;
+  if (t.family.empty() || t.family != family) return launch();
+  if (2 * (t.used + 1) > t.ev.size()) {
+    t.overflow = true;
+    return launch();
+  }
+  hipEvent_t a = t.ev[2 * t.used], b = t.ev[2 * t.used + 1];
+  ++t.used;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(b, s);
+}
+
 // Shape checks shared by the coupling entry points.
 ssc_status check_shape(ssc_dtype t, int n_N, int n_M, int d, int k) {
   if (t != SSC_F32 && t != SSC_BF16) return SSC_ERR_INVALID_ARG;
@@ -203,6 +234,47 @@ const char* ssc_status_string(ssc_status status) {
 
 int ssc_last_hip_error(void) { return g_last_hip; }
 
+int ssc_timer_arm(const char* family, int capacity) {
+  KernelTimer& t = g_timer;
+  for (hipEvent_t e : t.ev)
+    if (e != nullptr) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.used = 0;
+  t.overflow = false;
+  t.family = family != nullptr ? family : "";
+  if (t.family.empty() || capacity <= 0) {
+    t.family.clear();
+    return SSC_OK;
+  }
+  t.ev.resize(2 * (size_t)capacity, nullptr);
+  for (hipEvent_t& e : t.ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      t.family.clear();
+      return hip_status(r);
+    }
+  }
+  return SSC_OK;
+}
+
+int ssc_timer_read(float* total_ms, int* count) {
+  KernelTimer& t = g_timer;
+  if (total_ms == nullptr || count == nullptr) return SSC_ERR_INVALID_ARG;
+  float sum = 0.f;
+  for (size_t i = 0; i < t.used; ++i) {
+    hipError_t r = hipEventSynchronize(t.ev[2 * i + 1]);
+    float ms = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+    if (r != hipSuccess) return hip_status(r);
+    sum += ms;
+  }
+  *total_ms = sum;
+  *count = t.overflow ? -(int)t.used : (int)t.used;
+  t.used = 0;
+  t.overflow = false;
+  return SSC_OK;
+}
+
 int ssc_query(int which, int arg) {
   if (which == 0) return kpad_for(arg);
   if (which == 1) return kGroup;
@@ -241,7 +313,7 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   a.Q = Q; a.Kp = Kp; a.Vg = pv.Xg; a.O = O; a.lse = lse;
   a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
   a.npadM = L.npadM; a.n_M = n_M;
-  SSC_TRY(launch_fwd(dt(dtype), d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG, s));
+  SSC_TRY(timed("fwd", s, [&] { return launch_fwd(dt(dtype), d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG, s); }));
   return SSC_OK;
 }
 
@@ -285,13 +357,13 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
     q.Qp = pq.Xp; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp;
     q.Kp = pk.Xp; q.Vp = pv.Xp; q.Kg = pk.Xg; q.dQ = dQ;
     q.n_N = n_N; q.c2 = c2; q.scale = scale; q.npadM = L.npadM; q.n_M = n_M;
-    SSC_TRY(launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG, s));
+    SSC_TRY(timed("dq", s, [&] { return launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG, s); }));
   }
   DkvArgs b{};
   b.Kp = pk.Xp; b.Vp = pv.Xp; b.Qp = pq.Xp; b.dOp = po.Xp; b.Qg = pq.Xg; b.dOg = po.Xg;
   b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
   b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.npadN = L.npadN; b.n_N = n_N;
-  SSC_TRY(launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG, s));
+  SSC_TRY(timed("dkv", s, [&] { return launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG, s); }));
   return SSC_OK;
 }
 
@@ -390,7 +462,7 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
   a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN;
   a.idx = idx; a.s = s; a.poffM = pk.poff; a.offM = offM;
-  SSC_TRY(launch_fwd(T, d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs));
+  SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd(T, d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs); }));
   return SSC_OK;
 }
 
@@ -444,7 +516,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     q.n_N = n_N; q.c2 = c2; q.scale = scale;
     q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.poffN = poffN;
     q.idx = idx; q.s = s; q.poffM = poffM; q.offM = offM;
-    SSC_TRY(launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs));
+    SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq(T, d, KP, q, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs); }));
   }
   DkvArgs b{};
   b.Kp = pk.Xp; b.Vp = pv.Xp; b.Qp = pq.Xp; b.dOp = po.Xp; b.Qg = pq.Xg; b.dOg = po.Xg;
@@ -452,7 +524,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale;
   b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.poffM = poffM;
   b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.poffN = poffN; b.offN = offN;
-  SSC_TRY(launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG + P_M, hs));
+  SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG + P_M, hs); }));
   return SSC_OK;
 }
 
