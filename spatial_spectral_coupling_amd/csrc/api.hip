@@ -66,11 +66,64 @@ struct Layout {
   size_t poffN = kNone, poffM = kNone, itemsQ = kNone, itemsK = kNone, counters = kNone;
   size_t inv_off = kNone, inv_idx = kNone, scratch = kNone;
   size_t Qbar = kNone, KbarT = kNone;
+  size_t run_pf = kNone, inv_pf = kNone;
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
 };
 
+// bf16: only k-padded row copies of V and dO (plus rowdot / lse by row with a
+// sentinel entry at index n), the geo plan, run prefix sums and inverse lists.
+Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int P_M, int s) {
+  Layout L;
+  const size_t KP = (size_t)kpad_for(k);
+  const bool geo = op == SSC_OP_GEO_FWD || op == SSC_OP_GEO_BWD;
+  L.npadN = (int)round_up((size_t)n_N + 1, kGroup);
+  L.npadM = (int)round_up((size_t)n_M + 1, kGroup);
+  const size_t nN = (size_t)L.npadN, nM = (size_t)L.npadM;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  switch (op) {
+    case SSC_OP_DENSE_FWD:
+    case SSC_OP_GEO_FWD:
+      L.Vp = take(nM * KP * 2);
+      break;
+    case SSC_OP_DENSE_BWD:
+    case SSC_OP_GEO_BWD:
+      L.Vp = take(nM * KP * 2);
+      L.dOp = take(nN * KP * 2);
+      L.lse2p = take(nN * 4);
+      L.Dp = take(nN * 4);
+      break;
+    case SSC_OP_PATCH_TOPK:
+      L.Qbar = take((size_t)P_N * d * 8);
+      L.KbarT = take((size_t)d * P_M * 8);
+      break;
+  }
+  if (geo) {
+    const int rQ = kWavesQ * 32, rK = kWavesK * 32;
+    L.poffN = take(((size_t)P_N + 1) * 4);
+    L.poffM = take(((size_t)P_M + 1) * 4);
+    L.itemsQ = take(((size_t)(n_N + rQ - 1) / rQ + P_N) * sizeof(Item));
+    L.itemsK = take(((size_t)(n_M + rK - 1) / rK + P_M) * sizeof(Item));
+    L.counters = take(8 * 4);
+    L.scratch = take(((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.run_pf = take((size_t)P_N * (s + 1) * 4);
+    if (op == SSC_OP_GEO_BWD) {
+      L.inv_off = take(((size_t)P_M + 1) * 4);
+      L.inv_idx = take((size_t)P_N * s * 4);
+      L.inv_pf = take(((size_t)P_N * s + P_M) * 4);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
 Layout make_layout(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k, int P_N, int P_M, int s) {
+  if (t == SSC_BF16) return make_layout_bf16(op, n_N, n_M, d, k, P_N, P_M, s);
   Layout L;
   const size_t es = t == SSC_BF16 ? 2 : 4;
   const size_t KP = (size_t)kpad_for(k);
@@ -297,6 +350,17 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
+  if (dtype == SSC_BF16) {
+    PackArgs pv{};
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    SSC_TRY(launch_pack(DType::BF16, pv, L.npadM / kGroup, s));
+    FwdArgs a{};
+    a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
+    a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M;
+    const int rQ = kWavesQ * 32;
+    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ, s); }));
+    return SSC_OK;
+  }
   const int ngroups = L.npadM / kGroup;
   const void* Kp = K;
   if (n_M % kGroup != 0) {
@@ -336,6 +400,29 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
+  if (dtype == SSC_BF16) {
+    PackArgs pv{};
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, s));
+    PackArgs po{};
+    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KP;
+    po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
+    SSC_TRY(launch_pack(T, po, L.npadN / kGroup, s));
+    const float c2 = scale * kLog2e;
+    if (n_N > 0) {
+      DqArgs q{};
+      q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
+      q.n_N = n_N; q.c2 = c2; q.scale = scale; q.n_M = n_M;
+      const int rQ = kWavesQ * 32;
+      SSC_TRY(timed("dq", s, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ, s); }));
+    }
+    DkvArgs b{};
+    b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
+    b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
+    const int rK = kWavesK * 32;
+    SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK, s); }));
+    return SSC_OK;
+  }
 
   PackArgs pk{};
   pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.Xg = at<char>(ws, L.Kg); pk.n = n_M; pk.w = d; pk.W = d;
@@ -411,10 +498,16 @@ ssc_status geo_common_checks(ssc_dtype dtype, int d, int k, int n_N, int P_N, co
 }
 
 ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int* offM, const int* idx, int n_N,
-                           int n_M, int P_N, int P_M, int s, bool inverse, hipStream_t hs) {
+                           int n_M, int P_N, int P_M, int s, bool inverse, hipStream_t hs, bool bf16_path) {
   PlanArgs pl{};
   pl.offN = offN; pl.offM = offM; pl.idx = idx;
   pl.n_N = n_N; pl.n_M = n_M; pl.P_N = P_N; pl.P_M = P_M; pl.s = s;
+  pl.rowsQ = bf16_path ? kWavesQ * 32 : kRowsPerWG;
+  pl.rowsK = bf16_path ? kWavesK * 32 : kRowsPerWG;
+  if (bf16_path) {
+    pl.run_pf = at<int>(ws, L.run_pf);
+    if (inverse) pl.inv_pf = at<int>(ws, L.inv_pf);
+  }
   pl.poffN = at<int>(ws, L.poffN); pl.poffM = at<int>(ws, L.poffM);
   pl.itemsQ = at<Item>(ws, L.itemsQ); pl.itemsK = at<Item>(ws, L.itemsK);
   pl.counters = at<int>(ws, L.counters); pl.scratch = at<int>(ws, L.scratch);
@@ -446,8 +539,22 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
-  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs)) != SSC_OK) return st;
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs, dtype == SSC_BF16)) != SSC_OK)
+    return st;
   int* counters = at<int>(ws, L.counters);
+  if (dtype == SSC_BF16) {
+    PackArgs pv{};
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+    FwdArgs a{};
+    a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
+    a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
+    a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN;
+    a.idx = idx; a.s = s; a.offM = offM; a.run_pf = at<int>(ws, L.run_pf);
+    const int rQ = kWavesQ * 32;
+    SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
+    return SSC_OK;
+  }
 
   PackArgs pk{};
   pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.n = n_M; pk.w = d; pk.W = d;
@@ -487,8 +594,36 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
-  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs)) != SSC_OK) return st;
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs, dtype == SSC_BF16)) != SSC_OK)
+    return st;
   int* counters = at<int>(ws, L.counters);
+  if (dtype == SSC_BF16) {
+    PackArgs pv{};
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+    PackArgs po{};
+    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KP;
+    po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
+    SSC_TRY(launch_pack(T, po, L.npadN / kGroup, hs));
+    const float c2 = scale * kLog2e;
+    if (n_N > 0) {
+      DqArgs q{};
+      q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
+      q.n_N = n_N; q.c2 = c2; q.scale = scale;
+      q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN;
+      q.idx = idx; q.s = s; q.offM = offM; q.run_pf = at<int>(ws, L.run_pf);
+      const int rQ = kWavesQ * 32;
+      SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
+    }
+    DkvArgs b{};
+    b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
+    b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
+    b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
+    b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_pf = at<int>(ws, L.inv_pf);
+    const int rK = kWavesK * 32;
+    SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK + P_M, hs); }));
+    return SSC_OK;
+  }
   int* poffN = at<int>(ws, L.poffN);
   int* poffM = at<int>(ws, L.poffM);
 

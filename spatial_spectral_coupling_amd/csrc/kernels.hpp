@@ -7,6 +7,11 @@ namespace ssc {
 
 enum class DType { F32 = 0, BF16 = 1 };
 
+// Waves per workgroup of the bf16 kernels: query-side kernels (forward, dQ)
+// own kWavesQ * 32 rows, the dK/dV kernel owns kWavesK * 32 source rows.
+constexpr int kWavesQ = 8;
+constexpr int kWavesK = 4;
+
 // Work item of the row-block kernels: (patch, first row within the patch).
 struct Item {
   int patch, row0;
@@ -29,6 +34,10 @@ struct FwdArgs {
   const int* poffM;     // geo: padded source offsets
   const int* offM;      // geo: source offsets
   int npadM, n_M;       // dense key stream
+  // bf16 kernels: Kp is the caller's K (row-major), Vp the k-padded copy of V,
+  // run_pf [P_N][s + 1] the prefix sums of selected source-patch sizes.
+  const void* Vp;
+  const int* run_pf;
 };
 
 // dQ pass.
@@ -52,6 +61,7 @@ struct DqArgs {
   const int* poffM;
   const int* offM;
   int npadM, n_M;
+  const int* run_pf;    // bf16 kernels (Qp, Kp = caller rows; lse2p, Dp by row)
 };
 
 // dK / dV pass.
@@ -77,6 +87,9 @@ struct DkvArgs {
   const int* poffN;
   const int* offN;
   int npadN, n_N;       // dense query stream
+  // bf16 kernels: prefix sums of target-patch sizes along each inverse list,
+  // list q at inv_pf[inv_off[q] + q], length inv_off[q+1] - inv_off[q] + 1.
+  const int* inv_pf;
 };
 
 // Packing of one tensor into the padded patch layout.
@@ -109,7 +122,10 @@ struct PlanArgs {
   int* counters;        // [0] n itemsQ, [1] n itemsK, [2] groups N, [3] groups M, [4] status
   int* inv_off;         // [P_M + 1] or nullptr
   int* inv_idx;         // [P_N * s]
-  int* scratch;         // [P_M] counters for the inverse fill
+  int* scratch;         // [max(P_N, P_M) + 1] counters for scans and fills
+  int rowsQ, rowsK;     // rows per work item (target, source side)
+  int* run_pf;          // [P_N * (s + 1)] or nullptr
+  int* inv_pf;          // [P_N * s + P_M] or nullptr
 };
 
 struct PoolArgs {
@@ -132,6 +148,9 @@ struct TopkArgs {
 
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st);
+hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 bool supported(DType t, int D, int KP);

@@ -177,22 +177,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                                  a.poffN, lds);
   const int gM = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + kGroup - 1) & ~(kGroup - 1); },
                                  a.poffM, lds);
-  // ---- work items (row blocks of kRowsPerWG within a patch)
+  // ---- work items (row blocks of rowsQ / rowsK rows within a patch)
   int* tmp = a.scratch;  // [max(P_N, P_M) + 1]
-  const int nQ = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + kRowsPerWG - 1) / kRowsPerWG; },
-                                 tmp, lds);
+  const int rQ = a.rowsQ, rK = a.rowsK;
+  const int nQ = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + rQ - 1) / rQ; }, tmp, lds);
   for (int p = tid; p < a.P_N; p += kPlanThreads) {
     const int b = tmp[p], nt = tmp[p + 1] - b;
-    for (int t = 0; t < nt; ++t) a.itemsQ[b + t] = Item{p, t * kRowsPerWG};
+    for (int t = 0; t < nt; ++t) a.itemsQ[b + t] = Item{p, t * rQ};
   }
   __syncthreads();
-  const int nK = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + kRowsPerWG - 1) / kRowsPerWG; },
-                                 tmp, lds);
+  const int nK = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + rK - 1) / rK; }, tmp, lds);
   for (int q = tid; q < a.P_M; q += kPlanThreads) {
     const int b = tmp[q], nt = tmp[q + 1] - b;
-    for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * kRowsPerWG};
+    for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * rK};
   }
   __syncthreads();
+  // ---- per target patch: prefix sums of the selected source-patch sizes
+  if (a.run_pf != nullptr && a.idx != nullptr) {
+    for (int p = tid; p < a.P_N; p += kPlanThreads) {
+      int acc = 0;
+      int* pf = a.run_pf + (size_t)p * (a.s + 1);
+      for (int r = 0; r < a.s; ++r) {
+        pf[r] = acc;
+        const int q = a.idx[(size_t)p * a.s + r];
+        acc += offM[q + 1] - offM[q];
+      }
+      pf[a.s] = acc;
+    }
+    __syncthreads();
+  }
   // ---- inverse selection lists: inv[q] = target patches p with q in idx[p]
   if (a.inv_off != nullptr && a.idx != nullptr) {
     for (int q = tid; q < a.P_M; q += kPlanThreads) tmp[q] = 0;
@@ -220,6 +233,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           --j;
         }
         a.inv_idx[j + 1] = v;
+      }
+    }
+    if (a.inv_pf != nullptr) {
+      __syncthreads();
+      for (int q = tid; q < a.P_M; q += kPlanThreads) {
+        const int b = a.inv_off[q], e = a.inv_off[q + 1];
+        int* pf = a.inv_pf + b + q;
+        int acc = 0;
+        for (int i = b; i < e; ++i) {
+          pf[i - b] = acc;
+          const int p = a.inv_idx[i];
+          acc += offN[p + 1] - offN[p];
+        }
+        pf[e - b] = acc;
       }
     }
   }
