@@ -104,7 +104,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
       break;
   }
   if (geo) {
-    const int rQ = kWavesQ * 32, rK = kWavesK * 32;
+    const int rQ = kRowsFwd < kRowsDq ? kRowsFwd : kRowsDq, rK = kRowsDkv;
     L.poffN = take(((size_t)P_N + 1) * 4);
     L.poffM = take(((size_t)P_M + 1) * 4);
     L.itemsQ = take(((size_t)(n_N + rQ - 1) / rQ + P_N) * sizeof(Item));
@@ -357,7 +357,7 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M;
-    const int rQ = kWavesQ * 32;
+    const int rQ = kRowsFwd;
     SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ, s); }));
     return SSC_OK;
   }
@@ -413,13 +413,13 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
       DqArgs q{};
       q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
       q.n_N = n_N; q.c2 = c2; q.scale = scale; q.n_M = n_M;
-      const int rQ = kWavesQ * 32;
+      const int rQ = kRowsDq;
       SSC_TRY(timed("dq", s, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ, s); }));
     }
     DkvArgs b{};
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
-    const int rK = kWavesK * 32;
+    const int rK = kRowsDkv;
     SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK, s); }));
     return SSC_OK;
   }
@@ -502,8 +502,10 @@ ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int
   PlanArgs pl{};
   pl.offN = offN; pl.offM = offM; pl.idx = idx;
   pl.n_N = n_N; pl.n_M = n_M; pl.P_N = P_N; pl.P_M = P_M; pl.s = s;
-  pl.rowsQ = bf16_path ? kWavesQ * 32 : kRowsPerWG;
-  pl.rowsK = bf16_path ? kWavesK * 32 : kRowsPerWG;
+  // target rows per item: the forward call plans for the forward kernel, the
+  // backward call for the dQ kernel
+  pl.rowsQ = bf16_path ? (inverse ? kRowsDq : kRowsFwd) : kRowsPerWG;
+  pl.rowsK = bf16_path ? kRowsDkv : kRowsPerWG;
   if (bf16_path) {
     pl.run_pf = at<int>(ws, L.run_pf);
     if (inverse) pl.inv_pf = at<int>(ws, L.inv_pf);
@@ -549,9 +551,9 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
-    a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN;
+    a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
     a.idx = idx; a.s = s; a.offM = offM; a.run_pf = at<int>(ws, L.run_pf);
-    const int rQ = kWavesQ * 32;
+    const int rQ = kRowsFwd;
     SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
     return SSC_OK;
   }
@@ -610,9 +612,9 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
       DqArgs q{};
       q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
       q.n_N = n_N; q.c2 = c2; q.scale = scale;
-      q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN;
+      q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.n_M = n_M;
       q.idx = idx; q.s = s; q.offM = offM; q.run_pf = at<int>(ws, L.run_pf);
-      const int rQ = kWavesQ * 32;
+      const int rQ = kRowsDq;
       SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
     }
     DkvArgs b{};
@@ -620,7 +622,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
     b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
     b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_pf = at<int>(ws, L.inv_pf);
-    const int rK = kWavesK * 32;
+    const int rK = kRowsDkv;
     SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK + P_M, hs); }));
     return SSC_OK;
   }

@@ -15,9 +15,9 @@
 //  * rows are gathered one by one from the caller's arrays, so the geo
 //    support (concatenated source patches) needs no padding: a tile may span
 //    several patches and only the stream's last tile is partial;
-//  * LDS rows are XOR-swizzled at 16-byte granularity (slot = chunk ^ f(row))
-//    so that row-fragment reads (32 rows, one chunk) and transposed reads
-//    (4 rows x 32 bytes per 16 lanes) spread over the banks.
+//  * LDS rows carry two pad chunks (32 bytes) so that row-fragment reads
+//    (32 rows, one chunk) and transposed reads (4 rows x 32 bytes per 16
+//    lanes) spread over the banks with purely affine addresses.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,78 +29,147 @@ namespace tb {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// Geometry of a row tile of W bf16 columns: CW data chunks of 16 bytes per
-// row, padded to P slots (a power of two).
+// Geometry of a row tile of W bf16 columns: CW chunks of 16 bytes per row,
+// stored with a pitch of CW + 2 chunks.  The two pad chunks shift
+// consecutive rows by 32 bytes (mod the bank window), so the 16 lanes of a
+// transposed read (4 rows x 32 bytes) and the row-fragment reads of
+// consecutive rows spread over the banks, while every LDS address stays a
+// per-lane base plus a compile-time offset.
 template <int W>
 struct Geo {
   static constexpr int CW = W / 8;
-  static constexpr int P = CW <= 4 ? 4 : (CW <= 8 ? 8 : (CW <= 16 ? 16 : 32));
-  static constexpr int MASK = (P < 16 ? P : 16) - 1;
-  static constexpr int BYTES = kTile * P * 16;
+  static constexpr int PITCH = (CW + 2) * 16;   // bytes per row
+  static constexpr int BYTES = kTile * PITCH;
+  static constexpr int SLOTS = kTile * (CW + 2);  // 16-byte slots, a multiple of 64
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 2) & 1); }
-
+// Row-fragment reads for MFMA operands: rows rb*32 + l32, chunk 2*cc + h.
 template <int W>
-__device__ __forceinline__ int slot(int r, int c) {
-  return c ^ (swz(r) & Geo<W>::MASK);
+struct RowReader {
+  int lane_off;
+  __device__ __forceinline__ void init(int l32, int h) { lane_off = l32 * Geo<W>::PITCH + h * 16; }
+  __device__ __forceinline__ bf16x8 read(const char* tile, int rb, int cc) const {
+    return *reinterpret_cast<const bf16x8*>(tile + lane_off + rb * 32 * Geo<W>::PITCH + cc * 32);
+  }
+};
+
+// Transposed-operand reads with ds_read_b64_tr_b16: rows kc*16 + tr_r and
+// kc*16 + 8 + tr_r, columns cb*32 + tr_c .. +3 (tr_r = 4h + (i>>2),
+// tr_c = 16(G&1) + 4(i&3) for lane i of 16-lane group G), giving the 8
+// k-elements rows kc*16 + {4h..4h+3, 8+4h..8+4h+3} of column cb*32 + l32.
+template <int W>
+struct TrReader {
+  int lane_off;
+  __device__ __forceinline__ void init(int tr_r, int tr_c) { lane_off = tr_r * Geo<W>::PITCH + tr_c * 2; }
+  __device__ __forceinline__ bf16x8 frag(const char* tile, int cb, int kc) const {
+    const char* base = tile + lane_off + cb * 64 + kc * 16 * Geo<W>::PITCH;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * Geo<W>::PITCH));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// Eight probabilities (C-layout elements i0..i0+7) as a bf16 operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& c, int i0) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)c[i0 + j];
+  return r;
 }
 
-// 8 consecutive columns [8c, 8c+8) of tile row r.
-template <int W>
-__device__ __forceinline__ bf16x8 rd_row(const char* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + (r * Geo<W>::P + slot<W>(r, c)) * 16);
+// Buffer resource of a global array (base, byte size): raw buffer loads
+// take a 32-bit byte offset from it and return zero outside the range.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;  // raw 32-bit data format (gfx9)
+  return r;
 }
 
-// Transposed read: this lane addresses 4 columns starting at C (C % 4 == 0)
-// of row r.
-template <int W>
-__device__ __forceinline__ bf16x4 rd_tr(const char* tile, int r, int C) {
-  const char* p = tile + (r * Geo<W>::P + slot<W>(r, C >> 3)) * 16 + ((C >> 2) & 1) * 8;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
-}
+// Direct buffer load of `size` bytes per lane into LDS at lds + 4 * lane
+// (size 4) or lds + 16 * lane (size 16).
+extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds,
+                                                   int size, int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-// Operand of an MFMA whose contraction runs over tile rows: rows
-// kc*16 + {4h..4h+3, 8+4h..8+4h+3}, column block cb (32 columns); tr_r and
-// tr_c are this lane's row / column offsets (4h + (i>>2), 16(G&1) + 4(i&3)).
-template <int W>
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int cb, int kc, int tr_r, int tr_c) {
-  const bf16x4 lo = rd_tr<W>(tile, kc * 16 + tr_r, cb * 32 + tr_c);
-  const bf16x4 hi = rd_tr<W>(tile, kc * 16 + 8 + tr_r, cb * 32 + tr_c);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Issue the direct loads of one row tile (64 rows) into LDS.  `rows` holds
-// the 64 global row indices (negative = no row: any valid row is loaded and
-// masked later).  X has row stride ldx elements and at least CW chunks per
-// row; slots beyond CW receive a duplicate of chunk 0 (never read).
+// Issue the direct loads of one row tile (64 rows) into LDS: slot s of the
+// tile (16 bytes at s * 16) is row s / (CW + 2), chunk s % (CW + 2); pad
+// slots receive a copy of chunk 0 (never read).  Tile row r is global row
+// rows[r] (negative = no row: row 0 is loaded and masked later) or, when
+// rows == nullptr, row0 + r (rows at or past nrows read row 0).  The loop is
+// unrolled; each load needs one 32-bit offset.
 template <int W, int NW>
-__device__ __forceinline__ void load_tile(char* tile, const bf16* __restrict__ X, int ldx, const int* rows,
-                                          int wave, int lane) {
-  constexpr int P = Geo<W>::P, CW = Geo<W>::CW, NI = kTile * P / 64;
-  for (int inst = wave; inst < NI; inst += NW) {
-    const int s = inst * 64 + lane;
-    const int r = s / P, p = s % P;
-    int c = p ^ (swz(r) & Geo<W>::MASK);
-    if (c >= CW) c = 0;
-    int row = rows[r];
-    row = row < 0 ? 0 : row;
-    const bf16* src = X + (size_t)row * ldx + c * 8;
-    __builtin_amdgcn_global_load_lds((void*)src, (lds_void_t*)(tile + inst * 1024), 16, 0, 0);
+__device__ __forceinline__ void load_tile(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
+                                          int nrows, int wave, int lane) {
+  constexpr int CP = Geo<W>::CW + 2, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
+  // Recompute the per-lane slot arithmetic at every call instead of keeping
+  // loop-invariant offsets live across the whole tile loop.
+  asm volatile("" : "+v"(lane));
+  int off[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int inst = wave + j * NW;
+    const int s = (inst < NI ? inst : 0) * 64 + lane;
+    const int r = s / CP;
+    const int c = s - r * CP;
+    int row;
+    if (rows != nullptr) {
+      row = rows[r];
+      row = row < 0 ? 0 : row;
+    } else {
+      row = row0 + r;
+      row = row < nrows ? row : 0;
+    }
+    off[j] = row * (ldx * 2) + (c < Geo<W>::CW ? c : 0) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int inst = wave + j * NW;
+    if (NJ * NW == NI || inst < NI)
+      ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, off[j], 0, 0, 0);
   }
 }
 
 // 64 fp32 values gathered by row index (negative -> index `sentinel`).
-__device__ __forceinline__ void load_vec64(float* dst, const float* __restrict__ src, const int* rows, int sentinel,
-                                           int lane) {
-  int row = rows[lane];
-  row = row < 0 ? sentinel : row;
-  __builtin_amdgcn_global_load_lds((void*)(src + row), (lds_void_t*)dst, 4, 0, 0);
+__device__ __forceinline__ void load_vec64(float* dst, const i32x4& rsrc, const int* rows, int row0, int nrows,
+                                           int sentinel, int lane) {
+  int row;
+  if (rows != nullptr) {
+    row = rows[lane];
+    row = row < 0 ? sentinel : row;
+  } else {
+    row = row0 + lane;
+    row = row < nrows ? row : sentinel;
+  }
+  ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, row * 4, 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Depth of the operand-read pipelines (reads issued this many MFMAs ahead).
+constexpr int kAhead = 4;
+
+// Scheduling hints for the instruction scheduler (groups are filled in
+// order within the current scheduling region): R DS reads first, then
+// (1 MFMA, R/NA... ) pairs -- a pipelined chain of n MFMAs whose operand
+// reads (rpm reads per MFMA) run `ahead` MFMAs in front of their use.
+constexpr int kMaskMFMA = 0x008, kMaskDSRead = 0x100;
+template <int N, int RPM, int AHEAD>
+__device__ __forceinline__ void pipeline_hint() {
+  __builtin_amdgcn_sched_group_barrier(kMaskDSRead, RPM * AHEAD, 0);
+#pragma unroll
+  for (int j = 0; j < N - AHEAD; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDSRead, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMFMA, AHEAD, 0);
+}
 
 // Position -> row cursor over a run stream (one per thread; positions of a
 // thread only grow).  Run r covers positions [pf[r], pf[r+1]) and starts at
@@ -139,9 +208,10 @@ struct RowCursor {
 // forward
 // ---------------------------------------------------------------------------
 template <int D, int KP, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
   constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (KB + VB)];
+  __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
+  __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
   __shared__ int rowtab[2][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -165,13 +235,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16(FwdArgs a) {
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  const bool dense = a.items == nullptr;
+  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
+  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
-  const bool wave_on = q_begin + wave * 32 < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
   const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
   const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
+  RowReader<D> rk;
+  rk.init(l32, h);
+  TrReader<KP> tv;
+  tv.init(tr_r, tr_c);
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -191,70 +267,102 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16(FwdArgs a) {
   }
   __syncthreads();
   if (ntiles > 0) {
-    load_tile<D, NW>(smem, K, D, rowtab[0], wave, lane);
-    load_tile<KP, NW>(smem + KB, Vp, KP, rowtab[0], wave, lane);
+    load_tile<D, NW>(sm0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    load_tile<KP, NW>(sm0 + KB, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
   }
   wait_loads();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    char* Kt = smem + b * (KB + VB);
+  // Two statically distinct buffers: the step that reads one fills the other,
+  // so the compiler can tell the direct loads in flight from the LDS reads.
+  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
     char* Vt = Kt + KB;
     if (t + 1 < ntiles) {
-      char* Kn = smem + (b ^ 1) * (KB + VB);
-      load_tile<D, NW>(Kn, K, D, rowtab[b ^ 1], wave, lane);
-      load_tile<KP, NW>(Kn + KB, Vp, KP, rowtab[b ^ 1], wave, lane);
+      load_tile<D, NW>(Kn, rK, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
+      load_tile<KP, NW>(Kn + KB, rV, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
     }
-    if (wave_on) {
+    {
       f32x16 sc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sc[kb] = f32x16{};
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc)
-          sc[kb] = mma(rd_row<D>(Kt, kb * 32 + l32, 2 * dc + h), qf[dc], sc[kb]);
+        for (int dc = 0; dc < D / 16; ++dc) sc[kb] = mma(rk.read(Kt, kb, dc), qf[dc], sc[kb]);
       }
-      const int nvalid = total - t * kTile;  // keys >= nvalid are masked
-      float mloc = -INFINITY;
+      const int nvalid = total - t * kTile;  // keys >= nvalid are masked (last tile only)
+      const bool part = nvalid < kTile;
+      // row max of scale * s over the valid keys (a negative scale takes the min)
+      const float init = c2 >= 0.f ? -INFINITY : INFINITY;
+      float mx = init;
+      if (part) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = (kb * 32 + c_row(i, h) < nvalid) ? sc[kb][i] * c2 : -INFINITY;
-          sc[kb][i] = x;
-          mloc = fmaxf(mloc, x);
+          for (int i = 0; i < 16; ++i) {
+            const float v = kb * 32 + c_row(i, h) < nvalid ? sc[kb][i] : init;
+            mx = c2 >= 0.f ? fmaxf(mx, v) : fminf(mx, v);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = c2 >= 0.f ? fmaxf(mx, sc[kb][i]) : fminf(mx, sc[kb][i]);
         }
       }
+      float mloc = mx * c2;
       mloc = fmaxf(mloc, xor32(mloc));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fexp2(m_run - m_use);
-      float lsum = 0.f;
+      // Lazy rescaling: the reference max m_run may lag the true running max
+      // by up to 8 (log2 units), so probabilities stay below 2^8; the
+      // accumulators are rescaled only when some row exceeds that.
+      if (__any(mloc > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = fexp2(m_run - m_new);
+#pragma unroll
+        for (int cb = 0; cb < KP / 32; ++cb) acc[cb] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float nm = -m_run;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fexp2(sc[kb][i] - m_use);
-          sc[kb][i] = p;
-          lsum += p;
+        for (int i = 0; i < 16; ++i) sc[kb][i] = fexp2(fmaf(sc[kb][i], c2, nm));
+      }
+      if (part) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + c_row(i, h) >= nvalid) sc[kb][i] = 0.f;
         }
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      {
+        float lsum = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < KP / 32; ++cb) acc[cb] *= alpha;
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lsum += sc[kb][i];
+        }
+        l_run += lsum;
+      }
+      const bf16x8 pf[4] = {to_bf16x8(sc[0], 0), to_bf16x8(sc[0], 8), to_bf16x8(sc[1], 0), to_bf16x8(sc[1], 8)};
 #pragma unroll
       for (int cb = 0; cb < KP / 32; ++cb) {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          acc[cb] = mma(tr_frag<KP>(Vt, cb, kc, tr_r, tr_c), c_to_frag<bf16>(sc[kc >> 1], (kc & 1) * 8), acc[cb]);
+        for (int kc = 0; kc < 4; ++kc) acc[cb] = mma(tv.frag(Vt, cb, kc), pf[kc], acc[cb]);
       }
     }
     if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0, sm0, sm1);
+    step(t + 1, 1, sm1, sm0);
   }
+  if (t < ntiles) step(t, 0, sm0, sm1);
 
   const float l_tot = l_run + xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -282,12 +390,223 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// forward, pipelined variant: one wave per SIMD owns 64 query rows (two
+// 32-row blocks A and B sharing every K / V fragment read), tiles of 32 keys,
+// and the softmax of tile t runs while the score MFMAs of tile t+1 execute.
+// LDS: K and V double buffers (K one tile ahead of V).
+// ---------------------------------------------------------------------------
+constexpr int kTile2 = 32;
+
+template <int W>
+struct Geo2 {
+  static constexpr int CW = W / 8;
+  static constexpr int PITCH = (CW + 2) * 16;
+  static constexpr int BYTES = kTile2 * PITCH;
+  static constexpr int SLOTS = kTile2 * (CW + 2);
+};
+
+// Direct loads of a 32-row tile (see load_tile); 32 * (CW + 2) slots is a
+// multiple of 64 since CW is even, so every instruction is a full one.
+template <int W, int NW>
+__device__ __forceinline__ void load_tile32(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
+                                            int nrows, int wave, int lane) {
+  constexpr int CP = Geo2<W>::CW + 2, NSL = Geo2<W>::SLOTS, NI = (NSL + 63) / 64, NJ = (NI + NW - 1) / NW;
+  asm volatile("" : "+v"(lane));
+  int off[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int inst = wave + j * NW;
+    int s = (inst < NI ? inst : 0) * 64 + lane;
+    s = s < NSL ? s : 0;
+    const int r = s / CP;
+    const int c = s - r * CP;
+    int row;
+    if (rows != nullptr) {
+      row = rows[r];
+      row = row < 0 ? 0 : row;
+    } else {
+      row = row0 + r;
+      row = row < nrows ? row : 0;
+    }
+    off[j] = row * (ldx * 2) + (c < Geo2<W>::CW ? c : 0) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int inst = wave + j * NW;
+    if (inst < NI) ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, off[j], 0, 0, 0);
+  }
+}
+
+template <int D, int KP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd2_bf16(FwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int KB = Geo2<D>::BYTES, VB = Geo2<KP>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char k0[KB];
+  __shared__ __attribute__((aligned(1024))) char k1[KB];
+  __shared__ __attribute__((aligned(1024))) char v0[VB];
+  __shared__ __attribute__((aligned(1024))) char v1[VB];
+  __shared__ int rowtab[3][kTile2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int q_begin, q_end;
+  RowCursor rc;
+  if (a.items == nullptr) {
+    q_begin = blockIdx.x * (NW * 32);
+    q_end = a.n_N;
+    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
+  } else {
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const Item it = a.items[blockIdx.x];
+    q_begin = a.offN[it.patch] + it.row0;
+    q_end = a.offN[it.patch + 1];
+    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
+    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
+  }
+  const int total = rc.total;
+  const int ntiles = (total + kTile2 - 1) / kTile2;
+  const bool dense = a.items == nullptr;
+  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
+  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
+  const int row = q_begin + wave * 32 + l32;
+
+  const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    qf[dc] = row < q_end ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
+  RowReader<D> rk;
+  rk.init(l32, h);
+  TrReader<KP> tv;
+  tv.init(tr_r, tr_c);
+
+  f32x16 acc[KP / 32];
+#pragma unroll
+  for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.c2;
+
+  auto scores = [&](const char* Kt) {
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) sc = mma(rk.read(Kt, 0, dc), qf[dc], sc);
+    return sc;
+  };
+
+  if (tid < kTile2 && !dense) {
+    rc.init();
+    rowtab[0][tid] = rc.row(tid);
+    rowtab[1][tid] = rc.row(kTile2 + tid);
+    rowtab[2][tid] = rc.row(2 * kTile2 + tid);
+  }
+  __syncthreads();
+  if (ntiles > 0) {
+    load_tile32<D, NW>(k0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    load_tile32<KP, NW>(v0, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    if (ntiles > 1) load_tile32<D, NW>(k1, rK, D, dense ? nullptr : rowtab[1], kTile2, total, wave, lane);
+  }
+  wait_loads();
+  __syncthreads();
+  f32x16 sc = ntiles > 0 ? scores(k0) : f32x16{};
+
+  // step t: softmax(t) runs while the MFMAs of scores(t+1) (from Kn) execute;
+  // then P V(t) from Vt.  Loads K(t+2) into Kw (scores(t) are done with it)
+  // and V(t+1) into Vn.
+  auto step = [&](const int t, const char* Kn, char* Kw, const char* Vt, char* Vn) {
+    if (t + 2 < ntiles)
+      load_tile32<D, NW>(Kw, rK, D, dense ? nullptr : rowtab[(t + 2) % 3], (t + 2) * kTile2, total, wave, lane);
+    if (t + 1 < ntiles)
+      load_tile32<KP, NW>(Vn, rV, KP, dense ? nullptr : rowtab[(t + 1) % 3], (t + 1) * kTile2, total, wave, lane);
+    f32x16 sn = f32x16{};
+    if (t + 1 < ntiles) sn = scores(Kn);
+    const int nvalid = total - t * kTile2;
+    const float init = c2 >= 0.f ? -INFINITY : INFINITY;
+    float mx = init;
+    if (nvalid < kTile2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = c_row(i, h) < nvalid ? sc[i] : init;
+        mx = c2 >= 0.f ? fmaxf(mx, v) : fminf(mx, v);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = c2 >= 0.f ? fmaxf(mx, sc[i]) : fminf(mx, sc[i]);
+    }
+    float mloc = mx * c2;
+    mloc = fmaxf(mloc, xor32(mloc));
+    // lazy rescaling: the reference max may lag the running max by up to 8
+    if (__any(mloc > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fexp2(m_run - m_new);
+#pragma unroll
+      for (int cb = 0; cb < KP / 32; ++cb) acc[cb] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float nm = -m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fexp2(fmaf(sc[i], c2, nm));
+      if (nvalid < kTile2 && c_row(i, h) >= nvalid) p = 0.f;
+      sc[i] = p;
+      lsum += p;
+    }
+    l_run += lsum;
+    const bf16x8 p0 = to_bf16x8(sc, 0), p1 = to_bf16x8(sc, 8);
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+      acc[cb] = mma(tv.frag(Vt, cb, 0), p0, acc[cb]);
+      acc[cb] = mma(tv.frag(Vt, cb, 1), p1, acc[cb]);
+    }
+    if (tid < kTile2 && !dense && t + 3 < ntiles) rowtab[t % 3][tid] = rc.row((t + 3) * kTile2 + tid);
+    wait_loads();
+    __syncthreads();
+    sc = sn;
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, k1, k0, v0, v1);
+    step(t + 1, k0, k1, v1, v0);
+  }
+  if (t < ntiles) step(t, k1, k0, v0, v1);
+
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row < q_end) {
+    float* Orow = a.O + (size_t)row * a.k;
+    const bool vec = (a.k & 3) == 0;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * h;
+        if (vec) {
+          if (c < a.k)
+            *reinterpret_cast<f32x4*>(Orow + c) =
+                f32x4{acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) Orow[c + e] = acc[cb][4 * g + e] * inv;
+        }
+      }
+    }
+    if (h == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
 template <int D, int KP, int NW>
-__global__ __launch_bounds__(NW * 64) void dq_bf16(DqArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
   constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (KB + VB)];
+  __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
+  __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
   __shared__ int rowtab[2][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -311,14 +630,22 @@ __global__ __launch_bounds__(NW * 64) void dq_bf16(DqArgs a) {
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  const bool dense = a.items == nullptr;
+  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
+  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
-  const bool wave_on = q_begin + wave * 32 < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
   const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
   const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
   const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
+  RowReader<D> rk;
+  rk.init(l32, h);
+  RowReader<KP> rv;
+  rv.init(l32, h);
+  TrReader<D> tk;
+  tk.init(tr_r, tr_c);
 
   bf16x8 qf[D / 16], of[KP / 16];
 #pragma unroll
@@ -342,48 +669,60 @@ __global__ __launch_bounds__(NW * 64) void dq_bf16(DqArgs a) {
   }
   __syncthreads();
   if (ntiles > 0) {
-    load_tile<D, NW>(smem, K, D, rowtab[0], wave, lane);
-    load_tile<KP, NW>(smem + KB, Vp, KP, rowtab[0], wave, lane);
+    load_tile<D, NW>(sm0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    load_tile<KP, NW>(sm0 + KB, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
   }
   wait_loads();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    char* Kt = smem + b * (KB + VB);
+  // Two statically distinct buffers: the step that reads one fills the other,
+  // so the compiler can tell the direct loads in flight from the LDS reads.
+  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
     char* Vt = Kt + KB;
     if (t + 1 < ntiles) {
-      char* Kn = smem + (b ^ 1) * (KB + VB);
-      load_tile<D, NW>(Kn, K, D, rowtab[b ^ 1], wave, lane);
-      load_tile<KP, NW>(Kn + KB, Vp, KP, rowtab[b ^ 1], wave, lane);
+      load_tile<D, NW>(Kn, rK, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
+      load_tile<KP, NW>(Kn + KB, rV, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
     }
-    if (wave_on) {
+    {
       const int nvalid = total - t * kTile;
-      f32x16 ds[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) s = mma(rd_row<D>(Kt, kb * 32 + l32, 2 * dc + h), qf[dc], s);
+        for (int dc = 0; dc < D / 16; ++dc) s = mma(rk.read(Kt, kb, dc), qf[dc], s);
 #pragma unroll
-        for (int kc = 0; kc < KP / 16; ++kc) dp = mma(rd_row<KP>(Vt, kb * 32 + l32, 2 * kc + h), of[kc], dp);
+        for (int kc = 0; kc < KP / 16; ++kc) dp = mma(rv.read(Vt, kb, kc), of[kc], dp);
+        if (nvalid < kTile) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = (kb * 32 + c_row(i, h) < nvalid) ? fexp2(s[i] * c2 - lse2) : 0.f;
-          ds[kb][i] = p * (dp[i] - Dq);
+          for (int i = 0; i < 16; ++i) {
+            const float p = (kb * 32 + c_row(i, h) < nvalid) ? fexp2(fmaf(s[i], c2, -lse2)) : 0.f;
+            s[i] = p * (dp[i] - Dq);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = fexp2(fmaf(s[i], c2, -lse2));
+            s[i] = p * (dp[i] - Dq);
+          }
         }
-      }
+        const bf16x8 d0 = to_bf16x8(s, 0), d1 = to_bf16x8(s, 8);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          dq[db] = mma(tr_frag<D>(Kt, db, kc, tr_r, tr_c), c_to_frag<bf16>(ds[kc >> 1], (kc & 1) * 8), dq[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          dq[db] = mma(tk.frag(Kt, db, 2 * kb), d0, dq[db]);
+          dq[db] = mma(tk.frag(Kt, db, 2 * kb + 1), d1, dq[db]);
+        }
       }
     }
     if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0, sm0, sm1);
+    step(t + 1, 1, sm1, sm0);
   }
+  if (t < ntiles) step(t, 0, sm0, sm1);
 
   if (row_ok) {
     float* out = a.dQ + (size_t)row * D;
@@ -403,11 +742,14 @@ __global__ __launch_bounds__(NW * 64) void dq_bf16(DqArgs a) {
 // dK / dV
 // ---------------------------------------------------------------------------
 template <int D, int KP, int NW>
-__global__ __launch_bounds__(NW * 64) void dkv_bf16(DkvArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
   constexpr int QB = Geo<D>::BYTES, OB = Geo<KP>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (QB + OB)];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][kTile];
-  __shared__ __attribute__((aligned(16))) float Ds[2][kTile];
+  __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
+  __shared__ __attribute__((aligned(1024))) char sm1[QB + OB];
+  __shared__ __attribute__((aligned(16))) float ls0[kTile];
+  __shared__ __attribute__((aligned(16))) float ls1[kTile];
+  __shared__ __attribute__((aligned(16))) float ds0[kTile];
+  __shared__ __attribute__((aligned(16))) float ds1[kTile];
   __shared__ int rowtab[2][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -433,14 +775,26 @@ __global__ __launch_bounds__(NW * 64) void dkv_bf16(DkvArgs a) {
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  const bool dense = a.items == nullptr;
+  const i32x4 rQ = make_rsrc(a.Qp, (unsigned)(a.n_N * D * 2));
+  const i32x4 rO = make_rsrc(a.dOp, (unsigned)((a.n_N + 1) * KP * 2));
+  const i32x4 rL = make_rsrc(a.lse2p, (unsigned)((a.n_N + 1) * 4));
+  const i32x4 rD = make_rsrc(a.Dp, (unsigned)((a.n_N + 1) * 4));
   const int krow = k_begin + wave * 32 + l32;
   const bool key_ok = krow < k_end;
-  const bool wave_on = k_begin + wave * 32 < k_end;
 
   const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
   const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
   const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
   const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
+  RowReader<D> rq;
+  rq.init(l32, h);
+  RowReader<KP> ro;
+  ro.init(l32, h);
+  TrReader<D> tq;
+  tq.init(tr_r, tr_c);
+  TrReader<KP> to;
+  to.init(tr_r, tr_c);
   const int sentinel = a.n_N;  // lse2p[n_N] = +inf, Dp[n_N] = 0
 
   bf16x8 kf[D / 16], vf[KP / 16];
@@ -465,59 +819,89 @@ __global__ __launch_bounds__(NW * 64) void dkv_bf16(DkvArgs a) {
   }
   __syncthreads();
   if (ntiles > 0) {
-    load_tile<D, NW>(smem, Q, D, rowtab[0], wave, lane);
-    load_tile<KP, NW>(smem + QB, dOp, KP, rowtab[0], wave, lane);
-    if (wave == 0) load_vec64(lse2s[0], a.lse2p, rowtab[0], sentinel, lane);
-    if (wave == NW - 1) load_vec64(Ds[0], a.Dp, rowtab[0], sentinel, lane);
+    load_tile<D, NW>(sm0, rQ, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    load_tile<KP, NW>(sm0 + QB, rO, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    if (wave == 0) load_vec64(ls0, rL, dense ? nullptr : rowtab[0], 0, total, sentinel, lane);
+    if (wave == NW - 1) load_vec64(ds0, rD, dense ? nullptr : rowtab[0], 0, total, sentinel, lane);
   }
   wait_loads();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    char* Qt = smem + b * (QB + OB);
+  // Two statically distinct buffers: the step that reads one fills the other.
+  auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
+                  float* dsn) {
     char* Ot = Qt + QB;
     if (t + 1 < ntiles) {
-      char* Qn = smem + (b ^ 1) * (QB + OB);
-      load_tile<D, NW>(Qn, Q, D, rowtab[b ^ 1], wave, lane);
-      load_tile<KP, NW>(Qn + QB, dOp, KP, rowtab[b ^ 1], wave, lane);
-      if (wave == 0) load_vec64(lse2s[b ^ 1], a.lse2p, rowtab[b ^ 1], sentinel, lane);
-      if (wave == NW - 1) load_vec64(Ds[b ^ 1], a.Dp, rowtab[b ^ 1], sentinel, lane);
+      load_tile<D, NW>(Qn, rQ, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
+      load_tile<KP, NW>(Qn + QB, rO, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
+      if (wave == 0) load_vec64(lsn, rL, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
+      if (wave == NW - 1) load_vec64(dsn, rD, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
     }
-    if (wave_on) {
-      f32x16 pb[2], ds[2];
+    {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s = f32x16{}, dp = f32x16{};
+        // S and dP chains: operand reads run kAhead MFMAs ahead of their use.
+        constexpr int NA = D / 16, NB = KP / 16, N = NA + NB;
+        bf16x8 ring[kAhead];
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) s = mma(rd_row<D>(Qt, qb * 32 + l32, 2 * dc + h), kf[dc], s);
+        for (int j = 0; j < kAhead; ++j) ring[j] = j < NA ? rq.read(Qt, qb, j) : ro.read(Ot, qb, j - NA);
 #pragma unroll
-        for (int kc = 0; kc < KP / 16; ++kc) dp = mma(rd_row<KP>(Ot, qb * 32 + l32, 2 * kc + h), vf[kc], dp);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qr = qb * 32 + c_row(i, h);
-          const float p = fexp2(s[i] * c2 - lse2s[b][qr]);
-          pb[qb][i] = p;
-          ds[qb][i] = p * (dp[i] - Ds[b][qr]);
+        for (int j = 0; j < N; ++j) {
+          const bf16x8 cur = ring[j % kAhead];
+          if (j + kAhead < N)
+            ring[j % kAhead] = (j + kAhead) < NA ? rq.read(Qt, qb, j + kAhead) : ro.read(Ot, qb, j + kAhead - NA);
+          if (j < NA) s = mma(cur, kf[j], s);
+          else dp = mma(cur, vf[j - NA], dp);
         }
-      }
+        pipeline_hint<N, 1, kAhead>();
+        __builtin_amdgcn_sched_barrier(0);
+        // per-row lse and D of this lane's 16 query rows (4 runs of 4)
+        const f32x4* l4 = reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h);
+        const f32x4* d4 = reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h);
 #pragma unroll
-      for (int cb = 0; cb < KP / 32; ++cb) {
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lg = l4[2 * g], dg = d4[2 * g];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          dv[cb] = mma(tr_frag<KP>(Ot, cb, kc, tr_r, tr_c), c_to_frag<bf16>(pb[kc >> 1], (kc & 1) * 8), dv[cb]);
-      }
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g + e;
+            const float p = fexp2(fmaf(s[i], c2, -lg[e]));
+            s[i] = p;
+            dp[i] = p * (dp[i] - dg[e]);
+          }
+        }
+        const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
+        const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 8);
+        // dV (2 * KP/32 MFMAs) then dK (2 * D/32), transposed reads kAhead ahead
+        constexpr int MV = 2 * (KP / 32), MK = 2 * (D / 32), M = MV + MK;
+        auto trf = [&](int j) {
+          return j < MV ? to.frag(Ot, j >> 1, 2 * qb + (j & 1)) : tq.frag(Qt, (j - MV) >> 1, 2 * qb + ((j - MV) & 1));
+        };
+        bf16x8 tring[kAhead];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+        for (int j = 0; j < kAhead; ++j) tring[j] = trf(j);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          dk[db] = mma(tr_frag<D>(Qt, db, kc, tr_r, tr_c), c_to_frag<bf16>(ds[kc >> 1], (kc & 1) * 8), dk[db]);
+        for (int j = 0; j < M; ++j) {
+          const bf16x8 cur = tring[j % kAhead];
+          if (j + kAhead < M) tring[j % kAhead] = trf(j + kAhead);
+          if (j < MV) dv[j >> 1] = mma(cur, (j & 1) ? p1 : p0, dv[j >> 1]);
+          else dk[(j - MV) >> 1] = mma(cur, ((j - MV) & 1) ? d1 : d0, dk[(j - MV) >> 1]);
+        }
+        pipeline_hint<M, 2, kAhead>();
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+    step(t + 1, 1, sm1, sm0, ls1, ls0, ds1, ds0);
   }
+  if (t < ntiles) step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
 
   if (key_ok) {
     float* okr = a.dK + (size_t)krow * D;
@@ -570,7 +954,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_bf16(DkvArgs a) {
 hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                       \
   if (D == DD && KP == KK) {                                                                                \
-    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);          \
+    hipLaunchKernelGGL((tb::fwd2_bf16<DD, KK>), dim3(grid), dim3(256), 0, st, a);                            \
     return hipGetLastError();                                                                               \
   }
   SSC_BF16_INSTANCES(SSC_L)

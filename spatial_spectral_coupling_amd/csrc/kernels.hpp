@@ -11,6 +11,10 @@ enum class DType { F32 = 0, BF16 = 1 };
 // own kWavesQ * 32 rows, the dK/dV kernel owns kWavesK * 32 source rows.
 constexpr int kWavesQ = 8;
 constexpr int kWavesK = 4;
+// Rows owned by one workgroup of each bf16 kernel (work-item sizes).
+constexpr int kRowsFwd = 128;          // forward: 4 waves x 32 rows
+constexpr int kRowsDq = kWavesQ * 32;  // dQ
+constexpr int kRowsDkv = kWavesK * 32; // dK / dV
 
 // Work item of the row-block kernels: (patch, first row within the patch).
 struct Item {
