@@ -95,6 +95,49 @@ def time_steps(fns, steps, warmup, torch):
     return phase, total, wall
 
 
+KERNEL_SOURCES = ("spatial_spectral_coupling_amd/csrc/attn_bf16.hip", "spatial_spectral_coupling_amd/csrc/common.hpp",
+                  "spatial_spectral_coupling_amd/csrc/kernels.hpp", "spatial_spectral_coupling_amd/csrc/api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkv_bf16_60k_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dK/dV kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factors), or
+    None when the kernel sources changed since those counters were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and line.startswith("- "):
+                    key, val = line[2:].split(":", 1)
+                    fields[key.strip()] = val.strip().strip("`")
+        if fields.get("source_sha256") != kernel_source_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib: int, torch):
+    """A plain streaming kernel of known size (reads and writes `mib` MiB):
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.zeros(mib * 2 ** 18, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.bitwise_not(x, out=y)
+    torch.cuda.synchronize()
+    log(f"copy probe: {mib} MiB read + {mib} MiB written per launch, 3 launches")
+
+
 def cpu_baseline(c, offN, offM, idx_np, np):
     """The fp64 oracle on a bounded sample of the same workload, scaled to ms
     per step: dense fwd+bwd for 2048 target rows (x n_N / 2048), patch scoring
@@ -138,6 +181,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-160k", action="store_true", help="skip the informational 160k geo record")
     ap.add_argument("--dense-only", action="store_true", help="time only the dense coupling (profiling)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run a plain streaming kernel of MIB MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -208,8 +253,8 @@ def main():
                       "P": c["P"], "s": s}
     achieved = dkv_flops(pairs_dense, d, k) / dkv_avg / 1e9
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": f"ssc::dkv_kernel<bf16,{d},{ssc.kpad(k)}> (dense dK/dV pass)",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+            "kernel": f"ssc::tb::dkv_bf16<{d},{ssc.kpad(k)},4> (dense dK/dV pass)",
             "launch_ms": round(dkv_avg, 4), "launches": dkv_n,
             "flop_per_launch": dkv_flops(pairs_dense, d, k)}
 
@@ -241,6 +286,9 @@ def main():
                            "pct_peak": round(100 * f4 / g4 / 1e9 / PEAK_BF16_TFLOPS, 2),
                            "executed_pairs": p4, "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
         del geo4
+
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, torch)
 
     cpu = None
     if not args.no_cpu_baseline and not args.dense_only:

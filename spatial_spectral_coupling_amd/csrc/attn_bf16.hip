@@ -15,9 +15,9 @@
 //  * rows are gathered one by one from the caller's arrays, so the geo
 //    support (concatenated source patches) needs no padding: a tile may span
 //    several patches and only the stream's last tile is partial;
-//  * LDS rows carry two pad chunks (32 bytes) so that row-fragment reads
-//    (32 rows, one chunk) and transposed reads (4 rows x 32 bytes per 16
-//    lanes) spread over the banks with purely affine addresses.
+//  * LDS rows carry pad chunks so that row-fragment reads (32 rows, one
+//    chunk) and transposed reads (4 rows x 32 bytes per 16 lanes) spread
+//    over the banks with purely affine addresses.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,19 +29,42 @@ namespace tb {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// Geometry of a row tile of W bf16 columns: CW chunks of 16 bytes per row,
-// stored with a pitch of CW + 2 chunks.  The two pad chunks shift
-// consecutive rows by 32 bytes (mod the bank window), so the 16 lanes of a
-// transposed read (4 rows x 32 bytes) and the row-fragment reads of
-// consecutive rows spread over the banks, while every LDS address stays a
+// Row pitch (in 16-byte chunks) of an LDS tile with cw data chunks per row:
+// the smallest cw + e (e >= 1) such that
+//  * the pitch is an odd number of chunks -- 16 consecutive rows of a
+//    row-fragment read (16 bytes per lane) then start in 16 distinct
+//    16-byte bank groups of the 256-byte bank window;
+//  * the 4 rows x 32 bytes of a 16-lane transposed read are pairwise
+//    disjoint modulo the bank window.
+// Measured on gfx950 (512 threads per CU): row-fragment reads run at about
+// 195 B/clk per CU with such a pitch and at half that with an even one;
+// transposed reads at about 104 B/clk per CU.
+constexpr bool tr_rows_disjoint(int pitch_bytes) {
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b) {
+      const int d = ((b - a) * pitch_bytes) % 256;
+      if (d < 32 || d > 256 - 32) return false;
+    }
+  return true;
+}
+constexpr int tile_pitch_chunks(int cw) {
+  int p = cw + 1;
+  while (!((p & 1) && tr_rows_disjoint(p * 16))) ++p;
+  return p;
+}
+
+// Geometry of a 64-row tile of W bf16 columns: CW data chunks of 16 bytes per
+// row, stored with a pitch of CP chunks; every LDS address of a lane stays a
 // per-lane base plus a compile-time offset.
 template <int W>
 struct Geo {
   static constexpr int CW = W / 8;
-  static constexpr int PITCH = (CW + 2) * 16;   // bytes per row
+  static constexpr int CP = tile_pitch_chunks(CW);
+  static constexpr int PITCH = CP * 16;           // bytes per row
   static constexpr int BYTES = kTile * PITCH;
-  static constexpr int SLOTS = kTile * (CW + 2);  // 16-byte slots, a multiple of 64
+  static constexpr int SLOTS = kTile * CP;        // 16-byte slots, a multiple of 64
 };
+static_assert(Geo<128>::CP == 19 && Geo<224>::CP == 29 && Geo<64>::CP == 9, "tile pitch");
 
 // Row-fragment reads for MFMA operands: rows rb*32 + l32, chunk 2*cc + h.
 template <int W>
@@ -97,7 +120,7 @@ extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((ad
                                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 // Issue the direct loads of one row tile (64 rows) into LDS: slot s of the
-// tile (16 bytes at s * 16) is row s / (CW + 2), chunk s % (CW + 2); pad
+// tile (16 bytes at s * 16) is row s / CP, chunk s % CP; pad
 // slots receive a copy of chunk 0 (never read).  Tile row r is global row
 // rows[r] (negative = no row: row 0 is loaded and masked later) or, when
 // rows == nullptr, row0 + r (rows at or past nrows read row 0).  The loop is
@@ -105,7 +128,7 @@ extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((ad
 template <int W, int NW>
 __device__ __forceinline__ void load_tile(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
                                           int nrows, int wave, int lane) {
-  constexpr int CP = Geo<W>::CW + 2, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
+  constexpr int CP = Geo<W>::CP, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
   // Recompute the per-lane slot arithmetic at every call instead of keeping
   // loop-invariant offsets live across the whole tile loop.
   asm volatile("" : "+v"(lane));
@@ -367,216 +390,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const float l_tot = l_run + xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
-    float* Orow = a.O + (size_t)row * a.k;
-    const bool vec = (a.k & 3) == 0;
-#pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = cb * 32 + 8 * g + 4 * h;
-        if (vec) {
-          if (c < a.k)
-            *reinterpret_cast<f32x4*>(Orow + c) =
-                f32x4{acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c + e < a.k) Orow[c + e] = acc[cb][4 * g + e] * inv;
-        }
-      }
-    }
-    if (h == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// forward, pipelined variant: one wave per SIMD owns 64 query rows (two
-// 32-row blocks A and B sharing every K / V fragment read), tiles of 32 keys,
-// and the softmax of tile t runs while the score MFMAs of tile t+1 execute.
-// LDS: K and V double buffers (K one tile ahead of V).
-// ---------------------------------------------------------------------------
-constexpr int kTile2 = 32;
-
-template <int W>
-struct Geo2 {
-  static constexpr int CW = W / 8;
-  static constexpr int PITCH = (CW + 2) * 16;
-  static constexpr int BYTES = kTile2 * PITCH;
-  static constexpr int SLOTS = kTile2 * (CW + 2);
-};
-
-// Direct loads of a 32-row tile (see load_tile); 32 * (CW + 2) slots is a
-// multiple of 64 since CW is even, so every instruction is a full one.
-template <int W, int NW>
-__device__ __forceinline__ void load_tile32(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
-                                            int nrows, int wave, int lane) {
-  constexpr int CP = Geo2<W>::CW + 2, NSL = Geo2<W>::SLOTS, NI = (NSL + 63) / 64, NJ = (NI + NW - 1) / NW;
-  asm volatile("" : "+v"(lane));
-  int off[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int inst = wave + j * NW;
-    int s = (inst < NI ? inst : 0) * 64 + lane;
-    s = s < NSL ? s : 0;
-    const int r = s / CP;
-    const int c = s - r * CP;
-    int row;
-    if (rows != nullptr) {
-      row = rows[r];
-      row = row < 0 ? 0 : row;
-    } else {
-      row = row0 + r;
-      row = row < nrows ? row : 0;
-    }
-    off[j] = row * (ldx * 2) + (c < Geo2<W>::CW ? c : 0) * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int inst = wave + j * NW;
-    if (inst < NI) ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, off[j], 0, 0, 0);
-  }
-}
-
-template <int D, int KP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd2_bf16(FwdArgs a) {
-  constexpr int NW = 4;
-  constexpr int KB = Geo2<D>::BYTES, VB = Geo2<KP>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char k0[KB];
-  __shared__ __attribute__((aligned(1024))) char k1[KB];
-  __shared__ __attribute__((aligned(1024))) char v0[VB];
-  __shared__ __attribute__((aligned(1024))) char v1[VB];
-  __shared__ int rowtab[3][kTile2];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, l32 = lane & 31;
-  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  int q_begin, q_end;
-  RowCursor rc;
-  if (a.items == nullptr) {
-    q_begin = blockIdx.x * (NW * 32);
-    q_end = a.n_N;
-    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
-  } else {
-    if ((int)blockIdx.x >= *a.n_items) return;
-    const Item it = a.items[blockIdx.x];
-    q_begin = a.offN[it.patch] + it.row0;
-    q_end = a.offN[it.patch + 1];
-    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
-    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
-  }
-  const int total = rc.total;
-  const int ntiles = (total + kTile2 - 1) / kTile2;
-  const bool dense = a.items == nullptr;
-  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
-  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
-  const int row = q_begin + wave * 32 + l32;
-
-  const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc)
-    qf[dc] = row < q_end ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
-  RowReader<D> rk;
-  rk.init(l32, h);
-  TrReader<KP> tv;
-  tv.init(tr_r, tr_c);
-
-  f32x16 acc[KP / 32];
-#pragma unroll
-  for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = a.c2;
-
-  auto scores = [&](const char* Kt) {
-    f32x16 sc = f32x16{};
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) sc = mma(rk.read(Kt, 0, dc), qf[dc], sc);
-    return sc;
-  };
-
-  if (tid < kTile2 && !dense) {
-    rc.init();
-    rowtab[0][tid] = rc.row(tid);
-    rowtab[1][tid] = rc.row(kTile2 + tid);
-    rowtab[2][tid] = rc.row(2 * kTile2 + tid);
-  }
-  __syncthreads();
-  if (ntiles > 0) {
-    load_tile32<D, NW>(k0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    load_tile32<KP, NW>(v0, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    if (ntiles > 1) load_tile32<D, NW>(k1, rK, D, dense ? nullptr : rowtab[1], kTile2, total, wave, lane);
-  }
-  wait_loads();
-  __syncthreads();
-  f32x16 sc = ntiles > 0 ? scores(k0) : f32x16{};
-
-  // step t: softmax(t) runs while the MFMAs of scores(t+1) (from Kn) execute;
-  // then P V(t) from Vt.  Loads K(t+2) into Kw (scores(t) are done with it)
-  // and V(t+1) into Vn.
-  auto step = [&](const int t, const char* Kn, char* Kw, const char* Vt, char* Vn) {
-    if (t + 2 < ntiles)
-      load_tile32<D, NW>(Kw, rK, D, dense ? nullptr : rowtab[(t + 2) % 3], (t + 2) * kTile2, total, wave, lane);
-    if (t + 1 < ntiles)
-      load_tile32<KP, NW>(Vn, rV, KP, dense ? nullptr : rowtab[(t + 1) % 3], (t + 1) * kTile2, total, wave, lane);
-    f32x16 sn = f32x16{};
-    if (t + 1 < ntiles) sn = scores(Kn);
-    const int nvalid = total - t * kTile2;
-    const float init = c2 >= 0.f ? -INFINITY : INFINITY;
-    float mx = init;
-    if (nvalid < kTile2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = c_row(i, h) < nvalid ? sc[i] : init;
-        mx = c2 >= 0.f ? fmaxf(mx, v) : fminf(mx, v);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = c2 >= 0.f ? fmaxf(mx, sc[i]) : fminf(mx, sc[i]);
-    }
-    float mloc = mx * c2;
-    mloc = fmaxf(mloc, xor32(mloc));
-    // lazy rescaling: the reference max may lag the running max by up to 8
-    if (__any(mloc > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = fexp2(m_run - m_new);
-#pragma unroll
-      for (int cb = 0; cb < KP / 32; ++cb) acc[cb] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float nm = -m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = fexp2(fmaf(sc[i], c2, nm));
-      if (nvalid < kTile2 && c_row(i, h) >= nvalid) p = 0.f;
-      sc[i] = p;
-      lsum += p;
-    }
-    l_run += lsum;
-    const bf16x8 p0 = to_bf16x8(sc, 0), p1 = to_bf16x8(sc, 8);
-#pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb) {
-      acc[cb] = mma(tv.frag(Vt, cb, 0), p0, acc[cb]);
-      acc[cb] = mma(tv.frag(Vt, cb, 1), p1, acc[cb]);
-    }
-    if (tid < kTile2 && !dense && t + 3 < ntiles) rowtab[t % 3][tid] = rc.row((t + 3) * kTile2 + tid);
-    wait_loads();
-    __syncthreads();
-    sc = sn;
-  };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, k1, k0, v0, v1);
-    step(t + 1, k0, k1, v1, v0);
-  }
-  if (t < ntiles) step(t, k1, k0, v0, v1);
-
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row < q_end) {
     float* Orow = a.O + (size_t)row * a.k;
     const bool vec = (a.k & 3) == 0;
 #pragma unroll
@@ -954,7 +767,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                       \
   if (D == DD && KP == KK) {                                                                                \
-    hipLaunchKernelGGL((tb::fwd2_bf16<DD, KK>), dim3(grid), dim3(256), 0, st, a);                            \
+    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);          \
     return hipGetLastError();                                                                               \
   }
   SSC_BF16_INSTANCES(SSC_L)

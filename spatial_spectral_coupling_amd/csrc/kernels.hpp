@@ -12,7 +12,7 @@ enum class DType { F32 = 0, BF16 = 1 };
 constexpr int kWavesQ = 8;
 constexpr int kWavesK = 4;
 // Rows owned by one workgroup of each bf16 kernel (work-item sizes).
-constexpr int kRowsFwd = 128;          // forward: 4 waves x 32 rows
+constexpr int kRowsFwd = kWavesQ * 32; // forward
 constexpr int kRowsDq = kWavesQ * 32;  // dQ
 constexpr int kRowsDkv = kWavesK * 32; // dK / dV
 
