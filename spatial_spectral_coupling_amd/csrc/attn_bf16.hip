@@ -23,8 +23,22 @@
 
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace ssc {
 namespace tb {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time
+// (no loop for the unroller to give up on; every index is a constant).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
@@ -640,6 +654,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   wait_loads();
   __syncthreads();
 
+  // One tile = 64 query rows = two 32-row blocks qb.  Its MFMAs form four
+  // chains of L steps each, run as one software pipeline of 4L steps:
+  //   c = 0, 1: scores S = Q K^T and dP = dO V^T of block c (row reads);
+  //   c = 2, 3: dV += P^T dO and dK += dS^T Q of block c - 2 (transposed
+  //             reads), 2 (KP/32 + D/32) independent accumulators in turn.
+  // Operand reads run AH steps ahead of their MFMA (also across chain
+  // boundaries), and the softmax of block qb (P, dS and their bf16
+  // packing) is cut into slices spread over chain qb + 1, so that its VALU
+  // work issues while that chain's MFMAs execute.  Scheduling fences between
+  // steps keep this order.
+  constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB;
+  constexpr int NV = KP / 32, NK = D / 32, NVK = NV + NK;
+  constexpr int L = NA + NB;  // == 2 * NVK
+  static_assert(L == 2 * NVK, "chain lengths");
+  constexpr int U = 4 * L, AH = 5;
+  constexpr int SLICES = 24;  // 4 lse/D reads, 16 elements, 4 packings
+
   // Two statically distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
                   float* dsn) {
@@ -650,61 +681,73 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (wave == 0) load_vec64(lsn, rL, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
       if (wave == NW - 1) load_vec64(dsn, rD, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
     }
-    {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = f32x16{}, dp = f32x16{};
-        // S and dP chains: operand reads run kAhead MFMAs ahead of their use.
-        constexpr int NA = D / 16, NB = KP / 16, N = NA + NB;
-        bf16x8 ring[kAhead];
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j) ring[j] = j < NA ? rq.read(Qt, qb, j) : ro.read(Ot, qb, j - NA);
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          const bf16x8 cur = ring[j % kAhead];
-          if (j + kAhead < N)
-            ring[j % kAhead] = (j + kAhead) < NA ? rq.read(Qt, qb, j + kAhead) : ro.read(Ot, qb, j + kAhead - NA);
-          if (j < NA) s = mma(cur, kf[j], s);
-          else dp = mma(cur, vf[j - NA], dp);
-        }
-        pipeline_hint<N, 1, kAhead>();
-        __builtin_amdgcn_sched_barrier(0);
-        // per-row lse and D of this lane's 16 query rows (4 runs of 4)
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h);
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 lg = l4[2 * g], dg = d4[2 * g];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g + e;
-            const float p = fexp2(fmaf(s[i], c2, -lg[e]));
-            s[i] = p;
-            dp[i] = p * (dp[i] - dg[e]);
-          }
-        }
-        const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
-        const bf16x8 d0 = to_bf16x8(dp, 0), d1 = to_bf16x8(dp, 8);
-        // dV (2 * KP/32 MFMAs) then dK (2 * D/32), transposed reads kAhead ahead
-        constexpr int MV = 2 * (KP / 32), MK = 2 * (D / 32), M = MV + MK;
-        auto trf = [&](int j) {
-          return j < MV ? to.frag(Ot, j >> 1, 2 * qb + (j & 1)) : tq.frag(Qt, (j - MV) >> 1, 2 * qb + ((j - MV) & 1));
-        };
-        bf16x8 tring[kAhead];
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j) tring[j] = trf(j);
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-          const bf16x8 cur = tring[j % kAhead];
-          if (j + kAhead < M) tring[j % kAhead] = trf(j + kAhead);
-          if (j < MV) dv[j >> 1] = mma(cur, (j & 1) ? p1 : p0, dv[j >> 1]);
-          else dk[(j - MV) >> 1] = mma(cur, ((j - MV) & 1) ? d1 : d0, dk[(j - MV) >> 1]);
-        }
-        pipeline_hint<M, 2, kAhead>();
-        __builtin_amdgcn_sched_barrier(0);
+    f32x16 sc[2], dp[2];
+    bf16x8 pk[2][2], dk8[2][2];
+    f32x4 lg[4], dg[4];
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+
+    auto operand = [&](const int u) -> bf16x8 {
+      const int c = u / L, j = u % L;
+      if (c < 2) {
+        if (j < 2 * PAIRS) return (j & 1) ? ro.read(Ot, c, j >> 1) : rq.read(Qt, c, j >> 1);
+        return NA > NB ? rq.read(Qt, c, j - PAIRS) : ro.read(Ot, c, j - PAIRS);
       }
-    }
+      const int qb = c - 2, kk = j / NVK, m = j % NVK;
+      return m < NV ? to.frag(Ot, m, 2 * qb + kk) : tq.frag(Qt, m - NV, 2 * qb + kk);
+    };
+    auto mma_step = [&](const int u, const bf16x8& x) {
+      const int c = u / L, j = u % L;
+      if (c < 2) {
+        const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
+        const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
+        if (is_s) sc[c] = mma(x, kf[chunk], sc[c]);
+        else dp[c] = mma(x, vf[chunk], dp[c]);
+        return;
+      }
+      const int qb = c - 2, kk = j / NVK, m = j % NVK;
+      if (m < NV) dv[m] = mma(x, pk[qb][kk], dv[m]);
+      else dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
+    };
+    // Slice k of the softmax of block qb: k < 4 reads the lse / D values of
+    // element group k; k = 4..11 and 14..21 compute elements 0..7 and 8..15
+    // (P = exp2(S c2 - lse2), dS = P (dP - D)); 12, 13, 22, 23 pack halves.
+    auto slice = [&](const int qb, const int k) {
+      if (k < 4) {
+        lg[k] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * k);
+        dg[k] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * k);
+      } else if (k == 12) {
+        pk[qb][0] = to_bf16x8(sc[qb], 0);
+      } else if (k == 13) {
+        dk8[qb][0] = to_bf16x8(dp[qb], 0);
+      } else if (k == 22) {
+        pk[qb][1] = to_bf16x8(sc[qb], 8);
+      } else if (k == 23) {
+        dk8[qb][1] = to_bf16x8(dp[qb], 8);
+      } else {
+        const int i = k < 12 ? k - 4 : k - 6;
+        const float p = fexp2(fmaf(sc[qb][i], c2, -lg[i >> 2][i & 3]));
+        sc[qb][i] = p;
+        dp[qb][i] = p * (dp[qb][i] - dg[i >> 2][i & 3]);
+      }
+    };
+    auto side = [&](const int u) {
+      const int c = u / L, j = u % L;
+      if (c != 1 && c != 2) return;
+      static_for<SLICES>([&](auto k) {
+        if (k * L / SLICES == j) slice(c - 1, k);
+      });
+    };
+
+    bf16x8 ring[AH];
+    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    static_for<U>([&](auto u) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 cur = ring[u % AH];
+      if (u + AH < U) ring[u % AH] = operand(u + AH);
+      mma_step(u, cur);
+      side(u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
     if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
