@@ -171,6 +171,30 @@ __device__ __forceinline__ void load_tile(char* tile, const i32x4& rsrc, int ldx
   }
 }
 
+// The j-th direct load of this wave for a row tile (see load_tile); used to
+// spread a tile's loads over the MFMA pipeline of the previous tile.
+template <int W, int NW, bool GEO>
+__device__ __forceinline__ void load_tile_one(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
+                                              int nrows, int wave, int lane, int j) {
+  constexpr int CP = Geo<W>::CP, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
+  const int inst = wave + j * NW;
+  if (NJ * NW != NI && j == NJ - 1 && inst >= NI) return;  // only the last load can fall off (wave-uniform)
+  asm volatile("" : "+v"(lane));
+  const int s = inst * 64 + lane;
+  const int r = s / CP;
+  const int c = s - r * CP;
+  int row;
+  if (GEO) {
+    row = rows[r];
+    row = row < 0 ? 0 : row;
+  } else {
+    row = row0 + r;
+    row = row < nrows ? row : 0;
+  }
+  ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, row * (ldx * 2) + (c < Geo<W>::CW ? c : 0) * 16,
+                          0, 0, 0);
+}
+
 // 64 fp32 values gathered by row index (negative -> index `sentinel`).
 __device__ __forceinline__ void load_vec64(float* dst, const i32x4& rsrc, const int* rows, int row0, int nrows,
                                            int sentinel, int lane) {
@@ -568,7 +592,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-template <int D, int KP, int NW>
+template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
   constexpr int QB = Geo<D>::BYTES, OB = Geo<KP>::BYTES;
   __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
@@ -586,7 +610,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int k_begin, k_end;
   RowCursor rc;
-  if (a.items == nullptr) {
+  if (!GEO) {
     k_begin = blockIdx.x * (NW * 32);
     k_end = a.n_M;
     rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_N, 0, 0, 0};
@@ -602,7 +626,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
-  const bool dense = a.items == nullptr;
+  constexpr bool dense = !GEO;
   const i32x4 rQ = make_rsrc(a.Qp, (unsigned)(a.n_N * D * 2));
   const i32x4 rO = make_rsrc(a.dOp, (unsigned)((a.n_N + 1) * KP * 2));
   const i32x4 rL = make_rsrc(a.lse2p, (unsigned)((a.n_N + 1) * 4));
@@ -670,17 +694,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   static_assert(L == 2 * NVK, "chain lengths");
   constexpr int U = 4 * L, AH = 5;
   constexpr int SLICES = 24;  // 4 lse/D reads, 16 elements, 4 packings
+  // Direct loads of the next tile, spread over the first half of the
+  // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
+  // The last tile loads a clamped (valid) copy into the idle buffer.
+  constexpr int NJQ = (Geo<D>::SLOTS / 64 + NW - 1) / NW, NJO = (Geo<KP>::SLOTS / 64 + NW - 1) / NW;
+  constexpr int NL = NJQ + NJO + 1, LOAD0 = 1, LSTRIDE = (U / 2 - LOAD0) / NL > 0 ? (U / 2 - LOAD0) / NL : 1;
 
   // Two statically distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
                   float* dsn) {
     char* Ot = Qt + QB;
-    if (t + 1 < ntiles) {
-      load_tile<D, NW>(Qn, rQ, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
-      load_tile<KP, NW>(Qn + QB, rO, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
-      if (wave == 0) load_vec64(lsn, rL, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
-      if (wave == NW - 1) load_vec64(dsn, rD, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, sentinel, lane);
-    }
     f32x16 sc[2], dp[2];
     bf16x8 pk[2][2], dk8[2][2];
     f32x4 lg[4], dg[4];
@@ -708,29 +731,45 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (m < NV) dv[m] = mma(x, pk[qb][kk], dv[m]);
       else dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
     };
-    // Slice k of the softmax of block qb: k < 4 reads the lse / D values of
-    // element group k; k = 4..11 and 14..21 compute elements 0..7 and 8..15
-    // (P = exp2(S c2 - lse2), dS = P (dP - D)); 12, 13, 22, 23 pack halves.
+    // Slice k of the softmax of block qb, in dependency order: reads of the
+    // lse / D values of element group g (elements 4g .. 4g+3) two groups
+    // ahead of their use, the elements (P = exp2(S c2 - lse2),
+    // dS = P (dP - D)), and the bf16 packing of each half once complete.
+    //   k:  0 1 | 2..5 | 6 | 7..10 | 11 12 | 13 | 14..17 | 18..21 | 22 23
+    //       r0 r1 e0-3   r2 e4-7    pack 0   r3  e8-11    e12-15   pack 1
     auto slice = [&](const int qb, const int k) {
-      if (k < 4) {
-        lg[k] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * k);
-        dg[k] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * k);
-      } else if (k == 12) {
+      constexpr int kRead[4] = {0, 1, 6, 13};
+      constexpr int kElem0[4] = {2, 7, 14, 18};
+      if (k == kRead[0] || k == kRead[1] || k == kRead[2] || k == kRead[3]) {
+        const int g = k == kRead[0] ? 0 : k == kRead[1] ? 1 : k == kRead[2] ? 2 : 3;
+        lg[g] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * g);
+        dg[g] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * g);
+      } else if (k == 11) {
         pk[qb][0] = to_bf16x8(sc[qb], 0);
-      } else if (k == 13) {
+      } else if (k == 12) {
         dk8[qb][0] = to_bf16x8(dp[qb], 0);
       } else if (k == 22) {
         pk[qb][1] = to_bf16x8(sc[qb], 8);
       } else if (k == 23) {
         dk8[qb][1] = to_bf16x8(dp[qb], 8);
       } else {
-        const int i = k < 12 ? k - 4 : k - 6;
-        const float p = fexp2(fmaf(sc[qb][i], c2, -lg[i >> 2][i & 3]));
+        const int g = k < kElem0[1] ? 0 : k < kElem0[2] ? 1 : k < kElem0[3] ? 2 : 3;
+        const int i = 4 * g + (k - kElem0[g]);
+        const float p = fexp2(fmaf(sc[qb][i], c2, -lg[g][i & 3]));
         sc[qb][i] = p;
-        dp[qb][i] = p * (dp[qb][i] - dg[i >> 2][i & 3]);
+        dp[qb][i] = p * (dp[qb][i] - dg[g][i & 3]);
       }
     };
+    const int* rn = GEO ? rowtab[b ^ 1] : nullptr;
+    const int row0n = (t + 1) * kTile;
+    auto issue_load = [&](const int j) {
+      if (j < NJQ) load_tile_one<D, NW, GEO>(Qn, rQ, D, rn, row0n, total, wave, lane, j);
+      else if (j < NJQ + NJO) load_tile_one<KP, NW, GEO>(Qn + QB, rO, KP, rn, row0n, total, wave, lane, j - NJQ);
+      else if (wave == 0) load_vec64(lsn, rL, rn, row0n, total, sentinel, lane);
+      else if (wave == NW - 1) load_vec64(dsn, rD, rn, row0n, total, sentinel, lane);
+    };
     auto side = [&](const int u) {
+      if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
       const int c = u / L, j = u % L;
       if (c != 1 && c != 2) return;
       static_for<SLICES>([&](auto k) {
@@ -832,7 +871,10 @@ hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t 
 hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                       \
   if (D == DD && KP == KK) {                                                                                \
-    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK>), dim3(grid), dim3(kWavesK * 64), 0, st, a);          \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
     return hipGetLastError();                                                                               \
   }
   SSC_BF16_INSTANCES(SSC_L)
