@@ -133,81 +133,103 @@ extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((ad
                                                    int size, int voffset, int soffset, int offset,
                                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-// Issue the direct loads of one row tile (64 rows) into LDS: slot s of the
-// tile (16 bytes at s * 16) is row s / CP, chunk s % CP; pad
-// slots receive a copy of chunk 0 (never read).  Tile row r is global row
-// rows[r] (negative = no row: row 0 is loaded and masked later) or, when
-// rows == nullptr, row0 + r (rows at or past nrows read row 0).  The loop is
-// unrolled; each load needs one 32-bit offset.
+// Division of a tile slot index s < 64 CP by the constant CP as a 24-bit
+// multiply and shift (checked exhaustively at compile time).
+constexpr unsigned slot_magic(int cp) { return (1u << 20) / (unsigned)cp + 1u; }
+constexpr bool slot_magic_exact(int cp) {
+  for (unsigned s = 0; s < 64u * (unsigned)cp; ++s)
+    if (((s * slot_magic(cp)) >> 20) != s / (unsigned)cp) return false;
+  return true;
+}
+
+// Direct loads of 64-row tiles of one source array (row-major, W bf16 or
+// W / 2 fp32 columns, `limit` rows present) into LDS.  Slot s of a tile (16
+// bytes at s * 16) is tile row r = s / CP, chunk s - r CP; the pad chunks
+// of a row fetch the first chunks of the next row (never read).  The j-th
+// load of a wave is tile instruction wave + j * NW.
+//  * dense tiles are windows of consecutive rows: a buffer resource based at
+//    the tile's first row and bounded by the array's end (rows past it read
+//    zeros), so a lane's byte offset is the tile-independent 16 (s - r PADC);
+//  * geo tiles gather rows listed in an LDS table: phase 1 fetches this
+//    lane's row from the table, phase 2 (a few pipeline steps later) issues
+//    the load; a missing row reads past the end of the array (zeros).
 template <int W, int NW>
-__device__ __forceinline__ void load_tile(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
-                                          int nrows, int wave, int lane) {
-  constexpr int CP = Geo<W>::CP, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
-  // Recompute the per-lane slot arithmetic at every call instead of keeping
-  // loop-invariant offsets live across the whole tile loop.
-  asm volatile("" : "+v"(lane));
-  int off[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int inst = wave + j * NW;
-    const int s = (inst < NI ? inst : 0) * 64 + lane;
-    const int r = s / CP;
-    const int c = s - r * CP;
-    int row;
-    if (rows != nullptr) {
-      row = rows[r];
-      row = row < 0 ? 0 : row;
-    } else {
-      row = row0 + r;
-      row = row < nrows ? row : 0;
-    }
-    off[j] = row * (ldx * 2) + (c < Geo<W>::CW ? c : 0) * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int inst = wave + j * NW;
-    if (NJ * NW == NI || inst < NI)
-      ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, off[j], 0, 0, 0);
-  }
-}
+struct TileSrc {
+  static constexpr int CP = Geo<W>::CP, CW = Geo<W>::CW, RB = 2 * W;
+  static constexpr int NI = Geo<W>::SLOTS / 64;      // instructions per tile
+  static constexpr int NJ = (NI + NW - 1) / NW;      // per wave (at most)
+  static constexpr unsigned MAGIC = slot_magic(CP);
+  static_assert(slot_magic_exact(CP), "slot division");
 
-// The j-th direct load of this wave for a row tile (see load_tile); used to
-// spread a tile's loads over the MFMA pipeline of the previous tile.
-template <int W, int NW, bool GEO>
-__device__ __forceinline__ void load_tile_one(char* tile, const i32x4& rsrc, int ldx, const int* rows, int row0,
-                                              int nrows, int wave, int lane, int j) {
-  constexpr int CP = Geo<W>::CP, NI = Geo<W>::SLOTS / 64, NJ = (NI + NW - 1) / NW;
-  const int inst = wave + j * NW;
-  if (NJ * NW != NI && j == NJ - 1 && inst >= NI) return;  // only the last load can fall off (wave-uniform)
-  asm volatile("" : "+v"(lane));
-  const int s = inst * 64 + lane;
-  const int r = s / CP;
-  const int c = s - r * CP;
-  int row;
-  if (GEO) {
-    row = rows[r];
-    row = row < 0 ? 0 : row;
-  } else {
-    row = row0 + r;
-    row = row < nrows ? row : 0;
-  }
-  ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)(tile + inst * 1024), 16, row * (ldx * 2) + (c < Geo<W>::CW ? c : 0) * 16,
-                          0, 0, 0);
-}
+  const char* base;
+  int limit;
 
-// 64 fp32 values gathered by row index (negative -> index `sentinel`).
-__device__ __forceinline__ void load_vec64(float* dst, const i32x4& rsrc, const int* rows, int row0, int nrows,
-                                           int sentinel, int lane) {
-  int row;
-  if (rows != nullptr) {
-    row = rows[lane];
-    row = row < 0 ? sentinel : row;
-  } else {
-    row = row0 + lane;
-    row = row < nrows ? row : sentinel;
+  __device__ __forceinline__ void init(const void* b, int lim) {
+    base = reinterpret_cast<const char*>(b);
+    limit = lim;
   }
-  ssc_raw_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, row * 4, 0, 0, 0);
-}
+  __device__ __forceinline__ static bool present(int wave, int j) {
+    return NJ * NW == NI || j < NJ - 1 || wave + j * NW < NI;
+  }
+  __device__ __forceinline__ static int slot(int wave, int lane, int j) { return (wave + j * NW) * 64 + lane; }
+  __device__ __forceinline__ static int slot_row(int s) { return (int)(__umul24((unsigned)s, MAGIC) >> 20); }
+  __device__ __forceinline__ i32x4 window(int row0) const {
+    const int n = limit - row0;
+    return make_rsrc(base + (size_t)row0 * RB, n > 0 ? (unsigned)(n * RB) : 0u);
+  }
+  __device__ __forceinline__ i32x4 whole() const { return make_rsrc(base, (unsigned)(limit * RB)); }
+
+  __device__ __forceinline__ static void load_dense(char* tile, const i32x4& win, int wave, int lane, int j) {
+    if (!present(wave, j)) return;  // wave-uniform
+    asm volatile("" : "+v"(lane));
+    const int s = slot(wave, lane, j);
+    const int r = slot_row(s);
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, (s - r * (CP - CW)) * 16, 0, 0,
+                            0);
+  }
+  __device__ __forceinline__ static int geo_row(const int* rows, int wave, int lane, int j) {
+    if (!present(wave, j)) return -1;
+    asm volatile("" : "+v"(lane));
+    return rows[slot_row(slot(wave, lane, j))];
+  }
+  __device__ __forceinline__ void load_geo(char* tile, const i32x4& all, int grow, int wave, int lane, int j) const {
+    if (!present(wave, j)) return;
+    asm volatile("" : "+v"(lane));
+    const int s = slot(wave, lane, j);
+    const int r = slot_row(s);
+    const int off = grow < 0 ? limit * RB : grow * RB + (s - r * CP) * 16;
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
+  }
+  // The whole tile at once (first tile of a stream).
+  template <bool GEO>
+  __device__ __forceinline__ void load_tile(char* tile, const int* rows, int row0, int wave, int lane) const {
+    const i32x4 rs = GEO ? whole() : window(row0);
+    static_for<NJ>([&](auto j) {
+      if (GEO) load_geo(tile, rs, geo_row(rows, wave, lane, j), wave, lane, j);
+      else load_dense(tile, rs, wave, lane, j);
+    });
+  }
+};
+
+// 64 fp32 values of a per-row vector (`limit` entries) for the rows of a
+// tile: dense row0 + lane, geo the table row (missing rows read zero).
+struct VecSrc {
+  const float* base;
+  int limit;
+  __device__ __forceinline__ void init(const float* b, int lim) {
+    base = b;
+    limit = lim;
+  }
+  __device__ __forceinline__ void load_dense(float* dst, int row0, int lane) const {
+    const int n = limit - row0;
+    const i32x4 win = make_rsrc(base + row0, n > 0 ? (unsigned)(n * 4) : 0u);
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
+  }
+  __device__ __forceinline__ void load_geo(float* dst, int grow, int lane) const {
+    const i32x4 all = make_rsrc(base, (unsigned)(limit * 4));
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)dst, 4, grow < 0 ? limit * 4 : grow * 4, 0, 0, 0);
+  }
+};
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -268,7 +290,32 @@ struct RowCursor {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D, int KP, int NW>
+// Exact sign flip of eight bf16 values.
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u16x8, x) ^ (unsigned short)0x8000);
+}
+
+// One wave owns 32 query rows (their Q fragments stay in registers); the
+// workgroup streams the key rows through LDS in tiles of 64.  A tile's MFMAs
+// form four chains run as one software pipeline:
+//   c = 0, 1: scores of key half c (keys 32c .. 32c+31), A = K rows;
+//   c = 2, 3: O += P V over key half c - 2, A = transposed V reads.
+// Operand reads run AH steps ahead of their MFMA.  The softmax of half 0
+// (row maximum, exp2, row sum, bf16 packing) runs in slices during chain 1,
+// that of half 1 during chain 2.  The next tile's direct loads are spread
+// over the first half of the pipeline; scheduling fences between steps keep
+// this order.
+//
+// Softmax reference: the probabilities of a tile are taken relative to a
+// reference fixed for the whole tile (the first tile: the maximum of its
+// first half; later tiles: the running reference), and the accumulators are
+// rescaled only between tiles, when the running maximum has moved more than
+// 8 (log2 units) above the reference.  A tile whose maximum exceeds its
+// reference by more than 32 could overflow; a workgroup that saw one redoes
+// its rows in a second pass with the exact row maxima of the first pass as a
+// fixed reference (probabilities <= 1), so the result is exact either way.
+template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
   constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
@@ -282,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
-  if (a.items == nullptr) {
+  if (!GEO) {
     q_begin = blockIdx.x * (NW * 32);
     q_end = a.n_N;
     rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
@@ -296,134 +343,189 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
-  const bool dense = a.items == nullptr;
-  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
-  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
+  // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
+  // a zero row at n_M)
+  TileSrc<D, NW> sK;
+  sK.init(a.Kp, a.n_M);
+  TileSrc<KP, NW> sV;
+  sV.init(a.Vp, a.n_M + 1);
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
-  const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
-  const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
   RowReader<D> rk;
   rk.init(l32, h);
   TrReader<KP> tv;
   tv.init(tr_r, tr_c);
 
+  // A negative scale is folded into Q (exact sign flip), so the reference is
+  // always a maximum.
+  const bool neg = a.c2 < 0.f;
+  const float c2 = neg ? -a.c2 : a.c2;
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int dc = 0; dc < D / 16; ++dc)
+  for (int dc = 0; dc < D / 16; ++dc) {
     qf[dc] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
+    if (neg) qf[dc] = neg_bf16x8(qf[dc]);
+  }
 
   f32x16 acc[KP / 32];
+  float m_run, l_run, m_true = -INFINITY;
+  bool fixed = false;
+
+  constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;
+  constexpr int C1 = NS, C2 = 2 * NS, C3 = 2 * NS + NPV, U = 2 * NS + 2 * NPV, AH = 5;
+  constexpr int SLICES = 20;  // 2 maximum, 16 elements, 2 packings
+  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = a.c2;
+    for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
+    l_run = 0.f;
+    m_run = fixed ? m_true : -INFINITY;
+    bool lagged = false;
 
-  if (tid < kTile) {
-    rc.init();
-    rowtab[0][tid] = rc.row(tid);
-    rowtab[1][tid] = rc.row(kTile + tid);
-  }
-  __syncthreads();
-  if (ntiles > 0) {
-    load_tile<D, NW>(sm0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    load_tile<KP, NW>(sm0 + KB, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-  }
-  wait_loads();
-  __syncthreads();
-
-  // Two statically distinct buffers: the step that reads one fills the other,
-  // so the compiler can tell the direct loads in flight from the LDS reads.
-  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
-    char* Vt = Kt + KB;
-    if (t + 1 < ntiles) {
-      load_tile<D, NW>(Kn, rK, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
-      load_tile<KP, NW>(Kn + KB, rV, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
+    if (GEO && tid < kTile) {
+      rc.init();
+      rowtab[0][tid] = rc.row(tid);
+      rowtab[1][tid] = rc.row(kTile + tid);
     }
-    {
+    __syncthreads();
+    if (ntiles > 0) {
+      sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+      sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
+    }
+    wait_loads();
+    __syncthreads();
+
+    // Two statically distinct buffers: the step that reads one fills the
+    // other, so the compiler can tell the direct loads in flight from the LDS
+    // reads.  PART: the stream's last tile, whose keys at or past nvalid are
+    // masked.
+    auto step = [&](auto part_c, const int t, const int b, char* Kt, char* Kn) {
+      constexpr bool PART = decltype(part_c)::value;
+      char* Vt = Kt + KB;
+      const int nvalid = total - t * kTile;
+      const bool first = t == 0 && !fixed;
       f32x16 sc[2];
+      bf16x8 pf[2][2];
+      float mx[2], mh[2], mref = m_run, lsum = 0.f;
+      sc[0] = sc[1] = f32x16{};
+
+      auto operand = [&](const int u) -> bf16x8 {
+        if (u < C2) return rk.read(Kt, u / NS, u % NS);
+        const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
+        return tv.frag(Vt, j % NCB, 2 * hb + j / NCB);
+      };
+      auto mma_step = [&](const int u, const bf16x8& x) {
+        if (u < C2) {
+          sc[u / NS] = mma(x, qf[u % NS], sc[u / NS]);
+          return;
+        }
+        const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
+        acc[j % NCB] = mma(x, pf[hb][j / NCB], acc[j % NCB]);
+      };
+      auto valid = [&](const int hb, const int i) { return !PART || hb * 32 + c_row(i, h) < nvalid; };
+      // Slice k of the softmax of key half hb: 0, 1 row maximum (the first
+      // tile takes its reference from half 0); 2..9 and 11..18 elements 0..7
+      // and 8..15; 10 and 19 pack the halves.
+      auto slice = [&](const int hb, const int k) {
+        if (k <= 1) {
+          float m = k == 0 ? -INFINITY : mx[hb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) sc[kb] = mma(rk.read(Kt, kb, dc), qf[dc], sc[kb]);
-      }
-      const int nvalid = total - t * kTile;  // keys >= nvalid are masked (last tile only)
-      const bool part = nvalid < kTile;
-      // row max of scale * s over the valid keys (a negative scale takes the min)
-      const float init = c2 >= 0.f ? -INFINITY : INFINITY;
-      float mx = init;
-      if (part) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float v = kb * 32 + c_row(i, h) < nvalid ? sc[kb][i] : init;
-            mx = c2 >= 0.f ? fmaxf(mx, v) : fminf(mx, v);
+          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, valid(hb, i) ? sc[hb][i] : -INFINITY);
+          mx[hb] = m;
+          if (k == 1) {
+            float ml = m * c2;
+            ml = fmaxf(ml, xor32(ml));
+            mh[hb] = ml;
+            if (hb == 0) mref = first ? ml : m_run;
           }
+        } else if (k == 10 || k == 19) {
+          pf[hb][k == 19] = to_bf16x8(sc[hb], k == 19 ? 8 : 0);
+        } else {
+          const int i = k < 10 ? k - 2 : k - 3;
+          const float p = valid(hb, i) ? fexp2(fmaf(sc[hb][i], c2, -mref)) : 0.f;
+          sc[hb][i] = p;
+          lsum += p;
         }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = c2 >= 0.f ? fmaxf(mx, sc[kb][i]) : fminf(mx, sc[kb][i]);
+      };
+      const int* rn = rowtab[b ^ 1];
+      const int row0n = (t + 1) * kTile;
+      const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
+      int grow = -1;
+      auto load_row = [&](const int j) {  // geo phase 1
+        grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+      };
+      auto issue_load = [&](const int j) {
+        if (j < NJK) {
+          if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+          else sK.load_dense(Kn, winK, wave, lane, j);
+        } else {
+          if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+          else sV.load_dense(Kn + KB, winV, wave, lane, j - NJK);
         }
-      }
-      float mloc = mx * c2;
-      mloc = fmaxf(mloc, xor32(mloc));
-      // Lazy rescaling: the reference max m_run may lag the true running max
-      // by up to 8 (log2 units), so probabilities stay below 2^8; the
-      // accumulators are rescaled only when some row exceeds that.
-      if (__any(mloc > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mloc);
+      };
+      auto side = [&](const int u) {
+        if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+        if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+          load_row((u + 2 - LOAD0) / LSTRIDE);
+        if (u >= C1 && u < C2) {
+          static_for<SLICES>([&](auto k) {
+            if (k * NS / SLICES == u - C1) slice(0, k);
+          });
+        } else if (u >= C2 && u < C3) {
+          static_for<SLICES>([&](auto k) {
+            if (k * NPV / SLICES == u - C2) slice(1, k);
+          });
+        }
+      };
+
+      bf16x8 ring[AH];
+      static_for<AH>([&](auto u) { ring[u] = operand(u); });
+      static_for<U>([&](auto u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = ring[u % AH];
+        if (u + AH < U) ring[u % AH] = operand(u + AH);
+        mma_step(u, cur);
+        side(u);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+
+      // Between tiles: the sums of this tile join the running sum at the
+      // tile's reference; move the reference up when the maximum ran ahead.
+      l_run += lsum;
+      m_run = mref;
+      const float tmax = fmaxf(mh[0], mh[1]);
+      m_true = fmaxf(m_true, tmax);
+      lagged = lagged || tmax > mref + 32.f;
+      if (!fixed && __any(tmax > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, tmax);
         const float alpha = fexp2(m_run - m_new);
 #pragma unroll
-        for (int cb = 0; cb < KP / 32; ++cb) acc[cb] *= alpha;
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] *= alpha;
         l_run *= alpha;
         m_run = m_new;
       }
-      const float nm = -m_run;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = fexp2(fmaf(sc[kb][i], c2, nm));
-      }
-      if (part) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + c_row(i, h) >= nvalid) sc[kb][i] = 0.f;
-        }
-      }
-      {
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) lsum += sc[kb][i];
-        }
-        l_run += lsum;
-      }
-      const bf16x8 pf[4] = {to_bf16x8(sc[0], 0), to_bf16x8(sc[0], 8), to_bf16x8(sc[1], 0), to_bf16x8(sc[1], 8)};
-#pragma unroll
-      for (int cb = 0; cb < KP / 32; ++cb) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) acc[cb] = mma(tv.frag(Vt, cb, kc), pf[kc], acc[cb]);
-      }
+      if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+      wait_loads();
+      __syncthreads();
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      step(std::false_type{}, t, 0, sm0, sm1);
+      step(std::false_type{}, t + 1, 1, sm1, sm0);
     }
-    if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
-    wait_loads();
-    __syncthreads();
-  };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, 0, sm0, sm1);
-    step(t + 1, 1, sm1, sm0);
+    if (ntiles - t == 2) {
+      step(std::false_type{}, t, 0, sm0, sm1);
+      step(std::true_type{}, t + 1, 1, sm1, sm0);
+    } else if (ntiles - t == 1) {
+      step(std::true_type{}, t, 0, sm0, sm1);
+    }
+    if (fixed || !__syncthreads_or(lagged)) break;
+    fixed = true;
   }
-  if (t < ntiles) step(t, 0, sm0, sm1);
 
   const float l_tot = l_run + xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -453,7 +555,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, int KP, int NW>
+// One wave owns 32 query rows (Q and dO fragments, lse and D in registers);
+// the workgroup streams key tiles of 64 rows.  Chains of a tile:
+//   c = 0, 1: scores and dP = dO V^T of key half c, A = K and V rows
+//             (the two accumulations interleaved);
+//   c = 2, 3: dQ += dS K over key half c - 2, A = transposed K reads.
+// The softmax of half 0 (P = exp2(S c2 - lse2), dS = P (dP - D), bf16
+// packing) runs in slices during chain 1, that of half 1 during chain 2.
+template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
   constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
@@ -467,7 +576,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
-  if (a.items == nullptr) {
+  if (!GEO) {
     q_begin = blockIdx.x * (NW * 32);
     q_end = a.n_N;
     rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
@@ -481,16 +590,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
-  const bool dense = a.items == nullptr;
-  const i32x4 rK = make_rsrc(a.Kp, (unsigned)(a.n_M * D * 2));
-  const i32x4 rV = make_rsrc(a.Vp, (unsigned)((a.n_M + 1) * KP * 2));
+  // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
+  // a zero row at n_M)
+  TileSrc<D, NW> sK;
+  sK.init(a.Kp, a.n_M);
+  TileSrc<KP, NW> sV;
+  sV.init(a.Vp, a.n_M + 1);
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
   const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
-  const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
-  const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
   RowReader<D> rk;
   rk.init(l32, h);
   RowReader<KP> rv;
@@ -513,67 +623,123 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
-  if (tid < kTile) {
+  if (GEO && tid < kTile) {
     rc.init();
     rowtab[0][tid] = rc.row(tid);
     rowtab[1][tid] = rc.row(kTile + tid);
   }
   __syncthreads();
   if (ntiles > 0) {
-    load_tile<D, NW>(sm0, rK, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    load_tile<KP, NW>(sm0 + KB, rV, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
+    sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+    sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
   }
   wait_loads();
   __syncthreads();
 
-  // Two statically distinct buffers: the step that reads one fills the other,
-  // so the compiler can tell the direct loads in flight from the LDS reads.
-  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
+  constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB, LA = NA + NB;
+  constexpr int NK = D / 32, LB = 2 * NK;
+  constexpr int C1 = LA, C2 = 2 * LA, C3 = 2 * LA + LB, U = 2 * LA + 2 * LB, AH = 5;
+  constexpr int SLICES = 18;  // 16 elements, 2 packings
+  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+
+  auto step = [&](auto part_c, const int t, const int b, char* Kt, char* Kn) {
+    constexpr bool PART = decltype(part_c)::value;
     char* Vt = Kt + KB;
-    if (t + 1 < ntiles) {
-      load_tile<D, NW>(Kn, rK, D, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
-      load_tile<KP, NW>(Kn + KB, rV, KP, dense ? nullptr : rowtab[b ^ 1], (t + 1) * kTile, total, wave, lane);
-    }
-    {
-      const int nvalid = total - t * kTile;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) s = mma(rk.read(Kt, kb, dc), qf[dc], s);
-#pragma unroll
-        for (int kc = 0; kc < KP / 16; ++kc) dp = mma(rv.read(Vt, kb, kc), of[kc], dp);
-        if (nvalid < kTile) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = (kb * 32 + c_row(i, h) < nvalid) ? fexp2(fmaf(s[i], c2, -lse2)) : 0.f;
-            s[i] = p * (dp[i] - Dq);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fexp2(fmaf(s[i], c2, -lse2));
-            s[i] = p * (dp[i] - Dq);
-          }
-        }
-        const bf16x8 d0 = to_bf16x8(s, 0), d1 = to_bf16x8(s, 8);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dq[db] = mma(tk.frag(Kt, db, 2 * kb), d0, dq[db]);
-          dq[db] = mma(tk.frag(Kt, db, 2 * kb + 1), d1, dq[db]);
-        }
+    const int nvalid = total - t * kTile;
+    f32x16 sc[2], dp[2];
+    bf16x8 ds8[2][2];
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+
+    auto operand = [&](const int u) -> bf16x8 {
+      if (u < C2) {
+        const int kb = u / LA, j = u % LA;
+        if (j < 2 * PAIRS) return (j & 1) ? rv.read(Vt, kb, j >> 1) : rk.read(Kt, kb, j >> 1);
+        return NA > NB ? rk.read(Kt, kb, j - PAIRS) : rv.read(Vt, kb, j - PAIRS);
       }
-    }
-    if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+      const int kb = u < C3 ? 0 : 1, j = u - (kb ? C3 : C2);
+      return tk.frag(Kt, j % NK, 2 * kb + j / NK);
+    };
+    auto mma_step = [&](const int u, const bf16x8& x) {
+      if (u < C2) {
+        const int kb = u / LA, j = u % LA;
+        const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
+        const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
+        if (is_s) sc[kb] = mma(x, qf[chunk], sc[kb]);
+        else dp[kb] = mma(x, of[chunk], dp[kb]);
+        return;
+      }
+      const int kb = u < C3 ? 0 : 1, j = u - (kb ? C3 : C2);
+      dq[j % NK] = mma(x, ds8[kb][j / NK], dq[j % NK]);
+    };
+    // Slice k of the softmax of key half kb: 0..7 and 9..16 elements 0..7
+    // and 8..15, 8 and 17 pack the halves.  Masked keys (PART) get dS = 0.
+    auto slice = [&](const int kb, const int k) {
+      if (k == 8 || k == 17) {
+        ds8[kb][k == 17] = to_bf16x8(sc[kb], k == 17 ? 8 : 0);
+      } else {
+        const int i = k < 8 ? k : k - 1;
+        const float p = fexp2(fmaf(sc[kb][i], c2, -lse2));
+        const float ds = p * (dp[kb][i] - Dq);
+        sc[kb][i] = (!PART || kb * 32 + c_row(i, h) < nvalid) ? ds : 0.f;
+      }
+    };
+    const int* rn = rowtab[b ^ 1];
+    const int row0n = (t + 1) * kTile;
+    const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
+    int grow = -1;
+    auto load_row = [&](const int j) {  // geo phase 1
+      grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+    };
+    auto issue_load = [&](const int j) {
+      if (j < NJK) {
+        if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+        else sK.load_dense(Kn, winK, wave, lane, j);
+      } else {
+        if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+        else sV.load_dense(Kn + KB, winV, wave, lane, j - NJK);
+      }
+    };
+    auto side = [&](const int u) {
+      if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+      if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+        load_row((u + 2 - LOAD0) / LSTRIDE);
+      if (u >= C1 && u < C2) {
+        static_for<SLICES>([&](auto k) {
+          if (k * LA / SLICES == u - C1) slice(0, k);
+        });
+      } else if (u >= C2 && u < C3) {
+        static_for<SLICES>([&](auto k) {
+          if (k * LB / SLICES == u - C2) slice(1, k);
+        });
+      }
+    };
+
+    bf16x8 ring[AH];
+    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    static_for<U>([&](auto u) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 cur = ring[u % AH];
+      if (u + AH < U) ring[u % AH] = operand(u + AH);
+      mma_step(u, cur);
+      side(u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
   };
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, 0, sm0, sm1);
-    step(t + 1, 1, sm1, sm0);
+  for (; t + 2 < ntiles; t += 2) {
+    step(std::false_type{}, t, 0, sm0, sm1);
+    step(std::false_type{}, t + 1, 1, sm1, sm0);
   }
-  if (t < ntiles) step(t, 0, sm0, sm1);
+  if (ntiles - t == 2) {
+    step(std::false_type{}, t, 0, sm0, sm1);
+    step(std::true_type{}, t + 1, 1, sm1, sm0);
+  } else if (ntiles - t == 1) {
+    step(std::true_type{}, t, 0, sm0, sm1);
+  }
 
   if (row_ok) {
     float* out = a.dQ + (size_t)row * D;
@@ -627,10 +793,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
   constexpr bool dense = !GEO;
-  const i32x4 rQ = make_rsrc(a.Qp, (unsigned)(a.n_N * D * 2));
-  const i32x4 rO = make_rsrc(a.dOp, (unsigned)((a.n_N + 1) * KP * 2));
-  const i32x4 rL = make_rsrc(a.lse2p, (unsigned)((a.n_N + 1) * 4));
-  const i32x4 rD = make_rsrc(a.Dp, (unsigned)((a.n_N + 1) * 4));
+  // streamed target rows: Q (n_N rows), dO, lse2 and D (n_N + 1 entries:
+  // a zero / +inf sentinel row at n_N)
+  TileSrc<D, NW> sQ;
+  sQ.init(a.Qp, a.n_N);
+  TileSrc<KP, NW> sO;
+  sO.init(a.dOp, a.n_N + 1);
+  VecSrc sL, sD;
+  sL.init(a.lse2p, a.n_N + 1);
+  sD.init(a.Dp, a.n_N + 1);
   const int krow = k_begin + wave * 32 + l32;
   const bool key_ok = krow < k_end;
 
@@ -646,7 +817,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   tq.init(tr_r, tr_c);
   TrReader<KP> to;
   to.init(tr_r, tr_c);
-  const int sentinel = a.n_N;  // lse2p[n_N] = +inf, Dp[n_N] = 0
 
   bf16x8 kf[D / 16], vf[KP / 16];
 #pragma unroll
@@ -663,17 +833,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dk[db] = f32x16{};
 
-  if (tid < kTile) {
+  if (GEO && tid < kTile) {
     rc.init();
     rowtab[0][tid] = rc.row(tid);
     rowtab[1][tid] = rc.row(kTile + tid);
   }
   __syncthreads();
   if (ntiles > 0) {
-    load_tile<D, NW>(sm0, rQ, D, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    load_tile<KP, NW>(sm0 + QB, rO, KP, dense ? nullptr : rowtab[0], 0, total, wave, lane);
-    if (wave == 0) load_vec64(ls0, rL, dense ? nullptr : rowtab[0], 0, total, sentinel, lane);
-    if (wave == NW - 1) load_vec64(ds0, rD, dense ? nullptr : rowtab[0], 0, total, sentinel, lane);
+    sQ.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+    sO.template load_tile<GEO>(sm0 + QB, rowtab[0], 0, wave, lane);
+    if (wave == 0) {
+      if (GEO) sL.load_geo(ls0, rowtab[0][lane], lane);
+      else sL.load_dense(ls0, 0, lane);
+    }
+    if (wave == NW - 1) {
+      if (GEO) sD.load_geo(ds0, rowtab[0][lane], lane);
+      else sD.load_dense(ds0, 0, lane);
+    }
   }
   wait_loads();
   __syncthreads();
@@ -697,8 +873,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // Direct loads of the next tile, spread over the first half of the
   // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
   // The last tile loads a clamped (valid) copy into the idle buffer.
-  constexpr int NJQ = (Geo<D>::SLOTS / 64 + NW - 1) / NW, NJO = (Geo<KP>::SLOTS / 64 + NW - 1) / NW;
-  constexpr int NL = NJQ + NJO + 1, LOAD0 = 1, LSTRIDE = (U / 2 - LOAD0) / NL > 0 ? (U / 2 - LOAD0) / NL : 1;
+  constexpr int NJQ = TileSrc<D, NW>::NJ, NJO = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJQ + NJO + 1, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
 
   // Two statically distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
@@ -760,16 +936,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         dp[qb][i] = p * (dp[qb][i] - dg[g][i & 3]);
       }
     };
-    const int* rn = GEO ? rowtab[b ^ 1] : nullptr;
+    const int* rn = rowtab[b ^ 1];
     const int row0n = (t + 1) * kTile;
+    const i32x4 winQ = GEO ? sQ.whole() : sQ.window(row0n), winO = GEO ? sO.whole() : sO.window(row0n);
+    int grow = -1;
+    auto load_row = [&](const int j) {  // geo phase 1
+      if (j < NJQ) grow = sQ.geo_row(rn, wave, lane, j);
+      else if (j < NJQ + NJO) grow = sO.geo_row(rn, wave, lane, j - NJQ);
+      else grow = rn[lane];
+    };
     auto issue_load = [&](const int j) {
-      if (j < NJQ) load_tile_one<D, NW, GEO>(Qn, rQ, D, rn, row0n, total, wave, lane, j);
-      else if (j < NJQ + NJO) load_tile_one<KP, NW, GEO>(Qn + QB, rO, KP, rn, row0n, total, wave, lane, j - NJQ);
-      else if (wave == 0) load_vec64(lsn, rL, rn, row0n, total, sentinel, lane);
-      else if (wave == NW - 1) load_vec64(dsn, rD, rn, row0n, total, sentinel, lane);
+      if (j < NJQ) {
+        if (GEO) sQ.load_geo(Qn, winQ, grow, wave, lane, j);
+        else sQ.load_dense(Qn, winQ, wave, lane, j);
+      } else if (j < NJQ + NJO) {
+        if (GEO) sO.load_geo(Qn + QB, winO, grow, wave, lane, j - NJQ);
+        else sO.load_dense(Qn + QB, winO, wave, lane, j - NJQ);
+      } else if (wave == 0) {
+        if (GEO) sL.load_geo(lsn, grow, lane);
+        else sL.load_dense(lsn, row0n, lane);
+      } else if (wave == NW - 1) {
+        if (GEO) sD.load_geo(dsn, grow, lane);
+        else sD.load_dense(dsn, row0n, lane);
+      }
     };
     auto side = [&](const int u) {
       if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+      if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+        load_row((u + 2 - LOAD0) / LSTRIDE);
       const int c = u / L, j = u % L;
       if (c != 1 && c != 2) return;
       static_for<SLICES>([&](auto k) {
@@ -787,7 +981,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       side(u);
     });
     __builtin_amdgcn_sched_barrier(0);
-    if (tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
   };
@@ -849,7 +1043,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                       \
   if (D == DD && KP == KK) {                                                                                \
-    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);          \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
     return hipGetLastError();                                                                               \
   }
   SSC_BF16_INSTANCES(SSC_L)
@@ -860,7 +1057,10 @@ hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_
 hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                       \
   if (D == DD && KP == KK) {                                                                                \
-    hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);           \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
     return hipGetLastError();                                                                               \
   }
   SSC_BF16_INSTANCES(SSC_L)

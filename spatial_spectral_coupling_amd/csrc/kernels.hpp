@@ -9,7 +9,7 @@ enum class DType { F32 = 0, BF16 = 1 };
 
 // Waves per workgroup of the bf16 kernels: query-side kernels (forward, dQ)
 // own kWavesQ * 32 rows, the dK/dV kernel owns kWavesK * 32 source rows.
-constexpr int kWavesQ = 8;
+constexpr int kWavesQ = 4;
 constexpr int kWavesK = 4;
 // Rows owned by one workgroup of each bf16 kernel (work-item sizes).
 constexpr int kRowsFwd = kWavesQ * 32; // forward
