@@ -401,12 +401,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
     // Two statically distinct buffers: the step that reads one fills the
     // other, so the compiler can tell the direct loads in flight from the LDS
-    // reads.  PART: the stream's last tile, whose keys at or past nvalid are
-    // masked.
-    auto step = [&](auto part_c, const int t, const int b, char* Kt, char* Kn) {
-      constexpr bool PART = decltype(part_c)::value;
+    // reads.  The stream's last tile may be partial: its keys at or past
+    // nvalid are masked (a wave-uniform branch inside the softmax slices).
+    auto step = [&](const int t, const int b, char* Kt, char* Kn) {
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
+      const bool part = nvalid < kTile;
       const bool first = t == 0 && !fixed;
       f32x16 sc[2];
       bf16x8 pf[2][2];
@@ -426,15 +426,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
         acc[j % NCB] = mma(x, pf[hb][j / NCB], acc[j % NCB]);
       };
-      auto valid = [&](const int hb, const int i) { return !PART || hb * 32 + c_row(i, h) < nvalid; };
+      auto valid = [&](const int hb, const int i) { return hb * 32 + c_row(i, h) < nvalid; };
       // Slice k of the softmax of key half hb: 0, 1 row maximum (the first
       // tile takes its reference from half 0); 2..9 and 11..18 elements 0..7
       // and 8..15; 10 and 19 pack the halves.
       auto slice = [&](const int hb, const int k) {
         if (k <= 1) {
+          if (k == 0 && part) {
+            // masked keys get a score of -inf (the branch is kept: asm)
+            asm volatile("");
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[hb][i] = valid(hb, i) ? sc[hb][i] : -INFINITY;
+          }
           float m = k == 0 ? -INFINITY : mx[hb];
 #pragma unroll
-          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, valid(hb, i) ? sc[hb][i] : -INFINITY);
+          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sc[hb][i]);
           mx[hb] = m;
           if (k == 1) {
             float ml = m * c2;
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           pf[hb][k == 19] = to_bf16x8(sc[hb], k == 19 ? 8 : 0);
         } else {
           const int i = k < 10 ? k - 2 : k - 3;
-          const float p = valid(hb, i) ? fexp2(fmaf(sc[hb][i], c2, -mref)) : 0.f;
+          const float p = fexp2(fmaf(sc[hb][i], c2, -mref));
           sc[hb][i] = p;
           lsum += p;
         }
@@ -512,16 +518,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       wait_loads();
       __syncthreads();
     };
-    int t = 0;
-    for (; t + 2 < ntiles; t += 2) {
-      step(std::false_type{}, t, 0, sm0, sm1);
-      step(std::false_type{}, t + 1, 1, sm1, sm0);
-    }
-    if (ntiles - t == 2) {
-      step(std::false_type{}, t, 0, sm0, sm1);
-      step(std::true_type{}, t + 1, 1, sm1, sm0);
-    } else if (ntiles - t == 1) {
-      step(std::true_type{}, t, 0, sm0, sm1);
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, 0, sm0, sm1);
+      if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
     }
     if (fixed || !__syncthreads_or(lagged)) break;
     fixed = true;
@@ -643,10 +642,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
 
-  auto step = [&](auto part_c, const int t, const int b, char* Kt, char* Kn) {
-    constexpr bool PART = decltype(part_c)::value;
+  // Keys at or past nvalid (the stream's last tile) get dS = 0.
+  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
     char* Vt = Kt + KB;
     const int nvalid = total - t * kTile;
+    const bool part = nvalid < kTile;
     f32x16 sc[2], dp[2];
     bf16x8 ds8[2][2];
     sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
@@ -673,15 +673,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       dq[j % NK] = mma(x, ds8[kb][j / NK], dq[j % NK]);
     };
     // Slice k of the softmax of key half kb: 0..7 and 9..16 elements 0..7
-    // and 8..15, 8 and 17 pack the halves.  Masked keys (PART) get dS = 0.
+    // and 8..15, 8 and 17 pack the halves.
     auto slice = [&](const int kb, const int k) {
+      if (k == 0 && part) {
+        // masked keys get a score of -inf, hence P = dS = 0 (branch kept: asm)
+        asm volatile("");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] = kb * 32 + c_row(i, h) < nvalid ? sc[kb][i] : -INFINITY;
+      }
       if (k == 8 || k == 17) {
         ds8[kb][k == 17] = to_bf16x8(sc[kb], k == 17 ? 8 : 0);
       } else {
         const int i = k < 8 ? k : k - 1;
         const float p = fexp2(fmaf(sc[kb][i], c2, -lse2));
         const float ds = p * (dp[kb][i] - Dq);
-        sc[kb][i] = (!PART || kb * 32 + c_row(i, h) < nvalid) ? ds : 0.f;
+        sc[kb][i] = ds;
       }
     };
     const int* rn = rowtab[b ^ 1];
@@ -729,16 +735,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     wait_loads();
     __syncthreads();
   };
-  int t = 0;
-  for (; t + 2 < ntiles; t += 2) {
-    step(std::false_type{}, t, 0, sm0, sm1);
-    step(std::false_type{}, t + 1, 1, sm1, sm0);
-  }
-  if (ntiles - t == 2) {
-    step(std::false_type{}, t, 0, sm0, sm1);
-    step(std::true_type{}, t + 1, 1, sm1, sm0);
-  } else if (ntiles - t == 1) {
-    step(std::true_type{}, t, 0, sm0, sm1);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, 0, sm0, sm1);
+    if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
   }
 
   if (row_ok) {
