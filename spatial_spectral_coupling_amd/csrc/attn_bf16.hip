@@ -106,6 +106,16 @@ struct TrReader {
   }
 };
 
+// Elements 2m, 2m+1 of a bf16 operand fragment from two fp32 values (one
+// packed conversion, round to nearest even).
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void put_pair(bf16x8& v, int m, float a, float b) {
+  u32x4 w = __builtin_bit_cast(u32x4, v);
+  w[m] = __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
+  v = __builtin_bit_cast(bf16x8, w);
+}
+
 // Eight probabilities (C-layout elements i0..i0+7) as a bf16 operand.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& c, int i0) {
   bf16x8 r;
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;
   constexpr int C1 = NS, C2 = 2 * NS, C3 = 2 * NS + NPV, U = 2 * NS + 2 * NPV, AH = 5;
-  constexpr int SLICES = 20;  // 2 maximum, 16 elements, 2 packings
+  constexpr int SLICES = 10;  // 2 maximum, 8 element pairs
   constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
 
@@ -409,6 +419,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       const bool part = nvalid < kTile;
       const bool first = t == 0 && !fixed;
       f32x16 sc[2];
+      float sv[2][16];
       bf16x8 pf[2][2];
       float mx[2], mh[2], mref = m_run, lsum = 0.f;
       sc[0] = sc[1] = f32x16{};
@@ -427,20 +438,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         acc[j % NCB] = mma(x, pf[hb][j / NCB], acc[j % NCB]);
       };
       auto valid = [&](const int hb, const int i) { return hb * 32 + c_row(i, h) < nvalid; };
-      // Slice k of the softmax of key half hb: 0, 1 row maximum (the first
-      // tile takes its reference from half 0); 2..9 and 11..18 elements 0..7
-      // and 8..15; 10 and 19 pack the halves.
+      // Slice k of the softmax of key half hb (the scores are copied once out
+      // of the MFMA accumulators into sv): 0, 1 copy and row maximum (the
+      // first tile takes its reference from half 0); 2..9 element pairs
+      // 2m, 2m+1 = 2(k-2) .. : exp2, row sum and packed bf16 probabilities.
       auto slice = [&](const int hb, const int k) {
         if (k <= 1) {
           if (k == 0 && part) {
             // masked keys get a score of -inf (the branch is kept: asm)
             asm volatile("");
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sc[hb][i] = valid(hb, i) ? sc[hb][i] : -INFINITY;
+            for (int i = 0; i < 16; ++i) sv[hb][i] = valid(hb, i) ? sc[hb][i] : -INFINITY;
+          } else if (!part) {
+#pragma unroll
+            for (int i = 8 * k; i < 8 * k + 8; ++i) sv[hb][i] = sc[hb][i];
           }
           float m = k == 0 ? -INFINITY : mx[hb];
 #pragma unroll
-          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sc[hb][i]);
+          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sv[hb][i]);
           mx[hb] = m;
           if (k == 1) {
             float ml = m * c2;
@@ -448,13 +463,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             mh[hb] = ml;
             if (hb == 0) mref = first ? ml : m_run;
           }
-        } else if (k == 10 || k == 19) {
-          pf[hb][k == 19] = to_bf16x8(sc[hb], k == 19 ? 8 : 0);
         } else {
-          const int i = k < 10 ? k - 2 : k - 3;
-          const float p = fexp2(fmaf(sc[hb][i], c2, -mref));
-          sc[hb][i] = p;
-          lsum += p;
+          const int m = k - 2;
+          const float p0 = fexp2(fmaf(sv[hb][2 * m], c2, -mref));
+          const float p1 = fexp2(fmaf(sv[hb][2 * m + 1], c2, -mref));
+          lsum += p0 + p1;
+          put_pair(pf[hb][m >> 2], m & 3, p0, p1);
         }
       };
       const int* rn = rowtab[b ^ 1];
@@ -555,12 +569,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // dQ
 // ---------------------------------------------------------------------------
 // One wave owns 32 query rows (Q and dO fragments, lse and D in registers);
-// the workgroup streams key tiles of 64 rows.  Chains of a tile:
-//   c = 0, 1: scores and dP = dO V^T of key half c, A = K and V rows
-//             (the two accumulations interleaved);
-//   c = 2, 3: dQ += dS K over key half c - 2, A = transposed K reads.
-// The softmax of half 0 (P = exp2(S c2 - lse2), dS = P (dP - D), bf16
-// packing) runs in slices during chain 1, that of half 1 during chain 2.
+// the workgroup streams key tiles of 64 rows.  Per key half h of tile t:
+//   A_h(t): scores and dP = dO V^T, A = K and V rows (two accumulations
+//           interleaved);
+//   B_h(t): dQ += dS K, A = transposed K fragments;
+// and between them the softmax (P = exp2(S c2 - lse2), dS = P (dP - D),
+// bf16 packing).  Iteration t runs A0(t), B1(t-1), A1(t), B0(t): B1 of the
+// previous tile uses transposed K fragments kept in registers, so every
+// softmax gets a window of a full A chain plus a B chain to hide in.
 template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
   constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
@@ -637,58 +653,81 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB, LA = NA + NB;
   constexpr int NK = D / 32, LB = 2 * NK;
-  constexpr int C1 = LA, C2 = 2 * LA, C3 = 2 * LA + LB, U = 2 * LA + 2 * LB, AH = 5;
-  constexpr int SLICES = 18;  // 16 elements, 2 packings
+  // chains of iteration t: A0(t) | B1(t-1) | A1(t) | B0(t)
+  constexpr int CY = LA, CZ = LA + LB, CW = 2 * LA + LB, U = 2 * LA + 2 * LB, AH = 5;
+  constexpr int SLICES = 8;  // element pairs
   constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // position of softmax slice k of a half over its window
+  constexpr int WIN = LA + LB;
 
-  // Keys at or past nvalid (the stream's last tile) get dS = 0.
+  // Half 1 of the previous tile, finished in the next iteration: its scores
+  // and dP (slices still to run), its packed dS and its transposed K
+  // fragments.  Before the first tile they stand for an empty half: zero
+  // K fragments, and values whose remaining slices produce dS = 0 exactly
+  // (-inf scores; elements already past their slice hold 0), so the first
+  // iteration's B1 chain adds exactly 0.
+  f32x16 sc1, dp1;
+  bf16x8 ds1[2], kt[LB];
+  static_for<16>([&](auto ic) {
+    constexpr int i = ic, k = i / 2;
+    sc1[i] = k * WIN / SLICES < LB ? 0.f : -INFINITY;
+  });
+  dp1 = f32x16{};
+  ds1[0] = ds1[1] = bf16x8{};
+#pragma unroll
+  for (int j = 0; j < LB; ++j) kt[j] = bf16x8{};
+
+  // Slice k of the softmax of one half (scores sv, dP dv, packed dS out):
+  // element pair 2k, 2k+1 (P = exp2(S c2 - lse2), dS = P (dP - D)) packed
+  // into out; slice 0 first masks keys at or past nvalid (scores -inf, so
+  // P = dS = 0).
+  auto slice = [&](f32x16& sv, f32x16& dv, bf16x8* out, const int kb, const int k, const bool part,
+                   const int nvalid) {
+    if (k == 0 && part) {
+      asm volatile("");  // keeps the branch
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = kb * 32 + c_row(i, h) < nvalid ? sv[i] : -INFINITY;
+    }
+    const float d0 = fexp2(fmaf(sv[2 * k], c2, -lse2)) * (dv[2 * k] - Dq);
+    const float d1 = fexp2(fmaf(sv[2 * k + 1], c2, -lse2)) * (dv[2 * k + 1] - Dq);
+    put_pair(out[k >> 2], k & 3, d0, d1);
+  };
+
+  // Iteration t: the MFMAs of A0(t), B1(t-1), A1(t), B0(t) as one pipeline;
+  // the softmax of half 0 runs during B1(t-1) and A1(t), that of half 1
+  // during B0(t) and A0(t+1), so each has a 30-step window.  Two statically
+  // distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Kt, char* Kn) {
     char* Vt = Kt + KB;
     const int nvalid = total - t * kTile;
     const bool part = nvalid < kTile;
-    f32x16 sc[2], dp[2];
-    bf16x8 ds8[2][2];
-    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+    f32x16 sc0 = f32x16{}, dp0 = f32x16{};
+    bf16x8 ds0[2];
 
     auto operand = [&](const int u) -> bf16x8 {
-      if (u < C2) {
-        const int kb = u / LA, j = u % LA;
+      if (u < CY || (u >= CZ && u < CW)) {
+        const int kb = u < CY ? 0 : 1, j = u < CY ? u : u - CZ;
         if (j < 2 * PAIRS) return (j & 1) ? rv.read(Vt, kb, j >> 1) : rk.read(Kt, kb, j >> 1);
         return NA > NB ? rk.read(Kt, kb, j - PAIRS) : rv.read(Vt, kb, j - PAIRS);
       }
-      const int kb = u < C3 ? 0 : 1, j = u - (kb ? C3 : C2);
-      return tk.frag(Kt, j % NK, 2 * kb + j / NK);
+      if (u < CZ) return kt[u - CY];
+      const int j = u - CW;
+      return tk.frag(Kt, j % NK, j / NK);
     };
     auto mma_step = [&](const int u, const bf16x8& x) {
-      if (u < C2) {
-        const int kb = u / LA, j = u % LA;
+      if (u < CY || (u >= CZ && u < CW)) {
+        const int j = u < CY ? u : u - CZ;
         const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
         const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
-        if (is_s) sc[kb] = mma(x, qf[chunk], sc[kb]);
-        else dp[kb] = mma(x, of[chunk], dp[kb]);
+        f32x16& sv = u < CY ? sc0 : sc1;
+        f32x16& dv = u < CY ? dp0 : dp1;
+        if (is_s) sv = mma(x, qf[chunk], sv);
+        else dv = mma(x, of[chunk], dv);
         return;
       }
-      const int kb = u < C3 ? 0 : 1, j = u - (kb ? C3 : C2);
-      dq[j % NK] = mma(x, ds8[kb][j / NK], dq[j % NK]);
-    };
-    // Slice k of the softmax of key half kb: 0..7 and 9..16 elements 0..7
-    // and 8..15, 8 and 17 pack the halves.
-    auto slice = [&](const int kb, const int k) {
-      if (k == 0 && part) {
-        // masked keys get a score of -inf, hence P = dS = 0 (branch kept: asm)
-        asm volatile("");
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = kb * 32 + c_row(i, h) < nvalid ? sc[kb][i] : -INFINITY;
-      }
-      if (k == 8 || k == 17) {
-        ds8[kb][k == 17] = to_bf16x8(sc[kb], k == 17 ? 8 : 0);
-      } else {
-        const int i = k < 8 ? k : k - 1;
-        const float p = fexp2(fmaf(sc[kb][i], c2, -lse2));
-        const float ds = p * (dp[kb][i] - Dq);
-        sc[kb][i] = ds;
-      }
+      const int j = u < CZ ? u - CY : u - CW;
+      dq[j % NK] = mma(x, u < CZ ? ds1[j / NK] : ds0[j / NK], dq[j % NK]);
     };
     const int* rn = rowtab[b ^ 1];
     const int row0n = (t + 1) * kTile;
@@ -710,14 +749,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
       if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
         load_row((u + 2 - LOAD0) / LSTRIDE);
-      if (u >= C1 && u < C2) {
+      if (u < CY) {
+        // half 1 of the previous tile: window positions LB .. WIN-1
         static_for<SLICES>([&](auto k) {
-          if (k * LA / SLICES == u - C1) slice(0, k);
+          if (k * WIN / SLICES >= LB && k * WIN / SLICES - LB == u) slice(sc1, dp1, ds1, 1, k, false, kTile);
         });
-      } else if (u >= C2 && u < C3) {
+      } else if (u < CW) {
+        // half 0 of this tile: window positions 0 .. WIN-1 over B1 and A1
         static_for<SLICES>([&](auto k) {
-          if (k * LB / SLICES == u - C2) slice(1, k);
+          if (k * WIN / SLICES == u - CY) slice(sc0, dp0, ds0, 0, k, part, nvalid);
         });
+      } else {
+        // half 1 of this tile, window positions 0 .. LB-1; and its K^T
+        // fragments for the B1 chain of the next iteration
+        static_for<SLICES>([&](auto k) {
+          if (k * WIN / SLICES < LB && k * WIN / SLICES == u - CW) slice(sc1, dp1, ds1, 1, k, part, nvalid);
+        });
+        const int j = u - CW;
+        kt[j] = tk.frag(Kt, j % NK, 2 + j / NK);
+      }
+    };
+    auto pre = [&](const int u) {
+      if (u == CZ) {  // A1(t) starts: fresh accumulators for half 1
+        sc1 = f32x16{};
+        dp1 = f32x16{};
       }
     };
 
@@ -727,6 +782,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 cur = ring[u % AH];
       if (u + AH < U) ring[u % AH] = operand(u + AH);
+      pre(u);
       mma_step(u, cur);
       side(u);
     });
@@ -739,6 +795,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     step(t, 0, sm0, sm1);
     if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
   }
+  // drain: the rest of the last tile's half-1 softmax, then its B1 chain
+  static_for<SLICES>([&](auto k) {
+    if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, 1, k, false, kTile);
+  });
+  static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
 
   if (row_ok) {
     float* out = a.dQ + (size_t)row * D;
@@ -868,7 +929,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int L = NA + NB;  // == 2 * NVK
   static_assert(L == 2 * NVK, "chain lengths");
   constexpr int U = 4 * L, AH = 5;
-  constexpr int SLICES = 24;  // 4 lse/D reads, 16 elements, 4 packings
+  constexpr int SLICES = 12;  // 4 lse/D group reads, 8 element pairs
   // Direct loads of the next tile, spread over the first half of the
   // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
   // The last tile loads a clamped (valid) copy into the idle buffer.
@@ -906,33 +967,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (m < NV) dv[m] = mma(x, pk[qb][kk], dv[m]);
       else dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
     };
-    // Slice k of the softmax of block qb, in dependency order: reads of the
-    // lse / D values of element group g (elements 4g .. 4g+3) two groups
-    // ahead of their use, the elements (P = exp2(S c2 - lse2),
-    // dS = P (dP - D)), and the bf16 packing of each half once complete.
-    //   k:  0 1 | 2..5 | 6 | 7..10 | 11 12 | 13 | 14..17 | 18..21 | 22 23
-    //       r0 r1 e0-3   r2 e4-7    pack 0   r3  e8-11    e12-15   pack 1
+    // Slice k of the softmax of block qb, in dependency order: the lse / D
+    // values of element group g (elements 4g .. 4g+3) are read two slices
+    // ahead of their use, and each element pair m (elements 2m, 2m+1 of
+    // group m / 2) computes P = exp2(S c2 - lse2), dS = P (dP - D) and
+    // packs both into their bf16 operands.
+    //   k:  0  1  2  3  4  5  6  7  8  9  10 11
+    //       r0 r1 p0 p1 r2 p2 p3 r3 p4 p5 p6 p7
     auto slice = [&](const int qb, const int k) {
-      constexpr int kRead[4] = {0, 1, 6, 13};
-      constexpr int kElem0[4] = {2, 7, 14, 18};
+      constexpr int kRead[4] = {0, 1, 4, 7};
       if (k == kRead[0] || k == kRead[1] || k == kRead[2] || k == kRead[3]) {
         const int g = k == kRead[0] ? 0 : k == kRead[1] ? 1 : k == kRead[2] ? 2 : 3;
         lg[g] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * g);
         dg[g] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * g);
-      } else if (k == 11) {
-        pk[qb][0] = to_bf16x8(sc[qb], 0);
-      } else if (k == 12) {
-        dk8[qb][0] = to_bf16x8(dp[qb], 0);
-      } else if (k == 22) {
-        pk[qb][1] = to_bf16x8(sc[qb], 8);
-      } else if (k == 23) {
-        dk8[qb][1] = to_bf16x8(dp[qb], 8);
       } else {
-        const int g = k < kElem0[1] ? 0 : k < kElem0[2] ? 1 : k < kElem0[3] ? 2 : 3;
-        const int i = 4 * g + (k - kElem0[g]);
-        const float p = fexp2(fmaf(sc[qb][i], c2, -lg[g][i & 3]));
-        sc[qb][i] = p;
-        dp[qb][i] = p * (dp[qb][i] - dg[g][i & 3]);
+        const int m = k < 4 ? k - 2 : k < 7 ? k - 3 : k - 4;
+        const int i = 2 * m, g = i >> 2, e = i & 3;
+        const float p0 = fexp2(fmaf(sc[qb][i], c2, -lg[g][e]));
+        const float p1 = fexp2(fmaf(sc[qb][i + 1], c2, -lg[g][e + 1]));
+        put_pair(pk[qb][m >> 2], m & 3, p0, p1);
+        put_pair(dk8[qb][m >> 2], m & 3, p0 * (dp[qb][i] - dg[g][e]), p1 * (dp[qb][i + 1] - dg[g][e + 1]));
       }
     };
     const int* rn = rowtab[b ^ 1];

@@ -265,11 +265,19 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// patch pooling (fp64 sums in row order, then the mean)
+// patch pooling (fp64 sums, then the mean)
 // ---------------------------------------------------------------------------
+// One workgroup per patch.  Thread t owns the column pair t % (d/2) and the
+// row phase t / (d/2): it sums rows begin + phase, begin + phase + NPH, ...
+// in fp64, and the NPH phase sums are then added in phase order.  The order
+// is fixed, so the result is deterministic.  Every partial sum is exact in
+// fp64 (hence equal to the sum in any order, row order included) when the
+// patch has at most 4096 rows and its nonzero entries lie within a factor
+// 2^36 (bf16) or 2^20 (fp32) of each other.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
-  const int b = blockIdx.x;
+  __shared__ double part[256][2];
+  const int b = blockIdx.x, tid = threadIdx.x;
   const bool tgt = b < a.P_N;
   const int p = tgt ? b : b - a.P_N;
   const int* off = tgt ? a.offN : a.offM;
@@ -278,12 +286,34 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int begin = min(max(off[p], 0), n);
   const int end = min(max(off[p + 1], begin), n);
   const int cnt = end - begin;
-  for (int c = threadIdx.x; c < a.d; c += 256) {
-    double s = 0.0;
-    for (int r = begin; r < end; ++r) s += (double)to_f32(X[(size_t)r * a.d + c]);
-    const double mean = cnt > 0 ? s / (double)cnt : 0.0;
-    if (tgt) a.Qbar[(size_t)p * a.d + c] = mean;
-    else a.KbarT[(size_t)c * a.P_M + p] = mean;
+  const int npairs = a.d / 2, nph = 256 / npairs;  // d in {64, 128}: 4 or 8 phases
+  const int cp = tid % npairs, ph = tid / npairs;
+  double s0 = 0.0, s1 = 0.0;
+  if (ph < nph) {
+    for (int r = begin + ph; r < end; r += nph) {
+      const T* x = X + (size_t)r * a.d + 2 * cp;
+      s0 += (double)to_f32(x[0]);
+      s1 += (double)to_f32(x[1]);
+    }
+  }
+  part[tid][0] = s0;
+  part[tid][1] = s1;
+  __syncthreads();
+  if (tid < npairs) {
+    double t0 = 0.0, t1 = 0.0;
+    for (int q = 0; q < nph; ++q) {
+      t0 += part[q * npairs + tid][0];
+      t1 += part[q * npairs + tid][1];
+    }
+    const double m0 = cnt > 0 ? t0 / (double)cnt : 0.0, m1 = cnt > 0 ? t1 / (double)cnt : 0.0;
+    const int c = 2 * tid;
+    if (tgt) {
+      a.Qbar[(size_t)p * a.d + c] = m0;
+      a.Qbar[(size_t)p * a.d + c + 1] = m1;
+    } else {
+      a.KbarT[(size_t)c * a.P_M + p] = m0;
+      a.KbarT[(size_t)(c + 1) * a.P_M + p] = m1;
+    }
   }
 }
 
@@ -300,15 +330,30 @@ hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st) {
 constexpr int kMaxPatches = 8192;
 constexpr int kMaxD = 128;
 
+// The score row lives in LDS: statically sized for the largest P_M, or
+// (SMALL) for at most kSmallPatches, which leaves room for more workgroups
+// per CU.
+constexpr int kSmallPatches = 2048;
+
+template <bool SMALL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ double qb[kMaxD];
-  __shared__ double C[kMaxPatches];
+  __shared__ double C[SMALL ? kSmallPatches : kMaxPatches];
   const int p = blockIdx.x, tid = threadIdx.x;
   for (int c = tid; c < a.d; c += 256) qb[c] = a.Qbar[(size_t)p * a.d + c];
   __syncthreads();
   for (int q = tid; q < a.P_M; q += 256) {
+    // d is a multiple of 16 (64 or 128): unrolled so that the independent
+    // column loads are in flight together
     double acc = 0.0;
-    for (int c = 0; c < a.d; ++c) acc = fma(qb[c], a.KbarT[(size_t)c * a.P_M + q], acc);
+    const double* kt = a.KbarT + q;
+    for (int c0 = 0; c0 < a.d; c0 += 16) {
+      double kv[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) kv[c] = kt[(size_t)(c0 + c) * a.P_M];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc = fma(qb[c0 + c], kv[c], acc);
+    }
     C[q] = acc;
     if (a.scores != nullptr) a.scores[(size_t)p * a.P_M + q] = acc;
   }
@@ -326,7 +371,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.P_N), dim3(256), 0, st, a);
+  if (a.P_M <= kSmallPatches) hipLaunchKernelGGL(topk_kernel<true>, dim3(a.P_N), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(topk_kernel<false>, dim3(a.P_N), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
