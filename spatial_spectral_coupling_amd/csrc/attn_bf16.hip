@@ -189,13 +189,21 @@ struct TileSrc {
   }
   __device__ __forceinline__ i32x4 whole() const { return make_rsrc(base, (unsigned)(limit * RB)); }
 
+  // byte offset of this lane's chunk within a dense window (tile-independent)
+  __device__ __forceinline__ static int dense_offset(int wave, int lane, int j) {
+    const int s = slot(wave, lane, j);
+    return (s - slot_row(s) * (CP - CW)) * 16;
+  }
   __device__ __forceinline__ static void load_dense(char* tile, const i32x4& win, int wave, int lane, int j) {
     if (!present(wave, j)) return;  // wave-uniform
     asm volatile("" : "+v"(lane));
-    const int s = slot(wave, lane, j);
-    const int r = slot_row(s);
-    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, (s - r * (CP - CW)) * 16, 0, 0,
-                            0);
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, dense_offset(wave, lane, j), 0,
+                            0, 0);
+  }
+  // the same with the offset computed once outside the tile loop
+  __device__ __forceinline__ static void load_dense_at(char* tile, const i32x4& win, int off, int wave, int j) {
+    if (!present(wave, j)) return;
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
   }
   __device__ __forceinline__ static int geo_row(const int* rows, int wave, int lane, int j) {
     if (!present(wave, j)) return -1;
@@ -388,6 +396,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int SLICES = 10;  // 2 maximum, 8 element pairs
   constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane load offsets do not depend on the tile; kept in registers
+  int loff[NL];
+  static_for<NL>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+  });
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -481,10 +495,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       auto issue_load = [&](const int j) {
         if (j < NJK) {
           if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
-          else sK.load_dense(Kn, winK, wave, lane, j);
+          else sK.load_dense_at(Kn, winK, loff[j], wave, j);
         } else {
           if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
-          else sV.load_dense(Kn + KB, winV, wave, lane, j - NJK);
+          else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
         }
       };
       auto side = [&](const int u) {
@@ -658,6 +672,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int SLICES = 8;  // element pairs
   constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane load offsets do not depend on the tile; kept in registers
+  int loff[NL];
+  static_for<NL>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+  });
   // position of softmax slice k of a half over its window
   constexpr int WIN = LA + LB;
 
@@ -739,10 +759,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     auto issue_load = [&](const int j) {
       if (j < NJK) {
         if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
-        else sK.load_dense(Kn, winK, wave, lane, j);
+        else sK.load_dense_at(Kn, winK, loff[j], wave, j);
       } else {
         if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
-        else sV.load_dense(Kn + KB, winV, wave, lane, j - NJK);
+        else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
       }
     };
     auto side = [&](const int u) {
