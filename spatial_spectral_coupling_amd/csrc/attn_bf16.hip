@@ -948,13 +948,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int NV = KP / 32, NK = D / 32, NVK = NV + NK;
   constexpr int L = NA + NB;  // == 2 * NVK
   static_assert(L == 2 * NVK, "chain lengths");
-  constexpr int U = 4 * L, AH = 5;
+  constexpr int U = 4 * L, AH = 3;
   constexpr int SLICES = 12;  // 4 lse/D group reads, 8 element pairs
   // Direct loads of the next tile, spread over the first half of the
   // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
   // The last tile loads a clamped (valid) copy into the idle buffer.
   constexpr int NJQ = TileSrc<D, NW>::NJ, NJO = TileSrc<KP, NW>::NJ;
   constexpr int NL = NJQ + NJO + 1, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane tile load offsets do not depend on the tile
+  int loff[NJQ + NJO];
+  static_for<NJQ + NJO>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJQ ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJQ);
+  });
 
   // Two statically distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
@@ -1021,10 +1027,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     auto issue_load = [&](const int j) {
       if (j < NJQ) {
         if (GEO) sQ.load_geo(Qn, winQ, grow, wave, lane, j);
-        else sQ.load_dense(Qn, winQ, wave, lane, j);
+        else sQ.load_dense_at(Qn, winQ, loff[j], wave, j);
       } else if (j < NJQ + NJO) {
         if (GEO) sO.load_geo(Qn + QB, winO, grow, wave, lane, j - NJQ);
-        else sO.load_dense(Qn + QB, winO, wave, lane, j - NJQ);
+        else sO.load_dense_at(Qn + QB, winO, loff[j], wave, j - NJQ);
       } else if (wave == 0) {
         if (GEO) sL.load_geo(lsn, grow, lane);
         else sL.load_dense(lsn, row0n, lane);
