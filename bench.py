@@ -95,8 +95,9 @@ def time_steps(fns, steps, warmup, torch):
     return phase, total, wall
 
 
-KERNEL_SOURCES = ("spatial_spectral_coupling_amd/csrc/attn_bf16.hip", "spatial_spectral_coupling_amd/csrc/common.hpp",
-                  "spatial_spectral_coupling_amd/csrc/kernels.hpp", "spatial_spectral_coupling_amd/csrc/api.hip")
+KERNEL_SOURCES = ("spatial_spectral_coupling_amd/csrc/attn_bf16_kv.hip", "spatial_spectral_coupling_amd/csrc/tile_bf16.hpp",
+                  "spatial_spectral_coupling_amd/csrc/common.hpp", "spatial_spectral_coupling_amd/csrc/kernels.hpp",
+                  "spatial_spectral_coupling_amd/csrc/api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkv_bf16_60k_traffic.md")
 
 

@@ -1,0 +1,307 @@
+// bf16 dK / dV kernel of the spatial-spectral coupling on gfx950 (project
+// page "Spatial-Spectral Coupling as Attention", sections "How it works" and
+// "Geo-FlashAttention").
+#include "tile_bf16.hpp"
+
+namespace ssc {
+namespace tb {
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+template <int D, int KP, int NW, bool GEO>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
+  constexpr int QB = Geo<D>::BYTES, OB = Geo<KP>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
+  __shared__ __attribute__((aligned(1024))) char sm1[QB + OB];
+  __shared__ __attribute__((aligned(16))) float ls0[kTile];
+  __shared__ __attribute__((aligned(16))) float ls1[kTile];
+  __shared__ __attribute__((aligned(16))) float ds0[kTile];
+  __shared__ __attribute__((aligned(16))) float ds1[kTile];
+  __shared__ int rowtab[2][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int k_begin, k_end;
+  RowCursor rc;
+  if (!GEO) {
+    k_begin = blockIdx.x * (NW * 32);
+    k_end = a.n_M;
+    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_N, 0, 0, 0};
+  } else {
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const Item it = a.items[blockIdx.x];
+    k_begin = a.offM[it.patch] + it.row0;
+    k_end = a.offM[it.patch + 1];
+    const int i0 = a.inv_off[it.patch];
+    const int nr = a.inv_off[it.patch + 1] - i0;
+    const int* pf = a.inv_pf + i0 + it.patch;
+    rc = RowCursor{pf, a.inv_idx + i0, a.offN, nr, pf[nr], 0, 0, 0};
+  }
+  const int total = rc.total;
+  const int ntiles = (total + kTile - 1) / kTile;
+  constexpr bool dense = !GEO;
+  // streamed target rows: Q (n_N rows), dO, lse2 and D (n_N + 1 entries:
+  // a zero / +inf sentinel row at n_N)
+  TileSrc<D, NW> sQ;
+  sQ.init(a.Qp, a.n_N);
+  TileSrc<KP, NW> sO;
+  sO.init(a.dOp, a.n_N + 1);
+  VecSrc sL, sD;
+  sL.init(a.lse2p, a.n_N + 1);
+  sD.init(a.Dp, a.n_N + 1);
+  const int krow = k_begin + wave * 32 + l32;
+  const bool key_ok = krow < k_end;
+
+  const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
+  const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
+  const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
+  const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
+  RowReader<D> rq;
+  rq.init(l32, h);
+  RowReader<KP> ro;
+  ro.init(l32, h);
+  TrReader<D> tq;
+  tq.init(tr_r, tr_c);
+  TrReader<KP> to;
+  to.init(tr_r, tr_c);
+
+  bf16x8 kf[D / 16], vf[KP / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    kf[dc] = key_ok ? *reinterpret_cast<const bf16x8*>(K + (size_t)krow * D + dc * 16 + h * 8) : bf16x8{};
+#pragma unroll
+  for (int kc = 0; kc < KP / 16; ++kc)
+    vf[kc] = key_ok ? *reinterpret_cast<const bf16x8*>(Vp + (size_t)krow * KP + kc * 16 + h * 8) : bf16x8{};
+  const float c2 = a.c2;
+
+  f32x16 dv[KP / 32], dk[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < KP / 32; ++cb) dv[cb] = f32x16{};
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dk[db] = f32x16{};
+
+  if (GEO && tid < kTile) {
+    rc.init();
+    rowtab[0][tid] = rc.row(tid);
+    rowtab[1][tid] = rc.row(kTile + tid);
+  }
+  __syncthreads();
+  if (ntiles > 0) {
+    sQ.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+    sO.template load_tile<GEO>(sm0 + QB, rowtab[0], 0, wave, lane);
+    if (wave == 0) {
+      if (GEO) sL.load_geo(ls0, rowtab[0][lane], lane);
+      else sL.load_dense(ls0, 0, lane);
+    }
+    if (wave == NW - 1) {
+      if (GEO) sD.load_geo(ds0, rowtab[0][lane], lane);
+      else sD.load_dense(ds0, 0, lane);
+    }
+  }
+  wait_loads();
+  __syncthreads();
+
+  // One tile = 64 query rows = two 32-row blocks qb.  Its MFMAs form four
+  // chains of L steps each, run as one software pipeline of 4L steps:
+  //   c = 0, 1: scores S = Q K^T and dP = dO V^T of block c (row reads);
+  //   c = 2, 3: dV += P^T dO and dK += dS^T Q of block c - 2 (transposed
+  //             reads), 2 (KP/32 + D/32) independent accumulators in turn.
+  // Operand reads run AH steps ahead of their MFMA (also across chain
+  // boundaries), and the softmax of block qb (P, dS and their bf16
+  // packing) is cut into slices spread over chain qb + 1, so that its VALU
+  // work issues while that chain's MFMAs execute.  Scheduling fences between
+  // steps keep this order.
+  constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB;
+  constexpr int NV = KP / 32, NK = D / 32, NVK = NV + NK;
+  constexpr int L = NA + NB;  // == 2 * NVK
+  static_assert(L == 2 * NVK, "chain lengths");
+  constexpr int U = 4 * L, AH = 3;
+  constexpr int SLICES = 12;  // 4 lse/D group reads, 8 element pairs
+  // Direct loads of the next tile, spread over the first half of the
+  // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
+  // The last tile loads a clamped (valid) copy into the idle buffer.
+  constexpr int NJQ = TileSrc<D, NW>::NJ, NJO = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJQ + NJO + 1, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane tile load offsets do not depend on the tile
+  int loff[NJQ + NJO];
+  static_for<NJQ + NJO>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJQ ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJQ);
+  });
+
+  // Two statically distinct buffers: the step that reads one fills the other.
+  auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
+                  float* dsn) {
+    char* Ot = Qt + QB;
+    f32x16 sc[2], dp[2];
+    bf16x8 pk[2][2], dk8[2][2];
+    f32x4 lg[4], dg[4];
+    sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+
+    auto operand = [&](const int u) -> bf16x8 {
+      const int c = u / L, j = u % L;
+      if (c < 2) {
+        if (j < 2 * PAIRS) return (j & 1) ? ro.read(Ot, c, j >> 1) : rq.read(Qt, c, j >> 1);
+        return NA > NB ? rq.read(Qt, c, j - PAIRS) : ro.read(Ot, c, j - PAIRS);
+      }
+      const int qb = c - 2, kk = j / NVK, m = j % NVK;
+      return m < NV ? to.frag(Ot, m, 2 * qb + kk) : tq.frag(Qt, m - NV, 2 * qb + kk);
+    };
+    auto mma_step = [&](const int u, const bf16x8& x) {
+      const int c = u / L, j = u % L;
+      if (c < 2) {
+        const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
+        const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
+        if (is_s) sc[c] = mma(x, kf[chunk], sc[c]);
+        else dp[c] = mma(x, vf[chunk], dp[c]);
+        return;
+      }
+      const int qb = c - 2, kk = j / NVK, m = j % NVK;
+      if (m < NV) dv[m] = mma(x, pk[qb][kk], dv[m]);
+      else dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
+    };
+    // Slice k of the softmax of block qb, in dependency order: the lse / D
+    // values of element group g (elements 4g .. 4g+3) are read two slices
+    // ahead of their use, and each element pair m (elements 2m, 2m+1 of
+    // group m / 2) computes P = exp2(S c2 - lse2), dS = P (dP - D) and
+    // packs both into their bf16 operands.
+    //   k:  0  1  2  3  4  5  6  7  8  9  10 11
+    //       r0 r1 p0 p1 r2 p2 p3 r3 p4 p5 p6 p7
+    auto slice = [&](const int qb, const int k) {
+      constexpr int kRead[4] = {0, 1, 4, 7};
+      if (k == kRead[0] || k == kRead[1] || k == kRead[2] || k == kRead[3]) {
+        const int g = k == kRead[0] ? 0 : k == kRead[1] ? 1 : k == kRead[2] ? 2 : 3;
+        lg[g] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * g);
+        dg[g] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * g);
+      } else {
+        const int m = k < 4 ? k - 2 : k < 7 ? k - 3 : k - 4;
+        const int i = 2 * m, g = i >> 2, e = i & 3;
+        const float p0 = fexp2(fmaf(sc[qb][i], c2, -lg[g][e]));
+        const float p1 = fexp2(fmaf(sc[qb][i + 1], c2, -lg[g][e + 1]));
+        put_pair(pk[qb][m >> 2], m & 3, p0, p1);
+        put_pair(dk8[qb][m >> 2], m & 3, p0 * (dp[qb][i] - dg[g][e]), p1 * (dp[qb][i + 1] - dg[g][e + 1]));
+      }
+    };
+    const int* rn = rowtab[b ^ 1];
+    const int row0n = (t + 1) * kTile;
+    const i32x4 winQ = GEO ? sQ.whole() : sQ.window(row0n), winO = GEO ? sO.whole() : sO.window(row0n);
+    int grow = -1;
+    auto load_row = [&](const int j) {  // geo phase 1
+      if (j < NJQ) grow = sQ.geo_row(rn, wave, lane, j);
+      else if (j < NJQ + NJO) grow = sO.geo_row(rn, wave, lane, j - NJQ);
+      else grow = rn[lane];
+    };
+    auto issue_load = [&](const int j) {
+      if (j < NJQ) {
+        if (GEO) sQ.load_geo(Qn, winQ, grow, wave, lane, j);
+        else sQ.load_dense_at(Qn, winQ, loff[j], wave, j);
+      } else if (j < NJQ + NJO) {
+        if (GEO) sO.load_geo(Qn + QB, winO, grow, wave, lane, j - NJQ);
+        else sO.load_dense_at(Qn + QB, winO, loff[j], wave, j - NJQ);
+      } else if (wave == 0) {
+        if (GEO) sL.load_geo(lsn, grow, lane);
+        else sL.load_dense(lsn, row0n, lane);
+      } else if (wave == NW - 1) {
+        if (GEO) sD.load_geo(dsn, grow, lane);
+        else sD.load_dense(dsn, row0n, lane);
+      }
+    };
+    auto side = [&](const int u) {
+      if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+      if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+        load_row((u + 2 - LOAD0) / LSTRIDE);
+      const int c = u / L, j = u % L;
+      if (c != 1 && c != 2) return;
+      static_for<SLICES>([&](auto k) {
+        if (k * L / SLICES == j) slice(c - 1, k);
+      });
+    };
+
+    bf16x8 ring[AH];
+    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    static_for<U>([&](auto u) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 cur = ring[u % AH];
+      if (u + AH < U) ring[u % AH] = operand(u + AH);
+      mma_step(u, cur);
+      side(u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+    wait_loads();
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+    step(t + 1, 1, sm1, sm0, ls1, ls0, ds1, ds0);
+  }
+  if (t < ntiles) step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+
+  if (key_ok) {
+    float* okr = a.dK + (size_t)krow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = db * 32 + 8 * g + 4 * h;
+        *reinterpret_cast<f32x4*>(okr + c) = f32x4{a.scale * dk[db][4 * g], a.scale * dk[db][4 * g + 1],
+                                                   a.scale * dk[db][4 * g + 2], a.scale * dk[db][4 * g + 3]};
+      }
+    }
+    float* ovr = a.dV + (size_t)krow * a.k;
+    const bool vec = (a.k & 3) == 0;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * h;
+        if (vec) {
+          if (c < a.k)
+            *reinterpret_cast<f32x4*>(ovr + c) = f32x4{dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) ovr[c + e] = dv[cb][4 * g + e];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tb
+
+// ---------------------------------------------------------------------------
+// instances and launchers
+// ---------------------------------------------------------------------------
+#define SSC_BF16_INSTANCES(X) \
+  X(128, 224)                 \
+  X(128, 256)                 \
+  X(128, 128)                 \
+  X(128, 64)                  \
+  X(128, 32)                  \
+  X(64, 224)                  \
+  X(64, 256)                  \
+  X(64, 128)                  \
+  X(64, 64)                   \
+  X(64, 32)
+
+hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                       \
+  if (D == DD && KP == KK) {                                                                                \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
+    return hipGetLastError();                                                                               \
+  }
+  SSC_BF16_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssc

@@ -1,0 +1,586 @@
+// bf16 forward and dQ kernels of the spatial-spectral coupling on gfx950
+// (project page "Spatial-Spectral Coupling as Attention", sections "How it
+// works" and "Geo-FlashAttention").  Built with MFMA results in VGPRs
+// (-mllvm -amdgpu-mfma-vgpr-form=1, see build.py): their softmax reads the
+// score accumulators with plain VALU instructions.
+#include "tile_bf16.hpp"
+
+namespace ssc {
+namespace tb {
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+// Exact sign flip of eight bf16 values.
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u16x8, x) ^ (unsigned short)0x8000);
+}
+
+// One wave owns 32 query rows (their Q fragments stay in registers); the
+// workgroup streams the key rows through LDS in tiles of 64.  A tile's MFMAs
+// form four chains run as one software pipeline:
+//   c = 0, 1: scores of key half c (keys 32c .. 32c+31), A = K rows;
+//   c = 2, 3: O += P V over key half c - 2, A = transposed V reads.
+// Operand reads run AH steps ahead of their MFMA.  The softmax of half 0
+// (row maximum, exp2, row sum, bf16 packing) runs in slices during chain 1,
+// that of half 1 during chain 2.  The next tile's direct loads are spread
+// over the first half of the pipeline; scheduling fences between steps keep
+// this order.
+//
+// Softmax reference: the probabilities of a tile are taken relative to a
+// reference fixed for the whole tile (the first tile: the maximum of its
+// first half; later tiles: the running reference), and the accumulators are
+// rescaled only between tiles, when the running maximum has moved more than
+// 8 (log2 units) above the reference.  A tile whose maximum exceeds its
+// reference by more than 32 could overflow; a workgroup that saw one redoes
+// its rows in a second pass with the exact row maxima of the first pass as a
+// fixed reference (probabilities <= 1), so the result is exact either way.
+template <int D, int KP, int NW, bool GEO>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
+  constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
+  __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
+  __shared__ int rowtab[2][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int q_begin, q_end;
+  RowCursor rc;
+  if (!GEO) {
+    q_begin = blockIdx.x * (NW * 32);
+    q_end = a.n_N;
+    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
+  } else {
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const Item it = a.items[blockIdx.x];
+    q_begin = a.offN[it.patch] + it.row0;
+    q_end = a.offN[it.patch + 1];
+    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
+    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
+  }
+  const int total = rc.total;
+  const int ntiles = (total + kTile - 1) / kTile;
+  // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
+  // a zero row at n_M)
+  TileSrc<D, NW> sK;
+  sK.init(a.Kp, a.n_M);
+  TileSrc<KP, NW> sV;
+  sV.init(a.Vp, a.n_M + 1);
+  const int row = q_begin + wave * 32 + l32;
+  const bool row_ok = row < q_end;
+
+  const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
+  RowReader<D> rk;
+  rk.init(l32, h);
+  TrReader<KP> tv;
+  tv.init(tr_r, tr_c);
+
+  // A negative scale is folded into Q (exact sign flip), so the reference is
+  // always a maximum.
+  const bool neg = a.c2 < 0.f;
+  const float c2 = neg ? -a.c2 : a.c2;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc) {
+    qf[dc] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
+    if (neg) qf[dc] = neg_bf16x8(qf[dc]);
+  }
+
+  f32x16 acc[KP / 32];
+  float m_run, l_run, m_true = -INFINITY;
+  bool fixed = false;
+
+  constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;
+  constexpr int C1 = NS, C2 = 2 * NS, C3 = 2 * NS + NPV, U = 2 * NS + 2 * NPV, AH = 5;
+  constexpr int SLICES = 10;  // 2 maximum, 8 element pairs
+  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane load offsets do not depend on the tile; kept in registers
+  int loff[NL];
+  static_for<NL>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+  });
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
+    l_run = 0.f;
+    m_run = fixed ? m_true : -INFINITY;
+    bool lagged = false;
+
+    if (GEO && tid < kTile) {
+      rc.init();
+      rowtab[0][tid] = rc.row(tid);
+      rowtab[1][tid] = rc.row(kTile + tid);
+    }
+    __syncthreads();
+    if (ntiles > 0) {
+      sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+      sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
+    }
+    wait_loads();
+    __syncthreads();
+
+    // Two statically distinct buffers: the step that reads one fills the
+    // other, so the compiler can tell the direct loads in flight from the LDS
+    // reads.  The stream's last tile may be partial: its keys at or past
+    // nvalid are masked (a wave-uniform branch inside the softmax slices).
+    auto step = [&](const int t, const int b, char* Kt, char* Kn) {
+      char* Vt = Kt + KB;
+      const int nvalid = total - t * kTile;
+      const bool part = nvalid < kTile;
+      const bool first = t == 0 && !fixed;
+      f32x16 sc[2];
+      float sv[2][16];
+      bf16x8 pf[2][2];
+      float mx[2], mh[2], mref = m_run, lsum = 0.f;
+      sc[0] = sc[1] = f32x16{};
+
+      auto operand = [&](const int u) -> bf16x8 {
+        if (u < C2) return rk.read(Kt, u / NS, u % NS);
+        const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
+        return tv.frag(Vt, j % NCB, 2 * hb + j / NCB);
+      };
+      auto mma_step = [&](const int u, const bf16x8& x) {
+        if (u < C2) {
+          sc[u / NS] = mma(x, qf[u % NS], sc[u / NS]);
+          return;
+        }
+        const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
+        acc[j % NCB] = mma(x, pf[hb][j / NCB], acc[j % NCB]);
+      };
+      auto valid = [&](const int hb, const int i) { return hb * 32 + c_row(i, h) < nvalid; };
+      // Slice k of the softmax of key half hb (the scores are copied once out
+      // of the MFMA accumulators into sv): 0, 1 copy and row maximum (the
+      // first tile takes its reference from half 0); 2..9 element pairs
+      // 2m, 2m+1 = 2(k-2) .. : exp2, row sum and packed bf16 probabilities.
+      auto slice = [&](const int hb, const int k) {
+        if (k <= 1) {
+          if (k == 0 && part) {
+            // masked keys get a score of -inf (the branch is kept: asm)
+            asm volatile("");
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[hb][i] = valid(hb, i) ? sc[hb][i] : -INFINITY;
+          } else if (!part) {
+#pragma unroll
+            for (int i = 8 * k; i < 8 * k + 8; ++i) sv[hb][i] = sc[hb][i];
+          }
+          float m = k == 0 ? -INFINITY : mx[hb];
+#pragma unroll
+          for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sv[hb][i]);
+          mx[hb] = m;
+          if (k == 1) {
+            float ml = m * c2;
+            ml = fmaxf(ml, xor32(ml));
+            mh[hb] = ml;
+            if (hb == 0) mref = first ? ml : m_run;
+          }
+        } else {
+          const int m = k - 2;
+          const float p0 = fexp2(fmaf(sv[hb][2 * m], c2, -mref));
+          const float p1 = fexp2(fmaf(sv[hb][2 * m + 1], c2, -mref));
+          lsum += p0 + p1;
+          put_pair(pf[hb][m >> 2], m & 3, p0, p1);
+        }
+      };
+      const int* rn = rowtab[b ^ 1];
+      const int row0n = (t + 1) * kTile;
+      const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
+      int grow = -1;
+      auto load_row = [&](const int j) {  // geo phase 1
+        grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+      };
+      auto issue_load = [&](const int j) {
+        if (j < NJK) {
+          if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+          else sK.load_dense_at(Kn, winK, loff[j], wave, j);
+        } else {
+          if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+          else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
+        }
+      };
+      auto side = [&](const int u) {
+        if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+        if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+          load_row((u + 2 - LOAD0) / LSTRIDE);
+        if (u >= C1 && u < C2) {
+          static_for<SLICES>([&](auto k) {
+            if (k * NS / SLICES == u - C1) slice(0, k);
+          });
+        } else if (u >= C2 && u < C3) {
+          static_for<SLICES>([&](auto k) {
+            if (k * NPV / SLICES == u - C2) slice(1, k);
+          });
+        }
+      };
+
+      bf16x8 ring[AH];
+      static_for<AH>([&](auto u) { ring[u] = operand(u); });
+      static_for<U>([&](auto u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 cur = ring[u % AH];
+        if (u + AH < U) ring[u % AH] = operand(u + AH);
+        mma_step(u, cur);
+        side(u);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+
+      // Between tiles: the sums of this tile join the running sum at the
+      // tile's reference; move the reference up when the maximum ran ahead.
+      l_run += lsum;
+      m_run = mref;
+      const float tmax = fmaxf(mh[0], mh[1]);
+      m_true = fmaxf(m_true, tmax);
+      lagged = lagged || tmax > mref + 32.f;
+      if (!fixed && __any(tmax > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = fexp2(m_run - m_new);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+      wait_loads();
+      __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, 0, sm0, sm1);
+      if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
+    }
+    if (fixed || !__syncthreads_or(lagged)) break;
+    fixed = true;
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    float* Orow = a.O + (size_t)row * a.k;
+    const bool vec = (a.k & 3) == 0;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * h;
+        if (vec) {
+          if (c < a.k)
+            *reinterpret_cast<f32x4*>(Orow + c) =
+                f32x4{acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) Orow[c + e] = acc[cb][4 * g + e] * inv;
+        }
+      }
+    }
+    if (h == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+// One wave owns 32 query rows (Q and dO fragments, lse and D in registers);
+// the workgroup streams key tiles of 64 rows.  Per key half h of tile t:
+//   A_h(t): scores and dP = dO V^T, A = K and V rows (two accumulations
+//           interleaved);
+//   B_h(t): dQ += dS K, A = transposed K fragments;
+// and between them the softmax (P = exp2(S c2 - lse2), dS = P (dP - D),
+// bf16 packing).  Iteration t runs A0(t), B1(t-1), A1(t), B0(t): B1 of the
+// previous tile uses transposed K fragments kept in registers, so every
+// softmax gets a window of a full A chain plus a B chain to hide in.
+template <int D, int KP, int NW, bool GEO>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
+  constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
+  __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
+  __shared__ int rowtab[2][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int q_begin, q_end;
+  RowCursor rc;
+  if (!GEO) {
+    q_begin = blockIdx.x * (NW * 32);
+    q_end = a.n_N;
+    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
+  } else {
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const Item it = a.items[blockIdx.x];
+    q_begin = a.offN[it.patch] + it.row0;
+    q_end = a.offN[it.patch + 1];
+    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
+    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
+  }
+  const int total = rc.total;
+  const int ntiles = (total + kTile - 1) / kTile;
+  // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
+  // a zero row at n_M)
+  TileSrc<D, NW> sK;
+  sK.init(a.Kp, a.n_M);
+  TileSrc<KP, NW> sV;
+  sV.init(a.Vp, a.n_M + 1);
+  const int row = q_begin + wave * 32 + l32;
+  const bool row_ok = row < q_end;
+
+  const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
+  const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
+  RowReader<D> rk;
+  rk.init(l32, h);
+  RowReader<KP> rv;
+  rv.init(l32, h);
+  TrReader<D> tk;
+  tk.init(tr_r, tr_c);
+
+  bf16x8 qf[D / 16], of[KP / 16];
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    qf[dc] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
+#pragma unroll
+  for (int kc = 0; kc < KP / 16; ++kc)
+    of[kc] = row_ok ? *reinterpret_cast<const bf16x8*>(dOp + (size_t)row * KP + kc * 16 + h * 8) : bf16x8{};
+  const float lse2 = row_ok ? a.lse2p[row] : INFINITY;
+  const float Dq = row_ok ? a.Dp[row] : 0.f;
+  const float c2 = a.c2;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  if (GEO && tid < kTile) {
+    rc.init();
+    rowtab[0][tid] = rc.row(tid);
+    rowtab[1][tid] = rc.row(kTile + tid);
+  }
+  __syncthreads();
+  if (ntiles > 0) {
+    sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
+    sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
+  }
+  wait_loads();
+  __syncthreads();
+
+  constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB, LA = NA + NB;
+  constexpr int NK = D / 32, LB = 2 * NK;
+  // chains of iteration t: A0(t) | B1(t-1) | A1(t) | B0(t)
+  constexpr int CY = LA, CZ = LA + LB, CW = 2 * LA + LB, U = 2 * LA + 2 * LB, AH = 5;
+  constexpr int SLICES = 8;  // element pairs
+  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
+  constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
+  // dense: the per-lane load offsets do not depend on the tile; kept in registers
+  int loff[NL];
+  static_for<NL>([&](auto j) {
+    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+  });
+  // position of softmax slice k of a half over its window
+  constexpr int WIN = LA + LB;
+
+  // Half 1 of the previous tile, finished in the next iteration: its scores
+  // and dP (slices still to run), its packed dS and its transposed K
+  // fragments.  Before the first tile they stand for an empty half: zero
+  // K fragments, and values whose remaining slices produce dS = 0 exactly
+  // (-inf scores; elements already past their slice hold 0), so the first
+  // iteration's B1 chain adds exactly 0.
+  f32x16 sc1, dp1;
+  bf16x8 ds1[2], kt[LB];
+  static_for<16>([&](auto ic) {
+    constexpr int i = ic, k = i / 2;
+    sc1[i] = k * WIN / SLICES < LB ? 0.f : -INFINITY;
+  });
+  dp1 = f32x16{};
+  ds1[0] = ds1[1] = bf16x8{};
+#pragma unroll
+  for (int j = 0; j < LB; ++j) kt[j] = bf16x8{};
+
+  // Slice k of the softmax of one half (scores sv, dP dv, packed dS out):
+  // element pair 2k, 2k+1 (P = exp2(S c2 - lse2), dS = P (dP - D)) packed
+  // into out; slice 0 first masks keys at or past nvalid (scores -inf, so
+  // P = dS = 0).
+  auto slice = [&](f32x16& sv, f32x16& dv, bf16x8* out, const int kb, const int k, const bool part,
+                   const int nvalid) {
+    if (k == 0 && part) {
+      asm volatile("");  // keeps the branch
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = kb * 32 + c_row(i, h) < nvalid ? sv[i] : -INFINITY;
+    }
+    const float d0 = fexp2(fmaf(sv[2 * k], c2, -lse2)) * (dv[2 * k] - Dq);
+    const float d1 = fexp2(fmaf(sv[2 * k + 1], c2, -lse2)) * (dv[2 * k + 1] - Dq);
+    put_pair(out[k >> 2], k & 3, d0, d1);
+  };
+
+  // Iteration t: the MFMAs of A0(t), B1(t-1), A1(t), B0(t) as one pipeline;
+  // the softmax of half 0 runs during B1(t-1) and A1(t), that of half 1
+  // during B0(t) and A0(t+1), so each has a 30-step window.  Two statically
+  // distinct buffers: the step that reads one fills the other.
+  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
+    char* Vt = Kt + KB;
+    const int nvalid = total - t * kTile;
+    const bool part = nvalid < kTile;
+    f32x16 sc0 = f32x16{}, dp0 = f32x16{};
+    bf16x8 ds0[2];
+
+    auto operand = [&](const int u) -> bf16x8 {
+      if (u < CY || (u >= CZ && u < CW)) {
+        const int kb = u < CY ? 0 : 1, j = u < CY ? u : u - CZ;
+        if (j < 2 * PAIRS) return (j & 1) ? rv.read(Vt, kb, j >> 1) : rk.read(Kt, kb, j >> 1);
+        return NA > NB ? rk.read(Kt, kb, j - PAIRS) : rv.read(Vt, kb, j - PAIRS);
+      }
+      if (u < CZ) return kt[u - CY];
+      const int j = u - CW;
+      return tk.frag(Kt, j % NK, j / NK);
+    };
+    auto mma_step = [&](const int u, const bf16x8& x) {
+      if (u < CY || (u >= CZ && u < CW)) {
+        const int j = u < CY ? u : u - CZ;
+        const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
+        const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
+        f32x16& sv = u < CY ? sc0 : sc1;
+        f32x16& dv = u < CY ? dp0 : dp1;
+        if (is_s) sv = mma(x, qf[chunk], sv);
+        else dv = mma(x, of[chunk], dv);
+        return;
+      }
+      const int j = u < CZ ? u - CY : u - CW;
+      dq[j % NK] = mma(x, u < CZ ? ds1[j / NK] : ds0[j / NK], dq[j % NK]);
+    };
+    const int* rn = rowtab[b ^ 1];
+    const int row0n = (t + 1) * kTile;
+    const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
+    int grow = -1;
+    auto load_row = [&](const int j) {  // geo phase 1
+      grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+    };
+    auto issue_load = [&](const int j) {
+      if (j < NJK) {
+        if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+        else sK.load_dense_at(Kn, winK, loff[j], wave, j);
+      } else {
+        if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+        else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
+      }
+    };
+    auto side = [&](const int u) {
+      if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
+      if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
+        load_row((u + 2 - LOAD0) / LSTRIDE);
+      if (u < CY) {
+        // half 1 of the previous tile: window positions LB .. WIN-1
+        static_for<SLICES>([&](auto k) {
+          if (k * WIN / SLICES >= LB && k * WIN / SLICES - LB == u) slice(sc1, dp1, ds1, 1, k, false, kTile);
+        });
+      } else if (u < CW) {
+        // half 0 of this tile: window positions 0 .. WIN-1 over B1 and A1
+        static_for<SLICES>([&](auto k) {
+          if (k * WIN / SLICES == u - CY) slice(sc0, dp0, ds0, 0, k, part, nvalid);
+        });
+      } else {
+        // half 1 of this tile, window positions 0 .. LB-1; and its K^T
+        // fragments for the B1 chain of the next iteration
+        static_for<SLICES>([&](auto k) {
+          if (k * WIN / SLICES < LB && k * WIN / SLICES == u - CW) slice(sc1, dp1, ds1, 1, k, part, nvalid);
+        });
+        const int j = u - CW;
+        kt[j] = tk.frag(Kt, j % NK, 2 + j / NK);
+      }
+    };
+    auto pre = [&](const int u) {
+      if (u == CZ) {  // A1(t) starts: fresh accumulators for half 1
+        sc1 = f32x16{};
+        dp1 = f32x16{};
+      }
+    };
+
+    bf16x8 ring[AH];
+    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    static_for<U>([&](auto u) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 cur = ring[u % AH];
+      if (u + AH < U) ring[u % AH] = operand(u + AH);
+      pre(u);
+      mma_step(u, cur);
+      side(u);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+    wait_loads();
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, 0, sm0, sm1);
+    if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
+  }
+  // drain: the rest of the last tile's half-1 softmax, then its B1 chain
+  static_for<SLICES>([&](auto k) {
+    if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, 1, k, false, kTile);
+  });
+  static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
+
+  if (row_ok) {
+    float* out = a.dQ + (size_t)row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = db * 32 + 8 * g + 4 * h;
+        *reinterpret_cast<f32x4*>(out + c) = f32x4{a.scale * dq[db][4 * g], a.scale * dq[db][4 * g + 1],
+                                                   a.scale * dq[db][4 * g + 2], a.scale * dq[db][4 * g + 3]};
+      }
+    }
+  }
+}
+
+}  // namespace tb
+
+// ---------------------------------------------------------------------------
+// instances and launchers
+// ---------------------------------------------------------------------------
+#define SSC_BF16_INSTANCES(X) \
+  X(128, 224)                 \
+  X(128, 256)                 \
+  X(128, 128)                 \
+  X(128, 64)                  \
+  X(128, 32)                  \
+  X(64, 224)                  \
+  X(64, 256)                  \
+  X(64, 128)                  \
+  X(64, 64)                   \
+  X(64, 32)
+
+hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                       \
+  if (D == DD && KP == KK) {                                                                                \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+    return hipGetLastError();                                                                               \
+  }
+  SSC_BF16_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                       \
+  if (D == DD && KP == KK) {                                                                                \
+    if (a.items != nullptr)                                                                                 \
+      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+    return hipGetLastError();                                                                               \
+  }
+  SSC_BF16_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssc

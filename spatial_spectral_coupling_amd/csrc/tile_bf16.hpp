@@ -1,0 +1,313 @@
+// Tile machinery shared by the bf16 block kernels of the spatial-spectral
+// coupling on gfx950 (attn_bf16_q.hip: forward and dQ; attn_bf16_kv.hip:
+// dK / dV).
+//
+// Same mathematics as attn.hip (forward with online softmax; dQ pass; dK/dV
+// pass; project page "Spatial-Spectral Coupling as Attention", sections
+// "How it works" and "Geo-FlashAttention"), with a data movement built for
+// CDNA4:
+//  * tiles of 64 streamed rows are copied global -> LDS with direct buffer
+//    loads (16 bytes per lane) into one of two statically distinct buffers,
+//    spread over the MFMA pipeline of the tile before;
+//  * only row-layout tiles are staged.  Operands whose contraction runs along
+//    the tile's rows (V^T in the forward, K^T in dQ, Q^T and dO^T in dK/dV)
+//    are read with ds_read_b64_tr_b16: in a 16-lane group, lane j addresses
+//    row r0 + j/4, columns c0 + 4(j%4) .. +3, and lane i receives rows
+//    r0..r0+3 of column c0 + i -- four k-elements of an MFMA operand;
+//  * rows are gathered one by one from the caller's arrays, so the geo
+//    support (concatenated source patches) needs no padding: a tile may span
+//    several patches and only the stream's last tile is partial;
+//  * LDS rows carry pad chunks so that row-fragment reads (32 rows, one
+//    chunk) and transposed reads (4 rows x 32 bytes per 16 lanes) spread
+//    over the banks with purely affine addresses.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace ssc {
+namespace tb {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time
+// (no loop for the unroller to give up on; every index is a constant).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// Row pitch (in 16-byte chunks) of an LDS tile with cw data chunks per row:
+// the smallest cw + e (e >= 1) such that
+//  * the pitch is an odd number of chunks -- 16 consecutive rows of a
+//    row-fragment read (16 bytes per lane) then start in 16 distinct
+//    16-byte bank groups of the 256-byte bank window;
+//  * the 4 rows x 32 bytes of a 16-lane transposed read are pairwise
+//    disjoint modulo the bank window.
+// Measured on gfx950 (512 threads per CU): row-fragment reads run at about
+// 195 B/clk per CU with such a pitch and at half that with an even one;
+// transposed reads at about 104 B/clk per CU.
+constexpr bool tr_rows_disjoint(int pitch_bytes) {
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b) {
+      const int d = ((b - a) * pitch_bytes) % 256;
+      if (d < 32 || d > 256 - 32) return false;
+    }
+  return true;
+}
+constexpr int tile_pitch_chunks(int cw) {
+  int p = cw + 1;
+  while (!((p & 1) && tr_rows_disjoint(p * 16))) ++p;
+  return p;
+}
+
+// Geometry of a 64-row tile of W bf16 columns: CW data chunks of 16 bytes per
+// row, stored with a pitch of CP chunks; every LDS address of a lane stays a
+// per-lane base plus a compile-time offset.
+template <int W>
+struct Geo {
+  static constexpr int CW = W / 8;
+  static constexpr int CP = tile_pitch_chunks(CW);
+  static constexpr int PITCH = CP * 16;           // bytes per row
+  static constexpr int BYTES = kTile * PITCH;
+  static constexpr int SLOTS = kTile * CP;        // 16-byte slots, a multiple of 64
+};
+static_assert(Geo<128>::CP == 19 && Geo<224>::CP == 29 && Geo<64>::CP == 9, "tile pitch");
+
+// Row-fragment reads for MFMA operands: rows rb*32 + l32, chunk 2*cc + h.
+template <int W>
+struct RowReader {
+  int lane_off;
+  __device__ __forceinline__ void init(int l32, int h) { lane_off = l32 * Geo<W>::PITCH + h * 16; }
+  __device__ __forceinline__ bf16x8 read(const char* tile, int rb, int cc) const {
+    return *reinterpret_cast<const bf16x8*>(tile + lane_off + rb * 32 * Geo<W>::PITCH + cc * 32);
+  }
+};
+
+// Transposed-operand reads with ds_read_b64_tr_b16: rows kc*16 + tr_r and
+// kc*16 + 8 + tr_r, columns cb*32 + tr_c .. +3 (tr_r = 4h + (i>>2),
+// tr_c = 16(G&1) + 4(i&3) for lane i of 16-lane group G), giving the 8
+// k-elements rows kc*16 + {4h..4h+3, 8+4h..8+4h+3} of column cb*32 + l32.
+template <int W>
+struct TrReader {
+  int lane_off;
+  __device__ __forceinline__ void init(int tr_r, int tr_c) { lane_off = tr_r * Geo<W>::PITCH + tr_c * 2; }
+  __device__ __forceinline__ bf16x8 frag(const char* tile, int cb, int kc) const {
+    const char* base = tile + lane_off + cb * 64 + kc * 16 * Geo<W>::PITCH;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(base + 8 * Geo<W>::PITCH));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// Elements 2m, 2m+1 of a bf16 operand fragment from two fp32 values (one
+// packed conversion, round to nearest even).
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void put_pair(bf16x8& v, int m, float a, float b) {
+  u32x4 w = __builtin_bit_cast(u32x4, v);
+  w[m] = __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
+  v = __builtin_bit_cast(bf16x8, w);
+}
+
+// Eight probabilities (C-layout elements i0..i0+7) as a bf16 operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& c, int i0) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)c[i0 + j];
+  return r;
+}
+
+// Buffer resource of a global array (base, byte size): raw buffer loads
+// take a 32-bit byte offset from it and return zero outside the range.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;  // raw 32-bit data format (gfx9)
+  return r;
+}
+
+// Direct buffer load of `size` bytes per lane into LDS at lds + 4 * lane
+// (size 4) or lds + 16 * lane (size 16).
+extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds,
+                                                   int size, int voffset, int soffset, int offset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Division of a tile slot index s < 64 CP by the constant CP as a 24-bit
+// multiply and shift (checked exhaustively at compile time).
+constexpr unsigned slot_magic(int cp) { return (1u << 20) / (unsigned)cp + 1u; }
+constexpr bool slot_magic_exact(int cp) {
+  for (unsigned s = 0; s < 64u * (unsigned)cp; ++s)
+    if (((s * slot_magic(cp)) >> 20) != s / (unsigned)cp) return false;
+  return true;
+}
+
+// Direct loads of 64-row tiles of one source array (row-major, W bf16 or
+// W / 2 fp32 columns, `limit` rows present) into LDS.  Slot s of a tile (16
+// bytes at s * 16) is tile row r = s / CP, chunk s - r CP; the pad chunks
+// of a row fetch the first chunks of the next row (never read).  The j-th
+// load of a wave is tile instruction wave + j * NW.
+//  * dense tiles are windows of consecutive rows: a buffer resource based at
+//    the tile's first row and bounded by the array's end (rows past it read
+//    zeros), so a lane's byte offset is the tile-independent 16 (s - r PADC);
+//  * geo tiles gather rows listed in an LDS table: phase 1 fetches this
+//    lane's row from the table, phase 2 (a few pipeline steps later) issues
+//    the load; a missing row reads past the end of the array (zeros).
+template <int W, int NW>
+struct TileSrc {
+  static constexpr int CP = Geo<W>::CP, CW = Geo<W>::CW, RB = 2 * W;
+  static constexpr int NI = Geo<W>::SLOTS / 64;      // instructions per tile
+  static constexpr int NJ = (NI + NW - 1) / NW;      // per wave (at most)
+  static constexpr unsigned MAGIC = slot_magic(CP);
+  static_assert(slot_magic_exact(CP), "slot division");
+
+  const char* base;
+  int limit;
+
+  __device__ __forceinline__ void init(const void* b, int lim) {
+    base = reinterpret_cast<const char*>(b);
+    limit = lim;
+  }
+  __device__ __forceinline__ static bool present(int wave, int j) {
+    return NJ * NW == NI || j < NJ - 1 || wave + j * NW < NI;
+  }
+  __device__ __forceinline__ static int slot(int wave, int lane, int j) { return (wave + j * NW) * 64 + lane; }
+  __device__ __forceinline__ static int slot_row(int s) { return (int)(__umul24((unsigned)s, MAGIC) >> 20); }
+  __device__ __forceinline__ i32x4 window(int row0) const {
+    const int n = limit - row0;
+    return make_rsrc(base + (size_t)row0 * RB, n > 0 ? (unsigned)(n * RB) : 0u);
+  }
+  __device__ __forceinline__ i32x4 whole() const { return make_rsrc(base, (unsigned)(limit * RB)); }
+
+  // byte offset of this lane's chunk within a dense window (tile-independent)
+  __device__ __forceinline__ static int dense_offset(int wave, int lane, int j) {
+    const int s = slot(wave, lane, j);
+    return (s - slot_row(s) * (CP - CW)) * 16;
+  }
+  __device__ __forceinline__ static void load_dense(char* tile, const i32x4& win, int wave, int lane, int j) {
+    if (!present(wave, j)) return;  // wave-uniform
+    asm volatile("" : "+v"(lane));
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, dense_offset(wave, lane, j), 0,
+                            0, 0);
+  }
+  // the same with the offset computed once outside the tile loop
+  __device__ __forceinline__ static void load_dense_at(char* tile, const i32x4& win, int off, int wave, int j) {
+    if (!present(wave, j)) return;
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
+  }
+  __device__ __forceinline__ static int geo_row(const int* rows, int wave, int lane, int j) {
+    if (!present(wave, j)) return -1;
+    asm volatile("" : "+v"(lane));
+    return rows[slot_row(slot(wave, lane, j))];
+  }
+  __device__ __forceinline__ void load_geo(char* tile, const i32x4& all, int grow, int wave, int lane, int j) const {
+    if (!present(wave, j)) return;
+    asm volatile("" : "+v"(lane));
+    const int s = slot(wave, lane, j);
+    const int r = slot_row(s);
+    const int off = grow < 0 ? limit * RB : grow * RB + (s - r * CP) * 16;
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
+  }
+  // The whole tile at once (first tile of a stream).
+  template <bool GEO>
+  __device__ __forceinline__ void load_tile(char* tile, const int* rows, int row0, int wave, int lane) const {
+    const i32x4 rs = GEO ? whole() : window(row0);
+    static_for<NJ>([&](auto j) {
+      if (GEO) load_geo(tile, rs, geo_row(rows, wave, lane, j), wave, lane, j);
+      else load_dense(tile, rs, wave, lane, j);
+    });
+  }
+};
+
+// 64 fp32 values of a per-row vector (`limit` entries) for the rows of a
+// tile: dense row0 + lane, geo the table row (missing rows read zero).
+struct VecSrc {
+  const float* base;
+  int limit;
+  __device__ __forceinline__ void init(const float* b, int lim) {
+    base = b;
+    limit = lim;
+  }
+  __device__ __forceinline__ void load_dense(float* dst, int row0, int lane) const {
+    const int n = limit - row0;
+    const i32x4 win = make_rsrc(base + row0, n > 0 ? (unsigned)(n * 4) : 0u);
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
+  }
+  __device__ __forceinline__ void load_geo(float* dst, int grow, int lane) const {
+    const i32x4 all = make_rsrc(base, (unsigned)(limit * 4));
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)dst, 4, grow < 0 ? limit * 4 : grow * 4, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Depth of the operand-read pipelines (reads issued this many MFMAs ahead).
+constexpr int kAhead = 4;
+
+// Scheduling hints for the instruction scheduler (groups are filled in
+// order within the current scheduling region): R DS reads first, then
+// (1 MFMA, R/NA... ) pairs -- a pipelined chain of n MFMAs whose operand
+// reads (rpm reads per MFMA) run `ahead` MFMAs in front of their use.
+constexpr int kMaskMFMA = 0x008, kMaskDSRead = 0x100;
+template <int N, int RPM, int AHEAD>
+__device__ __forceinline__ void pipeline_hint() {
+  __builtin_amdgcn_sched_group_barrier(kMaskDSRead, RPM * AHEAD, 0);
+#pragma unroll
+  for (int j = 0; j < N - AHEAD; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kMaskMFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMaskDSRead, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMaskMFMA, AHEAD, 0);
+}
+
+// Position -> row cursor over a run stream (one per thread; positions of a
+// thread only grow).  Run r covers positions [pf[r], pf[r+1]) and starts at
+// global row start(r).  Dense: one run of `total` rows starting at row 0.
+struct RowCursor {
+  const int* pf;       // nullptr = dense
+  const int* list;     // run r -> patch
+  const int* off;      // patch -> first row
+  int nruns, total;
+  int r, next, base;   // current run, its end position, row - position
+
+  __device__ __forceinline__ void init() {
+    r = 0;
+    if (pf == nullptr) {
+      next = total;
+      base = 0;
+      return;
+    }
+    next = nruns > 0 ? pf[1] : 0;
+    base = nruns > 0 ? off[list[0]] - pf[0] : 0;
+  }
+  __device__ __forceinline__ int row(int x) {
+    if (x >= total) return -1;
+    if (pf != nullptr) {
+      while (x >= next) {
+        ++r;
+        next = pf[r + 1];
+        base = off[list[r]] - pf[r];
+      }
+    }
+    return base + x;
+  }
+};
+
+}  // namespace tb
+}  // namespace ssc
