@@ -15,7 +15,9 @@ What it computes (spatial-spectral-attention.github.io, "How it works" and
 * Geo-FlashAttention: per-shape patches -> patch-mean descriptors ->
   patch scores -> top-s source patches per target patch -> the exact softmax
   of each target row restricted to the union of its selected source patches;
-  forward and backward for the fixed selection.
+  forward and backward for the fixed selection;
+* the linear-attention (ELU feature map) coupling, the pages' linearized
+  baseline (`oracle.linear`), forward and backward.
 
 Every function is the plain definition, written out in fp64 with NumPy; a
 pure-Python brute force (`oracle.brute`) covers tiny inputs.  Parity status:
@@ -26,7 +28,9 @@ library routines, finite differences) -- none is "parity unpinned".
 from .dense import upcast, dense_fwd, dense_bwd, dense_rows, rowdot
 from .geo import (patch_means, patch_scores, topk, cut_gaps, geo_support,
                   geo_fwd, geo_bwd, executed_pairs)
+from .linear import elu1, elu1_grad, linear_fwd, linear_bwd, linear_weights
 
 __all__ = ["upcast", "dense_fwd", "dense_bwd", "dense_rows", "rowdot",
            "patch_means", "patch_scores", "topk", "cut_gaps", "geo_support",
-           "geo_fwd", "geo_bwd", "executed_pairs"]
+           "geo_fwd", "geo_bwd", "executed_pairs",
+           "elu1", "elu1_grad", "linear_fwd", "linear_bwd", "linear_weights"]
