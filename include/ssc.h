@@ -65,7 +65,9 @@ typedef enum {
   SSC_OP_DENSE_BWD = 1,
   SSC_OP_PATCH_TOPK = 2,
   SSC_OP_GEO_FWD = 3,
-  SSC_OP_GEO_BWD = 4
+  SSC_OP_GEO_BWD = 4,
+  SSC_OP_LINEAR_FWD = 5,
+  SSC_OP_LINEAR_BWD = 6
 } ssc_op;
 
 typedef void* ssc_stream; /* hipStream_t */
@@ -148,6 +150,39 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
                             const float* O, const void* dO, const float* lse,
                             float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
                             ssc_stream stream);
+
+/*
+ * Linear-attention (ELU feature map) coupling: the linearized baseline the
+ * pages compare against (ai4snews digest, "Interpretation"; project page,
+ * "Runtime and memory", Table 1 row "Linear attention (ELU)"), with the
+ * softmax replaced by phi(x) = elu(x) + 1 on the raw descriptors:
+ *   den[i]  = sum_j phi(Q[i]).phi(K[j]),
+ *   O[i, :] = sum_j phi(Q[i]).phi(K[j]) V[j, :] / den[i],
+ * evaluated in O(n (d + k)) as phi(Q) (phi(K)^T V) / (phi(Q) phi(K)^T 1).
+ * bf16 inputs only (SSC_F32 -> SSC_ERR_UNSUPPORTED); d in {64, 128};
+ * 1 <= k <= 255 (one padded column carries the normaliser); n_M >= 1;
+ * n_N = 0 is a no-op.  Q [n_N x d], K [n_M x d], V [n_M x k] bf16; O
+ * [n_N x k] and den [n_N] fp32.
+ */
+ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                               const void* Q, const void* K, const void* V,
+                               float* O, float* den, void* ws, size_t ws_bytes,
+                               ssc_stream stream);
+
+/*
+ * Linear-coupling backward: gradients of <dO, O> for the coupling above.
+ * O and den are the forward's outputs for the same inputs; dO [n_N x k] bf16.
+ * With g = dO / den, s = (dO . O) / den (per row):
+ *   dQ = phi'(Q) * (g (phi(K)^T V)^T - s (phi(K)^T 1)^T),
+ *   dK = phi'(K) * (V (phi(Q)^T g)^T - 1 (phi(Q)^T s)^T),
+ *   dV = phi(K) (phi(Q)^T g).
+ * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ */
+ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                               const void* Q, const void* K, const void* V,
+                               const float* O, const void* dO, const float* den,
+                               float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                               ssc_stream stream);
 
 /* Static text for a status code. */
 const char* ssc_status_string(ssc_status status);

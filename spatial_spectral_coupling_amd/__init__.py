@@ -30,13 +30,15 @@ __all__ = [
     "CouplingError", "KernelTimer", "lib", "library_path", "workspace_bytes", "kpad",
     "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
+    "coupling_linear_fwd", "coupling_linear_bwd", "linear_coupling",
     "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
+    "OP_LINEAR_FWD", "OP_LINEAR_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libssc.so")
 
-OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD = range(5)
+OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD = range(7)
 _F32, _BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
            4: "HIP launch failed"}
@@ -70,6 +72,9 @@ _SIGS = {
                               _vp, _vp, _sz, _vp]),
     "coupling_geo_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_linear_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_linear_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                 _vp]),
 }
 
 
@@ -328,3 +333,57 @@ def geo_coupling(Q, K, V, offN, offM, s: int, scale: Optional[float] = None):
     """Differentiable Geo-FlashAttention coupling; selection recomputed per call."""
     idx = patch_score_topk(Q.detach(), offN, K.detach(), offM, s)
     return _Geo.apply(Q, K, V, offN, offM, idx, _scale(scale, Q.shape[1]))
+
+
+# ---------------------------------------------------------------------------
+# linear-attention (ELU feature map) coupling
+# ---------------------------------------------------------------------------
+def coupling_linear_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = phi(Q)(phi(K)^T V) / (phi(Q) phi(K)^T 1), phi = elu + 1 (bf16 in, fp32
+    out), and the per-row normaliser den."""
+    dev = _check_dev(Q, K, V)
+    code = _same_dtype(Q, K, V)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    if K.shape != (n_M, d):
+        raise ValueError("K must be n_M x d")
+    O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
+    den = torch.empty(n_N, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_LINEAR_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_linear_fwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(O), _p(den), _p(ws),
+          ws.numel(), _stream(dev))
+    return O, den
+
+
+def coupling_linear_bwd(Q, K, V, O, dO, den):
+    """dQ, dK, dV (fp32) of <dO, O> for the linear coupling."""
+    dev = _check_dev(Q, K, V, O, dO, den)
+    code = _same_dtype(Q, K, V, dO)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
+    dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_LINEAR_BWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_linear_bwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(O), _p(dO), _p(den),
+          _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
+    return dQ, dK, dV
+
+
+class _LinearCoupling(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V):
+        O, den = coupling_linear_fwd(Q, K, V)
+        ctx.save_for_backward(Q, K, V, O, den)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, O, den = ctx.saved_tensors
+        dQ, dK, dV = coupling_linear_bwd(Q, K, V, O, dO.to(Q.dtype).contiguous(), den)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype)
+
+
+def linear_coupling(Q, K, V):
+    """Differentiable linear-attention coupling (autograd wrapper)."""
+    return _LinearCoupling.apply(Q, K, V)

@@ -241,6 +241,47 @@ ssc_status check_patches(int n_N, int P_N, int n_M, int P_M, int s) {
   return SSC_OK;
 }
 
+// Linear coupling: bf16 only, one spare padded column for the normaliser.
+int kpad_lin(int k) { return kpad_for(k + 1); }
+
+ssc_status check_linear(ssc_dtype t, int n_N, int n_M, int d, int k) {
+  if (t != SSC_F32 && t != SSC_BF16) return SSC_ERR_INVALID_ARG;
+  if (n_N < 0 || n_M < 1 || d < 1 || k < 1) return SSC_ERR_INVALID_ARG;
+  if (t != SSC_BF16 || (d != 64 && d != 128) || kpad_lin(k) == 0) return SSC_ERR_UNSUPPORTED;
+  return SSC_OK;
+}
+
+struct LinLayout {
+  size_t part = kNone, M = kNone, MT = kNone, dM = kNone, dMT = kNone, rden = kNone, s = kNone;
+  size_t total = 0;
+  int parts_M = 0, parts_N = 0;
+};
+
+LinLayout make_lin_layout(bool bwd, int n_N, int n_M, int d, int k) {
+  LinLayout L;
+  const size_t KP = (size_t)kpad_lin(k);
+  L.parts_M = (n_M + kLinGramRows - 1) / kLinGramRows;
+  L.parts_N = (n_N + kLinGramRows - 1) / kLinGramRows;
+  const int parts = bwd ? (L.parts_M > L.parts_N ? L.parts_M : L.parts_N) : L.parts_M;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = round_up(o + bytes, 256);
+    return at_;
+  };
+  L.part = take((size_t)parts * d * KP * 4);
+  L.M = take((size_t)d * KP * 2);
+  L.MT = take((size_t)d * KP * 2);
+  if (bwd) {
+    L.dM = take((size_t)d * KP * 2);
+    L.dMT = take((size_t)d * KP * 2);
+    L.rden = take((size_t)n_N * 4 + 4);
+    L.s = take((size_t)n_N * 4 + 4);
+  }
+  L.total = o;
+  return L;
+}
+
 ssc_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
   if (L.total == 0) return SSC_OK;
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
@@ -268,6 +309,10 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
       if (d != 64 && d != 128) return 0;
       if (check_patches(n_N, P_N, n_M, P_M, s) != SSC_OK) return 0;
       break;
+    case SSC_OP_LINEAR_FWD:
+    case SSC_OP_LINEAR_BWD:
+      if (check_linear(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
+      return make_lin_layout(op == SSC_OP_LINEAR_BWD, n_N, n_M, d, k).total;
     default:
       return 0;
   }
@@ -662,6 +707,65 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.poffM = poffM;
   b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.poffN = poffN; b.offN = offN;
   SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG + P_M, hs); }));
+  return SSC_OK;
+}
+
+ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                               const void* V, float* O, float* den, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, O, den})) return SSC_ERR_INVALID_ARG;
+  const LinLayout L = make_lin_layout(false, n_N, n_M, d, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
+  const Buf bO{O, (size_t)n_N * k * 4}, bd{den, (size_t)n_N * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bO, bd, bw}, {bQ, bK, bV})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_lin(k);
+  LinArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.den = den;
+  a.part = at<float>(ws, L.part); a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT);
+  a.n_N = n_N; a.n_M = n_M; a.k = k;
+  SSC_TRY(timed("lin_gram", s, [&] { return launch_lin_gram(d, KP, 0, a, L.parts_M, s); }));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), s));
+  SSC_TRY(timed("lin_apply", s, [&] { return launch_lin_apply(d, KP, 0, a, s); }));
+  return SSC_OK;
+}
+
+ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                               const void* V, const float* O, const void* dO, const float* den, float* dQ,
+                               float* dK, float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, O, dO, den, dQ, dK, dV})) return SSC_ERR_INVALID_ARG;
+  const LinLayout L = make_lin_layout(true, n_N, n_M, d, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
+  const Buf bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * 2}, bd{den, (size_t)n_N * 4};
+  const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
+  const Buf bw{ws, ws_bytes};
+  if (!disjoint({bdQ, bdK, bdV, bw}, {bQ, bK, bV, bO, bdO, bd})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_lin(k);
+  LinArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.O = const_cast<float*>(O); a.den = const_cast<float*>(den);
+  a.rden = at<float>(ws, L.rden); a.s = at<float>(ws, L.s); a.part = at<float>(ws, L.part);
+  a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT); a.dM = at<char>(ws, L.dM); a.dMT = at<char>(ws, L.dMT);
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.n_N = n_N; a.n_M = n_M; a.k = k;
+  SSC_TRY(launch_lin_gram(d, KP, 0, a, L.parts_M, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), s));
+  SSC_TRY(launch_lin_rowprep(a, s));
+  SSC_TRY(launch_lin_apply(d, KP, 1, a, s));
+  SSC_TRY(launch_lin_gram(d, KP, 1, a, L.parts_N, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), s));
+  SSC_TRY(launch_lin_apply(d, KP, 2, a, s));
   return SSC_OK;
 }
 

@@ -150,6 +150,29 @@ struct TopkArgs {
   double* scores;       // optional
 };
 
+// Linear-attention (ELU feature map) coupling: one argument block for all
+// of its kernels.
+constexpr int kLinGramRows = 512;  // rows per workgroup of the Gram sums
+struct LinArgs {
+  const void* Q;        // [n_N x D] bf16
+  const void* K;        // [n_M x D] bf16
+  const void* V;        // [n_M x k] bf16
+  const void* dO;       // [n_N x k] bf16 (backward)
+  float* O;             // [n_N x k] (forward output; backward input)
+  float* den;           // [n_N]     (forward output; backward input)
+  float* rden;          // [n_N]     1 / den (backward scratch)
+  float* s;             // [n_N]     (dO . O) / den (backward scratch)
+  float* part;          // [nparts x D x KP] Gram partials (scratch)
+  const void* M;        // [D x KP]  bf16 KVz_ext (row-major)
+  const void* MT;       // [KP x D]  bf16 KVz_ext^T
+  const void* dM;       // [D x KP]  bf16 dKVz_ext
+  const void* dMT;      // [KP x D]  bf16 dKVz_ext^T
+  float* dQ;            // [n_N x D]
+  float* dK;            // [n_M x D]
+  float* dV;            // [n_M x k]
+  int n_N, n_M, k;
+};
+
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
 hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
@@ -162,5 +185,9 @@ hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_lin_gram(int D, int KP, int mode, const LinArgs& a, int grid, hipStream_t st);
+hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, hipStream_t st);
+hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st);
+hipError_t launch_lin_apply(int D, int KP, int mode, const LinArgs& a, hipStream_t st);
 
 }  // namespace ssc

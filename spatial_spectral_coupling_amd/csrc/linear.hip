@@ -1,0 +1,434 @@
+// Linear-attention (ELU feature map) coupling on gfx950: the pages'
+// linearized baseline, which replaces the softmax by the feature map
+// phi(x) = elu(x) + 1 (ai4snews digest, "Interpretation"; project page,
+// "Runtime and memory", Table 1 row "Linear attention (ELU)"):
+//
+//   KV = phi(K)^T V,  z = phi(K)^T 1,  den_i = phi(q_i).z,
+//   O_i = phi(q_i) KV / den_i.
+//
+// Both products with the d x k matrices are done on bf16 MFMA with the
+// normaliser folded in: the source rows are extended by a constant column
+// (V_ext = [V | 1] at column kp-1), so one Gram product gives KV and z
+// together, and one row product gives phi(q_i) KV and den_i together.  The
+// backward uses the same folding:
+//   g_i = dO_i / den_i, s_i = (dO_i . O_i) / den_i, G_ext = [g | -s],
+//   dA = G_ext KVz_ext^T (gradient w.r.t. phi(Q)), dQ = phi'(Q) * dA,
+//   dKVz_ext = phi(Q)^T G_ext = [dKV | dz],
+//   dK = phi'(K) * (V_ext dKVz_ext^T), dV = phi(K) dKV.
+// Everything is O(n (d + k)) memory traffic: the kernels are HBM / latency
+// bound; the Gram sums are split over row blocks and reduced in a fixed
+// order (deterministic).
+#include "tile_bf16.hpp"
+
+namespace ssc {
+namespace lin {
+
+using tb::Geo;
+using tb::put_pair;
+using tb::RowReader;
+using tb::static_for;
+using tb::TrReader;
+
+constexpr int kGramTile = 128;  // rows per LDS tile of the Gram kernel
+constexpr int kApplyRows = 128; // rows per workgroup of the row kernels (4 waves x 32)
+
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Eight consecutive elements c0 .. c0+7 of a row of width w (elements past w
+// read as 0); vector load when the row stride allows it.
+__device__ __forceinline__ void row8(const bf16* row, int c0, int w, bool vec, float* out) {
+  if (vec && c0 + 8 <= w) {
+    const bf16x8 v = ld8(row + c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = c0 + e < w ? (float)row[c0 + e] : 0.f;
+  }
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) put_pair(r, m, v[2 * m], v[2 * m + 1]);
+  return r;
+}
+
+// Copy a row-major bf16 matrix [rows x W] (global, unpadded) into an LDS
+// tile with the padded pitch of Geo<W>.
+template <int W>
+__device__ __forceinline__ void stage_matrix(char* lds, const bf16* g, int rows, int tid) {
+  constexpr int CW = W / 8;
+  for (int ch = tid; ch < rows * CW; ch += 256) {
+    const int r = ch / CW, c = ch - r * CW;
+    *reinterpret_cast<bf16x8*>(lds + r * Geo<W>::PITCH + c * 16) = ld8(g + (size_t)r * W + c * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gram sums over a block of rows:  part[b] = A^T B  ([D x KP], fp32)
+//   MODE 0 (forward):  A = phi(K),  B = V_ext = [V | 1 at column KP-1]
+//   MODE 1 (backward): A = phi(Q),  B = G_ext = [dO / den | -s at KP-1]
+// Rows past the end contribute 0.
+// ---------------------------------------------------------------------------
+template <int D, int KP, int MODE>
+__global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
+  constexpr int AP = Geo<D>::PITCH, BP = Geo<KP>::PITCH;
+  __shared__ __attribute__((aligned(16))) char As[kGramTile * AP];
+  __shared__ __attribute__((aligned(16))) char Bs[kGramTile * BP];
+  constexpr int NMB = D / 32, NNB = KP / 32, NB = NMB * NNB, NBW = (NB + 3) / 4;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  TrReader<D> ta;
+  ta.init(tr_r, tr_c);
+  TrReader<KP> tbr;
+  tbr.init(tr_r, tr_c);
+
+  const int n = MODE == 0 ? a.n_M : a.n_N;
+  const int r_begin = blockIdx.x * kLinGramRows;
+  const int r_end = min(n, r_begin + kLinGramRows);
+  const bf16* X = reinterpret_cast<const bf16*>(MODE == 0 ? a.K : a.Q);
+  const bf16* Y = reinterpret_cast<const bf16*>(MODE == 0 ? a.V : a.dO);
+  const bool vec = (a.k & 7) == 0;
+
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int t = 0; t < NBW; ++t) acc[t] = f32x16{};
+
+  for (int r0 = r_begin; r0 < r_end; r0 += kGramTile) {
+    for (int ch = tid; ch < kGramTile * (D / 8); ch += 256) {
+      const int r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
+      float v[8];
+      if (gr < r_end) {
+        row8(X + (size_t)gr * D, c8 * 8, D, true, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = phi(v[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+      *reinterpret_cast<bf16x8*>(As + r * AP + c8 * 16) = pack8(v);
+    }
+    for (int ch = tid; ch < kGramTile * (KP / 8); ch += 256) {
+      const int r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+      float v[8];
+      if (gr < r_end) {
+        row8(Y + (size_t)gr * a.k, c8 * 8, a.k, vec, v);
+        if (MODE == 1) {
+          const float rd = a.rden[gr];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= rd;
+        }
+        if (c8 == KP / 8 - 1) v[7] = MODE == 0 ? 1.f : -a.s[gr];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+      *reinterpret_cast<bf16x8*>(Bs + r * BP + c8 * 16) = pack8(v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < kGramTile / 16; ++kc) {
+#pragma unroll
+      for (int t = 0; t < NBW; ++t) {
+        const int bi = wave + 4 * t;
+        if (NB % 4 == 0 || bi < NB)
+          acc[t] = mma(ta.frag(As, bi / NNB, kc), tbr.frag(Bs, bi % NNB, kc), acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+  float* part = a.part + (size_t)blockIdx.x * D * KP;
+#pragma unroll
+  for (int t = 0; t < NBW; ++t) {
+    const int bi = wave + 4 * t;
+    if (NB % 4 == 0 || bi < NB) {
+      const int mb = bi / NNB, nb = bi % NNB;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[(size_t)(mb * 32 + c_row(i, h)) * KP + nb * 32 + l32] = acc[t][i];
+    }
+  }
+}
+
+// Fixed-order sum of the Gram partials, written as bf16 in both layouts:
+// M [D x KP] and MT [KP x D].
+template <int D, int KP>
+__global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts, bf16* M, bf16* MT) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= D * KP) return;
+  const int d = idx / KP, c = idx - d * KP;
+  float s = 0.f;
+  for (int b = 0; b < nparts; ++b) s += part[(size_t)b * D * KP + idx];
+  const bf16 v = (bf16)s;
+  M[idx] = v;
+  MT[(size_t)c * D + d] = v;
+}
+
+// Per target row of the backward: rden = 1 / den, s = (dO . O) / den
+// (one wave per row).
+__global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.n_N) return;
+  const bf16* dO = reinterpret_cast<const bf16*>(a.dO) + (size_t)row * a.k;
+  const float* O = a.O + (size_t)row * a.k;
+  float acc = 0.f;
+  for (int c = lane; c < a.k; c += 64) acc += (float)dO[c] * O[c];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (lane == 0) {
+    const float rd = 1.f / a.den[row];
+    a.rden[row] = rd;
+    a.s[row] = acc * rd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernels (a wave owns 32 rows; lane l32 owns row l32 of the wave's block)
+//   MODE 0: O = phi(Q) KV / den, den = phi(Q) z        (LDS: KVz^T [KP x D])
+//   MODE 1: dQ = phi'(Q) * (G_ext KVz_ext^T)            (LDS: KVz_ext [D x KP])
+//   MODE 2: dK = phi'(K) * (V_ext dKVz_ext^T),
+//           dV = phi(K) dKV                              (LDS: both layouts)
+// Scores are computed transposed (C[col][row]) so that a lane holds its own
+// row and the operand fragments of that row come from its own registers.
+// ---------------------------------------------------------------------------
+template <int D, int KP, int MODE>
+__global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
+  constexpr int SZ_T = MODE == 1 ? 0 : KP * Geo<D>::PITCH;  // [KP x D] layout
+  constexpr int SZ_M = MODE == 0 ? 0 : D * Geo<KP>::PITCH;  // [D x KP] layout
+  __shared__ __attribute__((aligned(16))) char lds[SZ_T + SZ_M + 16];
+  char* LT = lds;
+  char* LM = lds + SZ_T;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int n = MODE == 2 ? a.n_M : a.n_N;
+  const int row = blockIdx.x * kApplyRows + wave * 32 + l32;
+  const bool row_ok = row < n;
+  const bool vec = (a.k & 7) == 0;
+
+  if (MODE != 1) stage_matrix<D>(LT, reinterpret_cast<const bf16*>(MODE == 0 ? a.MT : a.dMT), KP, tid);
+  if (MODE != 0) stage_matrix<KP>(LM, reinterpret_cast<const bf16*>(MODE == 1 ? a.M : a.dM), D, tid);
+  __syncthreads();
+
+  RowReader<D> rT;
+  rT.init(l32, h);
+  RowReader<KP> rM;
+  rM.init(l32, h);
+
+  // this lane's row of phi(X) (MODE 0: Q, MODE 2: K) as bf16 fragments
+  const bf16* X = reinterpret_cast<const bf16*>(MODE == 2 ? a.K : a.Q) + (size_t)(row_ok ? row : 0) * D;
+  bf16x8 xf[D / 16];
+  if (MODE != 1) {
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      float v[8];
+      row8(X, cc * 16 + 8 * h, D, true, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = row_ok ? phi(v[e]) : 0.f;
+      xf[cc] = pack8(v);
+    }
+  }
+
+  if (MODE == 0) {
+    f32x16 acc[KP / 32];
+#pragma unroll
+    for (int mb = 0; mb < KP / 32; ++mb) {
+      acc[mb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) acc[mb] = mma(rT.read(LT, mb, cc), xf[cc], acc[mb]);
+    }
+    // den = C[KP-1][row]: element 15 of the last block, held by the h = 1 lanes
+    const float own = acc[KP / 32 - 1][15], other = xor32(own);
+    const float den = h ? own : other;
+    if (row_ok) {
+      const float rd = 1.f / den;
+      float* Orow = a.O + (size_t)row * a.k;
+#pragma unroll
+      for (int mb = 0; mb < KP / 32; ++mb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = mb * 32 + 8 * g + 4 * h;
+          if ((a.k & 3) == 0 && c + 4 <= a.k) {
+            *reinterpret_cast<f32x4*>(Orow + c) =
+                f32x4{acc[mb][4 * g] * rd, acc[mb][4 * g + 1] * rd, acc[mb][4 * g + 2] * rd, acc[mb][4 * g + 3] * rd};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c + e < a.k) Orow[c + e] = acc[mb][4 * g + e] * rd;
+          }
+        }
+      }
+      if (h == 0) a.den[row] = den;
+    }
+    return;
+  }
+
+  if (MODE == 1) {
+    // G_ext row fragments: c < k: dO / den; c = KP-1: -s; else 0
+    const bf16* dOr = reinterpret_cast<const bf16*>(a.dO) + (size_t)(row_ok ? row : 0) * a.k;
+    const float rd = row_ok ? a.rden[row] : 0.f, sv = row_ok ? a.s[row] : 0.f;
+    bf16x8 gf[KP / 16];
+#pragma unroll
+    for (int cc = 0; cc < KP / 16; ++cc) {
+      float v[8];
+      row8(dOr, cc * 16 + 8 * h, a.k, vec, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= rd;
+      if (cc == KP / 16 - 1 && h == 1) v[7] = -sv;
+      gf[cc] = pack8(v);
+    }
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+      acc[mb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < KP / 16; ++cc) acc[mb] = mma(rM.read(LM, mb, cc), gf[cc], acc[mb]);
+    }
+    if (row_ok) {
+      const bf16* Qr = reinterpret_cast<const bf16*>(a.Q) + (size_t)row * D;
+      float* out = a.dQ + (size_t)row * D;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = mb * 32 + 8 * g + 4 * h;
+          const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qr + d0);
+          *reinterpret_cast<f32x4*>(out + d0) =
+              f32x4{dphi((float)q4[0]) * acc[mb][4 * g], dphi((float)q4[1]) * acc[mb][4 * g + 1],
+                    dphi((float)q4[2]) * acc[mb][4 * g + 2], dphi((float)q4[3]) * acc[mb][4 * g + 3]};
+        }
+      }
+    }
+    return;
+  }
+
+  // MODE 2: V_ext row fragments (c < k: V; c = KP-1: 1; else 0)
+  const bf16* Vr = reinterpret_cast<const bf16*>(a.V) + (size_t)(row_ok ? row : 0) * a.k;
+  bf16x8 vf[KP / 16];
+#pragma unroll
+  for (int cc = 0; cc < KP / 16; ++cc) {
+    float v[8];
+    row8(Vr, cc * 16 + 8 * h, a.k, vec, v);
+    if (cc == KP / 16 - 1 && h == 1) v[7] = 1.f;
+    vf[cc] = pack8(v);
+  }
+  f32x16 c1[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    c1[mb] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < KP / 16; ++cc) c1[mb] = mma(rM.read(LM, mb, cc), vf[cc], c1[mb]);
+  }
+  if (row_ok) {
+    const bf16* Kr = reinterpret_cast<const bf16*>(a.K) + (size_t)row * D;
+    float* out = a.dK + (size_t)row * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = mb * 32 + 8 * g + 4 * h;
+        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kr + d0);
+        *reinterpret_cast<f32x4*>(out + d0) =
+            f32x4{dphi((float)k4[0]) * c1[mb][4 * g], dphi((float)k4[1]) * c1[mb][4 * g + 1],
+                  dphi((float)k4[2]) * c1[mb][4 * g + 2], dphi((float)k4[3]) * c1[mb][4 * g + 3]};
+      }
+    }
+  }
+  f32x16 c2[KP / 32];
+#pragma unroll
+  for (int nb = 0; nb < KP / 32; ++nb) {
+    c2[nb] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) c2[nb] = mma(rT.read(LT, nb, cc), xf[cc], c2[nb]);
+  }
+  if (row_ok) {
+    float* out = a.dV + (size_t)row * a.k;
+#pragma unroll
+    for (int nb = 0; nb < KP / 32; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = nb * 32 + 8 * g + 4 * h;
+        if ((a.k & 3) == 0 && c + 4 <= a.k) {
+          *reinterpret_cast<f32x4*>(out + c) = f32x4{c2[nb][4 * g], c2[nb][4 * g + 1], c2[nb][4 * g + 2], c2[nb][4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) out[c + e] = c2[nb][4 * g + e];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace lin
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+#define SSC_LIN_INSTANCES(X) \
+  X(128, 224)                \
+  X(128, 256)                \
+  X(128, 128)                \
+  X(128, 64)                 \
+  X(128, 32)                 \
+  X(64, 224)                 \
+  X(64, 256)                 \
+  X(64, 128)                 \
+  X(64, 64)                  \
+  X(64, 32)
+
+hipError_t launch_lin_gram(int D, int KP, int mode, const LinArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                              \
+  if (D == DD && KP == KK) {                                                                       \
+    if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0>), dim3(grid), dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1>), dim3(grid), dim3(256), 0, st, a);           \
+    return hipGetLastError();                                                                      \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                    \
+  if (D == DD && KP == KK) {                                                                             \
+    hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 255) / 256), dim3(256), 0, st, part, nparts, \
+                       reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT));                        \
+    return hipGetLastError();                                                                            \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(lin::lin_rowprep, dim3((a.n_N + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lin_apply(int D, int KP, int mode, const LinArgs& a, hipStream_t st) {
+  const int n = mode == 2 ? a.n_M : a.n_N;
+  const int grid = (n + lin::kApplyRows - 1) / lin::kApplyRows;
+#define SSC_L(DD, KK)                                                                                 \
+  if (D == DD && KP == KK) {                                                                          \
+    if (mode == 0) hipLaunchKernelGGL((lin::lin_apply<DD, KK, 0>), dim3(grid), dim3(256), 0, st, a);   \
+    else if (mode == 1) hipLaunchKernelGGL((lin::lin_apply<DD, KK, 1>), dim3(grid), dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((lin::lin_apply<DD, KK, 2>), dim3(grid), dim3(256), 0, st, a);             \
+    return hipGetLastError();                                                                         \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssc

@@ -144,6 +144,32 @@ def test_geo_validation(L):
              A[9], A[10], A[11], None, 0, None) == WORKSPACE
 
 
+def test_linear_validation_and_workspace(L):
+    w = L.ssc_workspace_bytes
+    assert w(ssc.OP_LINEAR_FWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) >= 128 * 224 * 2 * 2
+    assert w(ssc.OP_LINEAR_BWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) > w(ssc.OP_LINEAR_FWD, BF16, 60000,
+                                                                           60000, 128, 200, 0, 0, 0)
+    assert w(ssc.OP_LINEAR_FWD, BF16, 10, 10, 128, 256, 0, 0, 0) == 0   # no column left for the normaliser
+    assert w(ssc.OP_LINEAR_FWD, F32, 10, 10, 128, 64, 0, 0, 0) == 0     # bf16 only
+    f = L.coupling_linear_fwd
+    args = lambda **kw: [kw.get("dt", BF16), kw.get("nN", 64), kw.get("nM", 64), kw.get("d", 128), kw.get("k", 200),
+                         kw.get("Q", A[0]), A[1], A[2], kw.get("O", A[3]), A[4], kw.get("ws", None),
+                         kw.get("wsb", 0), None]
+    assert f(*args(k=256)) == UNSUPPORTED
+    assert f(*args(dt=F32)) == UNSUPPORTED
+    assert f(*args(d=96)) == UNSUPPORTED
+    assert f(*args(nM=0)) == INVALID
+    assert f(*args(nN=0)) == OK
+    assert f(*args(Q=P(0))) == INVALID
+    assert f(*args()) == WORKSPACE
+    assert f(*args(O=A[1], ws=A[9], wsb=1 << 40)) == INVALID     # O aliases K
+    g = L.coupling_linear_bwd
+    bargs = lambda **kw: [BF16, 64, 64, 128, 200, A[0], A[1], A[2], A[3], A[4], A[5], kw.get("dQ", A[6]), A[7],
+                          A[8], kw.get("ws", None), kw.get("wsb", 0), None]
+    assert g(*bargs()) == WORKSPACE
+    assert g(*bargs(dQ=A[4], ws=A[9], wsb=1 << 40)) == INVALID   # dQ aliases dO
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ssc, "_lib", None)
     monkeypatch.setattr(ssc, "library_path", str(tmp_path / "missing.so"))
