@@ -259,6 +259,26 @@ def main():
             "launch_ms": round(dkv_avg, 4), "launches": dkv_n,
             "flop_per_launch": dkv_flops(pairs_dense, d, k)}
 
+    if not args.dense_only:
+        # the linearized baseline (ELU feature map) on the same 60k tensors: an
+        # informational record, not part of the step (HBM-bound, O(n (d + k)))
+        def lin_f():
+            st["lin"] = ssc.coupling_linear_fwd(dense["Q"], dense["K"], dense["V"])
+
+        def lin_b():
+            O_, den_ = st["lin"]
+            ssc.coupling_linear_bwd(dense["Q"], dense["K"], dense["V"], O_, dense["dO"], den_)
+
+        phl, totl, _ = time_steps([lin_f, lin_b], args.steps, args.warmup, torch)
+        nb = lambda rows, cols, es: float(rows) * cols * es
+        by = (nb(n, d, 2) * 2 + nb(n, k, 2) + nb(n, k, 4) + nb(n, 1, 4)                     # fwd
+              + nb(n, d, 2) * 2 + nb(n, k, 2) * 2 + nb(n, k, 4) + nb(n, 1, 4)              # bwd reads
+              + nb(n, d, 4) * 2 + nb(n, k, 4))                                             # bwd writes
+        rec["linear_60k"] = {"ms": round(totl, 4), "fwd_ms": round(phl[0], 4), "bwd_ms": round(phl[1], 4),
+                             "algorithmic_bytes": by, "gbps": round(by / totl / 1e6, 1),
+                             "pct_hbm": round(100 * by / totl / 1e6 / 8000.0, 2),
+                             "what": "ELU linear-attention coupling fwd+bwd, bf16 in / fp32 out, n=60000"}
+
     if not args.no_160k and not args.dense_only:
         log("generating the 160k workload")
         c4 = gen.make_config(4)
