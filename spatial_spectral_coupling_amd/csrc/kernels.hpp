@@ -152,7 +152,7 @@ struct TopkArgs {
 
 // Linear-attention (ELU feature map) coupling: one argument block for all
 // of its kernels.
-constexpr int kLinGramRows = 512;  // rows per workgroup of the Gram sums
+constexpr int kLinGramRows = 256;  // rows per workgroup of the Gram sums
 struct LinArgs {
   const void* Q;        // [n_N x D] bf16
   const void* K;        // [n_M x D] bf16

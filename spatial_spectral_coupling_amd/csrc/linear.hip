@@ -165,8 +165,16 @@ __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts,
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= D * KP) return;
   const int d = idx / KP, c = idx - d * KP;
-  float s = 0.f;
-  for (int b = 0; b < nparts; ++b) s += part[(size_t)b * D * KP + idx];
+  // eight independent partial sums (loads in flight together), combined in
+  // a fixed order
+  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int b = 0;
+  for (; b + 8 <= nparts; b += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s8[u] += part[(size_t)(b + u) * D * KP + idx];
+  }
+  for (int u = 0; b < nparts; ++b, ++u) s8[u] += part[(size_t)b * D * KP + idx];
+  const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   const bf16 v = (bf16)s;
   M[idx] = v;
   MT[(size_t)c * D + d] = v;
