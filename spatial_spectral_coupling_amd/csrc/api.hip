@@ -26,6 +26,10 @@ int kpad_for(int k) {
   return 0;
 }
 
+// bf16 forward: V padded with at least one spare column (the ones column
+// that carries the softmax row sums) unless k is the largest padded width.
+int kpad_fwd_bf16(int k) { return k < kKPads[4] ? kpad_for(k + 1) : kpad_for(k); }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Buf {
@@ -89,7 +93,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
   switch (op) {
     case SSC_OP_DENSE_FWD:
     case SSC_OP_GEO_FWD:
-      L.Vp = take(nM * KP * 2);
+      L.Vp = take(nM * (size_t)kpad_fwd_bf16(k) * 2);
       break;
     case SSC_OP_DENSE_BWD:
     case SSC_OP_GEO_BWD:
@@ -396,14 +400,16 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   if (dtype == SSC_BF16) {
+    const int KPf = kpad_fwd_bf16(k);
+    const bool ones = k < KPf;
     PackArgs pv{};
-    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
     SSC_TRY(launch_pack(DType::BF16, pv, L.npadM / kGroup, s));
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M;
     const int rQ = kRowsFwd;
-    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ, s); }));
+    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ, s); }));
     return SSC_OK;
   }
   const int ngroups = L.npadM / kGroup;
@@ -590,8 +596,10 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     return st;
   int* counters = at<int>(ws, L.counters);
   if (dtype == SSC_BF16) {
+    const int KPf = kpad_fwd_bf16(k);
+    const bool ones = k < KPf;
     PackArgs pv{};
-    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
     SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
@@ -599,7 +607,7 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
     a.idx = idx; a.s = s; a.offM = offM; a.run_pf = at<int>(ws, L.run_pf);
     const int rQ = kRowsFwd;
-    SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KP, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
+    SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
     return SSC_OK;
   }
 

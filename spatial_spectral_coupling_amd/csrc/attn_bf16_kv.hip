@@ -11,7 +11,7 @@ namespace tb {
 // ---------------------------------------------------------------------------
 template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
-  constexpr int QB = Geo<D>::BYTES, OB = Geo<KP>::BYTES;
+  constexpr int QB = TileSrc<D, NW>::ALLOC, OB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
   __shared__ __attribute__((aligned(1024))) char sm1[QB + OB];
   __shared__ __attribute__((aligned(16))) float ls0[kTile];

@@ -28,6 +28,11 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
 // over the first half of the pipeline; scheduling fences between steps keep
 // this order.
 //
+// Row sums: with ONES, column k of the padded V holds 1 for every source
+// row (0 past the end), so the PV MFMAs also accumulate the row sums of the
+// bf16 probabilities in that column of O; without a spare column (k = KP)
+// the softmax slices add them up.
+//
 // Softmax reference: the probabilities of a tile are taken relative to a
 // reference fixed for the whole tile (the first tile: the maximum of its
 // first half; later tiles: the running reference), and the accumulators are
@@ -36,9 +41,9 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
 // reference by more than 32 could overflow; a workgroup that saw one redoes
 // its rows in a second pass with the exact row maxima of the first pass as a
 // fixed reference (probabilities <= 1), so the result is exact either way.
-template <int D, int KP, int NW, bool GEO>
+template <int D, int KP, int NW, bool GEO, bool ONES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
-  constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
+  constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
   __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
   __shared__ int rowtab[2][kTile];
@@ -91,6 +96,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
 
   f32x16 acc[KP / 32];
+  // Initial score accumulators: zero, except in a partial last tile, where
+  // keys at or past its end start at -inf (their probabilities are then 0).
+  f32x16 bias[2];
   float m_run, l_run, m_true = -INFINITY;
   bool fixed = false;
 
@@ -109,6 +117,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
+    bias[0] = bias[1] = f32x16{};
     l_run = 0.f;
     m_run = fixed ? m_true : -INFINITY;
     bool lagged = false;
@@ -129,17 +138,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // Two statically distinct buffers: the step that reads one fills the
     // other, so the compiler can tell the direct loads in flight from the LDS
     // reads.  The stream's last tile may be partial: its keys at or past
-    // nvalid are masked (a wave-uniform branch inside the softmax slices).
+    // nvalid start from a score of -inf (bias, set before the pipeline).
     auto step = [&](const int t, const int b, char* Kt, char* Kn) {
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
-      const bool part = nvalid < kTile;
       const bool first = t == 0 && !fixed;
+      if (nvalid < kTile) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) bias[hb][i] = hb * 32 + c_row(i, h) < nvalid ? 0.f : -INFINITY;
+      }
       f32x16 sc[2];
       float sv[2][16];
       bf16x8 pf[2][2];
       float mx[2], mh[2], mref = m_run, lsum = 0.f;
-      sc[0] = sc[1] = f32x16{};
+      sc[0] = bias[0];
+      sc[1] = bias[1];
 
       auto operand = [&](const int u) -> bf16x8 {
         if (u < C2) return rk.read(Kt, u / NS, u % NS);
@@ -154,22 +169,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
         acc[j % NCB] = mma(x, pf[hb][j / NCB], acc[j % NCB]);
       };
-      auto valid = [&](const int hb, const int i) { return hb * 32 + c_row(i, h) < nvalid; };
       // Slice k of the softmax of key half hb (the scores are copied once out
       // of the MFMA accumulators into sv): 0, 1 copy and row maximum (the
       // first tile takes its reference from half 0); 2..9 element pairs
       // 2m, 2m+1 = 2(k-2) .. : exp2, row sum and packed bf16 probabilities.
       auto slice = [&](const int hb, const int k) {
         if (k <= 1) {
-          if (k == 0 && part) {
-            // masked keys get a score of -inf (the branch is kept: asm)
-            asm volatile("");
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sv[hb][i] = valid(hb, i) ? sc[hb][i] : -INFINITY;
-          } else if (!part) {
-#pragma unroll
-            for (int i = 8 * k; i < 8 * k + 8; ++i) sv[hb][i] = sc[hb][i];
-          }
+          for (int i = 8 * k; i < 8 * k + 8; ++i) sv[hb][i] = sc[hb][i];
           float m = k == 0 ? -INFINITY : mx[hb];
 #pragma unroll
           for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sv[hb][i]);
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           const int m = k - 2;
           const float p0 = fexp2(fmaf(sv[hb][2 * m], c2, -mref));
           const float p1 = fexp2(fmaf(sv[hb][2 * m + 1], c2, -mref));
-          lsum += p0 + p1;
+          if (!ONES) lsum += p0 + p1;
           put_pair(pf[hb][m >> 2], m & 3, p0, p1);
         }
       };
@@ -257,7 +264,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     fixed = true;
   }
 
-  const float l_tot = l_run + xor32(l_run);
+  float l_part = l_run;
+  if (ONES) {
+    // the row sum sits in column k of O, held by the lanes of one half
+    l_part = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (cb * 32 + c_row(i, h) == a.k) l_part = acc[cb][i];
+  }
+  const float l_tot = l_part + xor32(l_part);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     float* Orow = a.O + (size_t)row * a.k;
@@ -296,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // softmax gets a window of a full A chain plus a B chain to hide in.
 template <int D, int KP, int NW, bool GEO>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
-  constexpr int KB = Geo<D>::BYTES, VB = Geo<KP>::BYTES;
+  constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
   __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
   __shared__ int rowtab[2][kTile];
@@ -392,6 +409,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // iteration's B1 chain adds exactly 0.
   f32x16 sc1, dp1;
   bf16x8 ds1[2], kt[LB];
+  // Initial score accumulators of the two key halves: zero, except in a
+  // partial last tile, where keys at or past its end start at -inf (P = dS
+  // = 0 for them).
+  f32x16 bias[2];
+  bias[0] = bias[1] = f32x16{};
   static_for<16>([&](auto ic) {
     constexpr int i = ic, k = i / 2;
     sc1[i] = k * WIN / SLICES < LB ? 0.f : -INFINITY;
@@ -403,15 +425,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   // Slice k of the softmax of one half (scores sv, dP dv, packed dS out):
   // element pair 2k, 2k+1 (P = exp2(S c2 - lse2), dS = P (dP - D)) packed
-  // into out; slice 0 first masks keys at or past nvalid (scores -inf, so
-  // P = dS = 0).
-  auto slice = [&](f32x16& sv, f32x16& dv, bf16x8* out, const int kb, const int k, const bool part,
-                   const int nvalid) {
-    if (k == 0 && part) {
-      asm volatile("");  // keeps the branch
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = kb * 32 + c_row(i, h) < nvalid ? sv[i] : -INFINITY;
-    }
+  // into out.
+  auto slice = [&](f32x16& sv, f32x16& dv, bf16x8* out, const int k) {
     const float d0 = fexp2(fmaf(sv[2 * k], c2, -lse2)) * (dv[2 * k] - Dq);
     const float d1 = fexp2(fmaf(sv[2 * k + 1], c2, -lse2)) * (dv[2 * k + 1] - Dq);
     put_pair(out[k >> 2], k & 3, d0, d1);
@@ -424,8 +439,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   auto step = [&](const int t, const int b, char* Kt, char* Kn) {
     char* Vt = Kt + KB;
     const int nvalid = total - t * kTile;
-    const bool part = nvalid < kTile;
-    f32x16 sc0 = f32x16{}, dp0 = f32x16{};
+    if (nvalid < kTile) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bias[kb][i] = kb * 32 + c_row(i, h) < nvalid ? 0.f : -INFINITY;
+    }
+    f32x16 sc0 = bias[0], dp0 = f32x16{};
     bf16x8 ds0[2];
 
     auto operand = [&](const int u) -> bf16x8 {
@@ -475,18 +495,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (u < CY) {
         // half 1 of the previous tile: window positions LB .. WIN-1
         static_for<SLICES>([&](auto k) {
-          if (k * WIN / SLICES >= LB && k * WIN / SLICES - LB == u) slice(sc1, dp1, ds1, 1, k, false, kTile);
+          if (k * WIN / SLICES >= LB && k * WIN / SLICES - LB == u) slice(sc1, dp1, ds1, k);
         });
       } else if (u < CW) {
         // half 0 of this tile: window positions 0 .. WIN-1 over B1 and A1
         static_for<SLICES>([&](auto k) {
-          if (k * WIN / SLICES == u - CY) slice(sc0, dp0, ds0, 0, k, part, nvalid);
+          if (k * WIN / SLICES == u - CY) slice(sc0, dp0, ds0, k);
         });
       } else {
         // half 1 of this tile, window positions 0 .. LB-1; and its K^T
         // fragments for the B1 chain of the next iteration
         static_for<SLICES>([&](auto k) {
-          if (k * WIN / SLICES < LB && k * WIN / SLICES == u - CW) slice(sc1, dp1, ds1, 1, k, part, nvalid);
+          if (k * WIN / SLICES < LB && k * WIN / SLICES == u - CW) slice(sc1, dp1, ds1, k);
         });
         const int j = u - CW;
         kt[j] = tk.frag(Kt, j % NK, 2 + j / NK);
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     };
     auto pre = [&](const int u) {
       if (u == CZ) {  // A1(t) starts: fresh accumulators for half 1
-        sc1 = f32x16{};
+        sc1 = bias[1];
         dp1 = f32x16{};
       }
     };
@@ -520,7 +540,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   // drain: the rest of the last tile's half-1 softmax, then its B1 chain
   static_for<SLICES>([&](auto k) {
-    if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, 1, k, false, kTile);
+    if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, k);
   });
   static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
 
@@ -555,17 +575,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   X(64, 64)                   \
   X(64, 32)
 
-hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                                       \
-  if (D == DD && KP == KK) {                                                                                \
-    if (a.items != nullptr)                                                                                 \
-      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
-    else                                                                                                    \
-      hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
-    return hipGetLastError();                                                                               \
+// The forward takes the row sums from a ones column of V whenever k < KP;
+// only KP = 256 also has the variant without one (k = 256).
+hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st) {
+#define SSC_L1(DD, KK, OO)                                                                                      \
+  if (a.items != nullptr)                                                                                     \
+    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true, OO>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+  else                                                                                                        \
+    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false, OO>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+  return hipGetLastError();
+#define SSC_L(DD, KK)                   \
+  if (ones && D == DD && KP == KK) {    \
+    SSC_L1(DD, KK, true)                \
   }
   SSC_BF16_INSTANCES(SSC_L)
+  if (!ones && KP == 256) {
+    if (D == 128) {
+      SSC_L1(128, 256, false)
+    }
+    if (D == 64) {
+      SSC_L1(64, 256, false)
+    }
+  }
 #undef SSC_L
+#undef SSC_L1
   return hipErrorInvalidValue;
 }
 

@@ -102,6 +102,7 @@ struct PackArgs {
   void* Xp;             // [npad x W] or nullptr
   void* Xg;             // [npad/16][W][16] or nullptr
   int n, w, W;
+  int ones;             // 1: column w of every row present holds 1 (w < W)
   const int* poff;      // nullptr: dense (position = row)
   const int* off;
   int P;
@@ -175,7 +176,9 @@ struct LinArgs {
 
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
-hipError_t launch_fwd_bf16(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+// ones: column k of the padded V holds ones (k < KP); KP = 256 also runs
+// without (k = 256)
+hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st);
 hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);

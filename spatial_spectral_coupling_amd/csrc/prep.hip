@@ -59,6 +59,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     const int r = e / W, c = e - r * W;
     T v = T(0.f);
     if (r < nrows && c < w) v = X[(size_t)(row0 + r) * w + c];
+    else if (r < nrows && c == w && a.ones) v = T(1.f);
     tile[r * pitch + c] = v;
   }
   __syncthreads();

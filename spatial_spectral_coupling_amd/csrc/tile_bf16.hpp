@@ -147,11 +147,11 @@ extern "C" __device__ void ssc_raw_buffer_load_lds(i32x4 rsrc, __attribute__((ad
                                                    int size, int voffset, int soffset, int offset,
                                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-// Division of a tile slot index s < 64 CP by the constant CP as a 24-bit
+// Division of a tile slot index s < nslots by the constant CP as a 24-bit
 // multiply and shift (checked exhaustively at compile time).
 constexpr unsigned slot_magic(int cp) { return (1u << 20) / (unsigned)cp + 1u; }
-constexpr bool slot_magic_exact(int cp) {
-  for (unsigned s = 0; s < 64u * (unsigned)cp; ++s)
+constexpr bool slot_magic_exact(int cp, int nslots) {
+  for (unsigned s = 0; s < (unsigned)nslots; ++s)
     if (((s * slot_magic(cp)) >> 20) != s / (unsigned)cp) return false;
   return true;
 }
@@ -160,7 +160,12 @@ constexpr bool slot_magic_exact(int cp) {
 // W / 2 fp32 columns, `limit` rows present) into LDS.  Slot s of a tile (16
 // bytes at s * 16) is tile row r = s / CP, chunk s - r CP; the pad chunks
 // of a row fetch the first chunks of the next row (never read).  The j-th
-// load of a wave is tile instruction wave + j * NW.
+// load of a wave is tile instruction wave + j * NW.  Every wave issues the
+// same number of loads (no wave-uniform branches inside the pipelines): the
+// LDS buffer of a tile is rounded up to whole rounds of NW loads (ALLOC
+// bytes), and the slots past the tile's 64 rows fetch rows 64.. of the
+// window (dense; zeros past the array's end) or the array's end (geo) into
+// that never-read tail.
 //  * dense tiles are windows of consecutive rows: a buffer resource based at
 //    the tile's first row and bounded by the array's end (rows past it read
 //    zeros), so a lane's byte offset is the tile-independent 16 (s - r PADC);
@@ -171,9 +176,10 @@ template <int W, int NW>
 struct TileSrc {
   static constexpr int CP = Geo<W>::CP, CW = Geo<W>::CW, RB = 2 * W;
   static constexpr int NI = Geo<W>::SLOTS / 64;      // instructions per tile
-  static constexpr int NJ = (NI + NW - 1) / NW;      // per wave (at most)
+  static constexpr int NJ = (NI + NW - 1) / NW;      // per wave
+  static constexpr int ALLOC = NJ * NW * 1024;        // LDS bytes of a tile buffer
   static constexpr unsigned MAGIC = slot_magic(CP);
-  static_assert(slot_magic_exact(CP), "slot division");
+  static_assert(slot_magic_exact(CP, NJ * NW * 64), "slot division");
 
   const char* base;
   int limit;
@@ -181,9 +187,6 @@ struct TileSrc {
   __device__ __forceinline__ void init(const void* b, int lim) {
     base = reinterpret_cast<const char*>(b);
     limit = lim;
-  }
-  __device__ __forceinline__ static bool present(int wave, int j) {
-    return NJ * NW == NI || j < NJ - 1 || wave + j * NW < NI;
   }
   __device__ __forceinline__ static int slot(int wave, int lane, int j) { return (wave + j * NW) * 64 + lane; }
   __device__ __forceinline__ static int slot_row(int s) { return (int)(__umul24((unsigned)s, MAGIC) >> 20); }
@@ -199,23 +202,21 @@ struct TileSrc {
     return (s - slot_row(s) * (CP - CW)) * 16;
   }
   __device__ __forceinline__ static void load_dense(char* tile, const i32x4& win, int wave, int lane, int j) {
-    if (!present(wave, j)) return;  // wave-uniform
     asm volatile("" : "+v"(lane));
     ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, dense_offset(wave, lane, j), 0,
                             0, 0);
   }
   // the same with the offset computed once outside the tile loop
   __device__ __forceinline__ static void load_dense_at(char* tile, const i32x4& win, int off, int wave, int j) {
-    if (!present(wave, j)) return;
     ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
   }
   __device__ __forceinline__ static int geo_row(const int* rows, int wave, int lane, int j) {
-    if (!present(wave, j)) return -1;
     asm volatile("" : "+v"(lane));
-    return rows[slot_row(slot(wave, lane, j))];
+    const int r = slot_row(slot(wave, lane, j));
+    if ((j + 1) * NW <= NI) return rows[r];  // all rows of this load are tile rows
+    return r < kTile ? rows[r < kTile ? r : kTile - 1] : -1;
   }
   __device__ __forceinline__ void load_geo(char* tile, const i32x4& all, int grow, int wave, int lane, int j) const {
-    if (!present(wave, j)) return;
     asm volatile("" : "+v"(lane));
     const int s = slot(wave, lane, j);
     const int r = slot_row(s);

@@ -84,11 +84,14 @@ def test_geo_full_selection_equals_dense_on_gpu():
     gd = ssc.coupling_dense_bwd(dev["Q"], dev["K"], dev["V"], Od, dev["dO"], lsed, c["scale"])
     # Same support; the keys arrive in another order, so the reference max at
     # which each probability is rounded to bf16 differs: the two agree to the
-    # parity bars (each is separately within them of the oracle).
+    # parity bars (each is separately within them of the oracle).  The row
+    # sums are sums of those bf16 probabilities (relative rounding <= 2^-9
+    # each), so each lse is within ln(1 + 2^-9) < 1.96e-3 of the exact one and
+    # the two within twice that.
     say("geo(s=P_M) vs dense O max-abs", (O - Od).abs().max().item())
     assert (O - Od).abs().max().item() < 2e-2
     assert ((O - Od).norm() / Od.norm()).item() < 5e-3
-    assert (lse - lsed).abs().max().item() < 1e-3
+    assert (lse - lsed).abs().max().item() < 3.92e-3
     for a, b in zip(g, gd):
         assert ((a - b).norm() / b.norm()).item() < 1e-2
 
