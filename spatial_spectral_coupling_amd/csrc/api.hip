@@ -70,7 +70,7 @@ struct Layout {
   size_t poffN = kNone, poffM = kNone, itemsQ = kNone, itemsK = kNone, counters = kNone;
   size_t inv_off = kNone, inv_idx = kNone, scratch = kNone;
   size_t Qbar = kNone, KbarT = kNone;
-  size_t run_pf = kNone, inv_pf = kNone;
+  size_t run_tab = kNone, inv_tab = kNone;
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
 };
@@ -115,11 +115,11 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     L.itemsK = take(((size_t)(n_M + rK - 1) / rK + P_M) * sizeof(Item));
     L.counters = take(8 * 4);
     L.scratch = take(((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
-    L.run_pf = take((size_t)P_N * (s + 1) * 4);
+    L.run_tab = take((size_t)P_N * s * sizeof(RunEntry));
     if (op == SSC_OP_GEO_BWD) {
       L.inv_off = take(((size_t)P_M + 1) * 4);
       L.inv_idx = take((size_t)P_N * s * 4);
-      L.inv_pf = take(((size_t)P_N * s + P_M) * 4);
+      L.inv_tab = take((size_t)P_N * s * sizeof(RunEntry));
     }
   }
   L.total = off;
@@ -558,8 +558,8 @@ ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int
   pl.rowsQ = bf16_path ? (inverse ? kRowsDq : kRowsFwd) : kRowsPerWG;
   pl.rowsK = bf16_path ? kRowsDkv : kRowsPerWG;
   if (bf16_path) {
-    pl.run_pf = at<int>(ws, L.run_pf);
-    if (inverse) pl.inv_pf = at<int>(ws, L.inv_pf);
+    pl.run_tab = at<RunEntry>(ws, L.run_tab);
+    if (inverse) pl.inv_tab = at<RunEntry>(ws, L.inv_tab);
   }
   pl.poffN = at<int>(ws, L.poffN); pl.poffM = at<int>(ws, L.poffM);
   pl.itemsQ = at<Item>(ws, L.itemsQ); pl.itemsK = at<Item>(ws, L.itemsK);
@@ -605,7 +605,7 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
     a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
-    a.idx = idx; a.s = s; a.offM = offM; a.run_pf = at<int>(ws, L.run_pf);
+    a.idx = idx; a.s = s; a.offM = offM; a.run_tab = at<RunEntry>(ws, L.run_tab);
     const int rQ = kRowsFwd;
     SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
     return SSC_OK;
@@ -666,7 +666,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
       q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
       q.n_N = n_N; q.c2 = c2; q.scale = scale;
       q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.n_M = n_M;
-      q.idx = idx; q.s = s; q.offM = offM; q.run_pf = at<int>(ws, L.run_pf);
+      q.idx = idx; q.s = s; q.offM = offM; q.run_tab = at<RunEntry>(ws, L.run_tab);
       const int rQ = kRowsDq;
       SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
     }
@@ -674,7 +674,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
     b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
-    b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_pf = at<int>(ws, L.inv_pf);
+    b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_tab = at<RunEntry>(ws, L.inv_tab);
     const int rK = kRowsDkv;
     SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK + P_M, hs); }));
     return SSC_OK;

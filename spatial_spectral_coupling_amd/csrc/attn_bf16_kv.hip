@@ -18,7 +18,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   __shared__ __attribute__((aligned(16))) float ls1[kTile];
   __shared__ __attribute__((aligned(16))) float ds0[kTile];
   __shared__ __attribute__((aligned(16))) float ds1[kTile];
-  __shared__ int rowtab[2][kTile];
+  __shared__ int rowtab[2][kTile + 1];  // rows of the next tiles, sentinel at kTile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -27,10 +27,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int k_begin, k_end;
   RowCursor rc;
+  // gathered query rows missing from a tile read the sentinel row n_N + 1
+  // (past the end of Q, of the padded dO and of lse2 / D)
   if (!GEO) {
     k_begin = blockIdx.x * (NW * 32);
     k_end = a.n_M;
-    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_N, 0, 0, 0};
+    rc = RowCursor{nullptr, 1, a.n_N, a.n_N + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
     const Item it = a.items[blockIdx.x];
@@ -38,8 +40,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     k_end = a.offM[it.patch + 1];
     const int i0 = a.inv_off[it.patch];
     const int nr = a.inv_off[it.patch + 1] - i0;
-    const int* pf = a.inv_pf + i0 + it.patch;
-    rc = RowCursor{pf, a.inv_idx + i0, a.offN, nr, pf[nr], 0, 0, 0};
+    const RunEntry* tab = a.inv_tab + i0;
+    rc = RowCursor{tab, nr, nr > 0 ? tab[nr - 1].end : 0, a.n_N + 1};
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     rc.init();
     rowtab[0][tid] = rc.row(tid);
     rowtab[1][tid] = rc.row(kTile + tid);
+    if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
   }
   __syncthreads();
   if (ntiles > 0) {
@@ -129,8 +132,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // dense: the per-lane tile load offsets do not depend on the tile
   int loff[NJQ + NJO];
   static_for<NJQ + NJO>([&](auto j) {
-    loff[j] = GEO ? 0 : j < NJQ ? TileSrc<D, NW>::dense_offset(wave, lane, j)
-                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJQ);
+    loff[j] = GEO ? (j < NJQ ? TileSrc<D, NW>::geo_chunk(wave, lane, j) : TileSrc<KP, NW>::geo_chunk(wave, lane, j - NJQ))
+                  : (j < NJQ ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                             : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJQ));
+  });
+  // geo: the row-table entry each load reads (the vector load: this lane's row)
+  int gidx[NL];
+  static_for<NL>([&](auto j) {
+    gidx[j] = !GEO ? 0 : j < NJQ ? TileSrc<D, NW>::geo_index(wave, lane, j)
+                      : j < NJQ + NJO ? TileSrc<KP, NW>::geo_index(wave, lane, j - NJQ) : lane;
   });
 
   // Two statically distinct buffers: the step that reads one fills the other.
@@ -191,23 +201,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const i32x4 winQ = GEO ? sQ.whole() : sQ.window(row0n), winO = GEO ? sO.whole() : sO.window(row0n);
     int grow = -1;
     auto load_row = [&](const int j) {  // geo phase 1
-      if (j < NJQ) grow = sQ.geo_row(rn, wave, lane, j);
-      else if (j < NJQ + NJO) grow = sO.geo_row(rn, wave, lane, j - NJQ);
-      else grow = rn[lane];
+      grow = rn[gidx[j]];
     };
     auto issue_load = [&](const int j) {
       if (j < NJQ) {
-        if (GEO) sQ.load_geo(Qn, winQ, grow, wave, lane, j);
+        if (GEO) sQ.load_geo_at(Qn, winQ, grow, loff[j], wave, j);
         else sQ.load_dense_at(Qn, winQ, loff[j], wave, j);
       } else if (j < NJQ + NJO) {
-        if (GEO) sO.load_geo(Qn + QB, winO, grow, wave, lane, j - NJQ);
+        if (GEO) sO.load_geo_at(Qn + QB, winO, grow, loff[j], wave, j - NJQ);
         else sO.load_dense_at(Qn + QB, winO, loff[j], wave, j - NJQ);
-      } else if (wave == 0) {
-        if (GEO) sL.load_geo(lsn, grow, lane);
-        else sL.load_dense(lsn, row0n, lane);
-      } else if (wave == NW - 1) {
-        if (GEO) sD.load_geo(dsn, grow, lane);
-        else sD.load_dense(dsn, row0n, lane);
+      } else {
+        // even waves fetch lse, odd waves D (duplicate fetches write the
+        // same values); a wave-uniform select, no branch in the pipeline
+        const bool odd = wave & 1;
+        const VecSrc src = odd ? sD : sL;
+        float* dst = odd ? dsn : lsn;
+        if (GEO) src.load_geo(dst, grow, lane);
+        else src.load_dense(dst, row0n, lane);
       }
     };
     auto side = [&](const int u) {

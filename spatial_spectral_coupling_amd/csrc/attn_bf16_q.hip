@@ -46,7 +46,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
   __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
-  __shared__ int rowtab[2][kTile];
+  __shared__ int rowtab[2][kTile + 1];  // rows of the next tiles, sentinel at kTile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -55,17 +55,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
+  // gathered key rows missing from a tile read the sentinel row n_M + 1
+  // (past the end of K and of the padded V)
   if (!GEO) {
     q_begin = blockIdx.x * (NW * 32);
     q_end = a.n_N;
-    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
+    rc = RowCursor{nullptr, 1, a.n_M, a.n_M + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
     const Item it = a.items[blockIdx.x];
     q_begin = a.offN[it.patch] + it.row0;
     q_end = a.offN[it.patch + 1];
-    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
-    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
+    const RunEntry* tab = a.run_tab + (size_t)it.patch * a.s;
+    rc = RowCursor{tab, a.s, tab[a.s - 1].end, a.n_M + 1};
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
@@ -110,8 +112,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // dense: the per-lane load offsets do not depend on the tile; kept in registers
   int loff[NL];
   static_for<NL>([&](auto j) {
-    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
-                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+    loff[j] = GEO ? (j < NJK ? TileSrc<D, NW>::geo_chunk(wave, lane, j) : TileSrc<KP, NW>::geo_chunk(wave, lane, j - NJK))
+                  : (j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                             : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK));
+  });
+  // geo: the row-table entry each load reads
+  int gidx[NL];
+  static_for<NL>([&](auto j) {
+    gidx[j] = !GEO ? 0 : j < NJK ? TileSrc<D, NW>::geo_index(wave, lane, j)
+                                 : TileSrc<KP, NW>::geo_index(wave, lane, j - NJK);
   });
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -126,6 +135,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       rc.init();
       rowtab[0][tid] = rc.row(tid);
       rowtab[1][tid] = rc.row(kTile + tid);
+      if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
     }
     __syncthreads();
     if (ntiles > 0) {
@@ -200,14 +210,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
       int grow = -1;
       auto load_row = [&](const int j) {  // geo phase 1
-        grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+        grow = rn[gidx[j]];
       };
       auto issue_load = [&](const int j) {
         if (j < NJK) {
-          if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+          if (GEO) sK.load_geo_at(Kn, winK, grow, loff[j], wave, j);
           else sK.load_dense_at(Kn, winK, loff[j], wave, j);
         } else {
-          if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+          if (GEO) sV.load_geo_at(Kn + KB, winV, grow, loff[j], wave, j - NJK);
           else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
         }
       };
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
   __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
-  __shared__ int rowtab[2][kTile];
+  __shared__ int rowtab[2][kTile + 1];  // rows of the next tiles, sentinel at kTile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -325,17 +335,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
+  // gathered key rows missing from a tile read the sentinel row n_M + 1
+  // (past the end of K and of the padded V)
   if (!GEO) {
     q_begin = blockIdx.x * (NW * 32);
     q_end = a.n_N;
-    rc = RowCursor{nullptr, nullptr, nullptr, 1, a.n_M, 0, 0, 0};
+    rc = RowCursor{nullptr, 1, a.n_M, a.n_M + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
     const Item it = a.items[blockIdx.x];
     q_begin = a.offN[it.patch] + it.row0;
     q_end = a.offN[it.patch + 1];
-    const int* pf = a.run_pf + (size_t)it.patch * (a.s + 1);
-    rc = RowCursor{pf, a.idx + (size_t)it.patch * a.s, a.offM, a.s, pf[a.s], 0, 0, 0};
+    const RunEntry* tab = a.run_tab + (size_t)it.patch * a.s;
+    rc = RowCursor{tab, a.s, tab[a.s - 1].end, a.n_M + 1};
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
@@ -376,6 +388,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     rc.init();
     rowtab[0][tid] = rc.row(tid);
     rowtab[1][tid] = rc.row(kTile + tid);
+    if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
   }
   __syncthreads();
   if (ntiles > 0) {
@@ -395,8 +408,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // dense: the per-lane load offsets do not depend on the tile; kept in registers
   int loff[NL];
   static_for<NL>([&](auto j) {
-    loff[j] = GEO ? 0 : j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
-                                : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK);
+    loff[j] = GEO ? (j < NJK ? TileSrc<D, NW>::geo_chunk(wave, lane, j) : TileSrc<KP, NW>::geo_chunk(wave, lane, j - NJK))
+                  : (j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
+                             : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK));
+  });
+  // geo: the row-table entry each load reads
+  int gidx[NL];
+  static_for<NL>([&](auto j) {
+    gidx[j] = !GEO ? 0 : j < NJK ? TileSrc<D, NW>::geo_index(wave, lane, j)
+                                 : TileSrc<KP, NW>::geo_index(wave, lane, j - NJK);
   });
   // position of softmax slice k of a half over its window
   constexpr int WIN = LA + LB;
@@ -477,14 +497,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
     int grow = -1;
     auto load_row = [&](const int j) {  // geo phase 1
-      grow = j < NJK ? sK.geo_row(rn, wave, lane, j) : sV.geo_row(rn, wave, lane, j - NJK);
+      grow = rn[gidx[j]];
     };
     auto issue_load = [&](const int j) {
       if (j < NJK) {
-        if (GEO) sK.load_geo(Kn, winK, grow, wave, lane, j);
+        if (GEO) sK.load_geo_at(Kn, winK, grow, loff[j], wave, j);
         else sK.load_dense_at(Kn, winK, loff[j], wave, j);
       } else {
-        if (GEO) sV.load_geo(Kn + KB, winV, grow, wave, lane, j - NJK);
+        if (GEO) sV.load_geo_at(Kn + KB, winV, grow, loff[j], wave, j - NJK);
         else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
       }
     };

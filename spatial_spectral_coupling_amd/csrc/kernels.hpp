@@ -17,6 +17,13 @@ constexpr int kRowsDq = kWavesQ * 32;  // dQ
 constexpr int kRowsDkv = kWavesK * 32; // dK / dV
 
 // Work item of the row-block kernels: (patch, first row within the patch).
+// One run of a gathered row stream (the rows of one patch, in order): the
+// stream positions before `end` that are past the previous run map to rows
+// position + base.
+struct RunEntry {
+  int end, base;
+};
+
 struct Item {
   int patch, row0;
 };
@@ -39,9 +46,9 @@ struct FwdArgs {
   const int* offM;      // geo: source offsets
   int npadM, n_M;       // dense key stream
   // bf16 kernels: Kp is the caller's K (row-major), Vp the k-padded copy of V,
-  // run_pf [P_N][s + 1] the prefix sums of selected source-patch sizes.
+  // run_tab [P_N][s] the run table of each target patch's key stream.
   const void* Vp;
-  const int* run_pf;
+  const RunEntry* run_tab;
 };
 
 // dQ pass.
@@ -65,7 +72,7 @@ struct DqArgs {
   const int* poffM;
   const int* offM;
   int npadM, n_M;
-  const int* run_pf;    // bf16 kernels (Qp, Kp = caller rows; lse2p, Dp by row)
+  const RunEntry* run_tab;  // bf16 kernels (Qp, Kp = caller rows; lse2p, Dp by row)
 };
 
 // dK / dV pass.
@@ -91,9 +98,9 @@ struct DkvArgs {
   const int* poffN;
   const int* offN;
   int npadN, n_N;       // dense query stream
-  // bf16 kernels: prefix sums of target-patch sizes along each inverse list,
-  // list q at inv_pf[inv_off[q] + q], length inv_off[q+1] - inv_off[q] + 1.
-  const int* inv_pf;
+  // bf16 kernels: run table of each source patch's query stream, entries
+  // inv_tab[inv_off[q] .. inv_off[q+1]) (one per selecting target patch).
+  const RunEntry* inv_tab;
 };
 
 // Packing of one tensor into the padded patch layout.
@@ -129,8 +136,8 @@ struct PlanArgs {
   int* inv_idx;         // [P_N * s]
   int* scratch;         // [max(P_N, P_M) + 1] counters for scans and fills
   int rowsQ, rowsK;     // rows per work item (target, source side)
-  int* run_pf;          // [P_N * (s + 1)] or nullptr
-  int* inv_pf;          // [P_N * s + P_M] or nullptr
+  RunEntry* run_tab;    // [P_N * s] or nullptr: source runs of each target patch
+  RunEntry* inv_tab;    // [P_N * s] or nullptr: target runs of each source patch
 };
 
 struct PoolArgs {

@@ -193,17 +193,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * rK};
   }
   __syncthreads();
-  // ---- per target patch: prefix sums of the selected source-patch sizes
-  if (a.run_pf != nullptr && a.idx != nullptr) {
+  // ---- per target patch: the run table of its key stream (the selected
+  // source patches in selection order)
+  if (a.run_tab != nullptr && a.idx != nullptr) {
     for (int p = tid; p < a.P_N; p += kPlanThreads) {
       int acc = 0;
-      int* pf = a.run_pf + (size_t)p * (a.s + 1);
+      RunEntry* tab = a.run_tab + (size_t)p * a.s;
       for (int r = 0; r < a.s; ++r) {
-        pf[r] = acc;
         const int q = a.idx[(size_t)p * a.s + r];
-        acc += offM[q + 1] - offM[q];
+        const int n = offM[q + 1] - offM[q];
+        tab[r] = RunEntry{acc + n, offM[q] - acc};
+        acc += n;
       }
-      pf[a.s] = acc;
     }
     __syncthreads();
   }
@@ -236,18 +237,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         a.inv_idx[j + 1] = v;
       }
     }
-    if (a.inv_pf != nullptr) {
+    if (a.inv_tab != nullptr) {
       __syncthreads();
       for (int q = tid; q < a.P_M; q += kPlanThreads) {
         const int b = a.inv_off[q], e = a.inv_off[q + 1];
-        int* pf = a.inv_pf + b + q;
         int acc = 0;
         for (int i = b; i < e; ++i) {
-          pf[i - b] = acc;
           const int p = a.inv_idx[i];
-          acc += offN[p + 1] - offN[p];
+          const int n = offN[p + 1] - offN[p];
+          a.inv_tab[i] = RunEntry{acc + n, offN[p] - acc};
+          acc += n;
         }
-        pf[e - b] = acc;
       }
     }
   }

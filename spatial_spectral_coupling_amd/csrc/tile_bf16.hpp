@@ -210,25 +210,30 @@ struct TileSrc {
   __device__ __forceinline__ static void load_dense_at(char* tile, const i32x4& win, int off, int wave, int j) {
     ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
   }
-  __device__ __forceinline__ static int geo_row(const int* rows, int wave, int lane, int j) {
-    asm volatile("" : "+v"(lane));
+  // geo: the row-table index of this lane's load j (its tile row, or kTile,
+  // the table's sentinel entry, for the slots past the tile) and the byte
+  // offset of its chunk within the row; both tile-independent
+  __device__ __forceinline__ static int geo_index(int wave, int lane, int j) {
     const int r = slot_row(slot(wave, lane, j));
-    if ((j + 1) * NW <= NI) return rows[r];  // all rows of this load are tile rows
-    return r < kTile ? rows[r < kTile ? r : kTile - 1] : -1;
+    return r < kTile ? r : kTile;
   }
-  __device__ __forceinline__ void load_geo(char* tile, const i32x4& all, int grow, int wave, int lane, int j) const {
-    asm volatile("" : "+v"(lane));
+  __device__ __forceinline__ static int geo_chunk(int wave, int lane, int j) {
     const int s = slot(wave, lane, j);
-    const int r = slot_row(s);
-    const int off = grow < 0 ? limit * RB : grow * RB + (s - r * CP) * 16;
-    ssc_raw_buffer_load_lds(all, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, off, 0, 0, 0);
+    return (s - slot_row(s) * CP) * 16;
+  }
+  // grow: the table entry (a row of the array, or a sentinel row at or past
+  // `limit`, which reads zeros); rows and sentinels stay below 2^24
+  __device__ __forceinline__ void load_geo_at(char* tile, const i32x4& all, int grow, int coff, int wave,
+                                              int j) const {
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16,
+                            (int)(__umul24((unsigned)grow, (unsigned)RB) + (unsigned)coff), 0, 0, 0);
   }
   // The whole tile at once (first tile of a stream).
   template <bool GEO>
   __device__ __forceinline__ void load_tile(char* tile, const int* rows, int row0, int wave, int lane) const {
     const i32x4 rs = GEO ? whole() : window(row0);
     static_for<NJ>([&](auto j) {
-      if (GEO) load_geo(tile, rs, geo_row(rows, wave, lane, j), wave, lane, j);
+      if (GEO) load_geo_at(tile, rs, rows[geo_index(wave, lane, j)], geo_chunk(wave, lane, j), wave, j);
       else load_dense(tile, rs, wave, lane, j);
     });
   }
@@ -248,9 +253,10 @@ struct VecSrc {
     const i32x4 win = make_rsrc(base + row0, n > 0 ? (unsigned)(n * 4) : 0u);
     ssc_raw_buffer_load_lds(win, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
   }
+  // grow: a row, or a sentinel at or past `limit` (reads zero)
   __device__ __forceinline__ void load_geo(float* dst, int grow, int lane) const {
     const i32x4 all = make_rsrc(base, (unsigned)(limit * 4));
-    ssc_raw_buffer_load_lds(all, (lds_void_t*)dst, 4, grow < 0 ? limit * 4 : grow * 4, 0, 0, 0);
+    ssc_raw_buffer_load_lds(all, (lds_void_t*)dst, 4, grow * 4, 0, 0, 0);
   }
 };
 
@@ -278,35 +284,36 @@ __device__ __forceinline__ void pipeline_hint() {
 }
 
 // Position -> row cursor over a run stream (one per thread; positions of a
-// thread only grow).  Run r covers positions [pf[r], pf[r+1]) and starts at
-// global row start(r).  Dense: one run of `total` rows starting at row 0.
+// thread only grow).  Run r covers the positions from the end of run r - 1
+// up to tab[r].end and maps position x to row x + tab[r].base; positions at
+// or past `total` map to the sentinel row `none`.  The entry of the run after
+// the current one is fetched ahead, when the cursor enters a run, so a later
+// crossing finds it in registers (the tile loop's end-of-step wait covers
+// the fetch); runs shorter than a tile fall back to direct reads.  Dense
+// (tab == nullptr): position x is row x.
 struct RowCursor {
-  const int* pf;       // nullptr = dense
-  const int* list;     // run r -> patch
-  const int* off;      // patch -> first row
-  int nruns, total;
-  int r, next, base;   // current run, its end position, row - position
+  const RunEntry* tab;
+  int nruns, total, none;
+  int r;
+  RunEntry cur, pre;
 
   __device__ __forceinline__ void init() {
     r = 0;
-    if (pf == nullptr) {
-      next = total;
-      base = 0;
-      return;
-    }
-    next = nruns > 0 ? pf[1] : 0;
-    base = nruns > 0 ? off[list[0]] - pf[0] : 0;
+    cur = RunEntry{total, 0};
+    pre = cur;
+    if (tab == nullptr || nruns <= 0) return;
+    cur = tab[0];
+    pre = tab[nruns > 1 ? 1 : 0];
   }
   __device__ __forceinline__ int row(int x) {
-    if (x >= total) return -1;
-    if (pf != nullptr) {
-      while (x >= next) {
-        ++r;
-        next = pf[r + 1];
-        base = off[list[r]] - pf[r];
-      }
+    if (x >= total) return none;
+    if (tab != nullptr && x >= cur.end) {
+      ++r;
+      cur = pre;
+      while (x >= cur.end) cur = tab[++r];
+      pre = tab[r + 1 < nruns ? r + 1 : r];
     }
-    return base + x;
+    return x + cur.base;
   }
 };
 
