@@ -115,52 +115,103 @@ hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st) {
 // plan (one workgroup of 1024 threads)
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanRows = 32;       // target patches per chunk of the selection pass
+constexpr int kMaxPatches = 8192;   // per side
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
 
 // Exclusive scan of f(i), i < n, written to out[0..n] (out[n] = total).
-// Chunked over the block with a running carry; returns the total.
+// Chunks of kPlanThreads with a running carry: wave scans, then a scan of
+// the wave totals.  Returns the total.
 template <typename F>
-__device__ int block_scan_excl(int n, F f, int* out, int* lds /* kPlanThreads + 1 */) {
-  const int tid = threadIdx.x;
+__device__ int block_scan_excl(int n, F f, int* out, int* lds /* kPlanWaves + 1 */) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int carry = 0;
   for (int base = 0; base < n; base += kPlanThreads) {
     const int i = base + tid;
     const int v = i < n ? f(i) : 0;
-    lds[tid] = v;
+    const int inc = wave_incl_scan(v);
+    if (lane == 63) lds[w] = inc;
     __syncthreads();
-    for (int s = 1; s < kPlanThreads; s <<= 1) {
-      const int add = tid >= s ? lds[tid - s] : 0;
-      __syncthreads();
-      lds[tid] += add;
-      __syncthreads();
+    if (w == 0) {
+      const int t = lane < kPlanWaves ? lds[lane] : 0;
+      const int ti = wave_incl_scan(t);
+      if (lane < kPlanWaves) lds[lane] = ti - t;
+      if (lane == kPlanWaves - 1) lds[kPlanWaves] = ti;
     }
-    if (i < n) out[i] = carry + lds[tid] - v;
-    const int chunk_total = lds[kPlanThreads - 1];
     __syncthreads();
-    carry += chunk_total;
+    if (i < n) out[i] = carry + lds[w] + inc - v;
+    carry += lds[kPlanWaves];
+    __syncthreads();
   }
   if (tid == 0) out[n] = carry;
   __syncthreads();
   return carry;
 }
 
+// The selection is read in chunks of kPlanRows target patches: every entry
+// (p, q) of a chunk sets bit p - p0 of mask[q] (a bit already set is a
+// repeated source patch within row p).  For the inverse lists, the rank of
+// p among the chunk's patches selecting q is the number of mask bits below
+// it, so list q is filled in ascending p, chunk after chunk, with no sort.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int lds[kPlanThreads + 1];
+  __shared__ int lds[kPlanWaves + 1];
+  __shared__ int s_offM[kMaxPatches + 1];
+  __shared__ unsigned s_mask[kMaxPatches];
+  __shared__ int s_cur[kMaxPatches];   // counts, then the next free slot of list q
+  __shared__ int s_acc[kMaxPatches];   // target rows in list q so far
+  __shared__ int s_szN[kPlanRows], s_offN[kPlanRows];
   const int tid = threadIdx.x;
-  // ---- validation
+  const int P_N = a.P_N, P_M = a.P_M, S = a.s;
+  const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
+  // ---- offsets: validation, source offsets into LDS
   int bad = 0;
   if (tid == 0) {
-    bad |= a.offN[0] != 0 || a.offN[a.P_N] != a.n_N;
-    bad |= a.offM[0] != 0 || a.offM[a.P_M] != a.n_M;
+    bad |= a.offN[0] != 0 || a.offN[P_N] != a.n_N;
+    bad |= a.offM[0] != 0 || a.offM[P_M] != a.n_M;
   }
-  for (int p = tid; p < a.P_N; p += kPlanThreads) bad |= a.offN[p] > a.offN[p + 1];
-  for (int q = tid; q < a.P_M; q += kPlanThreads) bad |= a.offM[q] > a.offM[q + 1];
-  if (a.idx != nullptr) {
-    const int n = a.P_N * a.s;
-    for (int e = tid; e < n; e += kPlanThreads) {
-      const int q = a.idx[e];
-      bad |= q < 0 || q >= a.P_M;
-      const int p = e / a.s, r = e - p * a.s;
-      for (int r2 = 0; r2 < r; ++r2) bad |= a.idx[p * a.s + r2] == q;
+  for (int p = tid; p < P_N; p += kPlanThreads) bad |= a.offN[p] > a.offN[p + 1];
+  for (int q = tid; q <= P_M; q += kPlanThreads) {
+    const int o = a.offM[q];
+    s_offM[q] = o;
+    if (q < P_M) {
+      bad |= o > a.offM[q + 1];
+      s_mask[q] = 0u;
+      s_cur[q] = 0;
+      s_acc[q] = 0;
+    }
+  }
+  bad = __syncthreads_or(bad);
+  // ---- selection: range, repeats within a row, list lengths
+  if (!bad && a.idx != nullptr) {
+    for (int p0 = 0; p0 < P_N; p0 += kPlanRows) {
+      const int e0 = p0 * S, e1 = min(p0 + kPlanRows, P_N) * S;
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
+        const int q = a.idx[e];
+        if (q < 0 || q >= P_M) {
+          bad = 1;
+          continue;
+        }
+        const unsigned bit = 1u << (e / S - p0);
+        if (atomicOr(&s_mask[q], bit) & bit) bad = 1;
+        if (inverse) atomicAdd(&s_cur[q], 1);
+      }
+      __syncthreads();
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
+        const int q = a.idx[e];
+        if (q >= 0 && q < P_M) s_mask[q] = 0u;
+      }
+      __syncthreads();
     }
   }
   bad = __syncthreads_or(bad);
@@ -174,21 +225,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // ---- padded offsets
   const int* offN = a.offN;
   const int* offM = a.offM;
-  const int gN = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + kGroup - 1) & ~(kGroup - 1); },
+  const int gN = block_scan_excl(P_N, [=](int p) { return (offN[p + 1] - offN[p] + kGroup - 1) & ~(kGroup - 1); },
                                  a.poffN, lds);
-  const int gM = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + kGroup - 1) & ~(kGroup - 1); },
+  const int gM = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + kGroup - 1) & ~(kGroup - 1); },
                                  a.poffM, lds);
   // ---- work items (row blocks of rowsQ / rowsK rows within a patch)
   int* tmp = a.scratch;  // [max(P_N, P_M) + 1]
   const int rQ = a.rowsQ, rK = a.rowsK;
-  const int nQ = block_scan_excl(a.P_N, [=](int p) { return (offN[p + 1] - offN[p] + rQ - 1) / rQ; }, tmp, lds);
-  for (int p = tid; p < a.P_N; p += kPlanThreads) {
+  const int nQ = block_scan_excl(P_N, [=](int p) { return (offN[p + 1] - offN[p] + rQ - 1) / rQ; }, tmp, lds);
+  for (int p = tid; p < P_N; p += kPlanThreads) {
     const int b = tmp[p], nt = tmp[p + 1] - b;
     for (int t = 0; t < nt; ++t) a.itemsQ[b + t] = Item{p, t * rQ};
   }
   __syncthreads();
-  const int nK = block_scan_excl(a.P_M, [=](int q) { return (offM[q + 1] - offM[q] + rK - 1) / rK; }, tmp, lds);
-  for (int q = tid; q < a.P_M; q += kPlanThreads) {
+  const int nK = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + rK - 1) / rK; }, tmp, lds);
+  for (int q = tid; q < P_M; q += kPlanThreads) {
     const int b = tmp[q], nt = tmp[q + 1] - b;
     for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * rK};
   }
@@ -196,59 +247,61 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // ---- per target patch: the run table of its key stream (the selected
   // source patches in selection order)
   if (a.run_tab != nullptr && a.idx != nullptr) {
-    for (int p = tid; p < a.P_N; p += kPlanThreads) {
+    for (int p = tid; p < P_N; p += kPlanThreads) {
       int acc = 0;
-      RunEntry* tab = a.run_tab + (size_t)p * a.s;
-      for (int r = 0; r < a.s; ++r) {
-        const int q = a.idx[(size_t)p * a.s + r];
-        const int n = offM[q + 1] - offM[q];
-        tab[r] = RunEntry{acc + n, offM[q] - acc};
+      const int* row = a.idx + (size_t)p * S;
+      RunEntry* tab = a.run_tab + (size_t)p * S;
+#pragma unroll 8
+      for (int r = 0; r < S; ++r) {
+        const int q = row[r];
+        const int o = s_offM[q], n = s_offM[q + 1] - o;
+        tab[r] = RunEntry{acc + n, o - acc};
         acc += n;
       }
     }
-    __syncthreads();
   }
-  // ---- inverse selection lists: inv[q] = target patches p with q in idx[p]
-  if (a.inv_off != nullptr && a.idx != nullptr) {
-    for (int q = tid; q < a.P_M; q += kPlanThreads) tmp[q] = 0;
+  // ---- inverse selection lists: inv[q] = target patches p with q in idx[p],
+  // ascending, and their run tables
+  if (inverse) {
+    block_scan_excl(P_M, [&](int q) { return s_cur[q]; }, a.inv_off, lds);
+    for (int q = tid; q < P_M; q += kPlanThreads) s_cur[q] = a.inv_off[q];
     __syncthreads();
-    const int n = a.P_N * a.s;
-    for (int e = tid; e < n; e += kPlanThreads) atomicAdd(&tmp[a.idx[e]], 1);
-    __syncthreads();
-    block_scan_excl(a.P_M, [=](int q) { return tmp[q]; }, a.inv_off, lds);
-    for (int q = tid; q < a.P_M; q += kPlanThreads) tmp[q] = 0;
-    __syncthreads();
-    for (int e = tid; e < n; e += kPlanThreads) {
-      const int q = a.idx[e];
-      const int slot = atomicAdd(&tmp[q], 1);
-      a.inv_idx[a.inv_off[q] + slot] = e / a.s;
-    }
-    __syncthreads();
-    // each list ascending (insertion sort; lists hold distinct patches)
-    for (int q = tid; q < a.P_M; q += kPlanThreads) {
-      const int b = a.inv_off[q], e = a.inv_off[q + 1];
-      for (int i = b + 1; i < e; ++i) {
-        const int v = a.inv_idx[i];
-        int j = i - 1;
-        while (j >= b && a.inv_idx[j] > v) {
-          a.inv_idx[j + 1] = a.inv_idx[j];
-          --j;
-        }
-        a.inv_idx[j + 1] = v;
+    for (int p0 = 0; p0 < P_N; p0 += kPlanRows) {
+      const int e0 = p0 * S, e1 = min(p0 + kPlanRows, P_N) * S;
+      if (tid < kPlanRows && p0 + tid < P_N) {
+        const int o = offN[p0 + tid];
+        s_offN[tid] = o;
+        s_szN[tid] = offN[p0 + tid + 1] - o;
       }
-    }
-    if (a.inv_tab != nullptr) {
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) atomicOr(&s_mask[a.idx[e]], 1u << (e / S - p0));
       __syncthreads();
-      for (int q = tid; q < a.P_M; q += kPlanThreads) {
-        const int b = a.inv_off[q], e = a.inv_off[q + 1];
-        int acc = 0;
-        for (int i = b; i < e; ++i) {
-          const int p = a.inv_idx[i];
-          const int n = offN[p + 1] - offN[p];
-          a.inv_tab[i] = RunEntry{acc + n, offN[p] - acc};
-          acc += n;
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
+        const int q = a.idx[e], j = e / S - p0;
+        unsigned below = s_mask[q] & ((1u << j) - 1u);
+        const int slot = s_cur[q] + __popc(below);
+        int pre = s_acc[q];
+        while (below) {
+          pre += s_szN[__ffs(below) - 1];
+          below &= below - 1u;
+        }
+        a.inv_idx[slot] = p0 + j;
+        if (a.inv_tab != nullptr) a.inv_tab[slot] = RunEntry{pre + s_szN[j], s_offN[j] - pre};
+      }
+      __syncthreads();
+      // the chunk's last patch selecting q advances list q
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
+        const int q = a.idx[e], j = e / S - p0;
+        const unsigned m = s_mask[q];
+        if (31 - __clz(m) == j) {
+          int add = 0;
+          for (unsigned b = m; b; b &= b - 1u) add += s_szN[__ffs(b) - 1];
+          s_cur[q] += __popc(m);
+          s_acc[q] += add;
         }
       }
+      __syncthreads();
+      for (int e = e0 + tid; e < e1; e += kPlanThreads) s_mask[a.idx[e]] = 0u;
+      __syncthreads();
     }
   }
   if (tid == 0) {
@@ -328,7 +381,6 @@ hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // scores and top-s (one workgroup per target patch, the score row in LDS)
 // ---------------------------------------------------------------------------
-constexpr int kMaxPatches = 8192;
 constexpr int kMaxD = 128;
 
 // The score row lives in LDS: statically sized for the largest P_M, or
