@@ -71,6 +71,7 @@ struct Layout {
   size_t inv_off = kNone, inv_idx = kNone, scratch = kNone;
   size_t Qbar = kNone, KbarT = kNone;
   size_t run_tab = kNone, inv_tab = kNone;
+  size_t knorm = kNone;  // bf16 forward: partial maxima of the key-row norms
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
 };
@@ -94,6 +95,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     case SSC_OP_DENSE_FWD:
     case SSC_OP_GEO_FWD:
       L.Vp = take(nM * (size_t)kpad_fwd_bf16(k) * 2);
+      L.knorm = take(kNormParts * 4);
       break;
     case SSC_OP_DENSE_BWD:
     case SSC_OP_GEO_BWD:
@@ -405,9 +407,11 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
     PackArgs pv{};
     pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
     SSC_TRY(launch_pack(DType::BF16, pv, L.npadM / kGroup, s));
+    float* knorm = at<float>(ws, L.knorm);
+    SSC_TRY(launch_keynorm(K, n_M, d, knorm, s));
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
-    a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M;
+    a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M; a.knorm2 = knorm;
     const int rQ = kRowsFwd;
     SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ, s); }));
     return SSC_OK;
@@ -601,8 +605,10 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     PackArgs pv{};
     pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
     SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+    float* knorm = at<float>(ws, L.knorm);
+    SSC_TRY(launch_keynorm(K, n_M, d, knorm, hs));
     FwdArgs a{};
-    a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
+    a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse; a.knorm2 = knorm;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
     a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
     a.idx = idx; a.s = s; a.offM = offM; a.run_tab = at<RunEntry>(ws, L.run_tab);

@@ -23,7 +23,7 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
 //   c = 0, 1: scores of key half c (keys 32c .. 32c+31), A = K rows;
 //   c = 2, 3: O += P V over key half c - 2, A = transposed V reads.
 // Operand reads run AH steps ahead of their MFMA.  The softmax of half 0
-// (row maximum, exp2, row sum, bf16 packing) runs in slices during chain 1,
+// (row maximum if tracked, exp2, bf16 packing) runs in slices during chain 1,
 // that of half 1 during chain 2.  The next tile's direct loads are spread
 // over the first half of the pipeline; scheduling fences between steps keep
 // this order.
@@ -33,14 +33,18 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
 // bf16 probabilities in that column of O; without a spare column (k = KP)
 // the softmax slices add them up.
 //
-// Softmax reference: the probabilities of a tile are taken relative to a
-// reference fixed for the whole tile (the first tile: the maximum of its
-// first half; later tiles: the running reference), and the accumulators are
-// rescaled only between tiles, when the running maximum has moved more than
-// 8 (log2 units) above the reference.  A tile whose maximum exceeds its
-// reference by more than 32 could overflow; a workgroup that saw one redoes
-// its rows in a second pass with the exact row maxima of the first pass as a
-// fixed reference (probabilities <= 1), so the result is exact either way.
+// Softmax reference.  First pass: one fixed reference per row, the bound
+// c2 |q| max_j |k_j| on its scores, so no probability exceeds 1 and no row
+// maximum is tracked.  Only if that bound sits so far above a row's scores
+// that its row sum falls below 2^-60 (an underflow risk) does the workgroup
+// redo its rows with a running reference: the probabilities of a tile are
+// taken relative to a reference fixed for the whole tile (the first tile:
+// the maximum of its first half; later tiles: the running reference), and
+// the accumulators are rescaled only between tiles, when the running maximum
+// has moved more than 8 (log2 units) above the reference.  A tile whose
+// maximum exceeds its reference by more than 32 could overflow; a workgroup
+// that saw one redoes its rows once more with the exact row maxima as a
+// fixed reference, so the result is exact in every case.
 template <int D, int KP, int NW, bool GEO, bool ONES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
@@ -96,13 +100,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     qf[dc] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)row * D + dc * 16 + h * 8) : bf16x8{};
     if (neg) qf[dc] = neg_bf16x8(qf[dc]);
   }
+  // Bounded reference: every score of this row is at most |q| max_j |k_j|
+  // (Cauchy-Schwarz), so probabilities relative to c2 |q| Kmax never exceed 1
+  // and need no running maximum.  Kmax comes from the per-workgroup partial
+  // maxima of the key-row norms.
+  float m_bound;
+  {
+    float qn2 = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qn2 = fmaf((float)qf[dc][e], (float)qf[dc][e], qn2);
+    qn2 += xor32(qn2);
+    float km2 = 0.f;
+    for (int j = lane; j < kNormParts; j += 64) km2 = fmaxf(km2, a.knorm2[j]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) km2 = fmaxf(km2, __shfl_xor(km2, m, 64));
+    m_bound = c2 * sqrtf(qn2 * km2);
+  }
 
   f32x16 acc[KP / 32];
   // Initial score accumulators: zero, except in a partial last tile, where
   // keys at or past its end start at -inf (their probabilities are then 0).
   f32x16 bias[2];
   float m_run, l_run, m_true = -INFINITY;
-  bool fixed = false;
+  // mode 0: bounded reference; 1: running reference (when the bound left a
+  // row sum below 2^-60, i.e. the bound was far above the scores); 2: the
+  // exact row maxima of mode 1 as a fixed reference
+  int mode = 0;
 
   constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;
   constexpr int C1 = NS, C2 = 2 * NS, C3 = 2 * NS + NPV, U = 2 * NS + 2 * NPV, AH = 5;
@@ -123,12 +148,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
                                  : TileSrc<KP, NW>::geo_index(wave, lane, j - NJK);
   });
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // row sum of this lane's row (both halves)
+  auto row_sum = [&]() {
+    float l_part = l_run;
+    if (ONES) {
+      // the row sum sits in column k of O, held by the lanes of one half
+      l_part = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < KP / 32; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (cb * 32 + c_row(i, h) == a.k) l_part = acc[cb][i];
+    }
+    return l_part + xor32(l_part);
+  };
+
+  for (;;) {
+    const bool fixed = mode == 2;
 #pragma unroll
     for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
     bias[0] = bias[1] = f32x16{};
     l_run = 0.f;
-    m_run = fixed ? m_true : -INFINITY;
+    m_run = mode == 0 ? m_bound : fixed ? m_true : -INFINITY;
     bool lagged = false;
 
     if (GEO && tid < kTile) {
@@ -149,10 +190,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // other, so the compiler can tell the direct loads in flight from the LDS
     // reads.  The stream's last tile may be partial: its keys at or past
     // nvalid start from a score of -inf (bias, set before the pipeline).
-    auto step = [&](const int t, const int b, char* Kt, char* Kn) {
+    auto step = [&](auto bound_c, const int t, const int b, char* Kt, char* Kn) {
+      constexpr bool BOUND = decltype(bound_c)::value;
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
-      const bool first = t == 0 && !fixed;
+      const bool first = !BOUND && t == 0 && !fixed;
       if (nvalid < kTile) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
@@ -187,6 +229,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (k <= 1) {
 #pragma unroll
           for (int i = 8 * k; i < 8 * k + 8; ++i) sv[hb][i] = sc[hb][i];
+          if (BOUND) return;
           float m = k == 0 ? -INFINITY : mx[hb];
 #pragma unroll
           for (int i = 8 * k; i < 8 * k + 8; ++i) m = fmaxf(m, sv[hb][i]);
@@ -250,41 +293,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       // Between tiles: the sums of this tile join the running sum at the
       // tile's reference; move the reference up when the maximum ran ahead.
       l_run += lsum;
-      m_run = mref;
-      const float tmax = fmaxf(mh[0], mh[1]);
-      m_true = fmaxf(m_true, tmax);
-      lagged = lagged || tmax > mref + 32.f;
-      if (!fixed && __any(tmax > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = fexp2(m_run - m_new);
+      if (!BOUND) {
+        m_run = mref;
+        const float tmax = fmaxf(mh[0], mh[1]);
+        m_true = fmaxf(m_true, tmax);
+        lagged = lagged || tmax > mref + 32.f;
+        if (!fixed && __any(tmax > m_run + 8.f)) {
+          const float m_new = fmaxf(m_run, tmax);
+          const float alpha = fexp2(m_run - m_new);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[cb] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
+          for (int cb = 0; cb < NCB; ++cb) acc[cb] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
       }
       if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
       wait_loads();
       __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, 0, sm0, sm1);
-      if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
+    auto run = [&](auto bound_c) {
+      for (int t = 0; t < ntiles; t += 2) {
+        step(bound_c, t, 0, sm0, sm1);
+        if (t + 1 < ntiles) step(bound_c, t + 1, 1, sm1, sm0);
+      }
+    };
+    if (mode == 0) {
+      run(std::true_type{});
+      const float lt = row_sum();
+      if (!__syncthreads_or(total > 0 && !(lt >= 0x1p-60f))) break;
+      mode = 1;
+      continue;
     }
+    run(std::false_type{});
     if (fixed || !__syncthreads_or(lagged)) break;
-    fixed = true;
+    mode = 2;
   }
 
-  float l_part = l_run;
-  if (ONES) {
-    // the row sum sits in column k of O, held by the lanes of one half
-    l_part = 0.f;
-#pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (cb * 32 + c_row(i, h) == a.k) l_part = acc[cb][i];
-  }
-  const float l_tot = l_part + xor32(l_part);
+  const float l_tot = row_sum();
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     float* Orow = a.O + (size_t)row * a.k;

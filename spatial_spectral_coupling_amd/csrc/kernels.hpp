@@ -49,7 +49,13 @@ struct FwdArgs {
   // run_tab [P_N][s] the run table of each target patch's key stream.
   const void* Vp;
   const RunEntry* run_tab;
+  const float* knorm2;  // [kNormParts] partial maxima of |k_j|^2 over the key rows
 };
+
+// Partial maxima of the squared key-row norms (bf16 forward): kNormParts
+// workgroups, one partial each.
+constexpr int kNormParts = 256;
+hipError_t launch_keynorm(const void* K, int n, int d, float* part, hipStream_t st);
 
 // dQ pass.
 struct DqArgs {

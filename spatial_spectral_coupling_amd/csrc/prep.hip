@@ -160,6 +160,39 @@ __global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
   }
 }
 
+// Squared norms of bf16 rows (d = 64 or 128, 16-byte aligned rows), their
+// maximum per workgroup: one thread per 16-byte chunk, the d / 8 chunks of a
+// row reduced over consecutive lanes, grid-stride over the rows.
+__global__ __launch_bounds__(256) void keynorm_kernel(const bf16* K, int n, int d, float* part) {
+  __shared__ float wmax[4];
+  const int cpr = d / 8;                 // chunks per row: 8 or 16
+  const int rows_per_block = 256 / cpr;
+  const int tid = threadIdx.x, c = tid % cpr;
+  float best = 0.f;
+  for (int r0 = blockIdx.x * rows_per_block; r0 < n; r0 += gridDim.x * rows_per_block) {
+    const int r = r0 + tid / cpr;
+    float s2 = 0.f;
+    if (r < n) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(K + (size_t)r * d + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s2 = fmaf((float)v[e], (float)v[e], s2);
+    }
+    for (int m = cpr / 2; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
+    best = fmaxf(best, s2);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m, 64));
+  if ((tid & 63) == 0) wmax[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+hipError_t launch_keynorm(const void* K, int n, int d, float* part, hipStream_t st) {
+  hipLaunchKernelGGL(keynorm_kernel, dim3(kNormParts), dim3(256), 0, st, reinterpret_cast<const bf16*>(K), n, d,
+                     part);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (t == DType::BF16 && a.poff == nullptr && a.Xg == nullptr && a.Xp != nullptr && (a.W & 7) == 0) {

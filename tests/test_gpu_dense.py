@@ -107,6 +107,40 @@ def test_dense_rows_of_map_sum_to_one_and_determinism():
     assert np.max(np.abs(col - 1)) < 1e-2
 
 
+def test_dense_reference_fallbacks():
+    """The forward's first pass takes each row's reference from the bound
+    |q| max|k| on its scores.  Row 5 (query 60 e1) meets a key of norm 60
+    orthogonal to it, so the bound sits 459 (log2 units) above its scores and
+    its row sum underflows: the workgroup redoes its rows with a running
+    reference, and since a later tile's maximum (key 200 = 5 e1, 38 above the
+    first tile's) runs more than 32 ahead of it, once more with exact row
+    maxima.  Row 129 (query 60 e3, second workgroup) only needs the running
+    reference.  Both workgroups must still match the oracle."""
+    say("dense reference fallbacks")
+    nN, nM, d, k = 130, 300, 128, 200
+    c = gen.make_small(nN, nM, d, k, "bf16", seed=21)
+    Qf = f64(c["Q"], "bf16").astype(np.float32)
+    Kf = f64(c["K"], "bf16").astype(np.float32)
+    Qf[5] = 0.0
+    Qf[5, 0] = 60.0
+    Qf[129] = 0.0
+    Qf[129, 2] = 60.0
+    Kf[:, 0] = 0.0               # no key but 200 leans along e1
+    Kf[200] = 0.0
+    Kf[200, 0] = 5.0
+    Kf[250] = 0.0
+    Kf[250, 1] = 60.0            # the largest key norm, orthogonal to rows 5 and 129
+    c["Q"], c["K"] = gen.bf16_bits_from_f32(Qf), gen.bf16_bits_from_f32(Kf)
+    scale = 1 / math.sqrt(d)
+    Q, K, V = (to_dev(c[x], "bf16") for x in ("Q", "K", "V"))
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, scale)
+    Or, lser = dense_fwd(f64(c["Q"], "bf16"), f64(c["K"], "bf16"), f64(c["V"], "bf16"), scale)
+    check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what="reference fallbacks")
+    err5 = np.max(np.abs(O[5].cpu().numpy() - Or[5]))
+    say("row 5 max-abs", err5)
+    assert err5 <= 2e-2
+
+
 def test_dense_60k_full_size_sampled():
     """The 60k workload: sampled rows of O, lse and dQ; dK/dV of a backward
     whose upstream gradient lives on sampled rows; identities at full size."""
