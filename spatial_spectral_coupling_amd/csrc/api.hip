@@ -29,6 +29,9 @@ int kpad_for(int k) {
 // bf16 forward: V padded with at least one spare column (the ones column
 // that carries the softmax row sums) unless k is the largest padded width.
 int kpad_fwd_bf16(int k) { return k < kKPads[4] ? kpad_for(k + 1) : kpad_for(k); }
+// bf16 backward: two spare columns when they fit (V: ones, dO: -D as bf16
+// high + low parts, so the dP products yield dP - D).
+int kpad_bwd_bf16(int k) { return k + 2 <= kKPads[4] ? kpad_for(k + 2) : kpad_for(k); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -99,8 +102,8 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
       break;
     case SSC_OP_DENSE_BWD:
     case SSC_OP_GEO_BWD:
-      L.Vp = take(nM * KP * 2);
-      L.dOp = take(nN * KP * 2);
+      L.Vp = take(nM * (size_t)kpad_bwd_bf16(k) * 2);
+      L.dOp = take(nN * (size_t)kpad_bwd_bf16(k) * 2);
       L.lse2p = take(nN * 4);
       L.Dp = take(nN * 4);
       break;
@@ -456,11 +459,13 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
   if (dtype == SSC_BF16) {
+    const int KPb = kpad_bwd_bf16(k);
+    const bool dcol = k + 2 <= KPb;
     PackArgs pv{};
-    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPb; pv.ones = dcol ? 2 : 0;
     SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, s));
     PackArgs po{};
-    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KP;
+    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KPb; po.dcol = dcol;
     po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
     SSC_TRY(launch_pack(T, po, L.npadN / kGroup, s));
     const float c2 = scale * kLog2e;
@@ -469,13 +474,13 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
       q.Qp = Q; q.dOp = po.Xp; q.lse2p = po.lse2p; q.Dp = po.Dp; q.Kp = K; q.Vp = pv.Xp; q.dQ = dQ;
       q.n_N = n_N; q.c2 = c2; q.scale = scale; q.n_M = n_M;
       const int rQ = kRowsDq;
-      SSC_TRY(timed("dq", s, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ, s); }));
+      SSC_TRY(timed("dq", s, [&] { return launch_dq_bf16(d, KPb, dcol, q, (n_N + rQ - 1) / rQ, s); }));
     }
     DkvArgs b{};
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
     const int rK = kRowsDkv;
-    SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK, s); }));
+    SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK, s); }));
     return SSC_OK;
   }
 
@@ -659,11 +664,13 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     return st;
   int* counters = at<int>(ws, L.counters);
   if (dtype == SSC_BF16) {
+    const int KPb = kpad_bwd_bf16(k);
+    const bool dcol = k + 2 <= KPb;
     PackArgs pv{};
-    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KP;
+    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPb; pv.ones = dcol ? 2 : 0;
     SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
     PackArgs po{};
-    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KP;
+    po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KPb; po.dcol = dcol;
     po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
     SSC_TRY(launch_pack(T, po, L.npadN / kGroup, hs));
     const float c2 = scale * kLog2e;
@@ -674,7 +681,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
       q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.n_M = n_M;
       q.idx = idx; q.s = s; q.offM = offM; q.run_tab = at<RunEntry>(ws, L.run_tab);
       const int rQ = kRowsDq;
-      SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KP, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
+      SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KPb, dcol, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
     }
     DkvArgs b{};
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
@@ -682,7 +689,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
     b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_tab = at<RunEntry>(ws, L.inv_tab);
     const int rK = kRowsDkv;
-    SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KP, b, (n_M + rK - 1) / rK + P_M, hs); }));
+    SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK + P_M, hs); }));
     return SSC_OK;
   }
   int* poffN = at<int>(ws, L.poffN);

@@ -9,7 +9,7 @@ namespace tb {
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-template <int D, int KP, int NW, bool GEO>
+template <int D, int KP, int NW, bool GEO, bool DCOL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
   constexpr int QB = TileSrc<D, NW>::ALLOC, OB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (GEO) sL.load_geo(ls0, rowtab[0][lane], lane);
       else sL.load_dense(ls0, 0, lane);
     }
-    if (wave == NW - 1) {
+    if (!DCOL && wave == NW - 1) {
       if (GEO) sD.load_geo(ds0, rowtab[0][lane], lane);
       else sD.load_dense(ds0, 0, lane);
     }
@@ -186,14 +186,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (k == kRead[0] || k == kRead[1] || k == kRead[2] || k == kRead[3]) {
         const int g = k == kRead[0] ? 0 : k == kRead[1] ? 1 : k == kRead[2] ? 2 : 3;
         lg[g] = *reinterpret_cast<const f32x4*>(lsc + qb * 32 + 4 * h + 8 * g);
-        dg[g] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * g);
+        if (!DCOL) dg[g] = *reinterpret_cast<const f32x4*>(dsc + qb * 32 + 4 * h + 8 * g);
       } else {
         const int m = k < 4 ? k - 2 : k < 7 ? k - 3 : k - 4;
         const int i = 2 * m, g = i >> 2, e = i & 3;
         const float p0 = fexp2(fmaf(sc[qb][i], c2, -lg[g][e]));
         const float p1 = fexp2(fmaf(sc[qb][i + 1], c2, -lg[g][e + 1]));
         put_pair(pk[qb][m >> 2], m & 3, p0, p1);
-        put_pair(dk8[qb][m >> 2], m & 3, p0 * (dp[qb][i] - dg[g][e]), p1 * (dp[qb][i + 1] - dg[g][e + 1]));
+        // with DCOL the ones / -D columns already made dp = dP - D
+        const float e0 = DCOL ? dp[qb][i] : dp[qb][i] - dg[g][e];
+        const float e1 = DCOL ? dp[qb][i + 1] : dp[qb][i + 1] - dg[g][e + 1];
+        put_pair(dk8[qb][m >> 2], m & 3, p0 * e0, p1 * e1);
       }
     };
     const int* rn = rowtab[b ^ 1];
@@ -212,8 +215,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         else sO.load_dense_at(Qn + QB, winO, loff[j], wave, j - NJQ);
       } else {
         // even waves fetch lse, odd waves D (duplicate fetches write the
-        // same values); a wave-uniform select, no branch in the pipeline
-        const bool odd = wave & 1;
+        // same values; with DCOL every wave fetches lse); a wave-uniform
+        // select, no branch in the pipeline
+        const bool odd = !DCOL && (wave & 1);
         const VecSrc src = odd ? sD : sL;
         float* dst = odd ? dsn : lsn;
         if (GEO) src.load_geo(dst, grow, lane);
@@ -300,17 +304,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   X(64, 64)                   \
   X(64, 32)
 
-hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                                       \
-  if (D == DD && KP == KK) {                                                                                \
-    if (a.items != nullptr)                                                                                 \
-      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
-    else                                                                                                    \
-      hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
-    return hipGetLastError();                                                                               \
+hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st) {
+#define SSC_L1(DD, KK, CC)                                                                                    \
+  if (a.items != nullptr)                                                                                   \
+    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true, CC>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
+  else                                                                                                      \
+    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false, CC>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
+  return hipGetLastError();
+#define SSC_L(DD, KK)                   \
+  if (dcol && D == DD && KP == KK) {    \
+    SSC_L1(DD, KK, true)                \
   }
   SSC_BF16_INSTANCES(SSC_L)
+  if (!dcol && KP == 256) {
+    if (D == 128) {
+      SSC_L1(128, 256, false)
+    }
+    if (D == 64) {
+      SSC_L1(64, 256, false)
+    }
+  }
 #undef SSC_L
+#undef SSC_L1
   return hipErrorInvalidValue;
 }
 

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // bf16 packing).  Iteration t runs A0(t), B1(t-1), A1(t), B0(t): B1 of the
 // previous tile uses transposed K fragments kept in registers, so every
 // softmax gets a window of a full A chain plus a B chain to hide in.
-template <int D, int KP, int NW, bool GEO>
+template <int D, int KP, int NW, bool GEO, bool DCOL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
@@ -422,7 +422,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   for (int kc = 0; kc < KP / 16; ++kc)
     of[kc] = row_ok ? *reinterpret_cast<const bf16x8*>(dOp + (size_t)row * KP + kc * 16 + h * 8) : bf16x8{};
   const float lse2 = row_ok ? a.lse2p[row] : INFINITY;
-  const float Dq = row_ok ? a.Dp[row] : 0.f;
+  // dP accumulators end at dP - D: with DCOL the ones / -D columns of V and
+  // dO subtract D inside the MFMAs, otherwise they start at -D
+  const float Dq = !DCOL && row_ok ? a.Dp[row] : 0.f;
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dinit[i] = -Dq;
   const float c2 = a.c2;
 
   f32x16 dq[D / 32];
@@ -488,12 +493,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
   for (int j = 0; j < LB; ++j) kt[j] = bf16x8{};
 
-  // Slice k of the softmax of one half (scores sv, dP dv, packed dS out):
-  // element pair 2k, 2k+1 (P = exp2(S c2 - lse2), dS = P (dP - D)) packed
-  // into out.
+  // Slice k of the softmax of one half (scores sv, dv = dP - D, packed dS
+  // out): element pair 2k, 2k+1 (P = exp2(S c2 - lse2), dS = P (dP - D))
+  // packed into out.
   auto slice = [&](f32x16& sv, f32x16& dv, bf16x8* out, const int k) {
-    const float d0 = fexp2(fmaf(sv[2 * k], c2, -lse2)) * (dv[2 * k] - Dq);
-    const float d1 = fexp2(fmaf(sv[2 * k + 1], c2, -lse2)) * (dv[2 * k + 1] - Dq);
+    const float d0 = fexp2(fmaf(sv[2 * k], c2, -lse2)) * dv[2 * k];
+    const float d1 = fexp2(fmaf(sv[2 * k + 1], c2, -lse2)) * dv[2 * k + 1];
     put_pair(out[k >> 2], k & 3, d0, d1);
   };
 
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int i = 0; i < 16; ++i) bias[kb][i] = kb * 32 + c_row(i, h) < nvalid ? 0.f : -INFINITY;
     }
-    f32x16 sc0 = bias[0], dp0 = f32x16{};
+    f32x16 sc0 = bias[0], dp0 = dinit;
     bf16x8 ds0[2];
 
     auto operand = [&](const int u) -> bf16x8 {
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     auto pre = [&](const int u) {
       if (u == CZ) {  // A1(t) starts: fresh accumulators for half 1
         sc1 = bias[1];
-        dp1 = f32x16{};
+        dp1 = dinit;
       }
     };
 
@@ -667,17 +672,28 @@ hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                                       \
-  if (D == DD && KP == KK) {                                                                                \
-    if (a.items != nullptr)                                                                                 \
-      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
-    else                                                                                                    \
-      hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
-    return hipGetLastError();                                                                               \
+hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st) {
+#define SSC_L1(DD, KK, CC)                                                                                   \
+  if (a.items != nullptr)                                                                                  \
+    hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, true, CC>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
+  else                                                                                                     \
+    hipLaunchKernelGGL((tb::dq_bf16<DD, KK, kWavesQ, false, CC>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+  return hipGetLastError();
+#define SSC_L(DD, KK)                   \
+  if (dcol && D == DD && KP == KK) {    \
+    SSC_L1(DD, KK, true)                \
   }
   SSC_BF16_INSTANCES(SSC_L)
+  if (!dcol && KP == 256) {
+    if (D == 128) {
+      SSC_L1(128, 256, false)
+    }
+    if (D == 64) {
+      SSC_L1(64, 256, false)
+    }
+  }
 #undef SSC_L
+#undef SSC_L1
   return hipErrorInvalidValue;
 }
 

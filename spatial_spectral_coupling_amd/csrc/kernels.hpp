@@ -115,7 +115,8 @@ struct PackArgs {
   void* Xp;             // [npad x W] or nullptr
   void* Xg;             // [npad/16][W][16] or nullptr
   int n, w, W;
-  int ones;             // 1: column w of every row present holds 1 (w < W)
+  int ones;             // columns w .. w + ones - 1 of every row present hold 1
+  int dcol;             // with O: columns w, w + 1 hold -D as bf16 high + low parts
   const int* poff;      // nullptr: dense (position = row)
   const int* off;
   int P;
@@ -192,8 +193,10 @@ hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStr
 // ones: column k of the padded V holds ones (k < KP); KP = 256 also runs
 // without (k = 256)
 hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st);
-hipError_t launch_dq_bf16(int D, int KP, const DqArgs& a, int grid, hipStream_t st);
-hipError_t launch_dkv_bf16(int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
+// dcol: V carries two ones columns and dO the high / low parts of -D there
+// (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
+hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);
+hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st);
 hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 bool supported(DType t, int D, int KP);

@@ -104,10 +104,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
-// bf16 rows padded to W columns (position = row), plus the rowdot / lse
-// extras: 16 lanes per row, each owning the 16-byte chunks j, j + 16, ... of
-// the padded row; VEC: w % 8 == 0 and 16-byte aligned rows (of X and O),
-// so every chunk inside the row is one 16-byte load (two for O).
+// bf16 rows padded to W <= 256 columns (position = row), plus the rowdot /
+// lse extras: 16 lanes per row, each owning the 16-byte chunks j and j + 16
+// of the padded row; VEC: w % 8 == 0 and 16-byte aligned rows (of X and O),
+// so every chunk inside the row is one 16-byte load (two for O).  Present
+// rows get `ones` columns of 1 from column w on; with dcol (and O), columns w
+// and w + 1 hold -D split into a bf16 high part and a bf16 low part (their
+// sum is -D to about 2^-17 relative), so a product with a ones column adds -D.
 template <bool VEC>
 __global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
   const int r = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
@@ -117,46 +120,62 @@ __global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
   bf16* Xp = reinterpret_cast<bf16*>(a.Xp) + (size_t)r * a.W;
   const float* O = a.O != nullptr ? a.O + (size_t)r * w : nullptr;
   float part = 0.f;
-  for (int c = j; c < cw; c += 16) {
-    const int c0 = 8 * c;
-    bf16x8 v;
+  bf16x8 v[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int c = j + 16 * m, c0 = 8 * c;
+    if (c >= cw) continue;
     if (VEC && present && c0 + 8 <= w) {
-      v = *reinterpret_cast<const bf16x8*>(X + c0);
+      v[m] = *reinterpret_cast<const bf16x8*>(X + c0);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int col = c0 + e;
         float x = 0.f;
         if (present && col < w) x = (float)X[col];
-        else if (present && col == w && a.ones) x = 1.f;
-        v[e] = (bf16)x;
+        else if (present && col < w + a.ones) x = 1.f;
+        v[m][e] = (bf16)x;
       }
     }
     if (O != nullptr && present) {
       if (VEC && c0 + 8 <= w) {
         const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + c0), o1 = *reinterpret_cast<const f32x4*>(O + c0 + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part += (float)v[e] * o0[e] + (float)v[e + 4] * o1[e];
+        for (int e = 0; e < 4; ++e) part += (float)v[m][e] * o0[e] + (float)v[m][e + 4] * o1[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (c0 + e < w) part += (float)v[e] * O[c0 + e];
+          if (c0 + e < w) part += (float)v[m][e] * O[c0 + e];
       }
     }
-    *reinterpret_cast<bf16x8*>(Xp + c0) = v;
   }
   if (a.Dp != nullptr) {
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 16);
-    if (j == 0) {
-      a.Dp[r] = present ? part : 0.f;
-      float l2 = INFINITY;
-      if (present) {
-        const float l = a.lse[r];
-        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+  if (a.dcol && present) {
+    const bf16 hi = (bf16)(-part);
+    const bf16 lo = (bf16)(-part - (float)hi);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = 8 * (j + 16 * m) + e;
+        if (col == w) v[m][e] = hi;
+        if (col == w + 1) v[m][e] = lo;
       }
-      a.lse2p[r] = l2;
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    if (j + 16 * m < cw) *reinterpret_cast<bf16x8*>(Xp + 8 * (j + 16 * m)) = v[m];
+  if (a.Dp != nullptr && j == 0) {
+    a.Dp[r] = present ? part : 0.f;
+    float l2 = INFINITY;
+    if (present) {
+      const float l = a.lse[r];
+      l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
+    a.lse2p[r] = l2;
   }
 }
 
@@ -195,7 +214,7 @@ hipError_t launch_keynorm(const void* K, int n, int d, float* part, hipStream_t 
 
 hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (t == DType::BF16 && a.poff == nullptr && a.Xg == nullptr && a.Xp != nullptr && (a.W & 7) == 0) {
+  if (t == DType::BF16 && a.poff == nullptr && a.Xg == nullptr && a.Xp != nullptr && (a.W & 7) == 0 && a.W <= 256) {
     // dense row padding: one block per group of 16 positions
     const bool vec = (a.w & 7) == 0 && (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.O) & 15) == 0;
