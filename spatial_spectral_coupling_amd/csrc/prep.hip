@@ -444,6 +444,42 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 // fp64 (hence equal to the sum in any order, row order included) when the
 // patch has at most 4096 rows and its nonzero entries lie within a factor
 // 2^36 (bf16) or 2^20 (fp32) of each other.
+// bf16 rows (16-byte aligned, d in {64, 128}): thread t owns the 8-column
+// chunk t % (d/8) and the row phase t / (d/8) (16 or 32 phases), one 16-byte
+// load per row; same fixed phase order, same exactness.
+__global__ __launch_bounds__(256) void pool_bf16_kernel(PoolArgs a) {
+  __shared__ double part[256][8];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const bool tgt = b < a.P_N;
+  const int p = tgt ? b : b - a.P_N;
+  const int* off = tgt ? a.offN : a.offM;
+  const int n = tgt ? a.n_N : a.n_M;
+  const bf16* X = reinterpret_cast<const bf16*>(tgt ? a.Q : a.K);
+  const int begin = min(max(off[p], 0), n);
+  const int end = min(max(off[p + 1], begin), n);
+  const int cnt = end - begin;
+  const int nch = a.d / 8, nph = 256 / nch;
+  const int ch = tid % nch, ph = tid / nch;
+  double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int r = begin + ph; r < end; r += nph) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(X + (size_t)r * a.d + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += (double)(float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[tid][e] = s[e];
+  __syncthreads();
+  if (tid < a.d) {
+    const int c = tid, cc = c / 8, e = c % 8;
+    double t = 0.0;
+    for (int q = 0; q < nph; ++q) t += part[q * nch + cc][e];
+    const double m = cnt > 0 ? t / (double)cnt : 0.0;
+    if (tgt) a.Qbar[(size_t)p * a.d + c] = m;
+    else a.KbarT[(size_t)c * a.P_M + p] = m;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ double part[256][2];
@@ -489,7 +525,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st) {
   const int grid = a.P_N + a.P_M;
-  if (t == DType::BF16) hipLaunchKernelGGL(pool_kernel<bf16>, dim3(grid), dim3(256), 0, st, a);
+  if (t == DType::BF16 && (reinterpret_cast<uintptr_t>(a.Q) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.K) & 15) == 0 &&
+      (a.d == 64 || a.d == 128))
+    hipLaunchKernelGGL(pool_bf16_kernel, dim3(grid), dim3(256), 0, st, a);
+  else if (t == DType::BF16) hipLaunchKernelGGL(pool_kernel<bf16>, dim3(grid), dim3(256), 0, st, a);
   else hipLaunchKernelGGL(pool_kernel<float>, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
