@@ -56,6 +56,25 @@ def executed_pairs(offN, offM, idx) -> int:
     return int(np.sum(nT * nS[idx].sum(axis=1)))
 
 
+def executed_block_flops(offN, offM, idx, d, k, rows=128, tile=64):
+    """Algorithmic fwd + bwd work counted over the blocks the geo kernels
+    execute: work items of `rows` owned rows (padded) times whole tiles of
+    `tile` streamed rows.  Target-side items (forward, dQ) stream the selected
+    source patches; source-side items (dK/dV) stream the target patches that
+    selected them.  Returns (flop, target-side block pairs, source-side block
+    pairs)."""
+    import numpy as np
+    nT = np.diff(offN).astype(np.int64)
+    nS = np.diff(offM).astype(np.int64)
+    keys = nS[idx].sum(axis=1)
+    q_pairs = int(np.sum(-(-nT // rows) * rows * (-(-keys // tile)) * tile))
+    stream = np.zeros(len(nS), np.int64)
+    np.add.at(stream, idx.ravel(), np.repeat(nT, idx.shape[1]))
+    kv_pairs = int(np.sum(-(-nS // rows) * rows * (-(-stream // tile)) * tile))
+    flop = 2.0 * q_pairs * (2 * d + k) + 2.0 * kv_pairs * (2 * d + 2 * k)
+    return flop, q_pairs, kv_pairs
+
+
 def to_dev(a, dtype, torch, np):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -247,10 +266,15 @@ def main():
         pairs_geo = executed_pairs(offN, offM, idx_np)
         f_geo = algorithmic_flops(pairs_geo, d, k)
         geo_ms = phase[1] + phase[2]
+        fb_geo, qb, kvb = executed_block_flops(offN, offM, idx_np, d, k)
         rec["geo"] = {"ms": round(geo_ms, 4), "topk_ms": round(phase[1], 4), "fwd_bwd_ms": round(phase[2], 4),
                       "tflops": round(f_geo / geo_ms / 1e9, 1),
                       "pct_peak": round(100 * f_geo / geo_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                       "executed_pairs": pairs_geo, "algorithmic_flop": f_geo,
+                      "executed_blocks": {"tflops": round(fb_geo / phase[2] / 1e9, 1),
+                                          "pct_peak": round(100 * fb_geo / phase[2] / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                          "flop": fb_geo, "target_side_pairs": qb, "source_side_pairs": kvb,
+                                          "what": "fwd+bwd kernels only, over 128-row items x 64-row tiles"},
                       "P": c["P"], "s": s}
     achieved = dkv_flops(pairs_dense, d, k) / dkv_avg / 1e9
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -302,10 +326,15 @@ def main():
         p4 = executed_pairs(offN4, offM4, st4["idx"].cpu().numpy())
         f4 = algorithmic_flops(p4, c4["d"], c4["k"])
         g4 = ph4[0] + ph4[1]
+        fb4, qb4, kvb4 = executed_block_flops(offN4, offM4, st4["idx"].cpu().numpy(), c4["d"], c4["k"])
         rec["geo_160k"] = {"ms": round(g4, 4), "topk_ms": round(ph4[0], 4), "fwd_bwd_ms": round(ph4[1], 4),
                            "tflops": round(f4 / g4 / 1e9, 1),
                            "pct_peak": round(100 * f4 / g4 / 1e9 / PEAK_BF16_TFLOPS, 2),
-                           "executed_pairs": p4, "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
+                           "executed_pairs": p4,
+                           "executed_blocks": {"tflops": round(fb4 / ph4[1] / 1e9, 1),
+                                               "pct_peak": round(100 * fb4 / ph4[1] / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                               "flop": fb4, "target_side_pairs": qb4, "source_side_pairs": kvb4},
+                           "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
         del geo4
 
     if args.copy_probe > 0:
