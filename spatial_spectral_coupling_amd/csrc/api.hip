@@ -75,6 +75,7 @@ struct Layout {
   size_t Qbar = kNone, KbarT = kNone;
   size_t run_tab = kNone, inv_tab = kNone;
   size_t knorm = kNone;  // bf16 forward: partial maxima of the key-row norms
+  size_t splitQ = kNone, splitK = kNone, partQ = kNone, partK = kNone;  // bf16 geo: split items, partial sums
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
 };
@@ -116,10 +117,19 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     const int rQ = kRowsFwd < kRowsDq ? kRowsFwd : kRowsDq, rK = kRowsDkv;
     L.poffN = take(((size_t)P_N + 1) * 4);
     L.poffM = take(((size_t)P_M + 1) * 4);
-    L.itemsQ = take(((size_t)(n_N + rQ - 1) / rQ + P_N) * sizeof(Item));
-    L.itemsK = take(((size_t)(n_M + rK - 1) / rK + P_M) * sizeof(Item));
+    L.itemsQ = take(((size_t)(n_N + rQ - 1) / rQ + P_N + kRoundCUs) * sizeof(Item));
+    L.itemsK = take(((size_t)(n_M + rK - 1) / rK + P_M + kRoundCUs) * sizeof(Item));
     L.counters = take(8 * 4);
-    L.scratch = take(((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.scratch = take(3 * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.splitQ = take(kRoundCUs * sizeof(SplitItem));
+    L.splitK = take(kRoundCUs * sizeof(SplitItem));
+    // partial sums of split items: kRoundCUs parts x 256 threads x fields
+    const size_t T = (size_t)kRoundCUs * 256 * 4;
+    if (op == SSC_OP_GEO_FWD) L.partQ = take(T * ((size_t)(kpad_fwd_bf16(k) / 32) * 16 + 2));
+    if (op == SSC_OP_GEO_BWD) {
+      L.partQ = take(T * ((size_t)d / 32) * 16);
+      L.partK = take(T * ((size_t)d / 32 + kpad_bwd_bf16(k) / 32) * 16);
+    }
     L.run_tab = take((size_t)P_N * s * sizeof(RunEntry));
     if (op == SSC_OP_GEO_BWD) {
       L.inv_off = take(((size_t)P_M + 1) * 4);
@@ -175,7 +185,7 @@ Layout make_layout(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k, int P
     L.itemsQ = take(((size_t)(n_N + kRowsPerWG - 1) / kRowsPerWG + P_N) * sizeof(Item));
     L.itemsK = take(((size_t)(n_M + kRowsPerWG - 1) / kRowsPerWG + P_M) * sizeof(Item));
     L.counters = take(8 * 4);
-    L.scratch = take(((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.scratch = take(3 * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
     if (op == SSC_OP_GEO_BWD) {
       L.inv_off = take(((size_t)P_M + 1) * 4);
       L.inv_idx = take((size_t)P_N * s * 4);
@@ -569,6 +579,8 @@ ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int
   if (bf16_path) {
     pl.run_tab = at<RunEntry>(ws, L.run_tab);
     if (inverse) pl.inv_tab = at<RunEntry>(ws, L.inv_tab);
+    pl.splitQ = at<SplitItem>(ws, L.splitQ);
+    pl.splitK = at<SplitItem>(ws, L.splitK);
   }
   pl.poffN = at<int>(ws, L.poffN); pl.poffM = at<int>(ws, L.poffM);
   pl.itemsQ = at<Item>(ws, L.itemsQ); pl.itemsK = at<Item>(ws, L.itemsK);
@@ -617,8 +629,11 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e;
     a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
     a.idx = idx; a.s = s; a.offM = offM; a.run_tab = at<RunEntry>(ws, L.run_tab);
+    a.part = at<float>(ws, L.partQ); a.split = at<SplitItem>(ws, L.splitQ); a.n_split = counters + 5;
     const int rQ = kRowsFwd;
-    SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ + P_N, hs); }));
+    SSC_TRY(timed("geo_fwd", hs,
+                  [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ + P_N + kRoundCUs, hs); }));
+    SSC_TRY(launch_fwd_merge_bf16(d, KPf, ones, a, hs));
     return SSC_OK;
   }
 
@@ -680,16 +695,22 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
       q.n_N = n_N; q.c2 = c2; q.scale = scale;
       q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.n_M = n_M;
       q.idx = idx; q.s = s; q.offM = offM; q.run_tab = at<RunEntry>(ws, L.run_tab);
+      q.part = at<float>(ws, L.partQ); q.split = at<SplitItem>(ws, L.splitQ); q.n_split = counters + 5;
       const int rQ = kRowsDq;
-      SSC_TRY(timed("geo_dq", hs, [&] { return launch_dq_bf16(d, KPb, dcol, q, (n_N + rQ - 1) / rQ + P_N, hs); }));
+      SSC_TRY(timed("geo_dq", hs,
+                    [&] { return launch_dq_bf16(d, KPb, dcol, q, (n_N + rQ - 1) / rQ + P_N + kRoundCUs, hs); }));
+      SSC_TRY(launch_dq_merge_bf16(d, q, hs));
     }
     DkvArgs b{};
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
     b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
     b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_tab = at<RunEntry>(ws, L.inv_tab);
+    b.part = at<float>(ws, L.partK); b.split = at<SplitItem>(ws, L.splitK); b.n_split = counters + 6;
     const int rK = kRowsDkv;
-    SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK + P_M, hs); }));
+    SSC_TRY(timed("geo_dkv", hs,
+                  [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK + P_M + kRoundCUs, hs); }));
+    SSC_TRY(launch_dkv_merge_bf16(d, KPb, b, hs));
     return SSC_OK;
   }
   int* poffN = at<int>(ws, L.poffN);

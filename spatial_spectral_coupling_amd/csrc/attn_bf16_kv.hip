@@ -9,6 +9,41 @@ namespace tb {
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
+// Output of one source row (held by lanes l and l ^ 32): dK = scale * dk, dV.
+template <int D, int KP>
+__device__ __forceinline__ void dkv_store(const DkvArgs& a, int krow, bool key_ok, int h, const f32x16* dk,
+                                          const f32x16* dv) {
+  if (key_ok) {
+    float* okr = a.dK + (size_t)krow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = db * 32 + 8 * g + 4 * h;
+        *reinterpret_cast<f32x4*>(okr + c) = f32x4{a.scale * dk[db][4 * g], a.scale * dk[db][4 * g + 1],
+                                                   a.scale * dk[db][4 * g + 2], a.scale * dk[db][4 * g + 3]};
+      }
+    }
+    float* ovr = a.dV + (size_t)krow * a.k;
+    const bool vec = (a.k & 3) == 0;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * h;
+        if (vec) {
+          if (c < a.k)
+            *reinterpret_cast<f32x4*>(ovr + c) = f32x4{dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) ovr[c + e] = dv[cb][4 * g + e];
+        }
+      }
+    }
+  }
+}
+
 template <int D, int KP, int NW, bool GEO, bool DCOL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
   constexpr int QB = TileSrc<D, NW>::ALLOC, OB = TileSrc<KP, NW>::ALLOC;
@@ -27,6 +62,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int k_begin, k_end;
   RowCursor rc;
+  Item it{0, 0, 0, 0, -1};
   // gathered query rows missing from a tile read the sentinel row n_N + 1
   // (past the end of Q, of the padded dO and of lse2 / D)
   if (!GEO) {
@@ -35,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     rc = RowCursor{nullptr, 1, a.n_N, a.n_N + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
-    const Item it = a.items[blockIdx.x];
+    it = a.items[blockIdx.x];
     k_begin = a.offM[it.patch] + it.row0;
     k_end = a.offM[it.patch + 1];
     const int i0 = a.inv_off[it.patch];
@@ -45,6 +81,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  // tiles [t0, t1) of the stream (one part of a split item, or all of it)
+  const int t0 = GEO ? it.t0 : 0, t1 = GEO ? min(it.t1, ntiles) : ntiles;
   constexpr bool dense = !GEO;
   // streamed target rows: Q (n_N rows), dO, lse2 and D (n_N + 1 entries:
   // a zero / +inf sentinel row at n_N)
@@ -88,21 +126,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   if (GEO && tid < kTile) {
     rc.init();
-    rowtab[0][tid] = rc.row(tid);
-    rowtab[1][tid] = rc.row(kTile + tid);
+    rowtab[0][tid] = rc.row(t0 * kTile + tid);
+    rowtab[1][tid] = rc.row((t0 + 1) * kTile + tid);
     if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
   }
   __syncthreads();
-  if (ntiles > 0) {
-    sQ.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
-    sO.template load_tile<GEO>(sm0 + QB, rowtab[0], 0, wave, lane);
+  if (t1 > t0) {
+    sQ.template load_tile<GEO>(sm0, rowtab[0], t0 * kTile, wave, lane);
+    sO.template load_tile<GEO>(sm0 + QB, rowtab[0], t0 * kTile, wave, lane);
     if (wave == 0) {
       if (GEO) sL.load_geo(ls0, rowtab[0][lane], lane);
-      else sL.load_dense(ls0, 0, lane);
+      else sL.load_dense(ls0, t0 * kTile, lane);
     }
     if (!DCOL && wave == NW - 1) {
       if (GEO) sD.load_geo(ds0, rowtab[0][lane], lane);
-      else sD.load_dense(ds0, 0, lane);
+      else sD.load_dense(ds0, t0 * kTile, lane);
     }
   }
   wait_loads();
@@ -145,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   // Two statically distinct buffers: the step that reads one fills the other.
   auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
-                  float* dsn) {
+                  float* dsn) __attribute__((always_inline)) {
     char* Ot = Qt + QB;
     f32x16 sc[2], dp[2];
     bf16x8 pk[2][2], dk8[2][2];
@@ -245,46 +283,60 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       side(u);
     });
     __builtin_amdgcn_sched_barrier(0);
-    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+    if (GEO && tid < kTile && t + 2 < t1) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
   };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
     step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
     step(t + 1, 1, sm1, sm0, ls1, ls0, ds1, ds0);
   }
-  if (t < ntiles) step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+  if (t < t1) step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
 
-  if (key_ok) {
-    float* okr = a.dK + (size_t)krow * D;
+  if (GEO && it.slot >= 0) {
+    // one part of a split item: partial sums for the merge pass
+    constexpr int F = (D / 32 + KP / 32) * 16;
+    float* out = a.part + (size_t)it.slot * F * (NW * 64) + tid;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = db * 32 + 8 * g + 4 * h;
-        *reinterpret_cast<f32x4*>(okr + c) = f32x4{a.scale * dk[db][4 * g], a.scale * dk[db][4 * g + 1],
-                                                   a.scale * dk[db][4 * g + 2], a.scale * dk[db][4 * g + 3]};
-      }
-    }
-    float* ovr = a.dV + (size_t)krow * a.k;
-    const bool vec = (a.k & 3) == 0;
+      for (int i = 0; i < 16; ++i) out[(db * 16 + i) * (NW * 64)] = dk[db][i];
 #pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb) {
+    for (int cb = 0; cb < KP / 32; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = cb * 32 + 8 * g + 4 * h;
-        if (vec) {
-          if (c < a.k)
-            *reinterpret_cast<f32x4*>(ovr + c) = f32x4{dv[cb][4 * g], dv[cb][4 * g + 1], dv[cb][4 * g + 2], dv[cb][4 * g + 3]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c + e < a.k) ovr[c + e] = dv[cb][4 * g + e];
-        }
-      }
-    }
+      for (int i = 0; i < 16; ++i) out[((D / 32 + cb) * 16 + i) * (NW * 64)] = dv[cb][i];
+    return;
   }
+  dkv_store<D, KP>(a, krow, key_ok, h, dk, dv);
+}
+
+// Merge of the parts of split items: dK = scale * sum, dV = sum (part order).
+template <int D, int KP, int NW>
+__global__ __launch_bounds__(NW * 64) void dkv_merge_bf16(DkvArgs a) {
+  if ((int)blockIdx.x >= *a.n_split) return;
+  const SplitItem sp = a.split[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int krow = a.offM[sp.patch] + sp.row0 + wave * 32 + l32;
+  const bool key_ok = krow < a.offM[sp.patch + 1];
+  constexpr int F = (D / 32 + KP / 32) * 16, T = NW * 64;
+  const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  // all loads of a part are issued before its sums
+  float sum[F];
+  static_for<F>([&](auto f) { sum[f] = 0.f; });
+  for (int q = 0; q < sp.nparts; ++q) {
+    const float* pq = in + (size_t)q * F * T;
+    float v[F];
+    static_for<F>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
+    static_for<F>([&](auto f) { sum[f] += v[f]; });
+  }
+  f32x16 dk[D / 32], dv[KP / 32];
+  static_for<F>([&](auto fc) {
+    constexpr int f = fc, NK = (D / 32) * 16;
+    if constexpr (f < NK) dk[f / 16][f % 16] = sum[f];
+    else dv[(f - NK) / 16][(f - NK) % 16] = sum[f];
+  });
+  dkv_store<D, KP>(a, krow, key_ok, h, dk, dv);
 }
 
 }  // namespace tb
@@ -326,6 +378,17 @@ hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid,
   }
 #undef SSC_L
 #undef SSC_L1
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dkv_merge_bf16(int D, int KP, const DkvArgs& a, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                      \
+  if (D == DD && KP == KK) {                                                                               \
+    hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK>), dim3(kRoundCUs), dim3(kWavesK * 64), 0, st, a); \
+    return hipGetLastError();                                                                              \
+  }
+  SSC_BF16_INSTANCES(SSC_L)
+#undef SSC_L
   return hipErrorInvalidValue;
 }
 

@@ -45,6 +45,46 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(const bf16x8& x) {
 // maximum exceeds its reference by more than 32 could overflow; a workgroup
 // that saw one redoes its rows once more with the exact row maxima as a
 // fixed reference, so the result is exact in every case.
+// Output of one row (held by lanes l and l ^ 32): O = acc / l and lse in
+// natural log, from the accumulators relative to reference m.
+template <int KP, bool ONES>
+__device__ __forceinline__ void fwd_store(const FwdArgs& a, int row, bool row_ok, int h, const f32x16* acc, float l_run,
+                                          float m) {
+  float l_part = l_run;
+  if (ONES) {
+    // the row sum sits in column k of O, held by the lanes of one half
+    l_part = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (cb * 32 + c_row(i, h) == a.k) l_part = acc[cb][i];
+  }
+  const float l_tot = l_part + xor32(l_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    float* Orow = a.O + (size_t)row * a.k;
+    const bool vec = (a.k & 3) == 0;
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * h;
+        if (vec) {
+          if (c < a.k)
+            *reinterpret_cast<f32x4*>(Orow + c) =
+                f32x4{acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.k) Orow[c + e] = acc[cb][4 * g + e] * inv;
+        }
+      }
+    }
+    if (h == 0) a.lse[row] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 template <int D, int KP, int NW, bool GEO, bool ONES>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
@@ -59,6 +99,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
+  Item it{0, 0, 0, 0, -1};
   // gathered key rows missing from a tile read the sentinel row n_M + 1
   // (past the end of K and of the padded V)
   if (!GEO) {
@@ -67,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     rc = RowCursor{nullptr, 1, a.n_M, a.n_M + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
-    const Item it = a.items[blockIdx.x];
+    it = a.items[blockIdx.x];
     q_begin = a.offN[it.patch] + it.row0;
     q_end = a.offN[it.patch + 1];
     const RunEntry* tab = a.run_tab + (size_t)it.patch * a.s;
@@ -75,6 +116,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  // tiles [t0, t1) of the stream (one part of a split item, or all of it)
+  const int t0 = GEO ? it.t0 : 0, t1 = GEO ? min(it.t1, ntiles) : ntiles;
   // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
   // a zero row at n_M)
   TileSrc<D, NW> sK;
@@ -174,14 +217,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
     if (GEO && tid < kTile) {
       rc.init();
-      rowtab[0][tid] = rc.row(tid);
-      rowtab[1][tid] = rc.row(kTile + tid);
+      rowtab[0][tid] = rc.row(t0 * kTile + tid);
+      rowtab[1][tid] = rc.row((t0 + 1) * kTile + tid);
       if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
     }
     __syncthreads();
-    if (ntiles > 0) {
-      sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
-      sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
+    if (t1 > t0) {
+      sK.template load_tile<GEO>(sm0, rowtab[0], t0 * kTile, wave, lane);
+      sV.template load_tile<GEO>(sm0 + KB, rowtab[0], t0 * kTile, wave, lane);
     }
     wait_loads();
     __syncthreads();
@@ -190,11 +233,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // other, so the compiler can tell the direct loads in flight from the LDS
     // reads.  The stream's last tile may be partial: its keys at or past
     // nvalid start from a score of -inf (bias, set before the pipeline).
-    auto step = [&](auto bound_c, const int t, const int b, char* Kt, char* Kn) {
+    auto step = [&](auto bound_c, const int t, const int b, char* Kt, char* Kn) __attribute__((always_inline)) {
       constexpr bool BOUND = decltype(bound_c)::value;
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
-      const bool first = !BOUND && t == 0 && !fixed;
+      const bool first = !BOUND && t == t0 && !fixed;
       if (nvalid < kTile) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
@@ -307,20 +350,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           m_run = m_new;
         }
       }
-      if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+      if (GEO && tid < kTile && t + 2 < t1) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
       wait_loads();
       __syncthreads();
     };
-    auto run = [&](auto bound_c) {
-      for (int t = 0; t < ntiles; t += 2) {
-        step(bound_c, t, 0, sm0, sm1);
-        if (t + 1 < ntiles) step(bound_c, t + 1, 1, sm1, sm0);
+    auto run = [&](auto bound_c) __attribute__((always_inline)) {
+      const int nt = t1 - t0;  // (this loop form keeps the accumulators in registers)
+      for (int i = 0; i < nt; i += 2) {
+        step(bound_c, t0 + i, 0, sm0, sm1);
+        if (i + 1 < nt) step(bound_c, t0 + i + 1, 1, sm1, sm0);
       }
     };
     if (mode == 0) {
       run(std::true_type{});
       const float lt = row_sum();
-      if (!__syncthreads_or(total > 0 && !(lt >= 0x1p-60f))) break;
+      if (!__syncthreads_or(t1 > t0 && !(lt >= 0x1p-60f))) break;
       mode = 1;
       continue;
     }
@@ -329,29 +373,50 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     mode = 2;
   }
 
-  const float l_tot = row_sum();
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok) {
-    float* Orow = a.O + (size_t)row * a.k;
-    const bool vec = (a.k & 3) == 0;
-#pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = cb * 32 + 8 * g + 4 * h;
-        if (vec) {
-          if (c < a.k)
-            *reinterpret_cast<f32x4*>(Orow + c) =
-                f32x4{acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv, acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c + e < a.k) Orow[c + e] = acc[cb][4 * g + e] * inv;
-        }
-      }
-    }
-    if (h == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (GEO && it.slot >= 0) {
+    // one part of a split item: partial sums for the merge pass
+    constexpr int F = (KP / 32) * 16 + 2;
+    float* out = a.part + (size_t)it.slot * F * (NW * 64) + tid;
+    static_for<(KP / 32) * 16>([&](auto f) {
+      constexpr int cb = f / 16, i = f % 16;
+      out[f * (NW * 64)] = acc[cb][i];
+    });
+    out[(F - 2) * (NW * 64)] = m_run;
+    out[(F - 1) * (NW * 64)] = l_run;
+    return;
   }
+  fwd_store<KP, ONES>(a, row, row_ok, h, acc, l_run, m_run);
+}
+
+// Merge of the parts of split items (one workgroup per split item, the
+// producer's thread layout): acc = sum_q 2^(m_q - m) acc_q with m the largest
+// reference (all equal in the bounded first pass), then the forward's output.
+template <int D, int KP, int NW, bool ONES>
+__global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
+  if ((int)blockIdx.x >= *a.n_split) return;
+  const SplitItem sp = a.split[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int row = a.offN[sp.patch] + sp.row0 + wave * 32 + l32;
+  const bool row_ok = row < a.offN[sp.patch + 1];
+  constexpr int F = (KP / 32) * 16 + 2, T = NW * 64;
+  const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  float m = -INFINITY;
+  for (int q = 0; q < sp.nparts; ++q) m = fmaxf(m, in[((size_t)q * F + F - 2) * T]);
+  f32x16 acc[KP / 32];
+#pragma unroll
+  for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
+  float l = 0.f;
+  for (int q = 0; q < sp.nparts; ++q) {
+    const float* pq = in + (size_t)q * F * T;
+    const float mq = pq[(F - 2) * T];
+    const float w = mq == -INFINITY ? 0.f : fexp2(mq - m);
+#pragma unroll
+    for (int cb = 0; cb < KP / 32; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][i] = fmaf(w, pq[(cb * 16 + i) * T], acc[cb][i]);
+    l = fmaf(w, pq[(F - 1) * T], l);
+  }
+  fwd_store<KP, ONES>(a, row, row_ok, h, acc, l, m);
 }
 
 // ---------------------------------------------------------------------------
@@ -366,6 +431,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // bf16 packing).  Iteration t runs A0(t), B1(t-1), A1(t), B0(t): B1 of the
 // previous tile uses transposed K fragments kept in registers, so every
 // softmax gets a window of a full A chain plus a B chain to hide in.
+template <int D>
+__device__ __forceinline__ void dq_store(const DqArgs& a, int row, bool row_ok, int h, const f32x16* dq) {
+  if (!row_ok) return;
+  float* out = a.dQ + (size_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = db * 32 + 8 * g + 4 * h;
+      *reinterpret_cast<f32x4*>(out + c) = f32x4{a.scale * dq[db][4 * g], a.scale * dq[db][4 * g + 1],
+                                                 a.scale * dq[db][4 * g + 2], a.scale * dq[db][4 * g + 3]};
+    }
+  }
+}
+
 template <int D, int KP, int NW, bool GEO, bool DCOL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dq_bf16(DqArgs a) {
   constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
@@ -380,6 +460,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   int q_begin, q_end;
   RowCursor rc;
+  Item it{0, 0, 0, 0, -1};
   // gathered key rows missing from a tile read the sentinel row n_M + 1
   // (past the end of K and of the padded V)
   if (!GEO) {
@@ -388,7 +469,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     rc = RowCursor{nullptr, 1, a.n_M, a.n_M + 1};
   } else {
     if ((int)blockIdx.x >= *a.n_items) return;
-    const Item it = a.items[blockIdx.x];
+    it = a.items[blockIdx.x];
     q_begin = a.offN[it.patch] + it.row0;
     q_end = a.offN[it.patch + 1];
     const RunEntry* tab = a.run_tab + (size_t)it.patch * a.s;
@@ -396,6 +477,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
   const int total = rc.total;
   const int ntiles = (total + kTile - 1) / kTile;
+  // tiles [t0, t1) of the stream (one part of a split item, or all of it)
+  const int t0 = GEO ? it.t0 : 0, t1 = GEO ? min(it.t1, ntiles) : ntiles;
   // streamed source rows: K (n_M rows) and the k-padded V (n_M + 1 rows,
   // a zero row at n_M)
   TileSrc<D, NW> sK;
@@ -436,14 +519,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   if (GEO && tid < kTile) {
     rc.init();
-    rowtab[0][tid] = rc.row(tid);
-    rowtab[1][tid] = rc.row(kTile + tid);
+    rowtab[0][tid] = rc.row(t0 * kTile + tid);
+    rowtab[1][tid] = rc.row((t0 + 1) * kTile + tid);
     if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
   }
   __syncthreads();
-  if (ntiles > 0) {
-    sK.template load_tile<GEO>(sm0, rowtab[0], 0, wave, lane);
-    sV.template load_tile<GEO>(sm0 + KB, rowtab[0], 0, wave, lane);
+  if (t1 > t0) {
+    sK.template load_tile<GEO>(sm0, rowtab[0], t0 * kTile, wave, lane);
+    sV.template load_tile<GEO>(sm0 + KB, rowtab[0], t0 * kTile, wave, lane);
   }
   wait_loads();
   __syncthreads();
@@ -506,7 +589,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // the softmax of half 0 runs during B1(t-1) and A1(t), that of half 1
   // during B0(t) and A0(t+1), so each has a 30-step window.  Two statically
   // distinct buffers: the step that reads one fills the other.
-  auto step = [&](const int t, const int b, char* Kt, char* Kn) {
+  auto step = [&](const int t, const int b, char* Kt, char* Kn) __attribute__((always_inline)) {
     char* Vt = Kt + KB;
     const int nvalid = total - t * kTile;
     if (nvalid < kTile) {
@@ -600,13 +683,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       side(u);
     });
     __builtin_amdgcn_sched_barrier(0);
-    if (GEO && tid < kTile && t + 2 < ntiles) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
+    if (GEO && tid < kTile && t + 2 < t1) rowtab[b][tid] = rc.row((t + 2) * kTile + tid);
     wait_loads();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     step(t, 0, sm0, sm1);
-    if (t + 1 < ntiles) step(t + 1, 1, sm1, sm0);
+    if (t + 1 < t1) step(t + 1, 1, sm1, sm0);
   }
   // drain: the rest of the last tile's half-1 softmax, then its B1 chain
   static_for<SLICES>([&](auto k) {
@@ -614,18 +697,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   });
   static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
 
-  if (row_ok) {
-    float* out = a.dQ + (size_t)row * D;
+  if (GEO && it.slot >= 0) {
+    // one part of a split item: partial sums for the merge pass
+    constexpr int F = (D / 32) * 16;
+    float* out = a.part + (size_t)it.slot * F * (NW * 64) + tid;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = db * 32 + 8 * g + 4 * h;
-        *reinterpret_cast<f32x4*>(out + c) = f32x4{a.scale * dq[db][4 * g], a.scale * dq[db][4 * g + 1],
-                                                   a.scale * dq[db][4 * g + 2], a.scale * dq[db][4 * g + 3]};
-      }
-    }
+      for (int i = 0; i < 16; ++i) out[(db * 16 + i) * (NW * 64)] = dq[db][i];
+    return;
   }
+  dq_store<D>(a, row, row_ok, h, dq);
+}
+
+// Merge of the parts of split items: dQ = scale * (sum of the parts, in part
+// order).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_merge_bf16(DqArgs a) {
+  if ((int)blockIdx.x >= *a.n_split) return;
+  const SplitItem sp = a.split[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int row = a.offN[sp.patch] + sp.row0 + wave * 32 + l32;
+  const bool row_ok = row < a.offN[sp.patch + 1];
+  constexpr int F = (D / 32) * 16, T = NW * 64;
+  const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  // all loads of a part are issued before its sums
+  float sum[F];
+  static_for<F>([&](auto f) { sum[f] = 0.f; });
+  for (int q = 0; q < sp.nparts; ++q) {
+    const float* pq = in + (size_t)q * F * T;
+    float v[F];
+    static_for<F>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
+    static_for<F>([&](auto f) { sum[f] += v[f]; });
+  }
+  f32x16 dq[D / 32];
+  static_for<F>([&](auto f) { dq[f / 16][f % 16] = sum[f]; });
+  dq_store<D>(a, row, row_ok, h, dq);
 }
 
 }  // namespace tb
@@ -695,6 +802,27 @@ hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, h
 #undef SSC_L
 #undef SSC_L1
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                          \
+  if (D == DD && KP == KK) {                                                                                   \
+    if (ones)                                                                                                  \
+      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, true>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a); \
+    else                                                                                                       \
+      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, false>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a); \
+    return hipGetLastError();                                                                                  \
+  }
+  SSC_BF16_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dq_merge_bf16(int D, const DqArgs& a, hipStream_t st) {
+  if (D == 128) hipLaunchKernelGGL((tb::dq_merge_bf16<128, kWavesQ>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a);
+  else if (D == 64) hipLaunchKernelGGL((tb::dq_merge_bf16<64, kWavesQ>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace ssc

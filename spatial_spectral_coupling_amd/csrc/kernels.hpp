@@ -24,9 +24,27 @@ struct RunEntry {
   int end, base;
 };
 
+// A work item: rows row0 .. row0 + (rows per item) of a patch, and the
+// tiles [t0, t1) of its gathered stream (t1 past the end = to the end).
+// slot < 0: the item covers the whole stream and writes the outputs; slot
+// >= 0: one part of a split item, whose partial sums go to partial-buffer
+// slot `slot` and are combined by the merge pass in part order.
 struct Item {
-  int patch, row0;
+  int patch, row0, t0, t1, slot;
 };
+
+// A split item: its rows, number of parts and first partial-buffer slot.
+struct SplitItem {
+  int patch, row0, nparts, slot0;
+};
+
+// Geo scheduling: one round = one workgroup per CU of an MI355X (one
+// workgroup of the bf16 block kernels fills a CU).  The items left over
+// after the full rounds (the cheapest ones) are split into up to
+// kMaxParts parts along their stream, so the last round is not a tail of a
+// few long items; partial buffers hold at most kRoundCUs parts.
+constexpr int kRoundCUs = 256;
+constexpr int kMaxParts = 8;
 
 // Forward: O = softmax(Q K^T scale) V over each row's key stream.
 struct FwdArgs {
@@ -50,6 +68,10 @@ struct FwdArgs {
   const void* Vp;
   const RunEntry* run_tab;
   const float* knorm2;  // [kNormParts] partial maxima of |k_j|^2 over the key rows
+  // geo splitting: partial sums [slot][field][256 threads] and split items
+  float* part;
+  const SplitItem* split;
+  const int* n_split;
 };
 
 // Partial maxima of the squared key-row norms (bf16 forward): kNormParts
@@ -79,6 +101,9 @@ struct DqArgs {
   const int* offM;
   int npadM, n_M;
   const RunEntry* run_tab;  // bf16 kernels (Qp, Kp = caller rows; lse2p, Dp by row)
+  float* part;
+  const SplitItem* split;
+  const int* n_split;
 };
 
 // dK / dV pass.
@@ -107,6 +132,9 @@ struct DkvArgs {
   // bf16 kernels: run table of each source patch's query stream, entries
   // inv_tab[inv_off[q] .. inv_off[q+1]) (one per selecting target patch).
   const RunEntry* inv_tab;
+  float* part;
+  const SplitItem* split;
+  const int* n_split;
 };
 
 // Packing of one tensor into the padded patch layout.
@@ -138,10 +166,13 @@ struct PlanArgs {
   int* poffM;           // [P_M + 1]
   Item* itemsQ;         // row blocks of target patches
   Item* itemsK;         // row blocks of source patches
-  int* counters;        // [0] n itemsQ, [1] n itemsK, [2] groups N, [3] groups M, [4] status
+  int* counters;        // [0] n itemsQ, [1] n itemsK, [2] groups N, [3] groups M, [4] status,
+                        // [5] n splitQ, [6] n splitK
+  SplitItem* splitQ;    // [kRoundCUs] or nullptr (no splitting)
+  SplitItem* splitK;    // [kRoundCUs] or nullptr
   int* inv_off;         // [P_M + 1] or nullptr
   int* inv_idx;         // [P_N * s]
-  int* scratch;         // [max(P_N, P_M) + 1] counters for scans and fills
+  int* scratch;         // [3 (max(P_N, P_M) + 1)] counters for scans and fills
   int rowsQ, rowsK;     // rows per work item (target, source side)
   RunEntry* run_tab;    // [P_N * s] or nullptr: source runs of each target patch
   RunEntry* inv_tab;    // [P_N * s] or nullptr: target runs of each source patch
@@ -197,6 +228,10 @@ hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid,
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st);
+// merge passes of split geo items (kRoundCUs workgroups, idle past the count)
+hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hipStream_t st);
+hipError_t launch_dq_merge_bf16(int D, const DqArgs& a, hipStream_t st);
+hipError_t launch_dkv_merge_bf16(int D, int KP, const DkvArgs& a, hipStream_t st);
 hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 bool supported(DType t, int D, int KP);

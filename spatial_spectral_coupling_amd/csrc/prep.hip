@@ -275,6 +275,130 @@ __device__ int block_scan_excl(int n, F f, int* out, int* lds /* kPlanWaves + 1 
   return carry;
 }
 
+// Exclusive prefix of one value per thread over the workgroup; *total gets
+// the sum.
+__device__ int block_excl1(int v, int* lds /* kPlanWaves + 1 */, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) lds[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < kPlanWaves ? lds[lane] : 0;
+    const int ti = wave_incl_scan(t);
+    if (lane < kPlanWaves) lds[lane] = ti - t;
+    if (lane == kPlanWaves - 1) lds[kPlanWaves] = ti;
+  }
+  __syncthreads();
+  const int r = lds[w] + inc - v;
+  *total = lds[kPlanWaves];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kCostBuckets = 4096;  // item costs (stream tiles), clamped, for the dispatch order
+
+// Work items of one side: patch p has rows off[p] .. off[p+1] (items of
+// `rows` rows) and a gathered stream of tiles(p) tiles.  Without `spl` the
+// items come in patch order and cover whole streams.  With `spl`: N items
+// fill N / kRoundCUs full rounds plus R = N mod kRoundCUs; the R cheapest
+// items (cost ascending, then item order) are split into m = min(kMaxParts,
+// kRoundCUs / R) parts of their stream, and the dispatch order is the whole
+// items by decreasing cost, then the parts.  Which items are split and their
+// slots depend only on the costs, so the results do not depend on the
+// (atomic) order among equal-cost whole items.  Returns the number of units.
+template <typename TilesF>
+__device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* items, SplitItem* spl, int* n_split,
+                          int* tmp /* 3 (nP + 1) */, int* lds, int* hist /* kCostBuckets */, int* s_misc /* 2 */) {
+  const int tid = threadIdx.x;
+  int* eqb = tmp + (nP + 1);
+  int* spb = tmp + 2 * (nP + 1);
+  const int N = block_scan_excl(nP, [=](int p) { return (off[p + 1] - off[p] + rows - 1) / rows; }, tmp, lds);
+  int R = spl != nullptr ? N % kRoundCUs : 0;
+  int m = R > 0 ? min(kMaxParts, kRoundCUs / R) : 1;
+  if (m < 2) {
+    R = 0;
+    m = 1;
+  }
+  if (R == 0) {
+    for (int p = tid; p < nP; p += kPlanThreads) {
+      const int b = tmp[p], nt = tmp[p + 1] - b;
+      for (int t = 0; t < nt; ++t) items[b + t] = Item{p, t * rows, 0, 0x7fffffff, -1};
+    }
+    if (tid == 0 && n_split != nullptr) *n_split = 0;
+    __syncthreads();
+    return N;
+  }
+  auto cost = [&](int p) { return min(tiles(p), kCostBuckets - 1); };
+  for (int c = tid; c < kCostBuckets; c += kPlanThreads) hist[c] = 0;
+  __syncthreads();
+  for (int p = tid; p < nP; p += kPlanThreads) {
+    const int nt = tmp[p + 1] - tmp[p];
+    if (nt > 0) atomicAdd(&hist[cost(p)], nt);
+  }
+  __syncthreads();
+  // threshold bucket c*: the R-th cheapest item has cost c*
+  constexpr int BPT = kCostBuckets / kPlanThreads;
+  {
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) v += hist[BPT * tid + i];
+    int tot;
+    int cum = block_excl1(v, lds, &tot);
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int h = hist[BPT * tid + i];
+      if (cum < R && cum + h >= R) {
+        s_misc[0] = BPT * tid + i;
+        s_misc[1] = cum;
+      }
+      cum += h;
+    }
+  }
+  __syncthreads();
+  const int cstar = s_misc[0], need = R - s_misc[1];
+  block_scan_excl(nP, [&](int p) { return cost(p) == cstar ? tmp[p + 1] - tmp[p] : 0; }, eqb, lds);
+  auto nsplit = [&](int p) {
+    const int c = cost(p), nt = tmp[p + 1] - tmp[p];
+    return c < cstar ? nt : c == cstar ? min(max(need - eqb[p], 0), nt) : 0;
+  };
+  block_scan_excl(nP, nsplit, spb, lds);
+  // whole items by decreasing cost: start of each bucket in the order
+  {
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int c = kCostBuckets - 1 - (BPT * tid + i);
+      v += c > cstar ? hist[c] : c == cstar ? hist[c] - need : 0;
+    }
+    int tot;
+    int cum = block_excl1(v, lds, &tot);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int c = kCostBuckets - 1 - (BPT * tid + i);
+      const int hu = c > cstar ? hist[c] : c == cstar ? hist[c] - need : 0;
+      hist[c] = cum;
+      cum += hu;
+    }
+  }
+  __syncthreads();
+  const int U = N - R;
+  for (int p = tid; p < nP; p += kPlanThreads) {
+    const int nt = tmp[p + 1] - tmp[p], ns = nsplit(p), c = cost(p);
+    for (int t = ns; t < nt; ++t) items[atomicAdd(&hist[c], 1)] = Item{p, t * rows, 0, 0x7fffffff, -1};
+    const int T = tiles(p);
+    for (int t = 0; t < ns; ++t) {
+      const int j = spb[p] + t;
+      spl[j] = SplitItem{p, t * rows, m, j * m};
+      for (int q = 0; q < m; ++q)
+        items[U + j * m + q] = Item{p, t * rows, (int)((long long)q * T / m), (int)((long long)(q + 1) * T / m), j * m + q};
+    }
+  }
+  if (tid == 0) *n_split = R;
+  __syncthreads();
+  return U + R * m;
+}
+
 // The selection is read in chunks of kPlanRows target patches: every entry
 // (p, q) of a chunk sets bit p - p0 of mask[q] (a bit already set is a
 // repeated source patch within row p).  For the inverse lists, the rank of
@@ -345,21 +469,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                                  a.poffN, lds);
   const int gM = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + kGroup - 1) & ~(kGroup - 1); },
                                  a.poffM, lds);
-  // ---- work items (row blocks of rowsQ / rowsK rows within a patch)
-  int* tmp = a.scratch;  // [max(P_N, P_M) + 1]
-  const int rQ = a.rowsQ, rK = a.rowsK;
-  const int nQ = block_scan_excl(P_N, [=](int p) { return (offN[p + 1] - offN[p] + rQ - 1) / rQ; }, tmp, lds);
-  for (int p = tid; p < P_N; p += kPlanThreads) {
-    const int b = tmp[p], nt = tmp[p + 1] - b;
-    for (int t = 0; t < nt; ++t) a.itemsQ[b + t] = Item{p, t * rQ};
-  }
-  __syncthreads();
-  const int nK = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + rK - 1) / rK; }, tmp, lds);
-  for (int q = tid; q < P_M; q += kPlanThreads) {
-    const int b = tmp[q], nt = tmp[q + 1] - b;
-    for (int t = 0; t < nt; ++t) a.itemsK[b + t] = Item{q, t * rK};
-  }
-  __syncthreads();
   // ---- per target patch: the run table of its key stream (the selected
   // source patches in selection order)
   if (a.run_tab != nullptr && a.idx != nullptr) {
@@ -375,6 +484,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         acc += n;
       }
     }
+    __syncthreads();
   }
   // ---- inverse selection lists: inv[q] = target patches p with q in idx[p],
   // ascending, and their run tables
@@ -420,6 +530,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       __syncthreads();
     }
   }
+  // ---- work items (row blocks of rowsQ / rowsK rows within a patch)
+  __shared__ int s_misc[2];
+  int* tmp = a.scratch;  // [3 (max(P_N, P_M) + 1)]
+  const RunEntry* rt = a.run_tab;
+  const int* io = a.inv_off;
+  const RunEntry* it = a.inv_tab;
+  auto tilesQ = [=](int p) { return rt != nullptr ? (rt[(size_t)p * S + S - 1].end + kTile - 1) / kTile : 0; };
+  const int nQ = make_items(P_N, offN, a.rowsQ, tilesQ, a.itemsQ, rt != nullptr ? a.splitQ : nullptr, a.counters + 5,
+                            tmp, lds, s_acc, s_misc);
+  auto tilesK = [=](int q) {
+    if (it == nullptr) return 0;
+    const int b = io[q], e = io[q + 1];
+    return e > b ? (it[e - 1].end + kTile - 1) / kTile : 0;
+  };
+  // source-side items drive only the dK/dV pass (a plan with inverse lists)
+  const int nK = io != nullptr || rt == nullptr
+                     ? make_items(P_M, offM, a.rowsK, tilesK, a.itemsK, it != nullptr ? a.splitK : nullptr,
+                                  a.counters + 6, tmp, lds, s_acc, s_misc)
+                     : 0;
+  if (io == nullptr && rt != nullptr && tid == 0) a.counters[6] = 0;
   if (tid == 0) {
     a.counters[0] = nQ;
     a.counters[1] = nK;
