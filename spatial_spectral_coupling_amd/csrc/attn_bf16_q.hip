@@ -389,8 +389,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 }
 
 // Merge of the parts of split items (one workgroup per split item, the
-// producer's thread layout): acc = sum_q 2^(m_q - m) acc_q with m the largest
-// reference (all equal in the bounded first pass), then the forward's output.
+// producer's thread layout).  A part's sums are relative to its own
+// reference m_q (the bound, or a running maximum where that part fell back),
+// so the parts are combined at the reference of the largest part mass,
+// M = max_q (m_q + log2 l_q): acc = sum_q 2^(m_q - M) acc_q, where every
+// weighted part sum stays <= 1 and a part only underflows when its mass is
+// below 2^-126 of the largest.
 template <int D, int KP, int NW, bool ONES>
 __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
   if ((int)blockIdx.x >= *a.n_split) return;
@@ -400,20 +404,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
   const bool row_ok = row < a.offN[sp.patch + 1];
   constexpr int F = (KP / 32) * 16 + 2, T = NW * 64;
   const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  // row sum of part q (both halves of the row)
+  auto part_l = [&](const float* pq) {
+    float lv = pq[(F - 1) * T];
+    if (ONES) {
+      lv = 0.f;
+      static_for<(KP / 32) * 16>([&](auto f) {
+        constexpr int cb = f / 16, i = f % 16;
+        if (cb * 32 + c_row(i, h) == a.k) lv = pq[f * T];
+      });
+    }
+    return lv + xor32(lv);
+  };
   float m = -INFINITY;
-  for (int q = 0; q < sp.nparts; ++q) m = fmaxf(m, in[((size_t)q * F + F - 2) * T]);
+  for (int q = 0; q < sp.nparts; ++q) {
+    const float* pq = in + (size_t)q * F * T;
+    const float lq = part_l(pq);
+    if (lq > 0.f) m = fmaxf(m, pq[(F - 2) * T] + log2f(lq));
+  }
   f32x16 acc[KP / 32];
 #pragma unroll
   for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
   float l = 0.f;
   for (int q = 0; q < sp.nparts; ++q) {
     const float* pq = in + (size_t)q * F * T;
-    const float mq = pq[(F - 2) * T];
-    const float w = mq == -INFINITY ? 0.f : fexp2(mq - m);
-#pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[cb][i] = fmaf(w, pq[(cb * 16 + i) * T], acc[cb][i]);
+    const float w = part_l(pq) > 0.f ? fexp2(pq[(F - 2) * T] - m) : 0.f;
+    static_for<(KP / 32) * 16>([&](auto f) {
+      constexpr int cb = f / 16, i = f % 16;
+      acc[cb][i] = fmaf(w, pq[f * T], acc[cb][i]);
+    });
     l = fmaf(w, pq[(F - 1) * T], l);
   }
   fwd_store<KP, ONES>(a, row, row_ok, h, acc, l, m);

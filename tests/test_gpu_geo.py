@@ -69,6 +69,26 @@ GEO_SHAPES = [
 ]
 
 
+def test_geo_reference_fallbacks():
+    """A key of norm 60 makes the forward's bounded reference (|q| max|k|)
+    sit far above the scores of the query of norm 60 (original row 5), so the
+    parts of its split work item redo their rows with a running reference
+    while the other parts keep the bound: the merge then combines partial sums
+    taken at different references."""
+    c = gen.make_small(600, 700, 128, 200, "bf16", seed=31, P_N=9, P_M=11, s=3)
+    Qf = f64(c["Q"], "bf16").astype(np.float32)
+    Kf = f64(c["K"], "bf16").astype(np.float32)
+    Qf[5] = 0.0
+    Qf[5, 0] = 60.0
+    Kf[:, 0] = 0.0
+    Kf[200] = 0.0
+    Kf[200, 0] = 5.0
+    Kf[250] = 0.0
+    Kf[250, 1] = 60.0
+    c["Q"], c["K"] = gen.bf16_bits_from_f32(Qf), gen.bf16_bits_from_f32(Kf)
+    compare_geo(c, 3, "geo reference fallbacks")
+
+
 @pytest.mark.parametrize("dt,nN,nM,d,k,PN,PM,s", GEO_SHAPES)
 def test_geo_parity_small(dt, nN, nM, d, k, PN, PM, s):
     c = gen.make_small(nN, nM, d, k, dt, seed=nN + 3 * nM, P_N=PN, P_M=PM, s=s)
