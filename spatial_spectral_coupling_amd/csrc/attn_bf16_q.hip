@@ -404,16 +404,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
   const bool row_ok = row < a.offN[sp.patch + 1];
   constexpr int F = (KP / 32) * 16 + 2, T = NW * 64;
   const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
-  // row sum of part q (both halves of the row)
+  // row sum of part q (both halves of the row); with ONES, column k of O is
+  // field (k/32) 16 + 4 ((k%32)/8) + k%4 of the lanes of half ((k%32)/4) % 2
+  const int kk = a.k & 31, hk = (kk >> 2) & 1, fk = (a.k >> 5) * 16 + 4 * (kk >> 3) + (kk & 3);
   auto part_l = [&](const float* pq) {
-    float lv = pq[(F - 1) * T];
-    if (ONES) {
-      lv = 0.f;
-      static_for<(KP / 32) * 16>([&](auto f) {
-        constexpr int cb = f / 16, i = f % 16;
-        if (cb * 32 + c_row(i, h) == a.k) lv = pq[f * T];
-      });
-    }
+    const float lv = ONES ? (h == hk ? pq[(size_t)fk * T] : 0.f) : pq[(F - 1) * T];
     return lv + xor32(lv);
   };
   float m = -INFINITY;

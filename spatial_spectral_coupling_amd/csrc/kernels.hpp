@@ -76,7 +76,7 @@ struct FwdArgs {
 
 // Partial maxima of the squared key-row norms (bf16 forward): kNormParts
 // workgroups, one partial each.
-constexpr int kNormParts = 256;
+constexpr int kNormParts = 1024;
 hipError_t launch_keynorm(const void* K, int n, int d, float* part, hipStream_t st);
 
 // dQ pass.

@@ -308,11 +308,18 @@ constexpr int kCostBuckets = 4096;  // item costs (stream tiles), clamped, for t
 // (atomic) order among equal-cost whole items.  Returns the number of units.
 template <typename TilesF>
 __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* items, SplitItem* spl, int* n_split,
-                          int* tmp /* 3 (nP + 1) */, int* lds, int* hist /* kCostBuckets */, int* s_misc /* 2 */) {
+                          int* tmp /* 3 (nP + 1) */, int* lds, int* hist /* kCostBuckets */, int* s_misc /* 2 */,
+                          int* tl /* nP, LDS */, int* cn /* nP, LDS */) {
   const int tid = threadIdx.x;
   int* eqb = tmp + (nP + 1);
   int* spb = tmp + 2 * (nP + 1);
-  const int N = block_scan_excl(nP, [=](int p) { return (off[p + 1] - off[p] + rows - 1) / rows; }, tmp, lds);
+  // per patch: items and stream tiles, kept in LDS
+  for (int p = tid; p < nP; p += kPlanThreads) {
+    cn[p] = (off[p + 1] - off[p] + rows - 1) / rows;
+    tl[p] = spl != nullptr ? tiles(p) : 0;
+  }
+  __syncthreads();
+  const int N = block_scan_excl(nP, [=](int p) { return cn[p]; }, tmp, lds);
   int R = spl != nullptr ? N % kRoundCUs : 0;
   int m = R > 0 ? min(kMaxParts, kRoundCUs / R) : 1;
   if (m < 2) {
@@ -321,18 +328,18 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
   }
   if (R == 0) {
     for (int p = tid; p < nP; p += kPlanThreads) {
-      const int b = tmp[p], nt = tmp[p + 1] - b;
+      const int b = tmp[p], nt = cn[p];
       for (int t = 0; t < nt; ++t) items[b + t] = Item{p, t * rows, 0, 0x7fffffff, -1};
     }
     if (tid == 0 && n_split != nullptr) *n_split = 0;
     __syncthreads();
     return N;
   }
-  auto cost = [&](int p) { return min(tiles(p), kCostBuckets - 1); };
+  auto cost = [&](int p) { return min(tl[p], kCostBuckets - 1); };
   for (int c = tid; c < kCostBuckets; c += kPlanThreads) hist[c] = 0;
   __syncthreads();
   for (int p = tid; p < nP; p += kPlanThreads) {
-    const int nt = tmp[p + 1] - tmp[p];
+    const int nt = cn[p];
     if (nt > 0) atomicAdd(&hist[cost(p)], nt);
   }
   __syncthreads();
@@ -356,9 +363,9 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
   }
   __syncthreads();
   const int cstar = s_misc[0], need = R - s_misc[1];
-  block_scan_excl(nP, [&](int p) { return cost(p) == cstar ? tmp[p + 1] - tmp[p] : 0; }, eqb, lds);
+  block_scan_excl(nP, [&](int p) { return cost(p) == cstar ? cn[p] : 0; }, eqb, lds);
   auto nsplit = [&](int p) {
-    const int c = cost(p), nt = tmp[p + 1] - tmp[p];
+    const int c = cost(p), nt = cn[p];
     return c < cstar ? nt : c == cstar ? min(max(need - eqb[p], 0), nt) : 0;
   };
   block_scan_excl(nP, nsplit, spb, lds);
@@ -384,9 +391,9 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
   __syncthreads();
   const int U = N - R;
   for (int p = tid; p < nP; p += kPlanThreads) {
-    const int nt = tmp[p + 1] - tmp[p], ns = nsplit(p), c = cost(p);
+    const int nt = cn[p], ns = nsplit(p), c = cost(p);
     for (int t = ns; t < nt; ++t) items[atomicAdd(&hist[c], 1)] = Item{p, t * rows, 0, 0x7fffffff, -1};
-    const int T = tiles(p);
+    const int T = tl[p];
     for (int t = 0; t < ns; ++t) {
       const int j = spb[p] + t;
       spl[j] = SplitItem{p, t * rows, m, j * m};
@@ -458,6 +465,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (bad) {
     if (tid == 0) {
       a.counters[0] = a.counters[1] = a.counters[2] = a.counters[3] = 0;
+      a.counters[5] = a.counters[6] = 0;  // no split items either: the merge passes idle
       a.counters[4] = 1;
     }
     return;
@@ -537,8 +545,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int* io = a.inv_off;
   const RunEntry* it = a.inv_tab;
   auto tilesQ = [=](int p) { return rt != nullptr ? (rt[(size_t)p * S + S - 1].end + kTile - 1) / kTile : 0; };
+  int* s_tl = reinterpret_cast<int*>(s_mask);  // free after the selection passes
   const int nQ = make_items(P_N, offN, a.rowsQ, tilesQ, a.itemsQ, rt != nullptr ? a.splitQ : nullptr, a.counters + 5,
-                            tmp, lds, s_acc, s_misc);
+                            tmp, lds, s_acc, s_misc, s_tl, s_cur);
   auto tilesK = [=](int q) {
     if (it == nullptr) return 0;
     const int b = io[q], e = io[q + 1];
@@ -547,7 +556,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // source-side items drive only the dK/dV pass (a plan with inverse lists)
   const int nK = io != nullptr || rt == nullptr
                      ? make_items(P_M, offM, a.rowsK, tilesK, a.itemsK, it != nullptr ? a.splitK : nullptr,
-                                  a.counters + 6, tmp, lds, s_acc, s_misc)
+                                  a.counters + 6, tmp, lds, s_acc, s_misc, s_tl, s_cur)
                      : 0;
   if (io == nullptr && rt != nullptr && tid == 0) a.counters[6] = 0;
   if (tid == 0) {
