@@ -152,8 +152,10 @@ def test_geo_invalid_selection_computes_nothing():
     bad = torch.tensor([[0, 0], [1, 2], [3, 1], [2, 0]], dtype=torch.int32, device="cuda")  # repeated entry
     O = torch.full((200, 200), 7.0, device="cuda")
     lse = torch.full((200,), 7.0, device="cuda")
-    ws = torch.empty(ssc.workspace_bytes(ssc.OP_GEO_FWD, torch.bfloat16, 200, 210, 128, 200, 4, 4, 2),
-                     dtype=torch.uint8, device="cuda")
+    # a workspace holding leftovers (every byte 1): nothing may read a count
+    # the planner did not write for this call
+    ws = torch.full((ssc.workspace_bytes(ssc.OP_GEO_FWD, torch.bfloat16, 200, 210, 128, 200, 4, 4, 2),),
+                    1, dtype=torch.uint8, device="cuda")
     import ctypes
     st = ssc.lib().coupling_geo_fwd(1, 128, 200, 200, 4, ctypes.c_void_p(dev["offN"].data_ptr()), 210, 4,
                                     ctypes.c_void_p(dev["offM"].data_ptr()), 2, ctypes.c_void_p(bad.data_ptr()),
