@@ -17,7 +17,9 @@ What it computes (spatial-spectral-attention.github.io, "How it works" and
   of each target row restricted to the union of its selected source patches;
   forward and backward for the fixed selection;
 * the linear-attention (ELU feature map) coupling, the pages' linearized
-  baseline (`oracle.linear`), forward and backward.
+  baseline (`oracle.linear`), forward and backward;
+* the least-squares functional map C = Phi_N^+ (Pi Phi_M) that the coupled
+  pipelines compute from the product (`oracle.fmap`), forward and backward.
 
 Every function is the plain definition, written out in fp64 with NumPy; a
 pure-Python brute force (`oracle.brute`) covers tiny inputs.  Parity status:
@@ -29,8 +31,10 @@ from .dense import upcast, dense_fwd, dense_bwd, dense_rows, rowdot
 from .geo import (patch_means, patch_scores, topk, cut_gaps, geo_support,
                   geo_fwd, geo_bwd, executed_pairs)
 from .linear import elu1, elu1_grad, linear_fwd, linear_bwd, linear_weights
+from .fmap import fmap_solve, fmap_solve_bwd
 
 __all__ = ["upcast", "dense_fwd", "dense_bwd", "dense_rows", "rowdot",
            "patch_means", "patch_scores", "topk", "cut_gaps", "geo_support",
            "geo_fwd", "geo_bwd", "executed_pairs",
-           "elu1", "elu1_grad", "linear_fwd", "linear_bwd", "linear_weights"]
+           "elu1", "elu1_grad", "linear_fwd", "linear_bwd", "linear_weights",
+           "fmap_solve", "fmap_solve_bwd"]
