@@ -351,3 +351,18 @@ def make_small(n_N: int, n_M: int, d: int, k: int, dtype: str = "bf16",
             (np.arange(n_M) % P_M).astype(np.int32)
         out.update(P_N=P_N, P_M=P_M, s=s)
     return out
+
+
+def make_basis(n: int, k: int, seed: int = 0, cond: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """A seeded spectral-basis stand-in [n x k] (stored bf16 bits or fp32):
+    sqrt(n) times orthonormal columns, mixed by a random rotation after
+    scaling the columns geometrically from 1 down to 1/cond, so the basis has
+    condition number about `cond` (cond = 1: orthogonal columns of norm
+    sqrt(n), like an eigenbasis orthonormal in the vertex inner product)."""
+    ss = np.random.SeedSequence([8765, seed, n, k])
+    r = [np.random.default_rng(c) for c in ss.spawn(2)]
+    G = r[0].standard_normal((n, k))
+    Qr, _ = np.linalg.qr(G, mode="reduced") if n >= k else (G / math.sqrt(max(n, 1)), None)
+    scales = np.geomspace(1.0, 1.0 / cond, k)
+    W, _ = np.linalg.qr(r[1].standard_normal((k, k)))
+    return _store(math.sqrt(n) * (Qr * scales) @ W.T, dtype)

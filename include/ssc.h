@@ -67,7 +67,9 @@ typedef enum {
   SSC_OP_GEO_FWD = 3,
   SSC_OP_GEO_BWD = 4,
   SSC_OP_LINEAR_FWD = 5,
-  SSC_OP_LINEAR_BWD = 6
+  SSC_OP_LINEAR_BWD = 6,
+  SSC_OP_FMAP_FWD = 7,
+  SSC_OP_FMAP_BWD = 8
 } ssc_op;
 
 typedef void* ssc_stream; /* hipStream_t */
@@ -183,6 +185,28 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
                                const float* O, const void* dO, const float* den,
                                float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
                                ssc_stream stream);
+
+/*
+ * Functional-map solve after the coupling: the coupled pipelines consume only
+ * the product Pi_NM Phi_M (project page, "How it works"); this is the
+ * least-squares map between the two spectral bases,
+ *   C = argmin_C || Phi_N C - O ||_F = (Phi_N^T Phi_N)^{-1} Phi_N^T O,
+ * with O = Pi_NM Phi_M (e.g. a coupling forward's output) and Phi_N the
+ * target basis.  Phi_N [n x k] bf16 (SSC_F32 -> SSC_ERR_UNSUPPORTED), O
+ * [n x k] fp32, C [k x k] fp32 row-major (C[i*k + j]), fully overwritten.
+ * 1 <= k <= 256, n >= 1; Phi_N must have full column rank (else C is NaN).
+ * Rows are contiguous (row stride = width), pointers 16-byte aligned.
+ */
+ssc_status fmap_solve_fwd(ssc_dtype dtype, int n, int k, const void* PhiN, const float* O, float* C,
+                          void* ws, size_t ws_bytes, ssc_stream stream);
+
+/*
+ * Backward of the solve above for an upstream gradient dC [k x k] fp32, with
+ * the basis held fixed: dO = Phi_N (Phi_N^T Phi_N)^{-1} dC, [n x k] fp32,
+ * fully overwritten.
+ */
+ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const float* dC, float* dO,
+                          void* ws, size_t ws_bytes, ssc_stream stream);
 
 /* Static text for a status code. */
 const char* ssc_status_string(ssc_status status);

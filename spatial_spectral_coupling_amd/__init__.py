@@ -31,14 +31,16 @@ __all__ = [
     "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
     "coupling_linear_fwd", "coupling_linear_bwd", "linear_coupling",
+    "fmap_solve_fwd", "fmap_solve_bwd", "fmap_solve",
     "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
-    "OP_LINEAR_FWD", "OP_LINEAR_BWD",
+    "OP_LINEAR_FWD", "OP_LINEAR_BWD", "OP_FMAP_FWD", "OP_FMAP_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libssc.so")
 
-OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD = range(7)
+(OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD,
+ OP_FMAP_FWD, OP_FMAP_BWD) = range(9)
 _F32, _BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
            4: "HIP launch failed"}
@@ -75,6 +77,8 @@ _SIGS = {
     "coupling_linear_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "coupling_linear_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                  _vp]),
+    "fmap_solve_fwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fmap_solve_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -387,3 +391,49 @@ class _LinearCoupling(torch.autograd.Function):
 def linear_coupling(Q, K, V):
     """Differentiable linear-attention coupling (autograd wrapper)."""
     return _LinearCoupling.apply(Q, K, V)
+
+
+def fmap_solve_fwd(PhiN: torch.Tensor, O: torch.Tensor) -> torch.Tensor:
+    """Least-squares functional map C = (PhiN^T PhiN)^-1 PhiN^T O (k x k,
+    fp32) from the coupling's output O = Pi Phi_M (n x k fp32) and the target
+    basis PhiN (n x k bf16)."""
+    dev = _check_dev(PhiN, O)
+    code = _same_dtype(PhiN)
+    n, k = PhiN.shape
+    if O.shape != (n, k) or O.dtype != torch.float32:
+        raise ValueError("O must be n x k float32")
+    C = torch.empty(k, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_FMAP_FWD, code, n, 0, 0, k, 0, 0, 0), dev)
+    _call("fmap_solve_fwd", code, n, k, _p(PhiN), _p(O), _p(C), _p(ws), ws.numel(), _stream(dev))
+    return C
+
+
+def fmap_solve_bwd(PhiN: torch.Tensor, dC: torch.Tensor) -> torch.Tensor:
+    """dO = PhiN (PhiN^T PhiN)^-1 dC (n x k fp32) for an upstream gradient dC
+    (k x k fp32); the basis is held fixed."""
+    dev = _check_dev(PhiN, dC)
+    code = _same_dtype(PhiN)
+    n, k = PhiN.shape
+    if dC.shape != (k, k) or dC.dtype != torch.float32:
+        raise ValueError("dC must be k x k float32")
+    dO = torch.empty(n, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_FMAP_BWD, code, n, 0, 0, k, 0, 0, 0), dev)
+    _call("fmap_solve_bwd", code, n, k, _p(PhiN), _p(dC.contiguous()), _p(dO), _p(ws), ws.numel(), _stream(dev))
+    return dO
+
+
+class _FmapSolve(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, PhiN, O):
+        ctx.save_for_backward(PhiN)
+        return fmap_solve_fwd(PhiN, O)
+
+    @staticmethod
+    def backward(ctx, dC):
+        (PhiN,) = ctx.saved_tensors
+        return None, fmap_solve_bwd(PhiN, dC.float().contiguous())
+
+
+def fmap_solve(PhiN, O):
+    """Differentiable functional-map solve (gradient for O only)."""
+    return _FmapSolve.apply(PhiN, O)

@@ -301,6 +301,39 @@ LinLayout make_lin_layout(bool bwd, int n_N, int n_M, int d, int k) {
   return L;
 }
 
+// Functional-map solve: bf16 basis only; 1 <= k <= 256; n >= 1.
+ssc_status check_fmap(ssc_dtype t, int n, int k) {
+  if (n < 1 || k < 1) return SSC_ERR_INVALID_ARG;
+  if (t != SSC_BF16 || k > kFmMaxK || kpad_for(k) == 0) return SSC_ERR_UNSUPPORTED;
+  return SSC_OK;
+}
+
+struct FmLayout {
+  size_t part = kNone, G = kNone, R = kNone, L = kNone, X = kNone;
+  size_t total = 0;
+  int nblk = 0, nprod = 0;
+};
+
+FmLayout make_fm_layout(bool bwd, int n, int k) {
+  FmLayout L;
+  const size_t KP = (size_t)kpad_for(k);
+  L.nblk = (n + kFmRows - 1) / kFmRows;
+  L.nprod = bwd ? 1 : 3;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = round_up(o + bytes, 256);
+    return at_;
+  };
+  L.part = take((size_t)L.nprod * L.nblk * KP * KP * 4);
+  L.G = take(KP * KP * 4);
+  if (!bwd) L.R = take(KP * KP * 4);
+  L.L = take((size_t)k * (k + 1) / 2 * 4);
+  if (bwd) L.X = take(KP * KP * 2);
+  L.total = o;
+  return L;
+}
+
 ssc_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
   if (L.total == 0) return SSC_OK;
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
@@ -332,6 +365,10 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
     case SSC_OP_LINEAR_BWD:
       if (check_linear(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
       return make_lin_layout(op == SSC_OP_LINEAR_BWD, n_N, n_M, d, k).total;
+    case SSC_OP_FMAP_FWD:
+    case SSC_OP_FMAP_BWD:
+      if (check_fmap(dtype, n_N, k) != SSC_OK) return 0;
+      return make_fm_layout(op == SSC_OP_FMAP_BWD, n_N, k).total;
     default:
       return 0;
   }
@@ -808,6 +845,51 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   SSC_TRY(launch_lin_gram(d, KP, 1, a, L.parts_N, s));
   SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), s));
   SSC_TRY(launch_lin_apply(d, KP, 2, a, s));
+  return SSC_OK;
+}
+
+ssc_status fmap_solve_fwd(ssc_dtype dtype, int n, int k, const void* PhiN, const float* O, float* C, void* ws,
+                          size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_fmap(dtype, n, k);
+  if (st != SSC_OK) return st;
+  if (!all_ok({PhiN, O, C})) return SSC_ERR_INVALID_ARG;
+  const FmLayout L = make_fm_layout(false, n, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bP{PhiN, (size_t)n * k * 2}, bO{O, (size_t)n * k * 4}, bC{C, (size_t)k * k * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bC, bw}, {bP, bO})) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  FmArgs a{};
+  a.Phi = PhiN; a.O = O; a.C = C; a.n = n; a.k = k;
+  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.R = at<float>(ws, L.R); a.L = at<float>(ws, L.L);
+  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, a, L.nblk, 3, s); }));
+  SSC_TRY(launch_fm_reduce(KP, a, L.nblk, 3, s));
+  SSC_TRY(timed("fm_chol", s, [&] { return launch_fm_chol(KP, a, s); }));
+  SSC_TRY(timed("fm_solve", s, [&] { return launch_fm_solve(KP, 0, a, s); }));
+  return SSC_OK;
+}
+
+ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const float* dC, float* dO, void* ws,
+                          size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_fmap(dtype, n, k);
+  if (st != SSC_OK) return st;
+  if (!all_ok({PhiN, dC, dO})) return SSC_ERR_INVALID_ARG;
+  const FmLayout L = make_fm_layout(true, n, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bP{PhiN, (size_t)n * k * 2}, bdC{dC, (size_t)k * k * 4}, bdO{dO, (size_t)n * k * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bdO, bw}, {bP, bdC})) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int KP = kpad_for(k);
+  FmArgs a{};
+  a.Phi = PhiN; a.dC = dC; a.dO = dO; a.n = n; a.k = k;
+  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.L = at<float>(ws, L.L); a.X = at<bf16>(ws, L.X);
+  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, a, L.nblk, 1, s); }));
+  SSC_TRY(launch_fm_reduce(KP, a, L.nblk, 1, s));
+  SSC_TRY(timed("fm_chol", s, [&] { return launch_fm_chol(KP, a, s); }));
+  SSC_TRY(timed("fm_solve", s, [&] { return launch_fm_solve(KP, 1, a, s); }));
+  SSC_TRY(timed("fm_apply", s, [&] { return launch_fm_apply(KP, a, s); }));
   return SSC_OK;
 }
 

@@ -219,6 +219,24 @@ struct LinArgs {
   int n_N, n_M, k;
 };
 
+// Functional-map solve after the coupling (fmap.hip): C = (Phi^T Phi)^-1 Phi^T O
+// and its backward dO = Phi (Phi^T Phi)^-1 dC.
+constexpr int kFmRows = 2048;  // rows per workgroup of the Gram sums
+constexpr int kFmMaxK = 256;
+struct FmArgs {
+  const void* Phi;      // [n x k] bf16
+  const float* O;       // [n x k] (forward)
+  const float* dC;      // [k x k] (backward)
+  float* part;          // [nprod][nblk][KP x KP] Gram partials
+  float* G;             // [KP x KP] Phi^T Phi
+  float* R;             // [KP x KP] Phi^T O (forward)
+  float* L;             // [k (k + 1) / 2] Cholesky factor, packed by rows
+  float* C;             // [k x k] (forward output)
+  bf16* X;              // [KP x KP] G^-1 dC, zero padded (backward)
+  float* dO;            // [n x k] (backward output)
+  int n, k;
+};
+
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
 // ones: column k of the padded V holds ones (k < KP); KP = 256 also runs
@@ -228,6 +246,11 @@ hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid,
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st);
+hipError_t launch_fm_gram(int KP, const FmArgs& a, int nblk, int nprod, hipStream_t st);
+hipError_t launch_fm_reduce(int KP, const FmArgs& a, int nblk, int nprod, hipStream_t st);
+hipError_t launch_fm_chol(int KP, const FmArgs& a, hipStream_t st);
+hipError_t launch_fm_solve(int KP, int mode, const FmArgs& a, hipStream_t st);
+hipError_t launch_fm_apply(int KP, const FmArgs& a, hipStream_t st);
 // merge passes of split geo items (kRoundCUs workgroups, idle past the count)
 hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hipStream_t st);
 hipError_t launch_dq_merge_bf16(int D, const DqArgs& a, hipStream_t st);
