@@ -303,6 +303,27 @@ def main():
                              "pct_hbm": round(100 * by / totl / 1e6 / 8000.0, 2),
                              "what": "ELU linear-attention coupling fwd+bwd, bf16 in / fp32 out, n=60000"}
 
+    if not args.dense_only:
+        # the functional-map solve the coupling feeds (C = (Phi^T Phi)^-1 Phi^T O
+        # for the coupling output O, and its backward), informational as well
+        PhiN = torch.from_numpy(gen.make_basis(n, k, seed=1).view(np.int16)).view(torch.bfloat16).cuda()
+        O_fm, _ = ssc.coupling_dense_fwd(dense["Q"], dense["K"], dense["V"], sc)
+        dC_fm = torch.randn(k, k, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+
+        def fm_f():
+            ssc.fmap_solve_fwd(PhiN, O_fm)
+
+        def fm_b():
+            ssc.fmap_solve_bwd(PhiN, dC_fm)
+
+        phf, totf, _ = time_steps([fm_f, fm_b], args.steps, args.warmup, torch)
+        rec["fmap_60k"] = {"ms": round(totf, 4), "fwd_ms": round(phf[0], 4), "bwd_ms": round(phf[1], 4),
+                           "algorithmic_flop": {"fwd": 4.0 * n * k * k, "bwd": 4.0 * n * k * k},
+                           "algorithmic_bytes": {"fwd": float(n) * k * 6, "bwd": float(n) * k * 8},
+                           "what": "functional-map least squares C = (Phi^T Phi)^-1 Phi^T O on the 60k coupling "
+                                   "output, and its backward dO = Phi (Phi^T Phi)^-1 dC; k=200"}
+        del O_fm
+
     if not args.no_160k and not args.dense_only:
         log("generating the 160k workload")
         c4 = gen.make_config(4)

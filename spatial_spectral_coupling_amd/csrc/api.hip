@@ -309,26 +309,28 @@ ssc_status check_fmap(ssc_dtype t, int n, int k) {
 }
 
 struct FmLayout {
-  size_t part = kNone, G = kNone, R = kNone, L = kNone, X = kNone;
+  size_t part = kNone, G = kNone, R = kNone, Lrow = kNone, Lcol = kNone, rdiag = kNone, X = kNone;
   size_t total = 0;
-  int nblk = 0, nprod = 0;
+  int nblk = 0, rows = 0;
 };
 
 FmLayout make_fm_layout(bool bwd, int n, int k) {
   FmLayout L;
-  const size_t KP = (size_t)kpad_for(k);
-  L.nblk = (n + kFmRows - 1) / kFmRows;
-  L.nprod = bwd ? 1 : 3;
+  const int kp = kpad_for(k);
+  const size_t KP = (size_t)kp;
+  fm_blocks(n, kp, &L.rows, &L.nblk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
     o = round_up(o + bytes, 256);
     return at_;
   };
-  L.part = take((size_t)L.nprod * L.nblk * KP * KP * 4);
+  L.part = take((size_t)(bwd ? 1 : 2) * L.nblk * KP * KP * 4);
   L.G = take(KP * KP * 4);
   if (!bwd) L.R = take(KP * KP * 4);
-  L.L = take((size_t)k * (k + 1) / 2 * 4);
+  L.Lrow = take((size_t)k * (k + 1) / 2 * 4);
+  L.Lcol = take((size_t)k * (k + 1) / 2 * 4);
+  L.rdiag = take((size_t)k * 4);
   if (bwd) L.X = take(KP * KP * 2);
   L.total = o;
   return L;
@@ -862,9 +864,11 @@ ssc_status fmap_solve_fwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
   const int KP = kpad_for(k);
   FmArgs a{};
   a.Phi = PhiN; a.O = O; a.C = C; a.n = n; a.k = k;
-  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.R = at<float>(ws, L.R); a.L = at<float>(ws, L.L);
-  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, a, L.nblk, 3, s); }));
-  SSC_TRY(launch_fm_reduce(KP, a, L.nblk, 3, s));
+  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.R = at<float>(ws, L.R);
+  a.Lrow = at<float>(ws, L.Lrow); a.Lcol = at<float>(ws, L.Lcol); a.rdiag = at<float>(ws, L.rdiag);
+  a.rows = L.rows;
+  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, true, a, L.nblk, s); }));
+  SSC_TRY(launch_fm_reduce(KP, true, a, L.nblk, s));
   SSC_TRY(timed("fm_chol", s, [&] { return launch_fm_chol(KP, a, s); }));
   SSC_TRY(timed("fm_solve", s, [&] { return launch_fm_solve(KP, 0, a, s); }));
   return SSC_OK;
@@ -884,9 +888,11 @@ ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
   const int KP = kpad_for(k);
   FmArgs a{};
   a.Phi = PhiN; a.dC = dC; a.dO = dO; a.n = n; a.k = k;
-  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.L = at<float>(ws, L.L); a.X = at<bf16>(ws, L.X);
-  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, a, L.nblk, 1, s); }));
-  SSC_TRY(launch_fm_reduce(KP, a, L.nblk, 1, s));
+  a.part = at<float>(ws, L.part); a.G = at<float>(ws, L.G); a.X = at<bf16>(ws, L.X);
+  a.Lrow = at<float>(ws, L.Lrow); a.Lcol = at<float>(ws, L.Lcol); a.rdiag = at<float>(ws, L.rdiag);
+  a.rows = L.rows;
+  SSC_TRY(timed("fm_gram", s, [&] { return launch_fm_gram(KP, false, a, L.nblk, s); }));
+  SSC_TRY(launch_fm_reduce(KP, false, a, L.nblk, s));
   SSC_TRY(timed("fm_chol", s, [&] { return launch_fm_chol(KP, a, s); }));
   SSC_TRY(timed("fm_solve", s, [&] { return launch_fm_solve(KP, 1, a, s); }));
   SSC_TRY(timed("fm_apply", s, [&] { return launch_fm_apply(KP, a, s); }));

@@ -221,21 +221,25 @@ struct LinArgs {
 
 // Functional-map solve after the coupling (fmap.hip): C = (Phi^T Phi)^-1 Phi^T O
 // and its backward dO = Phi (Phi^T Phi)^-1 dC.
-constexpr int kFmRows = 2048;  // rows per workgroup of the Gram sums
 constexpr int kFmMaxK = 256;
 struct FmArgs {
   const void* Phi;      // [n x k] bf16
   const float* O;       // [n x k] (forward)
   const float* dC;      // [k x k] (backward)
-  float* part;          // [nprod][nblk][KP x KP] Gram partials
-  float* G;             // [KP x KP] Phi^T Phi
+  float* part;          // [nblk][nprod][KP x KP] Gram partials (G; forward also R)
+  float* G;             // [KP x KP] Phi^T Phi (lower 32-blocks)
   float* R;             // [KP x KP] Phi^T O (forward)
-  float* L;             // [k (k + 1) / 2] Cholesky factor, packed by rows
+  float* Lrow;          // [k (k + 1) / 2] Cholesky factor packed by rows
+  float* Lcol;          // [k (k + 1) / 2] the same packed by columns
+  float* rdiag;         // [k] 1 / L_ii
   float* C;             // [k x k] (forward output)
   bf16* X;              // [KP x KP] G^-1 dC, zero padded (backward)
   float* dO;            // [n x k] (backward output)
   int n, k;
+  int rows;             // rows per Gram block (a multiple of 64)
 };
+// Gram blocking for n rows at padded width KP (rows per block, block count).
+void fm_blocks(int n, int KP, int* rows, int* nblk);
 
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
@@ -246,8 +250,8 @@ hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid,
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st);
-hipError_t launch_fm_gram(int KP, const FmArgs& a, int nblk, int nprod, hipStream_t st);
-hipError_t launch_fm_reduce(int KP, const FmArgs& a, int nblk, int nprod, hipStream_t st);
+hipError_t launch_fm_gram(int KP, bool fwd, const FmArgs& a, int nblk, hipStream_t st);
+hipError_t launch_fm_reduce(int KP, bool fwd, const FmArgs& a, int nblk, hipStream_t st);
 hipError_t launch_fm_chol(int KP, const FmArgs& a, hipStream_t st);
 hipError_t launch_fm_solve(int KP, int mode, const FmArgs& a, hipStream_t st);
 hipError_t launch_fm_apply(int KP, const FmArgs& a, hipStream_t st);
