@@ -92,6 +92,27 @@ def prepare(c, torch, np, gen):
     return dense, geo, offN, offM
 
 
+def fps_record(c, P, steps, warmup, torch, np, gen, ssc):
+    """GPU geodesic FPS partition of the source mesh of workload c (P seeds):
+    ms per call, and whether the labels equal the host generator's."""
+    n = len(c["xM"])
+    off, adj = gen.mesh_csr(c["edges"], n)
+    x = torch.from_numpy(np.ascontiguousarray(c["xM"], np.float64)).cuda()
+    off_d, adj_d = torch.from_numpy(off).cuda(), torch.from_numpy(adj).cuda()
+    st = {}
+
+    def run():
+        st["out"] = ssc.fps_partition(x, off_d, adj_d, P)
+
+    ph, tot, _ = time_steps([run], steps, warmup, torch)
+    same = None
+    if "labM" in c:
+        same = bool(np.array_equal(st["out"][1].cpu().numpy(), c["labM"]))
+    return {"ms": round(tot, 3), "n": n, "P": P, "edges": int(len(c["edges"])),
+            "labels_equal_host_partition": same,
+            "what": "geodesic farthest-point sampling + Voronoi labels of the source mesh, fp64, one GPU"}
+
+
 def time_steps(fns, steps, warmup, torch):
     """Run the phases `fns` (list of callables) per step; returns per-phase ms
     (averaged) and total wall ms per step (events on the current stream)."""
@@ -324,6 +345,9 @@ def main():
                                    "output, and its backward dO = Phi (Phi^T Phi)^-1 dC; k=200"}
         del O_fm
 
+    if not args.dense_only:
+        rec["fps_60k"] = fps_record(c, c["P"], min(args.steps, 5), 1, torch, np, gen, ssc)
+
     if not args.no_160k and not args.dense_only:
         log("generating the 160k workload")
         c4 = gen.make_config(4)
@@ -357,6 +381,7 @@ def main():
                                                "flop": fb4, "target_side_pairs": qb4, "source_side_pairs": kvb4},
                            "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
         del geo4
+        rec["fps_160k"] = fps_record(c4, c4["P"], min(args.steps, 3), 1, torch, np, gen, ssc)
 
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, torch)

@@ -126,6 +126,18 @@ def mesh_edges(faces: np.ndarray) -> np.ndarray:
     return np.unique(e, axis=0)
 
 
+def mesh_csr(edges: np.ndarray, n: int):
+    """CSR adjacency of unique undirected edges, both directions of every
+    edge, neighbours ascending: (off int32 [n+1], adj int32 [2E])."""
+    e = np.asarray(edges, np.int64)
+    src = np.r_[e[:, 0], e[:, 1]]
+    dst = np.r_[e[:, 1], e[:, 0]]
+    order = np.lexsort((dst, src))
+    off = np.zeros(n + 1, np.int64)
+    np.add.at(off, src + 1, 1)
+    return np.cumsum(off).astype(np.int32), dst[order].astype(np.int32)
+
+
 def one_ring_smoother(n: int, edges: np.ndarray) -> sp.csr_matrix:
     """Closed 1-ring mean operator: (I + A) / (1 + deg)."""
     i, j = edges[:, 0], edges[:, 1]

@@ -69,13 +69,15 @@ typedef enum {
   SSC_OP_LINEAR_FWD = 5,
   SSC_OP_LINEAR_BWD = 6,
   SSC_OP_FMAP_FWD = 7,
-  SSC_OP_FMAP_BWD = 8
+  SSC_OP_FMAP_BWD = 8,
+  SSC_OP_FPS = 9
 } ssc_op;
 
 typedef void* ssc_stream; /* hipStream_t */
 
 /* Bytes of scratch an entry point needs for these sizes (0 if the sizes are
- * invalid).  Arguments not used by an op are ignored. */
+ * invalid).  Arguments not used by an op are ignored.  For SSC_OP_FPS:
+ * n_N = vertex count n, n_M = adjacency length nnz, P_N = seed count P. */
 size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, int k,
                            int P_N, int P_M, int s);
 
@@ -207,6 +209,29 @@ ssc_status fmap_solve_fwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
  */
 ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const float* dC, float* dO,
                           void* ws, size_t ws_bytes, ssc_stream stream);
+
+/*
+ * Geodesic farthest-point-sampling partition of one mesh (project page,
+ * sections "Abstract" and "Geo-FlashAttention": the surface is partitioned
+ * with geodesic farthest-point sampling).  Geodesic distance = shortest path
+ * on the edge graph, an edge weighing its Euclidean length
+ * sqrt((dx^2 + dy^2) + dz^2) in fp64, path lengths summed from the start
+ * vertex outward.  Seed 0 is vertex 0; seed t is the vertex farthest from
+ * seeds 0..t-1 (ties to the lower vertex index); labels[v] = t of v's
+ * nearest seed (ties to the earlier seed); dist[v] = that distance (+inf and
+ * label 0 where no seed is reachable).
+ *   x      [n x 3] fp64 positions
+ *   off    [n + 1] int32 CSR offsets (off[0] = 0, nondecreasing, off[n] = nnz)
+ *   adj    [nnz]   int32 neighbours; every undirected edge appears in both
+ *          directions (a one-way entry makes a one-way edge)
+ *   seeds  [P] int32, labels [n] int32, dist [n] fp64 -- outputs, fully written
+ * 1 <= P <= n.  Sizes are checked on the host (SSC_ERR_INVALID_ARG); the
+ * adjacency contents are checked on the device: an offset out of order or
+ * a neighbour outside [0, n) computes nothing and writes seeds = labels = -1
+ * and dist = NaN.  dtype is ignored (the path is fp64).
+ */
+ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const int* adj, int P, int* seeds,
+                         int* labels, double* dist, void* ws, size_t ws_bytes, ssc_stream stream);
 
 /* Static text for a status code. */
 const char* ssc_status_string(ssc_status status);

@@ -31,16 +31,16 @@ __all__ = [
     "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
     "coupling_linear_fwd", "coupling_linear_bwd", "linear_coupling",
-    "fmap_solve_fwd", "fmap_solve_bwd", "fmap_solve",
+    "fmap_solve_fwd", "fmap_solve_bwd", "fmap_solve", "fps_partition",
     "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
-    "OP_LINEAR_FWD", "OP_LINEAR_BWD", "OP_FMAP_FWD", "OP_FMAP_BWD",
+    "OP_LINEAR_FWD", "OP_LINEAR_BWD", "OP_FMAP_FWD", "OP_FMAP_BWD", "OP_FPS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libssc.so")
 
 (OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD,
- OP_FMAP_FWD, OP_FMAP_BWD) = range(9)
+ OP_FMAP_FWD, OP_FMAP_BWD, OP_FPS) = range(10)
 _F32, _BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
            4: "HIP launch failed"}
@@ -79,6 +79,7 @@ _SIGS = {
                                  _vp]),
     "fmap_solve_fwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fmap_solve_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fps_partition": (_i, [_i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -437,3 +438,25 @@ class _FmapSolve(torch.autograd.Function):
 def fmap_solve(PhiN, O):
     """Differentiable functional-map solve (gradient for O only)."""
     return _FmapSolve.apply(PhiN, O)
+
+
+def fps_partition(x: torch.Tensor, off: torch.Tensor, adj: torch.Tensor, P: int):
+    """Geodesic farthest-point sampling of P seeds on a mesh given by fp64
+    positions x [n x 3] and its CSR adjacency (off [n+1], adj [nnz] int32,
+    both directions of every edge).  Returns (seeds [P] int32, labels [n]
+    int32 = index of the nearest seed, dist [n] fp64)."""
+    dev = _check_dev(x, off, adj) if adj.numel() else _check_dev(x, off)
+    if x.dtype != torch.float64 or x.dim() != 2 or x.shape[1] != 3:
+        raise TypeError("x must be n x 3 float64")
+    if off.dtype != torch.int32 or adj.dtype != torch.int32:
+        raise TypeError("off and adj must be int32")
+    n, nnz = x.shape[0], adj.numel()
+    if off.numel() != n + 1:
+        raise ValueError("off must have n + 1 entries")
+    seeds = torch.empty(P, dtype=torch.int32, device=dev)
+    labels = torch.empty(n, dtype=torch.int32, device=dev)
+    dist = torch.empty(n, dtype=torch.float64, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_FPS, 0, n, nnz, 0, 0, P, 0, 0), dev)
+    _call("fps_partition", n, nnz, _p(x), _p(off), _p(adj) if nnz else None, P, _p(seeds), _p(labels), _p(dist),
+          _p(ws), ws.numel(), _stream(dev))
+    return seeds, labels, dist

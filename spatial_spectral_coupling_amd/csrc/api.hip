@@ -308,6 +308,39 @@ ssc_status check_fmap(ssc_dtype t, int n, int k) {
   return SSC_OK;
 }
 
+// Farthest-point sampling: n >= 1 vertices, nnz >= 0 adjacency entries,
+// 1 <= P <= n seeds.
+ssc_status check_fps(int n, int nnz, int P) {
+  if (n < 1 || nnz < 0 || P < 1 || P > n) return SSC_ERR_INVALID_ARG;
+  return SSC_OK;
+}
+
+struct FpsLayout {
+  size_t w = kNone, stamp = kNone, queue = kNone, cmax = kNone, cflag = kNone, bad = kNone;
+  size_t total = 0;
+  int nchunk = 0, nblk = 0;
+};
+
+FpsLayout make_fps_layout(int n, int nnz) {
+  FpsLayout L;
+  L.nchunk = (n + 255) / 256;
+  L.nblk = (n + 255) / 256;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = round_up(o + bytes, 256);
+    return at_;
+  };
+  L.w = take((size_t)nnz * 8);
+  L.stamp = take((size_t)n * 4);
+  L.queue = take((size_t)n * 8);
+  L.cmax = take((size_t)L.nchunk * 8);
+  L.cflag = take((size_t)L.nchunk * 4);
+  L.bad = take((size_t)L.nblk * 4);
+  L.total = o;
+  return L;
+}
+
 struct FmLayout {
   size_t part = kNone, G = kNone, R = kNone, Lrow = kNone, Lcol = kNone, rdiag = kNone, X = kNone;
   size_t total = 0;
@@ -371,6 +404,9 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
     case SSC_OP_FMAP_BWD:
       if (check_fmap(dtype, n_N, k) != SSC_OK) return 0;
       return make_fm_layout(op == SSC_OP_FMAP_BWD, n_N, k).total;
+    case SSC_OP_FPS:
+      if (check_fps(n_N, n_M, P_N) != SSC_OK) return 0;
+      return make_fps_layout(n_N, n_M).total;
     default:
       return 0;
   }
@@ -896,6 +932,28 @@ ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
   SSC_TRY(timed("fm_chol", s, [&] { return launch_fm_chol(KP, a, s); }));
   SSC_TRY(timed("fm_solve", s, [&] { return launch_fm_solve(KP, 1, a, s); }));
   SSC_TRY(timed("fm_apply", s, [&] { return launch_fm_apply(KP, a, s); }));
+  return SSC_OK;
+}
+
+ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const int* adj, int P, int* seeds,
+                         int* labels, double* dist, void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_fps(n, nnz, P);
+  if (st != SSC_OK) return st;
+  if (!all_ok({x, off, seeds, labels, dist}) || (nnz > 0 && adj == nullptr)) return SSC_ERR_INVALID_ARG;
+  const FpsLayout L = make_fps_layout(n, nnz);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bx{x, (size_t)n * 24}, bo{off, (size_t)(n + 1) * 4}, ba{adj, (size_t)nnz * 4};
+  const Buf bs{seeds, (size_t)P * 4}, bl{labels, (size_t)n * 4}, bd{dist, (size_t)n * 8}, bw{ws, ws_bytes};
+  if (!disjoint({bs, bl, bd, bw}, {bx, bo, ba})) return SSC_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FpsArgs a{};
+  a.x = x; a.off = off; a.adj = adj; a.n = n; a.nnz = nnz; a.P = P;
+  a.seeds = seeds; a.labels = labels; a.dist = dist;
+  a.w = at<double>(ws, L.w); a.stamp = at<int>(ws, L.stamp); a.queue = at<int>(ws, L.queue);
+  a.cmax = at<unsigned long long>(ws, L.cmax); a.cflag = at<int>(ws, L.cflag); a.bad = at<int>(ws, L.bad);
+  a.nchunk = L.nchunk; a.nblk = L.nblk;
+  SSC_TRY(timed("fps", s, [&] { return launch_fps(a, s); }));
   return SSC_OK;
 }
 

@@ -1,0 +1,257 @@
+// Geodesic farthest-point-sampling partition on gfx950.  Geo-FlashAttention
+// partitions each surface into patches by geodesic farthest-point sampling
+// (project page "Spatial-Spectral Coupling as Attention", sections
+// "Abstract" and "Geo-FlashAttention"):
+//
+//   * geodesic distance: shortest path on the mesh's edge graph, an edge
+//     weighing its Euclidean length sqrt((dx^2 + dy^2) + dz^2) in fp64;
+//   * seed 0 is vertex 0; seed t is the vertex farthest from the seeds
+//     chosen before it (ties to the lower vertex index);
+//   * every vertex is labelled with its nearest seed (ties to the earlier
+//     seed).
+//
+//   fps_prep  -- checks the adjacency (offsets and neighbour indices), edge
+//                lengths with explicitly rounded fp64 operations (no fused
+//                multiply-add), and the initial state (distance +inf,
+//                label 0, chunk maxima +inf);
+//   fps_run   -- one workgroup of 1024 threads runs all P steps.  Step t
+//                relaxes outward from seed t with a frontier worklist: a
+//                vertex's distance is lowered by a 64-bit atomic minimum on
+//                its bit pattern (non-negative doubles order like their
+//                bits) only when the path through seed t is strictly
+//                shorter, which also relabels it t and queues it for the
+//                next round; a vertex that seed t does not bring strictly
+//                closer stops the wave there (its neighbours cannot gain
+//                either: the distance field satisfies the triangle
+//                inequality in fp64 because rounding is monotone).  The
+//                converged field equals the shortest-path sums along the
+//                paths, as a Dijkstra run would form them.  The next seed is
+//                the argmax over per-chunk maxima (256 vertices a chunk,
+//                recomputed only for chunks the step touched).
+// dist is read only through device-coherent atomic loads, so no stale cache
+// line is ever used after an atomic update made in L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssc {
+namespace fps {
+
+constexpr int kThreads = 1024;
+constexpr int kChunk = 256;  // vertices per argmax chunk
+constexpr int kGroup = 8;    // lanes per frontier vertex (one per neighbour)
+typedef unsigned long long u64;
+constexpr u64 kInfBits = 0x7FF0000000000000ull;
+
+__device__ __forceinline__ u64 umax(u64 a, u64 b) { return a > b ? a : b; }
+
+__device__ __forceinline__ u64 load_bits(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Each operation rounded on its own (no fused multiply-add), as the
+// definition sums the squares.
+__device__ __forceinline__ double edge_len(const double* x, int u, int v) {
+#pragma clang fp contract(off)
+  const double dx = x[3 * u] - x[3 * v];
+  const double dy = x[3 * u + 1] - x[3 * v + 1];
+  const double dz = x[3 * u + 2] - x[3 * v + 2];
+  const double xx = dx * dx, yy = dy * dy, zz = dz * dz;
+  return sqrt((xx + yy) + zz);
+}
+
+// One thread per vertex: validation, edge lengths, initial state.  bad[b]
+// is 1 when block b saw an invalid offset or neighbour.
+__global__ __launch_bounds__(256) void fps_prep(FpsArgs a) {
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  int bad = 0;
+  if (u < a.n) {
+    const int o0 = a.off[u], o1 = a.off[u + 1];
+    if ((u == 0 && o0 != 0) || (u == a.n - 1 && o1 != a.nnz) || o0 < 0 || o1 < o0 || o1 > a.nnz) {
+      bad = 1;
+    } else {
+      for (int e = o0; e < o1; ++e) {
+        const int v = a.adj[e];
+        if (v < 0 || v >= a.n) {
+          bad = 1;
+        } else {
+          a.w[e] = edge_len(a.x, u, v);
+        }
+      }
+    }
+    reinterpret_cast<u64*>(a.dist)[u] = kInfBits;
+    a.labels[u] = 0;
+    a.stamp[u] = -1;
+  }
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < a.nchunk) {
+    a.cmax[c] = kInfBits;
+    a.cflag[c] = 0;
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) a.bad[blockIdx.x] = bad;
+}
+
+// Maximum of (bits, index) pairs: larger bits, then lower index.
+__device__ __forceinline__ void better(u64& b, int& i, u64 b2, int i2) {
+  if (b2 > b || (b2 == b && i2 < i)) {
+    b = b2;
+    i = i2;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
+  __shared__ int s_cnt[3];
+  __shared__ int s_flag;
+  __shared__ int s_seed;
+  __shared__ u64 s_wb[kThreads / 64];
+  __shared__ int s_wi[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n;
+  u64* dbits = reinterpret_cast<u64*>(a.dist);
+
+  if (tid == 0) {
+    s_flag = 0;
+    s_cnt[0] = s_cnt[1] = s_cnt[2] = 0;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.nblk; b += kThreads)
+    if (a.bad[b]) s_flag = 1;
+  __syncthreads();
+  if (s_flag) {  // invalid adjacency: nothing is computed
+    for (int t = tid; t < a.P; t += kThreads) a.seeds[t] = -1;
+    for (int v = tid; v < n; v += kThreads) {
+      a.labels[v] = -1;
+      dbits[v] = 0x7FF8000000000000ull;  // NaN
+    }
+    return;
+  }
+
+  // A step needs at most n rounds: shortest paths are simple (weights are
+  // non-negative and rounding is monotone), and after round h every vertex
+  // whose best path has h edges is final.  A step past n + 1 rounds would be
+  // a fault of this code; it ends the run with seeds[t] = -2.
+  int r = 0;                       // rounds run so far (uniform)
+  int seed = 0;
+  for (int t = 0; t < a.P; ++t) {
+    // seed t starts the queue of round r
+    if (tid == 0) {
+      a.seeds[t] = seed;
+      int c0 = 0;
+      if (load_bits(dbits + seed) > 0ull) {
+        atomicMin(dbits + seed, 0ull);
+        a.labels[seed] = t;
+        a.cflag[seed / kChunk] = 1;
+        a.stamp[seed] = r;
+        a.queue[(size_t)(r & 1) * n] = seed;
+        c0 = 1;
+      }
+      s_seed = c0;
+    }
+    __syncthreads();
+    int cnt = s_seed;
+    int rstep = 0;
+    while (cnt > 0 && rstep <= n) {
+      const int* qin = a.queue + (size_t)(r & 1) * n;
+      int* qout = a.queue + (size_t)((r + 1) & 1) * n;
+      int* ctr = &s_cnt[r % 3];
+      if (tid == 0) s_cnt[(r + 1) % 3] = 0;  // last read two rounds ago
+      const int stamp_next = r + 1;
+      for (int base = 0; base < cnt; base += kThreads / kGroup) {
+        const int q = base + tid / kGroup, j = tid % kGroup;
+        if (q < cnt) {
+          const int u = qin[q];
+          const double du = __longlong_as_double((long long)load_bits(dbits + u));
+          const int o1 = a.off[u + 1];
+          for (int e = a.off[u] + j; e < o1; e += kGroup) {
+            const int v = a.adj[e];
+            const double cand = du + a.w[e];
+            const u64 cb = (u64)__double_as_longlong(cand);
+            const u64 old = atomicMin(dbits + v, cb);
+            if (cb < old) {
+              a.labels[v] = t;
+              a.cflag[v / kChunk] = 1;
+              if (atomicExch(a.stamp + v, stamp_next) != stamp_next) qout[atomicAdd(ctr, 1)] = v;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      cnt = *ctr;
+      ++r;
+      ++rstep;
+    }
+    if (cnt > 0) {
+      if (tid == 0) a.seeds[t] = -2;
+      return;
+    }
+    if (t + 1 == a.P) break;
+
+    // chunk maxima of the chunks this step touched
+    for (int c = wave; c < a.nchunk; c += kThreads / 64) {
+      if (a.cflag[c]) {
+        u64 m = 0;
+#pragma unroll
+        for (int j = 0; j < kChunk / 64; ++j) {
+          const int v = c * kChunk + j * 64 + lane;
+          if (v < n) m = umax(m, load_bits(dbits + v));
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = umax(m, (u64)__shfl_xor(m, o, 64));
+        if (lane == 0) {
+          a.cmax[c] = m;
+          a.cflag[c] = 0;
+        }
+      }
+    }
+    __syncthreads();
+    // the largest chunk maximum, lowest chunk on ties
+    u64 bb = 0;
+    int bi = 0x7fffffff;
+    for (int c = tid; c < a.nchunk; c += kThreads) better(bb, bi, a.cmax[c], c);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const u64 b2 = __shfl_xor(bb, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      better(bb, bi, b2, i2);
+    }
+    if (lane == 0) {
+      s_wb[wave] = bb;
+      s_wi[wave] = bi;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      bb = lane < kThreads / 64 ? s_wb[lane] : 0;
+      bi = lane < kThreads / 64 ? s_wi[lane] : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const u64 b2 = __shfl_xor(bb, o, 64);
+        const int i2 = __shfl_xor(bi, o, 64);
+        better(bb, bi, b2, i2);
+      }
+      // lowest vertex of that chunk holding the maximum
+      int found = -1;
+#pragma unroll
+      for (int j = 0; j < kChunk / 64; ++j) {
+        const int v = bi * kChunk + j * 64 + lane;
+        const bool hit = v < n && load_bits(dbits + v) == bb;
+        const unsigned long long mask = __ballot(hit);
+        if (found < 0 && mask != 0ull) found = bi * kChunk + j * 64 + (__ffsll((long long)mask) - 1);
+      }
+      if (lane == 0) s_seed = found;
+    }
+    __syncthreads();
+    seed = s_seed;
+  }
+}
+
+}  // namespace fps
+
+hipError_t launch_fps(const FpsArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(fps::fps_prep, dim3(a.nblk), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fps::fps_run, dim3(1), dim3(fps::kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ssc

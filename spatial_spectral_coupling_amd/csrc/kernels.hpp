@@ -241,6 +241,25 @@ struct FmArgs {
 // Gram blocking for n rows at padded width KP (rows per block, block count).
 void fm_blocks(int n, int KP, int* rows, int* nblk);
 
+// Geodesic farthest-point-sampling partition (fps.hip).
+struct FpsArgs {
+  const double* x;      // [n x 3] vertex positions
+  const int* off;       // [n + 1] CSR offsets of the adjacency
+  const int* adj;       // [nnz] neighbour indices (both directions of every edge)
+  int n, nnz, P;
+  int* seeds;           // [P] output: seed vertices in sampling order
+  int* labels;          // [n] output: index of the nearest seed
+  double* dist;         // [n] output (and working field): distance to the nearest seed
+  double* w;            // [nnz] edge lengths (workspace)
+  int* stamp;           // [n] round in whose queue a vertex sits (workspace)
+  int* queue;           // [2 n] frontier worklists of two rounds (workspace)
+  unsigned long long* cmax;  // [nchunk] per-chunk maximum distance bits (workspace)
+  int* cflag;           // [nchunk] chunk touched by the current step (workspace)
+  int* bad;             // [nblk] per-block adjacency check (workspace)
+  int nchunk, nblk;
+};
+hipError_t launch_fps(const FpsArgs& a, hipStream_t st);
+
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
 // ones: column k of the padded V holds ones (k < KP); KP = 256 also runs
