@@ -175,3 +175,53 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ssc, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ssc.lib()
+
+
+def test_fmap_and_fps_workspace_sizes(L):
+    w = L.ssc_workspace_bytes
+    f = w(ssc.OP_FMAP_FWD, BF16, 60000, 0, 0, 200, 0, 0, 0)
+    b = w(ssc.OP_FMAP_BWD, BF16, 60000, 0, 0, 200, 0, 0, 0)
+    assert f >= 2 * 224 * 224 * 4 and b >= 224 * 224 * 2
+    assert w(ssc.OP_FMAP_FWD, F32, 60000, 0, 0, 200, 0, 0, 0) == 0       # bf16 basis only
+    assert w(ssc.OP_FMAP_FWD, BF16, 60000, 0, 0, 257, 0, 0, 0) == 0      # k > 256
+    assert w(ssc.OP_FMAP_BWD, BF16, 0, 0, 0, 16, 0, 0, 0) == 0           # n < 1
+    n, nnz = 160000, 960000
+    assert w(ssc.OP_FPS, 0, n, nnz, 0, 0, 640, 0, 0) >= nnz * 8 + n * 12
+    assert w(ssc.OP_FPS, 0, n, nnz, 0, 0, n + 1, 0, 0) == 0              # P > n
+    assert w(ssc.OP_FPS, 0, n, nnz, 0, 0, 0, 0, 0) == 0                  # P < 1
+    assert w(ssc.OP_FPS, 0, 0, 0, 0, 0, 1, 0, 0) == 0                    # no vertex
+
+
+def test_fmap_validation(L):
+    ws = A[5]
+    call = lambda dt=BF16, n=100, k=16, Phi=A[0], O=A[1], C=A[2], wsb=1 << 30: \
+        L.fmap_solve_fwd(dt, n, k, Phi, O, C, ws, wsb, None)
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(k=257) == UNSUPPORTED
+    assert call(k=0) == INVALID
+    assert call(n=0) == INVALID
+    assert call(Phi=None) == INVALID
+    assert call(C=P(0x100000 + 8)) == INVALID                        # misaligned
+    assert call(wsb=16) == WORKSPACE
+    assert call(C=A[0]) == INVALID                                   # output aliases the basis
+    bwd = lambda dt=BF16, n=100, k=16, dO=A[2], wsb=1 << 30: L.fmap_solve_bwd(dt, n, k, A[0], A[1], dO, ws, wsb,
+                                                                              None)
+    assert bwd(dt=F32) == UNSUPPORTED
+    assert bwd(wsb=16) == WORKSPACE
+    assert bwd(dO=A[1]) == INVALID                                   # output aliases dC
+
+
+def test_fps_validation(L):
+    def call(n=100, nnz=600, x=A[0], off=A[1], adj=A[2], Pn=10, seeds=A[3], labels=A[4], dist=A[5], ws=A[6],
+             wsb=1 << 30):
+        return L.fps_partition(n, nnz, x, off, adj, Pn, seeds, labels, dist, ws, wsb, None)
+    assert call(Pn=0) == INVALID
+    assert call(Pn=101) == INVALID
+    assert call(n=0) == INVALID
+    assert call(nnz=-1) == INVALID
+    assert call(adj=None) == INVALID                                 # nnz > 0 needs neighbours
+    assert call(x=None) == INVALID
+    assert call(wsb=64) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(dist=A[0]) == INVALID                                # output aliases the positions
+    assert call(labels=A[3]) == INVALID                              # two outputs alias
