@@ -378,3 +378,21 @@ def make_basis(n: int, k: int, seed: int = 0, cond: float = 1.0, dtype: str = "b
     scales = np.geomspace(1.0, 1.0 / cond, k)
     W, _ = np.linalg.qr(r[1].standard_normal((k, k)))
     return _store(math.sqrt(n) * (Qr * scales) @ W.T, dtype)
+
+
+def make_favor_directions(m: int, d: int, seed: int = 0, orthogonal: bool = True,
+                          dtype: str = "bf16") -> np.ndarray:
+    """Random feature directions W [m x d] for the Performer coupling, drawn
+    from a seeded stream: Gaussian rows, or (orthogonal=True) blocks of d
+    orthonormal rows scaled by the norms of independent Gaussian vectors, so
+    that every row keeps the N(0, I) length distribution."""
+    rng = np.random.default_rng(np.random.SeedSequence([2468, seed, m, d]))
+    if not orthogonal:
+        return _store(rng.standard_normal((m, d)), dtype)
+    blocks = []
+    for _ in range((m + d - 1) // d):
+        Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        blocks.append(Qm.T)
+    W = np.vstack(blocks)[:m]
+    norms = np.linalg.norm(rng.standard_normal((m, d)), axis=1)
+    return _store(W * norms[:, None], dtype)

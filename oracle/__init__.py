@@ -20,7 +20,9 @@ What it computes (spatial-spectral-attention.github.io, "How it works" and
   baseline (`oracle.linear`), forward and backward;
 * the least-squares functional map C = Phi_N^+ (Pi Phi_M) that the coupled
   pipelines compute from the product (`oracle.fmap`), forward and backward;
-* the geodesic farthest-point-sampling patch partition (`oracle.fps`).
+* the geodesic farthest-point-sampling patch partition (`oracle.fps`);
+* the Performer (FAVOR+ positive random features) coupling, the pages'
+  second linearized baseline (`oracle.performer`), forward and backward.
 
 Every function is the plain definition, written out in fp64 with NumPy; a
 pure-Python brute force (`oracle.brute`) covers tiny inputs.  Parity status:
@@ -34,9 +36,11 @@ from .geo import (patch_means, patch_scores, topk, cut_gaps, geo_support,
 from .linear import elu1, elu1_grad, linear_fwd, linear_bwd, linear_weights
 from .fmap import fmap_solve, fmap_solve_bwd
 from .fps import edge_lengths, geodesic_fps
+from .performer import favor_features, performer_fwd, performer_bwd
 
 __all__ = ["upcast", "dense_fwd", "dense_bwd", "dense_rows", "rowdot",
            "patch_means", "patch_scores", "topk", "cut_gaps", "geo_support",
            "geo_fwd", "geo_bwd", "executed_pairs",
            "elu1", "elu1_grad", "linear_fwd", "linear_bwd", "linear_weights",
-           "fmap_solve", "fmap_solve_bwd", "edge_lengths", "geodesic_fps"]
+           "fmap_solve", "fmap_solve_bwd", "edge_lengths", "geodesic_fps",
+           "favor_features", "performer_fwd", "performer_bwd"]
