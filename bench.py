@@ -325,6 +325,23 @@ def main():
                              "what": "ELU linear-attention coupling fwd+bwd, bf16 in / fp32 out, n=60000"}
 
     if not args.dense_only:
+        # the Performer (FAVOR+) coupling on the same 60k tensors, m = d random
+        # features: informational, like the linear record
+        Wf = torch.from_numpy(gen.make_favor_directions(d, d, seed=1).view(np.int16)).view(torch.bfloat16).cuda()
+
+        def pf_f():
+            st["pf"] = ssc.coupling_performer_fwd(dense["Q"], dense["K"], dense["V"], Wf, sc)
+
+        def pf_b():
+            O_, l_ = st["pf"]
+            ssc.coupling_performer_bwd(dense["Q"], dense["K"], dense["V"], Wf, O_, dense["dO"], l_, sc)
+
+        php, totp, _ = time_steps([pf_f, pf_b], args.steps, args.warmup, torch)
+        rec["performer_60k"] = {"ms": round(totp, 4), "fwd_ms": round(php[0], 4), "bwd_ms": round(php[1], 4),
+                                "m": d, "what": "Performer (FAVOR+, m = d orthogonal random features) coupling "
+                                                "fwd+bwd, bf16 in / fp32 out, n=60000"}
+
+    if not args.dense_only:
         # the functional-map solve the coupling feeds (C = (Phi^T Phi)^-1 Phi^T O
         # for the coupling output O, and its backward), informational as well
         PhiN = torch.from_numpy(gen.make_basis(n, k, seed=1).view(np.int16)).view(torch.bfloat16).cuda()

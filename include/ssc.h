@@ -70,7 +70,9 @@ typedef enum {
   SSC_OP_LINEAR_BWD = 6,
   SSC_OP_FMAP_FWD = 7,
   SSC_OP_FMAP_BWD = 8,
-  SSC_OP_FPS = 9
+  SSC_OP_FPS = 9,
+  SSC_OP_PERFORMER_FWD = 10,
+  SSC_OP_PERFORMER_BWD = 11
 } ssc_op;
 
 typedef void* ssc_stream; /* hipStream_t */
@@ -187,6 +189,41 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
                                const float* O, const void* dO, const float* den,
                                float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
                                ssc_stream stream);
+
+/*
+ * Performer coupling: the second linearized baseline the pages compare
+ * against (ai4snews digest, "Synopsis"; project page, "Abstract"), read as
+ * the FAVOR+ estimator with positive random features
+ *   phi(x)_i = exp(sqrt(scale) W[i] . x - scale |x|^2 / 2) / sqrt(m),
+ *   den[i]   = phi(Q[i]) . sum_j phi(K[j]),
+ *   O[i, :]  = phi(Q[i]) (sum_j phi(K[j]) V[j, :]) / den[i],
+ * with m = d directions W [d x d] bf16 (rows; drawn by the caller) and scale
+ * the softmax scale being approximated (e.g. 1/sqrt(d)).  Internally the
+ * features are shifted by per-feature and per-row maxima that cancel in the
+ * ratio (no overflow).  Outputs O [n_N x k] fp32 and lnden [n_N] = ln den[i]
+ * fp32.  bf16 inputs only; d in {64, 128}; 1 <= k <= 255; n_M >= 1; n_N = 0
+ * is a no-op.  Q [n_N x d], K [n_M x d], V [n_M x k] bf16.
+ */
+ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                                  const void* Q, const void* K, const void* V, const void* W,
+                                  float scale, float* O, float* lnden, void* ws, size_t ws_bytes,
+                                  ssc_stream stream);
+
+/*
+ * Performer backward: gradients of <dO, O> w.r.t. Q, K, V (W is held
+ * fixed), with O and lnden from the forward on the same inputs and dO
+ * [n_N x k] bf16.  With g = dO / den, s = (dO . O) / den per row and
+ * d phi_i / dx = phi_i (sqrt(scale) W[i] - scale x):
+ *   dPhiQ = g (phi(K)^T V)^T - s (phi(K)^T 1)^T,
+ *   dPhiK = V (phi(Q)^T g)^T - 1 (phi(Q)^T s)^T,
+ *   dV = phi(K) (phi(Q)^T g), and dQ, dK through d phi / dx.
+ * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ */
+ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+                                  const void* Q, const void* K, const void* V, const void* W,
+                                  float scale, const float* O, const void* dO, const float* lnden,
+                                  float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                                  ssc_stream stream);
 
 /*
  * Functional-map solve after the coupling: the coupled pipelines consume only

@@ -32,15 +32,17 @@ __all__ = [
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
     "coupling_linear_fwd", "coupling_linear_bwd", "linear_coupling",
     "fmap_solve_fwd", "fmap_solve_bwd", "fmap_solve", "fps_partition",
+    "coupling_performer_fwd", "coupling_performer_bwd", "performer_coupling",
     "OP_DENSE_FWD", "OP_DENSE_BWD", "OP_PATCH_TOPK", "OP_GEO_FWD", "OP_GEO_BWD",
-    "OP_LINEAR_FWD", "OP_LINEAR_BWD", "OP_FMAP_FWD", "OP_FMAP_BWD", "OP_FPS",
+    "OP_LINEAR_FWD", "OP_LINEAR_BWD", "OP_FMAP_FWD", "OP_FMAP_BWD", "OP_FPS", "OP_PERFORMER_FWD",
+    "OP_PERFORMER_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libssc.so")
 
 (OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD,
- OP_FMAP_FWD, OP_FMAP_BWD, OP_FPS) = range(10)
+ OP_FMAP_FWD, OP_FMAP_BWD, OP_FPS, OP_PERFORMER_FWD, OP_PERFORMER_BWD) = range(12)
 _F32, _BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
            4: "HIP launch failed"}
@@ -80,6 +82,9 @@ _SIGS = {
     "fmap_solve_fwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fmap_solve_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fps_partition": (_i, [_i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_performer_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_performer_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _sz, _vp]),
 }
 
 
@@ -460,3 +465,57 @@ def fps_partition(x: torch.Tensor, off: torch.Tensor, adj: torch.Tensor, P: int)
     _call("fps_partition", n, nnz, _p(x), _p(off), _p(adj) if nnz else None, P, _p(seeds), _p(labels), _p(dist),
           _p(ws), ws.numel(), _stream(dev))
     return seeds, labels, dist
+
+
+def coupling_performer_fwd(Q, K, V, W, scale: Optional[float] = None):
+    """Performer (FAVOR+) coupling: O = phi(Q) (phi(K)^T V) / den and ln den
+    (fp32), with m = d random directions W [d x d] bf16."""
+    dev = _check_dev(Q, K, V, W)
+    code = _same_dtype(Q, K, V, W)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    if K.shape != (n_M, d) or W.shape != (d, d):
+        raise ValueError("K must be n_M x d and W d x d")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
+    lnden = torch.empty(n_N, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_performer_fwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(lnden), _p(ws),
+          ws.numel(), _stream(dev))
+    return O, lnden
+
+
+def coupling_performer_bwd(Q, K, V, W, O, dO, lnden, scale: Optional[float] = None):
+    """dQ, dK, dV (fp32) of <dO, O> for the Performer coupling (W fixed)."""
+    dev = _check_dev(Q, K, V, W, O, dO, lnden)
+    code = _same_dtype(Q, K, V, W, dO)
+    n_N, d = Q.shape
+    n_M, k = V.shape
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
+    dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_BWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
+    _call("coupling_performer_bwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(dO), _p(lnden),
+          _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
+    return dQ, dK, dV
+
+
+class _PerformerCoupling(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, W, scale):
+        O, lnden = coupling_performer_fwd(Q, K, V, W, scale)
+        ctx.save_for_backward(Q, K, V, W, O, lnden)
+        ctx.scale = scale
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, W, O, lnden = ctx.saved_tensors
+        dQ, dK, dV = coupling_performer_bwd(Q, K, V, W, O, dO.to(Q.dtype).contiguous(), lnden, ctx.scale)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype), None, None
+
+
+def performer_coupling(Q, K, V, W, scale: Optional[float] = None):
+    """Differentiable Performer coupling (autograd wrapper; W gets no gradient)."""
+    return _PerformerCoupling.apply(Q, K, V, W, scale)

@@ -301,6 +301,47 @@ LinLayout make_lin_layout(bool bwd, int n_N, int n_M, int d, int k) {
   return L;
 }
 
+// Performer coupling: the linear layout plus the feature buffers.
+struct PfLayout {
+  LinLayout lin;
+  size_t part = kNone, M2 = kNone, FQ = kNone, FK = kNone, rowoff = kNone, den = kNone, dFQ = kNone,
+         dFK = kNone, Mlo = kNone, MTlo = kNone, dMlo = kNone, dMTlo = kNone;
+  size_t total = 0;
+  int nblk_M = 0;
+};
+
+PfLayout make_pf_layout(bool bwd, int n_N, int n_M, int d, int k) {
+  PfLayout L;
+  L.lin = make_lin_layout(bwd, n_N, n_M, d, k);
+  L.nblk_M = (n_M + 127) / 128;
+  size_t o = L.lin.total;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o = round_up(o + bytes, 256);
+    return at_;
+  };
+  L.part = take((size_t)L.nblk_M * d * 4);
+  L.M2 = take((size_t)d * 4);
+  L.FQ = take((size_t)n_N * d * 2);
+  L.FK = take((size_t)n_M * d * 2);
+  const size_t mat = (size_t)d * kpad_lin(k) * 2;
+  L.Mlo = take(mat);
+  L.MTlo = take(mat);
+  if (bwd) {
+    L.dMlo = take(mat);
+    L.dMTlo = take(mat);
+  }
+  if (!bwd) {
+    L.rowoff = take((size_t)n_N * 4);
+  } else {
+    L.den = take((size_t)n_N * 4);
+    L.dFQ = take((size_t)n_N * d * 4);
+    L.dFK = take((size_t)n_M * d * 4);
+  }
+  L.total = o;
+  return L;
+}
+
 // Functional-map solve: bf16 basis only; 1 <= k <= 256; n >= 1.
 ssc_status check_fmap(ssc_dtype t, int n, int k) {
   if (n < 1 || k < 1) return SSC_ERR_INVALID_ARG;
@@ -404,6 +445,10 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
     case SSC_OP_FMAP_BWD:
       if (check_fmap(dtype, n_N, k) != SSC_OK) return 0;
       return make_fm_layout(op == SSC_OP_FMAP_BWD, n_N, k).total;
+    case SSC_OP_PERFORMER_FWD:
+    case SSC_OP_PERFORMER_BWD:
+      if (check_linear(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
+      return make_pf_layout(op == SSC_OP_PERFORMER_BWD, n_N, n_M, d, k).total;
     case SSC_OP_FPS:
       if (check_fps(n_N, n_M, P_N) != SSC_OK) return 0;
       return make_fps_layout(n_N, n_M).total;
@@ -846,9 +891,9 @@ ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.den = den;
   a.part = at<float>(ws, L.part); a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT);
   a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(timed("lin_gram", s, [&] { return launch_lin_gram(d, KP, 0, a, L.parts_M, s); }));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), s));
-  SSC_TRY(timed("lin_apply", s, [&] { return launch_lin_apply(d, KP, 0, a, s); }));
+  SSC_TRY(timed("lin_gram", s, [&] { return launch_lin_gram(d, KP, 0, false, a, L.parts_M, s); }));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), nullptr, nullptr, s));
+  SSC_TRY(timed("lin_apply", s, [&] { return launch_lin_apply(d, KP, 0, false, a, s); }));
   return SSC_OK;
 }
 
@@ -876,13 +921,113 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT); a.dM = at<char>(ws, L.dM); a.dMT = at<char>(ws, L.dMT);
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(d, KP, 0, a, L.parts_M, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), s));
+  SSC_TRY(launch_lin_gram(d, KP, 0, false, a, L.parts_M, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), nullptr, nullptr, s));
   SSC_TRY(launch_lin_rowprep(a, s));
-  SSC_TRY(launch_lin_apply(d, KP, 1, a, s));
-  SSC_TRY(launch_lin_gram(d, KP, 1, a, L.parts_N, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), s));
-  SSC_TRY(launch_lin_apply(d, KP, 2, a, s));
+  SSC_TRY(launch_lin_apply(d, KP, 1, false, a, s));
+  SSC_TRY(launch_lin_gram(d, KP, 1, false, a, L.parts_N, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), nullptr, nullptr, s));
+  SSC_TRY(launch_lin_apply(d, KP, 2, false, a, s));
+  return SSC_OK;
+}
+
+// The key maxima and the key / query features of the Performer coupling.
+static ssc_status pf_features(int d, const PfLayout& L, void* ws, int n_N, int n_M, const void* Q, const void* K,
+                       const void* W, float scale, int qmode, float* rowoff, const float* lnden, float* den,
+                       hipStream_t s) {
+  PfArgs p{};
+  p.W = W; p.scale = scale; p.part = at<float>(ws, L.part); p.M2 = at<float>(ws, L.M2);
+  p.X = K; p.n = n_M; p.nblk = L.nblk_M; p.F = at<bf16>(ws, L.FK);
+  SSC_TRY(launch_pf_feat(d, 0, p, s));
+  SSC_TRY(launch_pf_maxreduce(d, p, s));
+  SSC_TRY(timed("pf_feat", s, [&] { return launch_pf_feat(d, 1, p, s); }));
+  p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.rowoff = rowoff; p.lnden = lnden; p.den = den;
+  SSC_TRY(launch_pf_feat(d, qmode, p, s));
+  return SSC_OK;
+}
+
+ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                                  const void* V, const void* W, float scale, float* O, float* lnden, void* ws,
+                                  size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SSC_ERR_INVALID_ARG;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, W, O, lnden})) return SSC_ERR_INVALID_ARG;
+  const PfLayout L = make_pf_layout(false, n_N, n_M, d, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
+  const Buf bW{W, (size_t)d * d * 2};
+  const Buf bO{O, (size_t)n_N * k * 4}, bd{lnden, (size_t)n_N * 4}, bw{ws, ws_bytes};
+  if (!disjoint({bO, bd, bw}, {bQ, bK, bV, bW})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* rowoff = at<float>(ws, L.rowoff);
+  st = pf_features(d, L, ws, n_N, n_M, Q, K, W, scale, 2, rowoff, nullptr, nullptr, s);
+  if (st != SSC_OK) return st;
+  const int KP = kpad_lin(k);
+  LinArgs a{};
+  a.Q = at<bf16>(ws, L.FQ); a.K = at<bf16>(ws, L.FK); a.V = V; a.O = O; a.den = lnden; a.rowoff = rowoff;
+  a.part = at<float>(ws, L.lin.part); a.M = at<char>(ws, L.lin.M); a.MT = at<char>(ws, L.lin.MT);
+  a.Mlo = at<char>(ws, L.Mlo); a.MTlo = at<char>(ws, L.MTlo);
+  a.n_N = n_N; a.n_M = n_M; a.k = k;
+  SSC_TRY(launch_lin_gram(d, KP, 0, true, a, L.lin.parts_M, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
+                            at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
+  SSC_TRY(launch_lin_apply(d, KP, 0, true, a, s));
+  return SSC_OK;
+}
+
+ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
+                                  const void* V, const void* W, float scale, const float* O, const void* dO,
+                                  const float* lnden, float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                                  ssc_stream stream) {
+  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SSC_ERR_INVALID_ARG;
+  if (n_N == 0) return SSC_OK;
+  if (!all_ok({Q, K, V, W, O, dO, lnden, dQ, dK, dV})) return SSC_ERR_INVALID_ARG;
+  const PfLayout L = make_pf_layout(true, n_N, n_M, d, k);
+  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
+  const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
+  const Buf bW{W, (size_t)d * d * 2}, bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * 2};
+  const Buf bd{lnden, (size_t)n_N * 4};
+  const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
+  const Buf bw{ws, ws_bytes};
+  if (!disjoint({bdQ, bdK, bdV, bw}, {bQ, bK, bV, bW, bO, bdO, bd})) return SSC_ERR_INVALID_ARG;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* den = at<float>(ws, L.den);
+  st = pf_features(d, L, ws, n_N, n_M, Q, K, W, scale, 3, nullptr, lnden, den, s);
+  if (st != SSC_OK) return st;
+  const int KP = kpad_lin(k);
+  LinArgs a{};
+  a.Q = at<bf16>(ws, L.FQ); a.K = at<bf16>(ws, L.FK); a.V = V; a.dO = dO; a.O = const_cast<float*>(O);
+  a.den = den; a.rden = at<float>(ws, L.lin.rden); a.s = at<float>(ws, L.lin.s); a.part = at<float>(ws, L.lin.part);
+  a.M = at<char>(ws, L.lin.M); a.MT = at<char>(ws, L.lin.MT); a.dM = at<char>(ws, L.lin.dM);
+  a.dMT = at<char>(ws, L.lin.dMT);
+  a.Mlo = at<char>(ws, L.Mlo); a.MTlo = at<char>(ws, L.MTlo); a.dMlo = at<char>(ws, L.dMlo);
+  a.dMTlo = at<char>(ws, L.dMTlo);
+  a.dQ = at<float>(ws, L.dFQ); a.dK = at<float>(ws, L.dFK); a.dV = dV;
+  a.n_N = n_N; a.n_M = n_M; a.k = k;
+  SSC_TRY(launch_lin_gram(d, KP, 0, true, a, L.lin.parts_M, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
+                            at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
+  SSC_TRY(launch_lin_rowprep(a, s));
+  SSC_TRY(launch_lin_apply(d, KP, 1, true, a, s));
+  SSC_TRY(launch_lin_gram(d, KP, 1, true, a, L.lin.parts_N, s));
+  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_N, at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT),
+                            at<char>(ws, L.dMlo), at<char>(ws, L.dMTlo), s));
+  SSC_TRY(launch_lin_apply(d, KP, 2, true, a, s));
+  SSC_TRY(launch_lin_apply(d, KP, 3, true, a, s));
+  PfArgs p{};
+  p.W = W; p.scale = scale;
+  p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.dF = at<float>(ws, L.dFQ); p.dX = dQ;
+  SSC_TRY(launch_pf_dx(d, 0, p, s));
+  p.X = K; p.n = n_M; p.F = at<bf16>(ws, L.FK); p.dF = at<float>(ws, L.dFK); p.dX = dK;
+  SSC_TRY(launch_pf_dx(d, 1, p, s));
   return SSC_OK;
 }
 

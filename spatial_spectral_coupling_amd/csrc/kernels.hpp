@@ -213,11 +213,40 @@ struct LinArgs {
   const void* MT;       // [KP x D]  bf16 KVz_ext^T
   const void* dM;       // [D x KP]  bf16 dKVz_ext
   const void* dMT;      // [KP x D]  bf16 dKVz_ext^T
+  // bf16 rounding remainders of the four matrices above (identity feature
+  // map: each product runs on the high + low pair); null otherwise
+  const void* Mlo;
+  const void* MTlo;
+  const void* dMlo;
+  const void* dMTlo;
   float* dQ;            // [n_N x D]
   float* dK;            // [n_M x D]
   float* dV;            // [n_M x k]
+  const float* rowoff;  // [n_N] identity feature map, forward: den is written as ln(den) + rowoff
   int n_N, n_M, k;
 };
+
+// Performer (FAVOR+) coupling pieces (performer.hip); m = D random features.
+struct PfArgs {
+  const void* X;        // [n x D] bf16 rows (Q or K)
+  const void* W;        // [D x D] bf16 random directions (rows)
+  int n, nblk;          // rows; row blocks of 128
+  float scale;          // softmax scale c (the features use sqrt(c))
+  float* part;          // [nblk x D] per-block key maxima of the exponents (log2 units)
+  float* M2;            // [D] per-feature key maximum (log2 units)
+  bf16* F;              // [n x D] shifted features exp(...) (output of the feature passes)
+  float* rowoff;        // [n] queries, forward: ln den - ln(den of the shifted features)
+  const float* lnden;   // [n] queries, backward: ln den from the forward
+  float* den;           // [n] queries, backward: den of the shifted features
+  const float* dF;      // [n x D] gradient w.r.t. the shifted features (pf_dx)
+  float* dX;            // [n x D] gradient w.r.t. the rows (pf_dx output)
+};
+// mode 0: key maxima, 1: key features, 2: query features + rowoff,
+// 3: query features + den from lnden
+hipError_t launch_pf_feat(int D, int mode, const PfArgs& a, hipStream_t st);
+hipError_t launch_pf_maxreduce(int D, const PfArgs& a, hipStream_t st);
+// mode 0: queries (no row-sum term), 1: keys
+hipError_t launch_pf_dx(int D, int mode, const PfArgs& a, hipStream_t st);
 
 // Functional-map solve after the coupling (fmap.hip): C = (Phi^T Phi)^-1 Phi^T O
 // and its backward dO = Phi (Phi^T Phi)^-1 dC.
@@ -285,9 +314,14 @@ hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-hipError_t launch_lin_gram(int D, int KP, int mode, const LinArgs& a, int grid, hipStream_t st);
-hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, hipStream_t st);
+// ident: the rows of Q / K are precomputed features (identity feature map)
+hipError_t launch_lin_gram(int D, int KP, int mode, bool ident, const LinArgs& a, int grid, hipStream_t st);
+// Mlo / MTlo (optional, may be null): the bf16 rounding remainders
+hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo,
+                             hipStream_t st);
 hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st);
-hipError_t launch_lin_apply(int D, int KP, int mode, const LinArgs& a, hipStream_t st);
+// mode 0: O / den, 1: dQ, 2: dK and dV; with ident, mode 2 gives dK only and
+// mode 3 dV
+hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st);
 
 }  // namespace ssc

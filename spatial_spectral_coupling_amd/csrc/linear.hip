@@ -18,6 +18,9 @@
 // Everything is O(n (d + k)) memory traffic: the kernels are HBM / latency
 // bound; the Gram sums are split over row blocks and reduced in a fixed
 // order (deterministic).
+// With FEAT = 1 the kernels take precomputed feature rows in place of Q and
+// K (identity map, phi' = 1: the "dQ" / "dK" outputs are then the gradients
+// w.r.t. the features); the Performer coupling runs on them.
 #include "tile_bf16.hpp"
 
 namespace ssc {
@@ -34,6 +37,8 @@ constexpr int kApplyRows = 128; // rows per workgroup of the row kernels (4 wave
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
+template <int FEAT>
+__device__ __forceinline__ float feat(float x) { return FEAT ? x : phi(x); }
 
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
@@ -76,11 +81,16 @@ __device__ __forceinline__ void stage_matrix(char* lds, const bf16* g, int rows,
 //   MODE 1 (backward): A = phi(Q),  B = G_ext = [dO / den | -s at KP-1]
 // Rows past the end contribute 0.
 // ---------------------------------------------------------------------------
-template <int D, int KP, int MODE>
+template <int D, int KP, int MODE, int FEAT>
 __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
   constexpr int AP = Geo<D>::PITCH, BP = Geo<KP>::PITCH;
-  __shared__ __attribute__((aligned(16))) char As[kGramTile * AP];
-  __shared__ __attribute__((aligned(16))) char Bs[kGramTile * BP];
+  // identity features, backward: G_ext as a bf16 high + low pair
+  constexpr bool BLO = FEAT == 1 && MODE == 1;
+  // rows per LDS tile (halved where the low part would not fit)
+  constexpr int TR = BLO && (kGramTile * (AP + 2 * BP) > 160 * 1024) ? kGramTile / 2 : kGramTile;
+  __shared__ __attribute__((aligned(16))) char As[TR * AP];
+  __shared__ __attribute__((aligned(16))) char Bs[TR * BP];
+  __shared__ __attribute__((aligned(16))) char Bl[BLO ? TR * BP : 16];
   constexpr int NMB = D / 32, NNB = KP / 32, NB = NMB * NNB, NBW = (NB + 3) / 4;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -103,21 +113,21 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
 #pragma unroll
   for (int t = 0; t < NBW; ++t) acc[t] = f32x16{};
 
-  for (int r0 = r_begin; r0 < r_end; r0 += kGramTile) {
-    for (int ch = tid; ch < kGramTile * (D / 8); ch += 256) {
+  for (int r0 = r_begin; r0 < r_end; r0 += TR) {
+    for (int ch = tid; ch < TR * (D / 8); ch += 256) {
       const int r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
       float v[8];
       if (gr < r_end) {
         row8(X + (size_t)gr * D, c8 * 8, D, true, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = phi(v[e]);
+        for (int e = 0; e < 8; ++e) v[e] = feat<FEAT>(v[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.f;
       }
       *reinterpret_cast<bf16x8*>(As + r * AP + c8 * 16) = pack8(v);
     }
-    for (int ch = tid; ch < kGramTile * (KP / 8); ch += 256) {
+    for (int ch = tid; ch < TR * (KP / 8); ch += 256) {
       const int r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
       float v[8];
       if (gr < r_end) {
@@ -132,16 +142,26 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = 0.f;
       }
-      *reinterpret_cast<bf16x8*>(Bs + r * BP + c8 * 16) = pack8(v);
+      const bf16x8 hv = pack8(v);
+      *reinterpret_cast<bf16x8*>(Bs + r * BP + c8 * 16) = hv;
+      if (BLO) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)hv[e];
+        *reinterpret_cast<bf16x8*>(Bl + r * BP + c8 * 16) = pack8(lo);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kc = 0; kc < kGramTile / 16; ++kc) {
+    for (int kc = 0; kc < TR / 16; ++kc) {
 #pragma unroll
       for (int t = 0; t < NBW; ++t) {
         const int bi = wave + 4 * t;
-        if (NB % 4 == 0 || bi < NB)
-          acc[t] = mma(ta.frag(As, bi / NNB, kc), tbr.frag(Bs, bi % NNB, kc), acc[t]);
+        if (NB % 4 == 0 || bi < NB) {
+          const bf16x8 af = ta.frag(As, bi / NNB, kc);
+          acc[t] = mma(af, tbr.frag(Bs, bi % NNB, kc), acc[t]);
+          if (BLO) acc[t] = mma(af, tbr.frag(Bl, bi % NNB, kc), acc[t]);
+        }
       }
     }
     __syncthreads();
@@ -159,9 +179,11 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
 }
 
 // Fixed-order sum of the Gram partials, written as bf16 in both layouts:
-// M [D x KP] and MT [KP x D].
+// M [D x KP] and MT [KP x D]; with Mlo / MTlo also the bf16 rounding of the
+// remainder (the pair carries the sum to about 2^-17).
 template <int D, int KP>
-__global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts, bf16* M, bf16* MT) {
+__global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts, bf16* M, bf16* MT, bf16* Mlo,
+                                                  bf16* MTlo) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= D * KP) return;
   const int d = idx / KP, c = idx - d * KP;
@@ -178,6 +200,11 @@ __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts,
   const bf16 v = (bf16)s;
   M[idx] = v;
   MT[(size_t)c * D + d] = v;
+  if (Mlo != nullptr) {
+    const bf16 lo = (bf16)(s - (float)v);
+    Mlo[idx] = lo;
+    MTlo[(size_t)c * D + d] = lo;
+  }
 }
 
 // Per target row of the backward: rden = 1 / den, s = (dO . O) / den
@@ -205,27 +232,39 @@ __global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
 //   MODE 1: dQ = phi'(Q) * (G_ext KVz_ext^T)            (LDS: KVz_ext [D x KP])
 //   MODE 2: dK = phi'(K) * (V_ext dKVz_ext^T),
 //           dV = phi(K) dKV                              (LDS: both layouts)
+// With FEAT = 1 the matrix of modes 0, 1 and of dK runs as a bf16 high + low
+// pair (both in LDS, two MFMAs per step), and so does G_ext in mode 1; mode 2
+// then gives dK only and mode 3 gives dV (the two layouts with a low part
+// exceed the LDS).
 // Scores are computed transposed (C[col][row]) so that a lane holds its own
 // row and the operand fragments of that row come from its own registers.
 // ---------------------------------------------------------------------------
-template <int D, int KP, int MODE>
+template <int D, int KP, int MODE, int FEAT>
 __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
-  constexpr int SZ_T = MODE == 1 ? 0 : KP * Geo<D>::PITCH;  // [KP x D] layout
-  constexpr int SZ_M = MODE == 0 ? 0 : D * Geo<KP>::PITCH;  // [D x KP] layout
-  __shared__ __attribute__((aligned(16))) char lds[SZ_T + SZ_M + 16];
+  // which layouts this mode reads, and whether with a low part
+  constexpr bool USE_T = FEAT ? (MODE == 0 || MODE == 3) : MODE != 1;
+  constexpr bool USE_M = FEAT ? (MODE == 1 || MODE == 2) : MODE != 0;
+  constexpr bool LO_T = FEAT && MODE == 0, LO_M = FEAT && USE_M;
+  constexpr int SZ_T = USE_T ? KP * Geo<D>::PITCH : 0;  // [KP x D] layout
+  constexpr int SZ_M = USE_M ? D * Geo<KP>::PITCH : 0;  // [D x KP] layout
+  __shared__ __attribute__((aligned(16))) char lds[SZ_T * (LO_T ? 2 : 1) + SZ_M * (LO_M ? 2 : 1) + 16];
   char* LT = lds;
-  char* LM = lds + SZ_T;
+  char* LTlo = lds + SZ_T;
+  char* LM = lds + SZ_T * (LO_T ? 2 : 1);
+  char* LMlo = LM + SZ_M;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int n = MODE == 2 ? a.n_M : a.n_N;
+  const int n = MODE >= 2 ? a.n_M : a.n_N;
   const int row = blockIdx.x * kApplyRows + wave * 32 + l32;
   const bool row_ok = row < n;
   const bool vec = (a.k & 7) == 0;
 
-  if (MODE != 1) stage_matrix<D>(LT, reinterpret_cast<const bf16*>(MODE == 0 ? a.MT : a.dMT), KP, tid);
-  if (MODE != 0) stage_matrix<KP>(LM, reinterpret_cast<const bf16*>(MODE == 1 ? a.M : a.dM), D, tid);
+  if (USE_T) stage_matrix<D>(LT, reinterpret_cast<const bf16*>(MODE == 0 ? a.MT : a.dMT), KP, tid);
+  if (LO_T) stage_matrix<D>(LTlo, reinterpret_cast<const bf16*>(a.MTlo), KP, tid);
+  if (USE_M) stage_matrix<KP>(LM, reinterpret_cast<const bf16*>(MODE == 1 ? a.M : a.dM), D, tid);
+  if (LO_M) stage_matrix<KP>(LMlo, reinterpret_cast<const bf16*>(MODE == 1 ? a.Mlo : a.dMlo), D, tid);
   __syncthreads();
 
   RowReader<D> rT;
@@ -234,15 +273,15 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   rM.init(l32, h);
 
   // this lane's row of phi(X) (MODE 0: Q, MODE 2: K) as bf16 fragments
-  const bf16* X = reinterpret_cast<const bf16*>(MODE == 2 ? a.K : a.Q) + (size_t)(row_ok ? row : 0) * D;
+  const bf16* X = reinterpret_cast<const bf16*>(MODE >= 2 ? a.K : a.Q) + (size_t)(row_ok ? row : 0) * D;
   bf16x8 xf[D / 16];
-  if (MODE != 1) {
+  if (MODE == 0 || (FEAT ? MODE == 3 : MODE == 2)) {
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
       float v[8];
       row8(X, cc * 16 + 8 * h, D, true, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = row_ok ? phi(v[e]) : 0.f;
+      for (int e = 0; e < 8; ++e) v[e] = row_ok ? feat<FEAT>(v[e]) : 0.f;
       xf[cc] = pack8(v);
     }
   }
@@ -253,7 +292,10 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
     for (int mb = 0; mb < KP / 32; ++mb) {
       acc[mb] = f32x16{};
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) acc[mb] = mma(rT.read(LT, mb, cc), xf[cc], acc[mb]);
+      for (int cc = 0; cc < D / 16; ++cc) {
+        acc[mb] = mma(rT.read(LT, mb, cc), xf[cc], acc[mb]);
+        if (LO_T) acc[mb] = mma(rT.read(LTlo, mb, cc), xf[cc], acc[mb]);
+      }
     }
     // den = C[KP-1][row]: element 15 of the last block, held by the h = 1 lanes
     const float own = acc[KP / 32 - 1][15], other = xor32(own);
@@ -276,7 +318,7 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
           }
         }
       }
-      if (h == 0) a.den[row] = den;
+      if (h == 0) a.den[row] = FEAT ? __logf(den) + a.rowoff[row] : den;
     }
     return;
   }
@@ -285,7 +327,9 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
     // G_ext row fragments: c < k: dO / den; c = KP-1: -s; else 0
     const bf16* dOr = reinterpret_cast<const bf16*>(a.dO) + (size_t)(row_ok ? row : 0) * a.k;
     const float rd = row_ok ? a.rden[row] : 0.f, sv = row_ok ? a.s[row] : 0.f;
-    bf16x8 gf[KP / 16];
+    // identity features: G_ext as a bf16 high + low pair too (the product
+    // takes hi.hi + lo.hi + hi.lo)
+    bf16x8 gf[KP / 16], gl[FEAT ? KP / 16 : 1];
 #pragma unroll
     for (int cc = 0; cc < KP / 16; ++cc) {
       float v[8];
@@ -294,13 +338,24 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
       for (int e = 0; e < 8; ++e) v[e] *= rd;
       if (cc == KP / 16 - 1 && h == 1) v[7] = -sv;
       gf[cc] = pack8(v);
+      if (FEAT) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)gf[cc][e];
+        gl[FEAT ? cc : 0] = pack8(lo);
+      }
     }
     f32x16 acc[D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
       acc[mb] = f32x16{};
 #pragma unroll
-      for (int cc = 0; cc < KP / 16; ++cc) acc[mb] = mma(rM.read(LM, mb, cc), gf[cc], acc[mb]);
+      for (int cc = 0; cc < KP / 16; ++cc) {
+        const bf16x8 mh = rM.read(LM, mb, cc);
+        acc[mb] = mma(mh, gf[cc], acc[mb]);
+        if (LO_M) acc[mb] = mma(rM.read(LMlo, mb, cc), gf[cc], acc[mb]);
+        if (FEAT) acc[mb] = mma(mh, gl[FEAT ? cc : 0], acc[mb]);
+      }
     }
     if (row_ok) {
       const bf16* Qr = reinterpret_cast<const bf16*>(a.Q) + (size_t)row * D;
@@ -310,16 +365,22 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = mb * 32 + 8 * g + 4 * h;
-          const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qr + d0);
-          *reinterpret_cast<f32x4*>(out + d0) =
-              f32x4{dphi((float)q4[0]) * acc[mb][4 * g], dphi((float)q4[1]) * acc[mb][4 * g + 1],
-                    dphi((float)q4[2]) * acc[mb][4 * g + 2], dphi((float)q4[3]) * acc[mb][4 * g + 3]};
+          if (FEAT) {
+            *reinterpret_cast<f32x4*>(out + d0) =
+                f32x4{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
+          } else {
+            const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qr + d0);
+            *reinterpret_cast<f32x4*>(out + d0) =
+                f32x4{dphi((float)q4[0]) * acc[mb][4 * g], dphi((float)q4[1]) * acc[mb][4 * g + 1],
+                      dphi((float)q4[2]) * acc[mb][4 * g + 2], dphi((float)q4[3]) * acc[mb][4 * g + 3]};
+          }
         }
       }
     }
     return;
   }
 
+  if (MODE == 2 || (FEAT && MODE == 3)) {
   // MODE 2: V_ext row fragments (c < k: V; c = KP-1: 1; else 0)
   const bf16* Vr = reinterpret_cast<const bf16*>(a.V) + (size_t)(row_ok ? row : 0) * a.k;
   bf16x8 vf[KP / 16];
@@ -330,12 +391,16 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
     if (cc == KP / 16 - 1 && h == 1) v[7] = 1.f;
     vf[cc] = pack8(v);
   }
+  if (MODE == 2) {
   f32x16 c1[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
     c1[mb] = f32x16{};
 #pragma unroll
-    for (int cc = 0; cc < KP / 16; ++cc) c1[mb] = mma(rM.read(LM, mb, cc), vf[cc], c1[mb]);
+    for (int cc = 0; cc < KP / 16; ++cc) {
+      c1[mb] = mma(rM.read(LM, mb, cc), vf[cc], c1[mb]);
+      if (LO_M) c1[mb] = mma(rM.read(LMlo, mb, cc), vf[cc], c1[mb]);
+    }
   }
   if (row_ok) {
     const bf16* Kr = reinterpret_cast<const bf16*>(a.K) + (size_t)row * D;
@@ -345,13 +410,19 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = mb * 32 + 8 * g + 4 * h;
-        const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kr + d0);
-        *reinterpret_cast<f32x4*>(out + d0) =
-            f32x4{dphi((float)k4[0]) * c1[mb][4 * g], dphi((float)k4[1]) * c1[mb][4 * g + 1],
-                  dphi((float)k4[2]) * c1[mb][4 * g + 2], dphi((float)k4[3]) * c1[mb][4 * g + 3]};
+        if (FEAT) {
+          *reinterpret_cast<f32x4*>(out + d0) = f32x4{c1[mb][4 * g], c1[mb][4 * g + 1], c1[mb][4 * g + 2], c1[mb][4 * g + 3]};
+        } else {
+          const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kr + d0);
+          *reinterpret_cast<f32x4*>(out + d0) =
+              f32x4{dphi((float)k4[0]) * c1[mb][4 * g], dphi((float)k4[1]) * c1[mb][4 * g + 1],
+                    dphi((float)k4[2]) * c1[mb][4 * g + 2], dphi((float)k4[3]) * c1[mb][4 * g + 3]};
+        }
       }
     }
   }
+  }
+  if (FEAT ? MODE == 3 : MODE == 2) {
   f32x16 c2[KP / 32];
 #pragma unroll
   for (int nb = 0; nb < KP / 32; ++nb) {
@@ -376,6 +447,8 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
       }
     }
   }
+  }
+  }
 }
 
 }  // namespace lin
@@ -395,23 +468,30 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   X(64, 64)                  \
   X(64, 32)
 
-hipError_t launch_lin_gram(int D, int KP, int mode, const LinArgs& a, int grid, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                              \
-  if (D == DD && KP == KK) {                                                                       \
-    if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0>), dim3(grid), dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1>), dim3(grid), dim3(256), 0, st, a);           \
-    return hipGetLastError();                                                                      \
+hipError_t launch_lin_gram(int D, int KP, int mode, bool ident, const LinArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                         \
+  if (D == DD && KP == KK) {                                                                                  \
+    if (ident) {                                                                                              \
+      if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0, 1>), dim3(grid), dim3(256), 0, st, a);      \
+      else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1, 1>), dim3(grid), dim3(256), 0, st, a);                \
+    } else {                                                                                                  \
+      if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0, 0>), dim3(grid), dim3(256), 0, st, a);      \
+      else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1, 0>), dim3(grid), dim3(256), 0, st, a);                \
+    }                                                                                                         \
+    return hipGetLastError();                                                                                 \
   }
   SSC_LIN_INSTANCES(SSC_L)
 #undef SSC_L
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, hipStream_t st) {
+hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo,
+                             hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                    \
   if (D == DD && KP == KK) {                                                                             \
     hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 255) / 256), dim3(256), 0, st, part, nparts, \
-                       reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT));                        \
+                       reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT), reinterpret_cast<bf16*>(Mlo),  \
+                       reinterpret_cast<bf16*>(MTlo));                                                   \
     return hipGetLastError();                                                                            \
   }
   SSC_LIN_INSTANCES(SSC_L)
@@ -424,15 +504,23 @@ hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_lin_apply(int D, int KP, int mode, const LinArgs& a, hipStream_t st) {
-  const int n = mode == 2 ? a.n_M : a.n_N;
+template <int D, int KP, int FEAT>
+void launch_lin_apply_t(int mode, const LinArgs& a, int grid, hipStream_t st) {
+  if (mode == 0) hipLaunchKernelGGL((lin::lin_apply<D, KP, 0, FEAT>), dim3(grid), dim3(256), 0, st, a);
+  else if (mode == 1) hipLaunchKernelGGL((lin::lin_apply<D, KP, 1, FEAT>), dim3(grid), dim3(256), 0, st, a);
+  else if (mode == 2) hipLaunchKernelGGL((lin::lin_apply<D, KP, 2, FEAT>), dim3(grid), dim3(256), 0, st, a);
+  else if constexpr (FEAT == 1) hipLaunchKernelGGL((lin::lin_apply<D, KP, 3, FEAT>), dim3(grid), dim3(256), 0, st, a);
+}
+
+hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st) {
+  if (mode == 3 && !ident) return hipErrorInvalidValue;
+  const int n = mode >= 2 ? a.n_M : a.n_N;
   const int grid = (n + lin::kApplyRows - 1) / lin::kApplyRows;
-#define SSC_L(DD, KK)                                                                                 \
-  if (D == DD && KP == KK) {                                                                          \
-    if (mode == 0) hipLaunchKernelGGL((lin::lin_apply<DD, KK, 0>), dim3(grid), dim3(256), 0, st, a);   \
-    else if (mode == 1) hipLaunchKernelGGL((lin::lin_apply<DD, KK, 1>), dim3(grid), dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((lin::lin_apply<DD, KK, 2>), dim3(grid), dim3(256), 0, st, a);             \
-    return hipGetLastError();                                                                         \
+#define SSC_L(DD, KK)                                                                 \
+  if (D == DD && KP == KK) {                                                          \
+    if (ident) launch_lin_apply_t<DD, KK, 1>(mode, a, grid, st);                      \
+    else launch_lin_apply_t<DD, KK, 0>(mode, a, grid, st);                            \
+    return hipGetLastError();                                                         \
   }
   SSC_LIN_INSTANCES(SSC_L)
 #undef SSC_L

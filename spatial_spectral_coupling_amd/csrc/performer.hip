@@ -1,0 +1,278 @@
+// Performer (FAVOR+) coupling on gfx950: the pages' second linearized
+// baseline (ai4snews digest, "Synopsis"; project page, "Abstract"), read as
+// the FAVOR+ estimator of the softmax kernel with positive random features:
+//
+//     phi(x)_i = exp(sqrt(c) w_i . x - c |x|^2 / 2) / sqrt(m),
+//     O_q = phi(q) (sum_j phi(k_j) v_j^T) / (phi(q) . sum_j phi(k_j)),
+//
+// with c the softmax scale and m = D directions w_i (rows of W, an input).
+// The ratio is unchanged when phi_i(k) is multiplied by e^{-M_i} for every
+// key and phi_i(q) by e^{M_i - M_q}: the kernels use M_i = max_j of key j's
+// exponent for feature i and M_q = the largest shifted query exponent of
+// row q, so every stored feature lies in (0, 1] and the largest query
+// feature of a row is 1 (no overflow; no row underflows entirely).  The
+// |q|^2 term and 1/sqrt(m) are row constants and cancel as well.  The
+// linear-attention kernels (identity feature map) then form the products;
+// ln den is reported for the true features: ln(den of the shifted features)
+// + M_q - c|q|^2/2 - ln m.
+//
+//   pf_feat      -- the features of 128 rows per workgroup: S = X W^T on bf16
+//                   MFMA (transposed: a lane owns a row, the features of that
+//                   row sit in its accumulators), then
+//                   mode 0: per-block maxima of the key exponents,
+//                   mode 1: key features exp2(s - M_i),
+//                   mode 2/3: query features exp2(u - M_q), u = s + M_i, and
+//                   the row offset (forward) or the shifted den recovered
+//                   from ln den (backward);
+//   pf_maxreduce -- M_i = max over the blocks (exact, order-free);
+//   pf_dx        -- dX = sqrt(c) (dF o F) W - c x rowsum(dF o F) (keys; for
+//                   queries the row sum vanishes: dO.O - dO.O), dF o F as a
+//                   bf16 high + low pair on MFMA.
+#include "tile_bf16.hpp"
+
+namespace ssc {
+namespace pf {
+
+using tb::Geo;
+using tb::put_pair;
+using tb::RowReader;
+using tb::TrReader;
+
+constexpr int kRows = 128;  // rows per workgroup (4 waves x 32)
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) put_pair(r, m, v[2 * m], v[2 * m + 1]);
+  return r;
+}
+
+// W [D x D] bf16 (row-major, global) into LDS with the padded pitch.
+template <int D>
+__device__ __forceinline__ void stage_w(char* lds, const bf16* W, int tid) {
+  constexpr int CW = D / 8;
+  for (int ch = tid; ch < D * CW; ch += 256) {
+    const int r = ch / CW, c = ch - r * CW;
+    *reinterpret_cast<bf16x8*>(lds + r * Geo<D>::PITCH + c * 16) =
+        *reinterpret_cast<const bf16x8*>(W + (size_t)r * D + c * 8);
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) char Ws[D * Geo<D>::PITCH];
+  __shared__ float sred[MODE == 0 ? 4 * D : D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  stage_w<D>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
+  if (MODE != 0)
+    for (int f = tid; f < D; f += 256) sred[f] = a.M2[f];
+  const int row = blockIdx.x * kRows + wave * 32 + l32;
+  const bool row_ok = row < a.n;
+  const bf16* X = reinterpret_cast<const bf16*>(a.X) + (size_t)(row_ok ? row : 0) * D;
+  bf16x8 xf[D / 16];
+  float ss = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(X + cc * 16 + 8 * h);
+    if (!row_ok) v = bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += (float)v[e] * (float)v[e];
+    xf[cc] = v;
+  }
+  ss += __shfl_xor(ss, 32, 64);
+  __syncthreads();
+  RowReader<D> rw;
+  rw.init(l32, h);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb) {
+    acc[fb] = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) acc[fb] = mma(rw.read(Ws, fb, cc), xf[cc], acc[fb]);
+  }
+  // feature fb*32 + c_row(i, h) of row l32 is acc[fb][i]; exponents in log2 units
+  const float sig2 = sqrtf(a.scale) * kLog2e;
+  const float sq2 = 0.5f * a.scale * ss * kLog2e;
+
+  if (MODE == 0) {
+#pragma unroll
+    for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = row_ok ? sig2 * acc[fb][i] - sq2 : -INFINITY;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        if (l32 == 0) sred[wave * D + fb * 32 + c_row(i, h)] = v;
+      }
+    __syncthreads();
+    for (int f = tid; f < D; f += 256)
+      a.part[(size_t)blockIdx.x * D + f] =
+          fmaxf(fmaxf(sred[f], sred[D + f]), fmaxf(sred[2 * D + f], sred[3 * D + f]));
+    return;
+  }
+
+  float mq = 0.f;
+  if (MODE >= 2) {
+    // u = s + M_i; M_q = max over the row's features (both lane halves)
+    float m = -INFINITY;
+#pragma unroll
+    for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[fb][i] = sig2 * acc[fb][i] + sred[fb * 32 + c_row(i, h)];
+        m = fmaxf(m, acc[fb][i]);
+      }
+    mq = fmaxf(m, __shfl_xor(m, 32, 64));
+  } else {
+#pragma unroll
+    for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[fb][i] = sig2 * acc[fb][i] - sq2 - sred[fb * 32 + c_row(i, h)];
+  }
+  if (!row_ok) return;
+  bf16* F = a.F + (size_t)row * D;
+#pragma unroll
+  for (int fb = 0; fb < D / 32; ++fb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)__builtin_amdgcn_exp2f(acc[fb][4 * q + e] - mq);
+      *reinterpret_cast<bf16x4*>(F + fb * 32 + 8 * q + 4 * h) = o;
+    }
+  if (MODE >= 2 && h == 0) {
+    const float off = (mq - sq2) * kLn2 - __logf((float)D);
+    if (MODE == 2) a.rowoff[row] = off;
+    else a.den[row] = __expf(a.lnden[row] - off);
+  }
+}
+
+__global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int D) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= D) return;
+  float m8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m8[u] = -INFINITY;
+  int b = 0;
+  for (; b + 8 <= a.nblk; b += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], a.part[(size_t)(b + u) * D + f]);
+  }
+  for (int u = 0; b < a.nblk; ++b, ++u) m8[u] = fmaxf(m8[u], a.part[(size_t)b * D + f]);
+  float m = m8[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u) m = fmaxf(m, m8[u]);
+  a.M2[f] = m;
+}
+
+// dX = sqrt(c) (dF o F) W  -  [keys] c x rowsum(dF o F).  A wave owns 32 rows;
+// W^T enters as transposed LDS reads (A operand: output dimension x feature),
+// so a lane's G fragment takes the features kc*16 + {4h..4h+3, 8+4h..8+4h+3}.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) char Ws[D * Geo<D>::PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  stage_w<D>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
+  const int row = blockIdx.x * kRows + wave * 32 + l32;
+  const bool row_ok = row < a.n;
+  const size_t r = (size_t)(row_ok ? row : 0) * D;
+  bf16x8 gh[D / 16], gl[D / 16];
+  float rs = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int f0 = kc * 16 + 8 * p + 4 * h;
+      const f32x4 df = *reinterpret_cast<const f32x4*>(a.dF + r + f0);
+      const bf16x4 fv = *reinterpret_cast<const bf16x4*>(a.F + r + f0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g = row_ok ? df[e] * (float)fv[e] : 0.f;
+        rs += g;
+        const float gh1 = (float)(bf16)g;
+        hi[4 * p + e] = gh1;
+        lo[4 * p + e] = g - gh1;
+      }
+    }
+    gh[kc] = pack8(hi);
+    gl[kc] = pack8(lo);
+  }
+  rs += __shfl_xor(rs, 32, 64);
+  __syncthreads();
+  const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  TrReader<D> tw;
+  tw.init(tr_r, tr_c);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    acc[db] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const bf16x8 w = tw.frag(Ws, db, kc);
+      acc[db] = mma(w, gh[kc], acc[db]);
+      acc[db] = mma(w, gl[kc], acc[db]);
+    }
+  }
+  if (!row_ok) return;
+  const float sig = sqrtf(a.scale), c = a.scale;
+  const bf16* X = reinterpret_cast<const bf16*>(a.X) + r;
+  float* out = a.dX + r;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d0 = db * 32 + 8 * q + 4 * h;
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = sig * acc[db][4 * q + e];
+      if (MODE == 1) {
+        const bf16x4 xv = *reinterpret_cast<const bf16x4*>(X + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] -= c * (float)xv[e] * rs;
+      }
+      *reinterpret_cast<f32x4*>(out + d0) = o;
+    }
+}
+
+}  // namespace pf
+
+#define SSC_PF_INSTANCES(X) X(128) X(64)
+
+hipError_t launch_pf_feat(int D, int mode, const PfArgs& a, hipStream_t st) {
+  const int grid = (a.n + pf::kRows - 1) / pf::kRows;
+#define SSC_L(DD)                                                                                  \
+  if (D == DD) {                                                                                   \
+    if (mode == 0) hipLaunchKernelGGL((pf::pf_feat<DD, 0>), dim3(grid), dim3(256), 0, st, a);      \
+    else if (mode == 1) hipLaunchKernelGGL((pf::pf_feat<DD, 1>), dim3(grid), dim3(256), 0, st, a); \
+    else if (mode == 2) hipLaunchKernelGGL((pf::pf_feat<DD, 2>), dim3(grid), dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((pf::pf_feat<DD, 3>), dim3(grid), dim3(256), 0, st, a);                \
+    return hipGetLastError();                                                                      \
+  }
+  SSC_PF_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pf_maxreduce(int D, const PfArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(pf::pf_maxreduce, dim3((D + 255) / 256), dim3(256), 0, st, a, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_pf_dx(int D, int mode, const PfArgs& a, hipStream_t st) {
+  const int grid = (a.n + pf::kRows - 1) / pf::kRows;
+#define SSC_L(DD)                                                                            \
+  if (D == DD) {                                                                             \
+    if (mode == 0) hipLaunchKernelGGL((pf::pf_dx<DD, 0>), dim3(grid), dim3(256), 0, st, a);  \
+    else hipLaunchKernelGGL((pf::pf_dx<DD, 1>), dim3(grid), dim3(256), 0, st, a);            \
+    return hipGetLastError();                                                                \
+  }
+  SSC_PF_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssc
