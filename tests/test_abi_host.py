@@ -225,3 +225,29 @@ def test_fps_validation(L):
     assert call(ws=None) == WORKSPACE
     assert call(dist=A[0]) == INVALID                                # output aliases the positions
     assert call(labels=A[3]) == INVALID                              # two outputs alias
+
+
+def test_performer_validation(L):
+    w = L.ssc_workspace_bytes
+    assert w(ssc.OP_PERFORMER_BWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) > \
+        w(ssc.OP_PERFORMER_FWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) > 60000 * 128 * 4
+    assert w(ssc.OP_PERFORMER_FWD, BF16, 10, 10, 96, 200, 0, 0, 0) == 0     # d unsupported
+    assert w(ssc.OP_PERFORMER_FWD, BF16, 10, 10, 128, 256, 0, 0, 0) == 0    # no normaliser column
+    ws = A[8]
+
+    def fwd(dt=BF16, nN=64, nM=64, d=128, k=200, scale=0.1, O=A[4], lnden=A[5], wsb=1 << 30):
+        return L.coupling_performer_fwd(dt, nN, nM, d, k, A[0], A[1], A[2], A[3], scale, O, lnden, ws, wsb, None)
+    assert fwd(dt=F32) == UNSUPPORTED
+    assert fwd(d=96) == UNSUPPORTED
+    assert fwd(nM=0) == INVALID
+    assert fwd(scale=0.0) == INVALID
+    assert fwd(scale=-1.0) == INVALID
+    assert fwd(wsb=64) == WORKSPACE
+    assert fwd(O=A[3]) == INVALID                                   # output aliases W
+    assert fwd(nN=0) == OK                                          # nothing to do
+
+    def bwd(dQ=A[6], wsb=1 << 30):
+        return L.coupling_performer_bwd(BF16, 64, 64, 128, 200, A[0], A[1], A[2], A[3], 0.1, A[4], A[9], A[5], dQ,
+                                        A[7], A[10], ws, wsb, None)
+    assert bwd(wsb=64) == WORKSPACE
+    assert bwd(dQ=A[0]) == INVALID                                  # gradient aliases Q
