@@ -149,22 +149,17 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
   }
 }
 
+// One workgroup per feature: the block maxima in parallel, then a tree.
 __global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int D) {
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= D) return;
-  float m8[8];
+  __shared__ float sm[4];
+  const int f = blockIdx.x, tid = threadIdx.x;
+  float m = -INFINITY;
+  for (int b = tid; b < a.nblk; b += 256) m = fmaxf(m, a.part[(size_t)b * D + f]);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) m8[u] = -INFINITY;
-  int b = 0;
-  for (; b + 8 <= a.nblk; b += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], a.part[(size_t)(b + u) * D + f]);
-  }
-  for (int u = 0; b < a.nblk; ++b, ++u) m8[u] = fmaxf(m8[u], a.part[(size_t)b * D + f]);
-  float m = m8[0];
-#pragma unroll
-  for (int u = 1; u < 8; ++u) m = fmaxf(m, m8[u]);
-  a.M2[f] = m;
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((tid & 63) == 0) sm[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) a.M2[f] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
 }
 
 // dX = sqrt(c) (dF o F) W  -  [keys] c x rowsum(dF o F).  A wave owns 32 rows;
@@ -258,7 +253,7 @@ hipError_t launch_pf_feat(int D, int mode, const PfArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_pf_maxreduce(int D, const PfArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pf::pf_maxreduce, dim3((D + 255) / 256), dim3(256), 0, st, a, D);
+  hipLaunchKernelGGL(pf::pf_maxreduce, dim3(D), dim3(256), 0, st, a, D);
   return hipGetLastError();
 }
 
