@@ -227,7 +227,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the coupling runs on a single "
+        print(json.dumps({"error": "the benchmark measures one GPU only; the coupling runs on a single "
                                    "MI355X (multi-GPU sharding is a design note, not implemented)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)

@@ -28,7 +28,7 @@ import scipy.sparse.csgraph as csgraph
 from scipy.spatial import ConvexHull
 
 __all__ = [
-    "CONFIGS",
+    "WORKLOADS",
     "Config",
     "bf16_bits_from_f32",
     "bf16_bits_to_f32",
@@ -61,7 +61,7 @@ class Config:
     seed_index: int = -1   # SeedSequence([1234, seed_index])
 
 
-CONFIGS = (
+WORKLOADS = (
     Config(0, "dense-1k-f32", 1000, 64, 30, "f32", "sphere-uniform", seed_index=0),
     Config(1, "dense-5k-bf16", 5000, 128, 200, "bf16", "mesh", seed_index=1),
     Config(2, "dense-60k-bf16", 60000, 128, 200, "bf16", "mesh-two", seed_index=2),
@@ -295,7 +295,7 @@ def make_config(i: int, with_partition: Optional[bool] = None) -> dict:
     patch labels in original order), P, s.  Positions xN, xM (fp64) and the
     edge list are included for the mesh workloads.
     """
-    cfg = CONFIGS[i]
+    cfg = WORKLOADS[i]
     st = _streams(cfg.seed_index)
     xm, xn_base, faces, edges = _geometry(cfg, st)
     xn, FN, FM, Phi, dO = _finish(cfg, st, xm, xn_base)
