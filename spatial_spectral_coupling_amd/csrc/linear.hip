@@ -64,14 +64,27 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
   return r;
 }
 
-// Copy a row-major bf16 matrix [rows x W] (global, unpadded) into an LDS
-// tile with the padded pitch of Geo<W>.
-template <int W>
-__device__ __forceinline__ void stage_matrix(char* lds, const bf16* g, int rows, int tid) {
-  constexpr int CW = W / 8;
-  for (int ch = tid; ch < rows * CW; ch += 256) {
-    const int r = ch / CW, c = ch - r * CW;
-    *reinterpret_cast<bf16x8*>(lds + r * Geo<W>::PITCH + c * 16) = ld8(g + (size_t)r * W + c * 8);
+// Copy a row-major bf16 matrix [ROWS x W] (global, unpadded) into an LDS
+// tile with the padded pitch of Geo<W>; loads are issued in batches of
+// eight before their stores, so they are in flight together.
+template <int W, int ROWS>
+__device__ __forceinline__ void stage_matrix(char* lds, const bf16* g, int tid) {
+  constexpr int CW = W / 8, N = ROWS * CW, B = 8;
+  for (int base = 0; base < N; base += B * 256) {
+    bf16x8 v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int ch = base + j * 256 + tid;
+      if (ch < N) v[j] = ld8(g + (size_t)ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int ch = base + j * 256 + tid;
+      if (ch < N) {
+        const int r = ch / CW, c = ch - r * CW;
+        *reinterpret_cast<bf16x8*>(lds + r * Geo<W>::PITCH + c * 16) = v[j];
+      }
+    }
   }
 }
 
@@ -114,34 +127,54 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
   for (int t = 0; t < NBW; ++t) acc[t] = f32x16{};
 
   for (int r0 = r_begin; r0 < r_end; r0 += TR) {
-    for (int ch = tid; ch < TR * (D / 8); ch += 256) {
-      const int r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
-      float v[8];
-      if (gr < r_end) {
-        row8(X + (size_t)gr * D, c8 * 8, D, true, v);
+    // every load of the tile first (in flight together), then the feature
+    // map / scaling and the LDS stores
+    constexpr int NXA = TR * (D / 8) / 256, NYB = TR * (KP / 8) / 256;
+    static_assert(NXA * 256 == TR * (D / 8) && NYB * 256 == TR * (KP / 8), "gram tile split");
+    bf16x8 xa[NXA], yb[NYB];
+    float rdv[MODE == 1 ? NYB : 1], sv[MODE == 1 ? NYB : 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = feat<FEAT>(v[e]);
+    for (int j = 0; j < NXA; ++j) {
+      const int ch = tid + 256 * j, r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
+      xa[j] = gr < r_end ? ld8(X + (size_t)gr * D + c8 * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int j = 0; j < NYB; ++j) {
+      const int ch = tid + 256 * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+      const bool in = gr < r_end && c8 * 8 < a.k;
+      if (in && vec && c8 * 8 + 8 <= a.k) {
+        yb[j] = ld8(Y + (size_t)gr * a.k + c8 * 8);
+      } else if (in) {
+        float v[8];
+        row8(Y + (size_t)gr * a.k, c8 * 8, a.k, false, v);
+        yb[j] = pack8(v);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        yb[j] = bf16x8{};
       }
+      if (MODE == 1) {
+        rdv[MODE == 1 ? j : 0] = gr < r_end ? a.rden[gr] : 0.f;
+        sv[MODE == 1 ? j : 0] = gr < r_end && c8 == KP / 8 - 1 ? a.s[gr] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NXA; ++j) {
+      const int ch = tid + 256 * j, r = ch / (D / 8), c8 = ch - r * (D / 8);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = r0 + r < r_end ? feat<FEAT>((float)xa[j][e]) : 0.f;
       *reinterpret_cast<bf16x8*>(As + r * AP + c8 * 16) = pack8(v);
     }
-    for (int ch = tid; ch < TR * (KP / 8); ch += 256) {
-      const int r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+#pragma unroll
+    for (int j = 0; j < NYB; ++j) {
+      const int ch = tid + 256 * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
       float v[8];
-      if (gr < r_end) {
-        row8(Y + (size_t)gr * a.k, c8 * 8, a.k, vec, v);
-        if (MODE == 1) {
-          const float rd = a.rden[gr];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= rd;
-        }
-        if (c8 == KP / 8 - 1) v[7] = MODE == 0 ? 1.f : -a.s[gr];
-      } else {
+      for (int e = 0; e < 8; ++e) v[e] = (float)yb[j][e];
+      if (MODE == 1) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        for (int e = 0; e < 8; ++e) v[e] *= rdv[MODE == 1 ? j : 0];
       }
+      if (gr < r_end && c8 == KP / 8 - 1) v[7] = MODE == 0 ? 1.f : -sv[MODE == 1 ? j : 0];
       const bf16x8 hv = pack8(v);
       *reinterpret_cast<bf16x8*>(Bs + r * BP + c8 * 16) = hv;
       if (BLO) {
@@ -184,19 +217,20 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
 template <int D, int KP>
 __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts, bf16* M, bf16* MT, bf16* Mlo,
                                                   bf16* MTlo) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= D * KP) return;
+  // eight threads per output element: thread u sums the partials u, u + 8,
+  // ... (one of eight independent partial sums), then the eight sums are
+  // combined in a fixed order (deterministic)
+  __shared__ float s8[8][32];
+  const int u = threadIdx.x >> 5, e = threadIdx.x & 31;
+  const int idx = blockIdx.x * 32 + e;
+  float acc = 0.f;
+  if (idx < D * KP)
+    for (int b = u; b < nparts; b += 8) acc += part[(size_t)b * D * KP + idx];
+  s8[u][e] = acc;
+  __syncthreads();
+  if (u != 0 || idx >= D * KP) return;
+  const float s = ((s8[0][e] + s8[1][e]) + (s8[2][e] + s8[3][e])) + ((s8[4][e] + s8[5][e]) + (s8[6][e] + s8[7][e]));
   const int d = idx / KP, c = idx - d * KP;
-  // eight independent partial sums (loads in flight together), combined in
-  // a fixed order
-  float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int b = 0;
-  for (; b + 8 <= nparts; b += 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s8[u] += part[(size_t)(b + u) * D * KP + idx];
-  }
-  for (int u = 0; b < nparts; ++b, ++u) s8[u] += part[(size_t)b * D * KP + idx];
-  const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   const bf16 v = (bf16)s;
   M[idx] = v;
   MT[(size_t)c * D + d] = v;
@@ -208,18 +242,29 @@ __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts,
 }
 
 // Per target row of the backward: rden = 1 / den, s = (dO . O) / den
-// (one wave per row).
+// (16 lanes per row, 16 rows per workgroup; the 16 partial dot products are
+// added in a fixed butterfly order).
 __global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.n_N) return;
-  const bf16* dO = reinterpret_cast<const bf16*>(a.dO) + (size_t)row * a.k;
-  const float* O = a.O + (size_t)row * a.k;
+  const int sub = threadIdx.x & 15;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool ok = row < a.n_N;
+  const bf16* dO = reinterpret_cast<const bf16*>(a.dO) + (size_t)(ok ? row : 0) * a.k;
+  const float* O = a.O + (size_t)(ok ? row : 0) * a.k;
   float acc = 0.f;
-  for (int c = lane; c < a.k; c += 64) acc += (float)dO[c] * O[c];
+  if (ok) {
+    if ((a.k & 3) == 0) {
+      for (int c = 4 * sub; c < a.k; c += 64) {
+        const bf16x4 g = *reinterpret_cast<const bf16x4*>(dO + c);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(O + c);
+        acc += ((float)g[0] * o[0] + (float)g[1] * o[1]) + ((float)g[2] * o[2] + (float)g[3] * o[3]);
+      }
+    } else {
+      for (int c = sub; c < a.k; c += 16) acc += (float)dO[c] * O[c];
+    }
+  }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (lane == 0) {
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (ok && sub == 0) {
     const float rd = 1.f / a.den[row];
     a.rden[row] = rd;
     a.s[row] = acc * rd;
@@ -261,10 +306,10 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   const bool row_ok = row < n;
   const bool vec = (a.k & 7) == 0;
 
-  if (USE_T) stage_matrix<D>(LT, reinterpret_cast<const bf16*>(MODE == 0 ? a.MT : a.dMT), KP, tid);
-  if (LO_T) stage_matrix<D>(LTlo, reinterpret_cast<const bf16*>(a.MTlo), KP, tid);
-  if (USE_M) stage_matrix<KP>(LM, reinterpret_cast<const bf16*>(MODE == 1 ? a.M : a.dM), D, tid);
-  if (LO_M) stage_matrix<KP>(LMlo, reinterpret_cast<const bf16*>(MODE == 1 ? a.Mlo : a.dMlo), D, tid);
+  if (USE_T) stage_matrix<D, KP>(LT, reinterpret_cast<const bf16*>(MODE == 0 ? a.MT : a.dMT), tid);
+  if (LO_T) stage_matrix<D, KP>(LTlo, reinterpret_cast<const bf16*>(a.MTlo), tid);
+  if (USE_M) stage_matrix<KP, D>(LM, reinterpret_cast<const bf16*>(MODE == 1 ? a.M : a.dM), tid);
+  if (LO_M) stage_matrix<KP, D>(LMlo, reinterpret_cast<const bf16*>(MODE == 1 ? a.Mlo : a.dMlo), tid);
   __syncthreads();
 
   RowReader<D> rT;
@@ -489,7 +534,7 @@ hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void*
                              hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                    \
   if (D == DD && KP == KK) {                                                                             \
-    hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 255) / 256), dim3(256), 0, st, part, nparts, \
+    hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 31) / 32), dim3(256), 0, st, part, nparts,   \
                        reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT), reinterpret_cast<bf16*>(Mlo),  \
                        reinterpret_cast<bf16*>(MTlo));                                                   \
     return hipGetLastError();                                                                            \
@@ -500,7 +545,7 @@ hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void*
 }
 
 hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(lin::lin_rowprep, dim3((a.n_N + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lin::lin_rowprep, dim3((a.n_N + 15) / 16), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
