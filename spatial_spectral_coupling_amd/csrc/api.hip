@@ -928,6 +928,7 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   SSC_TRY(launch_lin_gram(d, KP, 1, false, a, L.parts_N, s));
   SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), nullptr, nullptr, s));
   SSC_TRY(launch_lin_apply(d, KP, 2, false, a, s));
+  SSC_TRY(launch_lin_apply(d, KP, 3, false, a, s));
   return SSC_OK;
 }
 

@@ -320,8 +320,7 @@ hipError_t launch_lin_gram(int D, int KP, int mode, bool ident, const LinArgs& a
 hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo,
                              hipStream_t st);
 hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st);
-// mode 0: O / den, 1: dQ, 2: dK and dV; with ident, mode 2 gives dK only and
-// mode 3 dV
+// mode 0: O / den, 1: dQ, 2: dK, 3: dV
 hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st);
 
 }  // namespace ssc

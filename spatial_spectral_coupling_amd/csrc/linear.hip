@@ -275,20 +275,19 @@ __global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
 // Row kernels (a wave owns 32 rows; lane l32 owns row l32 of the wave's block)
 //   MODE 0: O = phi(Q) KV / den, den = phi(Q) z        (LDS: KVz^T [KP x D])
 //   MODE 1: dQ = phi'(Q) * (G_ext KVz_ext^T)            (LDS: KVz_ext [D x KP])
-//   MODE 2: dK = phi'(K) * (V_ext dKVz_ext^T),
-//           dV = phi(K) dKV                              (LDS: both layouts)
-// With FEAT = 1 the matrix of modes 0, 1 and of dK runs as a bf16 high + low
-// pair (both in LDS, two MFMAs per step), and so does G_ext in mode 1; mode 2
-// then gives dK only and mode 3 gives dV (the two layouts with a low part
-// exceed the LDS).
+//   MODE 2: dK = phi'(K) * (V_ext dKVz_ext^T)            (LDS: dKVz_ext [D x KP])
+//   MODE 3: dV = phi(K) dKV                              (LDS: dKVz_ext^T [KP x D])
+// (one layout each, so two workgroups fit a CU).  With FEAT = 1 the matrix of
+// modes 0, 1, 2 runs as a bf16 high + low pair (both in LDS, two MFMAs per
+// step), and so does G_ext in mode 1.
 // Scores are computed transposed (C[col][row]) so that a lane holds its own
 // row and the operand fragments of that row come from its own registers.
 // ---------------------------------------------------------------------------
 template <int D, int KP, int MODE, int FEAT>
 __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   // which layouts this mode reads, and whether with a low part
-  constexpr bool USE_T = FEAT ? (MODE == 0 || MODE == 3) : MODE != 1;
-  constexpr bool USE_M = FEAT ? (MODE == 1 || MODE == 2) : MODE != 0;
+  constexpr bool USE_T = MODE == 0 || MODE == 3;
+  constexpr bool USE_M = MODE == 1 || MODE == 2;
   constexpr bool LO_T = FEAT && MODE == 0, LO_M = FEAT && USE_M;
   constexpr int SZ_T = USE_T ? KP * Geo<D>::PITCH : 0;  // [KP x D] layout
   constexpr int SZ_M = USE_M ? D * Geo<KP>::PITCH : 0;  // [D x KP] layout
@@ -317,10 +316,10 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   RowReader<KP> rM;
   rM.init(l32, h);
 
-  // this lane's row of phi(X) (MODE 0: Q, MODE 2: K) as bf16 fragments
+  // this lane's row of phi(X) (MODE 0: Q, MODE 3: K) as bf16 fragments
   const bf16* X = reinterpret_cast<const bf16*>(MODE >= 2 ? a.K : a.Q) + (size_t)(row_ok ? row : 0) * D;
   bf16x8 xf[D / 16];
-  if (MODE == 0 || (FEAT ? MODE == 3 : MODE == 2)) {
+  if (MODE == 0 || MODE == 3) {
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
       float v[8];
@@ -425,7 +424,7 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
     return;
   }
 
-  if (MODE == 2 || (FEAT && MODE == 3)) {
+  if (MODE == 2 || MODE == 3) {
   // MODE 2: V_ext row fragments (c < k: V; c = KP-1: 1; else 0)
   const bf16* Vr = reinterpret_cast<const bf16*>(a.V) + (size_t)(row_ok ? row : 0) * a.k;
   bf16x8 vf[KP / 16];
@@ -467,7 +466,7 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
     }
   }
   }
-  if (FEAT ? MODE == 3 : MODE == 2) {
+  if (MODE == 3) {
   f32x16 c2[KP / 32];
 #pragma unroll
   for (int nb = 0; nb < KP / 32; ++nb) {
@@ -554,11 +553,10 @@ void launch_lin_apply_t(int mode, const LinArgs& a, int grid, hipStream_t st) {
   if (mode == 0) hipLaunchKernelGGL((lin::lin_apply<D, KP, 0, FEAT>), dim3(grid), dim3(256), 0, st, a);
   else if (mode == 1) hipLaunchKernelGGL((lin::lin_apply<D, KP, 1, FEAT>), dim3(grid), dim3(256), 0, st, a);
   else if (mode == 2) hipLaunchKernelGGL((lin::lin_apply<D, KP, 2, FEAT>), dim3(grid), dim3(256), 0, st, a);
-  else if constexpr (FEAT == 1) hipLaunchKernelGGL((lin::lin_apply<D, KP, 3, FEAT>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((lin::lin_apply<D, KP, 3, FEAT>), dim3(grid), dim3(256), 0, st, a);
 }
 
 hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st) {
-  if (mode == 3 && !ident) return hipErrorInvalidValue;
   const int n = mode >= 2 ? a.n_M : a.n_N;
   const int grid = (n + lin::kApplyRows - 1) / lin::kApplyRows;
 #define SSC_L(DD, KK)                                                                 \
