@@ -31,7 +31,8 @@
  *   are always fp32.  lse is in natural log.
  * - Supported shapes: d in {64, 128}; 1 <= k <= 256 (padded internally to
  *   the next of 32, 64, 128, 224, 256); n_M >= 1; n_N >= 0 (n_N = 0 is a
- *   no-op).  fp32 inputs: k <= 128.  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= P_M.
+ *   no-op); n_N, n_M <= 2^22 for the couplings (larger -> SSC_ERR_UNSUPPORTED).
+ *   fp32 inputs: k <= 128.  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= P_M.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
  *   stream) and re-entrant: no global mutable state (the optional kernel
  *   timer below is per thread), no host sync.
@@ -53,7 +54,7 @@ extern "C" {
 typedef enum {
   SSC_OK = 0,
   SSC_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, overlap */
-  SSC_ERR_UNSUPPORTED = 2,  /* d, k, P or s outside the compiled set */
+  SSC_ERR_UNSUPPORTED = 2,  /* d, k, P, s or a row count outside the compiled set */
   SSC_ERR_WORKSPACE = 3,    /* ws too small (or NULL with ws_bytes > 0) */
   SSC_ERR_HIP = 4           /* a HIP launch failed */
 } ssc_status;

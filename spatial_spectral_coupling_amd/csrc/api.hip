@@ -244,11 +244,16 @@ hipError_t timed(const char* family, hipStream_t s, F&& launch) {
 }
 
 // Shape checks shared by the coupling entry points.
+// Rows per side: tiles address rows with 32-bit byte offsets (rows x up to
+// 512 bytes), kept below 2^31.
+constexpr int kMaxRows = 1 << 22;
+
 ssc_status check_shape(ssc_dtype t, int n_N, int n_M, int d, int k) {
   if (t != SSC_F32 && t != SSC_BF16) return SSC_ERR_INVALID_ARG;
   if (n_N < 0 || n_M < 1 || d < 1 || k < 1) return SSC_ERR_INVALID_ARG;
   const int KP = kpad_for(k);
   if (KP == 0 || !supported(dt(t), d, KP)) return SSC_ERR_UNSUPPORTED;
+  if (n_N > kMaxRows || n_M > kMaxRows) return SSC_ERR_UNSUPPORTED;
   return SSC_OK;
 }
 
@@ -267,6 +272,7 @@ ssc_status check_linear(ssc_dtype t, int n_N, int n_M, int d, int k) {
   if (t != SSC_F32 && t != SSC_BF16) return SSC_ERR_INVALID_ARG;
   if (n_N < 0 || n_M < 1 || d < 1 || k < 1) return SSC_ERR_INVALID_ARG;
   if (t != SSC_BF16 || (d != 64 && d != 128) || kpad_lin(k) == 0) return SSC_ERR_UNSUPPORTED;
+  if (n_N > kMaxRows || n_M > kMaxRows) return SSC_ERR_UNSUPPORTED;
   return SSC_OK;
 }
 

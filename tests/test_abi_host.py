@@ -251,3 +251,13 @@ def test_performer_validation(L):
                                         A[7], A[10], ws, wsb, None)
     assert bwd(wsb=64) == WORKSPACE
     assert bwd(dQ=A[0]) == INVALID                                  # gradient aliases Q
+
+
+def test_row_count_limit(L):
+    # the couplings address rows with 32-bit byte offsets: at most 2^22 rows a side
+    big = (1 << 22) + 1
+    assert dense_fwd(L, nN=big) == UNSUPPORTED
+    assert dense_fwd(L, nM=big) == UNSUPPORTED
+    assert L.ssc_workspace_bytes(ssc.OP_DENSE_BWD, BF16, big, 64, 128, 200, 0, 0, 0) == 0
+    assert L.ssc_workspace_bytes(ssc.OP_LINEAR_FWD, BF16, 64, big, 128, 200, 0, 0, 0) == 0
+    assert L.ssc_workspace_bytes(ssc.OP_DENSE_FWD, BF16, 1 << 22, 1 << 22, 128, 200, 0, 0, 0) > 0
