@@ -82,9 +82,38 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     xf[cc] = v;
   }
   ss += __shfl_xor(ss, 32, 64);
-  __syncthreads();
+  const float sig2 = sqrtf(a.scale) * kLog2e;
+  const float sq2 = 0.5f * a.scale * ss * kLog2e;
   RowReader<D> rw;
   rw.init(l32, h);
+
+  if (MODE == 0) {
+    // Key maxima: the product with the operands swapped, C[row][feature],
+    // so a lane holds 16 rows of one feature and the maximum over the rows
+    // is mostly in-lane.  The row terms come through LDS (-inf for rows past
+    // the end).
+    __shared__ float s_sq[kRows];
+    s_sq[wave * 32 + l32] = row_ok ? sq2 : INFINITY;
+    __syncthreads();
+#pragma unroll
+    for (int fb = 0; fb < D / 32; ++fb) {
+      f32x16 c = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) c = mma(xf[cc], rw.read(Ws, fb, cc), c);
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, sig2 * c[i] - s_sq[wave * 32 + c_row(i, h)]);
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (h == 0) sred[wave * D + fb * 32 + l32] = m;
+    }
+    __syncthreads();
+    for (int f = tid; f < D; f += 256)
+      a.part[(size_t)blockIdx.x * D + f] =
+          fmaxf(fmaxf(sred[f], sred[D + f]), fmaxf(sred[2 * D + f], sred[3 * D + f]));
+    return;
+  }
+
+  __syncthreads();
   f32x16 acc[D / 32];
 #pragma unroll
   for (int fb = 0; fb < D / 32; ++fb) {
@@ -93,25 +122,6 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     for (int cc = 0; cc < D / 16; ++cc) acc[fb] = mma(rw.read(Ws, fb, cc), xf[cc], acc[fb]);
   }
   // feature fb*32 + c_row(i, h) of row l32 is acc[fb][i]; exponents in log2 units
-  const float sig2 = sqrtf(a.scale) * kLog2e;
-  const float sq2 = 0.5f * a.scale * ss * kLog2e;
-
-  if (MODE == 0) {
-#pragma unroll
-    for (int fb = 0; fb < D / 32; ++fb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = row_ok ? sig2 * acc[fb][i] - sq2 : -INFINITY;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-        if (l32 == 0) sred[wave * D + fb * 32 + c_row(i, h)] = v;
-      }
-    __syncthreads();
-    for (int f = tid; f < D; f += 256)
-      a.part[(size_t)blockIdx.x * D + f] =
-          fmaxf(fmaxf(sred[f], sred[D + f]), fmaxf(sred[2 * D + f], sred[3 * D + f]));
-    return;
-  }
 
   float mq = 0.f;
   if (MODE >= 2) {
