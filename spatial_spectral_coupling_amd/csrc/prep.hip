@@ -406,18 +406,44 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
   return U + R * m;
 }
 
+// Entries e0 .. e1 - 1 of the selection (one chunk of target patches): a
+// thread takes e0 + tid + r kPlanThreads.  The first kChunkRegs of them are
+// kept in registers across the phases of a chunk (every one when
+// s <= kChunkRegs kPlanThreads / kPlanRows); the rest are read again.
+constexpr int kChunkRegs = 2;
+
+__device__ __forceinline__ void load_chunk(const int* idx, int e0, int e1, int* qc) {
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    const int e = e0 + (int)threadIdx.x + r * kPlanThreads;
+    qc[r] = e < e1 ? idx[e] : -1;
+  }
+}
+
+template <typename F>
+__device__ __forceinline__ void for_chunk(const int* idx, int e0, int e1, const int* qc, F f) {
+#pragma unroll
+  for (int r = 0; r < kChunkRegs; ++r) {
+    const int e = e0 + (int)threadIdx.x + r * kPlanThreads;
+    if (e < e1) f(e, qc[r]);
+  }
+  for (int e = e0 + (int)threadIdx.x + kChunkRegs * kPlanThreads; e < e1; e += kPlanThreads) f(e, idx[e]);
+}
+
 // The selection is read in chunks of kPlanRows target patches: every entry
 // (p, q) of a chunk sets bit p - p0 of mask[q] (a bit already set is a
 // repeated source patch within row p).  For the inverse lists, the rank of
 // p among the chunk's patches selecting q is the number of mask bits below
 // it, so list q is filled in ascending p, chunk after chunk, with no sort.
+// Two mask arrays alternate between chunks, so the bits of one chunk are
+// cleared while the next chunk sets its own.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int lds[kPlanWaves + 1];
-  __shared__ int s_offM[kMaxPatches + 1];
+  __shared__ int s_offM[kMaxPatches + 1];  // source offsets; later the second mask array
   __shared__ unsigned s_mask[kMaxPatches];
   __shared__ int s_cur[kMaxPatches];   // counts, then the next free slot of list q
   __shared__ int s_acc[kMaxPatches];   // target rows in list q so far
-  __shared__ int s_szN[kPlanRows], s_offN[kPlanRows];
+  __shared__ int s_szN[2][kPlanRows], s_offN[2][kPlanRows];
   const int tid = threadIdx.x;
   const int P_N = a.P_N, P_M = a.P_M, S = a.s;
   const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
@@ -439,35 +465,69 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   }
   bad = __syncthreads_or(bad);
-  // ---- selection: range, repeats within a row, list lengths
+  const int nC = (P_N + kPlanRows - 1) / kPlanRows;  // selection chunks
+  auto chunk_end = [&](int c) { return min((c + 1) * kPlanRows, P_N) * S; };
+  // ---- selection: range and list lengths.  Repeats within a row: here by
+  // the chunk masks, or, with inverse lists, in their pass (which builds the
+  // same masks) before anything is published.
   if (!bad && a.idx != nullptr) {
-    for (int p0 = 0; p0 < P_N; p0 += kPlanRows) {
-      const int e0 = p0 * S, e1 = min(p0 + kPlanRows, P_N) * S;
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
-        const int q = a.idx[e];
-        if (q < 0 || q >= P_M) {
-          bad = 1;
-          continue;
+    if (inverse) {
+      const int nE = P_N * S;
+      for (int e = tid; e < nE; e += 4 * kPlanThreads) {
+        int qv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qv[r] = e + r * kPlanThreads < nE ? a.idx[e + r * kPlanThreads] : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = qv[r];
+          if (e + r * kPlanThreads >= nE) continue;
+          if (q < 0 || q >= P_M) bad = 1;
+          else atomicAdd(&s_cur[q], 1);
         }
-        const unsigned bit = 1u << (e / S - p0);
-        if (atomicOr(&s_mask[q], bit) & bit) bad = 1;
-        if (inverse) atomicAdd(&s_cur[q], 1);
       }
-      __syncthreads();
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
-        const int q = a.idx[e];
-        if (q >= 0 && q < P_M) s_mask[q] = 0u;
+    } else {
+      // s_cur is not needed without inverse lists: the second mask array
+      unsigned* const buf0 = s_mask;
+      unsigned* const buf1 = reinterpret_cast<unsigned*>(s_cur);
+      int qc[kChunkRegs], qp[kChunkRegs], qn[kChunkRegs];
+      load_chunk(a.idx, 0, chunk_end(0), qc);
+      for (int c = 0; c < nC; ++c) {
+        const int p0 = c * kPlanRows, e0 = p0 * S, e1 = chunk_end(c);
+        if (c + 1 < nC) load_chunk(a.idx, e1, chunk_end(c + 1), qn);
+        unsigned* cur = (c & 1) ? buf1 : buf0;
+        for_chunk(a.idx, e0, e1, qc, [&](int e, int q) {
+          if (q < 0 || q >= P_M) {
+            bad = 1;
+            return;
+          }
+          const unsigned bit = 1u << (e / S - p0);
+          if (atomicOr(&cur[q], bit) & bit) bad = 1;
+        });
+        if (c > 0) {
+          unsigned* prev = (c & 1) ? buf0 : buf1;
+          for_chunk(a.idx, e0 - kPlanRows * S, e0, qp, [&](int, int q) {
+            if (q >= 0 && q < P_M) prev[q] = 0u;
+          });
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kChunkRegs; ++r) {
+          qp[r] = qc[r];
+          qc[r] = qn[r];
+        }
       }
-      __syncthreads();
     }
   }
-  bad = __syncthreads_or(bad);
-  if (bad) {
+  auto fail = [&]() {
     if (tid == 0) {
       a.counters[0] = a.counters[1] = a.counters[2] = a.counters[3] = 0;
       a.counters[5] = a.counters[6] = 0;  // no split items either: the merge passes idle
       a.counters[4] = 1;
     }
+  };
+  bad = __syncthreads_or(bad);
+  if (bad) {
+    fail();
     return;
   }
   // ---- padded offsets
@@ -498,44 +558,93 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // ascending, and their run tables
   if (inverse) {
     block_scan_excl(P_M, [&](int q) { return s_cur[q]; }, a.inv_off, lds);
-    for (int q = tid; q < P_M; q += kPlanThreads) s_cur[q] = a.inv_off[q];
+    // a repeat within a row stops the pass before its chunk is placed (two
+    // copies of an entry would advance their list twice)
+    __shared__ int s_rep;
+    if (tid == 0) s_rep = 0;
+    for (int q = tid; q < P_M; q += kPlanThreads) {
+      s_cur[q] = a.inv_off[q];
+      s_offM[q] = 0;
+    }
     __syncthreads();
-    for (int p0 = 0; p0 < P_N; p0 += kPlanRows) {
-      const int e0 = p0 * S, e1 = min(p0 + kPlanRows, P_N) * S;
-      if (tid < kPlanRows && p0 + tid < P_N) {
-        const int o = offN[p0 + tid];
-        s_offN[tid] = o;
-        s_szN[tid] = offN[p0 + tid + 1] - o;
+    // Chunk c: phase A sets its bits in mask array c & 1 (a bit already set is a
+    // repeat) and advances the lists by chunk c - 1; phase B places its
+    // entries and clears the bits of chunk c - 1.
+    unsigned* const buf0 = s_mask;
+    unsigned* const buf1 = reinterpret_cast<unsigned*>(s_offM);
+    int qc[kChunkRegs], qp[kChunkRegs], qn[kChunkRegs];
+    load_chunk(a.idx, 0, chunk_end(0), qc);
+    int o_lo = 0, o_hi = 0;  // offN[p0 + tid], offN[p0 + tid + 1] of the next chunk
+    if (tid < kPlanRows && tid < P_N) {
+      o_lo = offN[tid];
+      o_hi = offN[tid + 1];
+    }
+    for (int c = 0; c < nC; ++c) {
+      const int p0 = c * kPlanRows, e0 = p0 * S, e1 = chunk_end(c), cb = c & 1;
+      const int* szN = s_szN[cb];
+      const int* sofN = s_offN[cb];
+      // phase A
+      if (tid < kPlanRows) {
+        s_offN[cb][tid] = o_lo;
+        s_szN[cb][tid] = o_hi - o_lo;
       }
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) atomicOr(&s_mask[a.idx[e]], 1u << (e / S - p0));
+      if (c + 1 < nC) {
+        load_chunk(a.idx, e1, chunk_end(c + 1), qn);
+        if (tid < kPlanRows && p0 + kPlanRows + tid < P_N) {
+          o_lo = offN[p0 + kPlanRows + tid];
+          o_hi = offN[p0 + kPlanRows + tid + 1];
+        }
+      }
+      if (c > 0) {
+        // the last patch of chunk c - 1 selecting q advances list q
+        const unsigned* prev = cb ? buf0 : buf1;
+        const int* szP = s_szN[cb ^ 1];
+        for_chunk(a.idx, e0 - kPlanRows * S, e0, qp, [&](int e, int q) {
+          const int j = e / S - (p0 - kPlanRows);
+          const unsigned m = prev[q];
+          if (31 - __clz(m) == j) {
+            int add = 0;
+            for (unsigned b = m; b; b &= b - 1u) add += szP[__ffs(b) - 1];
+            s_cur[q] += __popc(m);
+            s_acc[q] += add;
+          }
+        });
+      }
+      unsigned* cur = cb ? buf1 : buf0;
+      for_chunk(a.idx, e0, e1, qc, [&](int e, int q) {
+        const unsigned bit = 1u << (e / S - p0);
+        if (atomicOr(&cur[q], bit) & bit) s_rep = 1;
+      });
       __syncthreads();
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
-        const int q = a.idx[e], j = e / S - p0;
-        unsigned below = s_mask[q] & ((1u << j) - 1u);
+      if (s_rep) break;
+      // phase B
+      for_chunk(a.idx, e0, e1, qc, [&](int e, int q) {
+        const int j = e / S - p0;
+        unsigned below = cur[q] & ((1u << j) - 1u);
         const int slot = s_cur[q] + __popc(below);
         int pre = s_acc[q];
         while (below) {
-          pre += s_szN[__ffs(below) - 1];
+          pre += szN[__ffs(below) - 1];
           below &= below - 1u;
         }
         a.inv_idx[slot] = p0 + j;
-        if (a.inv_tab != nullptr) a.inv_tab[slot] = RunEntry{pre + s_szN[j], s_offN[j] - pre};
+        if (a.inv_tab != nullptr) a.inv_tab[slot] = RunEntry{pre + szN[j], sofN[j] - pre};
+      });
+      if (c > 0) {
+        unsigned* prev = cb ? buf0 : buf1;
+        for_chunk(a.idx, e0 - kPlanRows * S, e0, qp, [&](int, int q) { prev[q] = 0u; });
       }
       __syncthreads();
-      // the chunk's last patch selecting q advances list q
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) {
-        const int q = a.idx[e], j = e / S - p0;
-        const unsigned m = s_mask[q];
-        if (31 - __clz(m) == j) {
-          int add = 0;
-          for (unsigned b = m; b; b &= b - 1u) add += s_szN[__ffs(b) - 1];
-          s_cur[q] += __popc(m);
-          s_acc[q] += add;
-        }
+#pragma unroll
+      for (int r = 0; r < kChunkRegs; ++r) {
+        qp[r] = qc[r];
+        qc[r] = qn[r];
       }
-      __syncthreads();
-      for (int e = e0 + tid; e < e1; e += kPlanThreads) s_mask[a.idx[e]] = 0u;
-      __syncthreads();
+    }
+    // a repeated entry: nothing is published
+    if (s_rep) {
+      fail();
+      return;
     }
   }
   // ---- work items (row blocks of rowsQ / rowsK rows within a patch)

@@ -66,6 +66,10 @@ GEO_SHAPES = [
     ("bf16", 300, 260, 128, 200, 5, 5, 5),   # s = P_M
     ("bf16", 90, 300, 128, 100, 4, 25, 1),
     ("f32", 500, 520, 64, 30, 6, 8, 3),
+    # 70 target patches: three chunks of the planner's selection passes, the
+    # last one partial; s = 66 puts more entries in a chunk than its threads
+    # keep in registers
+    ("bf16", 700, 720, 64, 30, 70, 72, 66),
 ]
 
 
@@ -207,3 +211,42 @@ def test_geo_workload_160k_sampled():
     _, _, _, _, (_, dKm, dVm) = gpu_geo(dev, s, sc, idx=idx, dO=dOm)
     check_grads((unsort(dQ.cpu().numpy(), permN)[rows], unsort(dKm.cpu().numpy(), permM),
                  unsort(dVm.cpu().numpy(), permM)), (gr[0][rows], gr[1], gr[2]), "160k restricted")
+
+
+def test_geo_repeat_in_later_chunk_computes_nothing():
+    """A repeated entry in row 40 (the planner's second chunk of 32 target
+    patches): forward and backward compute nothing and leave every output
+    untouched; the valid selection still works afterwards."""
+    import ctypes
+    say("geo repeat in a later chunk")
+    c = gen.make_small(700, 720, 64, 30, "bf16", seed=8, P_N=70, P_M=72, s=4)
+    dev, permN, permM, P_N, P_M = sorted_problem(c)
+    sc = c["scale"]
+    idx, _, O, lse, g = gpu_geo(dev, 4, sc)
+    bad = idx.clone()
+    bad[40, 3] = bad[40, 0]
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L = ssc.lib()
+    O7 = torch.full_like(O, 7.0)
+    lse7 = torch.full_like(lse, 7.0)
+    ws = torch.empty((ssc.workspace_bytes(ssc.OP_GEO_FWD, torch.bfloat16, 700, 720, 64, 30, P_N, P_M, 4),),
+                     dtype=torch.uint8, device="cuda")
+    r = L.coupling_geo_fwd(1, 64, 30, 700, P_N, p(dev["offN"]), 720, P_M, p(dev["offM"]), 4, p(bad),
+                           p(dev["Q"]), p(dev["K"]), p(dev["V"]), ctypes.c_float(sc), p(O7), p(lse7), p(ws),
+                           ctypes.c_size_t(ws.numel()), st)
+    outs = [torch.full_like(x, 7.0) for x in g]
+    wsb = torch.empty((ssc.workspace_bytes(ssc.OP_GEO_BWD, torch.bfloat16, 700, 720, 64, 30, P_N, P_M, 4),),
+                      dtype=torch.uint8, device="cuda")
+    rb = L.coupling_geo_bwd(1, 64, 30, 700, P_N, p(dev["offN"]), 720, P_M, p(dev["offM"]), 4, p(bad),
+                            p(dev["Q"]), p(dev["K"]), p(dev["V"]), ctypes.c_float(sc), p(O), p(dev["dO"]), p(lse),
+                            p(outs[0]), p(outs[1]), p(outs[2]), p(wsb), ctypes.c_size_t(wsb.numel()), st)
+    torch.cuda.synchronize()
+    assert r == 0 and rb == 0
+    assert torch.all(O7 == 7.0) and torch.all(lse7 == 7.0)
+    for x in outs:
+        assert torch.all(x == 7.0)
+    _, _, O2, lse2, g2 = gpu_geo(dev, 4, sc, idx=idx)
+    assert torch.equal(O2, O) and torch.equal(lse2, lse)
+    for a, b in zip(g2, g):
+        assert torch.equal(a, b)
