@@ -311,32 +311,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   dkv_store<D, KP>(a, krow, key_ok, h, dk, dv);
 }
 
-// Merge of the parts of split items: dK = scale * sum, dV = sum (part order).
+// Merge of the parts of split items: dK = scale * sum, dV = sum (part order),
+// one workgroup per 32-column block (D/32 of dK, then KP/32 of dV).
 template <int D, int KP, int NW>
 __global__ __launch_bounds__(NW * 64) void dkv_merge_bf16(DkvArgs a) {
-  if ((int)blockIdx.x >= *a.n_split) return;
-  const SplitItem sp = a.split[blockIdx.x];
+  constexpr int NK = D / 32, NB = NK + KP / 32;
+  const int item = blockIdx.x / NB, blk = blockIdx.x - item * NB;
+  if (item >= *a.n_split) return;
+  const SplitItem sp = a.split[item];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int krow = a.offM[sp.patch] + sp.row0 + wave * 32 + l32;
   const bool key_ok = krow < a.offM[sp.patch + 1];
-  constexpr int F = (D / 32 + KP / 32) * 16, T = NW * 64;
-  const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  constexpr int F = NB * 16, T = NW * 64;
+  const float* in = a.part + (size_t)sp.slot0 * F * T + (size_t)blk * 16 * T + tid;
   // all loads of a part are issued before its sums
-  float sum[F];
-  static_for<F>([&](auto f) { sum[f] = 0.f; });
+  float sum[16];
+  static_for<16>([&](auto f) { sum[f] = 0.f; });
   for (int q = 0; q < sp.nparts; ++q) {
     const float* pq = in + (size_t)q * F * T;
-    float v[F];
-    static_for<F>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
-    static_for<F>([&](auto f) { sum[f] += v[f]; });
+    float v[16];
+    static_for<16>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
+    static_for<16>([&](auto f) { sum[f] += v[f]; });
   }
-  f32x16 dk[D / 32], dv[KP / 32];
-  static_for<F>([&](auto fc) {
-    constexpr int f = fc, NK = (D / 32) * 16;
-    if constexpr (f < NK) dk[f / 16][f % 16] = sum[f];
-    else dv[(f - NK) / 16][(f - NK) % 16] = sum[f];
-  });
-  dkv_store<D, KP>(a, krow, key_ok, h, dk, dv);
+  if (!key_ok) return;
+  if (blk < NK) {
+    float* okr = a.dK + (size_t)krow * D;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = blk * 32 + 8 * g + 4 * h;
+      *reinterpret_cast<f32x4*>(okr + c) =
+          f32x4{a.scale * sum[4 * g], a.scale * sum[4 * g + 1], a.scale * sum[4 * g + 2], a.scale * sum[4 * g + 3]};
+    }
+    return;
+  }
+  float* ovr = a.dV + (size_t)krow * a.k;
+  const bool vec = (a.k & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int c = (blk - NK) * 32 + 8 * g + 4 * h;
+    if (vec) {
+      if (c < a.k) *reinterpret_cast<f32x4*>(ovr + c) = f32x4{sum[4 * g], sum[4 * g + 1], sum[4 * g + 2], sum[4 * g + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < a.k) ovr[c + e] = sum[4 * g + e];
+    }
+  }
 }
 
 }  // namespace tb
@@ -384,7 +404,8 @@ hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid,
 hipError_t launch_dkv_merge_bf16(int D, int KP, const DkvArgs& a, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                                      \
   if (D == DD && KP == KK) {                                                                               \
-    hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK>), dim3(kRoundCUs), dim3(kWavesK * 64), 0, st, a); \
+    hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK>), dim3(kRoundCUs * (DD / 32 + KK / 32)),            \
+                       dim3(kWavesK * 64), 0, st, a);                                                       \
     return hipGetLastError();                                                                              \
   }
   SSC_BF16_INSTANCES(SSC_L)

@@ -388,8 +388,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   fwd_store<KP, ONES>(a, row, row_ok, h, acc, l_run, m_run);
 }
 
-// Merge of the parts of split items (one workgroup per split item, the
-// producer's thread layout).  A part's sums are relative to its own
+// Merge of the parts of split items (one workgroup per split item and
+// 32-column block of O, the producer's thread layout).  A part's sums are relative to its own
 // reference m_q (the bound, or a running maximum where that part fell back),
 // so the parts are combined at the reference of the largest part mass,
 // M = max_q (m_q + log2 l_q): acc = sum_q 2^(m_q - M) acc_q, where every
@@ -397,12 +397,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 // below 2^-126 of the largest.
 template <int D, int KP, int NW, bool ONES>
 __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
-  if ((int)blockIdx.x >= *a.n_split) return;
-  const SplitItem sp = a.split[blockIdx.x];
+  // every block recomputes the rows' common reference, weights and row sums
+  // with the same operations in the same order (so the blocks agree bit for
+  // bit); block 0 writes lse
+  constexpr int NB = KP / 32;
+  const int item = blockIdx.x / NB, cb = blockIdx.x - item * NB;
+  if (item >= *a.n_split) return;
+  const SplitItem sp = a.split[item];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int row = a.offN[sp.patch] + sp.row0 + wave * 32 + l32;
   const bool row_ok = row < a.offN[sp.patch + 1];
-  constexpr int F = (KP / 32) * 16 + 2, T = NW * 64;
+  constexpr int F = NB * 16 + 2, T = NW * 64;
   const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
   // row sum of part q (both halves of the row); with ONES, column k of O is
   // field (k/32) 16 + 4 ((k%32)/8) + k%4 of the lanes of half ((k%32)/4) % 2
@@ -417,20 +422,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
     const float lq = part_l(pq);
     if (lq > 0.f) m = fmaxf(m, pq[(F - 2) * T] + log2f(lq));
   }
-  f32x16 acc[KP / 32];
-#pragma unroll
-  for (int cb = 0; cb < KP / 32; ++cb) acc[cb] = f32x16{};
-  float l = 0.f;
+  float acc[16];
+  static_for<16>([&](auto i) { acc[i] = 0.f; });
+  float l = 0.f;  // this half's row sum (with ONES: column k, on its half only)
   for (int q = 0; q < sp.nparts; ++q) {
     const float* pq = in + (size_t)q * F * T;
     const float w = part_l(pq) > 0.f ? fexp2(pq[(F - 2) * T] - m) : 0.f;
-    static_for<(KP / 32) * 16>([&](auto f) {
-      constexpr int cb = f / 16, i = f % 16;
-      acc[cb][i] = fmaf(w, pq[f * T], acc[cb][i]);
-    });
-    l = fmaf(w, pq[(F - 1) * T], l);
+    static_for<16>([&](auto i) { acc[i] = fmaf(w, pq[(cb * 16 + i) * T], acc[i]); });
+    l = fmaf(w, ONES ? (h == hk ? pq[(size_t)fk * T] : 0.f) : pq[(F - 1) * T], l);
   }
-  fwd_store<KP, ONES>(a, row, row_ok, h, acc, l, m);
+  const float l_tot = l + xor32(l);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!row_ok) return;
+  float* Orow = a.O + (size_t)row * a.k;
+  const bool vec = (a.k & 3) == 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int c = cb * 32 + 8 * g + 4 * h;
+    if (vec) {
+      if (c < a.k)
+        *reinterpret_cast<f32x4*>(Orow + c) =
+            f32x4{acc[4 * g] * inv, acc[4 * g + 1] * inv, acc[4 * g + 2] * inv, acc[4 * g + 3] * inv};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < a.k) Orow[c + e] = acc[4 * g + e] * inv;
+    }
+  }
+  if (cb == 0 && h == 0) a.lse[row] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -725,28 +744,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 }
 
 // Merge of the parts of split items: dQ = scale * (sum of the parts, in part
-// order).
+// order), one workgroup per split item and 32-column block.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_merge_bf16(DqArgs a) {
-  if ((int)blockIdx.x >= *a.n_split) return;
-  const SplitItem sp = a.split[blockIdx.x];
+  constexpr int NB = D / 32;
+  const int item = blockIdx.x / NB, db = blockIdx.x - item * NB;
+  if (item >= *a.n_split) return;
+  const SplitItem sp = a.split[item];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int row = a.offN[sp.patch] + sp.row0 + wave * 32 + l32;
   const bool row_ok = row < a.offN[sp.patch + 1];
-  constexpr int F = (D / 32) * 16, T = NW * 64;
-  const float* in = a.part + (size_t)sp.slot0 * F * T + tid;
+  constexpr int F = NB * 16, T = NW * 64;
+  const float* in = a.part + (size_t)sp.slot0 * F * T + (size_t)db * 16 * T + tid;
   // all loads of a part are issued before its sums
-  float sum[F];
-  static_for<F>([&](auto f) { sum[f] = 0.f; });
+  float sum[16];
+  static_for<16>([&](auto f) { sum[f] = 0.f; });
   for (int q = 0; q < sp.nparts; ++q) {
     const float* pq = in + (size_t)q * F * T;
-    float v[F];
-    static_for<F>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
-    static_for<F>([&](auto f) { sum[f] += v[f]; });
+    float v[16];
+    static_for<16>([&](auto f) { v[f] = __builtin_nontemporal_load(pq + f * T); });
+    static_for<16>([&](auto f) { sum[f] += v[f]; });
   }
-  f32x16 dq[D / 32];
-  static_for<F>([&](auto f) { dq[f / 16][f % 16] = sum[f]; });
-  dq_store<D>(a, row, row_ok, h, dq);
+  if (!row_ok) return;
+  float* out = a.dQ + (size_t)row * D;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int c = db * 32 + 8 * g + 4 * h;
+    *reinterpret_cast<f32x4*>(out + c) =
+        f32x4{a.scale * sum[4 * g], a.scale * sum[4 * g + 1], a.scale * sum[4 * g + 2], a.scale * sum[4 * g + 3]};
+  }
 }
 
 }  // namespace tb
@@ -822,9 +848,11 @@ hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hip
 #define SSC_L(DD, KK)                                                                                          \
   if (D == DD && KP == KK) {                                                                                   \
     if (ones)                                                                                                  \
-      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, true>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a); \
+      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, true>), dim3(kRoundCUs * (KK / 32)), dim3(kWavesQ * 64), \
+                         0, st, a);                                                                                \
     else                                                                                                       \
-      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, false>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a); \
+      hipLaunchKernelGGL((tb::fwd_merge_bf16<DD, KK, kWavesQ, false>), dim3(kRoundCUs * (KK / 32)),             \
+                         dim3(kWavesQ * 64), 0, st, a);                                                        \
     return hipGetLastError();                                                                                  \
   }
   SSC_BF16_INSTANCES(SSC_L)
@@ -833,8 +861,10 @@ hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hip
 }
 
 hipError_t launch_dq_merge_bf16(int D, const DqArgs& a, hipStream_t st) {
-  if (D == 128) hipLaunchKernelGGL((tb::dq_merge_bf16<128, kWavesQ>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a);
-  else if (D == 64) hipLaunchKernelGGL((tb::dq_merge_bf16<64, kWavesQ>), dim3(kRoundCUs), dim3(kWavesQ * 64), 0, st, a);
+  if (D == 128)
+    hipLaunchKernelGGL((tb::dq_merge_bf16<128, kWavesQ>), dim3(kRoundCUs * 4), dim3(kWavesQ * 64), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL((tb::dq_merge_bf16<64, kWavesQ>), dim3(kRoundCUs * 2), dim3(kWavesQ * 64), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
