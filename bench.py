@@ -23,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -131,8 +132,36 @@ def time_steps(fns, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     phase = [sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) / steps for j in range(len(fns))]
-    total = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
+    per_step = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
+    total = sum(per_step) / steps
+    time_steps.per_step = per_step
     return phase, total, wall
+
+
+def step_stats(xs):
+    """Median, mean and nearest-rank 10th / 90th percentiles of per-step ms."""
+    a = sorted(xs)
+    n = len(a)
+    rank = lambda q: a[min(n - 1, max(0, math.ceil(q * n) - 1))]
+    med = a[n // 2] if n % 2 else 0.5 * (a[n // 2 - 1] + a[n // 2])
+    return {"median": round(med, 4), "mean": round(sum(a) / n, 4), "p10": round(rank(0.1), 4),
+            "p90": round(rank(0.9), 4), "n": n}
+
+
+def gpu_clocks():
+    """Current shader and memory clock of card 0 as rocm-smi reports them (None
+    when rocm-smi is not available)."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = json.loads(out.stdout).get("card0", {})
+        def pick(key):
+            keys = [k for k in card if key in k.lower()]
+            keys.sort(key=lambda k: "speed" not in k.lower())  # the speed entry before the level index
+            return card[keys[0]] if keys else None
+
+        return {"sclk": pick("sclk"), "mclk": pick("mclk"), "when": "right after the timed steps"}
+    except Exception:
+        return None
 
 
 KERNEL_SOURCES = ("spatial_spectral_coupling_amd/csrc/attn_bf16_kv.hip", "spatial_spectral_coupling_amd/csrc/tile_bf16.hpp",
@@ -274,6 +303,8 @@ def main():
     with ssc.KernelTimer("dkv", capacity=args.steps + 4) as kt:
         phase, total_ms, wall_ms = time_steps(fns, args.steps, 0, torch)
         dkv_ms, dkv_n = kt.read()
+    steps_ms = step_stats(time_steps.per_step)
+    clocks = gpu_clocks()
     peak_gib = torch.cuda.max_memory_allocated() / 2 ** 30
     dkv_avg = dkv_ms / max(dkv_n, 1)
     pairs_dense = float(n) * n
@@ -417,6 +448,7 @@ def main():
                                 f"n_N=n_M={n}, d={d}, k={k}, bf16 in / fp32 accumulate"),
                    "n": n, "d": d, "k": k, "P": c["P"], "s": s},
         "peak_gib": round(peak_gib, 3), "peak_gib_above_inputs": round(peak_gib - base_mem / 2 ** 30, 3),
+        "step_ms": steps_ms, "clocks": clocks,
         **rec,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -45,3 +45,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_step_stats_percentiles():
+    # nearest-rank percentiles and the median of per-step times, against a
+    # hand count: 10 values 1..10 -> p10 = 1, p90 = 9, median 5.5, mean 5.5
+    st = bench.step_stats([7.0, 3.0, 10.0, 1.0, 5.0, 9.0, 2.0, 8.0, 4.0, 6.0])
+    assert st == {"median": 5.5, "mean": 5.5, "p10": 1.0, "p90": 9.0, "n": 10}
+    st = bench.step_stats([2.0, 1.0, 3.0])
+    assert st["median"] == 2.0 and st["p10"] == 1.0 and st["p90"] == 3.0
