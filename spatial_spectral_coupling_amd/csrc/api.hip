@@ -120,7 +120,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     L.itemsQ = take(((size_t)(n_N + rQ - 1) / rQ + P_N + kRoundCUs) * sizeof(Item));
     L.itemsK = take(((size_t)(n_M + rK - 1) / rK + P_M + kRoundCUs) * sizeof(Item));
     L.counters = take(8 * 4);
-    L.scratch = take(3 * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.scratch = take((op == SSC_OP_GEO_BWD ? 6 : 3) * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
     L.splitQ = take(kRoundCUs * sizeof(SplitItem));
     L.splitK = take(kRoundCUs * sizeof(SplitItem));
     // partial sums of split items: kRoundCUs parts x 256 threads x fields
@@ -185,7 +185,7 @@ Layout make_layout(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k, int P
     L.itemsQ = take(((size_t)(n_N + kRowsPerWG - 1) / kRowsPerWG + P_N) * sizeof(Item));
     L.itemsK = take(((size_t)(n_M + kRowsPerWG - 1) / kRowsPerWG + P_M) * sizeof(Item));
     L.counters = take(8 * 4);
-    L.scratch = take(3 * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
+    L.scratch = take((op == SSC_OP_GEO_BWD ? 6 : 3) * ((size_t)(P_N > P_M ? P_N : P_M) + 1) * 4);
     if (op == SSC_OP_GEO_BWD) {
       L.inv_off = take(((size_t)P_M + 1) * 4);
       L.inv_idx = take((size_t)P_N * s * 4);

@@ -172,7 +172,7 @@ struct PlanArgs {
   SplitItem* splitK;    // [kRoundCUs] or nullptr
   int* inv_off;         // [P_M + 1] or nullptr
   int* inv_idx;         // [P_N * s]
-  int* scratch;         // [3 (max(P_N, P_M) + 1)] counters for scans and fills
+  int* scratch;         // [3 (max(P_N, P_M) + 1)] per workgroup (two with inverse lists): scans
   int rowsQ, rowsK;     // rows per work item (target, source side)
   RunEntry* run_tab;    // [P_N * s] or nullptr: source runs of each target patch
   RunEntry* inv_tab;    // [P_N * s] or nullptr: target runs of each source patch

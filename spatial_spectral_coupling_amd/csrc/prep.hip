@@ -447,6 +447,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int tid = threadIdx.x;
   const int P_N = a.P_N, P_M = a.P_M, S = a.s;
   const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
+  // With inverse lists the plan runs as two workgroups: role 0 builds the
+  // target side (selection check, padded offsets, run tables, target items),
+  // role 1 the source side (list lengths, inverse lists, source items).  Both
+  // check the same inputs the same way, so they reach the same verdict; each
+  // writes only its own outputs.  Without inverse lists one workgroup (role
+  // 0) does everything.
+  const int role = inverse ? (int)blockIdx.x : 0;
+  const int* offN = a.offN;
+  const int* offM = a.offM;
   // ---- offsets: validation, source offsets into LDS
   int bad = 0;
   if (tid == 0) {
@@ -467,11 +476,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   bad = __syncthreads_or(bad);
   const int nC = (P_N + kPlanRows - 1) / kPlanRows;  // selection chunks
   auto chunk_end = [&](int c) { return min((c + 1) * kPlanRows, P_N) * S; };
-  // ---- selection: range and list lengths.  Repeats within a row: here by
-  // the chunk masks, or, with inverse lists, in their pass (which builds the
-  // same masks) before anything is published.
+  // ---- selection: range (both roles), list lengths (role 1) and repeats
+  // within a row: role 0 here by the chunk masks, role 1 in its inverse
+  // pass (which builds the same masks) before anything is published.
   if (!bad && a.idx != nullptr) {
-    if (inverse) {
+    if (role == 1) {
       const int nE = P_N * S;
       for (int e = tid; e < nE; e += 4 * kPlanThreads) {
         int qv[4];
@@ -486,7 +495,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
       }
     } else {
-      // s_cur is not needed without inverse lists: the second mask array
+      // s_cur is not needed on the target side: the second mask array
       unsigned* const buf0 = s_mask;
       unsigned* const buf1 = reinterpret_cast<unsigned*>(s_cur);
       int qc[kChunkRegs], qp[kChunkRegs], qn[kChunkRegs];
@@ -531,15 +540,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     return;
   }
   // ---- padded offsets
-  const int* offN = a.offN;
-  const int* offM = a.offM;
-  const int gN = block_scan_excl(P_N, [=](int p) { return (offN[p + 1] - offN[p] + kGroup - 1) & ~(kGroup - 1); },
-                                 a.poffN, lds);
-  const int gM = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + kGroup - 1) & ~(kGroup - 1); },
-                                 a.poffM, lds);
+  int gN = 0, gM = 0;
+  if (role == 0) {
+    gN = block_scan_excl(P_N, [=](int p) { return (offN[p + 1] - offN[p] + kGroup - 1) & ~(kGroup - 1); }, a.poffN,
+                         lds);
+    gM = block_scan_excl(P_M, [&](int q) { return (s_offM[q + 1] - s_offM[q] + kGroup - 1) & ~(kGroup - 1); },
+                         a.poffM, lds);
+  }
   // ---- per target patch: the run table of its key stream (the selected
   // source patches in selection order)
-  if (a.run_tab != nullptr && a.idx != nullptr) {
+  if (role == 0 && a.run_tab != nullptr && a.idx != nullptr) {
     for (int p = tid; p < P_N; p += kPlanThreads) {
       int acc = 0;
       const int* row = a.idx + (size_t)p * S;
@@ -556,7 +566,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   // ---- inverse selection lists: inv[q] = target patches p with q in idx[p],
   // ascending, and their run tables
-  if (inverse) {
+  if (role == 1) {
     block_scan_excl(P_M, [&](int q) { return s_cur[q]; }, a.inv_off, lds);
     // a repeat within a row stops the pass before its chunk is placed (two
     // copies of an entry would advance their list twice)
@@ -649,36 +659,41 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   // ---- work items (row blocks of rowsQ / rowsK rows within a patch)
   __shared__ int s_misc[2];
-  int* tmp = a.scratch;  // [3 (max(P_N, P_M) + 1)]
+  // [3 (max(P_N, P_M) + 1)] per role
+  int* tmp = a.scratch + (size_t)role * 3 * ((P_N > P_M ? P_N : P_M) + 1);
   const RunEntry* rt = a.run_tab;
   const int* io = a.inv_off;
   const RunEntry* it = a.inv_tab;
   auto tilesQ = [=](int p) { return rt != nullptr ? (rt[(size_t)p * S + S - 1].end + kTile - 1) / kTile : 0; };
   int* s_tl = reinterpret_cast<int*>(s_mask);  // free after the selection passes
-  const int nQ = make_items(P_N, offN, a.rowsQ, tilesQ, a.itemsQ, rt != nullptr ? a.splitQ : nullptr, a.counters + 5,
-                            tmp, lds, s_acc, s_misc, s_tl, s_cur);
+  const int nQ = role == 0 ? make_items(P_N, offN, a.rowsQ, tilesQ, a.itemsQ, rt != nullptr ? a.splitQ : nullptr,
+                                        a.counters + 5, tmp, lds, s_acc, s_misc, s_tl, s_cur)
+                           : 0;
   auto tilesK = [=](int q) {
     if (it == nullptr) return 0;
     const int b = io[q], e = io[q + 1];
     return e > b ? (it[e - 1].end + kTile - 1) / kTile : 0;
   };
   // source-side items drive only the dK/dV pass (a plan with inverse lists)
-  const int nK = io != nullptr || rt == nullptr
-                     ? make_items(P_M, offM, a.rowsK, tilesK, a.itemsK, it != nullptr ? a.splitK : nullptr,
-                                  a.counters + 6, tmp, lds, s_acc, s_misc, s_tl, s_cur)
-                     : 0;
-  if (io == nullptr && rt != nullptr && tid == 0) a.counters[6] = 0;
+  const bool items_k = inverse ? role == 1 : io != nullptr || rt == nullptr;
+  const int nK = items_k ? make_items(P_M, offM, a.rowsK, tilesK, a.itemsK, it != nullptr ? a.splitK : nullptr,
+                                      a.counters + 6, tmp, lds, s_acc, s_misc, s_tl, s_cur)
+                         : 0;
+  if (!inverse && io == nullptr && rt != nullptr && tid == 0) a.counters[6] = 0;
   if (tid == 0) {
-    a.counters[0] = nQ;
-    a.counters[1] = nK;
-    a.counters[2] = gN / kGroup;
-    a.counters[3] = gM / kGroup;
-    a.counters[4] = 0;
+    if (role == 0) {
+      a.counters[0] = nQ;
+      a.counters[2] = gN / kGroup;
+      a.counters[3] = gM / kGroup;
+      a.counters[4] = 0;
+    }
+    if (role == 1 || !inverse) a.counters[1] = nK;
   }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
+  hipLaunchKernelGGL(plan_kernel, dim3(inverse ? 2 : 1), dim3(kPlanThreads), 0, st, a);
   return hipGetLastError();
 }
 
