@@ -250,3 +250,33 @@ def test_geo_repeat_in_later_chunk_computes_nothing():
     assert torch.equal(O2, O) and torch.equal(lse2, lse)
     for a, b in zip(g2, g):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("P_N,P_M,s", [(9, 1301, 16), (5, 2501, 33), (7, 255, 255), (6, 3, 1)])
+def test_topk_exact_ties_break_to_lower_index(P_N, P_M, s):
+    """Every score exact and many tied: small-integer descriptors, target
+    patches of exactly 4 rows (means are exact quarters), source patches of
+    one row drawn from 40 distinct vectors.  All products and sums are exact
+    in fp64, so the order of (score desc, index asc) is the same on both
+    sides and the top-s must agree bit for bit, ties included.  P_M covers an
+    odd count, several candidates per thread, and the large-P_M kernel."""
+    d = 64
+    rng = np.random.default_rng(P_M + 7 * s)
+    Qf = rng.integers(-4, 5, size=(4 * P_N, d)).astype(np.float32)
+    pool = rng.integers(-4, 5, size=(40, d)).astype(np.float32)
+    Kf = pool[rng.integers(0, 40, size=P_M)]
+    offN = np.arange(0, 4 * P_N + 1, 4, dtype=np.int32)
+    offM = np.arange(P_M + 1, dtype=np.int32)
+    labN = np.repeat(np.arange(P_N), 4)
+    labM = np.arange(P_M)
+    Cr = patch_scores(patch_means(Qf, labN, P_N), patch_means(Kf, labM, P_M))
+    assert np.array_equal(Cr * 4, np.round(Cr * 4))  # exact quarters
+    idxr = topk(Cr, s)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    idx, C = ssc.patch_score_topk(dev(Qf), torch.from_numpy(offN).cuda(), dev(Kf), torch.from_numpy(offM).cuda(), s,
+                                  return_scores=True)
+    torch.cuda.synchronize()
+    n_ties = int(sum(len(np.unique(r)) < P_M for r in Cr))
+    say(f"top-s exact ties P_N={P_N} P_M={P_M} s={s}: rows with tied scores {n_ties}")
+    np.testing.assert_array_equal(C.cpu().numpy(), Cr)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idxr)
