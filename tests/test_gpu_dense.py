@@ -47,6 +47,10 @@ SHAPES = [
     ("bf16", 200, 150, 128, 100),
     ("bf16", 64, 96, 64, 64),
     ("bf16", 257, 16, 128, 1),
+    # padded-width boundaries: forward kp 224 / backward kp 256 (k = 223);
+    # forward with its ones column, backward without spare columns (k = 255)
+    ("bf16", 150, 170, 128, 223),
+    ("bf16", 190, 210, 64, 255),
     ("f32", 300, 517, 64, 30),
     ("f32", 150, 260, 128, 128),
 ]

@@ -66,6 +66,7 @@ GEO_SHAPES = [
     ("bf16", 300, 260, 128, 200, 5, 5, 5),   # s = P_M
     ("bf16", 90, 300, 128, 100, 4, 25, 1),
     ("f32", 500, 520, 64, 30, 6, 8, 3),
+    ("bf16", 400, 420, 64, 255, 5, 6, 2),   # forward with a ones column, backward without spare columns
     # 70 target patches: three chunks of the planner's selection passes, the
     # last one partial; s = 66 puts more entries in a chunk than its threads
     # keep in registers
