@@ -450,8 +450,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // With inverse lists the plan runs as two workgroups: role 0 builds the
   // target side (selection check, padded offsets, run tables, target items),
   // role 1 the source side (list lengths, inverse lists, source items).  Both
-  // check the same inputs the same way, so they reach the same verdict; each
-  // writes only its own outputs.  Without inverse lists one workgroup (role
+  // check the same conditions on the same inputs (offsets, entry range,
+  // repeats within a row), so they reach the same verdict; each writes only
+  // its own outputs and counters.  Without inverse lists one workgroup (role
   // 0) does everything.
   const int role = inverse ? (int)blockIdx.x : 0;
   const int* offN = a.offN;
