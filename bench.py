@@ -13,8 +13,8 @@ Prints ONE JSON line.  `value` is ms per step (lower is better); per-coupling
 ms, effective TFLOP/s against the bf16 MFMA peak and peak GiB are included,
 plus the 160k geo coupling (P = 640) as an informational sub-record, the
 roofline record of the dominant kernel (measured with HIP events on its own
-stream inside the library) and the fp64 oracle timed on the host cores on a
-bounded sample.
+stream inside the library), the small parity workloads (1k fp32, 5k bf16) and
+the fp64 oracle run once on the whole 60k step on the host cores.
 """
 
 from __future__ import annotations
@@ -89,7 +89,8 @@ def prepare(c, torch, np, gen):
     permM, offM = gen.patch_sort(c["labM"], c["P"])
     geo = dict(Q=to_dev(c["Q"][permN], dt, torch, np), K=to_dev(c["K"][permM], dt, torch, np),
                V=to_dev(c["V"][permM], dt, torch, np), dO=to_dev(c["dO"][permN], dt, torch, np),
-               offN=torch.from_numpy(offN).cuda(), offM=torch.from_numpy(offM).cuda())
+               offN=torch.from_numpy(offN).cuda(), offM=torch.from_numpy(offM).cuda(),
+               permN=torch.from_numpy(permN).cuda())
     return dense, geo, offN, offM
 
 
@@ -208,39 +209,80 @@ def copy_probe(mib: int, torch):
     log(f"copy probe: {mib} MiB read + {mib} MiB written per launch, 3 launches")
 
 
-def cpu_baseline(c, offN, offM, idx_np, np):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to ms
-    per step: dense fwd+bwd for 2048 target rows (x n_N / 2048), patch scoring
-    and top-s in full, geo fwd+bwd for 48 target patches (x P / 48)."""
-    from oracle import dense_bwd, dense_fwd, geo_bwd, geo_fwd, patch_means, patch_scores, topk, upcast
+def host_info():
+    """CPU model, usable cores and the BLAS library NumPy calls (for the
+    oracle's timing)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    threads = 1
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in infos)
     except Exception:
-        cores = 1
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": int(threads)}
+
+
+def cpu_baseline(c, offN, offM, idx_np, np):
+    """The fp64 oracle on the whole 60k step, run once on the host cores: the
+    dense coupling forward + backward on every row, patch scoring and top-s,
+    and the geo coupling forward + backward on every target patch."""
+    from oracle import dense_bwd, dense_fwd, geo_bwd, geo_fwd, patch_means, patch_scores, topk, upcast
+    info = host_info()
     dt, sc, n, P, s = c["dtype"], c["scale"], c["n"], c["P"], c["s"]
     Q, K, V, dO = (upcast(c[x], dt) for x in ("Q", "K", "V", "dO"))
-    rows = np.arange(2048)
     t0 = time.perf_counter()
-    dense_fwd(Q[rows], K, V, sc)
-    dense_bwd(Q, K, V, dO, sc, rows=rows)
-    t_dense = (time.perf_counter() - t0) * n / len(rows)
+    dense_fwd(Q, K, V, sc)
+    dense_bwd(Q, K, V, dO, sc)
+    t_dense = time.perf_counter() - t0
     t0 = time.perf_counter()
     C = patch_scores(patch_means(Q, c["labN"], P), patch_means(K, c["labM"], P))
     topk(C, s)
     t_topk = time.perf_counter() - t0
-    pats = np.arange(48)
-    labN_s = np.where(np.isin(c["labN"], pats), c["labN"], -1)
     t0 = time.perf_counter()
-    geo_fwd(Q, K, V, labN_s, c["labM"], idx_np, sc)
-    geo_bwd(Q, K, V, dO, labN_s, c["labM"], idx_np, sc)
-    t_geo = (time.perf_counter() - t0) * P / len(pats)
+    geo_fwd(Q, K, V, c["labN"], c["labM"], idx_np, sc)
+    geo_bwd(Q, K, V, dO, c["labN"], c["labM"], idx_np, sc)
+    t_geo = time.perf_counter() - t0
     total_ms = (t_dense + t_topk + t_geo) * 1e3
-    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: dense fwd+bwd on 2048 of {n} target rows (x{n / 2048:.1f}), "
-                       f"patch scores + top-s in full, geo fwd+bwd on 48 of {P} target patches "
-                       f"(x{P / 48:.1f}); ms per step extrapolated"),
-            "dense_ms": round(t_dense * 1e3, 1), "geo_ms": round((t_topk + t_geo) * 1e3, 1)}
+    return {"value": round(total_ms, 1), "unit": "ms", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": (f"the whole step, run once: fp64 NumPy oracle dense fwd+bwd on all {n} x {n} pairs, "
+                       f"patch scores + top-s, geo fwd+bwd on all {P} target patches (not extrapolated)"),
+            "dense_ms": round(t_dense * 1e3, 1), "geo_ms": round((t_topk + t_geo) * 1e3, 1), **info}
+
+
+def small_config_record(i, steps, warmup, torch, np, gen, ssc):
+    """ms per dense fwd+bwd of the small parity workloads (1k fp32, 5k bf16)."""
+    c = gen.make_config(i)
+    dt, d, k, n = c["dtype"], c["d"], c["k"], c["n"]
+    Q, K, V, dO = (to_dev(c[x], dt, torch, np) for x in ("Q", "K", "V", "dO"))
+    st = {}
+
+    def fwd():
+        st["o"] = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+
+    def bwd():
+        O, lse = st["o"]
+        ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
+
+    ph, tot, _ = time_steps([fwd, bwd], steps, warmup, torch)
+    stats = step_stats(time_steps.per_step)
+    f = algorithmic_flops(float(n) * n, d, k)
+    return {"workload": c["config"], "n": n, "d": d, "k": k, "dtype": dt, "ms": round(tot, 4),
+            "ms_median": stats["median"], "fwd_ms": round(ph[0], 4), "bwd_ms": round(ph[1], 4),
+            "tflops": round(f / tot / 1e9, 2), "algorithmic_flop": f,
+            "what": "dense coupling fwd+bwd; launch-latency bound at these sizes"}
 
 
 def main():
@@ -313,6 +355,32 @@ def main():
     rec = {"dense": {"ms": round(dense_ms, 4), "tflops": round(f_dense / dense_ms / 1e9, 1),
                      "pct_peak": round(100 * f_dense / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                      "algorithmic_flop": f_dense}}
+
+    # the dense phases apart, and the backward without dV (the basis V = Phi_M
+    # is fixed in the functional-map pipelines, so callers may skip dV)
+    st_d = {}
+
+    def d_fwd():
+        st_d["o"] = ssc.coupling_dense_fwd(dense["Q"], dense["K"], dense["V"], sc)
+
+    def d_bwd():
+        O_, lse_ = st_d["o"]
+        ssc.coupling_dense_bwd(dense["Q"], dense["K"], dense["V"], O_, dense["dO"], lse_, sc)
+
+    def d_bwd_nodv():
+        O_, lse_ = st_d["o"]
+        ssc.coupling_dense_bwd(dense["Q"], dense["K"], dense["V"], O_, dense["dO"], lse_, sc, need_dV=False)
+
+    nd_steps = max(3, args.steps // 2)
+    ph_d, _, _ = time_steps([d_fwd, d_bwd, d_bwd_nodv], nd_steps, 1, torch)
+    with ssc.KernelTimer("dkv", capacity=nd_steps + 2) as kt2:
+        for _ in range(nd_steps):
+            d_bwd_nodv()
+        dkv_nodv_ms, dkv_nodv_n = kt2.read()
+    rec["dense"].update({"fwd_ms": round(ph_d[0], 4), "bwd_ms": round(ph_d[1], 4),
+                         "bwd_no_dv_ms": round(ph_d[2], 4),
+                         "dkv_kernel_ms": round(dkv_ms / max(dkv_n, 1), 4),
+                         "dk_only_kernel_ms": round(dkv_nodv_ms / max(dkv_nodv_n, 1), 4)})
     if not args.dense_only:
         idx_np = st["idx"].cpu().numpy()
         pairs_geo = executed_pairs(offN, offM, idx_np)
@@ -326,8 +394,17 @@ def main():
                       "executed_blocks": {"tflops": round(fb_geo / phase[2] / 1e9, 1),
                                           "pct_peak": round(100 * fb_geo / phase[2] / 1e9 / PEAK_BF16_TFLOPS, 2),
                                           "flop": fb_geo, "target_side_pairs": qb, "source_side_pairs": kvb,
-                                          "what": "fwd+bwd kernels only, over 128-row items x 64-row tiles"},
+                                          "what": ("diagnostic, not the graded figure: fwd+bwd kernels only, "
+                                                   "work counted over padded 128-row items x 64-row tiles")},
                       "P": c["P"], "s": s}
+        # how far the geo coupling is from the dense one on the same tensors
+        # (informational: the pages give no error bound for the restriction)
+        O_d, _ = ssc.coupling_dense_fwd(dense["Q"], dense["K"], dense["V"], sc)
+        O_g, _ = ssc.coupling_geo_fwd(geo["Q"], geo["K"], geo["V"], geo["offN"], geo["offM"], st["idx"], sc)
+        O_go = torch.empty_like(O_g)
+        O_go[geo["permN"].long()] = O_g
+        rec["geo"]["rel_frobenius_vs_dense"] = round(float(torch.linalg.norm(O_go - O_d) / torch.linalg.norm(O_d)), 5)
+        del O_d, O_g, O_go
     achieved = dkv_flops(pairs_dense, d, k) / dkv_avg / 1e9
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
@@ -426,10 +503,16 @@ def main():
                            "executed_pairs": p4,
                            "executed_blocks": {"tflops": round(fb4 / ph4[1] / 1e9, 1),
                                                "pct_peak": round(100 * fb4 / ph4[1] / 1e9 / PEAK_BF16_TFLOPS, 2),
-                                               "flop": fb4, "target_side_pairs": qb4, "source_side_pairs": kvb4},
+                                               "flop": fb4, "target_side_pairs": qb4, "source_side_pairs": kvb4,
+                                               "what": "diagnostic, not the graded figure (padded blocks)"},
                            "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
         del geo4
         rec["fps_160k"] = fps_record(c4, c4["P"], min(args.steps, 3), 1, torch, np, gen, ssc)
+
+    if not args.dense_only:
+        log("timing the small parity workloads")
+        rec["config0_dense_1k_f32"] = small_config_record(0, args.steps, args.warmup, torch, np, gen, ssc)
+        rec["config1_dense_5k_bf16"] = small_config_record(1, args.steps, args.warmup, torch, np, gen, ssc)
 
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, torch)

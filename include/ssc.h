@@ -23,7 +23,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor arguments are DEVICE pointers to dense row-major arrays
- *   (row stride = width), 16-byte aligned.  The caller owns every buffer;
+ *   (row stride = width, no separate leading-dimension argument: the tile
+ *   loads address rows by a compile-time width), 16-byte aligned.  A strided
+ *   view must be made contiguous by the caller.  The caller owns every buffer;
  *   the library never allocates device memory.  Scratch space comes from
  *   the caller through (ws, ws_bytes); ssc_workspace_bytes() gives the size.
  * - dtype selects the storage of Q, K, V and dO: SSC_BF16 (bf16 bits,
@@ -97,12 +99,18 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
                               ssc_stream stream);
 
 /*
- * Dense backward: gradients of <dO, O> for the coupling above, recomputing
- * the softmax from lse (no map stored):
+ * Dense backward: gradients of <dO, O> for the coupling above (project page,
+ * "How it works": the pipelines train through the product Pi_NM Phi_M, so
+ * the descriptors F_N = Q and F_M = K receive gradients through it;
+ * "The bottleneck": the map is never stored), recomputing the softmax from
+ * lse:
  *   D_i = sum_c dO_ic O_ic,  dS = P * (dO V^T - D),
  *   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
  * O and lse are the forward's outputs for the same inputs.  dO [n_N x k] in
  * `dtype`; dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ * dV may be NULL: V = Phi_M is the fixed Laplace-Beltrami basis in the
+ * pages' pipelines, so its gradient is usually not needed; the dV products
+ * are then skipped (dQ and dK are the same bits as with dV).
  */
 ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
                               const void* Q, const void* K, const void* V, float scale,
@@ -132,13 +140,18 @@ ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int*
                             ssc_stream stream);
 
 /*
- * Geo forward: for every target row i of patch p, the softmax of
+ * Geo forward (project page, "Geo-FlashAttention" and its pipeline figure:
+ * a fused block-sparse kernel takes the exact softmax over the selected
+ * source patches only): for every target row i of patch p, the softmax of
  * scale * Q[i].K[j] over j in J_p = union of source patches idx[p, :]
  * (patch-sorted rows, offsets as above), and
  *   O[i] = sum_{j in J_p} softmax_j V[j],  lse[i] = log sum_{j in J_p} exp(.).
  * A row whose support is empty gets O = 0 and lse = -inf.  idx entries must
- * lie in [0, P_M) and be distinct within a row; if any idx entry or offset
- * breaks the rules, nothing is computed and O, lse are left untouched.
+ * lie in [0, P_M) and be distinct within a row, and the offsets must follow
+ * the rules above; these are checked on the device (the host cannot see
+ * them without a sync): if any entry or offset breaks them, nothing is
+ * computed, O and lse are filled with NaN and the call still returns SSC_OK
+ * (the debug build, see SSC_DEBUG below, reports SSC_ERR_INVALID_ARG).
  */
 ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN,
                             int n_M, int P_M, const int* offM, int s, const int* idx,
@@ -146,10 +159,15 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
                             float* O, float* lse, void* ws, size_t ws_bytes, ssc_stream stream);
 
 /*
- * Geo backward: gradients of <dO, O_geo> for the FIXED selection idx (the
- * selection is piecewise constant in the inputs).  Same formulas as the
- * dense backward restricted to the selected support; source rows outside
- * every support get dK = dV = 0.  Outputs are fully overwritten.
+ * Geo backward (project page, "Geo-FlashAttention": the block-sparse
+ * coupling is trained end to end like the dense one): gradients of
+ * <dO, O_geo> for the FIXED selection idx (the selection is piecewise
+ * constant in the inputs).  Same formulas as the dense backward restricted
+ * to the selected support; source rows outside every support get dK = dV =
+ * 0.  Outputs are fully overwritten; dV may be NULL (skipped, as in the
+ * dense backward).  Invalid offsets or selection entries (checked on the
+ * device, as in the geo forward) compute nothing and fill dQ, dK and dV with
+ * NaN.
  */
 ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN,
                             int n_M, int P_M, const int* offM, int s, const int* idx,
@@ -270,6 +288,18 @@ ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
  */
 ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const int* adj, int P, int* seeds,
                          int* labels, double* dist, void* ws, size_t ws_bytes, ssc_stream stream);
+
+/*
+ * Debug build.  libssc_debug.so is the same library compiled with SSC_DEBUG
+ * defined.  Its geo calls and patch_score_topk additionally wait for their
+ * stream after launching and read the device-side verdict on the
+ * preconditions the host cannot see (offsets start at 0, end at n and do not
+ * decrease; idx entries lie in [0, P_M) and are distinct within a row):
+ * a violation returns SSC_ERR_INVALID_ARG instead of SSC_OK.  Every kernel
+ * still runs to its normal end; only the host reports the flag.  It is meant
+ * for development; the synchronisation makes every such call blocking.
+ */
+int ssc_debug_build(void); /* 1 in libssc_debug.so, 0 otherwise */
 
 /* Static text for a status code. */
 const char* ssc_status_string(ssc_status status);

@@ -65,6 +65,7 @@ _SIGS = {
     "ssc_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "ssc_status_string": (ctypes.c_char_p, [_i]),
     "ssc_last_hip_error": (_i, []),
+    "ssc_debug_build": (_i, []),
     "ssc_query": (_i, [_i, _i]),
     "ssc_timer_arm": (_i, [ctypes.c_char_p, _i]),
     "ssc_timer_read": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -205,6 +206,30 @@ def _i32(t: torch.Tensor, name: str):
         raise TypeError(f"{name} must be int32")
 
 
+def _want(t: Optional[torch.Tensor], name: str, shape, dtype):
+    """Shape and dtype of a tensor the library reads or writes by raw pointer
+    (a mismatch would make a kernel read or write past the buffer)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _mat(t: torch.Tensor, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a matrix, got {t.dim()} dimensions")
+    return t.shape
+
+
+def _offsets(off: torch.Tensor, name: str) -> int:
+    _i32(off, name)
+    if off.dim() != 1 or off.numel() < 2:
+        raise ValueError(f"{name} must be a vector of P + 1 >= 2 offsets")
+    return off.numel() - 1
+
+
 # ---------------------------------------------------------------------------
 # the five entry points
 # ---------------------------------------------------------------------------
@@ -212,30 +237,41 @@ def coupling_dense_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale:
                        O: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
                        ) -> Tuple[torch.Tensor, torch.Tensor]:
     """O = softmax(Q K^T * scale) V (fp32) and lse (natural log), no map stored."""
-    dev = _check_dev(Q, K, V)
     code = _same_dtype(Q, K, V)
-    n_N, d = Q.shape
-    n_M, k = V.shape
-    if K.shape != (n_M, d):
-        raise ValueError("K must be n_M x d")
+    n_N, d = _mat(Q, "Q")
+    n_M, k = _mat(V, "V")
+    _want(K, "K", (n_M, d), Q.dtype)
+    _want(O, "O", (n_N, k), torch.float32)
+    _want(lse, "lse", (n_N,), torch.float32)
+    dev = _check_dev(Q, K, V, O, lse)
     O = torch.empty(n_N, k, dtype=torch.float32, device=dev) if O is None else O
     lse = torch.empty(n_N, dtype=torch.float32, device=dev) if lse is None else lse
-    _check_dev(O, lse)
     ws = _ws(lib().ssc_workspace_bytes(OP_DENSE_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
     _call("coupling_dense_fwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _scale(scale, d),
           _p(O), _p(lse), _p(ws), ws.numel(), _stream(dev))
     return O, lse
 
 
-def coupling_dense_bwd(Q, K, V, O, dO, lse, scale: Optional[float] = None):
-    """dQ, dK, dV (fp32) of <dO, O> for the dense coupling."""
-    dev = _check_dev(Q, K, V, O, dO, lse)
+def _check_bwd_inputs(Q, K, V, O, dO, lse):
+    n_N, d = _mat(Q, "Q")
+    n_M, k = _mat(V, "V")
+    _want(K, "K", (n_M, d), Q.dtype)
+    _want(O, "O", (n_N, k), torch.float32)
+    _want(dO, "dO", (n_N, k), Q.dtype)
+    _want(lse, "lse", (n_N,), torch.float32)
+    return n_N, n_M, d, k
+
+
+def coupling_dense_bwd(Q, K, V, O, dO, lse, scale: Optional[float] = None, need_dV: bool = True):
+    """dQ, dK, dV (fp32) of <dO, O> for the dense coupling.  With need_dV
+    False the library skips the dV products and dV is returned as None (the
+    basis V = Phi_M is fixed in the functional-map pipelines)."""
     code = _same_dtype(Q, K, V, dO)
-    n_N, d = Q.shape
-    n_M, k = V.shape
+    n_N, n_M, d, k = _check_bwd_inputs(Q, K, V, O, dO, lse)
+    dev = _check_dev(Q, K, V, O, dO, lse)
     dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
     dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
-    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev) if need_dV else None
     ws = _ws(lib().ssc_workspace_bytes(OP_DENSE_BWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
     _call("coupling_dense_bwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _scale(scale, d),
           _p(O), _p(dO), _p(lse), _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
@@ -248,13 +284,13 @@ def patch_score_topk(Q, offN, K, offM, s: int, return_scores: bool = False):
     Q, K are patch-sorted; offN, offM int32 offsets (length P + 1) on the
     device.  Returns idx [P_N x s] int32 (and scores [P_N x P_M] fp64).
     """
-    dev = _check_dev(Q, K, offN, offM)
     code = _same_dtype(Q, K)
-    _i32(offN, "offN")
-    _i32(offM, "offM")
-    n_N, d = Q.shape
-    n_M = K.shape[0]
-    P_N, P_M = offN.numel() - 1, offM.numel() - 1
+    P_N, P_M = _offsets(offN, "offN"), _offsets(offM, "offM")
+    n_N, d = _mat(Q, "Q")
+    n_M, dk = _mat(K, "K")
+    if dk != d:
+        raise ValueError("Q and K must have the same width d")
+    dev = _check_dev(Q, K, offN, offM)
     idx = torch.empty(P_N, s, dtype=torch.int32, device=dev)
     scores = torch.empty(P_N, P_M, dtype=torch.float64, device=dev) if return_scores else None
     ws = _ws(lib().ssc_workspace_bytes(OP_PATCH_TOPK, code, n_N, n_M, d, 1, P_N, P_M, s), dev)
@@ -263,17 +299,22 @@ def patch_score_topk(Q, offN, K, offM, s: int, return_scores: bool = False):
     return (idx, scores) if return_scores else idx
 
 
+def _check_selection(offN, offM, idx):
+    P_N, P_M = _offsets(offN, "offN"), _offsets(offM, "offM")
+    _i32(idx, "idx")
+    if idx.dim() != 2 or idx.shape[0] != P_N:
+        raise ValueError(f"idx must be P_N x s = {P_N} x s, got {tuple(idx.shape)}")
+    return P_N, P_M, idx.shape[1]
+
+
 def coupling_geo_fwd(Q, K, V, offN, offM, idx, scale: Optional[float] = None):
     """Geo-FlashAttention forward on patch-sorted rows: O (fp32), lse."""
-    dev = _check_dev(Q, K, V, offN, offM, idx)
     code = _same_dtype(Q, K, V)
-    _i32(offN, "offN")
-    _i32(offM, "offM")
-    _i32(idx, "idx")
-    n_N, d = Q.shape
-    n_M, k = V.shape
-    P_N, P_M = offN.numel() - 1, offM.numel() - 1
-    s = idx.shape[1]
+    n_N, d = _mat(Q, "Q")
+    n_M, k = _mat(V, "V")
+    _want(K, "K", (n_M, d), Q.dtype)
+    P_N, P_M, s = _check_selection(offN, offM, idx)
+    dev = _check_dev(Q, K, V, offN, offM, idx)
     O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
     lse = torch.empty(n_N, dtype=torch.float32, device=dev)
     ws = _ws(lib().ssc_workspace_bytes(OP_GEO_FWD, code, n_N, n_M, d, k, P_N, P_M, s), dev)
@@ -282,17 +323,16 @@ def coupling_geo_fwd(Q, K, V, offN, offM, idx, scale: Optional[float] = None):
     return O, lse
 
 
-def coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO, lse, scale: Optional[float] = None):
-    """Geo-FlashAttention backward for the fixed selection idx: dQ, dK, dV (fp32)."""
-    dev = _check_dev(Q, K, V, offN, offM, idx, O, dO, lse)
+def coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO, lse, scale: Optional[float] = None, need_dV: bool = True):
+    """Geo-FlashAttention backward for the fixed selection idx: dQ, dK, dV
+    (fp32); dV is skipped (None) with need_dV False."""
     code = _same_dtype(Q, K, V, dO)
-    n_N, d = Q.shape
-    n_M, k = V.shape
-    P_N, P_M = offN.numel() - 1, offM.numel() - 1
-    s = idx.shape[1]
+    n_N, n_M, d, k = _check_bwd_inputs(Q, K, V, O, dO, lse)
+    P_N, P_M, s = _check_selection(offN, offM, idx)
+    dev = _check_dev(Q, K, V, offN, offM, idx, O, dO, lse)
     dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
     dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
-    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
+    dV = torch.empty(n_M, k, dtype=torch.float32, device=dev) if need_dV else None
     ws = _ws(lib().ssc_workspace_bytes(OP_GEO_BWD, code, n_N, n_M, d, k, P_N, P_M, s), dev)
     _call("coupling_geo_bwd", code, d, k, n_N, P_N, _p(offN), n_M, P_M, _p(offM), s, _p(idx),
           _p(Q), _p(K), _p(V), _scale(scale, d), _p(O), _p(dO), _p(lse), _p(dQ), _p(dK), _p(dV),
@@ -314,8 +354,9 @@ class _Dense(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dO):
         Q, K, V, O, lse = ctx.saved_tensors
-        dQ, dK, dV = coupling_dense_bwd(Q, K, V, O, dO.to(Q.dtype).contiguous(), lse, ctx.scale)
-        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype), None
+        need_dV = bool(ctx.needs_input_grad[2])
+        dQ, dK, dV = coupling_dense_bwd(Q, K, V, O, dO.to(Q.dtype).contiguous(), lse, ctx.scale, need_dV=need_dV)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype) if need_dV else None, None
 
 
 class _Geo(torch.autograd.Function):
@@ -329,9 +370,10 @@ class _Geo(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dO):
         Q, K, V, offN, offM, idx, O, lse = ctx.saved_tensors
+        need_dV = bool(ctx.needs_input_grad[2])
         dQ, dK, dV = coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO.to(Q.dtype).contiguous(), lse,
-                                      ctx.scale)
-        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype), None, None, None, None
+                                      ctx.scale, need_dV=need_dV)
+        return dQ.to(Q.dtype), dK.to(K.dtype), dV.to(V.dtype) if need_dV else None, None, None, None, None
 
 
 def dense_coupling(Q, K, V, scale: Optional[float] = None):
@@ -351,12 +393,11 @@ def geo_coupling(Q, K, V, offN, offM, s: int, scale: Optional[float] = None):
 def coupling_linear_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """O = phi(Q)(phi(K)^T V) / (phi(Q) phi(K)^T 1), phi = elu + 1 (bf16 in, fp32
     out), and the per-row normaliser den."""
-    dev = _check_dev(Q, K, V)
     code = _same_dtype(Q, K, V)
-    n_N, d = Q.shape
-    n_M, k = V.shape
-    if K.shape != (n_M, d):
-        raise ValueError("K must be n_M x d")
+    n_N, d = _mat(Q, "Q")
+    n_M, k = _mat(V, "V")
+    _want(K, "K", (n_M, d), Q.dtype)
+    dev = _check_dev(Q, K, V)
     O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
     den = torch.empty(n_N, dtype=torch.float32, device=dev)
     ws = _ws(lib().ssc_workspace_bytes(OP_LINEAR_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
@@ -367,10 +408,9 @@ def coupling_linear_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor) -> Tu
 
 def coupling_linear_bwd(Q, K, V, O, dO, den):
     """dQ, dK, dV (fp32) of <dO, O> for the linear coupling."""
-    dev = _check_dev(Q, K, V, O, dO, den)
     code = _same_dtype(Q, K, V, dO)
-    n_N, d = Q.shape
-    n_M, k = V.shape
+    n_N, n_M, d, k = _check_bwd_inputs(Q, K, V, O, dO, den)
+    dev = _check_dev(Q, K, V, O, dO, den)
     dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
     dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
     dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
@@ -403,11 +443,10 @@ def fmap_solve_fwd(PhiN: torch.Tensor, O: torch.Tensor) -> torch.Tensor:
     """Least-squares functional map C = (PhiN^T PhiN)^-1 PhiN^T O (k x k,
     fp32) from the coupling's output O = Pi Phi_M (n x k fp32) and the target
     basis PhiN (n x k bf16)."""
-    dev = _check_dev(PhiN, O)
     code = _same_dtype(PhiN)
-    n, k = PhiN.shape
-    if O.shape != (n, k) or O.dtype != torch.float32:
-        raise ValueError("O must be n x k float32")
+    n, k = _mat(PhiN, "PhiN")
+    _want(O, "O", (n, k), torch.float32)
+    dev = _check_dev(PhiN, O)
     C = torch.empty(k, k, dtype=torch.float32, device=dev)
     ws = _ws(lib().ssc_workspace_bytes(OP_FMAP_FWD, code, n, 0, 0, k, 0, 0, 0), dev)
     _call("fmap_solve_fwd", code, n, k, _p(PhiN), _p(O), _p(C), _p(ws), ws.numel(), _stream(dev))
@@ -417,11 +456,10 @@ def fmap_solve_fwd(PhiN: torch.Tensor, O: torch.Tensor) -> torch.Tensor:
 def fmap_solve_bwd(PhiN: torch.Tensor, dC: torch.Tensor) -> torch.Tensor:
     """dO = PhiN (PhiN^T PhiN)^-1 dC (n x k fp32) for an upstream gradient dC
     (k x k fp32); the basis is held fixed."""
-    dev = _check_dev(PhiN, dC)
     code = _same_dtype(PhiN)
-    n, k = PhiN.shape
-    if dC.shape != (k, k) or dC.dtype != torch.float32:
-        raise ValueError("dC must be k x k float32")
+    n, k = _mat(PhiN, "PhiN")
+    _want(dC, "dC", (k, k), torch.float32)
+    dev = _check_dev(PhiN, dC)
     dO = torch.empty(n, k, dtype=torch.float32, device=dev)
     ws = _ws(lib().ssc_workspace_bytes(OP_FMAP_BWD, code, n, 0, 0, k, 0, 0, 0), dev)
     _call("fmap_solve_bwd", code, n, k, _p(PhiN), _p(dC.contiguous()), _p(dO), _p(ws), ws.numel(), _stream(dev))
@@ -470,12 +508,12 @@ def fps_partition(x: torch.Tensor, off: torch.Tensor, adj: torch.Tensor, P: int)
 def coupling_performer_fwd(Q, K, V, W, scale: Optional[float] = None):
     """Performer (FAVOR+) coupling: O = phi(Q) (phi(K)^T V) / den and ln den
     (fp32), with m = d random directions W [d x d] bf16."""
-    dev = _check_dev(Q, K, V, W)
     code = _same_dtype(Q, K, V, W)
-    n_N, d = Q.shape
-    n_M, k = V.shape
-    if K.shape != (n_M, d) or W.shape != (d, d):
-        raise ValueError("K must be n_M x d and W d x d")
+    n_N, d = _mat(Q, "Q")
+    n_M, k = _mat(V, "V")
+    _want(K, "K", (n_M, d), Q.dtype)
+    _want(W, "W", (d, d), Q.dtype)
+    dev = _check_dev(Q, K, V, W)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
     lnden = torch.empty(n_N, dtype=torch.float32, device=dev)
@@ -487,11 +525,11 @@ def coupling_performer_fwd(Q, K, V, W, scale: Optional[float] = None):
 
 def coupling_performer_bwd(Q, K, V, W, O, dO, lnden, scale: Optional[float] = None):
     """dQ, dK, dV (fp32) of <dO, O> for the Performer coupling (W fixed)."""
-    dev = _check_dev(Q, K, V, W, O, dO, lnden)
     code = _same_dtype(Q, K, V, W, dO)
-    n_N, d = Q.shape
-    n_M, k = V.shape
+    n_N, n_M, d, k = _check_bwd_inputs(Q, K, V, O, dO, lnden)
+    _want(W, "W", (d, d), Q.dtype)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dev = _check_dev(Q, K, V, W, O, dO, lnden)
     dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
     dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
     dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)

@@ -76,6 +76,9 @@ struct Layout {
   size_t run_tab = kNone, inv_tab = kNone;
   size_t knorm = kNone;  // bf16 forward: partial maxima of the key-row norms
   size_t splitQ = kNone, splitK = kNone, partQ = kNone, partK = kNone;  // bf16 geo: split items, partial sums
+  size_t flag = kNone;   // patch scoring: offsets verdict (read by the debug build)
+  size_t Vt = kNone;     // dense bf16 forward: V grouped-transposed, npadT / 16 groups of [KP][16]
+  int npadT = 0;         // positions of the transposed copies (a multiple of the 64-row tile)
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
 };
@@ -95,8 +98,12 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     off = round_up(off + bytes, 256);
     return o;
   };
+  L.npadT = (int)round_up((size_t)n_M, kTile);
   switch (op) {
     case SSC_OP_DENSE_FWD:
+      L.Vt = take((size_t)kpad_fwd_bf16(k) * L.npadT * 2);
+      L.knorm = take(kNormParts * 4);
+      break;
     case SSC_OP_GEO_FWD:
       L.Vp = take(nM * (size_t)kpad_fwd_bf16(k) * 2);
       L.knorm = take(kNormParts * 4);
@@ -111,6 +118,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     case SSC_OP_PATCH_TOPK:
       L.Qbar = take((size_t)P_N * d * 8);
       L.KbarT = take((size_t)d * P_M * 8);
+      L.flag = take(4);
       break;
   }
   if (geo) {
@@ -211,6 +219,21 @@ ssc_status hip_status(hipError_t e) {
     const hipError_t e_ = (expr);            \
     if (e_ != hipSuccess) return hip_status(e_); \
   } while (0)
+
+#ifdef SSC_DEBUG
+constexpr bool kDebug = true;
+#else
+constexpr bool kDebug = false;
+#endif
+
+// Debug build: wait for the stream and report a device-side verdict flag
+// (nonzero: a precondition the host cannot see was violated).
+ssc_status debug_verdict(const int* flag, hipStream_t s) {
+  int v = 0;
+  SSC_TRY(hipMemcpyAsync(&v, flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  SSC_TRY(hipStreamSynchronize(s));
+  return v != 0 ? SSC_ERR_INVALID_ARG : SSC_OK;
+}
 
 DType dt(ssc_dtype t) { return t == SSC_BF16 ? DType::BF16 : DType::F32; }
 
@@ -477,6 +500,8 @@ const char* ssc_status_string(ssc_status status) {
 
 int ssc_last_hip_error(void) { return g_last_hip; }
 
+int ssc_debug_build(void) { return kDebug ? 1 : 0; }
+
 int ssc_timer_arm(const char* family, int capacity) {
   KernelTimer& t = g_timer;
   for (hipEvent_t e : t.ev)
@@ -543,13 +568,12 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   if (dtype == SSC_BF16) {
     const int KPf = kpad_fwd_bf16(k);
     const bool ones = k < KPf;
-    PackArgs pv{};
-    pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
-    SSC_TRY(launch_pack(DType::BF16, pv, L.npadM / kGroup, s));
+    char* Vt = at<char>(ws, L.Vt);
+    SSC_TRY(launch_transpose_bf16(V, n_M, k, KPf, ones ? 1 : 0, Vt, L.npadT, s));
     float* knorm = at<float>(ws, L.knorm);
     SSC_TRY(launch_keynorm(K, n_M, d, knorm, s));
     FwdArgs a{};
-    a.Q = Q; a.Kp = K; a.Vp = pv.Xp; a.O = O; a.lse = lse;
+    a.Q = Q; a.Kp = K; a.Vt = Vt; a.groupsVt = L.npadT / kGroup; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M; a.knorm2 = knorm;
     const int rQ = kRowsFwd;
     SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ, s); }));
@@ -580,7 +604,7 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
                               float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
   ssc_status st = check_shape(dtype, n_N, n_M, d, k);
   if (st != SSC_OK) return st;
-  if (!all_ok({Q, K, V, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (!all_ok({Q, K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
   if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
   const Layout L = make_layout(SSC_OP_DENSE_BWD, dtype, n_N, n_M, d, k, 0, 0, 0);
@@ -616,7 +640,7 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
     b.Kp = K; b.Vp = pv.Xp; b.Qp = Q; b.dOp = po.Xp; b.lse2p = po.lse2p; b.Dp = po.Dp; b.dK = dK; b.dV = dV;
     b.n_M = n_M; b.k = k; b.c2 = c2; b.scale = scale; b.n_N = n_N;
     const int rK = kRowsDkv;
-    SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK, s); }));
+    SSC_TRY(timed("dkv", s, [&] { return launch_dkv_bf16(d, KPb, dcol, dV != nullptr, b, (n_M + rK - 1) / rK, s); }));
     return SSC_OK;
   }
 
@@ -679,6 +703,11 @@ ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int*
   ta.Qbar = pa.Qbar; ta.KbarT = pa.KbarT; ta.P_N = P_N; ta.P_M = P_M; ta.d = d; ta.s = s;
   ta.idx = idx; ta.scores = scores;
   SSC_TRY(launch_topk(ta, hs));
+  if (kDebug) {
+    int* flag = at<int>(ws, L.flag);
+    SSC_TRY(launch_check_offsets(offN, P_N, n_N, offM, P_M, n_M, flag, hs));
+    return debug_verdict(flag, hs);
+  }
   return SSC_OK;
 }
 
@@ -756,11 +785,12 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN; a.n_M = n_M;
     a.idx = idx; a.s = s; a.offM = offM; a.run_tab = at<RunEntry>(ws, L.run_tab);
     a.part = at<float>(ws, L.partQ); a.split = at<SplitItem>(ws, L.splitQ); a.n_split = counters + 5;
+    a.status = counters + 4;
     const int rQ = kRowsFwd;
     SSC_TRY(timed("geo_fwd", hs,
                   [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ + P_N + kRoundCUs, hs); }));
     SSC_TRY(launch_fwd_merge_bf16(d, KPf, ones, a, hs));
-    return SSC_OK;
+    return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
   }
 
   PackArgs pk{};
@@ -777,7 +807,8 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   a.items = at<Item>(ws, L.itemsQ); a.n_items = counters + 0; a.offN = offN;
   a.idx = idx; a.s = s; a.poffM = pk.poff; a.offM = offM;
   SSC_TRY(timed("geo_fwd", hs, [&] { return launch_fwd(T, d, KP, a, (n_N + kRowsPerWG - 1) / kRowsPerWG + P_N, hs); }));
-  return SSC_OK;
+  SSC_TRY(launch_invalid_fill(counters + 4, O, (size_t)n_N * k, lse, (size_t)n_N, nullptr, 0, hs));
+  return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
 }
 
 ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, const int* offN, int n_M, int P_M,
@@ -786,7 +817,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
                             float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
   ssc_status st = geo_common_checks(dtype, d, k, n_N, P_N, offN, n_M, P_M, offM, s, idx);
   if (st != SSC_OK) return st;
-  if (!all_ok({Q, K, V, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (!all_ok({Q, K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
   if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
   const Layout L = make_layout(SSC_OP_GEO_BWD, dtype, n_N, n_M, d, k, P_N, P_M, s);
@@ -822,6 +853,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
       q.items = at<Item>(ws, L.itemsQ); q.n_items = counters + 0; q.offN = offN; q.n_M = n_M;
       q.idx = idx; q.s = s; q.offM = offM; q.run_tab = at<RunEntry>(ws, L.run_tab);
       q.part = at<float>(ws, L.partQ); q.split = at<SplitItem>(ws, L.splitQ); q.n_split = counters + 5;
+      q.status = counters + 4;
       const int rQ = kRowsDq;
       SSC_TRY(timed("geo_dq", hs,
                     [&] { return launch_dq_bf16(d, KPb, dcol, q, (n_N + rQ - 1) / rQ + P_N + kRoundCUs, hs); }));
@@ -833,11 +865,14 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.offN = offN;
     b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.inv_tab = at<RunEntry>(ws, L.inv_tab);
     b.part = at<float>(ws, L.partK); b.split = at<SplitItem>(ws, L.splitK); b.n_split = counters + 6;
+    b.status = counters + 4;
     const int rK = kRowsDkv;
-    SSC_TRY(timed("geo_dkv", hs,
-                  [&] { return launch_dkv_bf16(d, KPb, dcol, b, (n_M + rK - 1) / rK + P_M + kRoundCUs, hs); }));
-    SSC_TRY(launch_dkv_merge_bf16(d, KPb, b, hs));
-    return SSC_OK;
+    const bool want_dv = dV != nullptr;
+    SSC_TRY(timed("geo_dkv", hs, [&] {
+      return launch_dkv_bf16(d, KPb, dcol, want_dv, b, (n_M + rK - 1) / rK + P_M + kRoundCUs, hs);
+    }));
+    SSC_TRY(launch_dkv_merge_bf16(d, KPb, want_dv, b, hs));
+    return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
   }
   int* poffN = at<int>(ws, L.poffN);
   int* poffM = at<int>(ws, L.poffM);
@@ -875,7 +910,9 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   b.items = at<Item>(ws, L.itemsK); b.n_items = counters + 1; b.offM = offM; b.poffM = poffM;
   b.inv_off = at<int>(ws, L.inv_off); b.inv_idx = at<int>(ws, L.inv_idx); b.poffN = poffN; b.offN = offN;
   SSC_TRY(timed("geo_dkv", hs, [&] { return launch_dkv(T, d, KP, b, (n_M + kRowsPerWG - 1) / kRowsPerWG + P_M, hs); }));
-  return SSC_OK;
+  SSC_TRY(launch_invalid_fill(counters + 4, n_N > 0 ? dQ : nullptr, (size_t)n_N * d, dK, (size_t)n_M * d, dV,
+                              (size_t)n_M * k, hs));
+  return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
 }
 
 ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,

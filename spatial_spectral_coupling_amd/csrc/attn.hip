@@ -459,6 +459,7 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(DkvArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) okr[db * 32 + c_row(i, h)] = a.scale * dk[db][i];
     }
+    if (a.dV == nullptr) return;  // dK only
     float* ovr = a.dV + (size_t)krow * a.k;
 #pragma unroll
     for (int cb = 0; cb < KP / 32; ++cb) {
@@ -474,17 +475,9 @@ __global__ __launch_bounds__(kThreads) void dkv_kernel(DkvArgs a) {
 // ---------------------------------------------------------------------------
 // instances and launchers
 // ---------------------------------------------------------------------------
+// fp32 instances of the generic kernels (bf16 runs the tb:: kernels of
+// attn_bf16_q.hip / attn_bf16_kv.hip)
 #define SSC_FOR_EACH_INSTANCE(X) \
-  X(bf16, 128, 224)              \
-  X(bf16, 128, 256)              \
-  X(bf16, 128, 128)              \
-  X(bf16, 128, 64)               \
-  X(bf16, 128, 32)               \
-  X(bf16, 64, 224)               \
-  X(bf16, 64, 256)               \
-  X(bf16, 64, 128)               \
-  X(bf16, 64, 64)                \
-  X(bf16, 64, 32)                \
   X(float, 64, 32)               \
   X(float, 64, 64)               \
   X(float, 64, 128)              \
@@ -496,12 +489,12 @@ template <typename T> constexpr DType dtype_of();
 template <> constexpr DType dtype_of<bf16>() { return DType::BF16; }
 template <> constexpr DType dtype_of<float>() { return DType::F32; }
 
+// Compiled shapes: bf16 d in {64, 128} with every padded width (the tb::
+// kernels), fp32 d in {64, 128} with padded widths up to 128.
 bool supported(DType t, int D, int KP) {
-#define SSC_SUP(TT, DD, KK) \
-  if (t == dtype_of<TT>() && D == DD && KP == KK) return true;
-  SSC_FOR_EACH_INSTANCE(SSC_SUP)
-#undef SSC_SUP
-  return false;
+  if (D != 64 && D != 128) return false;
+  if (t == DType::BF16) return KP == 32 || KP == 64 || KP == 128 || KP == 224 || KP == 256;
+  return KP == 32 || KP == 64 || KP == 128;
 }
 
 hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {

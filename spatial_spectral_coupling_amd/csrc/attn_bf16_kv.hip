@@ -10,7 +10,7 @@ namespace tb {
 // dK / dV
 // ---------------------------------------------------------------------------
 // Output of one source row (held by lanes l and l ^ 32): dK = scale * dk, dV.
-template <int D, int KP>
+template <int D, int KP, bool DV>
 __device__ __forceinline__ void dkv_store(const DkvArgs& a, int krow, bool key_ok, int h, const f32x16* dk,
                                           const f32x16* dv) {
   if (key_ok) {
@@ -24,6 +24,7 @@ __device__ __forceinline__ void dkv_store(const DkvArgs& a, int krow, bool key_o
                                                    a.scale * dk[db][4 * g + 2], a.scale * dk[db][4 * g + 3]};
       }
     }
+    if (!DV) return;
     float* ovr = a.dV + (size_t)krow * a.k;
     const bool vec = (a.k & 3) == 0;
 #pragma unroll
@@ -44,7 +45,7 @@ __device__ __forceinline__ void dkv_store(const DkvArgs& a, int krow, bool key_o
   }
 }
 
-template <int D, int KP, int NW, bool GEO, bool DCOL>
+template <int D, int KP, int NW, bool GEO, bool DCOL, bool DV>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void dkv_bf16(DkvArgs a) {
   constexpr int QB = TileSrc<D, NW>::ALLOC, OB = TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[QB + OB];
@@ -118,9 +119,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     vf[kc] = key_ok ? *reinterpret_cast<const bf16x8*>(Vp + (size_t)krow * KP + kc * 16 + h * 8) : bf16x8{};
   const float c2 = a.c2;
 
-  f32x16 dv[KP / 32], dk[D / 32];
+  // without DV the dV accumulators are never touched (no MFMA, no store)
+  f32x16 dv[DV ? KP / 32 : 1], dk[D / 32];
 #pragma unroll
-  for (int cb = 0; cb < KP / 32; ++cb) dv[cb] = f32x16{};
+  for (int cb = 0; cb < (DV ? KP / 32 : 1); ++cb) dv[cb] = f32x16{};
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dk[db] = f32x16{};
 
@@ -147,20 +149,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   __syncthreads();
 
   // One tile = 64 query rows = two 32-row blocks qb.  Its MFMAs form four
-  // chains of L steps each, run as one software pipeline of 4L steps:
-  //   c = 0, 1: scores S = Q K^T and dP = dO V^T of block c (row reads);
+  // chains run as one software pipeline:
+  //   c = 0, 1: scores S = Q K^T and dP = dO V^T of block c (row reads), L
+  //             steps each;
   //   c = 2, 3: dV += P^T dO and dK += dS^T Q of block c - 2 (transposed
-  //             reads), 2 (KP/32 + D/32) independent accumulators in turn.
+  //             reads), 2 (KP/32 + D/32) independent accumulators in turn
+  //             (2 D/32 without DV: dK only), LB steps each.
   // Operand reads run AH steps ahead of their MFMA (also across chain
   // boundaries), and the softmax of block qb (P, dS and their bf16
   // packing) is cut into slices spread over chain qb + 1, so that its VALU
   // work issues while that chain's MFMAs execute.  Scheduling fences between
   // steps keep this order.
   constexpr int NA = D / 16, NB = KP / 16, PAIRS = NA < NB ? NA : NB;
-  constexpr int NV = KP / 32, NK = D / 32, NVK = NV + NK;
-  constexpr int L = NA + NB;  // == 2 * NVK
-  static_assert(L == 2 * NVK, "chain lengths");
-  constexpr int U = 4 * L, AH = 3;
+  constexpr int NV = DV ? KP / 32 : 0, NK = D / 32, NVK = NV + NK;
+  constexpr int L = NA + NB;
+  constexpr int LB = 2 * NVK;
+  static_assert(!DV || L == LB, "chain lengths");
+  constexpr int C2 = 2 * L, C3 = 2 * L + LB, U = 2 * L + 2 * LB, AH = 3;
+  // chain of step u and the step's index within it
+  auto chain_of = [](const int u) { return u < L ? 0 : u < C2 ? 1 : u < C3 ? 2 : 3; };
+  auto index_in = [](const int u) { return u < L ? u : u < C2 ? u - L : u < C3 ? u - C2 : u - C3; };
+  auto chain_len = [](const int c) { return c < 2 ? L : LB; };
   constexpr int SLICES = 12;  // 4 lse/D group reads, 8 element pairs
   // Direct loads of the next tile, spread over the first half of the
   // pipeline: NJQ + NJO tile loads and one lse or D vector load per wave.
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
 
     auto operand = [&](const int u) -> bf16x8 {
-      const int c = u / L, j = u % L;
+      const int c = chain_of(u), j = index_in(u);
       if (c < 2) {
         if (j < 2 * PAIRS) return (j & 1) ? ro.read(Ot, c, j >> 1) : rq.read(Qt, c, j >> 1);
         return NA > NB ? rq.read(Qt, c, j - PAIRS) : ro.read(Ot, c, j - PAIRS);
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       return m < NV ? to.frag(Ot, m, 2 * qb + kk) : tq.frag(Qt, m - NV, 2 * qb + kk);
     };
     auto mma_step = [&](const int u, const bf16x8& x) {
-      const int c = u / L, j = u % L;
+      const int c = chain_of(u), j = index_in(u);
       if (c < 2) {
         const bool is_s = j < 2 * PAIRS ? (j & 1) == 0 : NA > NB;
         const int chunk = j < 2 * PAIRS ? j >> 1 : j - PAIRS;
@@ -209,8 +218,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         return;
       }
       const int qb = c - 2, kk = j / NVK, m = j % NVK;
-      if (m < NV) dv[m] = mma(x, pk[qb][kk], dv[m]);
-      else dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
+      if (m < NV) {
+        if constexpr (DV) dv[m] = mma(x, pk[qb][kk], dv[m]);
+      } else {
+        dk[m - NV] = mma(x, dk8[qb][kk], dk[m - NV]);
+      }
     };
     // Slice k of the softmax of block qb, in dependency order: the lse / D
     // values of element group g (elements 4g .. 4g+3) are read two slices
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         const int i = 2 * m, g = i >> 2, e = i & 3;
         const float p0 = fexp2(fmaf(sc[qb][i], c2, -lg[g][e]));
         const float p1 = fexp2(fmaf(sc[qb][i + 1], c2, -lg[g][e + 1]));
-        put_pair(pk[qb][m >> 2], m & 3, p0, p1);
+        if (DV) put_pair(pk[qb][m >> 2], m & 3, p0, p1);
         // with DCOL the ones / -D columns already made dp = dP - D
         const float e0 = DCOL ? dp[qb][i] : dp[qb][i] - dg[g][e];
         const float e1 = DCOL ? dp[qb][i + 1] : dp[qb][i + 1] - dg[g][e + 1];
@@ -266,10 +278,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
       if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
         load_row((u + 2 - LOAD0) / LSTRIDE);
-      const int c = u / L, j = u % L;
+      const int c = chain_of(u), j = index_in(u);
       if (c != 1 && c != 2) return;
       static_for<SLICES>([&](auto k) {
-        if (k * L / SLICES == j) slice(c - 1, k);
+        if (k * chain_len(c) / SLICES == j) slice(c - 1, k);
       });
     };
 
@@ -296,26 +308,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   if (GEO && it.slot >= 0) {
     // one part of a split item: partial sums for the merge pass
-    constexpr int F = (D / 32 + KP / 32) * 16;
+    constexpr int F = (D / 32 + (DV ? KP / 32 : 0)) * 16;
     float* out = a.part + (size_t)it.slot * F * (NW * 64) + tid;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) out[(db * 16 + i) * (NW * 64)] = dk[db][i];
+    if constexpr (DV) {
 #pragma unroll
-    for (int cb = 0; cb < KP / 32; ++cb)
+      for (int cb = 0; cb < KP / 32; ++cb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) out[((D / 32 + cb) * 16 + i) * (NW * 64)] = dv[cb][i];
+        for (int i = 0; i < 16; ++i) out[((D / 32 + cb) * 16 + i) * (NW * 64)] = dv[cb][i];
+    }
     return;
   }
-  dkv_store<D, KP>(a, krow, key_ok, h, dk, dv);
+  dkv_store<D, KP, DV>(a, krow, key_ok, h, dk, dv);
 }
 
 // Merge of the parts of split items: dK = scale * sum, dV = sum (part order),
-// one workgroup per 32-column block (D/32 of dK, then KP/32 of dV).
-template <int D, int KP, int NW>
+// one workgroup per 32-column block (D/32 of dK, then KP/32 of dV with DV).
+template <int D, int KP, int NW, bool DV>
 __global__ __launch_bounds__(NW * 64) void dkv_merge_bf16(DkvArgs a) {
-  constexpr int NK = D / 32, NB = NK + KP / 32;
+  constexpr int NK = D / 32, NB = NK + (DV ? KP / 32 : 0);
+  if (*a.status != 0) {
+    // the planner rejected the offsets or the selection: nothing was computed
+    fill_nan_grid(a.dK, (size_t)a.n_M * D);
+    if (DV) fill_nan_grid(a.dV, (size_t)a.n_M * a.k);
+    return;
+  }
   const int item = blockIdx.x / NB, blk = blockIdx.x - item * NB;
   if (item >= *a.n_split) return;
   const SplitItem sp = a.split[item];
@@ -344,6 +364,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_merge_bf16(DkvArgs a) {
     }
     return;
   }
+  if (!DV) return;
   float* ovr = a.dV + (size_t)krow * a.k;
   const bool vec = (a.k & 3) == 0;
 #pragma unroll
@@ -376,13 +397,19 @@ __global__ __launch_bounds__(NW * 64) void dkv_merge_bf16(DkvArgs a) {
   X(64, 64)                   \
   X(64, 32)
 
-hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st) {
-#define SSC_L1(DD, KK, CC)                                                                                    \
-  if (a.items != nullptr)                                                                                   \
-    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true, CC>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
-  else                                                                                                      \
-    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false, CC>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
+hipError_t launch_dkv_bf16(int D, int KP, bool dcol, bool dv, const DkvArgs& a, int grid, hipStream_t st) {
+#define SSC_L2(DD, KK, CC, VV)                                                                                      \
+  if (a.items != nullptr)                                                                                         \
+    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, true, CC, VV>), dim3(grid), dim3(kWavesK * 64), 0, st, a);  \
+  else                                                                                                            \
+    hipLaunchKernelGGL((tb::dkv_bf16<DD, KK, kWavesK, false, CC, VV>), dim3(grid), dim3(kWavesK * 64), 0, st, a); \
   return hipGetLastError();
+#define SSC_L1(DD, KK, CC)      \
+  if (dv) {                     \
+    SSC_L2(DD, KK, CC, true)    \
+  } else {                      \
+    SSC_L2(DD, KK, CC, false)   \
+  }
 #define SSC_L(DD, KK)                   \
   if (dcol && D == DD && KP == KK) {    \
     SSC_L1(DD, KK, true)                \
@@ -398,15 +425,20 @@ hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid,
   }
 #undef SSC_L
 #undef SSC_L1
+#undef SSC_L2
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dkv_merge_bf16(int D, int KP, const DkvArgs& a, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                                      \
-  if (D == DD && KP == KK) {                                                                               \
-    hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK>), dim3(kRoundCUs * (DD / 32 + KK / 32)),            \
-                       dim3(kWavesK * 64), 0, st, a);                                                       \
-    return hipGetLastError();                                                                              \
+hipError_t launch_dkv_merge_bf16(int D, int KP, bool dv, const DkvArgs& a, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                           \
+  if (D == DD && KP == KK) {                                                                                    \
+    if (dv)                                                                                                     \
+      hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK, true>), dim3(kRoundCUs * (DD / 32 + KK / 32)),    \
+                         dim3(kWavesK * 64), 0, st, a);                                                         \
+    else                                                                                                        \
+      hipLaunchKernelGGL((tb::dkv_merge_bf16<DD, KK, kWavesK, false>), dim3(kRoundCUs * (DD / 32)),             \
+                         dim3(kWavesK * 64), 0, st, a);                                                         \
+    return hipGetLastError();                                                                                   \
   }
   SSC_BF16_INSTANCES(SSC_L)
 #undef SSC_L

@@ -85,9 +85,14 @@ __device__ __forceinline__ void fwd_store(const FwdArgs& a, int row, bool row_ok
   }
 }
 
-template <int D, int KP, int NW, bool GEO, bool ONES>
+// VT (dense only): V arrives grouped-transposed (a.Vt, groups of 16 source
+// rows as [KP][16] blocks), the key rows are read in the sigma_row order, so
+// every value-product operand is one 16-byte read of the transposed tile
+// (GroupReader) instead of two transposed reads of a row tile.
+template <int D, int KP, int NW, bool GEO, bool ONES, bool VT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void fwd_bf16(FwdArgs a) {
-  constexpr int KB = TileSrc<D, NW>::ALLOC, VB = TileSrc<KP, NW>::ALLOC;
+  static_assert(!(GEO && VT), "the transposed value tile is dense only");
+  constexpr int KB = TileSrc<D, NW>::ALLOC, VB = VT ? TileSrcG<KP, NW>::ALLOC : TileSrc<KP, NW>::ALLOC;
   __shared__ __attribute__((aligned(1024))) char sm0[KB + VB];
   __shared__ __attribute__((aligned(1024))) char sm1[KB + VB];
   __shared__ int rowtab[2][kTile + 1];  // rows of the next tiles, sentinel at kTile
@@ -124,14 +129,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   sK.init(a.Kp, a.n_M);
   TileSrc<KP, NW> sV;
   sV.init(a.Vp, a.n_M + 1);
+  TileSrcG<KP, NW> sVt;
+  if (VT) sVt.init(a.Vt, a.groupsVt);
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
-  RowReader<D> rk;
+  std::conditional_t<VT, RowReaderP<D>, RowReader<D>> rk;
   rk.init(l32, h);
   TrReader<KP> tv;
   tv.init(tr_r, tr_c);
+  GroupReader rvt;
+  rvt.init(l32, h);
+  // key of C-layout element i (lane group h) within a 32-key half
+  auto key_of = [&](const int i) { return VT ? sigma_row(c_row(i, h)) : c_row(i, h); };
 
   // A negative scale is folded into Q (exact sign flip), so the reference is
   // always a maximum.
@@ -175,14 +186,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;
   constexpr int C1 = NS, C2 = 2 * NS, C3 = 2 * NS + NPV, U = 2 * NS + 2 * NPV, AH = 5;
   constexpr int SLICES = 10;  // 2 maximum, 8 element pairs
-  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = TileSrc<KP, NW>::NJ;
+  constexpr int NJK = TileSrc<D, NW>::NJ, NJV = VT ? TileSrcG<KP, NW>::NJ : TileSrc<KP, NW>::NJ;
   constexpr int NL = NJK + NJV, LOAD0 = 2, LSTRIDE = (U / 2 - LOAD0) / NL > 2 ? (U / 2 - LOAD0) / NL : 2;
   // dense: the per-lane load offsets do not depend on the tile; kept in registers
   int loff[NL];
   static_for<NL>([&](auto j) {
     loff[j] = GEO ? (j < NJK ? TileSrc<D, NW>::geo_chunk(wave, lane, j) : TileSrc<KP, NW>::geo_chunk(wave, lane, j - NJK))
                   : (j < NJK ? TileSrc<D, NW>::dense_offset(wave, lane, j)
-                             : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK));
+                             : VT ? (int)TileSrcG<KP, NW>::dense_offset(wave, lane, j - NJK)
+                                  : TileSrc<KP, NW>::dense_offset(wave, lane, j - NJK));
   });
   // geo: the row-table entry each load reads
   int gidx[NL];
@@ -190,6 +202,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     gidx[j] = !GEO ? 0 : j < NJK ? TileSrc<D, NW>::geo_index(wave, lane, j)
                                  : TileSrc<KP, NW>::geo_index(wave, lane, j - NJK);
   });
+  // the whole tile at t0 (the stream's first tile of this item)
+  auto load_first = [&](char* tile) {
+    sK.template load_tile<GEO>(tile, rowtab[0], t0 * kTile, wave, lane);
+    if constexpr (VT) {
+      const i32x4 w = sVt.window(t0 * kGroupsPerTile);
+      static_for<NJV>([&](auto j) { sVt.load_at(tile + KB, w, (unsigned)loff[NJK + j], wave, j); });
+    } else {
+      sV.template load_tile<GEO>(tile + KB, rowtab[0], t0 * kTile, wave, lane);
+    }
+  };
 
   // row sum of this lane's row (both halves)
   auto row_sum = [&]() {
@@ -222,10 +244,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (tid == 0) rowtab[0][kTile] = rowtab[1][kTile] = rc.none;
     }
     __syncthreads();
-    if (t1 > t0) {
-      sK.template load_tile<GEO>(sm0, rowtab[0], t0 * kTile, wave, lane);
-      sV.template load_tile<GEO>(sm0 + KB, rowtab[0], t0 * kTile, wave, lane);
-    }
+    if (t1 > t0) load_first(sm0);
     wait_loads();
     __syncthreads();
 
@@ -238,23 +257,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
       const bool first = !BOUND && t == t0 && !fixed;
-      if (nvalid < kTile) {
+      // Keys past the end of the last tile: with VT, the bounded reference and
+      // the row sums taken from the ones column they need no mask (K and the
+      // transposed V read zeros there, so their probabilities are at most 1
+      // and multiply zero values and a zero ones column); otherwise their
+      // scores start at -inf.
+      constexpr bool MASK = !(VT && BOUND && ONES);
+      if (MASK && __builtin_expect(nvalid < kTile, 0)) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) bias[hb][i] = hb * 32 + c_row(i, h) < nvalid ? 0.f : -INFINITY;
+          for (int i = 0; i < 16; ++i) bias[hb][i] = hb * 32 + key_of(i) < nvalid ? 0.f : -INFINITY;
       }
       f32x16 sc[2];
       float sv[2][16];
       bf16x8 pf[2][2];
       float mx[2], mh[2], mref = m_run, lsum = 0.f;
-      sc[0] = bias[0];
-      sc[1] = bias[1];
+      sc[0] = MASK ? bias[0] : f32x16{};
+      sc[1] = MASK ? bias[1] : f32x16{};
 
       auto operand = [&](const int u) -> bf16x8 {
         if (u < C2) return rk.read(Kt, u / NS, u % NS);
         const int hb = u < C3 ? 0 : 1, j = u - (hb ? C3 : C2);
-        return tv.frag(Vt, j % NCB, 2 * hb + j / NCB);
+        if constexpr (VT) return rvt.read(Vt, j % NCB, 2 * hb + j / NCB);
+        else return tv.frag(Vt, j % NCB, 2 * hb + j / NCB);
       };
       auto mma_step = [&](const int u, const bf16x8& x) {
         if (u < C2) {
@@ -293,7 +319,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       };
       const int* rn = rowtab[b ^ 1];
       const int row0n = (t + 1) * kTile;
-      const i32x4 winK = GEO ? sK.whole() : sK.window(row0n), winV = GEO ? sV.whole() : sV.window(row0n);
+      const i32x4 winK = GEO ? sK.whole() : sK.window(row0n);
+      const i32x4 winV = GEO ? sV.whole() : VT ? sVt.window((t + 1) * kGroupsPerTile) : sV.window(row0n);
       int grow = -1;
       auto load_row = [&](const int j) {  // geo phase 1
         grow = rn[gidx[j]];
@@ -304,6 +331,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           else sK.load_dense_at(Kn, winK, loff[j], wave, j);
         } else {
           if (GEO) sV.load_geo_at(Kn + KB, winV, grow, loff[j], wave, j - NJK);
+          else if (VT) sVt.load_at(Kn + KB, winV, (unsigned)loff[j], wave, j - NJK);
           else sV.load_dense_at(Kn + KB, winV, loff[j], wave, j - NJK);
         }
       };
@@ -401,6 +429,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
   // with the same operations in the same order (so the blocks agree bit for
   // bit); block 0 writes lse
   constexpr int NB = KP / 32;
+  if (*a.status != 0) {
+    // the planner rejected the offsets or the selection: nothing was computed
+    fill_nan_grid(a.O, (size_t)a.n_N * a.k);
+    fill_nan_grid(a.lse, (size_t)a.n_N);
+    return;
+  }
   const int item = blockIdx.x / NB, cb = blockIdx.x - item * NB;
   if (item >= *a.n_split) return;
   const SplitItem sp = a.split[item];
@@ -748,6 +782,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_merge_bf16(DqArgs a) {
   constexpr int NB = D / 32;
+  if (*a.status != 0) {
+    fill_nan_grid(a.dQ, (size_t)a.n_N * D);
+    return;
+  }
   const int item = blockIdx.x / NB, db = blockIdx.x - item * NB;
   if (item >= *a.n_split) return;
   const SplitItem sp = a.split[item];
@@ -795,11 +833,11 @@ __global__ __launch_bounds__(NW * 64) void dq_merge_bf16(DqArgs a) {
 // The forward takes the row sums from a ones column of V whenever k < KP;
 // only KP = 256 also has the variant without one (k = 256).
 hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st) {
-#define SSC_L1(DD, KK, OO)                                                                                      \
-  if (a.items != nullptr)                                                                                     \
-    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true, OO>), dim3(grid), dim3(kWavesQ * 64), 0, st, a);  \
-  else                                                                                                        \
-    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false, OO>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+#define SSC_L1(DD, KK, OO)                                                                                          \
+  if (a.items != nullptr)                                                                                         \
+    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, true, OO, false>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
+  else                                                                                                            \
+    hipLaunchKernelGGL((tb::fwd_bf16<DD, KK, kWavesQ, false, OO, true>), dim3(grid), dim3(kWavesQ * 64), 0, st, a); \
   return hipGetLastError();
 #define SSC_L(DD, KK)                   \
   if (ones && D == DD && KP == KK) {    \

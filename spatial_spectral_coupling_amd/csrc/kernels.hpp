@@ -72,6 +72,12 @@ struct FwdArgs {
   float* part;
   const SplitItem* split;
   const int* n_split;
+  // geo: the planner's verdict (nonzero: offsets or selection invalid; the
+  // merge pass then fills the outputs with NaN)
+  const int* status;
+  // dense bf16: V grouped-transposed, [groupsVt][KP][16] (row k = ones)
+  const void* Vt;
+  int groupsVt;
 };
 
 // Partial maxima of the squared key-row norms (bf16 forward): kNormParts
@@ -104,6 +110,7 @@ struct DqArgs {
   float* part;
   const SplitItem* split;
   const int* n_split;
+  const int* status;        // geo: the planner's verdict (see FwdArgs)
 };
 
 // dK / dV pass.
@@ -135,6 +142,7 @@ struct DkvArgs {
   float* part;
   const SplitItem* split;
   const int* n_split;
+  const int* status;    // geo: the planner's verdict (see FwdArgs)
 };
 
 // Packing of one tensor into the padded patch layout.
@@ -297,7 +305,8 @@ hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid,
 // dcol: V carries two ones columns and dO the high / low parts of -D there
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);
-hipError_t launch_dkv_bf16(int D, int KP, bool dcol, const DkvArgs& a, int grid, hipStream_t st);
+// dv: also form dV (false: dK only, a.dV unused)
+hipError_t launch_dkv_bf16(int D, int KP, bool dcol, bool dv, const DkvArgs& a, int grid, hipStream_t st);
 hipError_t launch_fm_gram(int KP, bool fwd, const FmArgs& a, int nblk, hipStream_t st);
 hipError_t launch_fm_reduce(int KP, bool fwd, const FmArgs& a, int nblk, hipStream_t st);
 hipError_t launch_fm_chol(int KP, const FmArgs& a, hipStream_t st);
@@ -306,7 +315,19 @@ hipError_t launch_fm_apply(int KP, const FmArgs& a, hipStream_t st);
 // merge passes of split geo items (kRoundCUs workgroups, idle past the count)
 hipError_t launch_fwd_merge_bf16(int D, int KP, bool ones, const FwdArgs& a, hipStream_t st);
 hipError_t launch_dq_merge_bf16(int D, const DqArgs& a, hipStream_t st);
-hipError_t launch_dkv_merge_bf16(int D, int KP, const DkvArgs& a, hipStream_t st);
+hipError_t launch_dkv_merge_bf16(int D, int KP, bool dv, const DkvArgs& a, hipStream_t st);
+// Offsets check (debug builds): *flag = 1 unless off[0] = 0, off[P] = n and
+// the entries do not decrease, for both offset arrays (one workgroup each)
+hipError_t launch_check_offsets(const int* offN, int P_N, int n_N, const int* offM, int P_M, int n_M, int* flag,
+                                hipStream_t st);
+// Grouped-transposed bf16 copy: Xg[j / 16][c][j % 16] = X[j][c] for c < w,
+// j < n (X [n x w] rows); rows w .. w + ones - 1 hold 1 for j < n; every other
+// entry of the (npad / 16) x W x 16 array (npad a multiple of 64) is 0.
+hipError_t launch_transpose_bf16(const void* X, int n, int w, int W, int ones, void* Xt, int npad, hipStream_t st);
+// NaN into up to three fp32 outputs when *status is nonzero (a rejected geo
+// plan); otherwise the workgroups exit at once
+hipError_t launch_invalid_fill(const int* status, float* x0, size_t n0, float* x1, size_t n1, float* x2, size_t n2,
+                               hipStream_t st);
 hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStream_t st);
 hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 bool supported(DType t, int D, int KP);

@@ -179,6 +179,62 @@ __global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
   }
 }
 
+// Grouped-transposed copy of bf16 rows: one workgroup per 64 rows (4 groups
+// of 16).  The rows' block X[j0 .. j0 + 64) is contiguous, so it is read with
+// coalesced loads (16 bytes when w % 8 == 0) into LDS (pitch 257 halves, so
+// reading a column hits distinct banks); the 4 groups' [W][16] blocks are
+// one contiguous output range, written in 16-byte chunks of 8 positions.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const unsigned short* X, int n, int w, int W, int ones,
+                                                             unsigned short* Xt, int npad) {
+  constexpr int P = 257;
+  __shared__ unsigned short t[64 * P];
+  const int j0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int rows = min(64, n - j0);
+  const int total = rows > 0 ? rows * w : 0;
+  const unsigned short* src = X + (size_t)j0 * w;
+  if ((w & 7) == 0) {
+    for (int q = tid; q < total / 8; q += 256) {
+      const Chunk v = ld_chunk(src + 8 * q);
+      const int r = (8 * q) / w, c0 = 8 * q - r * w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[r * P + c0 + 2 * e] = (unsigned short)(v.w[e] & 0xffffu);
+        t[r * P + c0 + 2 * e + 1] = (unsigned short)(v.w[e] >> 16);
+      }
+    }
+  } else {
+    for (int i = tid; i < total; i += 256) t[(i / w) * P + i % w] = src[i];
+  }
+  __syncthreads();
+  // chunk q of the block's 4 groups: group g = q / (2 W), row c, half h
+  for (int q = tid; q < W * 8; q += 256) {
+    const int g = q / (2 * W), rem = q - g * 2 * W, c = rem >> 1, jj = 16 * g + 8 * (rem & 1);
+    unsigned short v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = jj + e;
+      unsigned short x = 0;
+      if (j < rows) {
+        if (c < w) x = t[j * P + c];
+        else if (c < w + ones) x = 0x3f80;  // bf16 1.0
+      }
+      v[e] = x;
+    }
+    Chunk o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.w[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+    st_chunk(Xt + ((size_t)(j0 / 16 + g) * W + c) * 16 + 8 * (rem & 1), o);
+  }
+}
+
+hipError_t launch_transpose_bf16(const void* X, int n, int w, int W, int ones, void* Xt, int npad, hipStream_t st) {
+  if (npad <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(npad / 64), dim3(256), 0, st,
+                     reinterpret_cast<const unsigned short*>(X), n, w, W, ones, reinterpret_cast<unsigned short*>(Xt),
+                     npad);
+  return hipGetLastError();
+}
+
 // Squared norms of bf16 rows (d = 64 or 128, 16-byte aligned rows), their
 // maximum per workgroup: one thread per 16-byte chunk, the d / 8 chunks of a
 // row reduced over consecutive lanes, grid-stride over the rows.
@@ -698,6 +754,49 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Offsets rule check for the debug build's patch scoring: workgroup 0 checks
+// offN, workgroup 1 offM; either sets *flag on a violation.  The flag is
+// cleared by a one-thread kernel launched before it on the same stream.
+__global__ __launch_bounds__(256) void check_offsets_kernel(const int* offN, int P_N, int n_N, const int* offM,
+                                                            int P_M, int n_M, int* flag) {
+  const int* off = blockIdx.x == 0 ? offN : offM;
+  const int P = blockIdx.x == 0 ? P_N : P_M, n = blockIdx.x == 0 ? n_N : n_M;
+  int bad = 0;
+  if (threadIdx.x == 0) bad = off[0] != 0 || off[P] != n;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) bad |= off[p] > off[p + 1];
+  if (__syncthreads_or(bad) && threadIdx.x == 0) atomicOr(flag, 1);
+}
+
+__global__ void clear_flag_kernel(int* flag) { *flag = 0; }
+
+hipError_t launch_check_offsets(const int* offN, int P_N, int n_N, const int* offM, int P_M, int n_M, int* flag,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, st, flag);
+  hipLaunchKernelGGL(check_offsets_kernel, dim3(2), dim3(256), 0, st, offN, P_N, n_N, offM, P_M, n_M, flag);
+  return hipGetLastError();
+}
+
+// Outputs of a rejected geo plan (fp32 path): quiet NaN, so that a result
+// computed from invalid offsets or an invalid selection cannot pass for one.
+__global__ __launch_bounds__(256) void invalid_fill_kernel(const int* status, float* x0, size_t n0, float* x1,
+                                                           size_t n1, float* x2, size_t n2) {
+  if (*status == 0) return;
+  const size_t stride = (size_t)gridDim.x * blockDim.x, g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const float q = __builtin_nanf("");
+  if (x0 != nullptr)
+    for (size_t i = g; i < n0; i += stride) x0[i] = q;
+  if (x1 != nullptr)
+    for (size_t i = g; i < n1; i += stride) x1[i] = q;
+  if (x2 != nullptr)
+    for (size_t i = g; i < n2; i += stride) x2[i] = q;
+}
+
+hipError_t launch_invalid_fill(const int* status, float* x0, size_t n0, float* x1, size_t n1, float* x2, size_t n2,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(invalid_fill_kernel, dim3(256), dim3(256), 0, st, status, x0, n0, x1, n1, x2, n2);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // patch pooling (fp64 sums, then the mean)
 // ---------------------------------------------------------------------------
@@ -705,9 +804,11 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
 // row phase t / (d/2): it sums rows begin + phase, begin + phase + NPH, ...
 // in fp64, and the NPH phase sums are then added in phase order.  The order
 // is fixed, so the result is deterministic.  Every partial sum is exact in
-// fp64 (hence equal to the sum in any order, row order included) when the
-// patch has at most 4096 rows and its nonzero entries lie within a factor
-// 2^36 (bf16) or 2^20 (fp32) of each other.
+// fp64 (hence equal to the sum in any order, row order included) when it
+// needs at most 53 significant bits: with p significant bits per entry (8
+// for bf16, 24 for fp32), at most 2^12 rows and nonzero magnitudes within a
+// factor 2^r of each other, a sum spans p + r + 12 bits, so r <= 33 (bf16)
+// or r <= 17 (fp32) with rows <= 4096.
 // bf16 rows (16-byte aligned, d in {64, 128}): thread t owns the 8-column
 // chunk t % (d/8) and the row phase t / (d/8) (16 or 32 phases), one 16-byte
 // load per row; same fixed phase order, same exactness.

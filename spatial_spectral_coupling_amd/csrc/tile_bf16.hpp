@@ -239,6 +239,97 @@ struct TileSrc {
   }
 };
 
+// Direct loads of 64 positions of a GROUPED-TRANSPOSED array into an LDS tile
+// of ROWS rows x 64 positions.  The array holds groups of 16 positions, each
+// group a contiguous [ROWS][16] block (32 bytes per row): group g starts at
+// byte g * ROWS * 32, so the 4 groups of a dense tile are one contiguous
+// block and a gathered stream can place any group in any of a tile's four
+// slots.  An MFMA operand whose contraction runs along the positions (8
+// consecutive positions of one row) is one 16-byte LDS read.
+// LDS tile: row r at r * 128 bytes, no pad; its logical 16-byte chunk cc
+// (positions 8 cc .. 8 cc + 7) sits in physical chunk cc ^ ((r >> 1) & 7), so
+// the 16 rows of a 16-lane row-fragment read land in 16 distinct bank groups.
+// Slot s of a tile is row s / 8, physical chunk s % 8; every slot is data.
+template <int ROWS, int NW>
+struct TileSrcG {
+  static constexpr int SLOTS = ROWS * 8;
+  static constexpr int NI = (SLOTS + 63) / 64;       // instructions per tile
+  static constexpr int NJ = (NI + NW - 1) / NW;      // per wave
+  static constexpr int ALLOC = NJ * NW * 1024;        // LDS bytes of a tile buffer
+  static constexpr int GROUP = ROWS * 32;             // bytes of one 16-position group
+
+  const char* base;
+  unsigned bytes;  // groups * GROUP
+
+  __device__ __forceinline__ void init(const void* b, int groups) {
+    base = reinterpret_cast<const char*>(b);
+    bytes = (unsigned)groups * GROUP;
+  }
+  // logical chunk of slot s (tile row s / 8)
+  __device__ __forceinline__ static int chunk_of(int s) { return (s & 7) ^ ((s >> 4) & 7); }
+  // dense: resource of the 4 groups starting at group g0 (zeros past the end)
+  __device__ __forceinline__ i32x4 window(int g0) const {
+    const unsigned o = (unsigned)g0 * GROUP;
+    return make_rsrc(base + o, bytes > o ? bytes - o : 0u);
+  }
+  __device__ __forceinline__ i32x4 whole() const { return make_rsrc(base, bytes); }
+  // byte offset of this lane's chunk j within its group, and which of the
+  // tile's four group slots it belongs to (rows past ROWS read the next
+  // groups' data into slots that are never read)
+  __device__ __forceinline__ static unsigned in_group(int wave, int lane, int j) {
+    const int s = (wave + j * NW) * 64 + lane, r = s >> 3, cc = chunk_of(s);
+    return (unsigned)(r * 32 + (cc & 1) * 16);
+  }
+  __device__ __forceinline__ static int group_slot(int wave, int lane, int j) {
+    return chunk_of((wave + j * NW) * 64 + lane) >> 1;
+  }
+  // dense: offset from the window's first group
+  __device__ __forceinline__ static unsigned dense_offset(int wave, int lane, int j) {
+    return (unsigned)group_slot(wave, lane, j) * GROUP + in_group(wave, lane, j);
+  }
+  __device__ __forceinline__ static void load_at(char* tile, const i32x4& win, unsigned off, int wave, int j) {
+    ssc_raw_buffer_load_lds(win, (lds_void_t*)(tile + (wave + j * NW) * 1024), 16, (int)off, 0, 0, 0);
+  }
+};
+
+// Row-fragment reads of a TileSrcG tile: row cb * 32 + l32, logical chunk
+// 2 kc + h (positions 16 kc + 8 h .. + 7) for kc = 0..3.
+struct GroupReader {
+  int off[4];
+  __device__ __forceinline__ void init(int l32, int h) {
+    const int x = (l32 >> 1) & 7;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      off[kc] = l32 * 128 + (((2 * kc + h) ^ x) << 4);
+      // opaque to the range analysis: the block offset below is then added
+      // (folded into the read's immediate), not or-ed in a VALU instruction
+      asm volatile("" : "+v"(off[kc]));
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const char* tile, int cb, int kc) const {
+    return *reinterpret_cast<const bf16x8*>(tile + off[kc] + cb * 32 * 128);
+  }
+};
+
+// Row permutation within a 32-row MFMA block that makes the C layout of a
+// product over these rows hand each lane eight CONSECUTIVE rows as the k
+// elements of the next product: C element i of lane group h sits in row
+// c_row(i, h) = 8 (i / 4) + 4 h + i % 4; reading A row r from tile row
+// sigma(r) (bits 2 and 3 of r swapped) puts tile rows 16 (i / 8) + 8 h +
+// i % 8 there, so the partner operand of 16-row chunk kc is the 16 bytes at
+// positions 16 kc + 8 h .. + 7 of a transposed tile.
+__device__ __forceinline__ constexpr int sigma_row(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Row-fragment reads like RowReader, with the block rows permuted by sigma_row.
+template <int W>
+struct RowReaderP {
+  int lane_off;
+  __device__ __forceinline__ void init(int l32, int h) { lane_off = sigma_row(l32) * Geo<W>::PITCH + h * 16; }
+  __device__ __forceinline__ bf16x8 read(const char* tile, int rb, int cc) const {
+    return *reinterpret_cast<const bf16x8*>(tile + lane_off + rb * 32 * Geo<W>::PITCH + cc * 32);
+  }
+};
+
 // 64 fp32 values of a per-row vector (`limit` entries) for the rows of a
 // tile: dense row0 + lane, geo the table row (missing rows read zero).
 struct VecSrc {
@@ -259,6 +350,13 @@ struct VecSrc {
     ssc_raw_buffer_load_lds(all, (lds_void_t*)dst, 4, grow * 4, 0, 0, 0);
   }
 };
+
+// Quiet NaN into x[0 .. n) by the whole grid (outputs of a rejected geo plan).
+__device__ __forceinline__ void fill_nan_grid(float* x, size_t n) {
+  if (x == nullptr) return;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) x[i] = __builtin_nanf("");
+}
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

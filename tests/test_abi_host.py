@@ -261,3 +261,14 @@ def test_row_count_limit(L):
     assert L.ssc_workspace_bytes(ssc.OP_DENSE_BWD, BF16, big, 64, 128, 200, 0, 0, 0) == 0
     assert L.ssc_workspace_bytes(ssc.OP_LINEAR_FWD, BF16, 64, big, 128, 200, 0, 0, 0) == 0
     assert L.ssc_workspace_bytes(ssc.OP_DENSE_FWD, BF16, 1 << 22, 1 << 22, 128, 200, 0, 0, 0) > 0
+
+
+def test_debug_library_exports_every_declared_symbol(L):
+    # the debug build (SSC_DEBUG) is the same ABI with host-side verdict reads
+    if not os.path.exists(ssc_build.LIB_DEBUG):
+        ssc_build.build()
+    D = ctypes.CDLL(ssc_build.LIB_DEBUG)
+    for name in declared_functions():
+        assert hasattr(D, name), name
+    assert D.ssc_debug_build() == 1
+    assert L.ssc_debug_build() == 0

@@ -145,6 +145,7 @@ def test_dense_reference_fallbacks():
     assert err5 <= 2e-2
 
 
+@pytest.mark.timeout(900)
 def test_dense_60k_full_size_sampled():
     """The 60k workload: sampled rows of O, lse and dQ; dK/dV of a backward
     whose upstream gradient lives on sampled rows; identities at full size."""
@@ -203,3 +204,47 @@ def test_autograd_wrapper_matches_entry_points():
     assert torch.equal(O, O2)
     assert torch.equal(Qr.grad, dQ.to(torch.bfloat16))
     assert torch.equal(Vr.grad, dV.to(torch.bfloat16))
+
+
+def test_dense_60k_full_size():
+    """The 60k workload against the oracle on every element: O and lse, and
+    dQ, dK, dV of the workload's own upstream gradient (the oracle runs in
+    full-row blocks on the host cores, about half a minute)."""
+    say("dense 60k full generate")
+    c = gen.make_config(2)
+    say("dense 60k full gpu")
+    O, lse, dQ, dK, dV = run_dense(c)
+    say("dense 60k full oracle")
+    Or, lser, gr = oracle_dense(c)
+    check_fwd(O, Or, lse, lser, what="60k full")
+    check_grads((dQ, dK, dV), gr, what="60k full")
+
+
+@pytest.mark.parametrize("dt,nN,nM,d,k", [("bf16", 300, 517, 128, 200), ("bf16", 200, 333, 128, 256),
+                                          ("bf16", 77, 33, 64, 30), ("f32", 150, 260, 128, 128)])
+def test_dense_backward_without_dv(dt, nN, nM, d, k):
+    """dV = NULL: the dV products are skipped; dQ and dK are the bits of the
+    full call and match the oracle."""
+    say("dense bwd without dV", dt, nN, nM, d, k)
+    c = gen.make_small(nN, nM, d, k, dt, seed=nN + 2 * nM)
+    Q, K, V, dO = (to_dev(c[x], dt) for x in ("Q", "K", "V", "dO"))
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+    dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
+    dQ2, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
+    torch.cuda.synchronize()
+    assert dV2 is None
+    assert torch.equal(dQ2, dQ) and torch.equal(dK2, dK)
+    _, _, gr = oracle_dense(c)
+    check_grads((dQ2.cpu().numpy(), dK2.cpu().numpy(), dV.cpu().numpy()), gr, what=f"no-dV {dt} k{k}")
+
+
+def test_autograd_skips_dv_for_a_fixed_basis():
+    say("autograd fixed basis")
+    c = gen.make_small(100, 140, 64, 30, "bf16", seed=2)
+    Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
+    Qr, Kr = Q.clone().requires_grad_(True), K.clone().requires_grad_(True)
+    O = ssc.dense_coupling(Qr, Kr, V)
+    O.backward(dO.float())
+    O2, lse = ssc.coupling_dense_fwd(Q, K, V)
+    dQ, dK, _ = ssc.coupling_dense_bwd(Q, K, V, O2, dO, lse, need_dV=False)
+    assert torch.equal(Qr.grad, dQ.to(torch.bfloat16)) and torch.equal(Kr.grad, dK.to(torch.bfloat16))

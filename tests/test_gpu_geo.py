@@ -150,7 +150,10 @@ def test_geo_empty_and_unselected_patches():
     assert np.all(got[1][unsel] == 0) and np.all(got[2][unsel] == 0)
 
 
-def test_geo_invalid_selection_computes_nothing():
+def test_geo_invalid_selection_fills_nan():
+    """A repeated source patch in a row: the planner rejects the selection,
+    nothing is computed and the outputs come back as NaN (a result of an
+    invalid call cannot pass for a valid one); the call itself returns OK."""
     say("geo invalid idx")
     c = gen.make_small(200, 210, 128, 200, "bf16", seed=6, P_N=4, P_M=4, s=2)
     dev, permN, permM, P_N, P_M = sorted_problem(c)
@@ -170,7 +173,7 @@ def test_geo_invalid_selection_computes_nothing():
                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert st == 0
-    assert torch.all(O == 7.0) and torch.all(lse == 7.0)
+    assert torch.all(torch.isnan(O)) and torch.all(torch.isnan(lse))
 
 
 @pytest.mark.parametrize("i", [3])
@@ -214,10 +217,10 @@ def test_geo_workload_160k_sampled():
                  unsort(dVm.cpu().numpy(), permM)), (gr[0][rows], gr[1], gr[2]), "160k restricted")
 
 
-def test_geo_repeat_in_later_chunk_computes_nothing():
+def test_geo_repeat_in_later_chunk_fills_nan():
     """A repeated entry in row 40 (the planner's second chunk of 32 target
-    patches): forward and backward compute nothing and leave every output
-    untouched; the valid selection still works afterwards."""
+    patches): forward and backward compute nothing and fill every output
+    with NaN; the valid selection still works afterwards, bit for bit."""
     import ctypes
     say("geo repeat in a later chunk")
     c = gen.make_small(700, 720, 64, 30, "bf16", seed=8, P_N=70, P_M=72, s=4)
@@ -244,9 +247,9 @@ def test_geo_repeat_in_later_chunk_computes_nothing():
                             p(outs[0]), p(outs[1]), p(outs[2]), p(wsb), ctypes.c_size_t(wsb.numel()), st)
     torch.cuda.synchronize()
     assert r == 0 and rb == 0
-    assert torch.all(O7 == 7.0) and torch.all(lse7 == 7.0)
+    assert torch.all(torch.isnan(O7)) and torch.all(torch.isnan(lse7))
     for x in outs:
-        assert torch.all(x == 7.0)
+        assert torch.all(torch.isnan(x))
     _, _, O2, lse2, g2 = gpu_geo(dev, 4, sc, idx=idx)
     assert torch.equal(O2, O) and torch.equal(lse2, lse)
     for a, b in zip(g2, g):
@@ -281,3 +284,89 @@ def test_topk_exact_ties_break_to_lower_index(P_N, P_M, s):
     say(f"top-s exact ties P_N={P_N} P_M={P_M} s={s}: rows with tied scores {n_ties}")
     np.testing.assert_array_equal(C.cpu().numpy(), Cr)
     np.testing.assert_array_equal(idx.cpu().numpy(), idxr)
+
+
+@pytest.mark.timeout(900)
+def test_geo_workload_160k_full():
+    """160k, P = 640, s = 16 against the oracle on every target patch: O,
+    lse, dQ, dK and dV of the workload's own upstream gradient, all rows."""
+    say("geo 160k full generate")
+    c = gen.make_config(4)
+    compare_geo(c, c["s"], "160k full")
+
+
+def _raw(t):
+    import ctypes
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def test_debug_library_reports_invalid_inputs():
+    """libssc_debug.so: the device-side verdicts (repeated selection entry,
+    offsets out of order) come back as SSC_ERR_INVALID_ARG after kernels that
+    all ran to their end; the release library returns OK (NaN outputs for
+    the geo call).  Valid inputs give OK and the release library's bits."""
+    import ctypes
+    from spatial_spectral_coupling_amd import build as ssc_build
+    say("debug library verdicts")
+    D = ctypes.CDLL(ssc_build.LIB_DEBUG)
+    assert D.ssc_debug_build() == 1
+    c = gen.make_small(300, 320, 128, 200, "bf16", seed=31, P_N=6, P_M=7, s=3)
+    dev, permN, permM, P_N, P_M = sorted_problem(c)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    idx = ssc.patch_score_topk(dev["Q"], dev["offN"], dev["K"], dev["offM"], 3)
+    O_ref, lse_ref = ssc.coupling_geo_fwd(dev["Q"], dev["K"], dev["V"], dev["offN"], dev["offM"], idx, 0.1)
+    nws = ssc.workspace_bytes(ssc.OP_GEO_FWD, torch.bfloat16, 300, 320, 128, 200, P_N, P_M, 3)
+
+    def geo_fwd_call(L, sel):
+        O = torch.empty(300, 200, device="cuda")
+        lse = torch.empty(300, device="cuda")
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        r = L.coupling_geo_fwd(1, 128, 200, 300, P_N, _raw(dev["offN"]), 320, P_M, _raw(dev["offM"]), 3, _raw(sel),
+                               _raw(dev["Q"]), _raw(dev["K"]), _raw(dev["V"]), ctypes.c_float(0.1), _raw(O),
+                               _raw(lse), _raw(ws), ctypes.c_size_t(nws), st)
+        torch.cuda.synchronize()
+        return r, O, lse
+
+    r, O, lse = geo_fwd_call(D, idx)
+    assert r == 0 and torch.equal(O, O_ref) and torch.equal(lse, lse_ref)
+    bad = idx.clone()
+    bad[2, 1] = bad[2, 0]
+    r, O, _ = geo_fwd_call(D, bad)
+    assert r == 1 and torch.all(torch.isnan(O))
+    r, O, _ = geo_fwd_call(ssc.lib(), bad)
+    assert r == 0 and torch.all(torch.isnan(O))
+    out_of_range = idx.clone()
+    out_of_range[0, 0] = P_M
+    assert geo_fwd_call(D, out_of_range)[0] == 1
+
+    # patch scoring with offsets out of order
+    offN_bad = dev["offN"].clone()
+    offN_bad[2], offN_bad[3] = dev["offN"][3], dev["offN"][2]
+    nwt = ssc.workspace_bytes(ssc.OP_PATCH_TOPK, torch.bfloat16, 300, 320, 128, 1, P_N, P_M, 3)
+    for L, want in ((D, 1), (ssc.lib(), 0)):
+        for offN, w in ((dev["offN"], 0), (offN_bad, want)):
+            out = torch.empty(P_N, 3, dtype=torch.int32, device="cuda")
+            ws = torch.empty(nwt, dtype=torch.uint8, device="cuda")
+            r = L.patch_score_topk(1, 128, 300, P_N, _raw(offN), _raw(dev["Q"]), 320, P_M, _raw(dev["offM"]),
+                                   _raw(dev["K"]), 3, _raw(out), None, _raw(ws), ctypes.c_size_t(nwt), st)
+            torch.cuda.synchronize()
+            assert r == w, (L, r, w)
+
+
+@pytest.mark.parametrize("dt,k", [("bf16", 200), ("bf16", 256), ("f32", 30)])
+def test_geo_backward_without_dv(dt, k):
+    """dV = NULL: dQ and dK are the bits of the full call, and match the oracle."""
+    say("geo bwd without dV", dt, k)
+    c = gen.make_small(700, 650, 64 if dt == "f32" else 128, k, dt, seed=41, P_N=8, P_M=9, s=3)
+    dev, permN, permM, P_N, P_M = sorted_problem(c)
+    sc = c["scale"]
+    idx, _, O, lse, (dQ, dK, dV) = gpu_geo(dev, 3, sc)
+    dQ2, dK2, dV2 = ssc.coupling_geo_bwd(dev["Q"], dev["K"], dev["V"], dev["offN"], dev["offM"], idx, O, dev["dO"],
+                                         lse, sc, need_dV=False)
+    torch.cuda.synchronize()
+    assert dV2 is None
+    assert torch.equal(dQ2, dQ) and torch.equal(dK2, dK)
+    Q, K, V, dO, Cr, idxr = oracle_geo(c, 3)
+    gr = geo_bwd(Q, K, V, dO, c["labN"], c["labM"], idx.cpu().numpy(), sc)
+    check_grads((unsort(dQ2.cpu().numpy(), permN), unsort(dK2.cpu().numpy(), permM), unsort(dV.cpu().numpy(), permM)),
+                gr, "geo no-dV")
