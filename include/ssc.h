@@ -140,6 +140,22 @@ ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int*
                             ssc_stream stream);
 
 /*
+ * patch_score_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * patch_score_topk minus (ws, ws_bytes); it allocates nothing.  Its scratch
+ * (the fp64 patch means) is a static device array of 4 MiB + 256 bytes per
+ * GPU, held until the process ends, which limits P_N, P_M <= 2048 (d <= 128):
+ * larger patch counts return SSC_ERR_WORKSPACE.  Every call on one GPU shares
+ * that array, so calls that may overlap on the same GPU (different streams
+ * or threads) race: serialise them.  The first call on a device looks up the
+ * array's device address (one hipGetSymbolAddress, no allocation).
+ */
+ssc_status patch_score_topk_noalloc(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN,
+                                    const void* Q, int n_M, int P_M, const int* offM, const void* K,
+                                    int s, int* idx, double* scores, ssc_stream stream);
+
+/*
  * Geo forward (project page, "Geo-FlashAttention" and its pipeline figure:
  * a fused block-sparse kernel takes the exact softmax over the selected
  * source patches only): for every target row i of patch p, the softmax of

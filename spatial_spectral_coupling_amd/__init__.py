@@ -73,6 +73,7 @@ _SIGS = {
     "coupling_dense_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _sz, _vp]),
     "patch_score_topk": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "patch_score_topk_noalloc": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
     "coupling_geo_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp,
                               _vp, _vp, _sz, _vp]),
     "coupling_geo_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp,

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -674,6 +675,61 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   return SSC_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free patch scoring: the same kernels with their scratch (the
+// fp64 patch means and the debug verdict) in a file-scope device array.
+// Its size bounds the patch counts; every GPU the library runs on holds its
+// own copy until the process ends.  The kernels write every scratch entry
+// they read (pooling writes each patch mean, the verdict flag is cleared by
+// a kernel), so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kNoAllocMaxPatches = 2048;  // P_N, P_M <= this, d <= 128
+constexpr size_t kNoAllocScratchBytes = 2 * (size_t)kNoAllocMaxPatches * 128 * sizeof(double) + 256;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // address of `scratch` on each device (set on first use there)
+
+// The device address of `scratch` on the device of `stream`: looked up once
+// per device with that device current (host code must never pass the
+// array's own name, which is a host-side stand-in, to a kernel).
+ssc_status scratch_on(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (stream != nullptr) {
+    SSC_TRY(hipStreamGetDevice(stream, &dev));
+  } else {
+    SSC_TRY(hipGetDevice(&dev));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SSC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    SSC_TRY(hipGetDevice(&cur));
+    if (cur != dev) SSC_TRY(hipSetDevice(dev));
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_status(e2);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr) return SSC_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSC_OK;
+}
+}  // namespace
+
+extern "C" {
+
 ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN, const void* Q, int n_M,
                             int P_M, const int* offM, const void* K, int s, int* idx, double* scores, void* ws,
                             size_t ws_bytes, ssc_stream stream) {
@@ -709,6 +765,22 @@ ssc_status patch_score_topk(ssc_dtype dtype, int d, int n_N, int P_N, const int*
     return debug_verdict(flag, hs);
   }
   return SSC_OK;
+}
+
+ssc_status patch_score_topk_noalloc(ssc_dtype dtype, int d, int n_N, int P_N, const int* offN, const void* Q,
+                                    int n_M, int P_M, const int* offM, const void* K, int s, int* idx,
+                                    double* scores, ssc_stream stream) {
+  if (dtype != SSC_F32 && dtype != SSC_BF16) return SSC_ERR_INVALID_ARG;
+  if (n_N < 0 || n_M < 0) return SSC_ERR_INVALID_ARG;
+  ssc_status st = check_patches(n_N, P_N, n_M, P_M, s);
+  if (st != SSC_OK) return st;
+  if (d != 64 && d != 128) return SSC_ERR_UNSUPPORTED;
+  if (P_N > kNoAllocMaxPatches || P_M > kNoAllocMaxPatches) return SSC_ERR_WORKSPACE;
+  const Layout L = make_layout(SSC_OP_PATCH_TOPK, dtype, n_N, n_M, d, 1, P_N, P_M, s);
+  if (L.total > kNoAllocScratchBytes) return SSC_ERR_WORKSPACE;
+  void* ptr = nullptr;
+  if ((st = scratch_on(reinterpret_cast<hipStream_t>(stream), &ptr)) != SSC_OK) return st;
+  return patch_score_topk(dtype, d, n_N, P_N, offN, Q, n_M, P_M, offM, K, s, idx, scores, ptr, L.total, stream);
 }
 
 namespace {

@@ -272,3 +272,14 @@ def test_debug_library_exports_every_declared_symbol(L):
         assert hasattr(D, name), name
     assert D.ssc_debug_build() == 1
     assert L.ssc_debug_build() == 0
+
+
+def test_noalloc_patch_scoring_rejects_patch_counts_past_its_scratch(L):
+    # the allocation-free patch scoring holds the patch means in a fixed
+    # device array: more than 2048 patches a side is refused before any HIP call
+    assert L.patch_score_topk_noalloc(BF16, 128, 10, 2049, None, None, 10, 3, None, None, 1, None, None,
+                                      None) == WORKSPACE
+    assert L.patch_score_topk_noalloc(BF16, 128, 10, 3, None, None, 10, 2049, None, None, 1, None, None,
+                                      None) == WORKSPACE
+    assert L.patch_score_topk_noalloc(BF16, 96, 10, 3, None, None, 10, 3, None, None, 1, None, None,
+                                      None) == UNSUPPORTED
