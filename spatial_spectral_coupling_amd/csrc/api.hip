@@ -79,6 +79,7 @@ struct Layout {
   size_t splitQ = kNone, splitK = kNone, partQ = kNone, partK = kNone;  // bf16 geo: split items, partial sums
   size_t flag = kNone;   // patch scoring: offsets verdict (read by the debug build)
   size_t Vt = kNone;     // dense bf16 forward: V grouped-transposed, npadT / 16 groups of [KP][16]
+  size_t fallback = kNone;  // dense bf16 forward: per-workgroup fallback marks
   int npadT = 0;         // positions of the transposed copies (a multiple of the 64-row tile)
   size_t total = 0;
   int npadN = 0, npadM = 0;  // padded positions (upper bound for geo)
@@ -104,6 +105,7 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
     case SSC_OP_DENSE_FWD:
       L.Vt = take((size_t)kpad_fwd_bf16(k) * L.npadT * 2);
       L.knorm = take(kNormParts * 4);
+      L.fallback = take(((size_t)n_N + kRowsFwd - 1) / kRowsFwd * 4);
       break;
     case SSC_OP_GEO_FWD:
       L.Vp = take(nM * (size_t)kpad_fwd_bf16(k) * 2);
@@ -576,8 +578,18 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
     FwdArgs a{};
     a.Q = Q; a.Kp = K; a.Vt = Vt; a.groupsVt = L.npadT / kGroup; a.O = O; a.lse = lse;
     a.n_N = n_N; a.k = k; a.c2 = scale * kLog2e; a.n_M = n_M; a.knorm2 = knorm;
-    const int rQ = kRowsFwd;
-    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, (n_N + rQ - 1) / rQ, s); }));
+    const int rQ = kRowsFwd, grid = (n_N + rQ - 1) / rQ;
+    if (!ones) {
+      SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, grid, s); }));
+      return SSC_OK;
+    }
+    // wave-specialised pass with the bounded reference, then the one-wave
+    // kernel on the workgroups whose row sums underflowed (none, normally:
+    // those workgroups exit at once)
+    a.fallback_out = at<int>(ws, L.fallback);
+    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_ws(d, KPf, a, grid, s); }));
+    a.fallback = a.fallback_out;
+    SSC_TRY(launch_fwd_bf16(d, KPf, ones, a, grid, s));
     return SSC_OK;
   }
   const int ngroups = L.npadM / kGroup;

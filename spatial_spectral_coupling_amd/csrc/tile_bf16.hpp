@@ -311,6 +311,24 @@ struct GroupReader {
   }
 };
 
+// The same reads restricted to the two 16-position chunks 2 kh, 2 kh + 1 of
+// one half of the tile (kh wave-uniform, known only at run time): the two
+// lane offsets are formed once, so no register array is indexed at run time.
+struct GroupReaderHalf {
+  int off[2];
+  __device__ __forceinline__ void init(int l32, int h, int kh) {
+    const int x = (l32 >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      off[kk] = l32 * 128 + (((4 * kh + 2 * kk + h) ^ x) << 4);
+      asm volatile("" : "+v"(off[kk]));
+    }
+  }
+  __device__ __forceinline__ bf16x8 read(const char* tile, int cb, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + off[kk] + cb * 32 * 128);
+  }
+};
+
 // Row permutation within a 32-row MFMA block that makes the C layout of a
 // product over these rows hand each lane eight CONSECUTIVE rows as the k
 // elements of the next product: C element i of lane group h sits in row
@@ -324,7 +342,10 @@ __device__ __forceinline__ constexpr int sigma_row(int r) { return (r & ~12) | (
 template <int W>
 struct RowReaderP {
   int lane_off;
-  __device__ __forceinline__ void init(int l32, int h) { lane_off = sigma_row(l32) * Geo<W>::PITCH + h * 16; }
+  // rb0: a run-time row block folded into the lane offset
+  __device__ __forceinline__ void init(int l32, int h, int rb0 = 0) {
+    lane_off = (rb0 * 32 + sigma_row(l32)) * Geo<W>::PITCH + h * 16;
+  }
   __device__ __forceinline__ bf16x8 read(const char* tile, int rb, int cc) const {
     return *reinterpret_cast<const bf16x8*>(tile + lane_off + rb * 32 * Geo<W>::PITCH + cc * 32);
   }
