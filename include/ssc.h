@@ -61,7 +61,17 @@ typedef enum {
   SSC_ERR_HIP = 4           /* a HIP launch failed */
 } ssc_status;
 
-typedef enum { SSC_F32 = 0, SSC_BF16 = 1 } ssc_dtype;
+/* The dtype and op enumerations each carry two range markers (never valid
+ * arguments): with them every 32-bit int is a value of the type, so a caller
+ * passing an unknown code through the ABI gets SSC_ERR_INVALID_ARG or
+ * SSC_ERR_UNSUPPORTED (0 from ssc_workspace_bytes) rather than undefined
+ * behaviour. */
+typedef enum {
+  SSC_F32 = 0,
+  SSC_BF16 = 1,
+  SSC_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  SSC_DTYPE_RANGE_MAX_ = 2147483647
+} ssc_dtype;
 
 typedef enum {
   SSC_OP_DENSE_FWD = 0,
@@ -75,7 +85,9 @@ typedef enum {
   SSC_OP_FMAP_BWD = 8,
   SSC_OP_FPS = 9,
   SSC_OP_PERFORMER_FWD = 10,
-  SSC_OP_PERFORMER_BWD = 11
+  SSC_OP_PERFORMER_BWD = 11,
+  SSC_OP_RANGE_MIN_ = -2147483647 - 1,
+  SSC_OP_RANGE_MAX_ = 2147483647
 } ssc_op;
 
 typedef void* ssc_stream; /* hipStream_t */

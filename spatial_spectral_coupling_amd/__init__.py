@@ -39,7 +39,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libssc.so")
+# SSC_LIBRARY selects another build of the library (the debug or the
+# host-sanitized one); by default the in-tree libssc.so.
+library_path = os.environ.get("SSC_LIBRARY") or os.path.join(_HERE, "libssc.so")
 
 (OP_DENSE_FWD, OP_DENSE_BWD, OP_PATCH_TOPK, OP_GEO_FWD, OP_GEO_BWD, OP_LINEAR_FWD, OP_LINEAR_BWD,
  OP_FMAP_FWD, OP_FMAP_BWD, OP_FPS, OP_PERFORMER_FWD, OP_PERFORMER_BWD) = range(12)

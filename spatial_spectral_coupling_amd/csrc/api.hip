@@ -123,6 +123,8 @@ Layout make_layout_bf16(ssc_op op, int n_N, int n_M, int d, int k, int P_N, int 
       L.KbarT = take((size_t)d * P_M * 8);
       L.flag = take(4);
       break;
+    default:  // the other ops have layouts of their own
+      break;
   }
   if (geo) {
     const int rQ = kRowsFwd < kRowsDq ? kRowsFwd : kRowsDq, rK = kRowsDkv;
@@ -188,6 +190,8 @@ Layout make_layout(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k, int P
     case SSC_OP_PATCH_TOPK:
       L.Qbar = take((size_t)P_N * d * 8);
       L.KbarT = take((size_t)d * P_M * 8);
+      break;
+    default:  // the other ops have layouts of their own
       break;
   }
   if (geo) {

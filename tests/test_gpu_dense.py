@@ -248,3 +248,21 @@ def test_autograd_skips_dv_for_a_fixed_basis():
     O2, lse = ssc.coupling_dense_fwd(Q, K, V)
     dQ, dK, _ = ssc.coupling_dense_bwd(Q, K, V, O2, dO, lse, need_dV=False)
     assert torch.equal(Qr.grad, dQ.to(torch.bfloat16)) and torch.equal(Kr.grad, dK.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("nN,nM,d,k", [(300, 40000, 128, 200), (70, 33000, 64, 30), (1, 32897, 128, 200)])
+def test_dense_backward_many_key_blocks(nN, nM, d, k):
+    """More key blocks of 128 rows than one round of 256 workgroups (the
+    dK / dV pass runs in two rounds) with few query rows: one to five query
+    tiles, ragged in both directions."""
+    say("dense bwd many key blocks", nN, nM, d, k)
+    c = gen.make_small(nN, nM, d, k, "bf16", seed=nN + nM)
+    Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+    dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
+    _, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
+    torch.cuda.synchronize()
+    assert dV2 is None and torch.equal(dK2, dK)
+    O_r, lse_r, gr = oracle_dense(c)
+    check_fwd(O.cpu().numpy(), O_r, lse.cpu().numpy(), lse_r, what=f"many blocks {nM}")
+    check_grads((dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()), gr, what=f"many blocks {nM}")
