@@ -264,7 +264,7 @@ def cpu_baseline(c, offN, offM, idx_np, np):
 
 def small_config_record(i, steps, warmup, torch, np, gen, ssc):
     """ms per dense fwd+bwd of the small parity workloads (1k fp32, 5k bf16)."""
-    c = gen.make_config(i)
+    c = gen.cached_config(i)
     dt, d, k, n = c["dtype"], c["d"], c["k"], c["n"]
     Q, K, V, dO = (to_dev(c[x], dt, torch, np) for x in ("Q", "K", "V", "dO"))
     st = {}
@@ -314,7 +314,7 @@ def main():
         b.build()
     torch.cuda.set_device(0)
     log("generating the 60k workload")
-    c = gen.make_config(3)
+    c = gen.cached_config(3)
     n, d, k, sc, s = c["n"], c["d"], c["k"], c["scale"], c["s"]
     dense, geo, offN, offM = prepare(c, torch, np, gen)
     torch.cuda.synchronize()
@@ -475,7 +475,7 @@ def main():
 
     if not args.no_160k and not args.dense_only:
         log("generating the 160k workload")
-        c4 = gen.make_config(4)
+        c4 = gen.cached_config(4)
         _, geo4, offN4, offM4 = prepare(c4, torch, np, gen)
         del _
         st4 = {}

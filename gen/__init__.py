@@ -19,7 +19,12 @@ the readings recorded in the project design notes.
 from __future__ import annotations
 
 import dataclasses
+import hashlib
+import json
 import math
+import os
+import shutil
+import tempfile
 from typing import Dict, Optional
 
 import numpy as np
@@ -40,6 +45,7 @@ __all__ = [
     "fps_partition",
     "patch_sort",
     "make_config",
+    "cached_config",
     "make_small",
 ]
 
@@ -310,6 +316,76 @@ def make_config(i: int, with_partition: Optional[bool] = None) -> dict:
         labN, _, _ = fps_partition(xn, edges, cfg.patches)
         labM, _, _ = fps_partition(xm, edges, cfg.patches)
         out.update(labN=labN, labM=labM, P=cfg.patches, s=cfg.s)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# cached workloads
+# ----------------------------------------------------------------------------
+def _generator_version() -> str:
+    """sha256 of this module's source: any change to the recipe invalidates
+    every cached workload."""
+    with open(os.path.abspath(__file__), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def _sha256_file(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as fh:
+        for chunk in iter(lambda: fh.read(1 << 22), b""):
+            h.update(chunk)
+    return h.hexdigest()
+
+
+def cached_config(i: int, root: Optional[str] = None) -> dict:
+    """make_config(i), kept on disk: root/cfg{i}/ holds one .npy per array
+    and manifest.json (workload name, seed index, generator version = sha256
+    of this module, and per array its file, shape, dtype and sha256).  A
+    cache whose manifest or any file does not match is regenerated.  root
+    defaults to $SSC_DATA_DIR, else data/ next to this package."""
+    cfg = WORKLOADS[i]
+    root = root or os.environ.get("SSC_DATA_DIR") or os.path.join(
+        os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "data")
+    d = os.path.join(root, f"cfg{i}")
+    version = _generator_version()
+    man_path = os.path.join(d, "manifest.json")
+    try:
+        with open(man_path) as fh:
+            man = json.load(fh)
+        if (man.get("generator_version") == version and man.get("config") == cfg.name
+                and man.get("seed_index") == cfg.seed_index):
+            out = dict(man["scalars"])
+            for name, meta in man["arrays"].items():
+                path = os.path.join(d, meta["file"])
+                if _sha256_file(path) != meta["sha256"]:
+                    raise ValueError(f"{path}: checksum mismatch")
+                a = np.load(path, allow_pickle=False)
+                if list(a.shape) != meta["shape"] or str(a.dtype) != meta["dtype"]:
+                    raise ValueError(f"{path}: shape or dtype mismatch")
+                out[name] = a
+            return out
+    except (OSError, ValueError, KeyError, json.JSONDecodeError):
+        pass
+    out = make_config(i)
+    os.makedirs(root, exist_ok=True)
+    tmp = tempfile.mkdtemp(prefix=f"cfg{i}.", dir=root)
+    arrays = {}
+    for name, v in out.items():
+        if isinstance(v, np.ndarray):
+            f = name + ".npy"
+            np.save(os.path.join(tmp, f), v, allow_pickle=False)
+            arrays[name] = {"file": f, "shape": list(v.shape), "dtype": str(v.dtype),
+                            "sha256": _sha256_file(os.path.join(tmp, f))}
+    scalars = {k: (v.item() if isinstance(v, np.generic) else v) for k, v in out.items()
+               if not isinstance(v, np.ndarray)}
+    with open(os.path.join(tmp, "manifest.json"), "w") as fh:
+        json.dump({"config": cfg.name, "index": i, "seed_index": cfg.seed_index,
+                   "generator_version": version, "scalars": scalars, "arrays": arrays}, fh, indent=1)
+    shutil.rmtree(d, ignore_errors=True)
+    try:
+        os.replace(tmp, d)
+    except OSError:  # another process placed its copy first
+        shutil.rmtree(tmp, ignore_errors=True)
     return out
 
 

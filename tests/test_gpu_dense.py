@@ -69,7 +69,7 @@ def test_dense_parity_small(dt, nN, nM, d, k):
 @pytest.mark.parametrize("i", [0, 1])
 def test_dense_workload_parity(i):
     say("dense workload", i)
-    c = gen.make_config(i)
+    c = gen.cached_config(i)
     O, lse, dQ, dK, dV = run_dense(c)
     Or, lser, gr = oracle_dense(c)
     check_fwd(O, Or, lse, lser, what=c["config"])
@@ -150,7 +150,7 @@ def test_dense_60k_full_size_sampled():
     """The 60k workload: sampled rows of O, lse and dQ; dK/dV of a backward
     whose upstream gradient lives on sampled rows; identities at full size."""
     say("dense 60k generate")
-    c = gen.make_config(2)
+    c = gen.cached_config(2)
     dt, sc = c["dtype"], c["scale"]
     Q, K, V, dO = (to_dev(c[x], dt) for x in ("Q", "K", "V", "dO"))
     say("dense 60k fwd+bwd")
@@ -211,7 +211,7 @@ def test_dense_60k_full_size():
     dQ, dK, dV of the workload's own upstream gradient (the oracle runs in
     full-row blocks on the host cores, about half a minute)."""
     say("dense 60k full generate")
-    c = gen.make_config(2)
+    c = gen.cached_config(2)
     say("dense 60k full gpu")
     O, lse, dQ, dK, dV = run_dense(c)
     say("dense 60k full oracle")

@@ -119,6 +119,17 @@ def test_geo_full_selection_equals_dense_on_gpu():
     assert (lse - lsed).abs().max().item() < 3.92e-3
     for a, b in zip(g, gd):
         assert ((a - b).norm() / b.norm()).item() < 1e-2
+    # and each of the two against the dense oracle (full selection = dense
+    # support): geo and dense are pinned to the same exact result, not only
+    # to each other
+    Q, K, V, dO = (f64(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
+    Or, lser = dense_fwd(Q, K, V, c["scale"])
+    gr = dense_bwd(Q, K, V, dO, c["scale"])
+    for tag, Ox, lx, gx in (("geo", O, lse, g), ("dense", Od, lsed, gd)):
+        check_fwd(unsort(Ox.cpu().numpy(), permN), Or, unsort(lx.cpu().numpy(), permN), lser, f"s=P_M {tag}")
+        got = (unsort(gx[0].cpu().numpy(), permN), unsort(gx[1].cpu().numpy(), permM),
+               unsort(gx[2].cpu().numpy(), permM))
+        check_grads(got, gr, f"s=P_M {tag}")
 
 
 def test_geo_empty_and_unselected_patches():
@@ -179,7 +190,7 @@ def test_geo_invalid_selection_fills_nan():
 @pytest.mark.parametrize("i", [3])
 def test_geo_workload_60k_full(i):
     say("geo workload generate", i)
-    c = gen.make_config(i)
+    c = gen.cached_config(i)
     compare_geo(c, c["s"], c["config"])
 
 
@@ -188,7 +199,7 @@ def test_geo_workload_160k_sampled():
     row of 48 sampled target patches; dK, dV of a backward whose upstream
     gradient lives on those patches only."""
     say("geo 160k generate")
-    c = gen.make_config(4)
+    c = gen.cached_config(4)
     s, sc = c["s"], c["scale"]
     dev, permN, permM, P_N, P_M = sorted_problem(c)
     say("geo 160k gpu")
@@ -291,7 +302,7 @@ def test_geo_workload_160k_full():
     """160k, P = 640, s = 16 against the oracle on every target patch: O,
     lse, dQ, dK and dV of the workload's own upstream gradient, all rows."""
     say("geo 160k full generate")
-    c = gen.make_config(4)
+    c = gen.cached_config(4)
     compare_geo(c, c["s"], "160k full")
 
 

@@ -76,7 +76,7 @@ def test_linear_parity_small(nN, nM, d, k):
 
 
 def test_linear_parity_60k():
-    c = gen.make_config(2)
+    c = gen.cached_config(2)
     say("linear 60k", c["n"], c["d"], c["k"])
     check_all(c, "linear 60k")
 

@@ -79,7 +79,7 @@ def test_performer_parity_small(nN, nM, d, k, spread):
 
 
 def test_performer_parity_60k():
-    c = gen.make_config(2)
+    c = gen.cached_config(2)
     say("performer 60k", c["n"], c["d"], c["k"])
     check_all(c, "performer 60k")
 
