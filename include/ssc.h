@@ -94,7 +94,8 @@ typedef void* ssc_stream; /* hipStream_t */
 
 /* Bytes of scratch an entry point needs for these sizes (0 if the sizes are
  * invalid).  Arguments not used by an op are ignored.  For SSC_OP_FPS:
- * n_N = vertex count n, n_M = adjacency length nnz, P_N = seed count P. */
+ * n_N = vertex count n, n_M = adjacency length nnz, P_N = seed count P.
+ * For SSC_OP_PERFORMER_*: P_N = feature count m (0 means m = d). */
 size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, int k,
                            int P_N, int P_M, int s);
 
@@ -244,14 +245,16 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
  *   phi(x)_i = exp(sqrt(scale) W[i] . x - scale |x|^2 / 2) / sqrt(m),
  *   den[i]   = phi(Q[i]) . sum_j phi(K[j]),
  *   O[i, :]  = phi(Q[i]) (sum_j phi(K[j]) V[j, :]) / den[i],
- * with m = d directions W [d x d] bf16 (rows; drawn by the caller) and scale
- * the softmax scale being approximated (e.g. 1/sqrt(d)).  Internally the
- * features are shifted by per-feature and per-row maxima that cancel in the
- * ratio (no overflow).  Outputs O [n_N x k] fp32 and lnden [n_N] = ln den[i]
- * fp32.  bf16 inputs only; d in {64, 128}; 1 <= k <= 255; n_M >= 1; n_N = 0
- * is a no-op.  Q [n_N x d], K [n_M x d], V [n_M x k] bf16.
+ * with m random directions W [m x d] bf16 (rows; drawn by the caller; the
+ * estimator's variance falls as 1/m) and scale the softmax scale being
+ * approximated (e.g. 1/sqrt(d)).  Internally the features are shifted by
+ * per-feature and per-row maxima that cancel in the ratio (no overflow).
+ * Outputs O [n_N x k] fp32 and lnden [n_N] = ln den[i] fp32.  bf16 inputs
+ * only; d and m in {64, 128} (other m: SSC_ERR_UNSUPPORTED); 1 <= k <= 255;
+ * n_M >= 1; n_N = 0 is a no-op.  Q [n_N x d], K [n_M x d], V [n_M x k]
+ * bf16.  ssc_workspace_bytes takes m in its P_N argument (0 means m = d).
  */
-ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, int m,
                                   const void* Q, const void* K, const void* V, const void* W,
                                   float scale, float* O, float* lnden, void* ws, size_t ws_bytes,
                                   ssc_stream stream);
@@ -266,7 +269,7 @@ ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
  *   dV = phi(K) (phi(Q)^T g), and dQ, dK through d phi / dx.
  * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
  */
-ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
+ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, int m,
                                   const void* Q, const void* K, const void* V, const void* W,
                                   float scale, const float* O, const void* dO, const float* lnden,
                                   float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,

@@ -86,8 +86,8 @@ _SIGS = {
     "fmap_solve_fwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fmap_solve_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fps_partition": (_i, [_i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "coupling_performer_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
-    "coupling_performer_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+    "coupling_performer_fwd": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "coupling_performer_bwd": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _sz, _vp]),
 }
 
@@ -508,21 +508,28 @@ def fps_partition(x: torch.Tensor, off: torch.Tensor, adj: torch.Tensor, P: int)
     return seeds, labels, dist
 
 
+def _directions(W, d, dtype):
+    """Feature count m of the Performer directions W [m x d]."""
+    m, _ = _mat(W, "W")
+    _want(W, "W", (m, d), dtype)
+    return m
+
+
 def coupling_performer_fwd(Q, K, V, W, scale: Optional[float] = None):
     """Performer (FAVOR+) coupling: O = phi(Q) (phi(K)^T V) / den and ln den
-    (fp32), with m = d random directions W [d x d] bf16."""
+    (fp32), with m random directions W [m x d] bf16 (m in {64, 128})."""
     code = _same_dtype(Q, K, V, W)
     n_N, d = _mat(Q, "Q")
     n_M, k = _mat(V, "V")
     _want(K, "K", (n_M, d), Q.dtype)
-    _want(W, "W", (d, d), Q.dtype)
+    m = _directions(W, d, Q.dtype)
     dev = _check_dev(Q, K, V, W)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     O = torch.empty(n_N, k, dtype=torch.float32, device=dev)
     lnden = torch.empty(n_N, dtype=torch.float32, device=dev)
-    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_FWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
-    _call("coupling_performer_fwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(lnden), _p(ws),
-          ws.numel(), _stream(dev))
+    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_FWD, code, n_N, n_M, d, k, m, 0, 0), dev)
+    _call("coupling_performer_fwd", code, n_N, n_M, d, k, m, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(lnden),
+          _p(ws), ws.numel(), _stream(dev))
     return O, lnden
 
 
@@ -530,15 +537,15 @@ def coupling_performer_bwd(Q, K, V, W, O, dO, lnden, scale: Optional[float] = No
     """dQ, dK, dV (fp32) of <dO, O> for the Performer coupling (W fixed)."""
     code = _same_dtype(Q, K, V, W, dO)
     n_N, n_M, d, k = _check_bwd_inputs(Q, K, V, O, dO, lnden)
-    _want(W, "W", (d, d), Q.dtype)
+    m = _directions(W, d, Q.dtype)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = _check_dev(Q, K, V, W, O, dO, lnden)
     dQ = torch.empty(n_N, d, dtype=torch.float32, device=dev)
     dK = torch.empty(n_M, d, dtype=torch.float32, device=dev)
     dV = torch.empty(n_M, k, dtype=torch.float32, device=dev)
-    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_BWD, code, n_N, n_M, d, k, 0, 0, 0), dev)
-    _call("coupling_performer_bwd", code, n_N, n_M, d, k, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(dO), _p(lnden),
-          _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
+    ws = _ws(lib().ssc_workspace_bytes(OP_PERFORMER_BWD, code, n_N, n_M, d, k, m, 0, 0), dev)
+    _call("coupling_performer_bwd", code, n_N, n_M, d, k, m, _p(Q), _p(K), _p(V), _p(W), sc, _p(O), _p(dO),
+          _p(lnden), _p(dQ), _p(dK), _p(dV), _p(ws), ws.numel(), _stream(dev))
     return dQ, dK, dV
 
 

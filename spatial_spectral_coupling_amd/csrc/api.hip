@@ -306,6 +306,15 @@ ssc_status check_linear(ssc_dtype t, int n_N, int n_M, int d, int k) {
   return SSC_OK;
 }
 
+// Performer: the linear coupling's shapes, and m in {64, 128} features.
+ssc_status check_performer(ssc_dtype t, int n_N, int n_M, int d, int k, int m) {
+  const ssc_status st = check_linear(t, n_N, n_M, d, k);
+  if (st != SSC_OK) return st;
+  if (m < 1) return SSC_ERR_INVALID_ARG;
+  if (m != 64 && m != 128) return SSC_ERR_UNSUPPORTED;
+  return SSC_OK;
+}
+
 struct LinLayout {
   size_t part = kNone, M = kNone, MT = kNone, dM = kNone, dMT = kNone, rden = kNone, s = kNone;
   size_t total = 0;
@@ -346,9 +355,10 @@ struct PfLayout {
   int nblk_M = 0;
 };
 
-PfLayout make_pf_layout(bool bwd, int n_N, int n_M, int d, int k) {
+// m features per row: the linear kernels run on feature rows of width m.
+PfLayout make_pf_layout(bool bwd, int n_N, int n_M, int m, int k) {
   PfLayout L;
-  L.lin = make_lin_layout(bwd, n_N, n_M, d, k);
+  L.lin = make_lin_layout(bwd, n_N, n_M, m, k);
   L.nblk_M = (n_M + 127) / 128;
   size_t o = L.lin.total;
   auto take = [&](size_t bytes) {
@@ -356,11 +366,11 @@ PfLayout make_pf_layout(bool bwd, int n_N, int n_M, int d, int k) {
     o = round_up(o + bytes, 256);
     return at_;
   };
-  L.part = take((size_t)L.nblk_M * d * 4);
-  L.M2 = take((size_t)d * 4);
-  L.FQ = take((size_t)n_N * d * 2);
-  L.FK = take((size_t)n_M * d * 2);
-  const size_t mat = (size_t)d * kpad_lin(k) * 2;
+  L.part = take((size_t)L.nblk_M * m * 4);
+  L.M2 = take((size_t)m * 4);
+  L.FQ = take((size_t)n_N * m * 2);
+  L.FK = take((size_t)n_M * m * 2);
+  const size_t mat = (size_t)m * kpad_lin(k) * 2;
   L.Mlo = take(mat);
   L.MTlo = take(mat);
   if (bwd) {
@@ -371,8 +381,8 @@ PfLayout make_pf_layout(bool bwd, int n_N, int n_M, int d, int k) {
     L.rowoff = take((size_t)n_N * 4);
   } else {
     L.den = take((size_t)n_N * 4);
-    L.dFQ = take((size_t)n_N * d * 4);
-    L.dFK = take((size_t)n_M * d * 4);
+    L.dFQ = take((size_t)n_N * m * 4);
+    L.dFK = take((size_t)n_M * m * 4);
   }
   L.total = o;
   return L;
@@ -482,9 +492,11 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
       if (check_fmap(dtype, n_N, k) != SSC_OK) return 0;
       return make_fm_layout(op == SSC_OP_FMAP_BWD, n_N, k).total;
     case SSC_OP_PERFORMER_FWD:
-    case SSC_OP_PERFORMER_BWD:
-      if (check_linear(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
-      return make_pf_layout(op == SSC_OP_PERFORMER_BWD, n_N, n_M, d, k).total;
+    case SSC_OP_PERFORMER_BWD: {
+      const int m = P_N == 0 ? d : P_N;  // P_N carries the feature count m
+      if (check_performer(dtype, n_N, n_M, d, k, m) != SSC_OK) return 0;
+      return make_pf_layout(op == SSC_OP_PERFORMER_BWD, n_N, n_M, m, k).total;
+    }
     case SSC_OP_FPS:
       if (check_fps(n_N, n_M, P_N) != SSC_OK) return 0;
       return make_fps_layout(n_N, n_M).total;
@@ -1064,67 +1076,68 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
 }
 
 // The key maxima and the key / query features of the Performer coupling.
-static ssc_status pf_features(int d, const PfLayout& L, void* ws, int n_N, int n_M, const void* Q, const void* K,
-                       const void* W, float scale, int qmode, float* rowoff, const float* lnden, float* den,
-                       hipStream_t s) {
+static ssc_status pf_features(int d, int m, const PfLayout& L, void* ws, int n_N, int n_M, const void* Q,
+                              const void* K, const void* W, float scale, int qmode, float* rowoff,
+                              const float* lnden, float* den, hipStream_t s) {
   PfArgs p{};
   p.W = W; p.scale = scale; p.part = at<float>(ws, L.part); p.M2 = at<float>(ws, L.M2);
   p.X = K; p.n = n_M; p.nblk = L.nblk_M; p.F = at<bf16>(ws, L.FK);
-  SSC_TRY(launch_pf_feat(d, 0, p, s));
-  SSC_TRY(launch_pf_maxreduce(d, p, s));
-  SSC_TRY(timed("pf_feat", s, [&] { return launch_pf_feat(d, 1, p, s); }));
+  SSC_TRY(launch_pf_feat(d, m, 0, p, s));
+  SSC_TRY(launch_pf_maxreduce(m, p, s));
+  SSC_TRY(timed("pf_feat", s, [&] { return launch_pf_feat(d, m, 1, p, s); }));
   p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.rowoff = rowoff; p.lnden = lnden; p.den = den;
-  SSC_TRY(launch_pf_feat(d, qmode, p, s));
+  SSC_TRY(launch_pf_feat(d, m, qmode, p, s));
   return SSC_OK;
 }
 
-ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
-                                  const void* V, const void* W, float scale, float* O, float* lnden, void* ws,
-                                  size_t ws_bytes, ssc_stream stream) {
-  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, int m, const void* Q,
+                                  const void* K, const void* V, const void* W, float scale, float* O, float* lnden,
+                                  void* ws, size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_performer(dtype, n_N, n_M, d, k, m);
   if (st != SSC_OK) return st;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SSC_ERR_INVALID_ARG;
   if (n_N == 0) return SSC_OK;
   if (!all_ok({Q, K, V, W, O, lnden})) return SSC_ERR_INVALID_ARG;
-  const PfLayout L = make_pf_layout(false, n_N, n_M, d, k);
+  const PfLayout L = make_pf_layout(false, n_N, n_M, m, k);
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
   const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
-  const Buf bW{W, (size_t)d * d * 2};
+  const Buf bW{W, (size_t)m * d * 2};
   const Buf bO{O, (size_t)n_N * k * 4}, bd{lnden, (size_t)n_N * 4}, bw{ws, ws_bytes};
   if (!disjoint({bO, bd, bw}, {bQ, bK, bV, bW})) return SSC_ERR_INVALID_ARG;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* rowoff = at<float>(ws, L.rowoff);
-  st = pf_features(d, L, ws, n_N, n_M, Q, K, W, scale, 2, rowoff, nullptr, nullptr, s);
+  st = pf_features(d, m, L, ws, n_N, n_M, Q, K, W, scale, 2, rowoff, nullptr, nullptr, s);
   if (st != SSC_OK) return st;
+  // the linear coupling on the m-wide feature rows
   const int KP = kpad_lin(k);
   LinArgs a{};
   a.Q = at<bf16>(ws, L.FQ); a.K = at<bf16>(ws, L.FK); a.V = V; a.O = O; a.den = lnden; a.rowoff = rowoff;
   a.part = at<float>(ws, L.lin.part); a.M = at<char>(ws, L.lin.M); a.MT = at<char>(ws, L.lin.MT);
   a.Mlo = at<char>(ws, L.Mlo); a.MTlo = at<char>(ws, L.MTlo);
   a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(d, KP, 0, true, a, L.lin.parts_M, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
+  SSC_TRY(launch_lin_gram(m, KP, 0, true, a, L.lin.parts_M, s));
+  SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
                             at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
-  SSC_TRY(launch_lin_apply(d, KP, 0, true, a, s));
+  SSC_TRY(launch_lin_apply(m, KP, 0, true, a, s));
   return SSC_OK;
 }
 
-ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, const void* Q, const void* K,
-                                  const void* V, const void* W, float scale, const float* O, const void* dO,
-                                  const float* lnden, float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
-                                  ssc_stream stream) {
-  ssc_status st = check_linear(dtype, n_N, n_M, d, k);
+ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, int m, const void* Q,
+                                  const void* K, const void* V, const void* W, float scale, const float* O,
+                                  const void* dO, const float* lnden, float* dQ, float* dK, float* dV, void* ws,
+                                  size_t ws_bytes, ssc_stream stream) {
+  ssc_status st = check_performer(dtype, n_N, n_M, d, k, m);
   if (st != SSC_OK) return st;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SSC_ERR_INVALID_ARG;
   if (n_N == 0) return SSC_OK;
   if (!all_ok({Q, K, V, W, O, dO, lnden, dQ, dK, dV})) return SSC_ERR_INVALID_ARG;
-  const PfLayout L = make_pf_layout(true, n_N, n_M, d, k);
+  const PfLayout L = make_pf_layout(true, n_N, n_M, m, k);
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
   const Buf bQ{Q, (size_t)n_N * d * 2}, bK{K, (size_t)n_M * d * 2}, bV{V, (size_t)n_M * k * 2};
-  const Buf bW{W, (size_t)d * d * 2}, bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * 2};
+  const Buf bW{W, (size_t)m * d * 2}, bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * 2};
   const Buf bd{lnden, (size_t)n_N * 4};
   const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
   const Buf bw{ws, ws_bytes};
@@ -1132,7 +1145,7 @@ ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* den = at<float>(ws, L.den);
-  st = pf_features(d, L, ws, n_N, n_M, Q, K, W, scale, 3, nullptr, lnden, den, s);
+  st = pf_features(d, m, L, ws, n_N, n_M, Q, K, W, scale, 3, nullptr, lnden, den, s);
   if (st != SSC_OK) return st;
   const int KP = kpad_lin(k);
   LinArgs a{};
@@ -1144,22 +1157,22 @@ ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
   a.dMTlo = at<char>(ws, L.dMTlo);
   a.dQ = at<float>(ws, L.dFQ); a.dK = at<float>(ws, L.dFK); a.dV = dV;
   a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(d, KP, 0, true, a, L.lin.parts_M, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
+  SSC_TRY(launch_lin_gram(m, KP, 0, true, a, L.lin.parts_M, s));
+  SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
                             at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
   SSC_TRY(launch_lin_rowprep(a, s));
-  SSC_TRY(launch_lin_apply(d, KP, 1, true, a, s));
-  SSC_TRY(launch_lin_gram(d, KP, 1, true, a, L.lin.parts_N, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.lin.parts_N, at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT),
+  SSC_TRY(launch_lin_apply(m, KP, 1, true, a, s));
+  SSC_TRY(launch_lin_gram(m, KP, 1, true, a, L.lin.parts_N, s));
+  SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_N, at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT),
                             at<char>(ws, L.dMlo), at<char>(ws, L.dMTlo), s));
-  SSC_TRY(launch_lin_apply(d, KP, 2, true, a, s));
-  SSC_TRY(launch_lin_apply(d, KP, 3, true, a, s));
+  SSC_TRY(launch_lin_apply(m, KP, 2, true, a, s));
+  SSC_TRY(launch_lin_apply(m, KP, 3, true, a, s));
   PfArgs p{};
   p.W = W; p.scale = scale;
   p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.dF = at<float>(ws, L.dFQ); p.dX = dQ;
-  SSC_TRY(launch_pf_dx(d, 0, p, s));
+  SSC_TRY(launch_pf_dx(d, m, 0, p, s));
   p.X = K; p.n = n_M; p.F = at<bf16>(ws, L.FK); p.dF = at<float>(ws, L.dFK); p.dX = dK;
-  SSC_TRY(launch_pf_dx(d, 1, p, s));
+  SSC_TRY(launch_pf_dx(d, m, 1, p, s));
   return SSC_OK;
 }
 

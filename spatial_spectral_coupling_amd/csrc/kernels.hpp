@@ -242,24 +242,25 @@ struct LinArgs {
 // Performer (FAVOR+) coupling pieces (performer.hip); m = D random features.
 struct PfArgs {
   const void* X;        // [n x D] bf16 rows (Q or K)
-  const void* W;        // [D x D] bf16 random directions (rows)
+  const void* W;        // [M x D] bf16 random directions (rows), M features
   int n, nblk;          // rows; row blocks of 128
   float scale;          // softmax scale c (the features use sqrt(c))
-  float* part;          // [nblk x D] per-block key maxima of the exponents (log2 units)
-  float* M2;            // [D] per-feature key maximum (log2 units)
-  bf16* F;              // [n x D] shifted features exp(...) (output of the feature passes)
+  float* part;          // [nblk x M] per-block key maxima of the exponents (log2 units)
+  float* M2;            // [M] per-feature key maximum (log2 units)
+  bf16* F;              // [n x M] shifted features exp(...) (output of the feature passes)
   float* rowoff;        // [n] queries, forward: ln den - ln(den of the shifted features)
   const float* lnden;   // [n] queries, backward: ln den from the forward
   float* den;           // [n] queries, backward: den of the shifted features
-  const float* dF;      // [n x D] gradient w.r.t. the shifted features (pf_dx)
+  const float* dF;      // [n x M] gradient w.r.t. the shifted features (pf_dx)
   float* dX;            // [n x D] gradient w.r.t. the rows (pf_dx output)
 };
 // mode 0: key maxima, 1: key features, 2: query features + rowoff,
 // 3: query features + den from lnden
-hipError_t launch_pf_feat(int D, int mode, const PfArgs& a, hipStream_t st);
-hipError_t launch_pf_maxreduce(int D, const PfArgs& a, hipStream_t st);
+// D = d, M = m in {64, 128}
+hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st);
+hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st);
 // mode 0: queries (no row-sum term), 1: keys
-hipError_t launch_pf_dx(int D, int mode, const PfArgs& a, hipStream_t st);
+hipError_t launch_pf_dx(int D, int M, int mode, const PfArgs& a, hipStream_t st);
 
 // Functional-map solve after the coupling (fmap.hip): C = (Phi^T Phi)^-1 Phi^T O
 // and its backward dO = Phi (Phi^T Phi)^-1 dC.

@@ -5,7 +5,8 @@
 //     phi(x)_i = exp(sqrt(c) w_i . x - c |x|^2 / 2) / sqrt(m),
 //     O_q = phi(q) (sum_j phi(k_j) v_j^T) / (phi(q) . sum_j phi(k_j)),
 //
-// with c the softmax scale and m = D directions w_i (rows of W, an input).
+// with c the softmax scale and m directions w_i (rows of W [m x d], an
+// input; m, d in {64, 128}).
 // The ratio is unchanged when phi_i(k) is multiplied by e^{-M_i} for every
 // key and phi_i(q) by e^{M_i - M_q}: the kernels use M_i = max_j of key j's
 // exponent for feature i and M_q = the largest shifted query exponent of
@@ -48,26 +49,27 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
   return r;
 }
 
-// W [D x D] bf16 (row-major, global) into LDS with the padded pitch.
-template <int D>
+// W [M x D] bf16 (row-major, global) into LDS with the padded pitch.
+template <int D, int M>
 __device__ __forceinline__ void stage_w(char* lds, const bf16* W, int tid) {
   constexpr int CW = D / 8;
-  for (int ch = tid; ch < D * CW; ch += 256) {
+  for (int ch = tid; ch < M * CW; ch += 256) {
     const int r = ch / CW, c = ch - r * CW;
     *reinterpret_cast<bf16x8*>(lds + r * Geo<D>::PITCH + c * 16) =
         *reinterpret_cast<const bf16x8*>(W + (size_t)r * D + c * 8);
   }
 }
 
-template <int D, int MODE>
+// D: row width d; M: feature count m.
+template <int D, int M, int MODE>
 __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
-  __shared__ __attribute__((aligned(16))) char Ws[D * Geo<D>::PITCH];
-  __shared__ float sred[MODE == 0 ? 4 * D : D];
+  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
+  __shared__ float sred[MODE == 0 ? 4 * M : M];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  stage_w<D>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
+  stage_w<D, M>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
   if (MODE != 0)
-    for (int f = tid; f < D; f += 256) sred[f] = a.M2[f];
+    for (int f = tid; f < M; f += 256) sred[f] = a.M2[f];
   const int row = blockIdx.x * kRows + wave * 32 + l32;
   const bool row_ok = row < a.n;
   const bf16* X = reinterpret_cast<const bf16*>(a.X) + (size_t)(row_ok ? row : 0) * D;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     s_sq[wave * 32 + l32] = row_ok ? sq2 : INFINITY;
     __syncthreads();
 #pragma unroll
-    for (int fb = 0; fb < D / 32; ++fb) {
+    for (int fb = 0; fb < M / 32; ++fb) {
       f32x16 c = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) c = mma(xf[cc], rw.read(Ws, fb, cc), c);
@@ -104,19 +106,19 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, sig2 * c[i] - s_sq[wave * 32 + c_row(i, h)]);
       m = fmaxf(m, __shfl_xor(m, 32, 64));
-      if (h == 0) sred[wave * D + fb * 32 + l32] = m;
+      if (h == 0) sred[wave * M + fb * 32 + l32] = m;
     }
     __syncthreads();
-    for (int f = tid; f < D; f += 256)
-      a.part[(size_t)blockIdx.x * D + f] =
-          fmaxf(fmaxf(sred[f], sred[D + f]), fmaxf(sred[2 * D + f], sred[3 * D + f]));
+    for (int f = tid; f < M; f += 256)
+      a.part[(size_t)blockIdx.x * M + f] =
+          fmaxf(fmaxf(sred[f], sred[M + f]), fmaxf(sred[2 * M + f], sred[3 * M + f]));
     return;
   }
 
   __syncthreads();
-  f32x16 acc[D / 32];
+  f32x16 acc[M / 32];
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb) {
+  for (int fb = 0; fb < M / 32; ++fb) {
     acc[fb] = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) acc[fb] = mma(rw.read(Ws, fb, cc), xf[cc], acc[fb]);
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     // u = s + M_i; M_q = max over the row's features (both lane halves)
     float m = -INFINITY;
 #pragma unroll
-    for (int fb = 0; fb < D / 32; ++fb)
+    for (int fb = 0; fb < M / 32; ++fb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         acc[fb][i] = sig2 * acc[fb][i] + sred[fb * 32 + c_row(i, h)];
@@ -137,14 +139,14 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     mq = fmaxf(m, __shfl_xor(m, 32, 64));
   } else {
 #pragma unroll
-    for (int fb = 0; fb < D / 32; ++fb)
+    for (int fb = 0; fb < M / 32; ++fb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[fb][i] = sig2 * acc[fb][i] - sq2 - sred[fb * 32 + c_row(i, h)];
   }
   if (!row_ok) return;
-  bf16* F = a.F + (size_t)row * D;
+  bf16* F = a.F + (size_t)row * M;
 #pragma unroll
-  for (int fb = 0; fb < D / 32; ++fb)
+  for (int fb = 0; fb < M / 32; ++fb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bf16x4 o;
@@ -153,18 +155,18 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
       *reinterpret_cast<bf16x4*>(F + fb * 32 + 8 * q + 4 * h) = o;
     }
   if (MODE >= 2 && h == 0) {
-    const float off = (mq - sq2) * kLn2 - __logf((float)D);
+    const float off = (mq - sq2) * kLn2 - __logf((float)M);
     if (MODE == 2) a.rowoff[row] = off;
     else a.den[row] = __expf(a.lnden[row] - off);
   }
 }
 
-// One workgroup per feature: the block maxima in parallel, then a tree.
-__global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int D) {
+// One workgroup per feature (M of them): the block maxima in parallel, then a tree.
+__global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int M) {
   __shared__ float sm[4];
   const int f = blockIdx.x, tid = threadIdx.x;
   float m = -INFINITY;
-  for (int b = tid; b < a.nblk; b += 256) m = fmaxf(m, a.part[(size_t)b * D + f]);
+  for (int b = tid; b < a.nblk; b += 256) m = fmaxf(m, a.part[(size_t)b * M + f]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if ((tid & 63) == 0) sm[tid >> 6] = m;
@@ -175,25 +177,25 @@ __global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int D) {
 // dX = sqrt(c) (dF o F) W  -  [keys] c x rowsum(dF o F).  A wave owns 32 rows;
 // W^T enters as transposed LDS reads (A operand: output dimension x feature),
 // so a lane's G fragment takes the features kc*16 + {4h..4h+3, 8+4h..8+4h+3}.
-template <int D, int MODE>
+template <int D, int M, int MODE>
 __global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
-  __shared__ __attribute__((aligned(16))) char Ws[D * Geo<D>::PITCH];
+  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  stage_w<D>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
+  stage_w<D, M>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
   const int row = blockIdx.x * kRows + wave * 32 + l32;
   const bool row_ok = row < a.n;
-  const size_t r = (size_t)(row_ok ? row : 0) * D;
-  bf16x8 gh[D / 16], gl[D / 16];
+  const size_t r = (size_t)(row_ok ? row : 0) * D, rf = (size_t)(row_ok ? row : 0) * M;
+  bf16x8 gh[M / 16], gl[M / 16];
   float rs = 0.f;
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < M / 16; ++kc) {
     float hi[8], lo[8];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int f0 = kc * 16 + 8 * p + 4 * h;
-      const f32x4 df = *reinterpret_cast<const f32x4*>(a.dF + r + f0);
-      const bf16x4 fv = *reinterpret_cast<const bf16x4*>(a.F + r + f0);
+      const f32x4 df = *reinterpret_cast<const f32x4*>(a.dF + rf + f0);
+      const bf16x4 fv = *reinterpret_cast<const bf16x4*>(a.F + rf + f0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float g = row_ok ? df[e] * (float)fv[e] : 0.f;
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
   for (int db = 0; db < D / 32; ++db) {
     acc[db] = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
+    for (int kc = 0; kc < M / 16; ++kc) {
       const bf16x8 w = tw.frag(Ws, db, kc);
       acc[db] = mma(w, gh[kc], acc[db]);
       acc[db] = mma(w, gl[kc], acc[db]);
@@ -245,35 +247,35 @@ __global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
 
 }  // namespace pf
 
-#define SSC_PF_INSTANCES(X) X(128) X(64)
+#define SSC_PF_INSTANCES(X) X(128, 128) X(128, 64) X(64, 64) X(64, 128)
 
-hipError_t launch_pf_feat(int D, int mode, const PfArgs& a, hipStream_t st) {
+hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
   const int grid = (a.n + pf::kRows - 1) / pf::kRows;
-#define SSC_L(DD)                                                                                  \
-  if (D == DD) {                                                                                   \
-    if (mode == 0) hipLaunchKernelGGL((pf::pf_feat<DD, 0>), dim3(grid), dim3(256), 0, st, a);      \
-    else if (mode == 1) hipLaunchKernelGGL((pf::pf_feat<DD, 1>), dim3(grid), dim3(256), 0, st, a); \
-    else if (mode == 2) hipLaunchKernelGGL((pf::pf_feat<DD, 2>), dim3(grid), dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((pf::pf_feat<DD, 3>), dim3(grid), dim3(256), 0, st, a);                \
-    return hipGetLastError();                                                                      \
+#define SSC_L(DD, MM)                                                                                        \
+  if (D == DD && M == MM) {                                                                                  \
+    if (mode == 0) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);           \
+    else if (mode == 1) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 1>), dim3(grid), dim3(256), 0, st, a);      \
+    else if (mode == 2) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 2>), dim3(grid), dim3(256), 0, st, a);      \
+    else hipLaunchKernelGGL((pf::pf_feat<DD, MM, 3>), dim3(grid), dim3(256), 0, st, a);                     \
+    return hipGetLastError();                                                                                \
   }
   SSC_PF_INSTANCES(SSC_L)
 #undef SSC_L
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_pf_maxreduce(int D, const PfArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(pf::pf_maxreduce, dim3(D), dim3(256), 0, st, a, D);
+hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(pf::pf_maxreduce, dim3(M), dim3(256), 0, st, a, M);
   return hipGetLastError();
 }
 
-hipError_t launch_pf_dx(int D, int mode, const PfArgs& a, hipStream_t st) {
+hipError_t launch_pf_dx(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
   const int grid = (a.n + pf::kRows - 1) / pf::kRows;
-#define SSC_L(DD)                                                                            \
-  if (D == DD) {                                                                             \
-    if (mode == 0) hipLaunchKernelGGL((pf::pf_dx<DD, 0>), dim3(grid), dim3(256), 0, st, a);  \
-    else hipLaunchKernelGGL((pf::pf_dx<DD, 1>), dim3(grid), dim3(256), 0, st, a);            \
-    return hipGetLastError();                                                                \
+#define SSC_L(DD, MM)                                                                                  \
+  if (D == DD && M == MM) {                                                                            \
+    if (mode == 0) hipLaunchKernelGGL((pf::pf_dx<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);        \
+    else hipLaunchKernelGGL((pf::pf_dx<DD, MM, 1>), dim3(grid), dim3(256), 0, st, a);                  \
+    return hipGetLastError();                                                                          \
   }
   SSC_PF_INSTANCES(SSC_L)
 #undef SSC_L

@@ -233,12 +233,22 @@ def test_performer_validation(L):
         w(ssc.OP_PERFORMER_FWD, BF16, 60000, 60000, 128, 200, 0, 0, 0) > 60000 * 128 * 4
     assert w(ssc.OP_PERFORMER_FWD, BF16, 10, 10, 96, 200, 0, 0, 0) == 0     # d unsupported
     assert w(ssc.OP_PERFORMER_FWD, BF16, 10, 10, 128, 256, 0, 0, 0) == 0    # no normaliser column
+    # the feature count m rides in P_N (0 = d): fewer features, less workspace
+    assert w(ssc.OP_PERFORMER_FWD, BF16, 1000, 1000, 128, 200, 128, 0, 0) == \
+        w(ssc.OP_PERFORMER_FWD, BF16, 1000, 1000, 128, 200, 0, 0, 0)
+    assert 0 < w(ssc.OP_PERFORMER_BWD, BF16, 1000, 1000, 128, 200, 64, 0, 0) < \
+        w(ssc.OP_PERFORMER_BWD, BF16, 1000, 1000, 128, 200, 128, 0, 0)
+    assert w(ssc.OP_PERFORMER_FWD, BF16, 1000, 1000, 64, 200, 128, 0, 0) > 0  # m > d
+    assert w(ssc.OP_PERFORMER_FWD, BF16, 10, 10, 128, 200, 96, 0, 0) == 0     # m unsupported
     ws = A[8]
 
-    def fwd(dt=BF16, nN=64, nM=64, d=128, k=200, scale=0.1, O=A[4], lnden=A[5], wsb=1 << 30):
-        return L.coupling_performer_fwd(dt, nN, nM, d, k, A[0], A[1], A[2], A[3], scale, O, lnden, ws, wsb, None)
+    def fwd(dt=BF16, nN=64, nM=64, d=128, k=200, m=128, scale=0.1, O=A[4], lnden=A[5], wsb=1 << 30):
+        return L.coupling_performer_fwd(dt, nN, nM, d, k, m, A[0], A[1], A[2], A[3], scale, O, lnden, ws, wsb, None)
     assert fwd(dt=F32) == UNSUPPORTED
     assert fwd(d=96) == UNSUPPORTED
+    assert fwd(m=96) == UNSUPPORTED
+    assert fwd(m=256) == UNSUPPORTED
+    assert fwd(m=0) == INVALID
     assert fwd(nM=0) == INVALID
     assert fwd(scale=0.0) == INVALID
     assert fwd(scale=-1.0) == INVALID
@@ -247,8 +257,8 @@ def test_performer_validation(L):
     assert fwd(nN=0) == OK                                          # nothing to do
 
     def bwd(dQ=A[6], wsb=1 << 30):
-        return L.coupling_performer_bwd(BF16, 64, 64, 128, 200, A[0], A[1], A[2], A[3], 0.1, A[4], A[9], A[5], dQ,
-                                        A[7], A[10], ws, wsb, None)
+        return L.coupling_performer_bwd(BF16, 64, 64, 128, 200, 128, A[0], A[1], A[2], A[3], 0.1, A[4], A[9], A[5],
+                                        dQ, A[7], A[10], ws, wsb, None)
     assert bwd(wsb=64) == WORKSPACE
     assert bwd(dQ=A[0]) == INVALID                                  # gradient aliases Q
 

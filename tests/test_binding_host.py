@@ -104,7 +104,7 @@ def test_linear_performer_fmap_checks():
     with pytest.raises(ValueError, match="W must"):
         ssc.coupling_performer_fwd(Q, K, V, z(128, 64))
     with pytest.raises(ValueError, match="W must"):
-        ssc.coupling_performer_bwd(Q, K, V, z(64, 128), O, dO, den)
+        ssc.coupling_performer_bwd(Q, K, V, z(64, 96), O, dO, den)
     with pytest.raises(ValueError, match="O must"):
         ssc.fmap_solve_fwd(z(50, 200), z(50, 199, dtype=F32))
     with pytest.raises(TypeError, match="dC must"):

@@ -32,9 +32,9 @@ def run(c, Wb, scale):
     return [t.cpu().numpy() for t in (O, lnden, dQ, dK, dV)]
 
 
-def check_all(c, what, wseed=0):
+def check_all(c, what, wseed=0, m=None):
     d = c["d"]
-    Wb = gen.make_favor_directions(d, d, seed=wseed)
+    Wb = gen.make_favor_directions(d if m is None else m, d, seed=wseed)
     scale = 1.0 / np.sqrt(d)
     O, lnden, dQ, dK, dV = run(c, Wb, scale)
     Q, K, V, dO = (f64(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
@@ -76,6 +76,17 @@ def test_performer_parity_small(nN, nM, d, k, spread):
     say("performer small", nN, nM, d, k, spread)
     c = gen.make_small(nN, nM, d, k, "bf16", seed=5 * nN + nM, spread=spread)
     check_all(c, f"performer {nN}x{nM} d{d} k{k} spread{spread}", wseed=nN)
+
+
+@pytest.mark.parametrize("nN,nM,d,k,m", [(300, 517, 128, 200, 64), (260, 700, 64, 128, 128),
+                                         (129, 1000, 64, 30, 64), (400, 600, 128, 200, 64)])
+def test_performer_feature_count(nN, nM, d, k, m):
+    """m random features other than d (fewer, or more than the row width):
+    the directions W are m x d and every output matches the oracle's
+    estimator with the same W."""
+    say("performer m", nN, nM, d, k, m)
+    c = gen.make_small(nN, nM, d, k, "bf16", seed=7 * nN + nM + m)
+    check_all(c, f"performer {nN}x{nM} d{d} k{k} m{m}", wseed=m, m=m)
 
 
 def test_performer_parity_60k():
