@@ -165,9 +165,9 @@ def gpu_clocks():
         return None
 
 
+# the dK/dV kernel's own sources (its code, tile machinery and constants)
 KERNEL_SOURCES = ("spatial_spectral_coupling_amd/csrc/attn_bf16_kv.hip", "spatial_spectral_coupling_amd/csrc/tile_bf16.hpp",
-                  "spatial_spectral_coupling_amd/csrc/common.hpp", "spatial_spectral_coupling_amd/csrc/kernels.hpp",
-                  "spatial_spectral_coupling_amd/csrc/api.hip")
+                  "spatial_spectral_coupling_amd/csrc/common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkv_bf16_60k_traffic.md")
 
 

@@ -599,11 +599,11 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
       SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, grid, s); }));
       return SSC_OK;
     }
-    // wave-specialised pass with the bounded reference, then the one-wave
+    // paired-wave pass with the bounded reference, then the one-wave
     // kernel on the workgroups whose row sums underflowed (none, normally:
     // those workgroups exit at once)
     a.fallback_out = at<int>(ws, L.fallback);
-    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_ws(d, KPf, a, grid, s); }));
+    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_pair(d, KPf, a, grid, s); }));
     a.fallback = a.fallback_out;
     SSC_TRY(launch_fwd_bf16(d, KPf, ones, a, grid, s));
     return SSC_OK;

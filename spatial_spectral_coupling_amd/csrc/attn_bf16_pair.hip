@@ -346,7 +346,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // The paired forward needs a spare padded column for the row sums (k < KP);
 // KP = 256 with k = 256 uses fwd_bf16 directly.
-hipError_t launch_fwd_ws(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
+hipError_t launch_fwd_pair(int D, int KP, const FwdArgs& a, int grid, hipStream_t st) {
 #define SSC_L(DD, KK)                                                                          \
   if (D == DD && KP == KK) {                                                                   \
     hipLaunchKernelGGL((tb::fwd_pair<DD, KK>), dim3(grid), dim3(512), 0, st, a);               \

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // gathered key rows missing from a tile read the sentinel row n_M + 1
   // (past the end of K and of the padded V)
   if (!GEO) {
-    // after the wave-specialised forward: only the workgroups it marked
+    // after the paired-wave forward: only the workgroups it marked
     if (VT && a.fallback != nullptr && a.fallback[blockIdx.x] == 0) return;
     q_begin = blockIdx.x * (NW * 32);
     q_end = a.n_N;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // mode 0: bounded reference; 1: running reference (when the bound left a
   // row sum below 2^-60, i.e. the bound was far above the scores); 2: the
   // exact row maxima of mode 1 as a fixed reference.  A workgroup redone
-  // after the wave-specialised forward (which ran mode 0) starts in mode 1.
+  // after the paired-wave forward (which ran mode 0) starts in mode 1.
   int mode = (!GEO && VT && a.fallback != nullptr) ? 1 : 0;
 
   constexpr int NS = D / 16, NCB = KP / 32, NPV = 2 * NCB;

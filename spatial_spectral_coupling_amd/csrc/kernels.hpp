@@ -78,8 +78,8 @@ struct FwdArgs {
   // dense bf16: V grouped-transposed, [groupsVt][KP][16] (row k = ones)
   const void* Vt;
   int groupsVt;
-  // dense bf16, wave-specialised forward: per 128-row workgroup, 1 where a
-  // row sum underflowed against the bounded reference (fwd_ws writes every
+  // dense bf16, paired-wave forward: per 128-row workgroup, 1 where a
+  // row sum underflowed against the bounded reference (fwd_pair writes every
   // entry); fwd_bf16 given `fallback` redoes exactly those workgroups
   int* fallback_out;
   const int* fallback;
@@ -308,8 +308,8 @@ hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStr
 // ones: column k of the padded V holds ones (k < KP); KP = 256 also runs
 // without (k = 256)
 hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st);
-// wave-specialised dense forward (8 waves, 128 rows a workgroup; needs k < KP)
-hipError_t launch_fwd_ws(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+// paired-wave dense forward (8 waves, 128 rows a workgroup; needs k < KP)
+hipError_t launch_fwd_pair(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
 // dcol: V carries two ones columns and dO the high / low parts of -D there
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);

@@ -51,6 +51,10 @@ SHAPES = [
     # forward with its ones column, backward without spare columns (k = 255)
     ("bf16", 150, 170, 128, 223),
     ("bf16", 190, 210, 64, 255),
+    # the remaining padded widths of the paired forward: kp 64 at d = 128,
+    # kp 224 at d = 64
+    ("bf16", 150, 170, 128, 40),
+    ("bf16", 140, 230, 64, 200),
     ("f32", 300, 517, 64, 30),
     ("f32", 150, 260, 128, 128),
 ]
