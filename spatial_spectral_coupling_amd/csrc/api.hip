@@ -599,11 +599,19 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
       SSC_TRY(timed("fwd", s, [&] { return launch_fwd_bf16(d, KPf, ones, a, grid, s); }));
       return SSC_OK;
     }
-    // paired-wave pass with the bounded reference, then the one-wave
-    // kernel on the workgroups whose row sums underflowed (none, normally:
-    // those workgroups exit at once)
+    // a pass with the bounded reference, then the one-wave kernel on the
+    // 128-row blocks whose row sums underflowed (none, normally: those
+    // workgroups exit at once).  The wide-wave pass (256 rows a workgroup)
+    // moves half the data per product; below 128 of its workgroups the
+    // paired-wave pass (128 rows) fills more of the chip, and only it has
+    // the kp = 256 instances.
     a.fallback_out = at<int>(ws, L.fallback);
-    SSC_TRY(timed("fwd", s, [&] { return launch_fwd_pair(d, KPf, a, grid, s); }));
+    const int gw = (n_N + 255) / 256;
+    if (KPf <= 224 && gw >= kWideMinWGs) {
+      SSC_TRY(timed("fwd", s, [&] { return launch_fwd_wide(d, KPf, a, gw, s); }));
+    } else {
+      SSC_TRY(timed("fwd", s, [&] { return launch_fwd_pair(d, KPf, a, grid, s); }));
+    }
     a.fallback = a.fallback_out;
     SSC_TRY(launch_fwd_bf16(d, KPf, ones, a, grid, s));
     return SSC_OK;

@@ -310,6 +310,10 @@ hipError_t launch_fwd(DType t, int D, int KP, const FwdArgs& a, int grid, hipStr
 hipError_t launch_fwd_bf16(int D, int KP, bool ones, const FwdArgs& a, int grid, hipStream_t st);
 // paired-wave dense forward (8 waves, 128 rows a workgroup; needs k < KP)
 hipError_t launch_fwd_pair(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
+// wide-wave dense forward (4 waves, 256 rows a workgroup; needs k < KP <= 224);
+// taken from kWideMinWGs workgroups on
+constexpr int kWideMinWGs = 128;
+hipError_t launch_fwd_wide(int D, int KP, const FwdArgs& a, int grid, hipStream_t st);
 // dcol: V carries two ones columns and dO the high / low parts of -D there
 // (k + 2 <= KP), so dP - D comes out of the MFMAs; KP = 256 also runs without
 hipError_t launch_dq_bf16(int D, int KP, bool dcol, const DqArgs& a, int grid, hipStream_t st);

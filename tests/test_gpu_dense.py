@@ -270,3 +270,45 @@ def test_dense_backward_many_key_blocks(nN, nM, d, k):
     O_r, lse_r, gr = oracle_dense(c)
     check_fwd(O.cpu().numpy(), O_r, lse.cpu().numpy(), lse_r, what=f"many blocks {nM}")
     check_grads((dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()), gr, what=f"many blocks {nM}")
+
+
+@pytest.mark.parametrize("nN,nM,d,k", [(32800, 517, 128, 200), (33000, 130, 128, 100), (32900, 70, 128, 40),
+                                       (32800, 65, 128, 1), (32850, 300, 64, 200), (32800, 96, 64, 30),
+                                       (32800, 200, 64, 100), (32800, 100, 64, 64)])
+def test_dense_wide_forward(nN, nM, d, k):
+    """From 128 workgroups of 256 rows on (n_N >= 32513) the forward runs the
+    wide-wave kernel (a wave owns 64 rows): every padded width it has, ragged
+    row and key tails, against the oracle."""
+    say("dense wide fwd", nN, nM, d, k)
+    c = gen.make_small(nN, nM, d, k, "bf16", seed=nN + nM + k)
+    Q, K, V = (to_dev(c[x], "bf16") for x in ("Q", "K", "V"))
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+    torch.cuda.synchronize()
+    Or, lser = dense_fwd(f64(c["Q"], "bf16"), f64(c["K"], "bf16"), f64(c["V"], "bf16"), c["scale"])
+    check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what=f"wide {nN}x{nM} d{d} k{k}")
+
+
+def test_dense_wide_forward_fallback():
+    """The wide kernel's underflow marks: row 5 (query 60 e1 against a key of
+    norm 60 orthogonal to it) and row 32700 (in the last workgroup) send
+    their 128-row blocks to the one-wave kernel; all rows match the oracle."""
+    say("dense wide fwd fallback")
+    nN, nM, d, k = 32800, 300, 128, 200
+    c = gen.make_small(nN, nM, d, k, "bf16", seed=23)
+    Qf = f64(c["Q"], "bf16").astype(np.float32)
+    Kf = f64(c["K"], "bf16").astype(np.float32)
+    for r, axis in ((5, 0), (32700, 2)):
+        Qf[r] = 0.0
+        Qf[r, axis] = 60.0
+    Kf[:, 0] = 0.0
+    Kf[:, 2] = 0.0
+    Kf[250] = 0.0
+    Kf[250, 1] = 60.0
+    c["Q"], c["K"] = gen.bf16_bits_from_f32(Qf), gen.bf16_bits_from_f32(Kf)
+    Q, K, V = (to_dev(c[x], "bf16") for x in ("Q", "K", "V"))
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+    torch.cuda.synchronize()
+    Or, lser = dense_fwd(f64(c["Q"], "bf16"), f64(c["K"], "bf16"), f64(c["V"], "bf16"), c["scale"])
+    check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what="wide fallback")
+    for r in (5, 32700):
+        assert np.max(np.abs(O[r].cpu().numpy() - Or[r])) <= 2e-2
