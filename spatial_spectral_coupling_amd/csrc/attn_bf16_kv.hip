@@ -96,6 +96,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   sD.init(a.Dp, a.n_N + 1);
   const int krow = k_begin + wave * 32 + l32;
   const bool key_ok = krow < k_end;
+  // A geo item's waves past the patch's last row own no keys: they take
+  // part in the loads and barriers only.
+  const bool wave_keys = !GEO || k_begin + wave * 32 < k_end;
 
   const bf16* K = reinterpret_cast<const bf16*>(a.Kp);
   const bf16* Vp = reinterpret_cast<const bf16*>(a.Vp);
@@ -191,8 +194,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   });
 
   // Two statically distinct buffers: the step that reads one fills the other.
-  auto step = [&](const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn, const float* dsc,
-                  float* dsn) __attribute__((always_inline)) {
+  auto step = [&](auto keys_c, const int t, const int b, char* Qt, char* Qn, const float* lsc, float* lsn,
+                  const float* dsc, float* dsn) __attribute__((always_inline)) {
+    constexpr bool KEYS = decltype(keys_c)::value;  // false: loads and barrier only
     char* Ot = Qt + QB;
     f32x16 sc[2], dp[2];
     bf16x8 pk[2][2], dk8[2][2];
@@ -278,6 +282,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
       if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
         load_row((u + 2 - LOAD0) / LSTRIDE);
+      if (!KEYS) return;
       const int c = chain_of(u), j = index_in(u);
       if (c != 1 && c != 2) return;
       static_for<SLICES>([&](auto k) {
@@ -286,12 +291,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     };
 
     bf16x8 ring[AH];
-    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    if (KEYS) static_for<AH>([&](auto u) { ring[u] = operand(u); });
     static_for<U>([&](auto u) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 cur = ring[u % AH];
-      if (u + AH < U) ring[u % AH] = operand(u + AH);
-      mma_step(u, cur);
+      if (KEYS) {
+        const bf16x8 cur = ring[u % AH];
+        if (u + AH < U) ring[u % AH] = operand(u + AH);
+        mma_step(u, cur);
+      }
       side(u);
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -299,12 +306,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     wait_loads();
     __syncthreads();
   };
-  int t = t0;
-  for (; t + 1 < t1; t += 2) {
-    step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
-    step(t + 1, 1, sm1, sm0, ls1, ls0, ds1, ds0);
+  auto run = [&](auto keys_c) __attribute__((always_inline)) {
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
+      step(keys_c, t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+      step(keys_c, t + 1, 1, sm1, sm0, ls1, ls0, ds1, ds0);
+    }
+    if (t < t1) step(keys_c, t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+  };
+  if (GEO && !wave_keys) {
+    // no keys, no outputs (the merge of a split item stores existing keys
+    // only, so this wave's rows of the partial buffer may stay unwritten)
+    run(std::false_type{});
+    return;
   }
-  if (t < t1) step(t, 0, sm0, sm1, ls0, ls1, ds0, ds1);
+  run(std::true_type{});
 
   if (GEO && it.slot >= 0) {
     // one part of a split item: partial sums for the merge pass

@@ -135,6 +135,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   if (VT) sVt.init(a.Vt, a.groupsVt);
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
+  // A geo item's waves past the patch's last row own no rows: they take
+  // part in the loads and barriers only (not at KP = 256, where the second
+  // copy of the pipeline would spill).
+  const bool wave_rows = !GEO || KP > 224 || q_begin + wave * 32 < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Q);
   std::conditional_t<VT, RowReaderP<D>, RowReader<D>> rk;
@@ -255,8 +259,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // other, so the compiler can tell the direct loads in flight from the LDS
     // reads.  The stream's last tile may be partial: its keys at or past
     // nvalid start from a score of -inf (bias, set before the pipeline).
-    auto step = [&](auto bound_c, const int t, const int b, char* Kt, char* Kn) __attribute__((always_inline)) {
+    auto step = [&](auto bound_c, auto rows_c, const int t, const int b, char* Kt, char* Kn)
+                    __attribute__((always_inline)) {
       constexpr bool BOUND = decltype(bound_c)::value;
+      constexpr bool ROWS = decltype(rows_c)::value;  // false: loads and barrier only
       char* Vt = Kt + KB;
       const int nvalid = total - t * kTile;
       const bool first = !BOUND && t == t0 && !fixed;
@@ -342,6 +348,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
         if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
           load_row((u + 2 - LOAD0) / LSTRIDE);
+        if (!ROWS) return;
         if (u >= C1 && u < C2) {
           static_for<SLICES>([&](auto k) {
             if (k * NS / SLICES == u - C1) slice(0, k);
@@ -354,12 +361,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       };
 
       bf16x8 ring[AH];
-      static_for<AH>([&](auto u) { ring[u] = operand(u); });
+      if (ROWS) static_for<AH>([&](auto u) { ring[u] = operand(u); });
       static_for<U>([&](auto u) {
         __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 cur = ring[u % AH];
-        if (u + AH < U) ring[u % AH] = operand(u + AH);
-        mma_step(u, cur);
+        if (ROWS) {
+          const bf16x8 cur = ring[u % AH];
+          if (u + AH < U) ring[u % AH] = operand(u + AH);
+          mma_step(u, cur);
+        }
         side(u);
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       // Between tiles: the sums of this tile join the running sum at the
       // tile's reference; move the reference up when the maximum ran ahead.
       l_run += lsum;
-      if (!BOUND) {
+      if (!BOUND && ROWS) {
         m_run = mref;
         const float tmax = fmaxf(mh[0], mh[1]);
         m_true = fmaxf(m_true, tmax);
@@ -387,15 +396,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     };
     auto run = [&](auto bound_c) __attribute__((always_inline)) {
       const int nt = t1 - t0;  // (this loop form keeps the accumulators in registers)
-      for (int i = 0; i < nt; i += 2) {
-        step(bound_c, t0 + i, 0, sm0, sm1);
-        if (i + 1 < nt) step(bound_c, t0 + i + 1, 1, sm1, sm0);
+      if (!GEO || KP > 224 || wave_rows) {
+        for (int i = 0; i < nt; i += 2) {
+          step(bound_c, std::true_type{}, t0 + i, 0, sm0, sm1);
+          if (i + 1 < nt) step(bound_c, std::true_type{}, t0 + i + 1, 1, sm1, sm0);
+        }
+      } else {
+        for (int i = 0; i < nt; i += 2) {
+          step(bound_c, std::false_type{}, t0 + i, 0, sm0, sm1);
+          if (i + 1 < nt) step(bound_c, std::false_type{}, t0 + i + 1, 1, sm1, sm0);
+        }
       }
     };
     if (mode == 0) {
       run(std::true_type{});
       const float lt = row_sum();
-      if (!__syncthreads_or(t1 > t0 && !(lt >= 0x1p-60f))) break;
+      if (!__syncthreads_or(t1 > t0 && row_ok && !(lt >= 0x1p-60f))) break;
       mode = 1;
       continue;
     }
@@ -557,6 +573,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   sV.init(a.Vp, a.n_M + 1);
   const int row = q_begin + wave * 32 + l32;
   const bool row_ok = row < q_end;
+  // A geo item's waves past the patch's last row own no rows: they take
+  // part in the loads and barriers only.
+  const bool wave_rows = !GEO || q_begin + wave * 32 < q_end;
 
   const bf16* Q = reinterpret_cast<const bf16*>(a.Qp);
   const bf16* dOp = reinterpret_cast<const bf16*>(a.dOp);
@@ -659,10 +678,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // the softmax of half 0 runs during B1(t-1) and A1(t), that of half 1
   // during B0(t) and A0(t+1), so each has a 30-step window.  Two statically
   // distinct buffers: the step that reads one fills the other.
-  auto step = [&](const int t, const int b, char* Kt, char* Kn) __attribute__((always_inline)) {
+  auto step = [&](auto rows_c, const int t, const int b, char* Kt, char* Kn) __attribute__((always_inline)) {
+    constexpr bool ROWS = decltype(rows_c)::value;  // false: loads and barrier only
     char* Vt = Kt + KB;
     const int nvalid = total - t * kTile;
-    if (nvalid < kTile) {
+    if (ROWS && nvalid < kTile) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -715,6 +735,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if (u >= LOAD0 && (u - LOAD0) % LSTRIDE == 0 && (u - LOAD0) / LSTRIDE < NL) issue_load((u - LOAD0) / LSTRIDE);
       if (GEO && u + 2 >= LOAD0 && (u + 2 - LOAD0) % LSTRIDE == 0 && (u + 2 - LOAD0) / LSTRIDE < NL)
         load_row((u + 2 - LOAD0) / LSTRIDE);
+      if (!ROWS) return;
       if (u < CY) {
         // half 1 of the previous tile: window positions LB .. WIN-1
         static_for<SLICES>([&](auto k) {
@@ -743,13 +764,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     };
 
     bf16x8 ring[AH];
-    static_for<AH>([&](auto u) { ring[u] = operand(u); });
+    if (ROWS) static_for<AH>([&](auto u) { ring[u] = operand(u); });
     static_for<U>([&](auto u) {
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 cur = ring[u % AH];
-      if (u + AH < U) ring[u % AH] = operand(u + AH);
-      pre(u);
-      mma_step(u, cur);
+      if (ROWS) {
+        const bf16x8 cur = ring[u % AH];
+        if (u + AH < U) ring[u % AH] = operand(u + AH);
+        pre(u);
+        mma_step(u, cur);
+      }
       side(u);
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -757,15 +780,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     wait_loads();
     __syncthreads();
   };
-  for (int t = t0; t < t1; t += 2) {
-    step(t, 0, sm0, sm1);
-    if (t + 1 < t1) step(t + 1, 1, sm1, sm0);
+  if (!GEO || wave_rows) {
+    for (int t = t0; t < t1; t += 2) {
+      step(std::true_type{}, t, 0, sm0, sm1);
+      if (t + 1 < t1) step(std::true_type{}, t + 1, 1, sm1, sm0);
+    }
+    // drain: the rest of the last tile's half-1 softmax, then its B1 chain
+    static_for<SLICES>([&](auto k) {
+      if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, k);
+    });
+    static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
+  } else {
+    for (int t = t0; t < t1; t += 2) {
+      step(std::false_type{}, t, 0, sm0, sm1);
+      if (t + 1 < t1) step(std::false_type{}, t + 1, 1, sm1, sm0);
+    }
   }
-  // drain: the rest of the last tile's half-1 softmax, then its B1 chain
-  static_for<SLICES>([&](auto k) {
-    if (k * WIN / SLICES >= LB) slice(sc1, dp1, ds1, k);
-  });
-  static_for<LB>([&](auto j) { dq[j % NK] = mma(kt[j], ds1[j / NK], dq[j % NK]); });
 
   if (GEO && it.slot >= 0) {
     // one part of a split item: partial sums for the merge pass
