@@ -403,7 +403,7 @@ ssc_status check_fps(int n, int nnz, int P) {
 }
 
 struct FpsLayout {
-  size_t w = kNone, stamp = kNone, queue = kNone, cmax = kNone, cflag = kNone, bad = kNone;
+  size_t w = kNone, adjp = kNone, wp = kNone, stamp = kNone, queue = kNone, cmax = kNone, cflag = kNone, bad = kNone;
   size_t total = 0;
   int nchunk = 0, nblk = 0;
 };
@@ -419,6 +419,8 @@ FpsLayout make_fps_layout(int n, int nnz) {
     return at_;
   };
   L.w = take((size_t)nnz * 8);
+  L.adjp = take((size_t)n * kFpsSlots * 4);
+  L.wp = take((size_t)n * kFpsSlots * 8);
   L.stamp = take((size_t)n * 4);
   L.queue = take((size_t)n * 8);
   L.cmax = take((size_t)L.nchunk * 8);
@@ -1249,6 +1251,7 @@ ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const 
   a.x = x; a.off = off; a.adj = adj; a.n = n; a.nnz = nnz; a.P = P;
   a.seeds = seeds; a.labels = labels; a.dist = dist;
   a.w = at<double>(ws, L.w); a.stamp = at<int>(ws, L.stamp); a.queue = at<int>(ws, L.queue);
+  a.adjp = at<int>(ws, L.adjp); a.wp = at<double>(ws, L.wp);
   a.cmax = at<unsigned long long>(ws, L.cmax); a.cflag = at<int>(ws, L.cflag); a.bad = at<int>(ws, L.bad);
   a.nchunk = L.nchunk; a.nblk = L.nblk;
   SSC_TRY(timed("fps", s, [&] { return launch_fps(a, s); }));

@@ -12,10 +12,16 @@
 //
 //   fps_prep  -- checks the adjacency (offsets and neighbour indices), edge
 //                lengths with explicitly rounded fp64 operations (no fused
-//                multiply-add), and the initial state (distance +inf,
-//                label 0, chunk maxima +inf);
+//                multiply-add), a padded copy of the adjacency (kFpsSlots
+//                neighbours and lengths per vertex, used when no vertex has
+//                more), and the initial state (distance +inf, label 0,
+//                chunk maxima +inf);
 //   fps_run   -- one workgroup of 1024 threads runs all P steps.  Step t
-//                relaxes outward from seed t with a frontier worklist: a
+//                relaxes outward from seed t with a frontier worklist (the
+//                first kLdsQueue entries of a round's queue sit in LDS; a
+//                vertex is queued once per round, which an LDS bitmap per
+//                round tracks up to kSeenBits vertices, per-vertex round
+//                stamps in the workspace beyond): a
 //                vertex's distance is lowered by a 64-bit atomic minimum on
 //                its bit pattern (non-negative doubles order like their
 //                bits) only when the path through seed t is strictly
@@ -39,6 +45,10 @@ namespace fps {
 constexpr int kThreads = 1024;
 constexpr int kChunk = 256;  // vertices per argmax chunk
 constexpr int kGroup = 8;    // lanes per frontier vertex (one per neighbour)
+static_assert(kGroup == kFpsSlots, "a lane per padded neighbour slot");
+constexpr int kLdsQueue = 8192;  // queue entries of a round held in LDS (the rest in the workspace)
+constexpr int kSeenWords = 8192;  // words of each of the two "queued this round" bitmaps
+constexpr int kSeenBits = 32 * kSeenWords;
 typedef unsigned long long u64;
 constexpr u64 kInfBits = 0x7FF0000000000000ull;
 
@@ -59,8 +69,9 @@ __device__ __forceinline__ double edge_len(const double* x, int u, int v) {
   return sqrt((xx + yy) + zz);
 }
 
-// One thread per vertex: validation, edge lengths, initial state.  bad[b]
-// is 1 when block b saw an invalid offset or neighbour.
+// One thread per vertex: validation, edge lengths, padded adjacency,
+// initial state.  Bit 0 of bad[b]: block b saw an invalid offset or
+// neighbour; bit 1: a vertex of block b has more than kFpsSlots neighbours.
 __global__ __launch_bounds__(256) void fps_prep(FpsArgs a) {
   const int u = blockIdx.x * 256 + threadIdx.x;
   int bad = 0;
@@ -69,14 +80,20 @@ __global__ __launch_bounds__(256) void fps_prep(FpsArgs a) {
     if ((u == 0 && o0 != 0) || (u == a.n - 1 && o1 != a.nnz) || o0 < 0 || o1 < o0 || o1 > a.nnz) {
       bad = 1;
     } else {
+      if (o1 - o0 > kFpsSlots) bad = 2;
       for (int e = o0; e < o1; ++e) {
         const int v = a.adj[e];
         if (v < 0 || v >= a.n) {
           bad = 1;
         } else {
-          a.w[e] = edge_len(a.x, u, v);
+          const double len = edge_len(a.x, u, v);
+          a.w[e] = len;
+          if (e - o0 < kFpsSlots) a.wp[(size_t)u * kFpsSlots + (e - o0)] = len;
         }
       }
+#pragma unroll
+      for (int j = 0; j < kFpsSlots; ++j)
+        a.adjp[(size_t)u * kFpsSlots + j] = j < o1 - o0 ? a.adj[o0 + j] : -1;
     }
     reinterpret_cast<u64*>(a.dist)[u] = kInfBits;
     a.labels[u] = 0;
@@ -87,8 +104,8 @@ __global__ __launch_bounds__(256) void fps_prep(FpsArgs a) {
     a.cmax[c] = kInfBits;
     a.cflag[c] = 0;
   }
-  bad = __syncthreads_or(bad);
-  if (threadIdx.x == 0) a.bad[blockIdx.x] = bad;
+  const int b0 = __syncthreads_or(bad & 1), b1 = __syncthreads_or(bad & 2);
+  if (threadIdx.x == 0) a.bad[blockIdx.x] = (b0 ? 1 : 0) | (b1 ? 2 : 0);
 }
 
 // Maximum of (bits, index) pairs: larger bits, then lower index.
@@ -100,6 +117,10 @@ __device__ __forceinline__ void better(u64& b, int& i, u64 b2, int i2) {
 }
 
 __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
+  __shared__ int s_queue[2][kLdsQueue];  // entries i < kLdsQueue of the two rounds' queues
+  // bit v of s_seen[b]: v sits in the queue of a round r with r & 1 == b
+  // (meshes of at most kSeenBits vertices)
+  __shared__ unsigned s_seen[2][kSeenWords];
   __shared__ int s_cnt[3];
   __shared__ int s_flag;
   __shared__ int s_seed;
@@ -113,10 +134,16 @@ __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
     s_flag = 0;
     s_cnt[0] = s_cnt[1] = s_cnt[2] = 0;
   }
+  const bool lds_seen = n <= kSeenBits;
+  for (int i = tid; i < 2 * kSeenWords; i += kThreads) (&s_seen[0][0])[i] = 0u;
   __syncthreads();
-  for (int b = tid; b < a.nblk; b += kThreads)
-    if (a.bad[b]) s_flag = 1;
-  __syncthreads();
+  int wide = 0;  // some vertex has more than kFpsSlots neighbours
+  for (int b = tid; b < a.nblk; b += kThreads) {
+    const int f = a.bad[b];
+    if (f & 1) s_flag = 1;
+    wide |= f & 2;
+  }
+  const bool padded = !__syncthreads_or(wide);
   if (s_flag) {  // invalid adjacency: nothing is computed
     for (int t = tid; t < a.P; t += kThreads) a.seeds[t] = -1;
     for (int v = tid; v < n; v += kThreads) {
@@ -142,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
         a.labels[seed] = t;
         a.cflag[seed / kChunk] = 1;
         a.stamp[seed] = r;
-        a.queue[(size_t)(r & 1) * n] = seed;
+        s_queue[r & 1][0] = seed;
         c0 = 1;
       }
       s_seed = c0;
@@ -151,6 +178,10 @@ __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
     int cnt = s_seed;
     int rstep = 0;
     while (cnt > 0 && rstep <= n) {
+      // queue entry i of a round: LDS below kLdsQueue, the workspace above
+      // (a round queues each vertex at most once, so i < n)
+      const int* qin_l = s_queue[r & 1];
+      int* qout_l = s_queue[(r + 1) & 1];
       const int* qin = a.queue + (size_t)(r & 1) * n;
       int* qout = a.queue + (size_t)((r + 1) & 1) * n;
       int* ctr = &s_cnt[r % 3];
@@ -159,19 +190,50 @@ __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
       for (int base = 0; base < cnt; base += kThreads / kGroup) {
         const int q = base + tid / kGroup, j = tid % kGroup;
         if (q < cnt) {
-          const int u = qin[q];
+          const int u = q < kLdsQueue ? qin_l[q] : qin[q];
+          // u leaves this round's bitmap (which the next round but one reuses)
+          if (lds_seen && j == 0) atomicAnd(&s_seen[r & 1][u >> 5], ~(1u << (u & 31)));
           const double du = __longlong_as_double((long long)load_bits(dbits + u));
-          const int o1 = a.off[u + 1];
-          for (int e = a.off[u] + j; e < o1; e += kGroup) {
-            const int v = a.adj[e];
-            const double cand = du + a.w[e];
+          // the padded adjacency: lane j takes neighbour slot j (kGroup ==
+          // kFpsSlots), read together with du; else the CSR rows
+          int e = 0, o1 = 0, v = -1;
+          double wuv = 0.0;
+          if (padded) {
+            v = a.adjp[(size_t)u * kFpsSlots + j];
+            wuv = a.wp[(size_t)u * kFpsSlots + j];
+          } else {
+            e = a.off[u] + j;
+            o1 = a.off[u + 1];
+          }
+          for (;;) {
+            if (!padded) {
+              if (e >= o1) break;
+              v = a.adj[e];
+              wuv = a.w[e];
+              e += kGroup;
+            } else if (v < 0) {
+              break;
+            }
+            const double cand = du + wuv;
             const u64 cb = (u64)__double_as_longlong(cand);
             const u64 old = atomicMin(dbits + v, cb);
             if (cb < old) {
               a.labels[v] = t;
               a.cflag[v / kChunk] = 1;
-              if (atomicExch(a.stamp + v, stamp_next) != stamp_next) qout[atomicAdd(ctr, 1)] = v;
+              bool first;
+              if (lds_seen) {
+                const unsigned bit = 1u << (v & 31);
+                first = (atomicOr(&s_seen[(r + 1) & 1][v >> 5], bit) & bit) == 0u;
+              } else {
+                first = atomicExch(a.stamp + v, stamp_next) != stamp_next;
+              }
+              if (first) {
+                const int i = atomicAdd(ctr, 1);
+                if (i < kLdsQueue) qout_l[i] = v;
+                else qout[i] = v;
+              }
             }
+            if (padded) break;
           }
         }
       }
@@ -186,9 +248,17 @@ __global__ __launch_bounds__(kThreads) void fps_run(FpsArgs a) {
     }
     if (t + 1 == a.P) break;
 
-    // chunk maxima of the chunks this step touched
-    for (int c = wave; c < a.nchunk; c += kThreads / 64) {
-      if (a.cflag[c]) {
+    // chunk maxima of the chunks this step touched: wave w owns the chunks
+    // c = w (mod 16); a lane reads the flag of one of them, so a wave finds
+    // its flagged chunks with one load and a ballot per 64 of them
+    constexpr int kWaves = kThreads / 64;
+    for (int c0 = wave; c0 < a.nchunk; c0 += 64 * kWaves) {
+      const int cl = c0 + kWaves * lane;
+      unsigned long long fl = __ballot(cl < a.nchunk && a.cflag[cl] != 0);
+      while (fl != 0ull) {
+        const int b = __ffsll((long long)fl) - 1;
+        fl &= fl - 1ull;
+        const int c = c0 + kWaves * b;
         u64 m = 0;
 #pragma unroll
         for (int j = 0; j < kChunk / 64; ++j) {

@@ -284,7 +284,9 @@ struct FmArgs {
 // Gram blocking for n rows at padded width KP (rows per block, block count).
 void fm_blocks(int n, int KP, int* rows, int* nblk);
 
-// Geodesic farthest-point-sampling partition (fps.hip).
+// Geodesic farthest-point-sampling partition (fps.hip).  Meshes whose
+// vertices have at most kFpsSlots neighbours also get a padded adjacency.
+constexpr int kFpsSlots = 8;
 struct FpsArgs {
   const double* x;      // [n x 3] vertex positions
   const int* off;       // [n + 1] CSR offsets of the adjacency
@@ -294,6 +296,8 @@ struct FpsArgs {
   int* labels;          // [n] output: index of the nearest seed
   double* dist;         // [n] output (and working field): distance to the nearest seed
   double* w;            // [nnz] edge lengths (workspace)
+  int* adjp;            // [n x kFpsSlots] neighbours per vertex, -1 past its degree (workspace)
+  double* wp;           // [n x kFpsSlots] their edge lengths (workspace)
   int* stamp;           // [n] round in whose queue a vertex sits (workspace)
   int* queue;           // [2 n] frontier worklists of two rounds (workspace)
   unsigned long long* cmax;  // [nchunk] per-chunk maximum distance bits (workspace)

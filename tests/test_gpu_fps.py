@@ -68,6 +68,37 @@ def test_fps_grid_ties():
     check_exact(x, np.array(e), 40, "grid 33x33 P=40")
 
 
+def test_fps_wide_vertices_and_long_queues():
+    # A hub joined to 10000 rim vertices (a ring): the hub has more
+    # neighbours than the padded adjacency holds, so the CSR rows are used,
+    # and the first round queues more vertices than the LDS part of the
+    # queue takes.
+    m = 10000
+    t = np.linspace(0.0, 2.0 * np.pi, m, endpoint=False)
+    rng = np.random.default_rng(11)
+    rim = np.c_[np.cos(t), np.sin(t), 0.1 * rng.random(m)] * (1.0 + 0.05 * rng.random((m, 1)))
+    x = np.vstack([np.zeros((1, 3)), rim])
+    e = [(0, i) for i in range(1, m + 1)] + [(i, i % m + 1) for i in range(1, m + 1)]
+    check_exact(x, np.array(e), 6, f"hub + ring of {m}, P=6")
+    # a grid with diagonals: interior vertices have exactly 8 neighbours
+    k = 40
+    ii, jj = np.meshgrid(np.arange(k), np.arange(k), indexing="ij")
+    xg = np.stack([ii.ravel(), jj.ravel(), 0.01 * (ii * jj).ravel() % 1.0], axis=1).astype(float)
+    idx = lambda i, j: i * k + j
+    eg = [(idx(i, j), idx(i + 1, j)) for i in range(k - 1) for j in range(k)]
+    eg += [(idx(i, j), idx(i, j + 1)) for i in range(k) for j in range(k - 1)]
+    eg += [(idx(i, j), idx(i + 1, j + 1)) for i in range(k - 1) for j in range(k - 1)]
+    eg += [(idx(i, j + 1), idx(i + 1, j)) for i in range(k - 1) for j in range(k - 1)]
+    check_exact(xg, np.array(eg), 50, f"grid {k}x{k} with diagonals, P=50")
+
+
+def test_fps_large_mesh_global_stamps():
+    # more vertices than the LDS bitmaps of queued vertices cover (2^18):
+    # the per-vertex round stamps in the workspace take over
+    x, e = sphere_mesh(270000, 5)
+    check_exact(x, e, 3, "sphere n=270000 P=3")
+
+
 def test_fps_disconnected_and_single_vertex():
     # three components; with 2 seeds the third stays at +inf with label 0
     x1 = np.c_[np.arange(5.0), np.zeros(5), np.zeros(5)]
