@@ -832,8 +832,11 @@ ssc_status geo_common_checks(ssc_dtype dtype, int d, int k, int n_N, int P_N, co
   return SSC_OK;
 }
 
+// pads / pad_grids: bf16 row-padding jobs (at most two) that run in the
+// plan's launch, on the CUs the plan leaves idle
 ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int* offM, const int* idx, int n_N,
-                           int n_M, int P_N, int P_M, int s, bool inverse, hipStream_t hs, bool bf16_path) {
+                           int n_M, int P_N, int P_M, int s, bool inverse, hipStream_t hs, bool bf16_path,
+                           const PackArgs* pads = nullptr, const int* pad_grids = nullptr, int npads = 0) {
   PlanArgs pl{};
   pl.offN = offN; pl.offM = offM; pl.idx = idx;
   pl.n_N = n_N; pl.n_M = n_M; pl.P_N = P_N; pl.P_M = P_M; pl.s = s;
@@ -854,7 +857,14 @@ ssc_status launch_geo_plan(const Layout& L, void* ws, const int* offN, const int
     pl.inv_off = at<int>(ws, L.inv_off);
     pl.inv_idx = at<int>(ws, L.inv_idx);
   }
-  SSC_TRY(launch_plan(pl, hs));
+  bool fuse = npads > 0;
+  for (int i = 0; i < npads; ++i) fuse = fuse && pad_bf16_applies(DType::BF16, pads[i]);
+  if (fuse) {
+    SSC_TRY(launch_plan_pad(pl, pads, pad_grids, npads, hs));
+  } else {
+    SSC_TRY(launch_plan(pl, hs));
+    for (int i = 0; i < npads; ++i) SSC_TRY(launch_pack(DType::BF16, pads[i], pad_grids[i], hs));
+  }
   return SSC_OK;
 }
 
@@ -878,15 +888,16 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
-  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs, dtype == SSC_BF16)) != SSC_OK)
-    return st;
   int* counters = at<int>(ws, L.counters);
   if (dtype == SSC_BF16) {
     const int KPf = kpad_fwd_bf16(k);
     const bool ones = k < KPf;
     PackArgs pv{};
     pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPf; pv.ones = ones;
-    SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
+    const int gv = L.npadM / kGroup;
+    // the V padding runs in the plan's launch
+    if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs, true, &pv, &gv, 1)) != SSC_OK)
+      return st;
     float* knorm = at<float>(ws, L.knorm);
     SSC_TRY(launch_keynorm(K, n_M, d, knorm, hs));
     FwdArgs a{};
@@ -902,6 +913,7 @@ ssc_status coupling_geo_fwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     SSC_TRY(launch_fwd_merge_bf16(d, KPf, ones, a, hs));
     return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
   }
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, false, hs, false)) != SSC_OK) return st;
 
   PackArgs pk{};
   pk.X = K; pk.Xp = at<char>(ws, L.Kp); pk.n = n_M; pk.w = d; pk.W = d;
@@ -942,19 +954,21 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
   const DType T = dt(dtype);
-  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs, dtype == SSC_BF16)) != SSC_OK)
-    return st;
   int* counters = at<int>(ws, L.counters);
   if (dtype == SSC_BF16) {
     const int KPb = kpad_bwd_bf16(k);
     const bool dcol = k + 2 <= KPb;
-    PackArgs pv{};
+    PackArgs pads[2]{};
+    PackArgs& pv = pads[0];
     pv.X = V; pv.Xp = at<char>(ws, L.Vp); pv.n = n_M; pv.w = k; pv.W = KPb; pv.ones = dcol ? 2 : 0;
-    SSC_TRY(launch_pack(T, pv, L.npadM / kGroup, hs));
-    PackArgs po{};
+    PackArgs& po = pads[1];
     po.X = dO; po.Xp = at<char>(ws, L.dOp); po.n = n_N; po.w = k; po.W = KPb; po.dcol = dcol;
     po.O = O; po.lse = lse; po.Dp = at<float>(ws, L.Dp); po.lse2p = at<float>(ws, L.lse2p);
-    SSC_TRY(launch_pack(T, po, L.npadN / kGroup, hs));
+    // the V and dO padding run in the plan's launch (no dO rows: V only)
+    const int grids[2] = {L.npadM / kGroup, L.npadN / kGroup};
+    if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs, true, pads, grids,
+                              n_N > 0 ? 2 : 1)) != SSC_OK)
+      return st;
     const float c2 = scale * kLog2e;
     if (n_N > 0) {
       DqArgs q{};
@@ -984,6 +998,7 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
     SSC_TRY(launch_dkv_merge_bf16(d, KPb, want_dv, b, hs));
     return kDebug ? debug_verdict(counters + 4, hs) : SSC_OK;
   }
+  if ((st = launch_geo_plan(L, ws, offN, offM, idx, n_N, n_M, P_N, P_M, s, true, hs, false)) != SSC_OK) return st;
   int* poffN = at<int>(ws, L.poffN);
   int* poffM = at<int>(ws, L.poffM);
 

@@ -348,7 +348,14 @@ hipError_t launch_dq(DType t, int D, int KP, const DqArgs& a, int grid, hipStrea
 hipError_t launch_dkv(DType t, int D, int KP, const DkvArgs& a, int grid, hipStream_t st);
 bool supported(DType t, int D, int KP);
 hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st);
+// launch_pack takes the bf16 row-padding kernel for these jobs (and its
+// 16-byte vector form for pad_bf16_vec ones)
+bool pad_bf16_applies(DType t, const PackArgs& a);
+bool pad_bf16_vec(const PackArgs& a);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+// the plan and up to two bf16 row-padding jobs (pad_bf16_applies, grid =
+// 16-row groups) in one launch
+hipError_t launch_plan_pad(const PlanArgs& a, const PackArgs* jobs, const int* grids, int njobs, hipStream_t st);
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // ident: the rows of Q / K are precomputed features (identity feature map)

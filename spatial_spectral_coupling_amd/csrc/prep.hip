@@ -111,9 +111,11 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 // rows get `ones` columns of 1 from column w on; with dcol (and O), columns w
 // and w + 1 hold -D split into a bf16 high part and a bf16 low part (their
 // sum is -D to about 2^-17 relative), so a product with a ones column adds -D.
+// Rows 16 blk .. 16 blk + 15 of one bf16 padding job, 16 threads a row
+// (tid < 256; no barrier, no LDS).
 template <bool VEC>
-__global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
-  const int r = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
+__device__ __forceinline__ void pad_rows(const PackArgs& a, int blk, int tid) {
+  const int r = blk * 16 + (tid >> 4), j = tid & 15;
   const int w = a.w, cw = a.W / 8;
   const bool present = r < a.n;
   const bf16* X = reinterpret_cast<const bf16*>(a.X) + (size_t)r * w;
@@ -177,6 +179,11 @@ __global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
     }
     a.lse2p[r] = l2;
   }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void pad_bf16_kernel(PackArgs a) {
+  pad_rows<VEC>(a, blockIdx.x, threadIdx.x);
 }
 
 // Grouped-transposed copy of bf16 rows: one workgroup per 64 rows (4 groups
@@ -268,12 +275,20 @@ hipError_t launch_keynorm(const void* K, int n, int d, float* part, hipStream_t 
   return hipGetLastError();
 }
 
+bool pad_bf16_applies(DType t, const PackArgs& a) {
+  return t == DType::BF16 && a.poff == nullptr && a.Xg == nullptr && a.Xp != nullptr && (a.W & 7) == 0 &&
+         a.W <= 256;
+}
+bool pad_bf16_vec(const PackArgs& a) {
+  return (a.w & 7) == 0 && (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.O) & 15) == 0;
+}
+
 hipError_t launch_pack(DType t, const PackArgs& a, int grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (t == DType::BF16 && a.poff == nullptr && a.Xg == nullptr && a.Xp != nullptr && (a.W & 7) == 0 && a.W <= 256) {
+  if (pad_bf16_applies(t, a)) {
     // dense row padding: one block per group of 16 positions
-    const bool vec = (a.w & 7) == 0 && (reinterpret_cast<uintptr_t>(a.X) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(a.O) & 15) == 0;
+    const bool vec = pad_bf16_vec(a);
     if (vec) hipLaunchKernelGGL(pad_bf16_kernel<true>, dim3(grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(pad_bf16_kernel<false>, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -493,7 +508,7 @@ __device__ __forceinline__ void for_chunk(const int* idx, int e0, int e1, const 
 // it, so list q is filled in ascending p, chunk after chunk, with no sort.
 // Two mask arrays alternate between chunks, so the bits of one chunk are
 // cleared while the next chunk sets its own.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+__device__ __forceinline__ void plan_body(const PlanArgs& a, const int role_block) {
   __shared__ int lds[kPlanWaves + 1];
   __shared__ int s_offM[kMaxPatches + 1];  // source offsets; later the second mask array
   __shared__ unsigned s_mask[kMaxPatches];
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // repeats within a row), so they reach the same verdict; each writes only
   // its own outputs and counters.  Without inverse lists one workgroup (role
   // 0) does everything.
-  const int role = inverse ? (int)blockIdx.x : 0;
+  const int role = inverse ? role_block : 0;
   const int* offN = a.offN;
   const int* offM = a.offM;
   // ---- offsets: validation, source offsets into LDS
@@ -748,9 +763,51 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) { plan_body(a, blockIdx.x); }
+
+// The plan (workgroups 0 .. nplan - 1) and up to two bf16 row-padding jobs
+// in one launch: the other workgroups take four 16-row blocks each (one per
+// 256 threads), so the padding runs on the other CUs while the plan's
+// workgroups run.  The jobs do not read what the plan writes.
+__global__ __launch_bounds__(kPlanThreads) void plan_pad_kernel(PlanArgs a, int nplan, PackArgs p0, int g0, int vec0,
+                                                               PackArgs p1, int g1, int vec1) {
+  if ((int)blockIdx.x < nplan) {
+    plan_body(a, blockIdx.x);
+    return;
+  }
+  const int vb = ((int)blockIdx.x - nplan) * (kPlanThreads / 256) + (int)threadIdx.x / 256;
+  const int vt = (int)threadIdx.x & 255;
+  if (vb < g0) {
+    if (vec0) pad_rows<true>(p0, vb, vt);
+    else pad_rows<false>(p0, vb, vt);
+  } else if (vb - g0 < g1) {
+    if (vec1) pad_rows<true>(p1, vb - g0, vt);
+    else pad_rows<false>(p1, vb - g0, vt);
+  }
+}
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
   const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
   hipLaunchKernelGGL(plan_kernel, dim3(inverse ? 2 : 1), dim3(kPlanThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_pad(const PlanArgs& a, const PackArgs* jobs, const int* grids, int njobs, hipStream_t st) {
+  if (njobs < 0 || njobs > 2) return hipErrorInvalidValue;
+  const bool inverse = a.inv_off != nullptr && a.idx != nullptr;
+  const int nplan = inverse ? 2 : 1;
+  PackArgs p[2]{};
+  int g[2] = {0, 0}, vec[2] = {0, 0};
+  for (int i = 0; i < njobs; ++i) {
+    if (!pad_bf16_applies(DType::BF16, jobs[i])) return hipErrorInvalidValue;
+    p[i] = jobs[i];
+    g[i] = grids[i] > 0 ? grids[i] : 0;
+    vec[i] = pad_bf16_vec(jobs[i]) ? 1 : 0;
+  }
+  const int per = kPlanThreads / 256;
+  const int nb = nplan + (g[0] + g[1] + per - 1) / per;
+  hipLaunchKernelGGL(plan_pad_kernel, dim3(nb), dim3(kPlanThreads), 0, st, a, nplan, p[0], g[0], vec[0], p[1], g[1],
+                     vec[1]);
   return hipGetLastError();
 }
 
