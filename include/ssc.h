@@ -32,8 +32,10 @@
  *   MFMA bf16 x bf16 -> fp32) or SSC_F32 (fp32 MFMA).  O, lse, dQ, dK, dV
  *   are always fp32.  lse is in natural log.
  * - Supported shapes: d in {64, 128}; 1 <= k <= 256 (padded internally to
- *   the next of 32, 64, 128, 224, 256); n_M >= 1; n_N >= 0 (n_N = 0 is a
- *   no-op); n_N, n_M <= 2^22 for the couplings (larger -> SSC_ERR_UNSUPPORTED).
+ *   the next of 32, 64, 128, 224, 256); n_M >= 1; n_N >= 0 (n_N = 0: a
+ *   forward computes nothing, a backward writes dK = dV = 0, and Q, O, dO,
+ *   lse and dQ may be NULL); n_N, n_M <= 2^22 for the couplings (larger ->
+ *   SSC_ERR_UNSUPPORTED).
  *   fp32 inputs: k <= 128.  Geo: 1 <= P_N, P_M <= 8192, 1 <= s <= P_M.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
  *   stream) and re-entrant: no global mutable state (the optional kernel

@@ -643,8 +643,9 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
                               float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
   ssc_status st = check_shape(dtype, n_N, n_M, d, k);
   if (st != SSC_OK) return st;
-  if (!all_ok({Q, K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
-  if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
+  // no target rows: dK = dV = 0, nothing reads Q, O, dO, lse or writes dQ
+  if (!all_ok({K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({Q, O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
   const Layout L = make_layout(SSC_OP_DENSE_BWD, dtype, n_N, n_M, d, k, 0, 0, 0);
   if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
@@ -939,8 +940,9 @@ ssc_status coupling_geo_bwd(ssc_dtype dtype, int d, int k, int n_N, int P_N, con
                             float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
   ssc_status st = geo_common_checks(dtype, d, k, n_N, P_N, offN, n_M, P_M, offM, s, idx);
   if (st != SSC_OK) return st;
-  if (!all_ok({Q, K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
-  if (n_N > 0 && !all_ok({O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
+  // no target rows: dK = dV = 0, nothing reads Q, O, dO, lse or writes dQ
+  if (!all_ok({K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({Q, O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
   const Layout L = make_layout(SSC_OP_GEO_BWD, dtype, n_N, n_M, d, k, P_N, P_M, s);
   if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;

@@ -109,6 +109,11 @@ def test_dense_bwd_validation(L):
     assert f(*args(nM=0)) == INVALID
     assert f(*args()) == WORKSPACE
     assert f(*args(dQ=A[0], ws=A[9], wsb=1 << 40)) == INVALID   # dQ aliases Q
+    # no target rows: Q, O, dO, lse and dQ may be NULL (only the workspace check remains)
+    assert f(BF16, 0, 64, 128, 200, None, A[1], A[2], 0.1, None, None, None, None, A[7], A[8], None, 0,
+             None) == WORKSPACE
+    assert f(BF16, 64, 64, 128, 200, None, A[1], A[2], 0.1, A[3], A[4], A[5], A[6], A[7], A[8], None, 0,
+             None) == INVALID                                   # with rows, Q is required
 
 
 def test_patch_topk_validation(L):
@@ -142,6 +147,11 @@ def test_geo_validation(L):
     g = L.coupling_geo_bwd
     assert g(BF16, 128, 200, 100, 4, A[0], 100, 4, A[1], 2, A[2], A[3], A[4], A[5], 0.1, A[6], A[7], A[8],
              A[9], A[10], A[11], None, 0, None) == WORKSPACE
+    # no target rows: Q, O, dO, lse and dQ may be NULL
+    assert g(BF16, 128, 200, 0, 4, A[0], 100, 4, A[1], 2, A[2], None, A[4], A[5], 0.1, None, None, None,
+             None, A[10], A[11], None, 0, None) == WORKSPACE
+    assert g(BF16, 128, 200, 100, 4, A[0], 100, 4, A[1], 2, A[2], None, A[4], A[5], 0.1, A[6], A[7], A[8],
+             A[9], A[10], A[11], None, 0, None) == INVALID
 
 
 def test_linear_validation_and_workspace(L):

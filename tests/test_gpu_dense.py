@@ -312,3 +312,21 @@ def test_dense_wide_forward_fallback():
     check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what="wide fallback")
     for r in (5, 32700):
         assert np.max(np.abs(O[r].cpu().numpy() - Or[r])) <= 2e-2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_dense_without_target_rows(dt):
+    """n_N = 0: the forward returns empty outputs and the backward writes
+    dK = dV = 0 (nothing reads the empty Q, O, dO, lse)."""
+    say("dense without target rows", dt)
+    c = gen.make_small(1, 300, 64, 30, dtype=dt, seed=6)
+    K, V = to_dev(c["K"], dt), to_dev(c["V"], dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    Q = torch.empty(0, 64, dtype=tdt, device="cuda")
+    dO = torch.empty(0, 30, dtype=tdt, device="cuda")
+    O, lse = ssc.coupling_dense_fwd(Q, K, V, 0.125)
+    assert O.shape == (0, 30) and lse.shape == (0,)
+    dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, 0.125)
+    torch.cuda.synchronize()
+    assert dQ.shape == (0, 64)
+    assert torch.count_nonzero(dK).item() == 0 and torch.count_nonzero(dV).item() == 0

@@ -13,7 +13,7 @@ import torch
 import gen
 import spatial_spectral_coupling_amd as ssc
 from oracle import (dense_bwd, dense_fwd, geo_bwd, geo_fwd, patch_means, patch_scores, topk)
-from tests._util import check_fwd, check_grads, check_idx, f64, say, sorted_problem, unsort
+from tests._util import check_fwd, check_grads, check_idx, f64, say, sorted_problem, to_dev, unsort
 
 pytestmark = pytest.mark.gpu
 
@@ -381,3 +381,25 @@ def test_geo_backward_without_dv(dt, k):
     gr = geo_bwd(Q, K, V, dO, c["labN"], c["labM"], idx.cpu().numpy(), sc)
     check_grads((unsort(dQ2.cpu().numpy(), permN), unsort(dK2.cpu().numpy(), permM), unsort(dV.cpu().numpy(), permM)),
                 gr, "geo no-dV")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_geo_without_target_rows(dt):
+    """No target rows (every target patch empty): the forward returns empty
+    outputs, and the backward's dK and dV are zero (no source row is in any
+    support); the padding jobs of the backward's plan launch shrink to V."""
+    say("geo without target rows", dt)
+    c = gen.make_small(1, 300, 64, 30, dtype=dt, seed=5)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    K, V = to_dev(c["K"], dt), to_dev(c["V"], dt)
+    Q = torch.empty(0, 64, dtype=tdt, device="cuda")
+    dO = torch.empty(0, 30, dtype=tdt, device="cuda")
+    offN = torch.zeros(3, dtype=torch.int32, device="cuda")          # two empty target patches
+    offM = torch.tensor([0, 100, 220, 300], dtype=torch.int32, device="cuda")
+    idx = torch.tensor([[0, 2], [1, 0]], dtype=torch.int32, device="cuda")
+    O, lse = ssc.coupling_geo_fwd(Q, K, V, offN, offM, idx, 0.125)
+    assert O.shape == (0, 30) and lse.shape == (0,)
+    dQ, dK, dV = ssc.coupling_geo_bwd(Q, K, V, offN, offM, idx, O, dO, lse, 0.125)
+    torch.cuda.synchronize()
+    assert dQ.shape == (0, 64)
+    assert torch.count_nonzero(dK).item() == 0 and torch.count_nonzero(dV).item() == 0
