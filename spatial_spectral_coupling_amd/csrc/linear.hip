@@ -224,8 +224,20 @@ __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts,
   const int u = threadIdx.x >> 5, e = threadIdx.x & 31;
   const int idx = blockIdx.x * 32 + e;
   float acc = 0.f;
-  if (idx < D * KP)
-    for (int b = u; b < nparts; b += 8) acc += part[(size_t)b * D * KP + idx];
+  if (idx < D * KP) {
+    // eight partials loaded together, added in the same order as one at a time
+    const float* src = part + idx;
+    constexpr size_t ST = (size_t)D * KP;
+    int b = u;
+    for (; b + 56 < nparts; b += 64) {
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[m] = __builtin_nontemporal_load(src + (size_t)(b + 8 * m) * ST);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc += v[m];
+    }
+    for (; b < nparts; b += 8) acc += src[(size_t)b * ST];
+  }
   s8[u][e] = acc;
   __syncthreads();
   if (u != 0 || idx >= D * KP) return;
