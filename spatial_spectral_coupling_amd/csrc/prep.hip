@@ -965,11 +965,23 @@ constexpr int kMaxD = 128;
 // per CU.
 constexpr int kSmallPatches = 2048;
 
+// s up to kGroupTop and at least kGroupMinCands candidates: the ranking first
+// keeps each 64-candidate group's top s (measured: 112 -> 76 us for the 640
+// patches of 160k vertices; slower for 256, which counts directly)
+constexpr int kGroupTop = 32;
+constexpr int kGroupMinCands = 512;
+
 template <bool SMALL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  constexpr int CAP = SMALL ? kSmallPatches : kMaxPatches;
+  constexpr int WCAP = (CAP + 63) / 64 * kGroupTop;  // group winners
   __shared__ double qb[kMaxD];
-  __shared__ double C[SMALL ? kSmallPatches : kMaxPatches];
+  __shared__ double C[CAP];
+  __shared__ double winv[WCAP];
+  __shared__ int win[WCAP];
+  __shared__ int nwin;
   const int p = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) nwin = 0;
   for (int c = tid; c < a.d; c += 256) qb[c] = a.Qbar[(size_t)p * a.d + c];
   __syncthreads();
   for (int q = tid; q < a.P_M; q += 256) {
@@ -989,6 +1001,45 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   }
   __syncthreads();
   // rank of q in the strict order (score desc, index asc)
+  if (a.s <= kGroupTop && a.P_M >= kGroupMinCands) {
+    // Two stages.  A candidate's rank within its group of 64 (the
+    // candidates a wave holds in one pass) is at most its rank overall, so
+    // the top s overall are among the groups' top s; and every candidate
+    // ahead of a top-s candidate is itself in the top s, so ranking the
+    // group winners against each other gives their exact overall ranks.
+    for (int base = 0; base < a.P_M; base += 256) {
+      const int q = base + tid, w0 = base + (tid & ~63);
+      const int wn = min(64, a.P_M - w0);  // (wave-uniform)
+      if (q < a.P_M) {
+        const double v = C[q];
+        int rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < wn; ++j) {
+          const double v2 = C[w0 + j];
+          rank += (v2 > v) || (v2 == v && w0 + j < q);
+        }
+        if (rank < a.s) {
+          const int slot = atomicAdd(&nwin, 1);
+          win[slot] = q;
+          winv[slot] = v;
+        }
+      }
+    }
+    __syncthreads();
+    const int nw = nwin;
+    for (int i = tid; i < nw; i += 256) {
+      const int q = win[i];
+      const double v = winv[i];
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < nw; ++j) {
+        const double v2 = winv[j];
+        rank += (v2 > v) || (v2 == v && win[j] < q);
+      }
+      if (rank < a.s) a.idx[(size_t)p * a.s + rank] = q;
+    }
+    return;
+  }
   for (int q = tid; q < a.P_M; q += 256) {
     const double v = C[q];
     int rank = 0;

@@ -267,7 +267,10 @@ def test_geo_repeat_in_later_chunk_fills_nan():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("P_N,P_M,s", [(9, 1301, 16), (5, 2501, 33), (7, 255, 255), (6, 3, 1)])
+# 1301 / 16, 512 / 8 and 2501 / 32 rank through the candidate groups (the last in the
+# kernel sized for the most patches); 2501 / 33, 255 / 255 and 3 / 1 count directly
+@pytest.mark.parametrize("P_N,P_M,s", [(9, 1301, 16), (5, 512, 8), (4, 2501, 32), (5, 2501, 33), (7, 255, 255),
+                                       (6, 3, 1)])
 def test_topk_exact_ties_break_to_lower_index(P_N, P_M, s):
     """Every score exact and many tied: small-integer descriptors, target
     patches of exactly 4 rows (means are exact quarters), source patches of
