@@ -2,8 +2,12 @@
 //   pack_kernel  -- rows of one tensor into the padded patch layout (row-major
 //                   copy and grouped-transposed copy), plus D = rowdot(dO, O)
 //                   and lse * log2(e) on the target side of the backward;
+//   pad_bf16_kernel -- bf16 rows padded to the MFMA width (ones / -D columns),
+//                   D and lse * log2(e) for the backward's target side;
 //   plan_kernel  -- validates patch offsets and the selection, builds padded
 //                   offsets, work items and the inverse selection lists;
+//   plan_pad_kernel -- the plan and the bf16 padding of a geo call in one
+//                   launch (the padding on the CUs the plan leaves idle);
 //   pool_kernel  -- patch-mean descriptors in fp64 ("pool source keys");
 //   topk_kernel  -- patch scores <Qbar_p, Kbar_q> in fp64 and the top-s source
 //                   patches per target patch, ties to the lower index
