@@ -318,6 +318,14 @@ ssc_status fmap_solve_bwd(ssc_dtype dtype, int n, int k, const void* PhiN, const
  * adjacency contents are checked on the device: an offset out of order or
  * a neighbour outside [0, n) computes nothing and writes seeds = labels = -1
  * and dist = NaN.  dtype is ignored (the path is fp64).
+ * From n = 32768 (and every vertex with at most 8 neighbours) the first
+ * steps run as a cooperative launch of 16 workgroups (fewer on a smaller
+ * GPU); if the runtime refuses it, or a grid-barrier wait of it gives up,
+ * one workgroup takes every step: the outputs are the same either way.
+ * Environment overrides, read at each call (tests and tuning):
+ * SSC_FPS_WIDE_STEPS (cap on those steps, 0 = none), SSC_FPS_WIDE_BLOCKS,
+ * SSC_FPS_WIDE_FRONTIER (a step whose round queues stay below it ends them),
+ * SSC_FPS_SPIN_LIMIT (polls of a barrier wait; 0 = give up at once).
  */
 ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const int* adj, int P, int* seeds,
                          int* labels, double* dist, void* ws, size_t ws_bytes, ssc_stream stream);

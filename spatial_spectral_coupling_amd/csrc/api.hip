@@ -3,8 +3,10 @@
 #include "ssc.h"
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <mutex>
 #include <string>
@@ -403,7 +405,8 @@ ssc_status check_fps(int n, int nnz, int P) {
 }
 
 struct FpsLayout {
-  size_t w = kNone, adjp = kNone, wp = kNone, stamp = kNone, queue = kNone, cmax = kNone, cflag = kNone, bad = kNone;
+  size_t w = kNone, adjp = kNone, wp = kNone, stamp = kNone, queue = kNone, cmax = kNone, cflag = kNone, bad = kNone,
+         ctl = kNone;
   size_t total = 0;
   int nchunk = 0, nblk = 0;
 };
@@ -426,6 +429,7 @@ FpsLayout make_fps_layout(int n, int nnz) {
   L.cmax = take((size_t)L.nchunk * 8);
   L.cflag = take((size_t)L.nchunk * 4);
   L.bad = take((size_t)L.nblk * 4);
+  L.ctl = take(sizeof(FpsCtl));
   L.total = o;
   return L;
 }
@@ -1271,6 +1275,21 @@ ssc_status fps_partition(int n, int nnz, const double* x, const int* off, const 
   a.adjp = at<int>(ws, L.adjp); a.wp = at<double>(ws, L.wp);
   a.cmax = at<unsigned long long>(ws, L.cmax); a.cflag = at<int>(ws, L.cflag); a.bad = at<int>(ws, L.bad);
   a.nchunk = L.nchunk; a.nblk = L.nblk;
+  a.ctl = at<FpsCtl>(ws, L.ctl);
+  // from kFpsWideMin vertices the first steps run on 16 workgroups until a
+  // step's largest round queue stays below 1024 vertices.  Overrides (tests
+  // and tuning): SSC_FPS_WIDE_STEPS caps those steps (0: none),
+  // SSC_FPS_WIDE_BLOCKS sets the workgroups, SSC_FPS_WIDE_FRONTIER the queue
+  // threshold, SSC_FPS_SPIN_LIMIT the polls of a barrier wait (0: every wait
+  // gives up at once, so the one-workgroup kernel redoes every step).
+  a.wide_steps = n >= kFpsWideMin ? P : 0;
+  a.spin = 1u << 20;
+  a.wide_blocks = 16;
+  a.wide_frontier = 1024;
+  if (const char* e = std::getenv("SSC_FPS_WIDE_FRONTIER")) a.wide_frontier = std::atoi(e);
+  if (const char* e = std::getenv("SSC_FPS_WIDE_STEPS")) a.wide_steps = std::max(0, std::min(P, std::atoi(e)));
+  if (const char* e = std::getenv("SSC_FPS_WIDE_BLOCKS")) a.wide_blocks = std::max(1, std::atoi(e));
+  if (const char* e = std::getenv("SSC_FPS_SPIN_LIMIT")) a.spin = (unsigned)std::strtoul(e, nullptr, 10);
   SSC_TRY(timed("fps", s, [&] { return launch_fps(a, s); }));
   return SSC_OK;
 }

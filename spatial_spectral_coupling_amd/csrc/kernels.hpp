@@ -304,7 +304,24 @@ struct FpsArgs {
   int* cflag;           // [nchunk] chunk touched by the current step (workspace)
   int* bad;             // [nblk] per-block adjacency check (workspace)
   int nchunk, nblk;
+  struct FpsCtl* ctl;   // control block of the multi-workgroup steps (workspace)
+  int wide_steps;       // steps 0 .. wide_steps - 1 run on many workgroups (0: none)
+  int wide_blocks;      // their workgroups (at most one per CU)
+  int wide_frontier;    // a step whose largest round queue stays below this ends them
+  unsigned spin;        // polls a grid-barrier wait may take before it gives up
 };
+// Control block of the multi-workgroup steps, zeroed by fps_prep.
+struct FpsCtl {
+  unsigned long long bar;  // grid-barrier arrivals
+  int abort;               // a barrier wait gave up: the one-workgroup kernel redoes every step
+  int status;              // 0: not run, 2: a step exceeded its round bound, 3: steps 0 .. t_end - 1 done
+  int t_end, r_end;        // steps done and rounds run by the multi-workgroup kernel
+  int cnt[3];              // queue counters of three consecutive rounds
+  int pad[7];
+};
+static_assert(sizeof(FpsCtl) == 64, "FpsCtl layout");
+// meshes from this many vertices run their first steps on many workgroups
+constexpr int kFpsWideMin = 32768;
 hipError_t launch_fps(const FpsArgs& a, hipStream_t st);
 
 // Launchers (return hipGetLastError() after the launch).

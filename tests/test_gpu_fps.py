@@ -99,6 +99,46 @@ def test_fps_large_mesh_global_stamps():
     check_exact(x, e, 3, "sphere n=270000 P=3")
 
 
+@pytest.mark.parametrize("env", [{"SSC_FPS_WIDE_STEPS": "0"}, {}, {"SSC_FPS_WIDE_STEPS": "1"},
+                                 {"SSC_FPS_WIDE_FRONTIER": "0"}, {"SSC_FPS_SPIN_LIMIT": "0"},
+                                 {"SSC_FPS_WIDE_BLOCKS": "1", "SSC_FPS_WIDE_FRONTIER": "0"}],
+                         ids=["off", "default", "one-step", "every-step", "barrier-gives-up", "one-block"])
+def test_fps_multi_workgroup_steps(monkeypatch, env):
+    # Meshes from 32768 vertices run their first steps on many workgroups
+    # (until a step's largest round queue stays small).  With those steps
+    # off, on (the default), limited to step 0, on for every step, with every
+    # grid-barrier wait giving up at once (the one-workgroup kernel then
+    # redoes every step from the initial state), and on a grid of one
+    # workgroup, the results must equal the oracle's bit for bit.
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    x, e = sphere_mesh(40000, 9)
+    check_exact(x, e, 12, f"sphere n=40000 P=12 {env}")
+
+
+def test_fps_multi_workgroup_small_and_irregular(monkeypatch):
+    # every step on many workgroups for small meshes, a mesh of several
+    # components (unreached vertices stay at +inf until a seed lands there)
+    # and a mesh whose hub exceeds the padded adjacency (the one-workgroup
+    # kernel then takes every step)
+    monkeypatch.setenv("SSC_FPS_WIDE_STEPS", "1000")
+    monkeypatch.setenv("SSC_FPS_WIDE_FRONTIER", "0")
+    x, e = sphere_mesh(300, 4)
+    check_exact(x, e, 30, "sphere n=300 P=30, all steps wide")
+    x1 = np.c_[np.arange(5.0), np.zeros(5), np.zeros(5)]
+    x2 = np.c_[np.arange(4.0), np.full(4, 10.0), np.zeros(4)]
+    x3 = np.c_[np.arange(3.0), np.full(3, 20.0), np.zeros(3)]
+    e3 = np.array([[0, 1], [1, 2], [2, 3], [3, 4], [5, 6], [6, 7], [7, 8], [9, 10], [10, 11]])
+    for P in (1, 2, 3, 5):
+        check_exact(np.vstack([x1, x2, x3]), e3, P, f"three components P={P}, all steps wide")
+    m = 2000
+    t = np.linspace(0.0, 2.0 * np.pi, m, endpoint=False)
+    rim = np.c_[np.cos(t), np.sin(t), np.zeros(m)]
+    xh = np.vstack([np.zeros((1, 3)), rim])
+    eh = [(0, i) for i in range(1, m + 1)] + [(i, i % m + 1) for i in range(1, m + 1)]
+    check_exact(xh, np.array(eh), 5, f"hub + ring of {m}, P=5, wide steps requested")
+
+
 def test_fps_disconnected_and_single_vertex():
     # three components; with 2 seeds the third stays at +inf with label 0
     x1 = np.c_[np.arange(5.0), np.zeros(5), np.zeros(5)]
