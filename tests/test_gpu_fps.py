@@ -160,7 +160,7 @@ def test_fps_60k_full_oracle():
     check_exact(x, e, 256, "60k P=256")
 
 
-def test_fps_160k_properties():
+def test_fps_160k_properties(monkeypatch):
     c = gen.make_config(4, with_partition=False)
     x, e, n = c["xM"], c["edges"], len(c["xM"])
     say(f"160k mesh: n={n} edges={len(e)}")
@@ -182,6 +182,20 @@ def test_fps_160k_properties():
     has[dst[ok]] = True
     has[s] = True
     assert has.all(), int((~has).sum())
+    # the sampling order at a few steps: seed t is the vertex farthest from
+    # seeds 0 .. t-1 (multi-source runs form the same bits, as above), ties
+    # to the lower index
+    for t in (1, 2, 5, 17, 100, 639):
+        dt = dijkstra(g, directed=True, indices=s[:t], min_only=True)
+        assert s[t] == int(np.argmax(dt)), t
+    # the first steps run on many workgroups by default: the one-workgroup
+    # path gives the same bits
+    monkeypatch.setenv("SSC_FPS_WIDE_STEPS", "0")
+    s1, l1, d1 = run_gpu(x, off, adj, 640)
+    say(f"160k: one-workgroup path equal {np.array_equal(s1, s) and np.array_equal(l1, l) and np.array_equal(d1, d)}")
+    np.testing.assert_array_equal(s1, s)
+    np.testing.assert_array_equal(l1, l)
+    np.testing.assert_array_equal(d1, d)
 
 
 def test_fps_invalid_inputs():
