@@ -321,14 +321,23 @@ struct LinLayout {
   size_t part = kNone, M = kNone, MT = kNone, dM = kNone, dMT = kNone, rden = kNone, s = kNone;
   size_t total = 0;
   int parts_M = 0, parts_N = 0;
+  int gram_rows = kLinGramRows;  // rows per workgroup of the Gram sums
 };
 
 LinLayout make_lin_layout(bool bwd, int n_N, int n_M, int d, int k) {
   LinLayout L;
   const size_t KP = (size_t)kpad_lin(k);
-  L.parts_M = (n_M + kLinGramRows - 1) / kLinGramRows;
-  L.parts_N = (n_N + kLinGramRows - 1) / kLinGramRows;
-  const int parts = bwd ? (L.parts_M > L.parts_N ? L.parts_M : L.parts_N) : L.parts_M;
+  // The Gram workgroups (one per CU: their tiles fill most of the LDS) run
+  // in one round where possible: the rows per workgroup double until the
+  // forward's key blocks, or the backward's key and query blocks together,
+  // number at most kRoundCUs.  Fewer workgroups also mean fewer partials.
+  auto nblk = [&](int n, int rows) { return (n + rows - 1) / rows; };
+  auto blocks = [&](int rows) { return nblk(n_M, rows) + (bwd ? nblk(n_N, rows) : 0); };
+  while (blocks(L.gram_rows) > kRoundCUs && L.gram_rows < (1 << 22)) L.gram_rows *= 2;
+  L.parts_M = nblk(n_M, L.gram_rows);
+  L.parts_N = nblk(n_N, L.gram_rows);
+  // the backward keeps both Gram sums' partials (one launch forms both)
+  const int parts = bwd ? L.parts_M + L.parts_N : L.parts_M;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = o;
@@ -1064,10 +1073,10 @@ ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   LinArgs a{};
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.den = den;
   a.part = at<float>(ws, L.part); a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT);
-  a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(timed("lin_gram", s, [&] { return launch_lin_gram(d, KP, 0, false, a, L.parts_M, s); }));
+  a.n_N = n_N; a.n_M = n_M; a.k = k; a.gram_rows = L.gram_rows;
+  SSC_TRY(timed("lin_gram", s, [&] { return launch_lin_gram(d, KP, false, a, L.parts_M, s); }));
   SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), nullptr, nullptr, s));
-  SSC_TRY(timed("lin_apply", s, [&] { return launch_lin_apply(d, KP, 0, false, a, s); }));
+  SSC_TRY(timed("lin_apply", s, [&] { return launch_lin_apply(d, KP, false, a, s); }));
   return SSC_OK;
 }
 
@@ -1094,15 +1103,14 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
   a.rden = at<float>(ws, L.rden); a.s = at<float>(ws, L.s); a.part = at<float>(ws, L.part);
   a.M = at<char>(ws, L.M); a.MT = at<char>(ws, L.MT); a.dM = at<char>(ws, L.dM); a.dMT = at<char>(ws, L.dMT);
   a.dQ = dQ; a.dK = dK; a.dV = dV;
-  a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(d, KP, 0, false, a, L.parts_M, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), nullptr, nullptr, s));
-  SSC_TRY(launch_lin_rowprep(a, s));
-  SSC_TRY(launch_lin_apply(d, KP, 1, false, a, s));
-  SSC_TRY(launch_lin_gram(d, KP, 1, false, a, L.parts_N, s));
-  SSC_TRY(launch_lin_reduce(d, KP, a.part, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), nullptr, nullptr, s));
-  SSC_TRY(launch_lin_apply(d, KP, 2, false, a, s));
-  SSC_TRY(launch_lin_apply(d, KP, 3, false, a, s));
+  a.n_N = n_N; a.n_M = n_M; a.k = k; a.gram_rows = L.gram_rows;
+  a.partN = a.part + (size_t)L.parts_M * d * KP;
+  // both Gram sums (the second also forms rden and s), both reductions, then
+  // the dQ, dK and dV rows: three launches
+  SSC_TRY(launch_lin_gram_bwd(d, KP, false, a, L.parts_M, L.parts_N, s));
+  SSC_TRY(launch_lin_reduce2(d, KP, a.part, L.parts_M, at<char>(ws, L.M), at<char>(ws, L.MT), nullptr, nullptr,
+                             a.partN, L.parts_N, at<char>(ws, L.dM), at<char>(ws, L.dMT), nullptr, nullptr, s));
+  SSC_TRY(launch_lin_apply_bwd(d, KP, false, a, s));
   return SSC_OK;
 }
 
@@ -1147,11 +1155,11 @@ ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
   a.Q = at<bf16>(ws, L.FQ); a.K = at<bf16>(ws, L.FK); a.V = V; a.O = O; a.den = lnden; a.rowoff = rowoff;
   a.part = at<float>(ws, L.lin.part); a.M = at<char>(ws, L.lin.M); a.MT = at<char>(ws, L.lin.MT);
   a.Mlo = at<char>(ws, L.Mlo); a.MTlo = at<char>(ws, L.MTlo);
-  a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(m, KP, 0, true, a, L.lin.parts_M, s));
+  a.n_N = n_N; a.n_M = n_M; a.k = k; a.gram_rows = L.lin.gram_rows;
+  SSC_TRY(launch_lin_gram(m, KP, true, a, L.lin.parts_M, s));
   SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
                             at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
-  SSC_TRY(launch_lin_apply(m, KP, 0, true, a, s));
+  SSC_TRY(launch_lin_apply(m, KP, true, a, s));
   return SSC_OK;
 }
 
@@ -1187,17 +1195,14 @@ ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
   a.Mlo = at<char>(ws, L.Mlo); a.MTlo = at<char>(ws, L.MTlo); a.dMlo = at<char>(ws, L.dMlo);
   a.dMTlo = at<char>(ws, L.dMTlo);
   a.dQ = at<float>(ws, L.dFQ); a.dK = at<float>(ws, L.dFK); a.dV = dV;
-  a.n_N = n_N; a.n_M = n_M; a.k = k;
-  SSC_TRY(launch_lin_gram(m, KP, 0, true, a, L.lin.parts_M, s));
-  SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
-                            at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), s));
-  SSC_TRY(launch_lin_rowprep(a, s));
-  SSC_TRY(launch_lin_apply(m, KP, 1, true, a, s));
-  SSC_TRY(launch_lin_gram(m, KP, 1, true, a, L.lin.parts_N, s));
-  SSC_TRY(launch_lin_reduce(m, KP, a.part, L.lin.parts_N, at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT),
-                            at<char>(ws, L.dMlo), at<char>(ws, L.dMTlo), s));
-  SSC_TRY(launch_lin_apply(m, KP, 2, true, a, s));
-  SSC_TRY(launch_lin_apply(m, KP, 3, true, a, s));
+  a.n_N = n_N; a.n_M = n_M; a.k = k; a.gram_rows = L.lin.gram_rows;
+  a.partN = a.part + (size_t)L.lin.parts_M * m * KP;
+  SSC_TRY(launch_lin_gram_bwd(m, KP, true, a, L.lin.parts_M, L.lin.parts_N, s));
+  SSC_TRY(launch_lin_reduce2(m, KP, a.part, L.lin.parts_M, at<char>(ws, L.lin.M), at<char>(ws, L.lin.MT),
+                             at<char>(ws, L.Mlo), at<char>(ws, L.MTlo), a.partN, L.lin.parts_N,
+                             at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT), at<char>(ws, L.dMlo),
+                             at<char>(ws, L.dMTlo), s));
+  SSC_TRY(launch_lin_apply_bwd(m, KP, true, a, s));
   PfArgs p{};
   p.W = W; p.scale = scale;
   p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.dF = at<float>(ws, L.dFQ); p.dX = dQ;

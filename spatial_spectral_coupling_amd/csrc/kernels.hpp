@@ -211,7 +211,7 @@ struct TopkArgs {
 
 // Linear-attention (ELU feature map) coupling: one argument block for all
 // of its kernels.
-constexpr int kLinGramRows = 256;  // rows per workgroup of the Gram sums
+constexpr int kLinGramRows = 256;  // least rows per workgroup of the Gram sums
 struct LinArgs {
   const void* Q;        // [n_N x D] bf16
   const void* K;        // [n_M x D] bf16
@@ -222,6 +222,7 @@ struct LinArgs {
   float* rden;          // [n_N]     1 / den (backward scratch)
   float* s;             // [n_N]     (dO . O) / den (backward scratch)
   float* part;          // [nparts x D x KP] Gram partials (scratch)
+  float* partN;         // backward: [nparts_N x D x KP] partials of the query-side Gram
   const void* M;        // [D x KP]  bf16 KVz_ext (row-major)
   const void* MT;       // [KP x D]  bf16 KVz_ext^T
   const void* dM;       // [D x KP]  bf16 dKVz_ext
@@ -237,6 +238,7 @@ struct LinArgs {
   float* dV;            // [n_M x k]
   const float* rowoff;  // [n_N] identity feature map, forward: den is written as ln(den) + rowoff
   int n_N, n_M, k;
+  int gram_rows;        // rows per workgroup of the Gram sums (a multiple of kLinGramRows)
 };
 
 // Performer (FAVOR+) coupling pieces (performer.hip); m = D random features.
@@ -376,12 +378,21 @@ hipError_t launch_plan_pad(const PlanArgs& a, const PackArgs* jobs, const int* g
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // ident: the rows of Q / K are precomputed features (identity feature map)
-hipError_t launch_lin_gram(int D, int KP, int mode, bool ident, const LinArgs& a, int grid, hipStream_t st);
+// Forward Gram sums phi(K)^T V_ext over `grid` row blocks into a.part.
+hipError_t launch_lin_gram(int D, int KP, bool ident, const LinArgs& a, int grid, hipStream_t st);
+// Backward: both Gram sums in one launch (gM key-row blocks into a.part, gN
+// query-row blocks into a.partN; the query side also writes a.rden and a.s).
+hipError_t launch_lin_gram_bwd(int D, int KP, bool ident, const LinArgs& a, int gM, int gN, hipStream_t st);
 // Mlo / MTlo (optional, may be null): the bf16 rounding remainders
 hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo,
                              hipStream_t st);
-hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st);
-// mode 0: O / den, 1: dQ, 2: dK, 3: dV
-hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st);
+// the backward's two reductions in one launch
+hipError_t launch_lin_reduce2(int D, int KP, const float* part0, int nparts0, void* M0, void* MT0, void* Mlo0,
+                              void* MTlo0, const float* part1, int nparts1, void* M1, void* MT1, void* Mlo1,
+                              void* MTlo1, hipStream_t st);
+// forward rows: O and den
+hipError_t launch_lin_apply(int D, int KP, bool ident, const LinArgs& a, hipStream_t st);
+// backward rows in one launch: dQ, dK and dV
+hipError_t launch_lin_apply_bwd(int D, int KP, bool ident, const LinArgs& a, hipStream_t st);
 
 }  // namespace ssc

@@ -17,7 +17,10 @@
 //   dK = phi'(K) * (V_ext dKVz_ext^T), dV = phi(K) dKV.
 // Everything is O(n (d + k)) memory traffic: the kernels are HBM / latency
 // bound; the Gram sums are split over row blocks and reduced in a fixed
-// order (deterministic).
+// order (deterministic).  The forward is three launches (Gram sums,
+// reduction, rows); so is the backward, whose two Gram sums (the second one
+// also forming s), two reductions and three row passes (dQ, dK, dV) each
+// share a launch, as none reads what the others of its launch write.
 // With FEAT = 1 the kernels take precomputed feature rows in place of Q and
 // K (identity map, phi' = 1: the "dQ" / "dK" outputs are then the gradients
 // w.r.t. the features); the Performer coupling runs on them.
@@ -33,6 +36,7 @@ using tb::static_for;
 using tb::TrReader;
 
 constexpr int kGramTile = 128;  // rows per LDS tile of the Gram kernel
+constexpr int kGramWaves = 8;   // waves per workgroup of the Gram kernel (two per SIMD)
 constexpr int kApplyRows = 128; // rows per workgroup of the row kernels (4 waves x 32)
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e); }
@@ -92,22 +96,44 @@ __device__ __forceinline__ void stage_matrix(char* lds, const bf16* g, int tid) 
 // Gram sums over a block of rows:  part[b] = A^T B  ([D x KP], fp32)
 //   MODE 0 (forward):  A = phi(K),  B = V_ext = [V | 1 at column KP-1]
 //   MODE 1 (backward): A = phi(Q),  B = G_ext = [dO / den | -s at KP-1]
-// Rows past the end contribute 0.
+// Rows past the end contribute 0.  In MODE 1 the row terms rden = 1 / den
+// and s = (dO . O) / den are formed here too: each thread adds the products
+// of its 8-column chunk of dO and O, the chunk sums of a row are added in
+// column order, and -s is then written into the last column of the tile
+// (rden and s also go out for the dQ rows).
 // ---------------------------------------------------------------------------
 template <int D, int KP, int MODE, int FEAT>
-__global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
-  constexpr int AP = Geo<D>::PITCH, BP = Geo<KP>::PITCH;
+struct GramCfg {
+  static constexpr int AP = Geo<D>::PITCH, BP = Geo<KP>::PITCH;
   // identity features, backward: G_ext as a bf16 high + low pair
-  constexpr bool BLO = FEAT == 1 && MODE == 1;
-  // rows per LDS tile (halved where the low part would not fit)
-  constexpr int TR = BLO && (kGramTile * (AP + 2 * BP) > 160 * 1024) ? kGramTile / 2 : kGramTile;
-  __shared__ __attribute__((aligned(16))) char As[TR * AP];
-  __shared__ __attribute__((aligned(16))) char Bs[TR * BP];
-  __shared__ __attribute__((aligned(16))) char Bl[BLO ? TR * BP : 16];
-  constexpr int NMB = D / 32, NNB = KP / 32, NB = NMB * NNB, NBW = (NB + 3) / 4;
+  static constexpr bool BLO = FEAT == 1 && MODE == 1;
+  static constexpr int PS = KP / 8 + 1;  // row stride of the chunk dot products
+  static constexpr int bytes(int tr) { return tr * AP + tr * BP * (BLO ? 2 : 1) + (MODE == 1 ? tr * PS * 4 : 0); }
+  // rows per LDS tile: halved for the backward (its tile loads of dO and O
+  // stay in flight in registers during the MFMAs) and where the tile would
+  // not fit the LDS
+  static constexpr int TR = MODE == 1 || bytes(kGramTile) > 160 * 1024 ? kGramTile / 2 : kGramTile;
+  static constexpr int LDS = bytes(TR);
+};
+
+template <int D, int KP, int MODE, int FEAT>
+__device__ __forceinline__ void gram_body(const LinArgs& a, int blk, char* smem, float* part_out) {
+  using C = GramCfg<D, KP, MODE, FEAT>;
+  constexpr int AP = C::AP, BP = C::BP, TR = C::TR, PS = C::PS;
+  constexpr bool BLO = C::BLO;
+  char* As = smem;
+  char* Bs = As + TR * AP;
+  char* Bl = Bs + TR * BP;
+  float* pdot = reinterpret_cast<float*>(Bs + TR * BP * (BLO ? 2 : 1));
+  // kGramWaves waves: wave w owns the 32-row block mb = w % NMB of the
+  // output and its column blocks nb = w / NMB + t * (kGramWaves / NMB), so
+  // its A operand fragment is read once per k step
+  constexpr int NMB = D / 32, NNB = KP / 32, WPM = kGramWaves / NMB, NBW = (NNB + WPM - 1) / WPM;
+  constexpr int NT = kGramWaves * 64;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mb = wave % NMB, nb0 = wave / NMB;
   const int h = lane >> 5, l32 = lane & 31;
   const int tr_r = 4 * h + ((lane & 15) >> 2), tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   TrReader<D> ta;
@@ -116,32 +142,37 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
   tbr.init(tr_r, tr_c);
 
   const int n = MODE == 0 ? a.n_M : a.n_N;
-  const int r_begin = blockIdx.x * kLinGramRows;
-  const int r_end = min(n, r_begin + kLinGramRows);
+  const int r_begin = blk * a.gram_rows;
+  const int r_end = min(n, r_begin + a.gram_rows);
   const bf16* X = reinterpret_cast<const bf16*>(MODE == 0 ? a.K : a.Q);
   const bf16* Y = reinterpret_cast<const bf16*>(MODE == 0 ? a.V : a.dO);
   const bool vec = (a.k & 7) == 0;
+  const bool vec4 = (a.k & 3) == 0;
+  const int nch = (a.k + 7) / 8;  // chunks of a row that hold data
 
   f32x16 acc[NBW];
 #pragma unroll
   for (int t = 0; t < NBW; ++t) acc[t] = f32x16{};
 
-  for (int r0 = r_begin; r0 < r_end; r0 += TR) {
-    // every load of the tile first (in flight together), then the feature
-    // map / scaling and the LDS stores
-    constexpr int NXA = TR * (D / 8) / 256, NYB = TR * (KP / 8) / 256;
-    static_assert(NXA * 256 == TR * (D / 8) && NYB * 256 == TR * (KP / 8), "gram tile split");
-    bf16x8 xa[NXA], yb[NYB];
-    float rdv[MODE == 1 ? NYB : 1], sv[MODE == 1 ? NYB : 1];
+  // The global loads of a tile go into registers; those of the next tile are
+  // issued as soon as the current one is in LDS, so they are in flight
+  // during its MFMAs.
+  // 16-byte chunks of a tile and per thread (the last round may be partial)
+  constexpr int CA = TR * (D / 8), CB = TR * (KP / 8);
+  constexpr int NXA = (CA + NT - 1) / NT, NYB = (CB + NT - 1) / NT;
+  bf16x8 xa[NXA], yb[NYB];
+  f32x4 ob[MODE == 1 ? 2 * NYB : 1];
+  float dv[MODE == 1 ? NYB : 1];
+  auto load_tile = [&](int r0) {
 #pragma unroll
     for (int j = 0; j < NXA; ++j) {
-      const int ch = tid + 256 * j, r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
-      xa[j] = gr < r_end ? ld8(X + (size_t)gr * D + c8 * 8) : bf16x8{};
+      const int ch = tid + NT * j, r = ch / (D / 8), c8 = ch - r * (D / 8), gr = r0 + r;
+      xa[j] = (CA % NT == 0 || ch < CA) && gr < r_end ? ld8(X + (size_t)gr * D + c8 * 8) : bf16x8{};
     }
 #pragma unroll
     for (int j = 0; j < NYB; ++j) {
-      const int ch = tid + 256 * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
-      const bool in = gr < r_end && c8 * 8 < a.k;
+      const int ch = tid + NT * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+      const bool in = (CB % NT == 0 || ch < CB) && gr < r_end && c8 * 8 < a.k;
       if (in && vec && c8 * 8 + 8 <= a.k) {
         yb[j] = ld8(Y + (size_t)gr * a.k + c8 * 8);
       } else if (in) {
@@ -152,13 +183,30 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
         yb[j] = bf16x8{};
       }
       if (MODE == 1) {
-        rdv[MODE == 1 ? j : 0] = gr < r_end ? a.rden[gr] : 0.f;
-        sv[MODE == 1 ? j : 0] = gr < r_end && c8 == KP / 8 - 1 ? a.s[gr] : 0.f;
+        const int jj = MODE == 1 ? j : 0;
+        dv[jj] = gr < r_end ? a.den[gr] : 1.f;
+        const float* Or = a.O + (size_t)(gr < r_end ? gr : 0) * a.k + c8 * 8;
+        if (in && vec4 && c8 * 8 + 8 <= a.k) {
+          ob[2 * jj] = *reinterpret_cast<const f32x4*>(Or);
+          ob[2 * jj + 1] = *reinterpret_cast<const f32x4*>(Or + 4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float o = in && c8 * 8 + e < a.k ? Or[e] : 0.f;
+            if (e < 4) ob[2 * jj][e] = o;
+            else ob[2 * jj + 1][e - 4] = o;
+          }
+        }
       }
     }
+  };
+  if (r_begin < r_end) load_tile(r_begin);
+
+  for (int r0 = r_begin; r0 < r_end; r0 += TR) {
 #pragma unroll
     for (int j = 0; j < NXA; ++j) {
-      const int ch = tid + 256 * j, r = ch / (D / 8), c8 = ch - r * (D / 8);
+      const int ch = tid + NT * j, r = ch / (D / 8), c8 = ch - r * (D / 8);
+      if (CA % NT != 0 && ch >= CA) continue;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = r0 + r < r_end ? feat<FEAT>((float)xa[j][e]) : 0.f;
@@ -166,15 +214,22 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < NYB; ++j) {
-      const int ch = tid + 256 * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+      const int ch = tid + NT * j, r = ch / (KP / 8), c8 = ch - r * (KP / 8), gr = r0 + r;
+      if (CB % NT != 0 && ch >= CB) continue;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (float)yb[j][e];
       if (MODE == 1) {
+        const int jj = MODE == 1 ? j : 0;
+        float pd = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= rdv[MODE == 1 ? j : 0];
+        for (int e = 0; e < 8; ++e) pd += v[e] * (e < 4 ? ob[2 * jj][e] : ob[2 * jj + 1][e - 4]);
+        if (gr < r_end && c8 < nch) pdot[r * PS + c8] = pd;
+        const float rd = 1.f / dv[jj];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= rd;
       }
-      if (gr < r_end && c8 == KP / 8 - 1) v[7] = MODE == 0 ? 1.f : -sv[MODE == 1 ? j : 0];
+      if (MODE == 0 && gr < r_end && c8 == KP / 8 - 1) v[7] = 1.f;
       const bf16x8 hv = pack8(v);
       *reinterpret_cast<bf16x8*>(Bs + r * BP + c8 * 16) = hv;
       if (BLO) {
@@ -184,49 +239,89 @@ __global__ __launch_bounds__(256) void lin_gram(LinArgs a) {
         *reinterpret_cast<bf16x8*>(Bl + r * BP + c8 * 16) = pack8(lo);
       }
     }
+    if (r0 + TR < r_end) load_tile(r0 + TR);
     __syncthreads();
+    if (MODE == 1) {
+      // s of each row of the tile: its chunk sums in column order; -s goes
+      // into column KP-1 (past k, so far a zero)
+      const int gr = r0 + tid;
+      if (tid < TR && gr < r_end) {
+        float sum = 0.f;
+        for (int c = 0; c < nch; ++c) sum += pdot[tid * PS + c];
+        const float rd = 1.f / a.den[gr];
+        const float sv = sum * rd;
+        const bf16 hs = (bf16)(-sv);
+        *reinterpret_cast<bf16*>(Bs + tid * BP + (KP - 1) * 2) = hs;
+        if (BLO) *reinterpret_cast<bf16*>(Bl + tid * BP + (KP - 1) * 2) = (bf16)(-sv - (float)hs);
+        a.rden[gr] = rd;
+        a.s[gr] = sv;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int kc = 0; kc < TR / 16; ++kc) {
+      const bf16x8 af = ta.frag(As, mb, kc);
 #pragma unroll
       for (int t = 0; t < NBW; ++t) {
-        const int bi = wave + 4 * t;
-        if (NB % 4 == 0 || bi < NB) {
-          const bf16x8 af = ta.frag(As, bi / NNB, kc);
-          acc[t] = mma(af, tbr.frag(Bs, bi % NNB, kc), acc[t]);
-          if (BLO) acc[t] = mma(af, tbr.frag(Bl, bi % NNB, kc), acc[t]);
+        const int nb = nb0 + WPM * t;
+        if (NNB % WPM == 0 || nb < NNB) {
+          acc[t] = mma(af, tbr.frag(Bs, nb, kc), acc[t]);
+          if (BLO) acc[t] = mma(af, tbr.frag(Bl, nb, kc), acc[t]);
         }
       }
     }
     __syncthreads();
   }
-  float* part = a.part + (size_t)blockIdx.x * D * KP;
+  float* part = part_out + (size_t)blk * D * KP;
 #pragma unroll
   for (int t = 0; t < NBW; ++t) {
-    const int bi = wave + 4 * t;
-    if (NB % 4 == 0 || bi < NB) {
-      const int mb = bi / NNB, nb = bi % NNB;
+    const int nb = nb0 + WPM * t;
+    if (NNB % WPM == 0 || nb < NNB) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) part[(size_t)(mb * 32 + c_row(i, h)) * KP + nb * 32 + l32] = acc[t][i];
     }
   }
 }
 
+// Forward: the Gram sums of the key side alone.
+template <int D, int KP, int FEAT>
+__global__ __launch_bounds__(kGramWaves * 64) void lin_gram(LinArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GramCfg<D, KP, 0, FEAT>::LDS];
+  gram_body<D, KP, 0, FEAT>(a, blockIdx.x, smem, a.part);
+}
+
+// Backward: both Gram sums in one launch (they read only inputs): workgroups
+// [0, gM) sum phi(K)^T V_ext into part, the others phi(Q)^T G_ext into partN.
+template <int D, int KP, int FEAT>
+__global__ __launch_bounds__(kGramWaves * 64) void lin_gram_bwd(LinArgs a, int gM) {
+  constexpr int L0 = GramCfg<D, KP, 0, FEAT>::LDS, L1 = GramCfg<D, KP, 1, FEAT>::LDS;
+  __shared__ __attribute__((aligned(16))) char smem[L0 > L1 ? L0 : L1];
+  if ((int)blockIdx.x < gM) gram_body<D, KP, 0, FEAT>(a, blockIdx.x, smem, a.part);
+  else gram_body<D, KP, 1, FEAT>(a, (int)blockIdx.x - gM, smem, a.partN);
+}
+
 // Fixed-order sum of the Gram partials, written as bf16 in both layouts:
 // M [D x KP] and MT [KP x D]; with Mlo / MTlo also the bf16 rounding of the
 // remainder (the pair carries the sum to about 2^-17).
+struct RedJob {
+  const float* part;
+  int nparts;
+  bf16 *M, *MT, *Mlo, *MTlo;
+};
+
 template <int D, int KP>
-__global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts, bf16* M, bf16* MT, bf16* Mlo,
-                                                  bf16* MTlo) {
+__device__ __forceinline__ void reduce_body(const RedJob& j, int blk) {
   // eight threads per output element: thread u sums the partials u, u + 8,
   // ... (one of eight independent partial sums), then the eight sums are
   // combined in a fixed order (deterministic)
   __shared__ float s8[8][32];
   const int u = threadIdx.x >> 5, e = threadIdx.x & 31;
-  const int idx = blockIdx.x * 32 + e;
+  const int idx = blk * 32 + e;
+  const int nparts = j.nparts;
   float acc = 0.f;
   if (idx < D * KP) {
     // eight partials loaded together, added in the same order as one at a time
-    const float* src = part + idx;
+    const float* src = j.part + idx;
     constexpr size_t ST = (size_t)D * KP;
     int b = u;
     for (; b + 56 < nparts; b += 64) {
@@ -244,43 +339,26 @@ __global__ __launch_bounds__(256) void lin_reduce(const float* part, int nparts,
   const float s = ((s8[0][e] + s8[1][e]) + (s8[2][e] + s8[3][e])) + ((s8[4][e] + s8[5][e]) + (s8[6][e] + s8[7][e]));
   const int d = idx / KP, c = idx - d * KP;
   const bf16 v = (bf16)s;
-  M[idx] = v;
-  MT[(size_t)c * D + d] = v;
-  if (Mlo != nullptr) {
+  j.M[idx] = v;
+  j.MT[(size_t)c * D + d] = v;
+  if (j.Mlo != nullptr) {
     const bf16 lo = (bf16)(s - (float)v);
-    Mlo[idx] = lo;
-    MTlo[(size_t)c * D + d] = lo;
+    j.Mlo[idx] = lo;
+    j.MTlo[(size_t)c * D + d] = lo;
   }
 }
 
-// Per target row of the backward: rden = 1 / den, s = (dO . O) / den
-// (16 lanes per row, 16 rows per workgroup; the 16 partial dot products are
-// added in a fixed butterfly order).
-__global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
-  const int sub = threadIdx.x & 15;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const bool ok = row < a.n_N;
-  const bf16* dO = reinterpret_cast<const bf16*>(a.dO) + (size_t)(ok ? row : 0) * a.k;
-  const float* O = a.O + (size_t)(ok ? row : 0) * a.k;
-  float acc = 0.f;
-  if (ok) {
-    if ((a.k & 3) == 0) {
-      for (int c = 4 * sub; c < a.k; c += 64) {
-        const bf16x4 g = *reinterpret_cast<const bf16x4*>(dO + c);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(O + c);
-        acc += ((float)g[0] * o[0] + (float)g[1] * o[1]) + ((float)g[2] * o[2] + (float)g[3] * o[3]);
-      }
-    } else {
-      for (int c = sub; c < a.k; c += 16) acc += (float)dO[c] * O[c];
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (ok && sub == 0) {
-    const float rd = 1.f / a.den[row];
-    a.rden[row] = rd;
-    a.s[row] = acc * rd;
-  }
+template <int D, int KP>
+__global__ __launch_bounds__(256) void lin_reduce(RedJob j) {
+  reduce_body<D, KP>(j, blockIdx.x);
+}
+
+// The backward's two reductions in one launch (G workgroups each).
+template <int D, int KP>
+__global__ __launch_bounds__(256) void lin_reduce2(RedJob j0, RedJob j1) {
+  constexpr int G = (D * KP + 31) / 32;
+  if ((int)blockIdx.x < G) reduce_body<D, KP>(j0, blockIdx.x);
+  else reduce_body<D, KP>(j1, (int)blockIdx.x - G);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,14 +374,21 @@ __global__ __launch_bounds__(256) void lin_rowprep(LinArgs a) {
 // row and the operand fragments of that row come from its own registers.
 // ---------------------------------------------------------------------------
 template <int D, int KP, int MODE, int FEAT>
-__global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
+struct ApplyCfg {
   // which layouts this mode reads, and whether with a low part
-  constexpr bool USE_T = MODE == 0 || MODE == 3;
-  constexpr bool USE_M = MODE == 1 || MODE == 2;
-  constexpr bool LO_T = FEAT && MODE == 0, LO_M = FEAT && USE_M;
-  constexpr int SZ_T = USE_T ? KP * Geo<D>::PITCH : 0;  // [KP x D] layout
-  constexpr int SZ_M = USE_M ? D * Geo<KP>::PITCH : 0;  // [D x KP] layout
-  __shared__ __attribute__((aligned(16))) char lds[SZ_T * (LO_T ? 2 : 1) + SZ_M * (LO_M ? 2 : 1) + 16];
+  static constexpr bool USE_T = MODE == 0 || MODE == 3;
+  static constexpr bool USE_M = MODE == 1 || MODE == 2;
+  static constexpr bool LO_T = FEAT && MODE == 0, LO_M = FEAT && USE_M;
+  static constexpr int SZ_T = USE_T ? KP * Geo<D>::PITCH : 0;  // [KP x D] layout
+  static constexpr int SZ_M = USE_M ? D * Geo<KP>::PITCH : 0;  // [D x KP] layout
+  static constexpr int LDS = SZ_T * (LO_T ? 2 : 1) + SZ_M * (LO_M ? 2 : 1) + 16;
+};
+
+template <int D, int KP, int MODE, int FEAT>
+__device__ __forceinline__ void apply_body(const LinArgs& a, int blk, char* lds) {
+  using C = ApplyCfg<D, KP, MODE, FEAT>;
+  constexpr bool USE_T = C::USE_T, USE_M = C::USE_M, LO_T = C::LO_T, LO_M = C::LO_M;
+  constexpr int SZ_T = C::SZ_T, SZ_M = C::SZ_M;
   char* LT = lds;
   char* LTlo = lds + SZ_T;
   char* LM = lds + SZ_T * (LO_T ? 2 : 1);
@@ -313,7 +398,7 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   const int wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int n = MODE >= 2 ? a.n_M : a.n_N;
-  const int row = blockIdx.x * kApplyRows + wave * 32 + l32;
+  const int row = blk * kApplyRows + wave * 32 + l32;
   const bool row_ok = row < n;
   const bool vec = (a.k & 7) == 0;
 
@@ -507,6 +592,28 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   }
 }
 
+// Forward rows (mode 0).
+template <int D, int KP, int FEAT>
+__global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[ApplyCfg<D, KP, 0, FEAT>::LDS];
+  apply_body<D, KP, 0, FEAT>(a, blockIdx.x, lds);
+}
+
+// Backward rows in one launch (all three read only the reduced matrices and
+// inputs): workgroups [0, g1) the dQ rows (mode 1), [g1, g1 + g2) the dK rows
+// (mode 2), the rest the dV rows (mode 3).
+template <int D, int KP, int FEAT>
+__global__ __launch_bounds__(256) void lin_apply_bwd(LinArgs a, int g1, int g2) {
+  constexpr int L1 = ApplyCfg<D, KP, 1, FEAT>::LDS, L2 = ApplyCfg<D, KP, 2, FEAT>::LDS,
+                L3 = ApplyCfg<D, KP, 3, FEAT>::LDS;
+  constexpr int L12 = L1 > L2 ? L1 : L2;
+  __shared__ __attribute__((aligned(16))) char lds[L12 > L3 ? L12 : L3];
+  const int b = blockIdx.x;
+  if (b < g1) apply_body<D, KP, 1, FEAT>(a, b, lds);
+  else if (b < g1 + g2) apply_body<D, KP, 2, FEAT>(a, b - g1, lds);
+  else apply_body<D, KP, 3, FEAT>(a, b - g1 - g2, lds);
+}
+
 }  // namespace lin
 
 // ---------------------------------------------------------------------------
@@ -524,30 +631,41 @@ __global__ __launch_bounds__(256) void lin_apply(LinArgs a) {
   X(64, 64)                  \
   X(64, 32)
 
-hipError_t launch_lin_gram(int D, int KP, int mode, bool ident, const LinArgs& a, int grid, hipStream_t st) {
-#define SSC_L(DD, KK)                                                                                         \
-  if (D == DD && KP == KK) {                                                                                  \
-    if (ident) {                                                                                              \
-      if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0, 1>), dim3(grid), dim3(256), 0, st, a);      \
-      else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1, 1>), dim3(grid), dim3(256), 0, st, a);                \
-    } else {                                                                                                  \
-      if (mode == 0) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0, 0>), dim3(grid), dim3(256), 0, st, a);      \
-      else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1, 0>), dim3(grid), dim3(256), 0, st, a);                \
-    }                                                                                                         \
-    return hipGetLastError();                                                                                 \
+hipError_t launch_lin_gram(int D, int KP, bool ident, const LinArgs& a, int grid, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                              \
+  if (D == DD && KP == KK) {                                                                       \
+    if (ident) hipLaunchKernelGGL((lin::lin_gram<DD, KK, 1>), dim3(grid), dim3(lin::kGramWaves * 64), 0, st, a); \
+    else hipLaunchKernelGGL((lin::lin_gram<DD, KK, 0>), dim3(grid), dim3(lin::kGramWaves * 64), 0, st, a);       \
+    return hipGetLastError();                                                                      \
   }
   SSC_LIN_INSTANCES(SSC_L)
 #undef SSC_L
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_lin_gram_bwd(int D, int KP, bool ident, const LinArgs& a, int gM, int gN, hipStream_t st) {
+#define SSC_L(DD, KK)                                                                                      \
+  if (D == DD && KP == KK) {                                                                               \
+    if (ident) hipLaunchKernelGGL((lin::lin_gram_bwd<DD, KK, 1>), dim3(gM + gN), dim3(lin::kGramWaves * 64), 0, st, a, gM); \
+    else hipLaunchKernelGGL((lin::lin_gram_bwd<DD, KK, 0>), dim3(gM + gN), dim3(lin::kGramWaves * 64), 0, st, a, gM);       \
+    return hipGetLastError();                                                                              \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
+static lin::RedJob red_job(const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo) {
+  return lin::RedJob{part, nparts, reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT),
+                     reinterpret_cast<bf16*>(Mlo), reinterpret_cast<bf16*>(MTlo)};
+}
+
 hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void* M, void* MT, void* Mlo, void* MTlo,
                              hipStream_t st) {
+  const lin::RedJob j = red_job(part, nparts, M, MT, Mlo, MTlo);
 #define SSC_L(DD, KK)                                                                                    \
   if (D == DD && KP == KK) {                                                                             \
-    hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 31) / 32), dim3(256), 0, st, part, nparts,   \
-                       reinterpret_cast<bf16*>(M), reinterpret_cast<bf16*>(MT), reinterpret_cast<bf16*>(Mlo),  \
-                       reinterpret_cast<bf16*>(MTlo));                                                   \
+    hipLaunchKernelGGL((lin::lin_reduce<DD, KK>), dim3((DD * KK + 31) / 32), dim3(256), 0, st, j);       \
     return hipGetLastError();                                                                            \
   }
   SSC_LIN_INSTANCES(SSC_L)
@@ -555,27 +673,42 @@ hipError_t launch_lin_reduce(int D, int KP, const float* part, int nparts, void*
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_lin_rowprep(const LinArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(lin::lin_rowprep, dim3((a.n_N + 15) / 16), dim3(256), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_lin_reduce2(int D, int KP, const float* part0, int nparts0, void* M0, void* MT0, void* Mlo0,
+                              void* MTlo0, const float* part1, int nparts1, void* M1, void* MT1, void* Mlo1,
+                              void* MTlo1, hipStream_t st) {
+  const lin::RedJob j0 = red_job(part0, nparts0, M0, MT0, Mlo0, MTlo0);
+  const lin::RedJob j1 = red_job(part1, nparts1, M1, MT1, Mlo1, MTlo1);
+#define SSC_L(DD, KK)                                                                                     \
+  if (D == DD && KP == KK) {                                                                              \
+    hipLaunchKernelGGL((lin::lin_reduce2<DD, KK>), dim3(2 * ((DD * KK + 31) / 32)), dim3(256), 0, st, j0, j1); \
+    return hipGetLastError();                                                                             \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
 }
 
-template <int D, int KP, int FEAT>
-void launch_lin_apply_t(int mode, const LinArgs& a, int grid, hipStream_t st) {
-  if (mode == 0) hipLaunchKernelGGL((lin::lin_apply<D, KP, 0, FEAT>), dim3(grid), dim3(256), 0, st, a);
-  else if (mode == 1) hipLaunchKernelGGL((lin::lin_apply<D, KP, 1, FEAT>), dim3(grid), dim3(256), 0, st, a);
-  else if (mode == 2) hipLaunchKernelGGL((lin::lin_apply<D, KP, 2, FEAT>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((lin::lin_apply<D, KP, 3, FEAT>), dim3(grid), dim3(256), 0, st, a);
+hipError_t launch_lin_apply(int D, int KP, bool ident, const LinArgs& a, hipStream_t st) {
+  const int grid = (a.n_N + lin::kApplyRows - 1) / lin::kApplyRows;
+#define SSC_L(DD, KK)                                                                         \
+  if (D == DD && KP == KK) {                                                                  \
+    if (ident) hipLaunchKernelGGL((lin::lin_apply<DD, KK, 1>), dim3(grid), dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((lin::lin_apply<DD, KK, 0>), dim3(grid), dim3(256), 0, st, a);       \
+    return hipGetLastError();                                                                 \
+  }
+  SSC_LIN_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_lin_apply(int D, int KP, int mode, bool ident, const LinArgs& a, hipStream_t st) {
-  const int n = mode >= 2 ? a.n_M : a.n_N;
-  const int grid = (n + lin::kApplyRows - 1) / lin::kApplyRows;
-#define SSC_L(DD, KK)                                                                 \
-  if (D == DD && KP == KK) {                                                          \
-    if (ident) launch_lin_apply_t<DD, KK, 1>(mode, a, grid, st);                      \
-    else launch_lin_apply_t<DD, KK, 0>(mode, a, grid, st);                            \
-    return hipGetLastError();                                                         \
+hipError_t launch_lin_apply_bwd(int D, int KP, bool ident, const LinArgs& a, hipStream_t st) {
+  const int g1 = (a.n_N + lin::kApplyRows - 1) / lin::kApplyRows;
+  const int g2 = (a.n_M + lin::kApplyRows - 1) / lin::kApplyRows;
+#define SSC_L(DD, KK)                                                                                             \
+  if (D == DD && KP == KK) {                                                                                      \
+    if (ident) hipLaunchKernelGGL((lin::lin_apply_bwd<DD, KK, 1>), dim3(g1 + 2 * g2), dim3(256), 0, st, a, g1, g2); \
+    else hipLaunchKernelGGL((lin::lin_apply_bwd<DD, KK, 0>), dim3(g1 + 2 * g2), dim3(256), 0, st, a, g1, g2);       \
+    return hipGetLastError();                                                                                     \
   }
   SSC_LIN_INSTANCES(SSC_L)
 #undef SSC_L
