@@ -293,6 +293,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-160k", action="store_true", help="skip the informational 160k geo record")
     ap.add_argument("--dense-only", action="store_true", help="time only the dense coupling (profiling)")
+    ap.add_argument("--no-fps", action="store_true", help="skip the GPU FPS records (counter passes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain streaming kernel of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -470,7 +471,7 @@ def main():
                                    "output, and its backward dO = Phi (Phi^T Phi)^-1 dC; k=200"}
         del O_fm
 
-    if not args.dense_only:
+    if not args.dense_only and not args.no_fps:
         rec["fps_60k"] = fps_record(c, c["P"], min(args.steps, 5), 1, torch, np, gen, ssc)
 
     if not args.no_160k and not args.dense_only:
@@ -507,7 +508,8 @@ def main():
                                                "what": "diagnostic, not the graded figure (padded blocks)"},
                            "peak_gib": round(pk4, 3), "P": c4["P"], "s": c4["s"]}
         del geo4
-        rec["fps_160k"] = fps_record(c4, c4["P"], min(args.steps, 3), 1, torch, np, gen, ssc)
+        if not args.no_fps:
+            rec["fps_160k"] = fps_record(c4, c4["P"], min(args.steps, 3), 1, torch, np, gen, ssc)
 
     if not args.dense_only:
         log("timing the small parity workloads")
