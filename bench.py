@@ -279,10 +279,20 @@ def small_config_record(i, steps, warmup, torch, np, gen, ssc):
     ph, tot, _ = time_steps([fwd, bwd], steps, warmup, torch)
     stats = step_stats(time_steps.per_step)
     f = algorithmic_flops(float(n) * n, d, k)
-    return {"workload": c["config"], "n": n, "d": d, "k": k, "dtype": dt, "ms": round(tot, 4),
-            "ms_median": stats["median"], "fwd_ms": round(ph[0], 4), "bwd_ms": round(ph[1], 4),
-            "tflops": round(f / tot / 1e9, 2), "algorithmic_flop": f,
-            "what": "dense coupling fwd+bwd; launch-latency bound at these sizes"}
+    rec = {"workload": c["config"], "n": n, "d": d, "k": k, "dtype": dt, "ms": round(tot, 4),
+           "ms_median": stats["median"], "fwd_ms": round(ph[0], 4), "bwd_ms": round(ph[1], 4),
+           "tflops": round(f / tot / 1e9, 2), "algorithmic_flop": f}
+    if dt == "bf16":
+        # the default route at this size is the one-patch geo coupling (split
+        # items); the dense kernels alone launch n / 128 workgroups
+        with ssc.dense_route("dense"):
+            phd, totd, _ = time_steps([fwd, bwd], steps, warmup, torch)
+        rec["route"] = "one-patch geo (split items)"
+        rec["dense_kernels"] = {"ms": round(totd, 4), "fwd_ms": round(phd[0], 4), "bwd_ms": round(phd[1], 4)}
+        rec["what"] = "dense coupling fwd+bwd on the one-patch geo route; occupancy / launch bound at this size"
+    else:
+        rec["what"] = "dense coupling fwd+bwd; launch-latency bound at these sizes"
+    return rec
 
 
 def main():

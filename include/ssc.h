@@ -362,6 +362,20 @@ int ssc_last_hip_error(void);
 int ssc_timer_arm(const char* family, int capacity);
 int ssc_timer_read(float* total_ms, int* count);
 
+/*
+ * Route of the bf16 dense couplings on the calling thread (a tuning and test
+ * aid, like the timer).  With few row blocks (at most 128 blocks of 128 rows
+ * on each side the call reads: n_N for the forward, n_N and n_M for the
+ * backward) the dense calls run as a geo coupling with one patch per side
+ * selecting the other, which is the same exact softmax over every key; the
+ * geo planner then splits each row block's key stream into parts (merged
+ * after the block kernel), so a small call fills the chip.  mode = -1: by
+ * size (the default), 0: always the dense kernels, 1: always the one-patch
+ * geo route.  Other values leave the mode unchanged.  Returns the previous
+ * mode.  ssc_workspace_bytes() for the dense ops covers both routes.
+ */
+int ssc_dense_split(int mode);
+
 /* Internal tile constants, exposed for tests and FLOP accounting:
  * which = 0: padded k for a given k (returns 0 if unsupported),
  * which = 1: row-group granularity of the padded patch layout. */

@@ -27,7 +27,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "CouplingError", "KernelTimer", "lib", "library_path", "workspace_bytes", "kpad",
+    "CouplingError", "KernelTimer", "dense_route", "lib", "library_path", "workspace_bytes", "kpad",
     "coupling_dense_fwd", "coupling_dense_bwd", "patch_score_topk",
     "coupling_geo_fwd", "coupling_geo_bwd", "dense_coupling", "geo_coupling",
     "coupling_linear_fwd", "coupling_linear_bwd", "linear_coupling",
@@ -69,6 +69,7 @@ _SIGS = {
     "ssc_last_hip_error": (_i, []),
     "ssc_debug_build": (_i, []),
     "ssc_query": (_i, [_i, _i]),
+    "ssc_dense_split": (_i, [_i]),
     "ssc_timer_arm": (_i, [ctypes.c_char_p, _i]),
     "ssc_timer_read": (_i, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
     "coupling_dense_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -112,6 +113,28 @@ def lib() -> ctypes.CDLL:
 def kpad(k: int) -> int:
     """Internal padded width of the basis (0 if k is unsupported)."""
     return int(lib().ssc_query(0, int(k)))
+
+
+class dense_route:
+    """Route of the bf16 dense couplings on this thread inside a `with`
+    block: "auto" (by size, the default), "dense" (always the dense kernels)
+    or "split" (always the one-patch geo route, whose planner splits short
+    item lists along their key stream)."""
+
+    _MODES = {"auto": -1, "dense": 0, "split": 1}
+
+    def __init__(self, mode: str):
+        if mode not in self._MODES:
+            raise ValueError(f"dense route must be one of {sorted(self._MODES)}")
+        self.mode = self._MODES[mode]
+
+    def __enter__(self):
+        self.prev = int(lib().ssc_dense_split(self.mode))
+        return self
+
+    def __exit__(self, *exc):
+        lib().ssc_dense_split(self.prev)
+        return False
 
 
 class KernelTimer:

@@ -471,12 +471,38 @@ FmLayout make_fm_layout(bool bwd, int n, int k) {
   return L;
 }
 
-ssc_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
-  if (L.total == 0) return SSC_OK;
-  if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
+// Dense bf16 couplings with few row blocks run as a geo coupling with one
+// patch per side selecting the other (the same exact softmax over every
+// key): the geo planner splits the items of a short item list along their
+// key stream and merges the parts, so the call fills the chip where the
+// dense kernels would launch a few dozen workgroups.  The one-patch offsets
+// and selection sit in the first kOnePatchBytes of the workspace, the geo
+// call's workspace after them.
+constexpr size_t kOnePatchBytes = 256;
+thread_local int g_dense_split = -1;  // -1: by size, 0: never, 1: always (bf16)
+
+bool dense_split_route(ssc_dtype t, int n_N, int n_M, bool bwd) {
+  if (t != SSC_BF16 || n_N <= 0 || g_dense_split == 0) return false;
+  if (g_dense_split == 1) return true;
+  // at most half a round of items, so that every item is split in two or more
+  const int half = kRoundCUs / 2;
+  const int iN = (n_N + kRowsFwd - 1) / kRowsFwd, iM = (n_M + kRowsDkv - 1) / kRowsDkv;
+  return bwd ? iN <= half && iM <= half : iN <= half;
+}
+
+size_t one_patch_ws(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k) {
+  const ssc_op g = op == SSC_OP_DENSE_FWD ? SSC_OP_GEO_FWD : SSC_OP_GEO_BWD;
+  return kOnePatchBytes + make_layout(g, t, n_N, n_M, d, k, 1, 1, 1).total;
+}
+
+ssc_status check_ws_bytes(size_t need, void* ws, size_t ws_bytes) {
+  if (need == 0) return SSC_OK;
+  if (ws == nullptr || ws_bytes < need) return SSC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
   return SSC_OK;
 }
+
+ssc_status check_ws(const Layout& L, void* ws, size_t ws_bytes) { return check_ws_bytes(L.total, ws, ws_bytes); }
 
 }  // namespace
 
@@ -486,9 +512,14 @@ size_t ssc_workspace_bytes(ssc_op op, ssc_dtype dtype, int n_N, int n_M, int d, 
                            int s) {
   switch (op) {
     case SSC_OP_DENSE_FWD:
-    case SSC_OP_DENSE_BWD:
+    case SSC_OP_DENSE_BWD: {
       if (check_shape(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
-      break;
+      // enough for either route (the one-patch geo route is bf16 only)
+      const size_t dn = make_layout(op, dtype, n_N, n_M, d, k, 0, 0, 0).total;
+      if (dtype != SSC_BF16) return dn;
+      const size_t gp = one_patch_ws(op, dtype, n_N, n_M, d, k);
+      return dn > gp ? dn : gp;
+    }
     case SSC_OP_GEO_FWD:
     case SSC_OP_GEO_BWD:
       if (check_shape(dtype, n_N, n_M, d, k) != SSC_OK) return 0;
@@ -577,6 +608,12 @@ int ssc_timer_read(float* total_ms, int* count) {
   return SSC_OK;
 }
 
+int ssc_dense_split(int mode) {
+  const int prev = g_dense_split;
+  if (mode >= -1 && mode <= 1) g_dense_split = mode;
+  return prev;
+}
+
 int ssc_query(int which, int arg) {
   if (which == 0) return kpad_for(arg);
   if (which == 1) return kGroup;
@@ -591,11 +628,21 @@ ssc_status coupling_dense_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   if (n_N == 0) return SSC_OK;
   if (!all_ok({Q, K, V, O, lse})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const bool split = dense_split_route(dtype, n_N, n_M, false);
   const Layout L = make_layout(SSC_OP_DENSE_FWD, dtype, n_N, n_M, d, k, 0, 0, 0);
-  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  if ((st = split ? check_ws_bytes(one_patch_ws(SSC_OP_DENSE_FWD, dtype, n_N, n_M, d, k), ws, ws_bytes)
+                  : check_ws(L, ws, ws_bytes)) != SSC_OK)
+    return st;
   const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
   const Buf bO{O, (size_t)n_N * k * 4}, bl{lse, (size_t)n_N * 4}, bw{ws, ws_bytes};
   if (!disjoint({bO, bl, bw}, {bQ, bK, bV})) return SSC_ERR_INVALID_ARG;
+  if (split) {
+    // every argument checked: the one-patch offsets, then the geo call
+    int* p = static_cast<int*>(ws);
+    SSC_TRY(launch_one_patch(p, n_N, n_M, reinterpret_cast<hipStream_t>(stream)));
+    return coupling_geo_fwd(dtype, d, k, n_N, 1, p, n_M, 1, p + 4, 1, p + 8, Q, K, V, scale, O, lse,
+                            static_cast<char*>(ws) + kOnePatchBytes, ws_bytes - kOnePatchBytes, stream);
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);
@@ -660,13 +707,22 @@ ssc_status coupling_dense_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, c
   if (!all_ok({K, V, dK}) || !aligned16(dV)) return SSC_ERR_INVALID_ARG;
   if (n_N > 0 && !all_ok({Q, O, dO, lse, dQ})) return SSC_ERR_INVALID_ARG;
   const size_t es = dtype == SSC_BF16 ? 2 : 4;
+  const bool split = dense_split_route(dtype, n_N, n_M, true);
   const Layout L = make_layout(SSC_OP_DENSE_BWD, dtype, n_N, n_M, d, k, 0, 0, 0);
-  if ((st = check_ws(L, ws, ws_bytes)) != SSC_OK) return st;
+  if ((st = split ? check_ws_bytes(one_patch_ws(SSC_OP_DENSE_BWD, dtype, n_N, n_M, d, k), ws, ws_bytes)
+                  : check_ws(L, ws, ws_bytes)) != SSC_OK)
+    return st;
   const Buf bQ{Q, (size_t)n_N * d * es}, bK{K, (size_t)n_M * d * es}, bV{V, (size_t)n_M * k * es};
   const Buf bO{O, (size_t)n_N * k * 4}, bdO{dO, (size_t)n_N * k * es}, bl{lse, (size_t)n_N * 4};
   const Buf bdQ{dQ, (size_t)n_N * d * 4}, bdK{dK, (size_t)n_M * d * 4}, bdV{dV, (size_t)n_M * k * 4};
   const Buf bw{ws, ws_bytes};
   if (!disjoint({bdQ, bdK, bdV, bw}, {bQ, bK, bV, bO, bdO, bl})) return SSC_ERR_INVALID_ARG;
+  if (split) {
+    int* p = static_cast<int*>(ws);
+    SSC_TRY(launch_one_patch(p, n_N, n_M, reinterpret_cast<hipStream_t>(stream)));
+    return coupling_geo_bwd(dtype, d, k, n_N, 1, p, n_M, 1, p + 4, 1, p + 8, Q, K, V, scale, O, dO, lse, dQ, dK,
+                            dV, static_cast<char*>(ws) + kOnePatchBytes, ws_bytes - kOnePatchBytes, stream);
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int KP = kpad_for(k);

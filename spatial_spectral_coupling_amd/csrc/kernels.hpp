@@ -376,6 +376,9 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 // 16-row groups) in one launch
 hipError_t launch_plan_pad(const PlanArgs& a, const PackArgs* jobs, const int* grids, int njobs, hipStream_t st);
 hipError_t launch_pool(DType t, const PoolArgs& a, hipStream_t st);
+// p[0..11]: offsets of one patch per side ({0, n_N} at p, {0, n_M} at p + 4)
+// and its selection ({0} at p + 8), the rest zero
+hipError_t launch_one_patch(int* p, int n_N, int n_M, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // ident: the rows of Q / K are precomputed features (identity feature map)
 // Forward Gram sums phi(K)^T V_ext over `grid` row blocks into a.part.

@@ -401,10 +401,21 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
     R = 0;
     m = 1;
   }
+  // the patch of item i (tmp[p] <= i < tmp[p + 1]): items are spread over the
+  // threads one by one, so a patch with many items is not left to one thread
+  auto patch_of = [&](int i) {
+    int lo = 0, hi = nP - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tmp[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
   if (R == 0) {
-    for (int p = tid; p < nP; p += kPlanThreads) {
-      const int b = tmp[p], nt = cn[p];
-      for (int t = 0; t < nt; ++t) items[b + t] = Item{p, t * rows, 0, 0x7fffffff, -1};
+    for (int i = tid; i < N; i += kPlanThreads) {
+      const int p = patch_of(i);
+      items[i] = Item{p, (i - tmp[p]) * rows, 0, 0x7fffffff, -1};
     }
     if (tid == 0 && n_split != nullptr) *n_split = 0;
     __syncthreads();
@@ -465,16 +476,18 @@ __device__ int make_items(int nP, const int* off, int rows, TilesF tiles, Item* 
   }
   __syncthreads();
   const int U = N - R;
-  for (int p = tid; p < nP; p += kPlanThreads) {
-    const int nt = cn[p], ns = nsplit(p), c = cost(p);
-    for (int t = ns; t < nt; ++t) items[atomicAdd(&hist[c], 1)] = Item{p, t * rows, 0, 0x7fffffff, -1};
-    const int T = tl[p];
-    for (int t = 0; t < ns; ++t) {
-      const int j = spb[p] + t;
-      spl[j] = SplitItem{p, t * rows, m, j * m};
-      for (int q = 0; q < m; ++q)
-        items[U + j * m + q] = Item{p, t * rows, (int)((long long)q * T / m), (int)((long long)(q + 1) * T / m), j * m + q};
+  // item t of patch p: split (its parts after the U whole items) if t <
+  // nsplit(p), else whole (placed in its cost bucket)
+  for (int i = tid; i < N; i += kPlanThreads) {
+    const int p = patch_of(i), t = i - tmp[p], ns = nsplit(p);
+    if (t >= ns) {
+      items[atomicAdd(&hist[cost(p)], 1)] = Item{p, t * rows, 0, 0x7fffffff, -1};
+      continue;
     }
+    const int T = tl[p], j = spb[p] + t;
+    spl[j] = SplitItem{p, t * rows, m, j * m};
+    for (int q = 0; q < m; ++q)
+      items[U + j * m + q] = Item{p, t * rows, (int)((long long)q * T / m), (int)((long long)(q + 1) * T / m), j * m + q};
   }
   if (tid == 0) *n_split = R;
   __syncthreads();
@@ -829,6 +842,19 @@ __global__ __launch_bounds__(256) void check_offsets_kernel(const int* offN, int
 }
 
 __global__ void clear_flag_kernel(int* flag) { *flag = 0; }
+
+// One patch per side selecting the other, each array 16-byte aligned:
+// offN = p[0..1] = {0, n_N}, offM = p[4..5] = {0, n_M}, idx = p[8] = {0}
+// (a dense coupling run through the geo kernels).
+__global__ void one_patch_kernel(int* p, int n_N, int n_M) {
+  const int t = threadIdx.x;
+  if (t < 12) p[t] = t == 1 ? n_N : t == 5 ? n_M : 0;
+}
+
+hipError_t launch_one_patch(int* p, int n_N, int n_M, hipStream_t st) {
+  hipLaunchKernelGGL(one_patch_kernel, dim3(1), dim3(64), 0, st, p, n_N, n_M);
+  return hipGetLastError();
+}
 
 hipError_t launch_check_offsets(const int* offN, int P_N, int n_N, const int* offM, int P_M, int n_M, int* flag,
                                 hipStream_t st) {

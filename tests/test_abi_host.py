@@ -100,6 +100,23 @@ def test_dense_fwd_validation(L):
     assert dense_fwd(L, lse=A[3], ws=A[5]) == INVALID       # two outputs overlap
 
 
+def test_dense_route_mode_and_workspace(L):
+    """The thread's dense route (by size / dense kernels / one-patch geo):
+    the setter returns the previous mode and ignores other values; the dense
+    workspace covers the one-patch route (its offsets plus a one-patch geo
+    workspace); a routed call checks every argument before any launch."""
+    assert L.ssc_dense_split(0) == -1
+    assert L.ssc_dense_split(7) == 0
+    assert L.ssc_dense_split(1) == 0
+    assert L.ssc_dense_split(-1) == 1
+    w = L.ssc_workspace_bytes
+    for op, gop in ((ssc.OP_DENSE_FWD, ssc.OP_GEO_FWD), (ssc.OP_DENSE_BWD, ssc.OP_GEO_BWD)):
+        for n in (5000, 60000):
+            assert w(op, BF16, n, n, 128, 200, 0, 0, 0) >= 256 + w(gop, BF16, n, n, 128, 200, 1, 1, 1)
+    assert dense_fwd(L, ws=A[5], wsb=300) == WORKSPACE
+    assert dense_fwd(L, K=A[3], ws=A[5]) == INVALID             # output O aliases K: nothing launched
+
+
 def test_dense_bwd_validation(L):
     f = L.coupling_dense_bwd
     args = lambda **kw: [kw.get("dt", BF16), kw.get("nN", 64), kw.get("nM", 64), kw.get("d", 128), kw.get("k", 200),

@@ -60,21 +60,28 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dt,nN,nM,d,k", SHAPES)
-def test_dense_parity_small(dt, nN, nM, d, k):
-    say("dense small", dt, nN, nM, d, k)
+# bf16 calls this small run as a one-patch geo coupling by default ("split");
+# "dense" forces the dense kernels, so both routes are checked
+ROUTED = [(r,) + sh for sh in SHAPES for r in (("dense", "split") if sh[0] == "bf16" else ("dense",))]
+
+
+@pytest.mark.parametrize("route,dt,nN,nM,d,k", ROUTED)
+def test_dense_parity_small(route, dt, nN, nM, d, k):
+    say("dense small", route, dt, nN, nM, d, k)
     c = gen.make_small(nN, nM, d, k, dt, seed=nN + nM)
-    O, lse, dQ, dK, dV = run_dense(c)
+    with ssc.dense_route(route):
+        O, lse, dQ, dK, dV = run_dense(c)
     Or, lser, gr = oracle_dense(c)
     check_fwd(O, Or, lse, lser, what=f"{dt} {nN}x{nM} d{d} k{k}")
     check_grads((dQ, dK, dV), gr, what=f"{dt} {nN}x{nM} d{d} k{k}")
 
 
-@pytest.mark.parametrize("i", [0, 1])
-def test_dense_workload_parity(i):
-    say("dense workload", i)
+@pytest.mark.parametrize("i,route", [(0, "auto"), (1, "auto"), (1, "dense")])
+def test_dense_workload_parity(i, route):
+    say("dense workload", i, route)
     c = gen.cached_config(i)
-    O, lse, dQ, dK, dV = run_dense(c)
+    with ssc.dense_route(route):
+        O, lse, dQ, dK, dV = run_dense(c)
     Or, lser, gr = oracle_dense(c)
     check_fwd(O, Or, lse, lser, what=c["config"])
     check_grads((dQ, dK, dV), gr, what=c["config"])
@@ -97,16 +104,18 @@ def test_dense_one_hot_permutation_returns_permuted_basis():
     assert err < 1e-3
 
 
-def test_dense_rows_of_map_sum_to_one_and_determinism():
-    say("dense ones column + determinism")
+@pytest.mark.parametrize("route", ["dense", "split"])
+def test_dense_rows_of_map_sum_to_one_and_determinism(route):
+    say("dense ones column + determinism", route)
     c = gen.make_small(700, 900, 128, 200, "bf16", seed=5)
     V = c["V"].copy()
     V[:, 7] = gen.bf16_bits_from_f32(np.ones(900, np.float32))
     Q, K, Vd, dO = to_dev(c["Q"], "bf16"), to_dev(c["K"], "bf16"), to_dev(V, "bf16"), to_dev(c["dO"], "bf16")
-    O1, l1 = ssc.coupling_dense_fwd(Q, K, Vd)
-    O2, l2 = ssc.coupling_dense_fwd(Q, K, Vd)
-    g1 = ssc.coupling_dense_bwd(Q, K, Vd, O1, dO, l1)
-    g2 = ssc.coupling_dense_bwd(Q, K, Vd, O1, dO, l1)
+    with ssc.dense_route(route):
+        O1, l1 = ssc.coupling_dense_fwd(Q, K, Vd)
+        O2, l2 = ssc.coupling_dense_fwd(Q, K, Vd)
+        g1 = ssc.coupling_dense_bwd(Q, K, Vd, O1, dO, l1)
+        g2 = ssc.coupling_dense_bwd(Q, K, Vd, O1, dO, l1)
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
@@ -115,7 +124,8 @@ def test_dense_rows_of_map_sum_to_one_and_determinism():
     assert np.max(np.abs(col - 1)) < 1e-2
 
 
-def test_dense_reference_fallbacks():
+@pytest.mark.parametrize("route", ["dense", "split"])
+def test_dense_reference_fallbacks(route):
     """The forward's first pass takes each row's reference from the bound
     |q| max|k| on its scores.  Row 5 (query 60 e1) meets a key of norm 60
     orthogonal to it, so the bound sits 459 (log2 units) above its scores and
@@ -123,8 +133,9 @@ def test_dense_reference_fallbacks():
     reference, and since a later tile's maximum (key 200 = 5 e1, 38 above the
     first tile's) runs more than 32 ahead of it, once more with exact row
     maxima.  Row 129 (query 60 e3, second workgroup) only needs the running
-    reference.  Both workgroups must still match the oracle."""
-    say("dense reference fallbacks")
+    reference.  Both workgroups must still match the oracle (on the dense
+    kernels, and on the one-patch geo route with its split items)."""
+    say("dense reference fallbacks", route)
     nN, nM, d, k = 130, 300, 128, 200
     c = gen.make_small(nN, nM, d, k, "bf16", seed=21)
     Qf = f64(c["Q"], "bf16").astype(np.float32)
@@ -141,9 +152,10 @@ def test_dense_reference_fallbacks():
     c["Q"], c["K"] = gen.bf16_bits_from_f32(Qf), gen.bf16_bits_from_f32(Kf)
     scale = 1 / math.sqrt(d)
     Q, K, V = (to_dev(c[x], "bf16") for x in ("Q", "K", "V"))
-    O, lse = ssc.coupling_dense_fwd(Q, K, V, scale)
+    with ssc.dense_route(route):
+        O, lse = ssc.coupling_dense_fwd(Q, K, V, scale)
     Or, lser = dense_fwd(f64(c["Q"], "bf16"), f64(c["K"], "bf16"), f64(c["V"], "bf16"), scale)
-    check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what="reference fallbacks")
+    check_fwd(O.cpu().numpy(), Or, lse.cpu().numpy(), lser, what=f"reference fallbacks {route}")
     err5 = np.max(np.abs(O[5].cpu().numpy() - Or[5]))
     say("row 5 max-abs", err5)
     assert err5 <= 2e-2
@@ -224,17 +236,20 @@ def test_dense_60k_full_size():
     check_grads((dQ, dK, dV), gr, what="60k full")
 
 
-@pytest.mark.parametrize("dt,nN,nM,d,k", [("bf16", 300, 517, 128, 200), ("bf16", 200, 333, 128, 256),
-                                          ("bf16", 77, 33, 64, 30), ("f32", 150, 260, 128, 128)])
-def test_dense_backward_without_dv(dt, nN, nM, d, k):
+@pytest.mark.parametrize("route,dt,nN,nM,d,k", [(r, "bf16", 300, 517, 128, 200) for r in ("dense", "split")] +
+                         [(r, "bf16", 200, 333, 128, 256) for r in ("dense", "split")] +
+                         [(r, "bf16", 77, 33, 64, 30) for r in ("dense", "split")] +
+                         [("dense", "f32", 150, 260, 128, 128)])
+def test_dense_backward_without_dv(route, dt, nN, nM, d, k):
     """dV = NULL: the dV products are skipped; dQ and dK are the bits of the
     full call and match the oracle."""
-    say("dense bwd without dV", dt, nN, nM, d, k)
+    say("dense bwd without dV", route, dt, nN, nM, d, k)
     c = gen.make_small(nN, nM, d, k, dt, seed=nN + 2 * nM)
     Q, K, V, dO = (to_dev(c[x], dt) for x in ("Q", "K", "V", "dO"))
-    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
-    dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
-    dQ2, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
+    with ssc.dense_route(route):
+        O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+        dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
+        dQ2, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
     torch.cuda.synchronize()
     assert dV2 is None
     assert torch.equal(dQ2, dQ) and torch.equal(dK2, dK)
@@ -330,3 +345,26 @@ def test_dense_without_target_rows(dt):
     torch.cuda.synchronize()
     assert dQ.shape == (0, 64)
     assert torch.count_nonzero(dK).item() == 0 and torch.count_nonzero(dV).item() == 0
+
+
+def test_dense_route_by_size():
+    """By default a bf16 call with at most 128 row blocks a side takes the
+    one-patch geo route (its kernels are timed as the geo families); the 60k
+    workload and a "dense" route take the dense kernels."""
+    say("dense route by size")
+    c = gen.make_small(5000, 5000, 128, 200, "bf16", seed=31)
+    Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
+
+    def launches(family, route, Q, K, V, dO):
+        with ssc.dense_route(route), ssc.KernelTimer(family, 8) as t:
+            O, lse = ssc.coupling_dense_fwd(Q, K, V)
+            ssc.coupling_dense_bwd(Q, K, V, O, dO, lse)
+            return t.read()[1]
+
+    assert launches("geo_fwd", "auto", Q, K, V, dO) == 1 and launches("geo_dkv", "auto", Q, K, V, dO) == 1
+    assert launches("fwd", "auto", Q, K, V, dO) == 0
+    assert launches("geo_fwd", "dense", Q, K, V, dO) == 0 and launches("dkv", "dense", Q, K, V, dO) == 1
+    n = 16512  # 129 row blocks of 128: past the split route
+    c = gen.make_small(n, 300, 64, 30, "bf16", seed=32)
+    Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
+    assert launches("geo_fwd", "auto", Q, K, V, dO) == 0 and launches("fwd", "auto", Q, K, V, dO) == 1
