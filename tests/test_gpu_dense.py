@@ -368,3 +368,17 @@ def test_dense_route_by_size():
     c = gen.make_small(n, 300, 64, 30, "bf16", seed=32)
     Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
     assert launches("geo_fwd", "auto", Q, K, V, dO) == 0 and launches("fwd", "auto", Q, K, V, dO) == 1
+
+
+@pytest.mark.timeout(600)
+def test_dense_12k_split_route_full():
+    """12000 x 12000 (the pages' smaller workloads are about this size): the
+    default route splits each of the 94 row blocks' key streams in two;
+    every element of O, lse, dQ, dK, dV against the oracle."""
+    say("dense 12k split route")
+    c = gen.make_small(12000, 12000, 128, 200, "bf16", seed=41)
+    O, lse, dQ, dK, dV = run_dense(c)
+    say("dense 12k oracle")
+    Or, lser, gr = oracle_dense(c)
+    check_fwd(O, Or, lse, lser, what="12k split route")
+    check_grads((dQ, dK, dV), gr, what="12k split route")
