@@ -353,7 +353,9 @@ int ssc_last_hip_error(void);
  * calling thread bracket each subsequent launch of one kernel family with a
  * pair of HIP events recorded on that launch's stream; `capacity` event pairs
  * are created up front (family NULL or capacity <= 0 disarms and frees them).
- * Families: "fwd", "dq", "dkv" (dense) and "geo_fwd", "geo_dq", "geo_dkv".
+ * Families: "fwd", "dq", "dkv" (dense) and "geo_fwd", "geo_dq", "geo_dkv"
+ * (dense calls on the one-patch route, see ssc_dense_split, are timed as
+ * the geo families).
  * ssc_timer_read() waits for the recorded events and returns the summed
  * milliseconds and the number of timed launches (negated if more launches
  * happened than pairs were available), then starts a new count.
