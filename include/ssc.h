@@ -366,12 +366,13 @@ int ssc_timer_read(float* total_ms, int* count);
 
 /*
  * Route of the bf16 dense couplings on the calling thread (a tuning and test
- * aid, like the timer).  With few row blocks (at most 128 blocks of 128 rows
- * on each side the call reads: n_N for the forward, n_N and n_M for the
- * backward) the dense calls run as a geo coupling with one patch per side
- * selecting the other, which is the same exact softmax over every key; the
- * geo planner then splits each row block's key stream into parts (merged
- * after the block kernel), so a small call fills the chip.  mode = -1: by
+ * aid, like the timer).  With few row blocks (at most 128 blocks of 128 rows:
+ * n_N for the forward; n_N or n_M for the backward, whose dQ pass has n_N /
+ * 128 and dK/dV pass n_M / 128 blocks) the dense calls run as a geo coupling
+ * with one patch per side selecting the other, which is the same exact
+ * softmax over every key; the geo planner then splits each short side's row
+ * blocks along their streams into parts (merged after the block kernel), so
+ * a small or lopsided call fills the chip.  mode = -1: by
  * size (the default), 0: always the dense kernels, 1: always the one-patch
  * geo route.  Other values leave the mode unchanged.  Returns the previous
  * mode.  ssc_workspace_bytes() for the dense ops covers both routes.

@@ -471,7 +471,7 @@ FmLayout make_fm_layout(bool bwd, int n, int k) {
   return L;
 }
 
-// Dense bf16 couplings with few row blocks run as a geo coupling with one
+// Dense bf16 couplings with few row blocks (on a side) run as a geo coupling with one
 // patch per side selecting the other (the same exact softmax over every
 // key): the geo planner splits the items of a short item list along their
 // key stream and merges the parts, so the call fills the chip where the
@@ -484,10 +484,13 @@ thread_local int g_dense_split = -1;  // -1: by size, 0: never, 1: always (bf16)
 bool dense_split_route(ssc_dtype t, int n_N, int n_M, bool bwd) {
   if (t != SSC_BF16 || n_N <= 0 || g_dense_split == 0) return false;
   if (g_dense_split == 1) return true;
-  // at most half a round of items, so that every item is split in two or more
+  // at most half a round of items on a side, so that each of its items is
+  // split in two or more: the forward's rows; either side of the backward
+  // (its dQ pass has n_N / 128 items, its dK/dV pass n_M / 128, and the
+  // planner splits each side on its own, so a long side stays whole items)
   const int half = kRoundCUs / 2;
   const int iN = (n_N + kRowsFwd - 1) / kRowsFwd, iM = (n_M + kRowsDkv - 1) / kRowsDkv;
-  return bwd ? iN <= half && iM <= half : iN <= half;
+  return bwd ? iN <= half || iM <= half : iN <= half;
 }
 
 size_t one_patch_ws(ssc_op op, ssc_dtype t, int n_N, int n_M, int d, int k) {

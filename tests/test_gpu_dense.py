@@ -269,17 +269,21 @@ def test_autograd_skips_dv_for_a_fixed_basis():
     assert torch.equal(Qr.grad, dQ.to(torch.bfloat16)) and torch.equal(Kr.grad, dK.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("nN,nM,d,k", [(300, 40000, 128, 200), (70, 33000, 64, 30), (1, 32897, 128, 200)])
-def test_dense_backward_many_key_blocks(nN, nM, d, k):
+@pytest.mark.parametrize("route,nN,nM,d,k", [(r,) + sh for sh in ((300, 40000, 128, 200), (70, 33000, 64, 30),
+                                                                  (1, 32897, 128, 200))
+                                             for r in ("dense", "auto")])
+def test_dense_backward_many_key_blocks(route, nN, nM, d, k):
     """More key blocks of 128 rows than one round of 256 workgroups (the
     dK / dV pass runs in two rounds) with few query rows: one to five query
-    tiles, ragged in both directions."""
-    say("dense bwd many key blocks", nN, nM, d, k)
+    tiles, ragged in both directions (on the dense kernels, and by default on
+    the one-patch route: split dQ items, whole dK/dV items)."""
+    say("dense bwd many key blocks", route, nN, nM, d, k)
     c = gen.make_small(nN, nM, d, k, "bf16", seed=nN + nM)
     Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
-    O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
-    dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
-    _, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
+    with ssc.dense_route(route):
+        O, lse = ssc.coupling_dense_fwd(Q, K, V, c["scale"])
+        dQ, dK, dV = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"])
+        _, dK2, dV2 = ssc.coupling_dense_bwd(Q, K, V, O, dO, lse, c["scale"], need_dV=False)
     torch.cuda.synchronize()
     assert dV2 is None and torch.equal(dK2, dK)
     O_r, lse_r, gr = oracle_dense(c)
@@ -368,6 +372,22 @@ def test_dense_route_by_size():
     c = gen.make_small(n, 300, 64, 30, "bf16", seed=32)
     Q, K, V, dO = (to_dev(c[x], "bf16") for x in ("Q", "K", "V", "dO"))
     assert launches("geo_fwd", "auto", Q, K, V, dO) == 0 and launches("fwd", "auto", Q, K, V, dO) == 1
+    # 129 query blocks but 3 key blocks: the backward's short side routes it
+    assert launches("geo_dkv", "auto", Q, K, V, dO) == 1 and launches("dkv", "auto", Q, K, V, dO) == 0
+
+
+@pytest.mark.parametrize("route", ["dense", "auto"])
+def test_dense_lopsided_backward(route):
+    """20000 target rows (157 blocks: whole dQ items) against 3000 source rows
+    (24 blocks: split dK/dV items on the default route), every element
+    against the oracle."""
+    say("dense lopsided", route)
+    c = gen.make_small(20000, 3000, 128, 200, "bf16", seed=43)
+    with ssc.dense_route(route):
+        O, lse, dQ, dK, dV = run_dense(c)
+    Or, lser, gr = oracle_dense(c)
+    check_fwd(O, Or, lse, lser, what=f"lopsided {route}")
+    check_grads((dQ, dK, dV), gr, what=f"lopsided {route}")
 
 
 @pytest.mark.timeout(600)
