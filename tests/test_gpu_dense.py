@@ -402,3 +402,16 @@ def test_dense_12k_split_route_full():
     Or, lser, gr = oracle_dense(c)
     check_fwd(O, Or, lse, lser, what="12k split route")
     check_grads((dQ, dK, dV), gr, what="12k split route")
+
+
+def test_dense_split_route_past_half_a_round():
+    """20000 x 2000 forced onto the one-patch route: 157 query blocks leave
+    more than half a round over, so they stay whole items (splitting the
+    cheapest in two was measured slower); 16 key blocks split in eight."""
+    say("dense split route, 157 query blocks")
+    c = gen.make_small(20000, 2000, 128, 200, "bf16", seed=44)
+    with ssc.dense_route("split"):
+        O, lse, dQ, dK, dV = run_dense(c)
+    Or, lser, gr = oracle_dense(c)
+    check_fwd(O, Or, lse, lser, what="split 157 blocks")
+    check_grads((dQ, dK, dV), gr, what="split 157 blocks")
