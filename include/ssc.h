@@ -232,7 +232,8 @@ ssc_status coupling_linear_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
  *   dQ = phi'(Q) * (g (phi(K)^T V)^T - s (phi(K)^T 1)^T),
  *   dK = phi'(K) * (V (phi(Q)^T g)^T - 1 (phi(Q)^T s)^T),
  *   dV = phi(K) (phi(Q)^T g).
- * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten
+ * (n_N = 0: dK = dV = 0, and Q, O, dO, den or ln den and dQ may be NULL).
  */
 ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k,
                                const void* Q, const void* K, const void* V,
@@ -269,7 +270,8 @@ ssc_status coupling_performer_fwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
  *   dPhiQ = g (phi(K)^T V)^T - s (phi(K)^T 1)^T,
  *   dPhiK = V (phi(Q)^T g)^T - 1 (phi(Q)^T s)^T,
  *   dV = phi(K) (phi(Q)^T g), and dQ, dK through d phi / dx.
- * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten.
+ * dQ [n_N x d], dK [n_M x d], dV [n_M x k] fp32, fully overwritten
+ * (n_N = 0: dK = dV = 0, and Q, O, dO, den or ln den and dQ may be NULL).
  */
 ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, int m,
                                   const void* Q, const void* K, const void* V, const void* W,

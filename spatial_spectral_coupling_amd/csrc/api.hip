@@ -1144,8 +1144,10 @@ ssc_status coupling_linear_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int k, 
                                float* dK, float* dV, void* ws, size_t ws_bytes, ssc_stream stream) {
   ssc_status st = check_linear(dtype, n_N, n_M, d, k);
   if (st != SSC_OK) return st;
-  if (n_N == 0) return SSC_OK;
-  if (!all_ok({Q, K, V, O, dO, den, dQ, dK, dV})) return SSC_ERR_INVALID_ARG;
+  // no target rows: dK = dV = 0 (the query-side Gram sum is empty), nothing
+  // reads Q, O, dO, den or writes dQ
+  if (!all_ok({K, V, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({Q, O, dO, den, dQ})) return SSC_ERR_INVALID_ARG;
   const LinLayout L = make_lin_layout(true, n_N, n_M, d, k);
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;
@@ -1229,8 +1231,9 @@ ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
   ssc_status st = check_performer(dtype, n_N, n_M, d, k, m);
   if (st != SSC_OK) return st;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SSC_ERR_INVALID_ARG;
-  if (n_N == 0) return SSC_OK;
-  if (!all_ok({Q, K, V, W, O, dO, lnden, dQ, dK, dV})) return SSC_ERR_INVALID_ARG;
+  // no target rows: dK = dV = 0, as for the linear coupling
+  if (!all_ok({K, V, W, dK, dV})) return SSC_ERR_INVALID_ARG;
+  if (n_N > 0 && !all_ok({Q, O, dO, lnden, dQ})) return SSC_ERR_INVALID_ARG;
   const PfLayout L = make_pf_layout(true, n_N, n_M, m, k);
   if (ws == nullptr || ws_bytes < L.total) return SSC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SSC_ERR_INVALID_ARG;

@@ -251,6 +251,7 @@ __global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
 
 hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
   const int grid = (a.n + pf::kRows - 1) / pf::kRows;
+  if (grid == 0) return hipSuccess;  // no rows
 #define SSC_L(DD, MM)                                                                                        \
   if (D == DD && M == MM) {                                                                                  \
     if (mode == 0) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);           \
@@ -271,6 +272,7 @@ hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st) {
 
 hipError_t launch_pf_dx(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
   const int grid = (a.n + pf::kRows - 1) / pf::kRows;
+  if (grid == 0) return hipSuccess;  // no rows
 #define SSC_L(DD, MM)                                                                                  \
   if (D == DD && M == MM) {                                                                            \
     if (mode == 0) hipLaunchKernelGGL((pf::pf_dx<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);        \

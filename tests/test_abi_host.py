@@ -193,6 +193,10 @@ def test_linear_validation_and_workspace(L):
     g = L.coupling_linear_bwd
     bargs = lambda **kw: [BF16, 64, 64, 128, 200, A[0], A[1], A[2], A[3], A[4], A[5], kw.get("dQ", A[6]), A[7],
                           A[8], kw.get("ws", None), kw.get("wsb", 0), None]
+    # no target rows: Q, O, dO, den and dQ may be NULL (dK = dV = 0 are still written)
+    assert g(BF16, 0, 64, 128, 200, None, A[1], A[2], None, None, None, None, A[7], A[8], None, 0, None) == WORKSPACE
+    assert g(BF16, 64, 64, 128, 200, None, A[1], A[2], A[3], A[4], A[5], A[6], A[7], A[8], None, 0,
+             None) == INVALID
     assert g(*bargs()) == WORKSPACE
     assert g(*bargs(dQ=A[4], ws=A[9], wsb=1 << 40)) == INVALID   # dQ aliases dO
 

@@ -105,3 +105,19 @@ def test_linear_rejects_unsupported():
     Qf = torch.zeros(4, 128, dtype=torch.float32, device="cuda")
     with pytest.raises(ssc.CouplingError):
         ssc.coupling_linear_fwd(Qf, Qf, Qf[:, :8].contiguous())
+
+
+def test_linear_without_target_rows():
+    """n_N = 0: the backward writes dK = dV = 0 (the query-side Gram sum is
+    empty; nothing reads the empty Q, O, dO, den)."""
+    say("linear without target rows")
+    c = gen.make_small(1, 300, 128, 200, "bf16", seed=7)
+    K, V = to_dev(c["K"], "bf16"), to_dev(c["V"], "bf16")
+    Q = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty(0, 200, dtype=torch.bfloat16, device="cuda")
+    O, den = ssc.coupling_linear_fwd(Q, K, V)
+    assert O.shape == (0, 200) and den.shape == (0,)
+    dQ, dK, dV = ssc.coupling_linear_bwd(Q, K, V, O, dO, den)
+    torch.cuda.synchronize()
+    assert dQ.shape == (0, 128)
+    assert torch.count_nonzero(dK).item() == 0 and torch.count_nonzero(dV).item() == 0

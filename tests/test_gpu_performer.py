@@ -124,3 +124,19 @@ def test_performer_rejects_unsupported():
         ssc.coupling_performer_fwd(Q96, Q96, V[:, :8].contiguous(), W96)   # d = 96
     with pytest.raises(ssc.CouplingError):
         ssc.coupling_performer_fwd(Q, Q, V[:, :8].contiguous(), W, scale=-1.0)
+
+
+def test_performer_without_target_rows():
+    """n_N = 0: the backward writes dK = dV = 0, as the linear coupling's."""
+    say("performer without target rows")
+    c = gen.make_small(1, 300, 128, 200, "bf16", seed=8)
+    K, V = to_dev(c["K"], "bf16"), to_dev(c["V"], "bf16")
+    W = to_dev(gen.make_favor_directions(128, 128, seed=5), "bf16")
+    Q = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty(0, 200, dtype=torch.bfloat16, device="cuda")
+    O, lnden = ssc.coupling_performer_fwd(Q, K, V, W, 128 ** -0.5)
+    assert O.shape == (0, 200)
+    dQ, dK, dV = ssc.coupling_performer_bwd(Q, K, V, W, O, dO, lnden, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert dQ.shape == (0, 128)
+    assert torch.count_nonzero(dK).item() == 0 and torch.count_nonzero(dV).item() == 0
