@@ -1184,9 +1184,10 @@ static ssc_status pf_features(int d, int m, const PfLayout& L, void* ws, int n_N
   p.X = K; p.n = n_M; p.nblk = L.nblk_M; p.F = at<bf16>(ws, L.FK);
   SSC_TRY(launch_pf_feat(d, m, 0, p, s));
   SSC_TRY(launch_pf_maxreduce(m, p, s));
-  SSC_TRY(timed("pf_feat", s, [&] { return launch_pf_feat(d, m, 1, p, s); }));
-  p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.rowoff = rowoff; p.lnden = lnden; p.den = den;
-  SSC_TRY(launch_pf_feat(d, m, qmode, p, s));
+  // key and query features in one launch (both need only the key maxima)
+  PfArgs pq = p;
+  pq.X = Q; pq.n = n_N; pq.F = at<bf16>(ws, L.FQ); pq.rowoff = rowoff; pq.lnden = lnden; pq.den = den;
+  SSC_TRY(timed("pf_feat", s, [&] { return launch_pf_feat_kq(d, m, qmode, p, pq, s); }));
   return SSC_OK;
 }
 
@@ -1265,12 +1266,13 @@ ssc_status coupling_performer_bwd(ssc_dtype dtype, int n_N, int n_M, int d, int 
                              at<char>(ws, L.lin.dM), at<char>(ws, L.lin.dMT), at<char>(ws, L.dMlo),
                              at<char>(ws, L.dMTlo), s));
   SSC_TRY(launch_lin_apply_bwd(m, KP, true, a, s));
-  PfArgs p{};
-  p.W = W; p.scale = scale;
-  p.X = Q; p.n = n_N; p.F = at<bf16>(ws, L.FQ); p.dF = at<float>(ws, L.dFQ); p.dX = dQ;
-  SSC_TRY(launch_pf_dx(d, m, 0, p, s));
-  p.X = K; p.n = n_M; p.F = at<bf16>(ws, L.FK); p.dF = at<float>(ws, L.dFK); p.dX = dK;
-  SSC_TRY(launch_pf_dx(d, m, 1, p, s));
+  // dQ and dK from the feature gradients, in one launch
+  PfArgs pq{};
+  pq.W = W; pq.scale = scale;
+  pq.X = Q; pq.n = n_N; pq.F = at<bf16>(ws, L.FQ); pq.dF = at<float>(ws, L.dFQ); pq.dX = dQ;
+  PfArgs pk = pq;
+  pk.X = K; pk.n = n_M; pk.F = at<bf16>(ws, L.FK); pk.dF = at<float>(ws, L.dFK); pk.dX = dK;
+  SSC_TRY(launch_pf_dx2(d, m, pq, pk, s));
   return SSC_OK;
 }
 

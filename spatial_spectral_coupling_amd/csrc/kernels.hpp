@@ -260,9 +260,12 @@ struct PfArgs {
 // 3: query features + den from lnden
 // D = d, M = m in {64, 128}
 hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st);
+// key features (ak, mode 1) and query features (aq, mode qmode = 2 or 3) in one launch
+hipError_t launch_pf_feat_kq(int D, int M, int qmode, const PfArgs& ak, const PfArgs& aq, hipStream_t st);
 hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st);
 // mode 0: queries (no row-sum term), 1: keys
-hipError_t launch_pf_dx(int D, int M, int mode, const PfArgs& a, hipStream_t st);
+// the query rows (aq, mode 0) and the key rows (ak, mode 1) of dX in one launch
+hipError_t launch_pf_dx2(int D, int M, const PfArgs& aq, const PfArgs& ak, hipStream_t st);
 
 // Functional-map solve after the coupling (fmap.hip): C = (Phi^T Phi)^-1 Phi^T O
 // and its backward dO = Phi (Phi^T Phi)^-1 dC.

@@ -25,10 +25,13 @@
 //                   mode 2/3: query features exp2(u - M_q), u = s + M_i, and
 //                   the row offset (forward) or the shifted den recovered
 //                   from ln den (backward);
+//                   (modes 1 and 2/3 share one launch, pf_feat_kq: both read
+//                   only the key maxima);
 //   pf_maxreduce -- M_i = max over the blocks (exact, order-free);
-//   pf_dx        -- dX = sqrt(c) (dF o F) W - c x rowsum(dF o F) (keys; for
+//   pf_dx2       -- dX = sqrt(c) (dF o F) W - c x rowsum(dF o F) (keys; for
 //                   queries the row sum vanishes: dO.O - dO.O), dF o F as a
-//                   bf16 high + low pair on MFMA.
+//                   bf16 high + low pair on MFMA; query and key rows in one
+//                   launch.
 #include "tile_bf16.hpp"
 
 namespace ssc {
@@ -61,16 +64,16 @@ __device__ __forceinline__ void stage_w(char* lds, const bf16* W, int tid) {
 }
 
 // D: row width d; M: feature count m.
+// blk: this workgroup's row block; LDS: Ws [M x D] (padded pitch), sred
+// (4 M floats for mode 0, else M), s_sq (kRows floats, mode 0).
 template <int D, int M, int MODE>
-__global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
-  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
-  __shared__ float sred[MODE == 0 ? 4 * M : M];
+__device__ __forceinline__ void feat_body(const PfArgs& a, int blk, char* Ws, float* sred, float* s_sq) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   stage_w<D, M>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
   if (MODE != 0)
     for (int f = tid; f < M; f += 256) sred[f] = a.M2[f];
-  const int row = blockIdx.x * kRows + wave * 32 + l32;
+  const int row = blk * kRows + wave * 32 + l32;
   const bool row_ok = row < a.n;
   const bf16* X = reinterpret_cast<const bf16*>(a.X) + (size_t)(row_ok ? row : 0) * D;
   bf16x8 xf[D / 16];
@@ -94,7 +97,6 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     // so a lane holds 16 rows of one feature and the maximum over the rows
     // is mostly in-lane.  The row terms come through LDS (-inf for rows past
     // the end).
-    __shared__ float s_sq[kRows];
     s_sq[wave * 32 + l32] = row_ok ? sq2 : INFINITY;
     __syncthreads();
 #pragma unroll
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
     }
     __syncthreads();
     for (int f = tid; f < M; f += 256)
-      a.part[(size_t)blockIdx.x * M + f] =
+      a.part[(size_t)blk * M + f] =
           fmaxf(fmaxf(sred[f], sred[M + f]), fmaxf(sred[2 * M + f], sred[3 * M + f]));
     return;
   }
@@ -161,6 +163,24 @@ __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
   }
 }
 
+template <int D, int M, int MODE>
+__global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
+  __shared__ float sred[MODE == 0 ? 4 * M : M];
+  __shared__ float s_sq[MODE == 0 ? kRows : 1];
+  feat_body<D, M, MODE>(a, blockIdx.x, Ws, sred, s_sq);
+}
+
+// The key features (mode 1, workgroups [0, gK)) and the query features (mode
+// QMODE, the rest) in one launch: both read only the key maxima.
+template <int D, int M, int QMODE>
+__global__ __launch_bounds__(256) void pf_feat_kq(PfArgs ak, PfArgs aq, int gK) {
+  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
+  __shared__ float sred[M];
+  if ((int)blockIdx.x < gK) feat_body<D, M, 1>(ak, blockIdx.x, Ws, sred, nullptr);
+  else feat_body<D, M, QMODE>(aq, (int)blockIdx.x - gK, Ws, sred, nullptr);
+}
+
 // One workgroup per feature (M of them): the block maxima in parallel, then a tree.
 __global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int M) {
   __shared__ float sm[4];
@@ -178,12 +198,11 @@ __global__ __launch_bounds__(256) void pf_maxreduce(PfArgs a, int M) {
 // W^T enters as transposed LDS reads (A operand: output dimension x feature),
 // so a lane's G fragment takes the features kc*16 + {4h..4h+3, 8+4h..8+4h+3}.
 template <int D, int M, int MODE>
-__global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
-  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
+__device__ __forceinline__ void dx_body(const PfArgs& a, int blk, char* Ws) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   stage_w<D, M>(Ws, reinterpret_cast<const bf16*>(a.W), tid);
-  const int row = blockIdx.x * kRows + wave * 32 + l32;
+  const int row = blk * kRows + wave * 32 + l32;
   const bool row_ok = row < a.n;
   const size_t r = (size_t)(row_ok ? row : 0) * D, rf = (size_t)(row_ok ? row : 0) * M;
   bf16x8 gh[M / 16], gl[M / 16];
@@ -245,6 +264,15 @@ __global__ __launch_bounds__(256) void pf_dx(PfArgs a) {
     }
 }
 
+// The query rows (mode 0, workgroups [0, gQ)) and the key rows (mode 1, the
+// rest) in one launch.
+template <int D, int M>
+__global__ __launch_bounds__(256) void pf_dx2(PfArgs aq, PfArgs ak, int gQ) {
+  __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
+  if ((int)blockIdx.x < gQ) dx_body<D, M, 0>(aq, blockIdx.x, Ws);
+  else dx_body<D, M, 1>(ak, (int)blockIdx.x - gQ, Ws);
+}
+
 }  // namespace pf
 
 #define SSC_PF_INSTANCES(X) X(128, 128) X(128, 64) X(64, 64) X(64, 128)
@@ -265,19 +293,32 @@ hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_pf_feat_kq(int D, int M, int qmode, const PfArgs& ak, const PfArgs& aq, hipStream_t st) {
+  const int gK = (ak.n + pf::kRows - 1) / pf::kRows, gQ = (aq.n + pf::kRows - 1) / pf::kRows;
+  if (gK + gQ == 0) return hipSuccess;
+#define SSC_L(DD, MM)                                                                                          \
+  if (D == DD && M == MM) {                                                                                    \
+    if (qmode == 2) hipLaunchKernelGGL((pf::pf_feat_kq<DD, MM, 2>), dim3(gK + gQ), dim3(256), 0, st, ak, aq, gK); \
+    else hipLaunchKernelGGL((pf::pf_feat_kq<DD, MM, 3>), dim3(gK + gQ), dim3(256), 0, st, ak, aq, gK);            \
+    return hipGetLastError();                                                                                  \
+  }
+  SSC_PF_INSTANCES(SSC_L)
+#undef SSC_L
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(pf::pf_maxreduce, dim3(M), dim3(256), 0, st, a, M);
   return hipGetLastError();
 }
 
-hipError_t launch_pf_dx(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
-  const int grid = (a.n + pf::kRows - 1) / pf::kRows;
-  if (grid == 0) return hipSuccess;  // no rows
-#define SSC_L(DD, MM)                                                                                  \
-  if (D == DD && M == MM) {                                                                            \
-    if (mode == 0) hipLaunchKernelGGL((pf::pf_dx<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);        \
-    else hipLaunchKernelGGL((pf::pf_dx<DD, MM, 1>), dim3(grid), dim3(256), 0, st, a);                  \
-    return hipGetLastError();                                                                          \
+hipError_t launch_pf_dx2(int D, int M, const PfArgs& aq, const PfArgs& ak, hipStream_t st) {
+  const int gQ = (aq.n + pf::kRows - 1) / pf::kRows, gK = (ak.n + pf::kRows - 1) / pf::kRows;
+  if (gQ + gK == 0) return hipSuccess;
+#define SSC_L(DD, MM)                                                                              \
+  if (D == DD && M == MM) {                                                                        \
+    hipLaunchKernelGGL((pf::pf_dx2<DD, MM>), dim3(gQ + gK), dim3(256), 0, st, aq, ak, gQ);         \
+    return hipGetLastError();                                                                      \
   }
   SSC_PF_INSTANCES(SSC_L)
 #undef SSC_L
