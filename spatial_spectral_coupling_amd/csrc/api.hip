@@ -1182,7 +1182,7 @@ static ssc_status pf_features(int d, int m, const PfLayout& L, void* ws, int n_N
   PfArgs p{};
   p.W = W; p.scale = scale; p.part = at<float>(ws, L.part); p.M2 = at<float>(ws, L.M2);
   p.X = K; p.n = n_M; p.nblk = L.nblk_M; p.F = at<bf16>(ws, L.FK);
-  SSC_TRY(launch_pf_feat(d, m, 0, p, s));
+  SSC_TRY(launch_pf_keymax(d, m, p, s));
   SSC_TRY(launch_pf_maxreduce(m, p, s));
   // key and query features in one launch (both need only the key maxima)
   PfArgs pq = p;

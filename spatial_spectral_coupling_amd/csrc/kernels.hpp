@@ -256,11 +256,10 @@ struct PfArgs {
   const float* dF;      // [n x M] gradient w.r.t. the shifted features (pf_dx)
   float* dX;            // [n x D] gradient w.r.t. the rows (pf_dx output)
 };
-// mode 0: key maxima, 1: key features, 2: query features + rowoff,
-// 3: query features + den from lnden
-// D = d, M = m in {64, 128}
-hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st);
-// key features (ak, mode 1) and query features (aq, mode qmode = 2 or 3) in one launch
+// D = d, M = m in {64, 128}.  Per-block maxima of the key exponents (a.part).
+hipError_t launch_pf_keymax(int D, int M, const PfArgs& a, hipStream_t st);
+// key features (ak) and query features (aq) in one launch; qmode 2: with the
+// row offset (forward), 3: with den from ln den (backward)
 hipError_t launch_pf_feat_kq(int D, int M, int qmode, const PfArgs& ak, const PfArgs& aq, hipStream_t st);
 hipError_t launch_pf_maxreduce(int M, const PfArgs& a, hipStream_t st);
 // mode 0: queries (no row-sum term), 1: keys

@@ -163,11 +163,13 @@ __device__ __forceinline__ void feat_body(const PfArgs& a, int blk, char* Ws, fl
   }
 }
 
+// The per-block key maxima (mode 0).
 template <int D, int M, int MODE>
 __global__ __launch_bounds__(256) void pf_feat(PfArgs a) {
+  static_assert(MODE == 0, "the feature modes run in pf_feat_kq");
   __shared__ __attribute__((aligned(16))) char Ws[M * Geo<D>::PITCH];
-  __shared__ float sred[MODE == 0 ? 4 * M : M];
-  __shared__ float s_sq[MODE == 0 ? kRows : 1];
+  __shared__ float sred[4 * M];
+  __shared__ float s_sq[kRows];
   feat_body<D, M, MODE>(a, blockIdx.x, Ws, sred, s_sq);
 }
 
@@ -277,16 +279,13 @@ __global__ __launch_bounds__(256) void pf_dx2(PfArgs aq, PfArgs ak, int gQ) {
 
 #define SSC_PF_INSTANCES(X) X(128, 128) X(128, 64) X(64, 64) X(64, 128)
 
-hipError_t launch_pf_feat(int D, int M, int mode, const PfArgs& a, hipStream_t st) {
+hipError_t launch_pf_keymax(int D, int M, const PfArgs& a, hipStream_t st) {
   const int grid = (a.n + pf::kRows - 1) / pf::kRows;
   if (grid == 0) return hipSuccess;  // no rows
-#define SSC_L(DD, MM)                                                                                        \
-  if (D == DD && M == MM) {                                                                                  \
-    if (mode == 0) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);           \
-    else if (mode == 1) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 1>), dim3(grid), dim3(256), 0, st, a);      \
-    else if (mode == 2) hipLaunchKernelGGL((pf::pf_feat<DD, MM, 2>), dim3(grid), dim3(256), 0, st, a);      \
-    else hipLaunchKernelGGL((pf::pf_feat<DD, MM, 3>), dim3(grid), dim3(256), 0, st, a);                     \
-    return hipGetLastError();                                                                                \
+#define SSC_L(DD, MM)                                                                         \
+  if (D == DD && M == MM) {                                                                   \
+    hipLaunchKernelGGL((pf::pf_feat<DD, MM, 0>), dim3(grid), dim3(256), 0, st, a);            \
+    return hipGetLastError();                                                                 \
   }
   SSC_PF_INSTANCES(SSC_L)
 #undef SSC_L
