@@ -465,25 +465,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_bf16(FwdArgs a) {
   // row sum of part q (both halves of the row); with ONES, column k of O is
   // field (k/32) 16 + 4 ((k%32)/8) + k%4 of the lanes of half ((k%32)/4) % 2
   const int kk = a.k & 31, hk = (kk >> 2) & 1, fk = (a.k >> 5) * 16 + 4 * (kk >> 3) + (kk & 3);
-  auto part_l = [&](const float* pq) {
-    const float lv = ONES ? (h == hk ? pq[(size_t)fk * T] : 0.f) : pq[(F - 1) * T];
-    return lv + xor32(lv);
-  };
+  // every part's values are loaded first (at most kMaxParts), then combined
+  // in part order: the reference m, then the weighted sums
+  float ref[kMaxParts], lh[kMaxParts], lt[kMaxParts], v[kMaxParts][16];
+  static_for<kMaxParts>([&](auto q) {
+    if (q < sp.nparts) {
+      const float* pq = in + (size_t)q * F * T;
+      ref[q] = pq[(F - 2) * T];
+      lh[q] = ONES ? (h == hk ? pq[(size_t)fk * T] : 0.f) : pq[(F - 1) * T];
+      static_for<16>([&](auto i) { v[q][i] = pq[(cb * 16 + i) * T]; });
+    }
+  });
+  static_for<kMaxParts>([&](auto q) {
+    if (q < sp.nparts) lt[q] = lh[q] + xor32(lh[q]);
+  });
   float m = -INFINITY;
-  for (int q = 0; q < sp.nparts; ++q) {
-    const float* pq = in + (size_t)q * F * T;
-    const float lq = part_l(pq);
-    if (lq > 0.f) m = fmaxf(m, pq[(F - 2) * T] + log2f(lq));
-  }
+  static_for<kMaxParts>([&](auto q) {
+    if (q < sp.nparts && lt[q] > 0.f) m = fmaxf(m, ref[q] + log2f(lt[q]));
+  });
   float acc[16];
   static_for<16>([&](auto i) { acc[i] = 0.f; });
   float l = 0.f;  // this half's row sum (with ONES: column k, on its half only)
-  for (int q = 0; q < sp.nparts; ++q) {
-    const float* pq = in + (size_t)q * F * T;
-    const float w = part_l(pq) > 0.f ? fexp2(pq[(F - 2) * T] - m) : 0.f;
-    static_for<16>([&](auto i) { acc[i] = fmaf(w, pq[(cb * 16 + i) * T], acc[i]); });
-    l = fmaf(w, ONES ? (h == hk ? pq[(size_t)fk * T] : 0.f) : pq[(F - 1) * T], l);
-  }
+  static_for<kMaxParts>([&](auto q) {
+    if (q < sp.nparts) {
+      const float w = lt[q] > 0.f ? fexp2(ref[q] - m) : 0.f;
+      static_for<16>([&](auto i) { acc[i] = fmaf(w, v[q][i], acc[i]); });
+      l = fmaf(w, lh[q], l);
+    }
+  });
   const float l_tot = l + xor32(l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!row_ok) return;
