@@ -357,7 +357,9 @@ int ssc_last_hip_error(void);
  * are created up front (family NULL or capacity <= 0 disarms and frees them).
  * Families: "fwd", "dq", "dkv" (dense) and "geo_fwd", "geo_dq", "geo_dkv"
  * (dense calls on the one-patch route, see ssc_dense_split, are timed as
- * the geo families).
+ * the geo families); "lin_gram", "lin_apply" (linear forward), "pf_feat"
+ * (Performer features), "fm_gram", "fm_chol", "fm_solve", "fm_apply"
+ * (functional-map solve) and "fps" (FPS partition).
  * ssc_timer_read() waits for the recorded events and returns the summed
  * milliseconds and the number of timed launches (negated if more launches
  * happened than pairs were available), then starts a new count.
