@@ -119,7 +119,9 @@ class dense_route:
     """Route of the bf16 dense couplings on this thread inside a `with`
     block: "auto" (by size, the default), "dense" (always the dense kernels)
     or "split" (always the one-patch geo route, whose planner splits short
-    item lists along their key stream)."""
+    item lists along their key stream).  The setting is per thread: calls
+    that torch's autograd engine makes from its own thread (the backward of
+    `dense_coupling`) keep the default."""
 
     _MODES = {"auto": -1, "dense": 0, "split": 1}
 
