@@ -370,8 +370,11 @@ __global__ __launch_bounds__(256) void lin_reduce2(RedJob j0, RedJob j1) {
 // (one layout each, so two workgroups fit a CU).  With FEAT = 1 the matrix of
 // modes 0, 1, 2 runs as a bf16 high + low pair (both in LDS, two MFMAs per
 // step), and so does G_ext in mode 1.
-// Scores are computed transposed (C[col][row]) so that a lane holds its own
-// row and the operand fragments of that row come from its own registers.
+// A lane loads the operand fragments of its own row into registers.  Modes
+// 1 and 2 take them as the A operand (C[row][col]: a lane holds 32
+// consecutive columns of 16 rows, so the dQ / dK stores are whole lines, and
+// reads the phi' factor of those entries from Q or K); modes 0 and 3 take
+// them as the B operand (C[col][row]: the lane holds its own row).
 // ---------------------------------------------------------------------------
 template <int D, int KP, int MODE, int FEAT>
 struct ApplyCfg {
@@ -486,6 +489,9 @@ __device__ __forceinline__ void apply_body(const LinArgs& a, int blk, char* lds)
         gl[FEAT ? cc : 0] = pack8(lo);
       }
     }
+    // dQ as C[row][col] (the lane's G_ext fragments as the A operand): lane
+    // (l32, h) holds rows base + c_row(i, h) at columns mb * 32 + l32, so a
+    // store writes 32 consecutive columns of a row
     f32x16 acc[D / 32];
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
@@ -493,29 +499,22 @@ __device__ __forceinline__ void apply_body(const LinArgs& a, int blk, char* lds)
 #pragma unroll
       for (int cc = 0; cc < KP / 16; ++cc) {
         const bf16x8 mh = rM.read(LM, mb, cc);
-        acc[mb] = mma(mh, gf[cc], acc[mb]);
-        if (LO_M) acc[mb] = mma(rM.read(LMlo, mb, cc), gf[cc], acc[mb]);
-        if (FEAT) acc[mb] = mma(mh, gl[FEAT ? cc : 0], acc[mb]);
+        acc[mb] = mma(gf[cc], mh, acc[mb]);
+        if (LO_M) acc[mb] = mma(gf[cc], rM.read(LMlo, mb, cc), acc[mb]);
+        if (FEAT) acc[mb] = mma(gl[FEAT ? cc : 0], mh, acc[mb]);
       }
     }
-    if (row_ok) {
-      const bf16* Qr = reinterpret_cast<const bf16*>(a.Q) + (size_t)row * D;
-      float* out = a.dQ + (size_t)row * D;
+    const int base = blk * kApplyRows + wave * 32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = base + c_row(i, h);
+      if (r >= n) continue;
+      const bf16* Qr = reinterpret_cast<const bf16*>(a.Q) + (size_t)r * D;
+      float* out = a.dQ + (size_t)r * D;
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = mb * 32 + 8 * g + 4 * h;
-          if (FEAT) {
-            *reinterpret_cast<f32x4*>(out + d0) =
-                f32x4{acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
-          } else {
-            const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qr + d0);
-            *reinterpret_cast<f32x4*>(out + d0) =
-                f32x4{dphi((float)q4[0]) * acc[mb][4 * g], dphi((float)q4[1]) * acc[mb][4 * g + 1],
-                      dphi((float)q4[2]) * acc[mb][4 * g + 2], dphi((float)q4[3]) * acc[mb][4 * g + 3]};
-          }
-        }
+        const int d = mb * 32 + l32;
+        out[d] = FEAT ? acc[mb][i] : dphi((float)Qr[d]) * acc[mb][i];
       }
     }
     return;
@@ -533,33 +532,28 @@ __device__ __forceinline__ void apply_body(const LinArgs& a, int blk, char* lds)
     vf[cc] = pack8(v);
   }
   if (MODE == 2) {
+  // dK as C[row][col], as dQ in mode 1
   f32x16 c1[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) {
     c1[mb] = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < KP / 16; ++cc) {
-      c1[mb] = mma(rM.read(LM, mb, cc), vf[cc], c1[mb]);
-      if (LO_M) c1[mb] = mma(rM.read(LMlo, mb, cc), vf[cc], c1[mb]);
+      c1[mb] = mma(vf[cc], rM.read(LM, mb, cc), c1[mb]);
+      if (LO_M) c1[mb] = mma(vf[cc], rM.read(LMlo, mb, cc), c1[mb]);
     }
   }
-  if (row_ok) {
-    const bf16* Kr = reinterpret_cast<const bf16*>(a.K) + (size_t)row * D;
-    float* out = a.dK + (size_t)row * D;
+  const int base = blk * kApplyRows + wave * 32;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = base + c_row(i, h);
+    if (r >= n) continue;
+    const bf16* Kr = reinterpret_cast<const bf16*>(a.K) + (size_t)r * D;
+    float* out = a.dK + (size_t)r * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = mb * 32 + 8 * g + 4 * h;
-        if (FEAT) {
-          *reinterpret_cast<f32x4*>(out + d0) = f32x4{c1[mb][4 * g], c1[mb][4 * g + 1], c1[mb][4 * g + 2], c1[mb][4 * g + 3]};
-        } else {
-          const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(Kr + d0);
-          *reinterpret_cast<f32x4*>(out + d0) =
-              f32x4{dphi((float)k4[0]) * c1[mb][4 * g], dphi((float)k4[1]) * c1[mb][4 * g + 1],
-                    dphi((float)k4[2]) * c1[mb][4 * g + 2], dphi((float)k4[3]) * c1[mb][4 * g + 3]};
-        }
-      }
+      const int d = mb * 32 + l32;
+      out[d] = FEAT ? c1[mb][i] : dphi((float)Kr[d]) * c1[mb][i];
     }
   }
   }
